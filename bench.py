@@ -1,0 +1,327 @@
+"""Benchmark: quantize GB/s (algorithmic bytes in + out) on one MI355X.
+
+One step = one pass of the whole quantizer path over full-size synthetic
+inputs already resident in HBM (an MoE layer's worth of quantization work):
+  act   MXFP8 row+col of a 2048x2048 BF16 activation
+  wgt   MXFP8 row+col of an 8192x2048 BF16 weight
+  tok   per-token NVFP4 of 8192x2048 Student-t(3)*0.5 activations, + BF16 dequant
+  exp   NVFP4 export of 128 experts (gate/up 768x2048 under one scale per pair,
+        down 2048x768 under its own), + BF16 dequant of all three
+  grp   grouped MXFP8 row+col and per-token NVFP4 of 262,144 expert-sorted rows
+        x 2048 (32,768 tokens routed top-8 of 128), + BF16 dequant of both
+Algorithmic bytes count each input read once and each output written once.
+Each leg is bracketed by HIP events on the stream the library launches on.
+
+Prints one JSON line.  Extra fields: per-leg GB/s and % of the 8 TB/s HBM
+peak ("legs"), the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, MXFP8 row+col & NVFP4"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def csrc_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "nvfp4_block_scaled_amax_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Leg:
+    def __init__(self, name, launch, bytes_in, bytes_out, elems, kernels, desc):
+        self.name, self.launch = name, launch
+        self.bytes_in, self.bytes_out, self.elems = bytes_in, bytes_out, elems
+        self.kernels, self.desc = kernels, desc
+        self.times_ms = []
+
+    @property
+    def bytes(self):
+        return self.bytes_in + self.bytes_out
+
+
+def build_legs(torch, mxq, api, W, log):
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    u8 = torch.uint8
+    legs = []
+    E = mxq
+
+    def empty(shape, dt=u8):
+        return torch.empty(shape, dtype=dt, device="cuda")
+
+    # act / wgt: MXFP8 row+col
+    for name, (rows, cols, x_np) in (("act", (2048, 2048, W.config2_activation("random"))),
+                                     ("wgt", (8192, 2048, W.config2_weight("random")))):
+        x = dev(x_np)
+        rc, rs, cc, cs = empty((rows, cols)), empty((rows, cols // 32)), empty((rows, cols)), \
+            empty((rows // 32, cols))
+        n = rows * cols
+        legs.append(Leg(f"mxfp8_rowcol_{name}",
+                        (lambda x=x, rows=rows, cols=cols, rc=rc, rs=rs, cc=cc, cs=cs:
+                         E.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs)),
+                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_dense_kernel"],
+                        f"MXFP8 row+col {rows}x{cols}"))
+    log("act/wgt ready")
+
+    # tok: per-token NVFP4 + dequant
+    rows, cols = 8192, 2048
+    x = dev(W.config3())
+    n = rows * cols
+    codes, bs, ts = empty((rows, cols // 2)), empty((rows, cols // 16)), \
+        empty((rows,), torch.float32)
+    y = empty((rows, cols), torch.bfloat16)
+    q_out = n // 2 + n // 16 + 4 * rows
+    legs.append(Leg("nvfp4_tok", lambda: E.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts),
+                    2 * n, q_out, n, ["nvfp4_kernel"], "NVFP4 per-token 8192x2048"))
+    legs.append(Leg("nvfp4_tok_dequant",
+                    lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, codes, bs, ts, 1, rows, cols, y),
+                    q_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 8192x2048"))
+    log("tok ready")
+
+    # exp: expert export + dequant
+    gate, up, down = W.config4()
+    g, u, dn = dev(gate), dev(up), dev(down)
+    del gate, up, down
+    NE, I, H = 128, 768, 2048
+    ng = NE * I * H
+    gc, gb, uc, ub = empty((NE, I, H // 2)), empty((NE, I, H // 16)), empty((NE, I, H // 2)), \
+        empty((NE, I, H // 16))
+    dc, db = empty((NE, H, I // 2)), empty((NE, H, I // 16))
+    sp, sd = empty((NE,), torch.float32), empty((NE,), torch.float32)
+    yg, yu, yd = empty((NE * I, H), torch.bfloat16), empty((NE * I, H), torch.bfloat16), \
+        empty((NE * H, I), torch.bfloat16)
+    pair_out = 2 * (ng // 2 + ng // 16) + 4 * NE
+    down_out = ng // 2 + ng // 16 + 4 * NE
+    legs.append(Leg("nvfp4_export_gateup",
+                    lambda: E.mxq_nvfp4_quantize_gateup_pair(g, u, NE, I, H, gc, gb, uc, ub, sp),
+                    2 * 2 * ng, pair_out, 2 * ng,
+                    ["zero_u32_kernel", "scope_amax_kernel", "nvfp4_kernel", "scope_finalize_kernel"],
+                    "NVFP4 gate/up export 128x2x768x2048, shared scale per pair"))
+    legs.append(Leg("nvfp4_export_down",
+                    lambda: E.mxq_nvfp4_quantize_gateup_pair(dn, None, NE, H, I, dc, db, None, None, sd),
+                    2 * ng, down_out, ng,
+                    ["zero_u32_kernel", "scope_amax_kernel", "nvfp4_kernel", "scope_finalize_kernel"],
+                    "NVFP4 down export 128x2048x768"))
+
+    def exp_dequant():
+        E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, gc, gb, sp, I, NE * I, H, yg)
+        E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, uc, ub, sp, I, NE * I, H, yu)
+        E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, dc, db, sd, H, NE * H, I, yd)
+    legs.append(Leg("nvfp4_export_dequant", exp_dequant, pair_out + down_out, 2 * 3 * ng, 3 * ng,
+                    ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 of gate, up, down"))
+    log("exp ready")
+
+    # grp: grouped
+    xg_np, off_np = W.config5()
+    R, K = xg_np.shape
+    G = off_np.size - 1
+    xg = dev(xg_np)
+    del xg_np
+    off = torch.from_numpy(off_np).cuda()
+    n = R * K
+    g8 = {"row_codes": empty((R, K)), "row_scales": empty((R, K // 32)),
+          "col_codes": empty((R, K)), "col_scales": empty((R // 32 + G, K)),
+          "col_scale_offsets": empty((G + 1,), torch.int64)}
+    g4 = {"codes": empty((R, K // 2)), "block_scales": empty((R, K // 16)),
+          "token_scales": empty((R,), torch.float32)}
+    col_scale_rows = int(sum((int(off_np[e + 1]) - int(off_np[e]) + 31) // 32 for e in range(G)))
+    mx_out = 2 * n + n // 32 + col_scale_rows * K + 8 * (G + 1)
+    nv_out = n // 2 + n // 16 + 4 * R
+    legs.append(Leg("grouped_mxfp8_rowcol",
+                    lambda: E.mxq_grouped_quantize(E.MXQ_FMT_MXFP8_ROWCOL, xg, R, K, off, G, g8),
+                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_grouped_kernel"],
+                    f"grouped MXFP8 row+col {R}x{K}, {G} segments"))
+    legs.append(Leg("grouped_nvfp4",
+                    lambda: E.mxq_grouped_quantize(E.MXQ_FMT_NVFP4, xg, R, K, off, G, g4),
+                    2 * n + 8 * (G + 1), nv_out, n, ["nvfp4_kernel"],
+                    f"grouped per-token NVFP4 {R}x{K}"))
+    y8, y4 = empty((R, K), torch.bfloat16), empty((R, K), torch.bfloat16)
+    legs.append(Leg("grouped_dequant_mxfp8",
+                    lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_MXFP8_ROW, g8["row_codes"],
+                                                  g8["row_scales"], None, 0, R, K, y8),
+                    n + n // 32, 2 * n, n, ["dequant_mxfp8_kernel"], "MXFP8 rowwise -> BF16"))
+    legs.append(Leg("grouped_dequant_nvfp4",
+                    lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, g4["codes"], g4["block_scales"],
+                                                  g4["token_scales"], 1, R, K, y4),
+                    nv_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16"))
+    log("grp ready")
+    return legs
+
+
+def cpu_baseline(W, log):
+    """The oracle (as it stands) on a bounded sample of every leg: 1/64 of the
+    rows (1/64 of the experts for the export), timed on the host cores."""
+    import oracle
+    if not os.path.exists(oracle._LIB):
+        oracle.build()
+    total_bytes, t0 = 0, time.perf_counter()
+    x = W.config2_weight("random")[:128]
+    oracle.mxfp8_rowwise(x)
+    oracle.mxfp8_colwise(x)
+    total_bytes += x.size * 4 + x.size // 16
+    a = W.config2_activation("random")[:32]
+    oracle.mxfp8_rowwise(a)
+    oracle.mxfp8_colwise(a)
+    total_bytes += a.size * 4 + a.size // 16
+    t = W.config3()[:128]
+    c, b, s = oracle.nvfp4_per_token(t)
+    oracle.dequant_nvfp4(c, b, s, 1)
+    total_bytes += 2 * (2 * t.size + t.size // 2 + t.size // 16 + 4 * 128)
+    gate, up, down = W.config4(2)
+    gc, gb, uc, ub, sp = oracle.nvfp4_gateup_pair(gate, up)
+    dc, db, _, _, sd = oracle.nvfp4_gateup_pair(down, None)
+    oracle.dequant_nvfp4(gc.reshape(-1, 1024), gb.reshape(-1, 128), sp, 768)
+    oracle.dequant_nvfp4(uc.reshape(-1, 1024), ub.reshape(-1, 128), sp, 768)
+    oracle.dequant_nvfp4(dc.reshape(-1, 384), db.reshape(-1, 48), sd, 2048)
+    ng = gate.size
+    total_bytes += 2 * (3 * 2 * ng + 3 * (ng // 2 + ng // 16))
+    xg = W.student_t_activations(4096, 2048, 5)
+    rc, rs = oracle.mxfp8_rowwise(xg)
+    oracle.mxfp8_colwise(xg)
+    c, b, s = oracle.nvfp4_per_token(xg)
+    oracle.dequant_mxfp8_rowwise(rc, rs)
+    oracle.dequant_nvfp4(c, b, s, 1)
+    n = xg.size
+    total_bytes += (2 * n + 2 * n + n // 16) + (2 * n + n // 2 + n // 16) + \
+        (n + n // 32 + 2 * n) + (n // 2 + n // 16 + 2 * n)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {total_bytes / 1e9:.3f} GB in {dt:.1f} s")
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": ("1/64 of each leg's rows (128 weight rows, 32 activation rows, 128 "
+                       "tokens, 2 of 128 experts, 4096 of 262144 grouped rows; generation "
+                       "excluded)"),
+            "seconds": round(dt, 2), "bytes": total_bytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantizers shard by rows with no exchange, "
+              "and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_block_scaled_amax_amd as mxq
+    from nvfp4_block_scaled_amax_amd import api
+    from nvfp4_block_scaled_amax_amd import workloads as W
+
+    mxq.lib()
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    legs = build_legs(torch, mxq, api, W, log)
+    log(f"inputs generated and resident in {time.perf_counter() - t_gen:.1f} s")
+
+    stream = torch.cuda.current_stream()
+
+    def step(timed):
+        for leg in legs:
+            if timed:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                leg.launch()
+                b.record(stream)
+                leg._ev.append((a, b))
+            else:
+                leg.launch()
+
+    for leg in legs:
+        leg._ev = []
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s)")
+
+    total_bytes = sum(l.bytes for l in legs)
+    total_elems = sum(l.elems for l in legs)
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    leg_info = {}
+    for l in legs:
+        ts = [a.elapsed_time(b) for a, b in l._ev]
+        ms = float(np.mean(ts))
+        gbs = l.bytes / (ms * 1e-3) / 1e9
+        leg_info[l.name] = {"desc": l.desc, "ms": round(ms, 5), "ms_min": round(float(np.min(ts)), 5),
+                            "bytes": l.bytes, "GB_s": round(gbs, 1),
+                            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                            "elements_per_s": round(l.elems / (ms * 1e-3), 1)}
+    dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
+    dom_ms = leg_info[dom.name]["ms"]
+    achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("csrc_digest") == csrc_digest() and tr.get("leg") == dom.name:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom.kernels[-1], "leg": dom.name, "algorithmic_bytes": dom.bytes,
+                "ms_per_launch": dom_ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W, log)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "moe-layer quantize step: MXFP8 row+col 2048x2048 + 8192x2048, "
+                               "per-token NVFP4 8192x2048 + dequant, NVFP4 export of 128 "
+                               "experts (gate/up pairs + down) + dequant, grouped MXFP8 row+col "
+                               "+ NVFP4 over 262144x2048 top-8/128 + dequant",
+                   "bytes_per_step": total_bytes, "elements_per_step": total_elems},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(total_elems / (ms_per_step * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": leg_info,
+        "csrc_digest": csrc_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

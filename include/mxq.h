@@ -1,0 +1,233 @@
+/*
+ * mxq.h -- C ABI of libmxq: bit-exact MXFP8 and per-token NVFP4 quantizers
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the precision contract that training forward and
+ * rollout share, as described on the page "Miles: end-to-end MXFP8 and
+ * per-token NVFP4 RL on Blackwell" (aioga.com news page, English text):
+ * its MXFP8 format and MXFP8 recipe paragraphs, its NVFP4 format paragraph,
+ * its per-token activation scale paragraphs, its gate/up pairing paragraph
+ * and its dequantized-backward paragraph.  Each entry point below names the
+ * passage it implements.
+ *
+ * ---------------------------------------------------------------------------
+ * Formats (readings where the pages only name the format):
+ *   BF16   input/output, passed as uint16_t bit patterns.
+ *   E4M3   1-4-3 float without infinities: largest finite 448 (0x7E), NaN
+ *          0x7F/0xFF (never produced), subnormals down to 2^-9.
+ *   E8M0   unsigned byte b meaning 2^(b-127); 0xFF (NaN) is never produced.
+ *   E2M1   1-2-1 float in a nibble: magnitudes {0,.5,1,1.5,2,3,4,6}, bit 3 is
+ *          the sign.  Two per byte, the even element in the low nibble.
+ *   FP32   IEEE binary32.
+ *
+ * Arithmetic (the same for every entry point):
+ *   - Every narrowing conversion rounds to the nearest value of the target
+ *     format, an exact tie going to the even code; magnitudes at or above the
+ *     largest finite value give that value; the sign is kept (a negative input
+ *     that rounds to zero gives a negative-zero code).  Every result is
+ *     rounded once, from the exact value.
+ *   - MXFP8: per block of 32 values, e = the smallest integer >= -127 with
+ *     amax <= 448 * 2^e (so the block maximum is never clipped); scale byte
+ *     e + 127; code = E4M3(x / 2^e).  An all-zero block gets byte 0x00.
+ *   - NVFP4: s = fp32(amax_scope / 2688) (one IEEE binary32 division; 2688 =
+ *     6 * 448); s is the decode multiplier.  Per block of 16 values: block
+ *     scale b = E4M3(amax_block / (6 s)); element code c = E2M1(x / (dec(b) s)).
+ *     If dec(b) == 0 (which includes s == 0) the block's codes are 0x0.
+ *   - Dequant: BF16(dec(code) * dec(scale) [* s]) rounded once from the exact
+ *     product, ties to even, saturating at the largest finite BF16 (0x7F7F).
+ *   - NaN and Inf inputs are outside the contract.
+ *
+ * Layouts: plain row-major, no padding, no swizzle.  X is [rows][cols] with
+ * cols the contiguous (contraction) dimension.
+ *
+ * Conventions for every entry point:
+ *   - Every array is device memory of the current HIP device, allocated and
+ *     owned by the caller.  The library allocates nothing and keeps no state
+ *     between calls.  Inputs are never modified.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue their kernels and return; results are valid once the
+ *     stream has been synchronized.  Calls on one stream are ordered.
+ *   - A return value other than MXQ_OK means nothing was launched and nothing
+ *     was written.  All validation happens on the host before any launch:
+ *     null pointers, sizes, divisibility, 16-byte alignment of every array
+ *     that the kernels access with vector loads or stores, pointers that are
+ *     not device memory of the current device, arrays whose extent runs past
+ *     the end of their device allocation (the allocation the runtime knows:
+ *     a tensor carved from a caching allocator's segment is checked against
+ *     the segment), and overlapping ranges between any input and any output
+ *     or between two outputs.  A failed launch returns MXQ_ERR_LAUNCH; faults
+ *     on the device surface at synchronization.
+ *   - Sizes are int64_t; element counts up to 2^62 are supported.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_VERSION 1
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    MXQ_ERR_SIZE = 2,      /* a size is <= 0 (or n_groups < 1)                */
+    MXQ_ERR_SHAPE = 3,     /* cols (or rows) not divisible as required        */
+    MXQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                */
+    MXQ_ERR_ALIAS = 5,     /* an output overlaps an input or another output   */
+    MXQ_ERR_OFFSETS = 6,   /* inconsistent optional-output combination        */
+    MXQ_ERR_DEVICE = 7,    /* not device memory of the current device         */
+    MXQ_ERR_LAUNCH = 8,    /* the kernel launch failed                        */
+    MXQ_ERR_ARG = 9        /* an enum argument has an unknown value           */
+} mxq_status;
+
+typedef enum {
+    MXQ_FMT_MXFP8_ROW = 1,     /* MXFP8 rowwise 1x32 copy                    */
+    MXQ_FMT_MXFP8_COL = 2,     /* MXFP8 columnwise 32x1 copy                 */
+    MXQ_FMT_MXFP8_ROWCOL = 3,  /* both MXFP8 copies from one read            */
+    MXQ_FMT_NVFP4 = 4          /* NVFP4 with a per-token FP32 scale          */
+} mxq_format;
+
+/*
+ * MXFP8 quantize, rowwise and columnwise copies from one read of X.
+ * Implements the MXFP8 format paragraph (32 E4M3 values per E8M0 scale, scale
+ * rounded up so the block maximum is not clipped) and the MXFP8 recipe
+ * paragraph (rowwise 1x32 and columnwise 32x1 copies, each quantized from the
+ * full-precision data, both made during one quantization).
+ *
+ *   x          [rows][cols] BF16, 16-byte aligned.
+ *   row_codes  [rows][cols] E4M3; row_codes[i][k] is x[i][k]'s code under the
+ *              scale of its rowwise block k/32.
+ *   row_scales [rows][cols/32] E8M0.
+ *   col_codes  [rows][cols] E4M3, same index as x; col_codes[i][k] is
+ *              x[i][k]'s code under the scale of its columnwise block i/32.
+ *   col_scales [rows/32][cols] E8M0.
+ *   Pass both row pointers NULL to skip the rowwise copy, both col pointers
+ *   NULL to skip the columnwise copy (not both copies); one NULL of a pair is
+ *   MXQ_ERR_OFFSETS.  Requires cols % 32 == 0, and rows % 32 == 0 when the
+ *   columnwise copy is requested.  Code arrays must be 16-byte aligned.
+ */
+int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols,
+                              uint8_t *row_codes, uint8_t *row_scales,
+                              uint8_t *col_codes, uint8_t *col_scales,
+                              void *stream);
+
+/*
+ * NVFP4 quantize with one online FP32 scale per token (row), in one call that
+ * returns the packed codes, the E4M3 block scales and the per-token scales.
+ * Implements the NVFP4 format paragraph (E2M1 codes, one E4M3 scale per 16
+ * values rounded to the nearest E4M3 value, one FP32 scale over a larger
+ * scope) and the per-token activation paragraphs (the scope is one token; the
+ * scale is computed inside the quantization call, with no separate pass).
+ *
+ *   x            [rows][cols] BF16, 16-byte aligned; cols % 16 == 0.
+ *   codes        [rows][cols/2] packed E2M1, 16-byte aligned.
+ *   block_scales [rows][cols/16] E4M3.
+ *   token_scales [rows] FP32: s_t = fp32(amax_t / 2688), the decode multiplier.
+ */
+int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *codes, uint8_t *block_scales,
+                                 float *token_scales, void *stream);
+
+/*
+ * NVFP4 weight export with one FP32 scale per scope.  Implements the gate/up
+ * pairing paragraph: a SwiGLU expert's gate and up projections are quantized
+ * together under one shared FP32 scale (the scope is gate[e] together with
+ * up[e]); with up == NULL each gate[e] is its own scope (e.g. a down
+ * projection).  Blocks of 16 run along each tensor's last dimension, the
+ * contraction axis (the paragraph on one-dimensional blocks and contraction
+ * axes).  The scope's amax is reduced over every element of the scope before
+ * any code is produced.
+ *
+ *   gate, up             [n_experts][rows][cols] BF16, 16-byte aligned;
+ *                        cols % 16 == 0.
+ *   gate_codes, up_codes [n_experts][rows][cols/2], 16-byte aligned.
+ *   gate_block_scales, up_block_scales  [n_experts][rows][cols/16].
+ *   scope_scales         [n_experts] FP32; used as the amax accumulator during
+ *                        the call and holding s_e = fp32(amax_e / 2688) when
+ *                        it completes.
+ *   up, up_codes and up_block_scales must be all NULL or all non-NULL.
+ */
+int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up,
+                                   int64_t n_experts, int64_t rows, int64_t cols,
+                                   uint8_t *gate_codes, uint8_t *gate_block_scales,
+                                   uint8_t *up_codes, uint8_t *up_block_scales,
+                                   float *scope_scales, void *stream);
+
+/*
+ * Dequantize to BF16: the exact low-precision operands made by the calls
+ * above, decoded and rounded once to BF16.  Implements the dequantized-
+ * backward paragraph (backward GEMMs consume BF16 dequantizations of the exact
+ * forward operands).
+ *
+ *   fmt == MXQ_FMT_MXFP8_ROW: codes [rows][cols], scales [rows][cols/32];
+ *          cols % 32 == 0.
+ *   fmt == MXQ_FMT_MXFP8_COL: codes [rows][cols], scales [rows/32][cols];
+ *          rows % 32 == 0, cols % 32 == 0.
+ *   fmt == MXQ_FMT_NVFP4: codes [rows][cols/2], scales [rows][cols/16] (E4M3),
+ *          fp32_scales[i / rows_per_fp32_scale] is row i's FP32 scale
+ *          (1 = per token, rows = one per tensor, R = one per R-row expert);
+ *          cols % 16 == 0, rows_per_fp32_scale >= 1.
+ *   fp32_scales and rows_per_fp32_scale are ignored for MXFP8 (may be NULL/0).
+ *   out [rows][cols] BF16, 16-byte aligned.
+ */
+int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
+                        const float *fp32_scales, int64_t rows_per_fp32_scale,
+                        int64_t rows, int64_t cols, uint16_t *out, void *stream);
+
+/*
+ * Outputs of the grouped call.  MXFP8 uses the first five fields, NVFP4 the
+ * last three; the others are ignored.
+ *   row_codes, row_scales  as mxq_mxfp8_quantize_rowcol over all total_rows.
+ *   col_codes   [total_rows][cols], same index as x.
+ *   col_scales  room for total_rows/32 + n_groups rows of cols bytes; segment
+ *               e's blocks of 32 rows start at its first row, its last block
+ *               covers the rows that remain (amax over existing rows), and its
+ *               scale rows start at P[e] = sum_{f<e} ceil(n_f / 32).
+ *   col_scale_offsets [n_groups + 1] int64, written by the call: P[0..G].
+ *   codes, block_scales, token_scales  as mxq_nvfp4_quantize_per_token.
+ */
+typedef struct {
+    uint8_t *row_codes;
+    uint8_t *row_scales;
+    uint8_t *col_codes;
+    uint8_t *col_scales;
+    int64_t *col_scale_offsets;
+    uint8_t *codes;
+    uint8_t *block_scales;
+    float *token_scales;
+} mxq_grouped_out;
+
+/*
+ * Grouped quantize over ragged MoE expert segments: x holds the rows of all
+ * experts, sorted by expert; segment e is rows [seg_offsets[e],
+ * seg_offsets[e+1]).  Rowwise MXFP8 and per-token NVFP4 outputs do not depend
+ * on the segments (per-token scales make every row independent of the others:
+ * the batch-invariance argument of the per-token paragraphs); columnwise MXFP8
+ * blocks restart at each segment.  Implements the MXFP8 and NVFP4 passages
+ * above for the MoE expert path.
+ *
+ *   fmt           MXQ_FMT_MXFP8_ROWCOL or MXQ_FMT_NVFP4.
+ *   x             [total_rows][cols] BF16, 16-byte aligned.
+ *   seg_offsets   device int64 [n_groups + 1], 0 = o_0 <= ... <= o_G =
+ *                 total_rows (read on the device; not validated on the host).
+ *   out           host pointer to the output struct (device arrays inside).
+ */
+int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
+                         int64_t cols, const int64_t *seg_offsets,
+                         int64_t n_groups, const mxq_grouped_out *out,
+                         void *stream);
+
+/* A static, human-readable message for a status code. */
+const char *mxq_status_string(int status);
+
+/* MXQ_VERSION of the built library. */
+int mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

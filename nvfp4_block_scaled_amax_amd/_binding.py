@@ -1,0 +1,160 @@
+"""ctypes binding of libmxq.so: one Python function per C entry point, with the
+same name and argument order as include/mxq.h.
+
+Array arguments may be torch tensors (their data_ptr() is passed), plain
+integer addresses, or None for NULL.  `stream` may be None (torch's current
+stream on the current device), a torch.cuda.Stream, or an integer hipStream_t.
+A status other than MXQ_OK raises MXQError.  This module only marshals
+arguments; every step runs in the library's kernels, and a missing library
+raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxq.so")
+
+MXQ_OK = 0
+MXQ_ERR_NULL = 1
+MXQ_ERR_SIZE = 2
+MXQ_ERR_SHAPE = 3
+MXQ_ERR_ALIGN = 4
+MXQ_ERR_ALIAS = 5
+MXQ_ERR_OFFSETS = 6
+MXQ_ERR_DEVICE = 7
+MXQ_ERR_LAUNCH = 8
+MXQ_ERR_ARG = 9
+
+MXQ_FMT_MXFP8_ROW = 1
+MXQ_FMT_MXFP8_COL = 2
+MXQ_FMT_MXFP8_ROWCOL = 3
+MXQ_FMT_NVFP4 = 4
+
+# Every symbol include/mxq.h declares.
+EXPORTS = (
+    "mxq_mxfp8_quantize_rowcol",
+    "mxq_nvfp4_quantize_per_token",
+    "mxq_nvfp4_quantize_gateup_pair",
+    "mxq_dequantize_bf16",
+    "mxq_grouped_quantize",
+    "mxq_status_string",
+    "mxq_version",
+)
+
+
+class MXQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {mxq_status_string(status)}")
+
+
+class mxq_grouped_out(ctypes.Structure):
+    _fields_ = [("row_codes", ctypes.c_void_p), ("row_scales", ctypes.c_void_p),
+                ("col_codes", ctypes.c_void_p), ("col_scales", ctypes.c_void_p),
+                ("col_scale_offsets", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("block_scales", ctypes.c_void_p), ("token_scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmxq.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmxq.so is not built ({LIB_PATH}); run "
+                           "`python -m nvfp4_block_scaled_amax_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "mxq_mxfp8_quantize_rowcol": [P, I64, I64, P, P, P, P, P],
+        "mxq_nvfp4_quantize_per_token": [P, I64, I64, P, P, P, P],
+        "mxq_nvfp4_quantize_gateup_pair": [P, P, I64, I64, I64, P, P, P, P, P, P],
+        "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
+        "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = I
+    L.mxq_status_string.argtypes = [I]
+    L.mxq_status_string.restype = ctypes.c_char_p
+    L.mxq_version.argtypes = []
+    L.mxq_version.restype = I
+    _lib = L
+    return L
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MXQ_OK:
+        raise MXQError(status, where)
+
+
+def mxq_status_string(status: int) -> str:
+    return lib().mxq_status_string(status).decode()
+
+
+def mxq_version() -> int:
+    return lib().mxq_version()
+
+
+def mxq_mxfp8_quantize_rowcol(x, rows, cols, row_codes, row_scales, col_codes, col_scales,
+                              stream=None):
+    _check(lib().mxq_mxfp8_quantize_rowcol(_ptr(x), rows, cols, _ptr(row_codes),
+                                           _ptr(row_scales), _ptr(col_codes), _ptr(col_scales),
+                                           _stream(stream)),
+           "mxq_mxfp8_quantize_rowcol")
+
+
+def mxq_nvfp4_quantize_per_token(x, rows, cols, codes, block_scales, token_scales, stream=None):
+    _check(lib().mxq_nvfp4_quantize_per_token(_ptr(x), rows, cols, _ptr(codes),
+                                              _ptr(block_scales), _ptr(token_scales),
+                                              _stream(stream)),
+           "mxq_nvfp4_quantize_per_token")
+
+
+def mxq_nvfp4_quantize_gateup_pair(gate, up, n_experts, rows, cols, gate_codes,
+                                   gate_block_scales, up_codes, up_block_scales, scope_scales,
+                                   stream=None):
+    _check(lib().mxq_nvfp4_quantize_gateup_pair(_ptr(gate), _ptr(up), n_experts, rows, cols,
+                                                _ptr(gate_codes), _ptr(gate_block_scales),
+                                                _ptr(up_codes), _ptr(up_block_scales),
+                                                _ptr(scope_scales), _stream(stream)),
+           "mxq_nvfp4_quantize_gateup_pair")
+
+
+def mxq_dequantize_bf16(fmt, codes, scales, fp32_scales, rows_per_fp32_scale, rows, cols, out,
+                        stream=None):
+    _check(lib().mxq_dequantize_bf16(fmt, _ptr(codes), _ptr(scales), _ptr(fp32_scales),
+                                     rows_per_fp32_scale, rows, cols, _ptr(out), _stream(stream)),
+           "mxq_dequantize_bf16")
+
+
+def mxq_grouped_quantize(fmt, x, total_rows, cols, seg_offsets, n_groups, out, stream=None):
+    """`out`: an mxq_grouped_out, or a dict with its field names."""
+    if not isinstance(out, mxq_grouped_out):
+        out = mxq_grouped_out(**{k: _ptr(v) for k, v in out.items()})
+    _check(lib().mxq_grouped_quantize(fmt, _ptr(x), total_rows, cols, _ptr(seg_offsets),
+                                      n_groups, ctypes.byref(out), _stream(stream)),
+           "mxq_grouped_quantize")

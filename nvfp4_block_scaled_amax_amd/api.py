@@ -1,0 +1,128 @@
+"""Tensor-level helpers over the C ABI: allocate outputs with torch.empty on
+the input's device and call the library.  BF16 inputs may be torch.bfloat16 or
+int16/uint16 tensors of bit patterns; they must be contiguous HIP tensors."""
+from __future__ import annotations
+
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _binding as B
+
+
+def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        if not x.is_contiguous():
+            raise ValueError("input must be contiguous")
+        return x
+    raise TypeError(f"expected a BF16 tensor (or its int16 bits), got {x.dtype}")
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+class MXFP8RowCol(NamedTuple):
+    row_codes: Optional[torch.Tensor]
+    row_scales: Optional[torch.Tensor]
+    col_codes: Optional[torch.Tensor]
+    col_scales: Optional[torch.Tensor]
+
+
+def mxfp8_quantize_rowcol(x, rowwise: bool = True, colwise: bool = True,
+                          stream=None) -> MXFP8RowCol:
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    u8 = torch.uint8
+    rc = _empty((rows, cols), u8, x) if rowwise else None
+    rs = _empty((rows, cols // 32), u8, x) if rowwise else None
+    cc = _empty((rows, cols), u8, x) if colwise else None
+    cs = _empty((rows // 32, cols), u8, x) if colwise else None
+    B.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs, stream)
+    return MXFP8RowCol(rc, rs, cc, cs)
+
+
+class NVFP4(NamedTuple):
+    codes: torch.Tensor
+    block_scales: torch.Tensor
+    fp32_scales: torch.Tensor
+
+
+def nvfp4_quantize_per_token(x, stream=None) -> NVFP4:
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    codes = _empty((rows, cols // 2), torch.uint8, x)
+    bs = _empty((rows, cols // 16), torch.uint8, x)
+    ts = _empty((rows,), torch.float32, x)
+    B.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts, stream)
+    return NVFP4(codes, bs, ts)
+
+
+class GateUpNVFP4(NamedTuple):
+    gate_codes: torch.Tensor
+    gate_block_scales: torch.Tensor
+    up_codes: Optional[torch.Tensor]
+    up_block_scales: Optional[torch.Tensor]
+    scope_scales: torch.Tensor
+
+
+def nvfp4_quantize_gateup_pair(gate, up=None, stream=None) -> GateUpNVFP4:
+    gate = _bf16_bits(gate)
+    E, rows, cols = gate.shape
+    gc = _empty((E, rows, cols // 2), torch.uint8, gate)
+    gb = _empty((E, rows, cols // 16), torch.uint8, gate)
+    uc = ub = None
+    if up is not None:
+        up = _bf16_bits(up)
+        if up.shape != gate.shape:
+            raise ValueError("gate and up must have the same shape")
+        uc = torch.empty_like(gc)
+        ub = torch.empty_like(gb)
+    sc = _empty((E,), torch.float32, gate)
+    B.mxq_nvfp4_quantize_gateup_pair(gate, up, E, rows, cols, gc, gb, uc, ub, sc, stream)
+    return GateUpNVFP4(gc, gb, uc, ub, sc)
+
+
+def dequantize_bf16(fmt: int, codes, scales, fp32_scales=None, rows_per_fp32_scale: int = 1,
+                    stream=None) -> torch.Tensor:
+    """Returns a torch.bfloat16 tensor [rows][cols]."""
+    rows = codes.shape[0] if codes.dim() == 2 else codes.shape[0] * codes.shape[1]
+    last = codes.shape[-1]
+    cols = 2 * last if fmt == B.MXQ_FMT_NVFP4 else last
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    B.mxq_dequantize_bf16(fmt, codes, scales, fp32_scales, rows_per_fp32_scale, rows, cols, out,
+                          stream)
+    return out
+
+
+class GroupedMXFP8(NamedTuple):
+    row_codes: torch.Tensor
+    row_scales: torch.Tensor
+    col_codes: torch.Tensor
+    col_scales: torch.Tensor          # capacity rows; the first P[G] are written
+    col_scale_offsets: torch.Tensor
+
+
+def grouped_quantize_mxfp8(x, seg_offsets, stream=None) -> GroupedMXFP8:
+    x = _bf16_bits(x)
+    R, cols = x.shape
+    G = seg_offsets.numel() - 1
+    u8 = torch.uint8
+    out = GroupedMXFP8(_empty((R, cols), u8, x), _empty((R, cols // 32), u8, x),
+                       _empty((R, cols), u8, x), _empty((R // 32 + G, cols), u8, x),
+                       _empty((G + 1,), torch.int64, x))
+    B.mxq_grouped_quantize(B.MXQ_FMT_MXFP8_ROWCOL, x, R, cols, seg_offsets, G,
+                           out._asdict(), stream)
+    return out
+
+
+def grouped_quantize_nvfp4(x, seg_offsets, stream=None) -> NVFP4:
+    x = _bf16_bits(x)
+    R, cols = x.shape
+    G = seg_offsets.numel() - 1
+    res = NVFP4(_empty((R, cols // 2), torch.uint8, x), _empty((R, cols // 16), torch.uint8, x),
+                _empty((R,), torch.float32, x))
+    B.mxq_grouped_quantize(B.MXQ_FMT_NVFP4, x, R, cols, seg_offsets, G,
+                           {"codes": res.codes, "block_scales": res.block_scales,
+                            "token_scales": res.fp32_scales}, stream)
+    return res

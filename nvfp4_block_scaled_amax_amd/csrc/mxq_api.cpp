@@ -1,0 +1,304 @@
+// mxq_api.cpp -- the C ABI of libmxq (declared in include/mxq.h): host-side
+// validation, then the launch.  Nothing here allocates device memory.
+#include "mxq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mxq_launch.h"
+
+namespace {
+
+// One array argument: its extent in bytes, required alignment, and whether
+// the call writes it.
+struct Buf {
+    const void *p;
+    int64_t bytes;
+    int align;
+    bool output;
+};
+
+constexpr int64_t MAX_ELEMS = (int64_t)1 << 62;
+
+bool size_ok(int64_t a, int64_t b)
+{
+    return a > 0 && b > 0 && a <= MAX_ELEMS / b;
+}
+
+// Device memory of the current device, and [p, p + bytes) inside one
+// allocation.
+int check_device(const Buf &b, int device)
+{
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, b.p) != hipSuccess) {
+        (void)hipGetLastError();
+        return MXQ_ERR_DEVICE;
+    }
+    if (attr.type != hipMemoryTypeDevice || attr.device != device)
+        return MXQ_ERR_DEVICE;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(b.p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return MXQ_ERR_DEVICE;
+    }
+    const uintptr_t lo = (uintptr_t)base, p = (uintptr_t)b.p;
+    if (p < lo || (uint64_t)(p - lo) + (uint64_t)b.bytes > (uint64_t)size)
+        return MXQ_ERR_DEVICE;
+    return MXQ_OK;
+}
+
+bool overlaps(const Buf &a, const Buf &b)
+{
+    const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+    const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// Alignment, device residency and extent of every buffer, then pairwise
+// overlap between any output and any other buffer.
+int check_bufs(const Buf *bufs, int n)
+{
+    for (int i = 0; i < n; i++)
+        if (((uintptr_t)bufs[i].p) % (uintptr_t)bufs[i].align != 0)
+            return MXQ_ERR_ALIGN;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return MXQ_ERR_DEVICE;
+    }
+    for (int i = 0; i < n; i++) {
+        const int st = check_device(bufs[i], device);
+        if (st != MXQ_OK)
+            return st;
+    }
+    for (int i = 0; i < n; i++)
+        for (int j = i + 1; j < n; j++)
+            if ((bufs[i].output || bufs[j].output) && overlaps(bufs[i], bufs[j]))
+                return MXQ_ERR_ALIAS;
+    return MXQ_OK;
+}
+
+int launched(hipError_t e)
+{
+    return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxq_version(void)
+{
+    return MXQ_VERSION;
+}
+
+const char *mxq_status_string(int status)
+{
+    switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "a required pointer is NULL";
+    case MXQ_ERR_SIZE: return "a size is not positive (or too large), or n_groups < 1";
+    case MXQ_ERR_SHAPE: return "rows/cols not divisible as the format requires";
+    case MXQ_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes for vector-accessed arrays)";
+    case MXQ_ERR_ALIAS: return "an output overlaps an input or another output";
+    case MXQ_ERR_OFFSETS: return "inconsistent combination of optional outputs";
+    case MXQ_ERR_DEVICE: return "an array is not device memory of the current device, or extends past the end of its allocation";
+    case MXQ_ERR_LAUNCH: return "kernel launch failed";
+    case MXQ_ERR_ARG: return "unknown format argument";
+    default: return "unknown status";
+    }
+}
+
+int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,
+                              uint8_t *row_scales, uint8_t *col_codes, uint8_t *col_scales,
+                              void *stream)
+{
+    if (!x)
+        return MXQ_ERR_NULL;
+    if ((row_codes == nullptr) != (row_scales == nullptr) ||
+        (col_codes == nullptr) != (col_scales == nullptr) || (!row_codes && !col_codes))
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols))
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0 || (col_codes && rows % 32 != 0))
+        return MXQ_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    Buf b[5];
+    int k = 0;
+    b[k++] = {x, 2 * n, 16, false};
+    if (row_codes) {
+        b[k++] = {row_codes, n, 16, true};
+        b[k++] = {row_scales, n / 32, 1, true};
+    }
+    if (col_codes) {
+        b[k++] = {col_codes, n, 16, true};
+        b[k++] = {col_scales, n / 32, 8, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_dense(x, rows, cols, row_codes, row_scales, col_codes,
+                                            col_scales, (hipStream_t)stream));
+}
+
+int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                                 uint8_t *block_scales, float *token_scales, void *stream)
+{
+    if (!x || !codes || !block_scales || !token_scales)
+        return MXQ_ERR_NULL;
+    if (!size_ok(rows, cols))
+        return MXQ_ERR_SIZE;
+    if (cols % 16 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    const Buf b[4] = {{x, 2 * n, 16, false},
+                      {codes, n / 2, 16, true},
+                      {block_scales, n / 16, 1, true},
+                      {token_scales, 4 * rows, 4, true}};
+    const int st = check_bufs(b, 4);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_per_token(x, rows, cols, codes, block_scales, token_scales,
+                                                (hipStream_t)stream));
+}
+
+int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
+                                   int64_t rows, int64_t cols, uint8_t *gate_codes,
+                                   uint8_t *gate_block_scales, uint8_t *up_codes,
+                                   uint8_t *up_block_scales, float *scope_scales, void *stream)
+{
+    if (!gate || !gate_codes || !gate_block_scales || !scope_scales)
+        return MXQ_ERR_NULL;
+    const bool has_up = up != nullptr;
+    if ((up_codes != nullptr) != has_up || (up_block_scales != nullptr) != has_up)
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols) || n_experts <= 0 || !size_ok(n_experts, rows * cols))
+        return MXQ_ERR_SIZE;
+    if (cols % 16 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t n = n_experts * rows * cols;
+    Buf b[7];
+    int k = 0;
+    b[k++] = {gate, 2 * n, 16, false};
+    b[k++] = {gate_codes, n / 2, 16, true};
+    b[k++] = {gate_block_scales, n / 16, 1, true};
+    b[k++] = {scope_scales, 4 * n_experts, 4, true};
+    if (has_up) {
+        b[k++] = {up, 2 * n, 16, false};
+        b[k++] = {up_codes, n / 2, 16, true};
+        b[k++] = {up_block_scales, n / 16, 1, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_scoped(gate, up, n_experts, rows, cols, gate_codes,
+                                             gate_block_scales, up_codes, up_block_scales,
+                                             scope_scales, (hipStream_t)stream));
+}
+
+int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
+                        const float *fp32_scales, int64_t rows_per_fp32_scale, int64_t rows,
+                        int64_t cols, uint16_t *out, void *stream)
+{
+    if (fmt != MXQ_FMT_MXFP8_ROW && fmt != MXQ_FMT_MXFP8_COL && fmt != MXQ_FMT_NVFP4)
+        return MXQ_ERR_ARG;
+    if (!codes || !scales || !out || (fmt == MXQ_FMT_NVFP4 && !fp32_scales))
+        return MXQ_ERR_NULL;
+    if (!size_ok(rows, cols) || (fmt == MXQ_FMT_NVFP4 && rows_per_fp32_scale < 1))
+        return MXQ_ERR_SIZE;
+    const int64_t n = rows * cols;
+    if (fmt == MXQ_FMT_NVFP4) {
+        if (cols % 16 != 0)
+            return MXQ_ERR_SHAPE;
+        const int64_t n_scales = (rows + rows_per_fp32_scale - 1) / rows_per_fp32_scale;
+        const Buf b[4] = {{codes, n / 2, 8, false},
+                          {scales, n / 16, 1, false},
+                          {fp32_scales, 4 * n_scales, 4, false},
+                          {out, 2 * n, 16, true}};
+        const int st = check_bufs(b, 4);
+        if (st != MXQ_OK)
+            return st;
+        return launched(mxq::launch_dequant_nvfp4(codes, scales, fp32_scales, rows_per_fp32_scale,
+                                                  rows, cols, out, (hipStream_t)stream));
+    }
+    const bool col = fmt == MXQ_FMT_MXFP8_COL;
+    if (cols % 32 != 0 || (col && rows % 32 != 0))
+        return MXQ_ERR_SHAPE;
+    const Buf b[3] = {{codes, n, 16, false}, {scales, n / 32, col ? 16 : 1, false},
+                      {out, 2 * n, 16, true}};
+    const int st = check_bufs(b, 3);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_dequant_mxfp8(col, codes, scales, rows, cols, out,
+                                              (hipStream_t)stream));
+}
+
+int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t cols,
+                         const int64_t *seg_offsets, int64_t n_groups, const mxq_grouped_out *out,
+                         void *stream)
+{
+    if (fmt != MXQ_FMT_MXFP8_ROWCOL && fmt != MXQ_FMT_NVFP4)
+        return MXQ_ERR_ARG;
+    if (!x || !seg_offsets || !out)
+        return MXQ_ERR_NULL;
+    if (!size_ok(total_rows, cols) || n_groups < 1 || n_groups > MAX_ELEMS / 8)
+        return MXQ_ERR_SIZE;
+    const int64_t n = total_rows * cols;
+    if (fmt == MXQ_FMT_NVFP4) {
+        if (!out->codes || !out->block_scales || !out->token_scales)
+            return MXQ_ERR_NULL;
+        if (cols % 16 != 0)
+            return MXQ_ERR_SHAPE;
+        const Buf b[5] = {{x, 2 * n, 16, false},
+                          {seg_offsets, 8 * (n_groups + 1), 8, false},
+                          {out->codes, n / 2, 16, true},
+                          {out->block_scales, n / 16, 1, true},
+                          {out->token_scales, 4 * total_rows, 4, true}};
+        const int st = check_bufs(b, 5);
+        if (st != MXQ_OK)
+            return st;
+        // Per-token outputs do not depend on the segments.
+        return launched(mxq::launch_nvfp4_per_token(x, total_rows, cols, out->codes,
+                                                    out->block_scales, out->token_scales,
+                                                    (hipStream_t)stream));
+    }
+    uint8_t *rc = out->row_codes, *rs = out->row_scales, *cc = out->col_codes,
+            *cs = out->col_scales;
+    int64_t *P = out->col_scale_offsets;
+    if ((rc == nullptr) != (rs == nullptr) || (cc == nullptr) != (cs == nullptr) ||
+        (cc != nullptr) != (P != nullptr) || (!rc && !cc))
+        return MXQ_ERR_OFFSETS;
+    if (cols % 32 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t scale_rows = total_rows / 32 + n_groups;
+    if (scale_rows > MAX_ELEMS / cols)
+        return MXQ_ERR_SIZE;
+    Buf b[7];
+    int k = 0;
+    b[k++] = {x, 2 * n, 16, false};
+    b[k++] = {seg_offsets, 8 * (n_groups + 1), 8, false};
+    if (rc) {
+        b[k++] = {rc, n, 16, true};
+        b[k++] = {rs, n / 32, 1, true};
+    }
+    if (cc) {
+        b[k++] = {cc, n, 16, true};
+        b[k++] = {cs, scale_rows * cols, 8, true};
+        b[k++] = {P, 8 * (n_groups + 1), 8, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    if (!cc) {
+        // Rowwise only: identical to the dense call over all rows.
+        return launched(mxq::launch_mxfp8_dense(x, total_rows, cols, rc, rs, nullptr, nullptr,
+                                                (hipStream_t)stream));
+    }
+    return launched(mxq::launch_mxfp8_grouped(x, total_rows, cols, seg_offsets, n_groups, rc, rs,
+                                              cc, cs, P, (hipStream_t)stream));
+}
+
+}  // extern "C"

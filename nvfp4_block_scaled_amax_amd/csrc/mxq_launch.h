@@ -1,0 +1,37 @@
+// mxq_launch.h -- internal launchers behind the C ABI (mxq_api.cpp).  Each
+// launcher enqueues on `stream` and returns the launch status; arguments have
+// been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,
+                              uint8_t *row_scales, uint8_t *col_codes, uint8_t *col_scales,
+                              hipStream_t stream);
+
+// Writes P (col_scale_offsets) and quantizes; at most `max_tiles` column
+// blocks (the capacity of col_scales) are written whatever the offsets say.
+hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                const int64_t *seg_offsets, int64_t n_groups, uint8_t *row_codes,
+                                uint8_t *row_scales, uint8_t *col_codes, uint8_t *col_scales,
+                                int64_t *col_scale_offsets, hipStream_t stream);
+
+hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                                  uint8_t *block_scales, float *token_scales, hipStream_t stream);
+
+hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
+                               int64_t rows, int64_t cols, uint8_t *gate_codes,
+                               uint8_t *gate_block_scales, uint8_t *up_codes,
+                               uint8_t *up_block_scales, float *scope_scales, hipStream_t stream);
+
+hipError_t launch_dequant_mxfp8(bool col, const uint8_t *codes, const uint8_t *scales,
+                                int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream);
+
+hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *block_scales,
+                                const float *fp32_scales, int64_t rows_per_scale, int64_t rows,
+                                int64_t cols, uint16_t *out, hipStream_t stream);
+
+}  // namespace mxq

@@ -1,0 +1,101 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/mxq.h declares, and its host-side validation rejects bad arguments
+before any device call.  No kernel runs here."""
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_amax_amd as mxq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "mxq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_builds_and_loads():
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.skip("libmxq.so not built")
+    L = mxq.lib()
+    assert L is not None
+
+
+def test_exports_every_declared_symbol():
+    L = mxq.lib()
+    decl = declared_functions()
+    assert set(decl) == set(mxq.EXPORTS), decl
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define MXQ_VERSION (\d+)", text).group(1))
+    assert mxq.mxq_version() == v
+    msgs = [mxq.mxq_status_string(s) for s in range(10)]
+    assert len(set(msgs)) == 10
+    assert mxq.mxq_status_string(12345) == "unknown status"
+
+
+A = 1 << 20          # a fake 16-byte-aligned address; never dereferenced
+
+
+def status_of(fn, *args):
+    with pytest.raises(mxq.MXQError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def test_validation_before_any_device_call():
+    q = mxq.mxq_mxfp8_quantize_rowcol
+    assert status_of(q, None, 32, 32, A, A, A, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(q, A, 32, 32, A, None, A, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(q, A, 32, 32, None, None, None, None, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(q, A, 0, 32, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(q, A, -32, 32, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(q, A, 1 << 40, 1 << 40, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(q, A, 32, 48, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(q, A, 48, 32, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE      # colwise needs rows % 32
+    assert status_of(q, A + 2, 32, 32, A, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(q, A, 32, 32, A + 8, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+
+    n = mxq.mxq_nvfp4_quantize_per_token
+    assert status_of(n, A, 4, 16, A, A, None, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(n, A, 4, 24, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(n, A, 4, 16, A, A, A + 2, 0) == mxq.MXQ_ERR_ALIGN
+
+    p = mxq.mxq_nvfp4_quantize_gateup_pair
+    assert status_of(p, A, A, 2, 4, 16, A, A, None, A, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(p, A, None, 2, 4, 16, A, A, A, None, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(p, A, A, 0, 4, 16, A, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(p, A, A, 2, 4, 8, A, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+
+    d = mxq.mxq_dequantize_bf16
+    assert status_of(d, 0, A, A, None, 0, 32, 32, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(d, mxq.MXQ_FMT_NVFP4, A, A, None, 1, 32, 32, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(d, mxq.MXQ_FMT_NVFP4, A, A, A, 0, 32, 32, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(d, mxq.MXQ_FMT_MXFP8_COL, A, A, None, 0, 48, 32, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(d, mxq.MXQ_FMT_MXFP8_ROW, A, A, None, 0, 32, 16, A, 0) == mxq.MXQ_ERR_SHAPE
+
+    g = mxq.mxq_grouped_quantize
+    out8 = {"row_codes": A, "row_scales": A, "col_codes": A, "col_scales": A,
+            "col_scale_offsets": A}
+    assert status_of(g, 5, A, 64, 32, A, 2, out8, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 64, 32, A, 0, out8, 0) == mxq.MXQ_ERR_SIZE
+    bad = dict(out8, col_scale_offsets=None)
+    assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 64, 32, A, 2, bad, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(g, mxq.MXQ_FMT_NVFP4, A, 64, 32, A, 2, {"codes": A}, 0) == mxq.MXQ_ERR_NULL
+
+
+def test_fake_device_pointers_rejected_without_gpu():
+    """Well-formed arguments that are not device memory fail host-side."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("covered by the GPU error-path tests")
+    st = status_of(mxq.mxq_mxfp8_quantize_rowcol, A, 32, 32, A * 2, A * 3, A * 4, A * 5, 0)
+    assert st == mxq.MXQ_ERR_DEVICE

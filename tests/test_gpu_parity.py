@@ -1,0 +1,542 @@
+"""GPU parity: every output byte of the HIP path equals the CPU oracle's.
+
+All inputs are seeded and synthetic (nvfp4_block_scaled_amax_amd.workloads, or
+constructed here); expected values come only from the oracle.  The bar is
+bit-exact for every code, scale byte, FP32 scale and BF16 output.  Full-size
+workloads are those the benchmark times, in the same launch configuration;
+where the oracle would be slow on the whole tensor, sampled experts,
+segments or rows are compared (every sampled output in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_amax_amd as mxq
+from nvfp4_block_scaled_amax_amd import api
+from nvfp4_block_scaled_amax_amd import workloads as W
+from gpu_util import ExactBuffer, announce, assert_same, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------------------
+# MXFP8
+# ---------------------------------------------------------------------------
+
+def check_mxfp8(orc, x: np.ndarray, name: str, rowwise=True, colwise=True):
+    announce(f"mxfp8 rowcol {name} shape={x.shape} row={rowwise} col={colwise}")
+    r = api.mxfp8_quantize_rowcol(dev(x), rowwise=rowwise, colwise=colwise)
+    torch.cuda.synchronize()
+    if rowwise:
+        c, s = orc.mxfp8_rowwise(x)
+        assert_same(host(r.row_scales), s, f"{name} row_scales")
+        assert_same(host(r.row_codes), c, f"{name} row_codes")
+    if colwise:
+        c, s = orc.mxfp8_colwise(x)
+        assert_same(host(r.col_scales), s, f"{name} col_scales")
+        assert_same(host(r.col_codes), c, f"{name} col_codes")
+
+
+def test_mxfp8_config1(orc):
+    check_mxfp8(orc, W.config1(), "config1 256x512 N(0,1) seed0")
+
+
+@pytest.mark.parametrize("mode", W.MXFP8_MODES)
+def test_mxfp8_config2_activation(orc, mode):
+    check_mxfp8(orc, W.config2_activation(mode), f"config2 act 2048x2048 {mode}")
+
+
+@pytest.mark.parametrize("mode", W.MXFP8_MODES)
+def test_mxfp8_config2_weight(orc, mode):
+    check_mxfp8(orc, W.config2_weight(mode), f"config2 weight 8192x2048 {mode}")
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 32), (32, 64), (64, 96), (96, 288), (32, 2080),
+                                       (160, 544), (32, 4128)])
+def test_mxfp8_shapes(orc, rows, cols):
+    """Column counts that leave partial wavefront and workgroup tiles."""
+    x = W.mode_random(rows, cols, rows * 7 + cols)
+    check_mxfp8(orc, x, f"random {rows}x{cols}")
+    xb = W.mode_boundary(rows, cols, rows + cols)
+    check_mxfp8(orc, xb, f"boundary {rows}x{cols}")
+
+
+def test_mxfp8_rowwise_only_and_ragged_rows(orc):
+    x = W.mode_boundary(96, 256, 3)[:77]
+    check_mxfp8(orc, x, "rowwise 77x256", rowwise=True, colwise=False)
+    check_mxfp8(orc, W.mode_random(64, 128, 4), "colwise-only 64x128", rowwise=False,
+                colwise=True)
+
+
+def _mxfp8_exhaustive_input():
+    """Rows of 32: for every scale exponent e in [-127, 120], blocks led by the
+    amax 448 * 2^e (BF16 max for e = 120) followed by every finite BF16 x with
+    |x| <= that amax, 31 per block."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allb[(allb & 0x7F80) != 0x7F80]
+    mag = W.bf16_to_f64(fin & 0x7FFF)
+    rows = []
+    for e in range(-127, 121):
+        amax = 448.0 * 2.0 ** e
+        abits = W.bf16_bits(np.array([amax]))[0] if e < 120 else np.uint16(0x7F7F)
+        A = W.bf16_to_f64(np.array([abits], np.uint16))[0]
+        xs = fin[mag <= A]
+        n = -(-xs.size // 31)
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:xs.size] = xs
+        blk = np.empty((n, 32), np.uint16)
+        blk[:, 0] = abits
+        blk[:, 1:] = pad.reshape(n, 31)
+        rows.append(blk)
+    X = np.concatenate(rows)
+    extra = (-X.shape[0]) % 32
+    return np.concatenate([X, np.zeros((extra, 32), np.uint16)])
+
+
+def test_mxfp8_exhaustive_code_map(orc):
+    """Every finite BF16 value under every E8M0 scale its block can have, through
+    both the rowwise and (transposed) columnwise kernels."""
+    X = _mxfp8_exhaustive_input()
+    check_mxfp8(orc, X, "exhaustive rows", rowwise=True, colwise=True)
+    XT = np.ascontiguousarray(X.T)
+    check_mxfp8(orc, XT, "exhaustive transposed", rowwise=True, colwise=True)
+
+
+def test_mxfp8_deterministic():
+    x = dev(W.config2_weight("random"))
+    announce("mxfp8 determinism 8192x2048")
+    a = api.mxfp8_quantize_rowcol(x)
+    b = api.mxfp8_quantize_rowcol(x)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 per token
+# ---------------------------------------------------------------------------
+
+def check_nvfp4(orc, x: np.ndarray, name: str):
+    announce(f"nvfp4 per-token {name} shape={x.shape}")
+    r = api.nvfp4_quantize_per_token(dev(x))
+    torch.cuda.synchronize()
+    c, b, s = orc.nvfp4_per_token(x)
+    assert_same(host(r.fp32_scales).view(np.uint32), s.view(np.uint32), f"{name} token_scales")
+    assert_same(host(r.block_scales), b, f"{name} block_scales")
+    assert_same(host(r.codes), c, f"{name} codes")
+    return r
+
+
+def test_nvfp4_config3(orc):
+    check_nvfp4(orc, W.config3(), "config3 8192x2048 t3")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (5, 48), (4, 512), (7, 768), (9, 1040),
+                                       (6, 2048), (3, 2064), (4, 4096), (2, 4112), (2, 8192)])
+def test_nvfp4_shapes(orc, rows, cols):
+    """Row lengths for every register-resident chunk count, partial chunks, and
+    the generic (re-reading) path above 4096."""
+    check_nvfp4(orc, W.student_t_activations(rows, cols, rows + cols), f"t3 {rows}x{cols}")
+    check_nvfp4(orc, W.nvfp4_boundary(rows, cols, cols), f"boundary {rows}x{cols}")
+
+
+def test_nvfp4_boundary_rows(orc):
+    check_nvfp4(orc, W.nvfp4_boundary(64, 2048, 17), "boundary 64x2048")
+    check_nvfp4(orc, W.nvfp4_boundary(64, 64, 18), "boundary 64x64")
+
+
+def _tie_sweep():
+    """Rows whose FP32 scale is an exact power of two (amax 21 * 2^j), blocks
+    whose scale is each E4M3 value d in turn (block amax 6 d s), and elements at
+    every E2M1 midpoint and value times d s, with their BF16 neighbours: exact
+    and near ties of both rounding steps."""
+    e4 = [(c & 7) * 2.0 ** -9 if (c >> 3) == 0 else (8 + (c & 7)) * 2.0 ** ((c >> 3) - 10)
+          for c in range(1, 127)]
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rows = []
+    rng = np.random.default_rng(44)
+    for j in (-60, -9, 0, 7, 40, 100):
+        s = 2.0 ** (j - 7)
+        At = 21.0 * 2.0 ** j
+        blocks = []
+        for d in e4:
+            q = np.array(mids + vals) * d * s
+            qb = W.bf16_bits(q)
+            cand = np.concatenate([qb, qb + 1, qb - 1]).astype(np.uint16)
+            cand = cand[(cand & 0x7FFF) < 0x7F80]
+            Ab = W.bf16_bits(np.array([6.0 * d * s]))[0]
+            cand = cand[W.bf16_to_f64(cand) <= W.bf16_to_f64(np.array([Ab], np.uint16))[0]]
+            signs = (rng.integers(0, 2, cand.size).astype(np.uint16) << 15)
+            cand = cand | signs
+            for k in range(0, cand.size, 15):
+                blk = np.zeros(16, np.uint16)
+                blk[0] = Ab
+                part = cand[k:k + 15]
+                blk[1:1 + part.size] = part
+                blocks.append(blk)
+        flat = np.concatenate(blocks)
+        K = 2048
+        n_rows = -(-flat.size // (K - 16))
+        pad = np.zeros(n_rows * (K - 16), np.uint16)
+        pad[:flat.size] = flat
+        body = pad.reshape(n_rows, K - 16)
+        head = np.zeros((n_rows, 16), np.uint16)
+        head[:, 0] = W.bf16_bits(np.array([At]))[0]
+        rows.append(np.concatenate([head, body], axis=1))
+    return np.concatenate(rows)
+
+
+def test_nvfp4_tie_sweep(orc):
+    check_nvfp4(orc, _tie_sweep(), "tie sweep")
+
+
+def _wide_range_rows(n_rows: int, cols: int, seed: int):
+    """Rows whose amax spans the whole BF16 range (log-uniform exponent, with a
+    band around 2^-90, where the kernel changes arithmetic paths) and whose
+    blocks sit 0..40 binades below the row amax; zero blocks included."""
+    rng = np.random.default_rng(seed)
+    X = np.empty((n_rows, cols), np.uint16)
+    for r in range(n_rows):
+        if r % 3 == 0:
+            ea = rng.uniform(-95, -85)
+        else:
+            ea = rng.uniform(-132, 127)
+        A = 2.0 ** ea
+        v = np.empty(cols)
+        for b in range(cols // 16):
+            depth = rng.uniform(0, 40)
+            v[16 * b:16 * b + 16] = rng.uniform(-1, 1, 16) * A * 2.0 ** -depth
+        v[int(rng.integers(0, cols))] = A
+        if r % 5 == 0:
+            v[:16] = 0.0
+        bits = W.bf16_bits(np.clip(v, -3.38e38, 3.38e38))
+        X[r] = bits
+    return X
+
+
+def test_nvfp4_wide_range(orc):
+    check_nvfp4(orc, _wide_range_rows(300, 256, 5), "wide range 300x256")
+    check_nvfp4(orc, _wide_range_rows(40, 2048, 6), "wide range 40x2048")
+
+
+def test_nvfp4_batch_invariance():
+    """Per-token outputs of a row do not depend on the other rows of the batch."""
+    x = W.config3()[:512]
+    announce("nvfp4 batch invariance")
+    full = api.nvfp4_quantize_per_token(dev(x))
+    perm = np.random.default_rng(3).permutation(512)
+    part = api.nvfp4_quantize_per_token(dev(np.ascontiguousarray(x[perm])))
+    torch.cuda.synchronize()
+    p = torch.from_numpy(perm).cuda()
+    for a, b in zip(full, part):
+        assert torch.equal(a[p], b)
+
+
+# ---------------------------------------------------------------------------
+# Scoped NVFP4 (gate/up pairs, down)
+# ---------------------------------------------------------------------------
+
+def check_pair(orc, gate, up, name, experts=None):
+    announce(f"nvfp4 gateup {name} gate={gate.shape} up={None if up is None else up.shape}")
+    r = api.nvfp4_quantize_gateup_pair(dev(gate), None if up is None else dev(up))
+    torch.cuda.synchronize()
+    sc = host(r.scope_scales)
+    E = gate.shape[0]
+    experts = range(E) if experts is None else experts
+    for e in experts:
+        gc, gb, uc, ub, s = orc.nvfp4_gateup_pair(gate[e:e + 1], None if up is None else up[e:e + 1])
+        assert_same(sc[e:e + 1].view(np.uint32), s.view(np.uint32), f"{name} e{e} scale")
+        assert_same(host(r.gate_block_scales[e]), gb[0], f"{name} e{e} gate bs")
+        assert_same(host(r.gate_codes[e]), gc[0], f"{name} e{e} gate codes")
+        if up is not None:
+            assert_same(host(r.up_block_scales[e]), ub[0], f"{name} e{e} up bs")
+            assert_same(host(r.up_codes[e]), uc[0], f"{name} e{e} up codes")
+
+
+def test_gateup_small(orc):
+    rng = np.random.default_rng(9)
+    g = W.bf16_bits(rng.normal(0, 0.02, (3, 48, 64)))
+    u = W.bf16_bits(rng.normal(0, 0.05, (3, 48, 64)))
+    check_pair(orc, g, u, "small pair")
+    check_pair(orc, g, None, "small single")
+    z = np.zeros((2, 16, 32), np.uint16)
+    check_pair(orc, z, z.copy(), "zeros pair")
+    wide = _wide_range_rows(64, 256, 7).reshape(4, 16, 256)
+    check_pair(orc, wide, None, "wide single")
+
+
+def test_gateup_config4_full(orc):
+    """The expert-weight export at full size (128 experts; gate/up 768x2048 with
+    a shared scale per pair, down 2048x768 alone), checked on sampled experts."""
+    gate, up, down = W.config4()
+    sample = [0, 1, 63, 127]
+    check_pair(orc, gate, up, "config4 gate/up", experts=sample)
+    check_pair(orc, down, None, "config4 down", experts=sample)
+
+
+# ---------------------------------------------------------------------------
+# Dequant
+# ---------------------------------------------------------------------------
+
+def test_dequant_mxfp8(orc):
+    for name, x in [("config1", W.config1()), ("boundary", W.mode_boundary(256, 512, 3)),
+                    ("maxes", W.mode_maxes(64, 64)), ("zeros", W.mode_zeros(32, 64))]:
+        rc, rs = orc.mxfp8_rowwise(x)
+        cc, cs = orc.mxfp8_colwise(x)
+        announce(f"dequant mxfp8 {name}")
+        yr = api.dequantize_bf16(mxq.MXQ_FMT_MXFP8_ROW, dev(rc), dev(rs))
+        yc = api.dequantize_bf16(mxq.MXQ_FMT_MXFP8_COL, dev(cc), dev(cs))
+        torch.cuda.synchronize()
+        assert_same(host(yr), orc.dequant_mxfp8_rowwise(rc, rs), f"{name} row dequant")
+        assert_same(host(yc), orc.dequant_mxfp8_colwise(cc, cs), f"{name} col dequant")
+
+
+def test_dequant_mxfp8_random_bytes(orc):
+    """Arbitrary E4M3 codes (no NaN) under every E8M0 byte: overflow saturates,
+    underflow rounds into BF16 subnormals."""
+    rng = np.random.default_rng(31)
+    codes = rng.integers(0, 256, (512, 256)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    scales = rng.integers(0, 255, (512, 8)).astype(np.uint8)
+    announce("dequant mxfp8 random bytes")
+    y = api.dequantize_bf16(mxq.MXQ_FMT_MXFP8_ROW, dev(codes), dev(scales))
+    torch.cuda.synchronize()
+    assert_same(host(y), orc.dequant_mxfp8_rowwise(codes, scales), "random row dequant")
+    cs = rng.integers(0, 255, (16, 256)).astype(np.uint8)
+    y = api.dequantize_bf16(mxq.MXQ_FMT_MXFP8_COL, dev(codes), dev(cs))
+    torch.cuda.synchronize()
+    assert_same(host(y), orc.dequant_mxfp8_colwise(codes, cs), "random col dequant")
+
+
+def test_dequant_nvfp4(orc):
+    for name, x in [("config3", W.config3()), ("boundary", W.nvfp4_boundary(64, 2048, 2)),
+                    ("wide", _wide_range_rows(200, 256, 8)), ("ties", _tie_sweep()[:64])]:
+        c, b, s = orc.nvfp4_per_token(x)
+        announce(f"dequant nvfp4 {name} {x.shape}")
+        y = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, dev(c), dev(b), dev(s), 1)
+        torch.cuda.synchronize()
+        assert_same(host(y), orc.dequant_nvfp4(c, b, s, 1), f"{name} nvfp4 dequant")
+
+
+def test_dequant_nvfp4_random_bytes(orc):
+    """Random codes and block scales under FP32 scales across the whole range
+    (subnormal, around 2^-100, huge), per token and per group of rows."""
+    rng = np.random.default_rng(32)
+    rows, cols = 1024, 128
+    codes = rng.integers(0, 256, (rows, cols // 2)).astype(np.uint8)
+    bs = rng.integers(0, 256, (rows, cols // 16)).astype(np.uint8)
+    bs[(bs & 0x7F) == 0x7F] = 0x38
+    e = rng.integers(-149, 117, rows)
+    m = rng.integers(0, 1 << 23, rows)
+    sb = np.where(e < -126, m >> np.minimum(-126 - e, 23), ((e + 127) << 23) | m).astype(np.uint32)
+    s = sb.view(np.float32)
+    s[::7] = np.float32(2.0 ** -100)
+    announce("dequant nvfp4 random bytes")
+    y = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, dev(codes), dev(bs), dev(s), 1)
+    torch.cuda.synchronize()
+    assert_same(host(y), orc.dequant_nvfp4(codes, bs, s, 1), "random nvfp4 dequant")
+    s8 = np.ascontiguousarray(s[:rows // 8])
+    y = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, dev(codes), dev(bs), dev(s8), 8)
+    torch.cuda.synchronize()
+    assert_same(host(y), orc.dequant_nvfp4(codes, bs, s8, 8), "random nvfp4 dequant /8")
+
+
+def test_dequant_config4_round_trip(orc):
+    """Dequant of the export with one scale per expert (rows_per_fp32_scale =
+    rows of one expert), sampled experts."""
+    gate, up, down = W.config4(8)
+    announce("dequant config4 round trip (8 experts)")
+    r = api.nvfp4_quantize_gateup_pair(dev(gate), dev(up))
+    y = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, r.gate_codes, r.gate_block_scales,
+                            r.scope_scales, 768)
+    torch.cuda.synchronize()
+    gc, gb, uc, ub, sc = orc.nvfp4_gateup_pair(gate, up)
+    want = orc.dequant_nvfp4(gc.reshape(-1, 1024), gb.reshape(-1, 128), sc, 768)
+    assert_same(host(y), want, "config4 gate round trip")
+
+
+# ---------------------------------------------------------------------------
+# Grouped
+# ---------------------------------------------------------------------------
+
+def check_grouped(orc, x, off, name, seg_sample=None, row_sample=None):
+    announce(f"grouped {name} R={x.shape[0]} G={off.size - 1}")
+    xd = dev(x)
+    od = dev(off)
+    g8 = api.grouped_quantize_mxfp8(xd, od)
+    g4 = api.grouped_quantize_nvfp4(xd, od)
+    torch.cuda.synchronize()
+    G = off.size - 1
+    P = host(g8.col_scale_offsets)
+    counts = [(int(off[e + 1]) - int(off[e]) + 31) // 32 for e in range(G)]
+    assert list(P) == list(np.concatenate([[0], np.cumsum(counts)]))
+    segs = range(G) if seg_sample is None else seg_sample
+    rc, rs = host(g8.row_codes), host(g8.row_scales)
+    cc, cs = host(g8.col_codes), host(g8.col_scales)
+    c4, b4, s4 = host(g4.codes), host(g4.block_scales), host(g4.fp32_scales)
+    for e in segs:
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        seg = x[a:b]
+        sub_off = np.array([0, b - a], np.int64)
+        oc, os_, _ = orc.mxfp8_colwise_grouped(seg, sub_off)
+        assert_same(cc[a:b], oc, f"{name} seg{e} col codes")
+        assert_same(cs[P[e]:P[e + 1]], os_, f"{name} seg{e} col scales")
+        orow, orows = orc.mxfp8_rowwise(seg)
+        assert_same(rc[a:b], orow, f"{name} seg{e} row codes")
+        assert_same(rs[a:b], orows, f"{name} seg{e} row scales")
+        nc, nb, ns = orc.nvfp4_per_token(seg)
+        assert_same(c4[a:b], nc, f"{name} seg{e} nvfp4 codes")
+        assert_same(b4[a:b], nb, f"{name} seg{e} nvfp4 bs")
+        assert_same(s4[a:b].view(np.uint32), ns.view(np.uint32), f"{name} seg{e} nvfp4 s")
+    return g8, g4
+
+
+def test_grouped_ragged_stress(orc):
+    """Segments of 0, 1, 31, 32, 33 and 4096 rows among random ones."""
+    off = W.ragged_offsets(16384, 24, seed=7)
+    x = W.student_t_activations(int(off[-1]), 256, 70)
+    check_grouped(orc, x, off, "ragged stress")
+
+
+def test_grouped_small_edge(orc):
+    off = np.array([0, 0, 1, 1, 33, 65, 65, 96, 97], np.int64)
+    x = W.mode_boundary(128, 64, 3)[:97]
+    check_grouped(orc, x, off, "edge segments")
+    off1 = np.array([0, 5], np.int64)
+    check_grouped(orc, W.mode_random(32, 32, 1)[:5], off1, "one short segment")
+
+
+def test_grouped_config5_full(orc):
+    """The grouped workload at full size (262,144 expert-sorted rows of 2048,
+    128 uniform top-8 segments), sampled segments, plus the dequant of both
+    formats on the same sample."""
+    x, off = W.config5()
+    g8, g4 = check_grouped(orc, x, off, "config5", seg_sample=[0, 1, 64, 127])
+    announce("grouped config5 dequant")
+    y8 = api.dequantize_bf16(mxq.MXQ_FMT_MXFP8_ROW, g8.row_codes, g8.row_scales)
+    y4 = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, g4.codes, g4.block_scales, g4.fp32_scales, 1)
+    torch.cuda.synchronize()
+    for e in (0, 127):
+        a, b = int(off[e]), int(off[e + 1])
+        rc, rs = orc.mxfp8_rowwise(x[a:b])
+        assert_same(host(y8[a:b]), orc.dequant_mxfp8_rowwise(rc, rs), f"config5 seg{e} mx deq")
+        c, bb, s = orc.nvfp4_per_token(x[a:b])
+        assert_same(host(y4[a:b]), orc.dequant_nvfp4(c, bb, s, 1), f"config5 seg{e} nv deq")
+
+
+# ---------------------------------------------------------------------------
+# Error paths: nothing launched, nothing written
+# ---------------------------------------------------------------------------
+
+def test_errors_leave_outputs_untouched():
+    x = dev(W.config1())
+    rows, cols = 256, 512
+    rc = torch.full((rows, cols), 0xA5, dtype=torch.uint8, device="cuda")
+    rs = torch.full((rows, cols // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    cc = torch.full((rows, cols), 0xA5, dtype=torch.uint8, device="cuda")
+    cs = torch.full((rows // 32, cols), 0xA5, dtype=torch.uint8, device="cuda")
+    host_buf = np.zeros((rows, cols), np.uint8)
+    announce("error paths")
+    cases = [
+        (mxq.MXQ_ERR_ALIGN, (x.data_ptr() + 2, rows, cols, rc, rs, cc, cs)),
+        (mxq.MXQ_ERR_DEVICE, (x, rows, cols, host_buf.ctypes.data, rs, cc, cs)),
+        (mxq.MXQ_ERR_ALIAS, (x, rows, cols, rc, rs, rc, cs)),
+        (mxq.MXQ_ERR_ALIAS, (x, rows, cols, x.data_ptr(), rs, cc, cs)),
+        (mxq.MXQ_ERR_SHAPE, (x, rows, cols - 16, rc, rs, cc, cs)),
+        (mxq.MXQ_ERR_OFFSETS, (x, rows, cols, rc, None, cc, cs)),
+        (mxq.MXQ_ERR_NULL, (None, rows, cols, rc, rs, cc, cs)),
+    ]
+    for status, args in cases:
+        with pytest.raises(mxq.MXQError) as ei:
+            mxq.mxq_mxfp8_quantize_rowcol(*args)
+        assert ei.value.status == status, (status, ei.value)
+    torch.cuda.synchronize()
+    for t in (rc, rs, cc, cs):
+        assert bool((t == 0xA5).all())
+    # A valid call afterwards works and writes.
+    mxq.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs)
+    torch.cuda.synchronize()
+    assert not bool((rs == 0xA5).all())
+
+
+def test_errors_buffer_too_small():
+    """An array that ends before the call's extent is rejected when the array is
+    its own allocation (hipMalloc).  Inside a caching-allocator segment only the
+    segment's end is known, so the check guards the allocation, not the tensor."""
+    rows, cols = 8192, 512
+    need = rows * cols
+    x = ExactBuffer(2 * need)
+    small = ExactBuffer(need // 2)                 # row codes need `need` bytes
+    full = [ExactBuffer(need), ExactBuffer(need // 32), ExactBuffer(need), ExactBuffer(need // 32)]
+    try:
+        if not (x.exact and small.exact and all(b.exact for b in full)):
+            pytest.skip("runtime does not report exact allocation extents")
+        announce("error paths: too-small buffers")
+        rc, rs, cc, cs = (b.ptr for b in full)
+        for args in [(x.ptr, rows, cols, small.ptr, rs, cc, cs),
+                     (x.ptr, rows * 2, cols, rc, rs, cc, cs)]:
+            with pytest.raises(mxq.MXQError) as ei:
+                mxq.mxq_mxfp8_quantize_rowcol(*args)
+            assert ei.value.status == mxq.MXQ_ERR_DEVICE
+        torch.cuda.synchronize()
+    finally:
+        for b in [x, small] + full:
+            b.free()
+
+
+def test_errors_other_entry_points():
+    """Rejected before launch: outputs overlapping the input, unknown formats,
+    empty group lists.  (Too-small arrays: test_errors_buffer_too_small.)"""
+    x = dev(W.config1())
+    codes = torch.empty((256, 256), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((256, 32), dtype=torch.uint8, device="cuda")
+    ts = torch.empty((256,), dtype=torch.float32, device="cuda")
+    announce("error paths nvfp4/dequant/grouped")
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.mxq_nvfp4_quantize_per_token(x, 256, 512, x.data_ptr() + 4096, bs, ts)
+    assert ei.value.status == mxq.MXQ_ERR_ALIAS
+    out = torch.empty((256, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.mxq_dequantize_bf16(7, codes, bs, None, 1, 256, 512, out)
+    assert ei.value.status == mxq.MXQ_ERR_ARG
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.mxq_grouped_quantize(mxq.MXQ_FMT_NVFP4, x, 256, 512,
+                                 torch.zeros(3, dtype=torch.int64, device="cuda"), 0,
+                                 {"codes": codes, "block_scales": bs, "token_scales": ts})
+    assert ei.value.status == mxq.MXQ_ERR_SIZE
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.mxq_nvfp4_quantize_gateup_pair(x, x, 2, 128, 512, codes, bs, codes, bs, ts)
+    assert ei.value.status == mxq.MXQ_ERR_ALIAS
+
+
+def test_grouped_malformed_offsets_stay_in_bounds():
+    """Offsets are device data the host cannot validate: non-monotone or
+    out-of-range offsets must not move any access out of bounds (the call
+    completes; its bytes are meaningless).  Outputs are bracketed by canaries."""
+    R, cols, G = 64, 64, 3
+    x = dev(W.mode_random(R, cols, 5))
+    off = torch.tensor([0, 1000, -5, 64], dtype=torch.int64, device="cuda")
+    guard = 4096
+    big = torch.full((R * cols + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    cs_big = torch.full(((R // 32 + G) * cols + 2 * guard,), 0x5A, dtype=torch.uint8,
+                        device="cuda")
+    rc = big[guard:guard + R * cols]
+    cc = torch.empty(R * cols, dtype=torch.uint8, device="cuda")
+    rs = torch.empty(R * cols // 32, dtype=torch.uint8, device="cuda")
+    cs = cs_big[guard:guard + (R // 32 + G) * cols]
+    P = torch.empty(G + 1, dtype=torch.int64, device="cuda")
+    announce("grouped malformed offsets")
+    mxq.mxq_grouped_quantize(mxq.MXQ_FMT_MXFP8_ROWCOL, x, R, cols, off, G,
+                             {"row_codes": rc, "row_scales": rs, "col_codes": cc,
+                              "col_scales": cs, "col_scale_offsets": P})
+    torch.cuda.synchronize()
+    assert bool((big[:guard] == 0x5A).all()) and bool((big[-guard:] == 0x5A).all())
+    assert bool((cs_big[:guard] == 0x5A).all()) and bool((cs_big[-guard:] == 0x5A).all())
