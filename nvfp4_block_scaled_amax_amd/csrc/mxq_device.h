@@ -52,6 +52,13 @@ __device__ __forceinline__ uint32_t hmax_u16(uint32_t a)
     return lo > hi ? lo : hi;
 }
 
+// Index of this wavefront within its workgroup, as a wave-uniform value (so
+// that everything derived from it lives in scalar registers).
+__device__ __forceinline__ int wave_in_group()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane exchanges.  DPP patterns act within rows of 16 lanes; the
 // gfx950 permlane swaps exchange rows (16-lane) and halves (32-lane).

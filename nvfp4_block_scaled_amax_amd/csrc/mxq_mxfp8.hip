@@ -2,172 +2,190 @@
 // read of X (the MXFP8 format and MXFP8 recipe paragraphs of the page
 // "Miles: end-to-end MXFP8 and per-token NVFP4 RL on Blackwell").
 //
-// Tiling.  A wavefront owns a tile of 32 rows x 64 columns (4 KB of BF16).
-// Lane l holds column group g = l & 7 (8 consecutive columns, one 16-byte
-// load per row) of rows 4 * (l >> 3) .. +3, so every load instruction reads
-// eight 128-byte row segments.  Both reductions stay inside the wavefront:
-//   rowwise 1x32 block = 4 lanes (g & 3): in-lane max over 8 values, then two
-//     DPP exchanges (lane ^ 1, lane ^ 2);
-//   columnwise 32x1 block = 8 lanes (l >> 3): in-lane max over 4 rows (packed
-//     16-bit max), then lane ^ 8 (DPP row_ror:8), ^ 16 and ^ 32 (gfx950
-//     permlane swaps).
-// No LDS and no barrier.  Magnitudes are compared as integers (|x| =
-// bits & 0x7FFF orders like the value).  Rowwise codes come from one
-// v_cvt_scalef32_pk_fp8_bf16 per pair of elements; columnwise codes pair
-// rows r and r+1 of one column (which share a scale), convert, and are
-// regrouped into row order with byte permutes.
+// Tiling.  A wavefront tile is 32 rows x 128 columns (8 KB of BF16).  Lane l
+// holds column group g = l & 15 (8 consecutive columns, one 16-byte load per
+// row) of the 8 rows 8 * (l >> 4) .. +7, so each load or code store
+// instruction covers four 256-byte (or 128-byte) row segments.  Both
+// reductions stay inside the wavefront:
+//   rowwise 1x32 block = the 4 lanes of a quad: in-lane max over 8 values,
+//     then DPP exchanges with lane ^ 1 and lane ^ 2;
+//   columnwise 32x1 block = the 4 lanes l, l^16, l^32, l^48: packed 16-bit
+//     max over the lane's 8 rows, then the gfx950 permlane16/permlane32 swaps.
+// No LDS, no barrier.  Magnitudes are compared as integers (|x| = bits &
+// 0x7FFF orders like the value).
 //
-// Grouped variant: tiles are 32-row blocks of ragged segments; a segment's
-// last tile may be short (missing rows read as 0, are not written), which
-// gives the amax over existing rows.  The tile -> (segment, block) map is a
-// binary search in the prefix array P that a one-workgroup kernel writes
-// first.
+// Scale.  For a block amax a (15-bit magnitude bits = 128 E + m), the
+// smallest unclipped exponent byte is max(0, E - 8 + [m > 96]) =
+// max(0, a - 993) >> 7 (993 = 8 * 128 - 31); shifted left by 16 instead it is
+// the byte in an f32 exponent field, which is the scale operand of the
+// conversions (they use only the exponent field).
+//
+// Codes.  Rowwise: one v_cvt_scalef32_pk_fp8_bf16 per element pair.
+// Columnwise: rows 2p and 2p+1 of one column share a scale, so they are
+// paired with a byte permute, converted, and regrouped into row order.
+//
+// Schedule.  A persistent grid: each wavefront owns one 128-column strip and
+// a contiguous range of 32-row tiles down it, and loads the next tile while
+// it converts the current one.  For ragged segments (grouped call) the tile
+// range is in "segment tile" space: tile T lies in the segment e with
+// P[e] <= T < P[e+1], found by a forward scan that advances about once per
+// segment.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
 namespace mxq {
 
 constexpr int TILE_ROWS = 32;
-constexpr int WAVE_COLS = 64;
+constexpr int TILE_COLS = 128;                  // per wavefront
 constexpr int WAVES_PER_WG = 4;
-constexpr int WG_COLS = WAVE_COLS * WAVES_PER_WG;   // 256 columns per workgroup
 
-// Byte permute: result byte i = selected byte of {hi:lo}, selector byte i in
-// 0..7 (0-3 from lo, 4-7 from hi).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-struct TileRows {
-    int64_t row0;        // first row of the tile
-    int nrows;           // rows present (1..32)
-    int64_t scale_row;   // row of col_scales for this tile
+// Saturating subtraction (v_sub_u32 / v_pk_sub_u16 with clamp).
+__device__ __forceinline__ uint32_t subsat(uint32_t a, uint32_t b)
+{
+    return __builtin_elementwise_sub_sat(a, b);
+}
+__device__ __forceinline__ uint32_t pk_subsat(uint32_t a, uint32_t b)
+{
+    ushort2_t r = __builtin_elementwise_sub_sat(__builtin_bit_cast(ushort2_t, a),
+                                                __builtin_bit_cast(ushort2_t, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pk_shr7(uint32_t a)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(ushort2_t, a) >> (unsigned short)7);
+}
+
+// Two BF16 (packed) over 2^(b-127) -> two E4M3 codes written into the low
+// (HI = false) or high (HI = true) 16 bits of `old`.  `scale` carries b in
+// its exponent field.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t old, uint32_t bf16pair, uint32_t scale)
+{
+    short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+        __builtin_bit_cast(short2_t, old), __builtin_bit_cast(bf16x2_t, bf16pair), u2f(scale), HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+struct Tile {
+    int64_t row0;      // first row
+    int nrows;         // rows present, 1..32
+    int64_t srow;      // row of col_scales
 };
 
-template <bool ROW, bool COL>
-__device__ __forceinline__ void mxfp8_tile(const uint16_t *__restrict__ x, int64_t cols,
-                                           TileRows t, int64_t col_base,
-                                           uint8_t *__restrict__ row_codes,
-                                           uint8_t *__restrict__ row_scales,
-                                           uint8_t *__restrict__ col_codes,
-                                           uint8_t *__restrict__ col_scales)
+template <bool FULL>
+__device__ __forceinline__ void load_tile(uint32_t (&v)[8][4], const uint16_t *__restrict__ x,
+                                          int64_t cols, int64_t col0, const Tile &t, int rg,
+                                          bool col_ok)
 {
-    const int lane = __lane_id();
-    const int g = lane & 7;
-    const int rg = lane >> 3;
-    const int64_t col0 = col_base + 8 * g;
-    const bool col_ok = col0 < cols;     // cols % 32 == 0: a 32-column block is all in or all out
-    // Element offset of this lane's first row; row i adds i * cols.
-    const int64_t base = (t.row0 + 4 * rg) * cols + col0;
-    const int nr = t.nrows - 4 * rg;     // rows of this lane present: r < nr
-
-    uint32_t v[4][4];
+    const uint16_t *p = x + (t.row0 + 8 * rg) * cols + col0;
+    const int nr = t.nrows - 8 * rg;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (col_ok && i < nr) {
-            uint4 q = ld_nt16(x + base + i * cols);
+    for (int i = 0; i < 8; i++) {
+        if (FULL || (col_ok && i < nr)) {
+            const uint4 q = ld_nt16(p + i * cols);
             v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
         } else {
             v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0u;
         }
     }
+}
+
+template <bool ROW, bool COL, bool FULL>
+__device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], int64_t cols, int64_t col0,
+                                             const Tile &t, int g, int rg, bool col_ok,
+                                             uint8_t *__restrict__ row_codes,
+                                             uint8_t *__restrict__ row_scales,
+                                             uint8_t *__restrict__ col_codes,
+                                             uint8_t *__restrict__ col_scales)
+{
+    const int64_t base = (t.row0 + 8 * rg) * cols + col0;
+    const int nr = t.nrows - 8 * rg;
+    uint32_t a[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            a[i][j] = v[i][j] & 0x7FFF7FFFu;
 
     if constexpr (ROW) {
         const int64_t nb = cols >> 5;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint32_t m = pk_max_u16(pk_max_u16(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
-                                    pk_max_u16(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu));
-            uint32_t a = hmax_u16(m);
-            a = max(a, dpp<DPP_XOR1>(a));
-            a = max(a, dpp<DPP_XOR2>(a));
-            const uint32_t b = e8m0_byte(a);
-            const uint32_t c01 = mx_e4m3_pair(v[i][0], b) | (mx_e4m3_pair(v[i][1], b) << 16);
-            const uint32_t c23 = mx_e4m3_pair(v[i][2], b) | (mx_e4m3_pair(v[i][3], b) << 16);
-            if (col_ok && i < nr) {
-                st_nt8(row_codes + base + i * cols, c01, c23);
+        for (int i = 0; i < 8; i++) {
+            const uint32_t m = pk_max_u16(pk_max_u16(a[i][0], a[i][1]), pk_max_u16(a[i][2], a[i][3]));
+            uint32_t am = hmax_u16(m);
+            am = max(am, dpp<DPP_XOR1>(am));
+            am = max(am, dpp<DPP_XOR2>(am));
+            const uint32_t sc = subsat(am, 993u) & 0xFF80u;      // byte << 7
+            const uint32_t scale = sc << 16;                     // byte << 23
+            const uint32_t w0 = cvt2<true>(cvt2<false>(0u, v[i][0], scale), v[i][1], scale);
+            const uint32_t w1 = cvt2<true>(cvt2<false>(0u, v[i][2], scale), v[i][3], scale);
+            if (FULL || (col_ok && i < nr)) {
+                st_nt8(row_codes + base + i * cols, w0, w1);
                 if ((g & 3) == 0)
-                    row_scales[(base >> 5) + i * nb] = (uint8_t)b;
+                    row_scales[(base >> 5) + i * nb] = (uint8_t)(sc >> 7);
             }
         }
     }
 
     if constexpr (COL) {
-        // Column amax over the 32 rows, two columns per dword.
-        uint32_t m[4];
+        uint32_t slo[4], shi[4], sb[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            m[j] = pk_max_u16(pk_max_u16(v[0][j] & 0x7FFF7FFFu, v[1][j] & 0x7FFF7FFFu),
-                              pk_max_u16(v[2][j] & 0x7FFF7FFFu, v[3][j] & 0x7FFF7FFFu));
-            m[j] = pk_max_u16(m[j], dpp<DPP_ROR8>(m[j]));
-            m[j] = max16_pk_u16(m[j]);
-            m[j] = max32_pk_u16(m[j]);
+            uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a[0][j], a[1][j]), pk_max_u16(a[2][j], a[3][j])),
+                                    pk_max_u16(pk_max_u16(a[4][j], a[5][j]), pk_max_u16(a[6][j], a[7][j])));
+            m = max16_pk_u16(m);
+            m = max32_pk_u16(m);
+            const uint32_t sc = pk_subsat(m, 0x03E103E1u) & 0xFF80FF80u;   // bytes << 7, per half
+            slo[j] = sc << 16;                                          // column 2j
+            shi[j] = sc & 0xFFFF0000u;                                  // column 2j+1
+            sb[j] = pk_shr7(sc);                                        // the two bytes
         }
-        // Scale bytes: column 2j in the low half, 2j+1 in the high half.
-        uint32_t sb[4];
+        // P[p][j] bytes: {col 2j: row 2p, 2p+1 | col 2j+1: row 2p, 2p+1}.
+        uint32_t P[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            sb[j] = e8m0_byte2(m[j]);
-
-        // Codes: pair rows (0,1) and (2,3) of each column, convert with the
-        // column's scale, then regroup bytes into row order.
-        // P[p][j]: bytes {col 2j: row 2p, row 2p+1 | col 2j+1: row 2p, row 2p+1}.
-        uint32_t P[2][4];
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
+        for (int p = 0; p < 4; p++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const uint32_t ra = v[2 * p][j], rb = v[2 * p + 1][j];
-                const uint32_t lo_pair = perm(rb, ra, 0x05040100u);   // {ra.lo, rb.lo}: column 2j
-                const uint32_t hi_pair = perm(rb, ra, 0x07060302u);   // {ra.hi, rb.hi}: column 2j+1
-                P[p][j] = mx_e4m3_pair(lo_pair, sb[j] & 0xFFu) |
-                          (mx_e4m3_pair(hi_pair, sb[j] >> 16) << 16);
+                P[p][j] = cvt2<true>(cvt2<false>(0u, perm(rb, ra, 0x05040100u), slo[j]),
+                                     perm(rb, ra, 0x07060302u), shi[j]);
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int p = i >> 1, k = i & 1;       // row 2p + k
-            // Row codes for columns 0..3 (from P[p][0], P[p][1]) and 4..7.
-            const uint32_t sel = k ? 0x07050301u : 0x06040200u;
+        for (int i = 0; i < 8; i++) {
+            const int p = i >> 1;
+            const uint32_t sel = (i & 1) ? 0x07050301u : 0x06040200u;
             const uint32_t w0 = perm(P[p][1], P[p][0], sel);
             const uint32_t w1 = perm(P[p][3], P[p][2], sel);
-            if (col_ok && i < nr)
+            if (FULL || (col_ok && i < nr))
                 st_nt8(col_codes + base + i * cols, w0, w1);
         }
-        if (col_ok && rg == 0) {
-            const uint32_t s0 = (sb[0] & 0xFFu) | ((sb[0] >> 8) & 0xFF00u) |
-                                ((sb[1] & 0xFFu) << 16) | ((sb[1] & 0xFF0000u) << 8);
-            const uint32_t s1 = (sb[2] & 0xFFu) | ((sb[2] >> 8) & 0xFF00u) |
-                                ((sb[3] & 0xFFu) << 16) | ((sb[3] & 0xFF0000u) << 8);
-            *reinterpret_cast<uint2 *>(col_scales + t.scale_row * cols + col0) = make_uint2(s0, s1);
+        if ((FULL || col_ok) && rg == 0) {
+            const uint32_t s0 = perm(sb[1], sb[0], 0x06040200u);     // columns 0..3
+            const uint32_t s1 = perm(sb[3], sb[2], 0x06040200u);     // columns 4..7
+            st_nt8(col_scales + t.srow * cols + col0, s0, s1);
         }
     }
 }
 
-// Workgroup w covers column block w % ncb (256 columns) of 32-row tile
-// w / ncb, so consecutive workgroups sweep one tile's rows left to right.
-// Dense tensor.
-template <bool ROW, bool COL>
-__global__ void __launch_bounds__(256) mxfp8_dense_kernel(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ncb,
-    uint8_t *__restrict__ row_codes, uint8_t *__restrict__ row_scales,
-    uint8_t *__restrict__ col_codes, uint8_t *__restrict__ col_scales)
-{
-    const int64_t tile = (int64_t)blockIdx.x / ncb;
-    const int64_t cb = (int64_t)blockIdx.x - tile * ncb;
-    TileRows t;
-    t.row0 = tile * TILE_ROWS;
-    const int64_t left = rows - t.row0;
-    t.nrows = left < TILE_ROWS ? (int)left : TILE_ROWS;
-    t.scale_row = tile;
-    const int64_t col_base = cb * WG_COLS + (threadIdx.x >> 6) * WAVE_COLS;
-    mxfp8_tile<ROW, COL>(x, cols, t, col_base, row_codes, row_scales, col_codes, col_scales);
-}
+struct Geometry {
+    const uint16_t *x;
+    int64_t rows;          // dense: rows; grouped: total rows
+    int64_t cols;
+    int64_t nct;           // 128-column strips
+    int64_t max_tiles;     // grouped: capacity of col_scales in rows
+    const int64_t *off;    // grouped: segment offsets
+    const int64_t *P;      // grouped: prefix of ceil(n_e / 32)
+    int64_t n_groups;
+};
 
-// Segment e's rows, clamped into [0, total_rows): the offsets are device data
-// the host cannot check, so malformed offsets must never move an access out
-// of bounds (they give meaningless bytes instead).
+// Segment e's rows clamped into [0, total_rows): offsets are device data the
+// host cannot check, so malformed offsets must never move an access out of
+// bounds (they give meaningless bytes instead).
 __device__ __forceinline__ void segment_rows(const int64_t *__restrict__ off, int64_t e,
                                              int64_t total_rows, int64_t *lo, int64_t *hi)
 {
@@ -176,6 +194,112 @@ __device__ __forceinline__ void segment_rows(const int64_t *__restrict__ off, in
     b = b < a ? a : (b > total_rows ? total_rows : b);
     *lo = a;
     *hi = b;
+}
+
+// Tile T of the strip -> rows.  Dense: T * 32.  Grouped: advance *e until
+// P[*e] <= T < P[*e + 1].
+template <bool GROUPED>
+__device__ __forceinline__ Tile tile_rows(const Geometry &G, int64_t T, int64_t *e)
+{
+    Tile t;
+    t.srow = T;
+    if constexpr (!GROUPED) {
+        t.row0 = T * TILE_ROWS;
+        const int64_t left = G.rows - t.row0;
+        t.nrows = left < TILE_ROWS ? (int)left : TILE_ROWS;
+    } else {
+        while (*e + 1 < G.n_groups && G.P[*e + 1] <= T)
+            ++*e;
+        int64_t lo, hi;
+        segment_rows(G.off, *e, G.rows, &lo, &hi);
+        t.row0 = lo + (T - G.P[*e]) * TILE_ROWS;
+        const int64_t left = hi - t.row0;
+        t.nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+    }
+    return t;
+}
+
+template <bool ROW, bool COL>
+__device__ __forceinline__ void do_tile(const uint32_t (&v)[8][4], const Geometry &G, int64_t col0,
+                                        const Tile &t, bool full, int g, int rg, bool col_ok,
+                                        uint8_t *rc, uint8_t *rs, uint8_t *cc, uint8_t *cs)
+{
+    if (full)
+        convert_tile<ROW, COL, true>(v, G.cols, col0, t, g, rg, col_ok, rc, rs, cc, cs);
+    else
+        convert_tile<ROW, COL, false>(v, G.cols, col0, t, g, rg, col_ok, rc, rs, cc, cs);
+}
+
+template <bool ROW, bool COL, bool GROUPED>
+__global__ void __launch_bounds__(256) mxfp8_kernel(Geometry G, uint8_t *__restrict__ rc,
+                                                    uint8_t *__restrict__ rs,
+                                                    uint8_t *__restrict__ cc,
+                                                    uint8_t *__restrict__ cs)
+{
+    const int lane = __lane_id();
+    const int g = lane & 15, rg = lane >> 4;
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    // Strip and tile range of this wavefront.
+    const int64_t strip = wave % G.nct;
+    const int64_t slot = wave / G.nct, nslots = nwaves / G.nct;
+    int64_t ntiles;
+    if constexpr (GROUPED) {
+        ntiles = G.P[G.n_groups];
+        if (ntiles > G.max_tiles)
+            ntiles = G.max_tiles;
+    } else {
+        ntiles = (G.rows + TILE_ROWS - 1) / TILE_ROWS;
+    }
+    if (slot >= nslots)
+        return;
+    const int64_t per = (ntiles + nslots - 1) / nslots;
+    int64_t T = slot * per;
+    const int64_t Tend = T + per < ntiles ? T + per : ntiles;
+    if (T >= Tend)
+        return;
+    const int64_t col0 = strip * TILE_COLS + 8 * g;
+    const bool col_ok = col0 < G.cols;                  // cols % 32 == 0: whole 32-column blocks
+    const bool strip_full = strip * TILE_COLS + TILE_COLS <= G.cols;
+    int64_t e = 0;
+
+    uint32_t va[8][4], vb[8][4];
+    Tile ta = tile_rows<GROUPED>(G, T, &e), tb;
+    bool fa = strip_full && ta.nrows == TILE_ROWS, fb = false;
+    if (fa)
+        load_tile<true>(va, G.x, G.cols, col0, ta, rg, col_ok);
+    else
+        load_tile<false>(va, G.x, G.cols, col0, ta, rg, col_ok);
+    for (;;) {
+        // Prefetch T + 1 into vb, convert T from va.
+        const bool more = T + 1 < Tend;
+        if (more) {
+            tb = tile_rows<GROUPED>(G, T + 1, &e);
+            fb = strip_full && tb.nrows == TILE_ROWS;
+            if (fb)
+                load_tile<true>(vb, G.x, G.cols, col0, tb, rg, col_ok);
+            else
+                load_tile<false>(vb, G.x, G.cols, col0, tb, rg, col_ok);
+        }
+        do_tile<ROW, COL>(va, G, col0, ta, fa, g, rg, col_ok, rc, rs, cc, cs);
+        if (!more)
+            break;
+        T += 1;
+        // Prefetch T + 1 into va, convert T from vb.
+        const bool more2 = T + 1 < Tend;
+        if (more2) {
+            ta = tile_rows<GROUPED>(G, T + 1, &e);
+            fa = strip_full && ta.nrows == TILE_ROWS;
+            if (fa)
+                load_tile<true>(va, G.x, G.cols, col0, ta, rg, col_ok);
+            else
+                load_tile<false>(va, G.x, G.cols, col0, ta, rg, col_ok);
+        }
+        do_tile<ROW, COL>(vb, G, col0, tb, fb, g, rg, col_ok, rc, rs, cc, cs);
+        if (!more2)
+            break;
+        T += 1;
+    }
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
@@ -212,62 +336,53 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
         P[n_groups] = carry;
 }
 
-// Grouped: the grid enumerates max_tiles = total_rows/32 + n_groups tiles
-// (the capacity of col_scales); tiles at or beyond P[G] exit.
-template <bool ROW, bool COL>
-__global__ void __launch_bounds__(256) mxfp8_grouped_kernel(
-    const uint16_t *__restrict__ x, int64_t total_rows, int64_t cols, int64_t ncb,
-    const int64_t *__restrict__ off, int64_t n_groups, const int64_t *__restrict__ P,
-    uint8_t *__restrict__ row_codes, uint8_t *__restrict__ row_scales,
-    uint8_t *__restrict__ col_codes, uint8_t *__restrict__ col_scales)
-{
-    const int64_t tile = (int64_t)blockIdx.x / ncb;
-    const int64_t cb = (int64_t)blockIdx.x - tile * ncb;
-    if (tile >= P[n_groups])
-        return;
-    // The last e with P[e] <= tile; then P[e] <= tile < P[e+1], so segment e
-    // is not empty.
-    int64_t lo = 0, hi = n_groups - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (P[mid] <= tile)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int64_t e = lo;
-    int64_t s_lo, s_hi;
-    segment_rows(off, e, total_rows, &s_lo, &s_hi);
-    TileRows t;
-    t.row0 = s_lo + (tile - P[e]) * TILE_ROWS;
-    const int64_t left = s_hi - t.row0;
-    t.nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
-    t.scale_row = tile;
-    const int64_t col_base = cb * WG_COLS + (threadIdx.x >> 6) * WAVE_COLS;
-    mxfp8_tile<ROW, COL>(x, cols, t, col_base, row_codes, row_scales, col_codes, col_scales);
-}
-
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
+// Wavefronts to launch: enough to fill the device (4 per SIMD) but not more
+// than one per tile, rounded to a multiple of the strip count.
+static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    const int64_t target = (int64_t)cus * 16;
+    int64_t slots = target / nct;
+    if (slots < 1)
+        slots = 1;
+    if (slots > tiles_per_strip)
+        slots = tiles_per_strip;
+    return slots * nct;
+}
+
+template <bool GROUPED>
+static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc, uint8_t *rs,
+                         uint8_t *cc, uint8_t *cs, hipStream_t stream)
+{
+    const int64_t waves = wave_count(G.nct, tiles_per_strip);
+    const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    const dim3 grid((unsigned)wgs), block(64 * WAVES_PER_WG);
+    if (rc && cc)
+        hipLaunchKernelGGL((mxfp8_kernel<true, true, GROUPED>), grid, block, 0, stream, G, rc, rs,
+                           cc, cs);
+    else if (rc)
+        hipLaunchKernelGGL((mxfp8_kernel<true, false, GROUPED>), grid, block, 0, stream, G, rc, rs,
+                           cc, cs);
+    else
+        hipLaunchKernelGGL((mxfp8_kernel<false, true, GROUPED>), grid, block, 0, stream, G, rc, rs,
+                           cc, cs);
+    return hipGetLastError();
+}
+
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
                               uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
-    const int64_t ncb = (cols + WG_COLS - 1) / WG_COLS;
-    const int64_t tiles = (rows + TILE_ROWS - 1) / TILE_ROWS;
-    const dim3 grid((unsigned)(ncb * tiles));
-    const dim3 block(256);
-    if (rc && cc)
-        hipLaunchKernelGGL((mxfp8_dense_kernel<true, true>), grid, block, 0, stream, x, rows, cols,
-                           ncb, rc, rs, cc, cs);
-    else if (rc)
-        hipLaunchKernelGGL((mxfp8_dense_kernel<true, false>), grid, block, 0, stream, x, rows, cols,
-                           ncb, rc, rs, cc, cs);
-    else
-        hipLaunchKernelGGL((mxfp8_dense_kernel<false, true>), grid, block, 0, stream, x, rows, cols,
-                           ncb, rc, rs, cc, cs);
-    return hipGetLastError();
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0};
+    return launch<false>(G, (rows + TILE_ROWS - 1) / TILE_ROWS, rc, rs, cc, cs, stream);
 }
 
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,
@@ -280,18 +395,9 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
     if (err != hipSuccess)
         return err;
     const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
-    const int64_t ncb = (cols + WG_COLS - 1) / WG_COLS;
-    const dim3 grid((unsigned)(ncb * max_tiles));
-    if (rc && cc)
-        hipLaunchKernelGGL((mxfp8_grouped_kernel<true, true>), grid, dim3(256), 0, stream, x,
-                           total_rows, cols, ncb, off, n_groups, P, rc, rs, cc, cs);
-    else if (cc)
-        hipLaunchKernelGGL((mxfp8_grouped_kernel<false, true>), grid, dim3(256), 0, stream, x,
-                           total_rows, cols, ncb, off, n_groups, P, rc, rs, cc, cs);
-    else
-        hipLaunchKernelGGL((mxfp8_grouped_kernel<true, false>), grid, dim3(256), 0, stream, x,
-                           total_rows, cols, ncb, off, n_groups, P, rc, rs, cc, cs);
-    return hipGetLastError();
+    Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
+               n_groups};
+    return launch<true>(G, max_tiles, rc, rs, cc, cs, stream);
 }
 
 }  // namespace mxq

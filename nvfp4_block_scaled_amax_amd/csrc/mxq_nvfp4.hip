@@ -1,41 +1,75 @@
 // mxq_nvfp4.hip -- NVFP4 quantizers: per-token FP32 scale (the per-token
 // activation paragraphs of the page "Miles: end-to-end MXFP8 and per-token
-// NVFP4 RL on Blackwell") and scoped weight export with one FP32 scale per
-// gate/up pair or per tensor (its gate/up pairing paragraph).  The arithmetic
-// is the page's NVFP4 format paragraph under the readings stated in mxq.h:
+// NVFP4 RL on Blackwell") and weight export with one FP32 scale per gate/up
+// pair or per tensor (its gate/up pairing paragraph).  The arithmetic is the
+// page's NVFP4 format paragraph under the readings stated in mxq.h:
 //   s = fp32(A_scope / 2688), b = E4M3(A_block / (6 s)), c = E2M1(x / (dec(b) s)).
 //
-// Layout.  One wavefront owns one row.  The row is read in chunks of 512
-// elements; in chunk c lane l holds elements 512c + 8l .. +7 (one 16-byte
-// load), so a 16-element block is the lane pair (2m, 2m+1): the block amax is
-// an in-lane max and one DPP exchange, the token amax a wavefront reduction.
-// For rows up to 4096 elements the whole row stays in registers (one HBM
-// read); longer rows are read twice.
+// Layout.  A lane owns whole 16-element blocks (two 16-byte loads each) and
+// holds them as f32, so a block's amax is an in-lane max (|x| comes free as a
+// source modifier) and its scale work is done once.  Per-token: one wavefront
+// per row, persistent over rows with the next row's loads in flight while the
+// current one is converted; the token amax is a wavefront reduction.  Export:
+// the tensor is a flat array of blocks (each lies in one scope), 64 blocks per
+// wavefront step, with the scope's FP32 scale computed beforehand.
 //
 // Exact decisions without division.  Dividing per element is too slow and
-// multiplying by a rounded reciprocal is not exact.  Instead every decision is
-// bracketed: with r ~ 1/D (D = 6s for block scales, dec(b) s for codes) built
-// from v_rcp_f32 and rounded products, relative error below 2^-21, the kernel
-// forms q_lo = x * r(1 - 2^-19) and q_hi = x * r(1 + 2^-19), which satisfy
-// |q_lo| < |x / D| < |q_hi| (strictly; all operands normal on this path).
-// Rounding is monotone, so when the hardware's exact nearest-even conversions
-// of q_lo and q_hi agree, that code is the exactly rounded code of x / D.
-// When they differ (x / D within 2^-18 of a rounding midpoint, which random
-// data hits a few times per million elements), the lane decides exactly in
-// binary64: |x| against midpoint * D, a product with at most 31 significant
-// bits, hence exact.  Rows whose scope amax is below 2^-90 (an FP32 scale
-// below 2^-101) would take the reciprocals out of the normal range; they go to
-// a binary64 path that divides once per element.
+// multiplying by a rounded reciprocal is not exact.  Every decision is
+// bracketed instead: with r ~ 1/D (D = 6s for block scales, dec(b) s for codes)
+// built from v_rcp_f32 (under 1 ulp) and rounded products, relative error
+// below 2^-21, the kernel forms q_lo = x * r (1 - 2^-19) and
+// q_hi = x * r (1 + 2^-19), so |q_lo| < |x / D| < |q_hi| with all operands
+// normal.  Conversion is monotone, so when the hardware's exact nearest-even
+// conversions of q_lo and q_hi agree, that code is the exactly rounded code of
+// x / D.  When they differ (x / D within ~2^-18 of a rounding midpoint, a few
+// per million random elements), the lane decides exactly in binary64: |x|
+// against midpoint * D, a product of at most 31 significant bits, hence exact.
+// Scales below 2^-101 would take the reciprocals out of the normal range; such
+// scopes use a binary64 path that divides once per element.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
 namespace mxq {
 
-constexpr int ROWS_PER_WG = 4;               // one row per wavefront
-constexpr uint32_t FAST_MIN_AMAX = 0x1280u;  // BF16 bits of 2^-90
+constexpr int WAVES_PER_WG = 4;
+constexpr float S_FAST_MIN = 0x1p-101f;
 constexpr float BRACKET_LO = 1.0f - 0x1p-19f;
 constexpr float BRACKET_HI = 1.0f + 0x1p-19f;
 constexpr float ONE_SIXTH = 1.0f / 6.0f;
+
+// ---------------------------------------------------------------------------
+// One 16-element block
+// ---------------------------------------------------------------------------
+struct Blk {
+    uint32_t w[8];     // 16 BF16, packed in pairs
+};
+
+__device__ __forceinline__ void load_blk(Blk &b, const uint16_t *p)
+{
+    const uint4 q0 = ld_nt16(p), q1 = ld_nt16(p + 8);
+    b.w[0] = q0.x; b.w[1] = q0.y; b.w[2] = q0.z; b.w[3] = q0.w;
+    b.w[4] = q1.x; b.w[5] = q1.y; b.w[6] = q1.z; b.w[7] = q1.w;
+}
+
+__device__ __forceinline__ void zero_blk(Blk &b)
+{
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        b.w[i] = 0u;
+}
+
+// Largest |x| of the block, as non-negative f32 bits (compare as integers).
+__device__ __forceinline__ uint32_t blk_amax(const Blk &b)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t lo = (b.w[i] << 16) & 0x7FFFFFFFu;
+        const uint32_t hi = b.w[i] & 0x7FFF0000u;
+        m = max(m, max(lo, hi));
+    }
+    return m;
+}
 
 // Exact block scale when the bracket straddles a midpoint: blo and blo + 1 are
 // the candidates; compare A with their midpoint times 6 s exactly.
@@ -51,40 +85,59 @@ __device__ __attribute__((noinline)) uint32_t block_scale_exact(float A, float s
     return (blo & 1u) ? blo + 1 : blo;
 }
 
-// Fix the nibbles where the bracket codes differ.  lo/hi: 8 codes each; xs:
-// the 8 inputs as f32; D = d s exactly as (d, s).
-__device__ __attribute__((noinline)) uint32_t codes_exact(uint32_t lo, uint32_t hi,
-                                                          const float *xs, float d, float s)
+// Nibble i of the bracket results lo/hi differ: decide it exactly.  x: the
+// element (BF16 bits), D2 = 2 d s in binary64 (exact).
+__device__ __forceinline__ uint32_t fix_nibble(uint32_t lo, uint32_t hi, int i, uint32_t xbits,
+                                               double Dd)
 {
-    const double D = (double)d * (double)s;
-    uint32_t out = lo;
-#pragma unroll 1
-    for (int i = 0; i < 8; i++) {
-        const uint32_t a = (lo >> (4 * i)) & 0xFu, b = (hi >> (4 * i)) & 0xFu;
-        if (a == b)
-            continue;
-        const uint32_t klo = a & 7u, khi = b & 7u;     // khi == klo + 1
-        const double t = (e2m1_value_f64(klo) + e2m1_value_f64(khi)) * D;  // 2 * mid * D
-        const double ax = 2.0 * fabs((double)xs[i]);
-        uint32_t k;
-        if (ax > t)
-            k = khi;
-        else if (ax < t)
-            k = klo;
-        else
-            k = (klo & 1u) ? khi : klo;
-        out = (out & ~(0xFu << (4 * i))) | ((k | (a & 8u)) << (4 * i));
-    }
-    return out;
+    const uint32_t a = (lo >> (4 * i)) & 0xFu, b = (hi >> (4 * i)) & 0xFu;
+    if (a == b)
+        return lo;
+    const uint32_t klo = a & 7u, khi = b & 7u;     // khi == klo + 1
+    const double t = (e2m1_value_f64(klo) + e2m1_value_f64(khi)) * Dd;   // 2 * mid * D
+    const double ax = 2.0 * fabs((double)u2f(xbits << 16));
+    uint32_t k;
+    if (ax > t)
+        k = khi;
+    else if (ax < t)
+        k = klo;
+    else
+        k = (klo & 1u) ? khi : klo;
+    return (lo & ~(0xFu << (4 * i))) | ((k | (a & 8u)) << (4 * i));
 }
 
-// One 8-element slice (a lane's half of a 16-block) on the fast path.
-// Returns 8 packed codes; *b_out gets the block scale byte.
-__device__ __forceinline__ uint32_t quant8_fast(const uint32_t (&v)[4], uint32_t bamax, float s,
-                                                float inv_s, float r6_lo, float r6_hi,
-                                                uint32_t *b_out)
+// Fix the nibbles of one 8-code word.  w0..w3: the 8 inputs (BF16 pairs).
+__device__ __attribute__((noinline)) uint32_t codes_exact(uint32_t lo, uint32_t hi, uint32_t w0,
+                                                          uint32_t w1, uint32_t w2, uint32_t w3,
+                                                          float d, float s)
 {
-    const float A = u2f(bamax << 16);
+    const double D = (double)d * (double)s;
+    const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        lo = fix_nibble(lo, hi, i, bits, D);
+    }
+    return lo;
+}
+
+// The 8 codes of 8 values times r, written with the hardware conversion.
+__device__ __forceinline__ uint32_t codes8(const uint32_t *w, float r)
+{
+    uint32_t c = 0;
+    c = e2m1_pair<0>(c, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r);
+    c = e2m1_pair<1>(c, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r);
+    c = e2m1_pair<2>(c, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r);
+    c = e2m1_pair<3>(c, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r);
+    return c;
+}
+
+// Fast path for one block: codes (two words) and the block scale byte.
+__device__ __forceinline__ void quant_blk_fast(const Blk &blk, uint32_t amax_bits, float s,
+                                               float inv_s, float r6_lo, float r6_hi,
+                                               uint32_t *b_out, uint32_t *c0, uint32_t *c1)
+{
+    const float A = u2f(amax_bits);
     const float plo = fminf(A * r6_lo, 448.0f);
     const float phi = fminf(A * r6_hi, 448.0f);
     const uint32_t bb = e4m3_pair_rne(plo, phi);
@@ -92,180 +145,205 @@ __device__ __forceinline__ uint32_t quant8_fast(const uint32_t (&v)[4], uint32_t
     if (b != (bb >> 8))
         b = block_scale_exact(A, s, b);
     *b_out = b;
-    if (b == 0)
-        return 0u;
+    if (b == 0) {
+        *c0 = 0u;
+        *c1 = 0u;
+        return;
+    }
     const float d = e4m3_value(b);
     const float r = __builtin_amdgcn_rcpf(d) * inv_s;
     const float rlo = r * BRACKET_LO, rhi = r * BRACKET_HI;
-    float xs[8];
+    uint32_t lo0 = codes8(blk.w, rlo), hi0 = codes8(blk.w, rhi);
+    uint32_t lo1 = codes8(blk.w + 4, rlo), hi1 = codes8(blk.w + 4, rhi);
+    if (lo0 != hi0)
+        lo0 = codes_exact(lo0, hi0, blk.w[0], blk.w[1], blk.w[2], blk.w[3], d, s);
+    if (lo1 != hi1)
+        lo1 = codes_exact(lo1, hi1, blk.w[4], blk.w[5], blk.w[6], blk.w[7], d, s);
+    *c0 = lo0;
+    *c1 = lo1;
+}
+
+// binary64 path (0 < s < 2^-101): one division per element.  Returns the
+// scale byte and the two code words (by value, so nothing goes to scratch).
+struct BlkOut {
+    uint32_t b, c0, c1;
+};
+
+__device__ __attribute__((noinline)) BlkOut quant_blk_f64(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                          uint32_t w3, uint32_t w4, uint32_t w5,
+                                                          uint32_t w6, uint32_t w7,
+                                                          uint32_t amax_bits, float s)
+{
+    const uint32_t w[8] = {w0, w1, w2, w3, w4, w5, w6, w7};
+    const double A = (double)u2f(amax_bits);
+    BlkOut o;
+    o.b = e4m3_code_f64(A / (6.0 * (double)s));
+    o.c0 = o.c1 = 0u;
+    if (o.b != 0) {
+        const double D = (double)e4m3_value(o.b) * (double)s;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        xs[2 * j] = bf16_lo(v[j]);
-        xs[2 * j + 1] = bf16_hi(v[j]);
+        for (int i = 0; i < 16; i++) {
+            const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+            const double xv = (double)u2f(bits << 16);
+            const uint32_t k = e2m1_code_f64(fabs(xv) / D) | ((bits >> 12) & 8u);
+            if (i < 8)
+                o.c0 |= k << (4 * i);
+            else
+                o.c1 |= k << (4 * (i - 8));
+        }
     }
-    uint32_t lo = 0, hi = 0;
-    lo = e2m1_pair<0>(lo, xs[0] * rlo, xs[1] * rlo);
-    hi = e2m1_pair<0>(hi, xs[0] * rhi, xs[1] * rhi);
-    lo = e2m1_pair<1>(lo, xs[2] * rlo, xs[3] * rlo);
-    hi = e2m1_pair<1>(hi, xs[2] * rhi, xs[3] * rhi);
-    lo = e2m1_pair<2>(lo, xs[4] * rlo, xs[5] * rlo);
-    hi = e2m1_pair<2>(hi, xs[4] * rhi, xs[5] * rhi);
-    lo = e2m1_pair<3>(lo, xs[6] * rlo, xs[7] * rlo);
-    hi = e2m1_pair<3>(hi, xs[6] * rhi, xs[7] * rhi);
-    if (lo != hi)
-        lo = codes_exact(lo, hi, xs, d, s);
-    return lo;
+    return o;
 }
 
-// One 8-element slice on the binary64 path (tiny scopes).
-__device__ __attribute__((noinline)) uint32_t quant8_f64(const uint32_t *v, uint32_t bamax,
-                                                         float s, uint32_t *b_out)
+// Per-scale constants of the fast path.
+struct ScaleK {
+    float s, inv_s, r6_lo, r6_hi;
+};
+
+__device__ __forceinline__ ScaleK scale_k(float s)
 {
-    const double A = (double)u2f(bamax << 16);
-    const uint32_t b = e4m3_code_f64(A / (6.0 * (double)s));
-    *b_out = b;
-    if (b == 0)
-        return 0u;
-    const double D = (double)e4m3_value(b) * (double)s;
-    uint32_t out = 0;
-    for (int i = 0; i < 8; i++) {
-        const uint32_t bits = (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
-        const double xv = (double)u2f(bits << 16);
-        const uint32_t k = e2m1_code_f64(fabs(xv) / D) | ((bits >> 12) & 8u);
-        out |= k << (4 * i);
-    }
-    return out;
+    ScaleK k;
+    k.s = s;
+    k.inv_s = __builtin_amdgcn_rcpf(s);
+    const float r6 = k.inv_s * ONE_SIXTH;
+    k.r6_lo = r6 * BRACKET_LO;
+    k.r6_hi = r6 * BRACKET_HI;
+    return k;
 }
 
-// Block amax of this lane's 8 values, exchanged with the partner lane.
-__device__ __forceinline__ uint32_t slice_amax(const uint32_t (&v)[4])
+// Quantize one block under scale k (any path) and store 8 code bytes and the
+// scale byte.
+__device__ __forceinline__ void emit_blk(const Blk &blk, uint32_t amax_bits, const ScaleK &k,
+                                         uint8_t *__restrict__ codes8p, uint8_t *__restrict__ bsp)
 {
-    const uint32_t m = pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
-                                  pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu));
-    const uint32_t h = hmax_u16(m);
-    return max(h, dpp<DPP_XOR1>(h));
-}
-
-// Quantize one slice and store its codes (and, from even lanes, the block
-// scale).  k0 = index of the slice's first element in the row.
-__device__ __forceinline__ void emit_slice(const uint32_t (&v)[4], uint32_t bamax, uint32_t A,
-                                           float s, float inv_s, float r6_lo, float r6_hi,
-                                           int64_t k0, uint8_t *__restrict__ codes_row,
-                                           uint8_t *__restrict__ bs_row, int lane)
-{
-    uint32_t b, c;
-    if (A >= FAST_MIN_AMAX) {
-        c = quant8_fast(v, bamax, s, inv_s, r6_lo, r6_hi, &b);
-    } else if (A == 0) {
-        b = 0;
-        c = 0;
+    uint32_t b, c0, c1;
+    if (k.s >= S_FAST_MIN) {
+        quant_blk_fast(blk, amax_bits, k.s, k.inv_s, k.r6_lo, k.r6_hi, &b, &c0, &c1);
+    } else if (k.s == 0.0f) {
+        b = 0u;
+        c0 = c1 = 0u;
     } else {
-        c = quant8_f64(v, bamax, s, &b);
+        const BlkOut o = quant_blk_f64(blk.w[0], blk.w[1], blk.w[2], blk.w[3], blk.w[4], blk.w[5],
+                                       blk.w[6], blk.w[7], amax_bits, k.s);
+        b = o.b;
+        c0 = o.c0;
+        c1 = o.c1;
     }
-    st_nt4(codes_row + (k0 >> 1), c);
-    if ((lane & 1) == 0)
-        bs_row[k0 >> 4] = (uint8_t)b;
+    st_nt8(codes8p, c0, c1);
+    *bsp = (uint8_t)b;
 }
 
-// SCOPED == false: the scope is the row itself (per-token scale, written to
-// token_scales).  SCOPED == true: the scope amax (BF16 bits as u32) is
-// scope_amax[row / rows_per_scope]; rows at or beyond `rows_a` come from the
-// second tensor (x_b, codes_b, bs_b) -- the up half of a gate/up pair.
-// NC > 0: the row (<= 512 * NC elements) is kept in registers; NC == 0:
-// generic length, read twice.
-template <int NC, bool SCOPED>
-__global__ void __launch_bounds__(256) nvfp4_kernel(
-    const uint16_t *__restrict__ x_a, const uint16_t *__restrict__ x_b, int64_t rows_a,
-    int64_t rows, int64_t cols, uint8_t *__restrict__ codes_a, uint8_t *__restrict__ codes_b,
-    uint8_t *__restrict__ bs_a, uint8_t *__restrict__ bs_b, float *__restrict__ token_scales,
-    const uint32_t *__restrict__ scope_amax, int64_t rows_per_scope)
+// ---------------------------------------------------------------------------
+// Per-token kernel: a wavefront per row; block j of the row is held by lane
+// j % 64 in slot j / 64.  NB slots cover rows of up to 1024 * NB elements.
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void load_row(Blk (&r)[NB], const uint16_t *__restrict__ xr,
+                                         int64_t nblk, int lane)
 {
-    const int64_t row_all = (int64_t)blockIdx.x * ROWS_PER_WG + (threadIdx.x >> 6);
-    if (row_all >= rows)
-        return;
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        const int64_t blk = 64 * j + lane;
+        if (blk < nblk)
+            load_blk(r[j], xr + 16 * blk);
+        else
+            zero_blk(r[j]);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void token_row(const Blk (&r)[NB], int64_t row, int64_t cols,
+                                          int64_t nblk, int lane, uint8_t *__restrict__ codes,
+                                          uint8_t *__restrict__ bs, float *__restrict__ ts)
+{
+    uint32_t am[NB];
+    uint32_t A = 0;
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        am[j] = blk_amax(r[j]);
+        A = max(A, am[j]);
+    }
+    A = wave_max_u32(A);
+    const float s = u2f(A) / 2688.0f;
+    if (lane == 0)
+        ts[row] = s;
+    const ScaleK k = scale_k(s);
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        const int64_t blk = 64 * j + lane;
+        if (blk < nblk)
+            emit_blk(r[j], am[j], k, codes + row * (cols >> 1) + 8 * blk,
+                     bs + row * (cols >> 4) + blk);
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) nvfp4_token_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ bs,
+                                                          float *__restrict__ ts)
+{
     const int lane = __lane_id();
-    const bool second = SCOPED && row_all >= rows_a;
-    const int64_t row = second ? row_all - rows_a : row_all;
-    const uint16_t *xr = (second ? x_b : x_a) + row * cols;
-    uint8_t *codes_row = (second ? codes_b : codes_a) + row * (cols >> 1);
-    uint8_t *bs_row = (second ? bs_b : bs_a) + row * (cols >> 4);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
+    if (row >= rows)
+        return;
+    const int64_t nblk = cols >> 4;
+    Blk ra[NB], rb[NB];
+    load_row<NB>(ra, x + row * cols, nblk, lane);
+    for (;;) {
+        const int64_t n1 = row + nwaves;
+        if (n1 < rows)
+            load_row<NB>(rb, x + n1 * cols, nblk, lane);
+        token_row<NB>(ra, row, cols, nblk, lane, codes, bs, ts);
+        if (n1 >= rows)
+            break;
+        row = n1;
+        const int64_t n2 = row + nwaves;
+        if (n2 < rows)
+            load_row<NB>(ra, x + n2 * cols, nblk, lane);
+        token_row<NB>(rb, row, cols, nblk, lane, codes, bs, ts);
+        if (n2 >= rows)
+            break;
+        row = n2;
+    }
+}
 
-    if constexpr (NC > 0) {
-        uint32_t v[NC][4];
-        uint32_t bam[NC];
-        uint32_t rmax = 0;
-#pragma unroll
-        for (int c = 0; c < NC; c++) {
-            const int64_t k0 = 512 * c + 8 * lane;
-            if (k0 < cols) {
-                const uint4 q = ld_nt16(xr + k0);
-                v[c][0] = q.x; v[c][1] = q.y; v[c][2] = q.z; v[c][3] = q.w;
-            } else {
-                v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0u;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < NC; c++) {
-            bam[c] = slice_amax(v[c]);
-            rmax = max(rmax, bam[c]);
-        }
-        uint32_t A;
-        if constexpr (SCOPED) {
-            A = scope_amax[row / rows_per_scope];
-        } else {
-            A = wave_max_u32(rmax);
-        }
-        const float s = u2f(A << 16) / 2688.0f;
-        if (!SCOPED && lane == 0)
-            token_scales[row] = s;
-        const float inv_s = __builtin_amdgcn_rcpf(s);
-        const float r6 = inv_s * ONE_SIXTH;
-        const float r6_lo = r6 * BRACKET_LO, r6_hi = r6 * BRACKET_HI;
-#pragma unroll
-        for (int c = 0; c < NC; c++) {
-            const int64_t k0 = 512 * c + 8 * lane;
-            if (k0 < cols)
-                emit_slice(v[c], bam[c], A, s, inv_s, r6_lo, r6_hi, k0, codes_row, bs_row, lane);
-        }
-    } else {
-        uint32_t A;
-        if constexpr (SCOPED) {
-            A = scope_amax[row / rows_per_scope];
-        } else {
-            uint32_t rmax = 0;
-            for (int64_t k0 = 8 * lane; k0 < cols; k0 += 512) {
-                const uint4 q = ld16(xr + k0);
-                const uint32_t v[4] = {q.x, q.y, q.z, q.w};
-                const uint32_t m = pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
-                                              pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu));
-                rmax = max(rmax, hmax_u16(m));
-            }
-            A = wave_max_u32(rmax);
-        }
-        const float s = u2f(A << 16) / 2688.0f;
-        if (!SCOPED && lane == 0)
-            token_scales[row] = s;
-        const float inv_s = __builtin_amdgcn_rcpf(s);
-        const float r6 = inv_s * ONE_SIXTH;
-        const float r6_lo = r6 * BRACKET_LO, r6_hi = r6 * BRACKET_HI;
-        // Uniform trip count so the DPP exchange sees every lane active.
-        for (int64_t base = 0; base < cols; base += 512) {
-            const int64_t k0 = base + 8 * lane;
-            uint32_t v[4] = {0u, 0u, 0u, 0u};
-            if (k0 < cols) {
-                const uint4 q = ld16(xr + k0);
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-            }
-            const uint32_t bam = slice_amax(v);
-            if (k0 < cols)
-                emit_slice(v, bam, A, s, inv_s, r6_lo, r6_hi, k0, codes_row, bs_row, lane);
-        }
+// Rows longer than 4096 elements: the row is read twice (amax, then codes).
+__global__ void __launch_bounds__(256) nvfp4_token_long_kernel(const uint16_t *__restrict__ x,
+                                                               int64_t rows, int64_t cols,
+                                                               uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ bs,
+                                                               float *__restrict__ ts)
+{
+    const int lane = __lane_id();
+    const int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
+    if (row >= rows)
+        return;
+    const int64_t nblk = cols >> 4;
+    const uint16_t *xr = x + row * cols;
+    uint32_t A = 0;
+    for (int64_t blk = lane; blk < nblk; blk += 64) {
+        Blk b;
+        load_blk(b, xr + 16 * blk);
+        A = max(A, blk_amax(b));
+    }
+    A = wave_max_u32(A);
+    const float s = u2f(A) / 2688.0f;
+    if (lane == 0)
+        ts[row] = s;
+    const ScaleK k = scale_k(s);
+    for (int64_t blk = lane; blk < nblk; blk += 64) {
+        Blk b;
+        load_blk(b, xr + 16 * blk);
+        emit_blk(b, blk_amax(b), k, codes + row * (cols >> 1) + 8 * blk,
+                 bs + row * (cols >> 4) + blk);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Scope amax for the weight export: zero, reduce (atomic max per workgroup),
-// and the final conversion of the amax bits to the FP32 scale.
+// Export: scope amax, FP32 scales, then a flat pass over the blocks.
 // ---------------------------------------------------------------------------
 __global__ void zero_u32_kernel(uint32_t *p, int64_t n)
 {
@@ -279,6 +357,7 @@ constexpr int64_t AMAX_CHUNK = 256 * 8 * AMAX_LOADS;        // elements per work
 
 // Workgroup w reduces chunk w % chunks of scope w / chunks.  A scope is
 // tensor a's slice [e * n_per, (e+1) * n_per) followed by tensor b's (if any).
+// The result is the amax's BF16 magnitude bits (as u32) in amax[e].
 __global__ void __launch_bounds__(256) scope_amax_kernel(const uint16_t *__restrict__ a,
                                                          const uint16_t *__restrict__ b,
                                                          int64_t n_per, int64_t chunks,
@@ -294,7 +373,7 @@ __global__ void __launch_bounds__(256) scope_amax_kernel(const uint16_t *__restr
         const int64_t i = ch * AMAX_CHUNK + (int64_t)it * 2048 + 8 * threadIdx.x;
         if (i < n_scope) {
             const uint16_t *p = (i < n_per) ? a + e * n_per + i : b + e * n_per + (i - n_per);
-            const uint4 q = ld16(p);
+            const uint4 q = ld_nt16(p);
             m = pk_max_u16(m, pk_max_u16(pk_max_u16(q.x & 0x7FFF7FFFu, q.y & 0x7FFF7FFFu),
                                          pk_max_u16(q.z & 0x7FFF7FFFu, q.w & 0x7FFF7FFFu)));
         }
@@ -309,6 +388,7 @@ __global__ void __launch_bounds__(256) scope_amax_kernel(const uint16_t *__restr
     }
 }
 
+// amax bits -> s = fp32(amax / 2688), in place.
 __global__ void scope_finalize_kernel(uint32_t *p, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -318,42 +398,117 @@ __global__ void scope_finalize_kernel(uint32_t *p, int64_t n)
     }
 }
 
+// Flat export pass over one tensor of nblk blocks; block j belongs to scope
+// j / bps (bps = blocks per scope).  Step t covers blocks 64 t .. 64 t + 63;
+// when bps >= 64 a step spans at most two scopes, so the scope comes from one
+// wave-uniform division and a compare.
+__device__ __forceinline__ void scoped_step(const Blk &blk, int64_t t, int lane, int64_t nblk,
+                                            int64_t bps, const float *__restrict__ scope_s,
+                                            uint8_t *__restrict__ codes, uint8_t *__restrict__ bs)
+{
+    const int64_t j = 64 * t + lane;
+    int64_t e;
+    if (bps >= 64) {
+        const int64_t e0 = (64 * t) / bps;                 // wave-uniform
+        e = e0 + (j >= (e0 + 1) * bps ? 1 : 0);
+    } else {
+        e = j / bps;
+    }
+    if (j >= nblk)
+        return;
+    const ScaleK k = scale_k(scope_s[e]);
+    emit_blk(blk, blk_amax(blk), k, codes + 8 * j, bs + j);
+}
+
+__global__ void __launch_bounds__(256) nvfp4_scoped_kernel(const uint16_t *__restrict__ x,
+                                                           int64_t nblk, int64_t bps,
+                                                           const float *__restrict__ scope_s,
+                                                           uint8_t *__restrict__ codes,
+                                                           uint8_t *__restrict__ bs)
+{
+    const int lane = __lane_id();
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t nsteps = (nblk + 63) >> 6;
+    int64_t t = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
+    if (t >= nsteps)
+        return;
+    Blk ba, bb;
+    {
+        const int64_t j = 64 * t + lane;
+        if (j < nblk)
+            load_blk(ba, x + 16 * j);
+        else
+            zero_blk(ba);
+    }
+    for (;;) {
+        const int64_t t1 = t + nwaves;
+        if (t1 < nsteps) {
+            const int64_t j1 = 64 * t1 + lane;
+            if (j1 < nblk)
+                load_blk(bb, x + 16 * j1);
+            else
+                zero_blk(bb);
+        }
+        scoped_step(ba, t, lane, nblk, bps, scope_s, codes, bs);
+        if (t1 >= nsteps)
+            break;
+        t = t1;
+        const int64_t t2 = t + nwaves;
+        if (t2 < nsteps) {
+            const int64_t j2 = 64 * t2 + lane;
+            if (j2 < nblk)
+                load_blk(ba, x + 16 * j2);
+            else
+                zero_blk(ba);
+        }
+        scoped_step(bb, t, lane, nblk, bps, scope_s, codes, bs);
+        if (t2 >= nsteps)
+            break;
+        t = t2;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <bool SCOPED>
-static hipError_t launch_nvfp4(const uint16_t *xa, const uint16_t *xb, int64_t rows_a,
-                               int64_t rows, int64_t cols, uint8_t *ca, uint8_t *cb, uint8_t *ba,
-                               uint8_t *bb, float *ts, const uint32_t *scope_amax,
-                               int64_t rows_per_scope, hipStream_t stream)
+static int64_t device_waves(int per_simd)
 {
-    const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG));
-    const dim3 block(64 * ROWS_PER_WG);
-    const int64_t nc = (cols + 511) / 512;
-#define MXQ_NVFP4_CASE(N)                                                                     \
-    hipLaunchKernelGGL((nvfp4_kernel<N, SCOPED>), grid, block, 0, stream, xa, xb, rows_a, rows, \
-                       cols, ca, cb, ba, bb, ts, scope_amax, rows_per_scope)
-    switch (nc) {
-    case 1: MXQ_NVFP4_CASE(1); break;
-    case 2: MXQ_NVFP4_CASE(2); break;
-    case 3: MXQ_NVFP4_CASE(3); break;
-    case 4: MXQ_NVFP4_CASE(4); break;
-    case 5:
-    case 6: MXQ_NVFP4_CASE(6); break;
-    case 7:
-    case 8: MXQ_NVFP4_CASE(8); break;
-    default: MXQ_NVFP4_CASE(0); break;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 256;
     }
-#undef MXQ_NVFP4_CASE
-    return hipGetLastError();
+    return (int64_t)cus * 4 * per_simd;
+}
+
+static unsigned wg_count(int64_t work_waves, int per_simd)
+{
+    int64_t w = device_waves(per_simd);
+    if (w > work_waves)
+        w = work_waves;
+    return (unsigned)((w + WAVES_PER_WG - 1) / WAVES_PER_WG);
 }
 
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *bs, float *ts, hipStream_t stream)
 {
-    return launch_nvfp4<false>(x, nullptr, rows, rows, cols, codes, nullptr, bs, nullptr, ts,
-                               nullptr, 1, stream);
+    const int64_t nblk = cols >> 4;
+    const int64_t nb = (nblk + 63) / 64;
+    const dim3 block(64 * WAVES_PER_WG);
+    const dim3 grid(wg_count(rows, 4));
+    switch (nb) {
+    case 1: hipLaunchKernelGGL(nvfp4_token_kernel<1>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
+    case 2: hipLaunchKernelGGL(nvfp4_token_kernel<2>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
+    case 3: hipLaunchKernelGGL(nvfp4_token_kernel<3>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
+    case 4: hipLaunchKernelGGL(nvfp4_token_kernel<4>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
+    default: {
+        const dim3 g2((unsigned)((rows + WAVES_PER_WG - 1) / WAVES_PER_WG));
+        hipLaunchKernelGGL(nvfp4_token_long_kernel, g2, block, 0, stream, x, rows, cols, codes, bs, ts);
+    }
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
@@ -369,14 +524,16 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
     const int64_t chunks = (n_scope + AMAX_CHUNK - 1) / AMAX_CHUNK;
     hipLaunchKernelGGL(scope_amax_kernel, dim3((unsigned)(chunks * n_experts)), dim3(256), 0,
                        stream, gate, up, n_per, chunks, amax);
-    const int64_t rows_a = n_experts * rows;
-    const int64_t rows_all = up ? 2 * rows_a : rows_a;
-    hipError_t err = launch_nvfp4<true>(gate, up, rows_a, rows_all, cols, gc, uc, gbs, ubs,
-                                        nullptr, amax, rows, stream);
-    if (err != hipSuccess)
-        return err;
     hipLaunchKernelGGL(scope_finalize_kernel, dim3(small_grid), dim3(256), 0, stream, amax,
                        n_experts);
+    const int64_t nblk = n_experts * n_per / 16;
+    const int64_t bps = n_per / 16;
+    const dim3 grid(wg_count((nblk + 63) / 64, 4)), block(64 * WAVES_PER_WG);
+    hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, gate, nblk, bps,
+                       (const float *)scope_scales, gc, gbs);
+    if (up)
+        hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, up, nblk, bps,
+                           (const float *)scope_scales, uc, ubs);
     return hipGetLastError();
 }
 
