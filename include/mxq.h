@@ -42,8 +42,9 @@
  *
  * Conventions for every entry point:
  *   - Every array is device memory of the current HIP device, allocated and
- *     owned by the caller.  The library allocates nothing and keeps no state
- *     between calls.  Inputs are never modified.
+ *     owned by the caller.  The library allocates no device memory and keeps
+ *     no state between calls beyond a per-process cache of each kernel's
+ *     occupancy.  Inputs are never modified.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue their kernels and return; results are valid once the
  *     stream has been synchronized.  Calls on one stream are ordered.
@@ -172,6 +173,7 @@ int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up,
  *          cols % 16 == 0, rows_per_fp32_scale >= 1.
  *   fp32_scales and rows_per_fp32_scale are ignored for MXFP8 (may be NULL/0).
  *   out [rows][cols] BF16, 16-byte aligned.
+ *   rows * cols must be below 2^36 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
                         const float *fp32_scales, int64_t rows_per_fp32_scale,

@@ -5,7 +5,10 @@
 One hipcc invocation compiles every source under csrc/ into
 ``nvfp4_block_scaled_amax_amd/libmxq.so``.  Packed-FP32 instruction selection
 is disabled (-packed-fp32-ops); division and square root stay IEEE (no
-fast-math); FP32 denormals are kept.
+fast-math); FP32 denormals are kept.  IEEE mode is off (-mno-amdgpu-ieee,
+which requires -fno-honor-nans): it only changes how min/max treat NaN
+operands, so |x| folds into max as a source modifier; NaN inputs are outside
+the quantizers' contract and no kernel produces one from finite inputs.
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ def command(out: str = LIB):
     return ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *sources(), "-o", out]
 

@@ -210,6 +210,8 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
     if (!size_ok(rows, cols) || (fmt == MXQ_FMT_NVFP4 && rows_per_fp32_scale < 1))
         return MXQ_ERR_SIZE;
     const int64_t n = rows * cols;
+    if (n / 16 > (int64_t)0xFFFFFFFF)        // 16-element units are indexed in 32 bits
+        return MXQ_ERR_SIZE;
     if (fmt == MXQ_FMT_NVFP4) {
         if (cols % 16 != 0)
             return MXQ_ERR_SHAPE;

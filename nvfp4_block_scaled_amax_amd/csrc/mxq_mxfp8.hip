@@ -340,18 +340,19 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Wavefronts to launch: enough to fill the device (4 per SIMD) but not more
-// than one per tile, rounded to a multiple of the strip count.
+// Wavefronts to launch: OVERSUBSCRIBE times as many as the device holds at
+// once (measured: more wavefronts in flight keep more loads and stores
+// outstanding than the in-wave prefetch alone), but not more than one per
+// tile, as a whole number of strips.
+constexpr int OVERSUBSCRIBE = 4;
+
+template <bool ROW, bool COL, bool GROUPED>
 static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-        (void)hipGetLastError();
-        cus = 256;
-    }
-    const int64_t target = (int64_t)cus * 16;
-    int64_t slots = target / nct;
+    const int64_t resident =
+        resident_workgroups((const void *)mxfp8_kernel<ROW, COL, GROUPED>, 64 * WAVES_PER_WG) *
+        WAVES_PER_WG * OVERSUBSCRIBE;
+    int64_t slots = resident / nct;
     if (slots < 1)
         slots = 1;
     if (slots > tiles_per_strip)
@@ -359,23 +360,26 @@ static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
     return slots * nct;
 }
 
+template <bool ROW, bool COL, bool GROUPED>
+static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc,
+                             uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
+{
+    const int64_t waves = wave_count<ROW, COL, GROUPED>(G.nct, tiles_per_strip);
+    const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    hipLaunchKernelGGL((mxfp8_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
+                       dim3(64 * WAVES_PER_WG), 0, stream, G, rc, rs, cc, cs);
+    return hipGetLastError();
+}
+
 template <bool GROUPED>
 static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc, uint8_t *rs,
                          uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
-    const int64_t waves = wave_count(G.nct, tiles_per_strip);
-    const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
-    const dim3 grid((unsigned)wgs), block(64 * WAVES_PER_WG);
     if (rc && cc)
-        hipLaunchKernelGGL((mxfp8_kernel<true, true, GROUPED>), grid, block, 0, stream, G, rc, rs,
-                           cc, cs);
-    else if (rc)
-        hipLaunchKernelGGL((mxfp8_kernel<true, false, GROUPED>), grid, block, 0, stream, G, rc, rs,
-                           cc, cs);
-    else
-        hipLaunchKernelGGL((mxfp8_kernel<false, true, GROUPED>), grid, block, 0, stream, G, rc, rs,
-                           cc, cs);
-    return hipGetLastError();
+        return launch_one<true, true, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+    if (rc)
+        return launch_one<true, false, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+    return launch_one<false, true, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
 }
 
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,

@@ -7,9 +7,12 @@
 //
 // Layout.  A lane owns whole 16-element blocks (two 16-byte loads each) and
 // holds them as f32, so a block's amax is an in-lane max (|x| comes free as a
-// source modifier) and its scale work is done once.  Per-token: one wavefront
-// per row, persistent over rows with the next row's loads in flight while the
-// current one is converted; the token amax is a wavefront reduction.  Export:
+// source modifier: the library is built with IEEE mode off, which only
+// changes how min/max treat NaN, and NaN inputs are outside the contract) and
+// its scale work is done once.  Per-token: one wavefront per row, grid-stride
+// over rows with many wavefronts per SIMD (measured faster than prefetching
+// the next row inside a wavefront); the token amax is a wavefront reduction.
+// Export:
 // the tensor is a flat array of blocks (each lies in one scope), 64 blocks per
 // wavefront step, with the scope's FP32 scale computed beforehand.
 //
@@ -58,17 +61,27 @@ __device__ __forceinline__ void zero_blk(Blk &b)
         b.w[i] = 0u;
 }
 
-// Largest |x| of the block, as non-negative f32 bits (compare as integers).
-__device__ __forceinline__ uint32_t blk_amax(const Blk &b)
+// The block's 16 values as f32 (exact) and its largest |x| as non-negative
+// f32 bits.  With IEEE mode off the max takes |x| as a source modifier.
+struct BlkF {
+    float x[16];
+    uint32_t amax;
+};
+
+__device__ __forceinline__ BlkF unpack_blk(const Blk &b)
 {
-    uint32_t m = 0;
+    BlkF f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const uint32_t lo = (b.w[i] << 16) & 0x7FFFFFFFu;
-        const uint32_t hi = b.w[i] & 0x7FFF0000u;
-        m = max(m, max(lo, hi));
+        f.x[2 * i] = bf16_lo(b.w[i]);
+        f.x[2 * i + 1] = bf16_hi(b.w[i]);
     }
-    return m;
+    float m = fmaxf(fabsf(f.x[0]), fabsf(f.x[1]));
+#pragma unroll
+    for (int i = 2; i < 16; i += 2)
+        m = fmaxf(m, fmaxf(fabsf(f.x[i]), fabsf(f.x[i + 1])));
+    f.amax = f2u(m);
+    return f;
 }
 
 // Exact block scale when the bracket straddles a midpoint: blo and blo + 1 are
@@ -121,23 +134,25 @@ __device__ __attribute__((noinline)) uint32_t codes_exact(uint32_t lo, uint32_t 
     return lo;
 }
 
-// The 8 codes of 8 values times r, written with the hardware conversion.
-__device__ __forceinline__ uint32_t codes8(const uint32_t *w, float r)
+// The 8 codes of 8 values times r, written with the hardware conversion.  The
+// four conversions overwrite all four bytes, so the first one's "old" operand
+// can be any value; the first product is used.
+__device__ __forceinline__ uint32_t codes8(const float *x, float r)
 {
-    uint32_t c = 0;
-    c = e2m1_pair<0>(c, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r);
-    c = e2m1_pair<1>(c, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r);
-    c = e2m1_pair<2>(c, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r);
-    c = e2m1_pair<3>(c, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r);
+    const float p0 = x[0] * r;
+    uint32_t c = e2m1_pair<0>(f2u(p0), p0, x[1] * r);
+    c = e2m1_pair<1>(c, x[2] * r, x[3] * r);
+    c = e2m1_pair<2>(c, x[4] * r, x[5] * r);
+    c = e2m1_pair<3>(c, x[6] * r, x[7] * r);
     return c;
 }
 
 // Fast path for one block: codes (two words) and the block scale byte.
-__device__ __forceinline__ void quant_blk_fast(const Blk &blk, uint32_t amax_bits, float s,
+__device__ __forceinline__ void quant_blk_fast(const Blk &blk, const BlkF &f, float s,
                                                float inv_s, float r6_lo, float r6_hi,
                                                uint32_t *b_out, uint32_t *c0, uint32_t *c1)
 {
-    const float A = u2f(amax_bits);
+    const float A = u2f(f.amax);
     const float plo = fminf(A * r6_lo, 448.0f);
     const float phi = fminf(A * r6_hi, 448.0f);
     const uint32_t bb = e4m3_pair_rne(plo, phi);
@@ -153,8 +168,8 @@ __device__ __forceinline__ void quant_blk_fast(const Blk &blk, uint32_t amax_bit
     const float d = e4m3_value(b);
     const float r = __builtin_amdgcn_rcpf(d) * inv_s;
     const float rlo = r * BRACKET_LO, rhi = r * BRACKET_HI;
-    uint32_t lo0 = codes8(blk.w, rlo), hi0 = codes8(blk.w, rhi);
-    uint32_t lo1 = codes8(blk.w + 4, rlo), hi1 = codes8(blk.w + 4, rhi);
+    uint32_t lo0 = codes8(f.x, rlo), hi0 = codes8(f.x, rhi);
+    uint32_t lo1 = codes8(f.x + 8, rlo), hi1 = codes8(f.x + 8, rhi);
     if (lo0 != hi0)
         lo0 = codes_exact(lo0, hi0, blk.w[0], blk.w[1], blk.w[2], blk.w[3], d, s);
     if (lo1 != hi1)
@@ -213,18 +228,18 @@ __device__ __forceinline__ ScaleK scale_k(float s)
 
 // Quantize one block under scale k (any path) and store 8 code bytes and the
 // scale byte.
-__device__ __forceinline__ void emit_blk(const Blk &blk, uint32_t amax_bits, const ScaleK &k,
+__device__ __forceinline__ void emit_blk(const Blk &blk, const BlkF &f, const ScaleK &k,
                                          uint8_t *__restrict__ codes8p, uint8_t *__restrict__ bsp)
 {
     uint32_t b, c0, c1;
     if (k.s >= S_FAST_MIN) {
-        quant_blk_fast(blk, amax_bits, k.s, k.inv_s, k.r6_lo, k.r6_hi, &b, &c0, &c1);
+        quant_blk_fast(blk, f, k.s, k.inv_s, k.r6_lo, k.r6_hi, &b, &c0, &c1);
     } else if (k.s == 0.0f) {
         b = 0u;
         c0 = c1 = 0u;
     } else {
         const BlkOut o = quant_blk_f64(blk.w[0], blk.w[1], blk.w[2], blk.w[3], blk.w[4], blk.w[5],
-                                       blk.w[6], blk.w[7], amax_bits, k.s);
+                                       blk.w[6], blk.w[7], f.amax, k.s);
         b = o.b;
         c0 = o.c0;
         c1 = o.c1;
@@ -237,47 +252,49 @@ __device__ __forceinline__ void emit_blk(const Blk &blk, uint32_t amax_bits, con
 // Per-token kernel: a wavefront per row; block j of the row is held by lane
 // j % 64 in slot j / 64.  NB slots cover rows of up to 1024 * NB elements.
 // ---------------------------------------------------------------------------
-template <int NB>
+// FULL: the row has exactly 64 NB blocks, so no lane is masked.
+template <int NB, bool FULL>
 __device__ __forceinline__ void load_row(Blk (&r)[NB], const uint16_t *__restrict__ xr,
                                          int64_t nblk, int lane)
 {
 #pragma unroll
     for (int j = 0; j < NB; j++) {
         const int64_t blk = 64 * j + lane;
-        if (blk < nblk)
+        if (FULL || blk < nblk)
             load_blk(r[j], xr + 16 * blk);
         else
             zero_blk(r[j]);
     }
 }
 
-template <int NB>
+template <int NB, bool FULL>
 __device__ __forceinline__ void token_row(const Blk (&r)[NB], int64_t row, int64_t cols,
                                           int64_t nblk, int lane, uint8_t *__restrict__ codes,
                                           uint8_t *__restrict__ bs, float *__restrict__ ts)
 {
-    uint32_t am[NB];
+    BlkF f[NB];
     uint32_t A = 0;
 #pragma unroll
     for (int j = 0; j < NB; j++) {
-        am[j] = blk_amax(r[j]);
-        A = max(A, am[j]);
+        f[j] = unpack_blk(r[j]);
+        A = max(A, f[j].amax);
     }
-    A = wave_max_u32(A);
+    A = __builtin_amdgcn_readfirstlane(wave_max_u32(A));
     const float s = u2f(A) / 2688.0f;
     if (lane == 0)
         ts[row] = s;
     const ScaleK k = scale_k(s);
+    uint8_t *crow = codes + row * (cols >> 1);
+    uint8_t *brow = bs + row * (cols >> 4);
 #pragma unroll
     for (int j = 0; j < NB; j++) {
-        const int64_t blk = 64 * j + lane;
-        if (blk < nblk)
-            emit_blk(r[j], am[j], k, codes + row * (cols >> 1) + 8 * blk,
-                     bs + row * (cols >> 4) + blk);
+        const int blk = 64 * j + lane;
+        if (FULL || blk < nblk)
+            emit_blk(r[j], f[j], k, crow + 8 * blk, brow + blk);
     }
 }
 
-template <int NB>
+template <int NB, bool FULL>
 __global__ void __launch_bounds__(256) nvfp4_token_kernel(const uint16_t *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           uint8_t *__restrict__ codes,
@@ -286,27 +303,12 @@ __global__ void __launch_bounds__(256) nvfp4_token_kernel(const uint16_t *__rest
 {
     const int lane = __lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
-    int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
-    if (row >= rows)
-        return;
     const int64_t nblk = cols >> 4;
-    Blk ra[NB], rb[NB];
-    load_row<NB>(ra, x + row * cols, nblk, lane);
-    for (;;) {
-        const int64_t n1 = row + nwaves;
-        if (n1 < rows)
-            load_row<NB>(rb, x + n1 * cols, nblk, lane);
-        token_row<NB>(ra, row, cols, nblk, lane, codes, bs, ts);
-        if (n1 >= rows)
-            break;
-        row = n1;
-        const int64_t n2 = row + nwaves;
-        if (n2 < rows)
-            load_row<NB>(ra, x + n2 * cols, nblk, lane);
-        token_row<NB>(rb, row, cols, nblk, lane, codes, bs, ts);
-        if (n2 >= rows)
-            break;
-        row = n2;
+    for (int64_t row = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group(); row < rows;
+         row += nwaves) {
+        Blk r[NB];
+        load_row<NB, FULL>(r, x + row * cols, nblk, lane);
+        token_row<NB, FULL>(r, row, cols, nblk, lane, codes, bs, ts);
     }
 }
 
@@ -327,7 +329,7 @@ __global__ void __launch_bounds__(256) nvfp4_token_long_kernel(const uint16_t *_
     for (int64_t blk = lane; blk < nblk; blk += 64) {
         Blk b;
         load_blk(b, xr + 16 * blk);
-        A = max(A, blk_amax(b));
+        A = max(A, unpack_blk(b).amax);
     }
     A = wave_max_u32(A);
     const float s = u2f(A) / 2688.0f;
@@ -337,7 +339,7 @@ __global__ void __launch_bounds__(256) nvfp4_token_long_kernel(const uint16_t *_
     for (int64_t blk = lane; blk < nblk; blk += 64) {
         Blk b;
         load_blk(b, xr + 16 * blk);
-        emit_blk(b, blk_amax(b), k, codes + row * (cols >> 1) + 8 * blk,
+        emit_blk(b, unpack_blk(b), k, codes + row * (cols >> 1) + 8 * blk,
                  bs + row * (cols >> 4) + blk);
     }
 }
@@ -417,7 +419,7 @@ __device__ __forceinline__ void scoped_step(const Blk &blk, int64_t t, int lane,
     if (j >= nblk)
         return;
     const ScaleK k = scale_k(scope_s[e]);
-    emit_blk(blk, blk_amax(blk), k, codes + 8 * j, bs + j);
+    emit_blk(blk, unpack_blk(blk), k, codes + 8 * j, bs + j);
 }
 
 __global__ void __launch_bounds__(256) nvfp4_scoped_kernel(const uint16_t *__restrict__ x,
@@ -429,42 +431,15 @@ __global__ void __launch_bounds__(256) nvfp4_scoped_kernel(const uint16_t *__res
     const int lane = __lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
     const int64_t nsteps = (nblk + 63) >> 6;
-    int64_t t = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
-    if (t >= nsteps)
-        return;
-    Blk ba, bb;
-    {
+    for (int64_t t = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group(); t < nsteps;
+         t += nwaves) {
         const int64_t j = 64 * t + lane;
+        Blk b;
         if (j < nblk)
-            load_blk(ba, x + 16 * j);
+            load_blk(b, x + 16 * j);
         else
-            zero_blk(ba);
-    }
-    for (;;) {
-        const int64_t t1 = t + nwaves;
-        if (t1 < nsteps) {
-            const int64_t j1 = 64 * t1 + lane;
-            if (j1 < nblk)
-                load_blk(bb, x + 16 * j1);
-            else
-                zero_blk(bb);
-        }
-        scoped_step(ba, t, lane, nblk, bps, scope_s, codes, bs);
-        if (t1 >= nsteps)
-            break;
-        t = t1;
-        const int64_t t2 = t + nwaves;
-        if (t2 < nsteps) {
-            const int64_t j2 = 64 * t2 + lane;
-            if (j2 < nblk)
-                load_blk(ba, x + 16 * j2);
-            else
-                zero_blk(ba);
-        }
-        scoped_step(bb, t, lane, nblk, bps, scope_s, codes, bs);
-        if (t2 >= nsteps)
-            break;
-        t = t2;
+            zero_blk(b);
+        scoped_step(b, t, lane, nblk, bps, scope_s, codes, bs);
     }
 }
 
@@ -472,23 +447,27 @@ __global__ void __launch_bounds__(256) nvfp4_scoped_kernel(const uint16_t *__res
 // Launchers
 // ---------------------------------------------------------------------------
 
-static int64_t device_waves(int per_simd)
-{
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-        (void)hipGetLastError();
-        cus = 256;
-    }
-    return (int64_t)cus * 4 * per_simd;
-}
+// Workgroups for a grid-stride kernel: OVERSUBSCRIBE times what the device
+// holds at once (measured: more wavefronts in flight keep more loads
+// outstanding than in-wave prefetching), at most one wavefront per unit of
+// work.
+constexpr int OVERSUBSCRIBE = 8;
 
-static unsigned wg_count(int64_t work_waves, int per_simd)
+static unsigned grid_for(const void *kernel, int64_t work_waves)
 {
-    int64_t w = device_waves(per_simd);
+    int64_t w = resident_workgroups(kernel, 64 * WAVES_PER_WG) * WAVES_PER_WG * OVERSUBSCRIBE;
     if (w > work_waves)
         w = work_waves;
     return (unsigned)((w + WAVES_PER_WG - 1) / WAVES_PER_WG);
+}
+
+template <int NB, bool FULL>
+static void launch_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                         uint8_t *bs, float *ts, hipStream_t stream)
+{
+    const dim3 grid(grid_for((const void *)nvfp4_token_kernel<NB, FULL>, rows));
+    hipLaunchKernelGGL((nvfp4_token_kernel<NB, FULL>), grid, dim3(64 * WAVES_PER_WG), 0, stream,
+                       x, rows, cols, codes, bs, ts);
 }
 
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
@@ -496,16 +475,20 @@ hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols,
 {
     const int64_t nblk = cols >> 4;
     const int64_t nb = (nblk + 63) / 64;
-    const dim3 block(64 * WAVES_PER_WG);
-    const dim3 grid(wg_count(rows, 4));
+    const bool full = nblk == 64 * nb;
     switch (nb) {
-    case 1: hipLaunchKernelGGL(nvfp4_token_kernel<1>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
-    case 2: hipLaunchKernelGGL(nvfp4_token_kernel<2>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
-    case 3: hipLaunchKernelGGL(nvfp4_token_kernel<3>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
-    case 4: hipLaunchKernelGGL(nvfp4_token_kernel<4>, grid, block, 0, stream, x, rows, cols, codes, bs, ts); break;
+    case 1: full ? launch_token<1, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_token<1, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 2: full ? launch_token<2, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_token<2, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 3: full ? launch_token<3, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_token<3, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 4: full ? launch_token<4, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_token<4, false>(x, rows, cols, codes, bs, ts, stream); break;
     default: {
         const dim3 g2((unsigned)((rows + WAVES_PER_WG - 1) / WAVES_PER_WG));
-        hipLaunchKernelGGL(nvfp4_token_long_kernel, g2, block, 0, stream, x, rows, cols, codes, bs, ts);
+        hipLaunchKernelGGL(nvfp4_token_long_kernel, g2, dim3(64 * WAVES_PER_WG), 0, stream, x,
+                           rows, cols, codes, bs, ts);
     }
     }
     return hipGetLastError();
@@ -528,7 +511,8 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
                        n_experts);
     const int64_t nblk = n_experts * n_per / 16;
     const int64_t bps = n_per / 16;
-    const dim3 grid(wg_count((nblk + 63) / 64, 4)), block(64 * WAVES_PER_WG);
+    const dim3 grid(grid_for((const void *)nvfp4_scoped_kernel, (nblk + 63) / 64));
+    const dim3 block(64 * WAVES_PER_WG);
     hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, gate, nblk, bps,
                        (const float *)scope_scales, gc, gbs);
     if (up)
