@@ -35,13 +35,32 @@ METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, MXFP8 row+col &
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def csrc_digest() -> str:
+CSRC = os.path.join(ROOT, "nvfp4_block_scaled_amax_amd", "csrc")
+COMMON_SOURCES = ["mxq_device.h", "mxq_launch.h", "mxq_runtime.cpp", "../build.py"]
+KERNEL_SOURCES = {
+    "mxfp8_kernel": ["mxq_mxfp8.hip"],
+    "grouped_prefix_kernel": ["mxq_mxfp8.hip"],
+    "nvfp4_token_kernel": ["mxq_nvfp4.hip"],
+    "nvfp4_scoped_kernel": ["mxq_nvfp4.hip"],
+    "dequant_mxfp8_kernel": ["mxq_dequant.hip"],
+    "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
+}
+
+
+def csrc_digest(files=None) -> str:
+    """Digest of the sources a kernel is built from (all of csrc/ by default)."""
+    if files is None:
+        files = sorted(os.listdir(CSRC)) + ["../build.py"]
     h = hashlib.sha256()
-    d = os.path.join(ROOT, "nvfp4_block_scaled_amax_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_digest(kernel: str) -> str:
+    base = kernel.split("<")[0]
+    return csrc_digest(KERNEL_SOURCES[base] + COMMON_SOURCES)
 
 
 class Leg:
@@ -56,7 +75,7 @@ class Leg:
         return self.bytes_in + self.bytes_out
 
 
-def build_legs(torch, mxq, api, W, log):
+def build_legs(torch, mxq, api, W, log, want=lambda group: True):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     u8 = torch.uint8
     legs = []
@@ -66,8 +85,11 @@ def build_legs(torch, mxq, api, W, log):
         return torch.empty(shape, dtype=dt, device="cuda")
 
     # act / wgt: MXFP8 row+col
-    for name, (rows, cols, x_np) in (("act", (2048, 2048, W.config2_activation("random"))),
-                                     ("wgt", (8192, 2048, W.config2_weight("random")))):
+    for name, rows, cols, gen in (("act", 2048, 2048, W.config2_activation),
+                                  ("wgt", 8192, 2048, W.config2_weight)):
+        if not want(name):
+            continue
+        x_np = gen("random")
         x = dev(x_np)
         rc, rs, cc, cs = empty((rows, cols)), empty((rows, cols // 32)), empty((rows, cols)), \
             empty((rows // 32, cols))
@@ -75,11 +97,24 @@ def build_legs(torch, mxq, api, W, log):
         legs.append(Leg(f"mxfp8_rowcol_{name}",
                         (lambda x=x, rows=rows, cols=cols, rc=rc, rs=rs, cc=cc, cs=cs:
                          E.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs)),
-                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_dense_kernel"],
+                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_kernel<true, true, false>"],
                         f"MXFP8 row+col {rows}x{cols}"))
     log("act/wgt ready")
 
-    # tok: per-token NVFP4 + dequant
+    if want("tok"):
+        build_tok(torch, E, W, legs, dev, empty)
+        log("tok ready")
+    if want("exp"):
+        build_exp(torch, E, W, legs, dev, empty)
+        log("exp ready")
+    if want("grp"):
+        build_grp(torch, E, W, legs, dev, empty)
+        log("grp ready")
+    return legs
+
+
+def build_tok(torch, E, W, legs, dev, empty):
+    """Per-token NVFP4 of 8192x2048 Student-t activations, + dequant."""
     rows, cols = 8192, 2048
     x = dev(W.config3())
     n = rows * cols
@@ -88,13 +123,14 @@ def build_legs(torch, mxq, api, W, log):
     y = empty((rows, cols), torch.bfloat16)
     q_out = n // 2 + n // 16 + 4 * rows
     legs.append(Leg("nvfp4_tok", lambda: E.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts),
-                    2 * n, q_out, n, ["nvfp4_kernel"], "NVFP4 per-token 8192x2048"))
+                    2 * n, q_out, n, ["nvfp4_token_kernel<2, true>"], "NVFP4 per-token 8192x2048"))
     legs.append(Leg("nvfp4_tok_dequant",
                     lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, codes, bs, ts, 1, rows, cols, y),
                     q_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 8192x2048"))
-    log("tok ready")
 
-    # exp: expert export + dequant
+
+def build_exp(torch, E, W, legs, dev, empty):
+    """NVFP4 export of 128 experts (gate/up pairs + down), + dequant."""
     gate, up, down = W.config4()
     g, u, dn = dev(gate), dev(up), dev(down)
     del gate, up, down
@@ -111,12 +147,12 @@ def build_legs(torch, mxq, api, W, log):
     legs.append(Leg("nvfp4_export_gateup",
                     lambda: E.mxq_nvfp4_quantize_gateup_pair(g, u, NE, I, H, gc, gb, uc, ub, sp),
                     2 * 2 * ng, pair_out, 2 * ng,
-                    ["zero_u32_kernel", "scope_amax_kernel", "nvfp4_kernel", "scope_finalize_kernel"],
+                    ["zero_u32_kernel", "scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
                     "NVFP4 gate/up export 128x2x768x2048, shared scale per pair"))
     legs.append(Leg("nvfp4_export_down",
                     lambda: E.mxq_nvfp4_quantize_gateup_pair(dn, None, NE, H, I, dc, db, None, None, sd),
                     2 * ng, down_out, ng,
-                    ["zero_u32_kernel", "scope_amax_kernel", "nvfp4_kernel", "scope_finalize_kernel"],
+                    ["zero_u32_kernel", "scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
                     "NVFP4 down export 128x2048x768"))
 
     def exp_dequant():
@@ -125,9 +161,11 @@ def build_legs(torch, mxq, api, W, log):
         E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, dc, db, sd, H, NE * H, I, yd)
     legs.append(Leg("nvfp4_export_dequant", exp_dequant, pair_out + down_out, 2 * 3 * ng, 3 * ng,
                     ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 of gate, up, down"))
-    log("exp ready")
 
-    # grp: grouped
+
+def build_grp(torch, E, W, legs, dev, empty):
+    """Grouped MXFP8 row+col and NVFP4 over 262144 expert-sorted rows, + dequant."""
+    u8 = torch.uint8
     xg_np, off_np = W.config5()
     R, K = xg_np.shape
     G = off_np.size - 1
@@ -145,45 +183,48 @@ def build_legs(torch, mxq, api, W, log):
     nv_out = n // 2 + n // 16 + 4 * R
     legs.append(Leg("grouped_mxfp8_rowcol",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_MXFP8_ROWCOL, xg, R, K, off, G, g8),
-                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_grouped_kernel"],
+                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_kernel<true, true, true>"],
                     f"grouped MXFP8 row+col {R}x{K}, {G} segments"))
     legs.append(Leg("grouped_nvfp4",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_NVFP4, xg, R, K, off, G, g4),
-                    2 * n + 8 * (G + 1), nv_out, n, ["nvfp4_kernel"],
+                    2 * n + 8 * (G + 1), nv_out, n, ["nvfp4_token_kernel<2, true>"],
                     f"grouped per-token NVFP4 {R}x{K}"))
     y8, y4 = empty((R, K), torch.bfloat16), empty((R, K), torch.bfloat16)
     legs.append(Leg("grouped_dequant_mxfp8",
                     lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_MXFP8_ROW, g8["row_codes"],
                                                   g8["row_scales"], None, 0, R, K, y8),
-                    n + n // 32, 2 * n, n, ["dequant_mxfp8_kernel"], "MXFP8 rowwise -> BF16"))
+                    n + n // 32, 2 * n, n, ["dequant_mxfp8_kernel<false>"], "MXFP8 rowwise -> BF16"))
     legs.append(Leg("grouped_dequant_nvfp4",
                     lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, g4["codes"], g4["block_scales"],
                                                   g4["token_scales"], 1, R, K, y4),
                     nv_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16"))
-    log("grp ready")
-    return legs
+
+
+CPU_SAMPLE_DIV = 1
 
 
 def cpu_baseline(W, log):
-    """The oracle (as it stands) on a bounded sample of every leg: 1/64 of the
-    rows (1/64 of the experts for the export), timed on the host cores."""
+    """The oracle (as it stands) on a bounded sample of the workload: 1/D of
+    every leg's rows (1/D of the experts for the export; D = CPU_SAMPLE_DIV,
+    1 = one whole step, about 15 s on 16 host cores), timed on the host cores.
+    Input generation is outside the timed region."""
     import oracle
     if not os.path.exists(oracle._LIB):
         oracle.build()
+    D = CPU_SAMPLE_DIV
+    wgt = W.config2_weight("random")[:8192 // D]
+    act = W.config2_activation("random")[:2048 // D]
+    tok = W.config3()[:8192 // D]
+    gate, up, down = W.config4(128 // D)
+    xg = W.student_t_activations(262144 // D, 2048, 5)
     total_bytes, t0 = 0, time.perf_counter()
-    x = W.config2_weight("random")[:128]
-    oracle.mxfp8_rowwise(x)
-    oracle.mxfp8_colwise(x)
-    total_bytes += x.size * 4 + x.size // 16
-    a = W.config2_activation("random")[:32]
-    oracle.mxfp8_rowwise(a)
-    oracle.mxfp8_colwise(a)
-    total_bytes += a.size * 4 + a.size // 16
-    t = W.config3()[:128]
-    c, b, s = oracle.nvfp4_per_token(t)
+    for x in (wgt, act):
+        oracle.mxfp8_rowwise(x)
+        oracle.mxfp8_colwise(x)
+        total_bytes += x.size * 4 + x.size // 16
+    c, b, s = oracle.nvfp4_per_token(tok)
     oracle.dequant_nvfp4(c, b, s, 1)
-    total_bytes += 2 * (2 * t.size + t.size // 2 + t.size // 16 + 4 * 128)
-    gate, up, down = W.config4(2)
+    total_bytes += 2 * (2 * tok.size + tok.size // 2 + tok.size // 16 + 4 * tok.shape[0])
     gc, gb, uc, ub, sp = oracle.nvfp4_gateup_pair(gate, up)
     dc, db, _, _, sd = oracle.nvfp4_gateup_pair(down, None)
     oracle.dequant_nvfp4(gc.reshape(-1, 1024), gb.reshape(-1, 128), sp, 768)
@@ -191,7 +232,6 @@ def cpu_baseline(W, log):
     oracle.dequant_nvfp4(dc.reshape(-1, 384), db.reshape(-1, 48), sd, 2048)
     ng = gate.size
     total_bytes += 2 * (3 * 2 * ng + 3 * (ng // 2 + ng // 16))
-    xg = W.student_t_activations(4096, 2048, 5)
     rc, rs = oracle.mxfp8_rowwise(xg)
     oracle.mxfp8_colwise(xg)
     c, b, s = oracle.nvfp4_per_token(xg)
@@ -204,9 +244,10 @@ def cpu_baseline(W, log):
     log(f"cpu baseline: {total_bytes / 1e9:.3f} GB in {dt:.1f} s")
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": ("1/64 of each leg's rows (128 weight rows, 32 activation rows, 128 "
-                       "tokens, 2 of 128 experts, 4096 of 262144 grouped rows; generation "
-                       "excluded)"),
+            "sample": (f"1/{D} of each leg (one pass of the oracle over every leg of the step "
+                       f"at 1/{D} of its rows): {8192 // D} weight rows, {2048 // D} activation "
+                       f"rows, {8192 // D} tokens, {128 // D} of 128 experts, {262144 // D} "
+                       "grouped rows (one expert segment); input generation excluded"),
             "seconds": round(dt, 2), "bytes": total_bytes}
 
 
@@ -217,6 +258,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--groups", default="act,wgt,tok,exp,grp",
+                    help="comma list of leg groups to run (for profiling single kernels)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also time a plain elementwise copy of this many MiB (int32 bitwise "
+                         "not, reads and writes each byte once), reported apart from the step, "
+                         "to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
 
     def log(msg):
@@ -236,7 +283,15 @@ def main():
     mxq.lib()
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    legs = build_legs(torch, mxq, api, W, log)
+    groups = set(args.groups.split(","))
+    legs = build_legs(torch, mxq, api, W, log, want=lambda g: g in groups)
+    calib = None
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        calib = Leg("copy_calibration", lambda: torch.bitwise_not(src, out=dst), nbytes, nbytes,
+                    nbytes // 4, ["elementwise_kernel"], f"int32 bitwise not of {nbytes} bytes")
     log(f"inputs generated and resident in {time.perf_counter() - t_gen:.1f} s")
 
     stream = torch.cuda.current_stream()
@@ -257,6 +312,10 @@ def main():
         leg._ev = []
     for _ in range(args.warmup):
         step(False)
+    if calib is not None:
+        calib._ev = []
+        for _ in range(args.warmup):
+            calib.launch()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
@@ -269,6 +328,15 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if calib is not None:
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            calib.launch()
+            b.record(stream)
+            calib._ev.append((a, b))
+        torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s)")
@@ -276,28 +344,32 @@ def main():
     total_bytes = sum(l.bytes for l in legs)
     total_elems = sum(l.elems for l in legs)
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
-    leg_info = {}
-    for l in legs:
+    def info(l):
         ts = [a.elapsed_time(b) for a, b in l._ev]
         ms = float(np.mean(ts))
         gbs = l.bytes / (ms * 1e-3) / 1e9
-        leg_info[l.name] = {"desc": l.desc, "ms": round(ms, 5), "ms_min": round(float(np.min(ts)), 5),
-                            "bytes": l.bytes, "GB_s": round(gbs, 1),
-                            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                            "elements_per_s": round(l.elems / (ms * 1e-3), 1)}
+        return {"desc": l.desc, "kernels": l.kernels, "ms": round(ms, 5),
+                "ms_min": round(float(np.min(ts)), 5), "bytes": l.bytes, "GB_s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "elements_per_s": round(l.elems / (ms * 1e-3), 1)}
+
+    leg_info = {l.name: info(l) for l in legs}
     dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
     dom_ms = leg_info[dom.name]["ms"]
     achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated
+    # against a plain copy; null once the kernel's sources have changed.
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("csrc_digest") == csrc_digest() and tr.get("leg") == dom.name:
+            tr = json.load(f).get("kernels", {}).get(dom.kernels[-1])
+        if tr and tr.get("source_digest") == kernel_digest(dom.kernels[-1]) \
+                and tr.get("leg") == dom.name:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom.kernels[-1], "leg": dom.name, "algorithmic_bytes": dom.bytes,
-                "ms_per_launch": dom_ms}
+                "kernel": dom.kernels[-1], "leg": dom.name, "leg_kernels": dom.kernels,
+                "algorithmic_bytes": dom.bytes, "ms_per_launch": dom_ms}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -312,12 +384,14 @@ def main():
                                "per-token NVFP4 8192x2048 + dequant, NVFP4 export of 128 "
                                "experts (gate/up pairs + down) + dequant, grouped MXFP8 row+col "
                                "+ NVFP4 over 262144x2048 top-8/128 + dequant",
-                   "bytes_per_step": total_bytes, "elements_per_step": total_elems},
+                   "groups": sorted(groups), "bytes_per_step": total_bytes,
+                   "elements_per_step": total_elems},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "elements_per_s": round(total_elems / (ms_per_step * 1e-3), 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": leg_info,
+        "copy_calibration": info(calib) if calib is not None else None,
         "csrc_digest": csrc_digest(),
     }
     print(json.dumps(line), flush=True)
