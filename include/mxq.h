@@ -127,6 +127,7 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols,
  *   codes        [rows][cols/2] packed E2M1, 16-byte aligned.
  *   block_scales [rows][cols/16] E4M3.
  *   token_scales [rows] FP32: s_t = fp32(amax_t / 2688), the decode multiplier.
+ *   rows must be below 2^31 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *codes, uint8_t *block_scales,
@@ -150,6 +151,7 @@ int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
  *                        the call and holding s_e = fp32(amax_e / 2688) when
  *                        it completes.
  *   up, up_codes and up_block_scales must be all NULL or all non-NULL.
+ *   n_experts * rows * cols must be below 2^36 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up,
                                    int64_t n_experts, int64_t rows, int64_t cols,
@@ -216,6 +218,7 @@ typedef struct {
  *   seg_offsets   device int64 [n_groups + 1], 0 = o_0 <= ... <= o_G =
  *                 total_rows (read on the device; not validated on the host).
  *   out           host pointer to the output struct (device arrays inside).
+ *   For NVFP4, total_rows must be below 2^31 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
                          int64_t cols, const int64_t *seg_offsets,

@@ -21,6 +21,8 @@ struct Buf {
 };
 
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 62;
+constexpr int64_t MAX_GRID_ROWS = 0x7FFFFFFF;     // per-token NVFP4: one workgroup per row
+constexpr int64_t MAX_BLOCKS = 0xFFFFFFFF;        // 16-element blocks indexed in 32 bits
 
 bool size_ok(int64_t a, int64_t b)
 {
@@ -149,7 +151,7 @@ int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, 
 {
     if (!x || !codes || !block_scales || !token_scales)
         return MXQ_ERR_NULL;
-    if (!size_ok(rows, cols))
+    if (!size_ok(rows, cols) || rows > MAX_GRID_ROWS)
         return MXQ_ERR_SIZE;
     if (cols % 16 != 0)
         return MXQ_ERR_SHAPE;
@@ -180,6 +182,8 @@ int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up, int
     if (cols % 16 != 0)
         return MXQ_ERR_SHAPE;
     const int64_t n = n_experts * rows * cols;
+    if (n / 16 > MAX_BLOCKS)
+        return MXQ_ERR_SIZE;
     Buf b[7];
     int k = 0;
     b[k++] = {gate, 2 * n, 16, false};
@@ -210,7 +214,7 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
     if (!size_ok(rows, cols) || (fmt == MXQ_FMT_NVFP4 && rows_per_fp32_scale < 1))
         return MXQ_ERR_SIZE;
     const int64_t n = rows * cols;
-    if (n / 16 > (int64_t)0xFFFFFFFF)        // 16-element units are indexed in 32 bits
+    if (n / 16 > MAX_BLOCKS)
         return MXQ_ERR_SIZE;
     if (fmt == MXQ_FMT_NVFP4) {
         if (cols % 16 != 0)
@@ -252,6 +256,8 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t
     if (fmt == MXQ_FMT_NVFP4) {
         if (!out->codes || !out->block_scales || !out->token_scales)
             return MXQ_ERR_NULL;
+        if (total_rows > MAX_GRID_ROWS)
+            return MXQ_ERR_SIZE;
         if (cols % 16 != 0)
             return MXQ_ERR_SHAPE;
         const Buf b[5] = {{x, 2 * n, 16, false},

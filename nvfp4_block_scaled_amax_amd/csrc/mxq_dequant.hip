@@ -3,10 +3,14 @@
 // per-token NVFP4 RL on Blackwell").  y = BF16(dec(code) * dec(scale) [* s]),
 // rounded once from the exact product, ties to even, saturating at 0x7F7F.
 //
-// Work unit: 16 consecutive elements of the flattened [rows][cols] array
-// (cols is a multiple of 16, so the 16 share a row, and for NVFP4 a block):
-// one 16-byte (MXFP8) or 8-byte (NVFP4) code load, 32 bytes of BF16 out.
-// Grid-stride over units with many wavefronts per SIMD.
+// Work layout: each wavefront takes 1024 consecutive elements of the flattened
+// [rows][cols] array per step; lane l converts the 8-element chunks starting
+// at 8l and 512 + 8l (cols is a multiple of 16, so a chunk never straddles a
+// row or an NVFP4 block).  Every 16-byte store instruction of the wave then
+// covers 1 KiB of contiguous output, whole cache lines: 32 contiguous bytes
+// per lane would leave each store instruction writing half lines, which the
+// streaming stores turn into extra HBM write traffic.  Grid-stride over
+// wave steps.
 //
 // MXFP8.  dec(c) 2^e has at most 4 significant bits, so it is a BF16 value
 // unless it lies below the BF16 normal range or overflows.  One
@@ -32,7 +36,11 @@
 namespace mxq {
 
 constexpr int WAVES_PER_WG = 4;
-constexpr int OVERSUBSCRIBE = 8;
+// Grid size in multiples of the resident workgroups (0: one wave step per
+// wavefront, the whole array in one launch wave).  Measured on the 262144 x
+// 2048 grouped shape.
+constexpr int MXFP8_OVERSUBSCRIBE = 0;
+constexpr int NVFP4_OVERSUBSCRIBE = 16;
 constexpr float NV_FAST_MIN_S = 0x1p-100f;
 constexpr float BF16_MAX = 0x1.FEp127f;
 
@@ -70,74 +78,85 @@ __device__ __forceinline__ uint32_t any_byte_ge247(uint32_t w)
     return (((w & 0x7F7F7F7Fu) + 0x09090909u) & w & 0x80808080u) != 0u;
 }
 
-// Unsigned division of n < 2^32 by a fixed d via a multiply and a shift
-// (round-up method: m = floor(2^32 (2^l - d) / d) + 1, l = ceil(log2 d)).
-struct Div {
-    uint32_t m, l;
-};
-__device__ __forceinline__ uint32_t udiv(uint32_t n, Div d)
+constexpr int64_t WAVE_SPAN = 1024;     // elements per wavefront step
+constexpr int64_t HALF_SPAN = 512;
+
+// Eight BF16 (16 bytes) of one MXFP8 chunk: codes cw (8 bytes), scales sw
+// (one byte per element for the columnwise layout, else the chunk's one
+// scale byte in every byte).
+template <bool COL>
+__device__ __forceinline__ u32x4_t mx_chunk(uint2 cq, uint2 sq)
 {
-    return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
+    const uint32_t cw[2] = {cq.x, cq.y}, sw[2] = {sq.x, sq.y};
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const uint32_t c = cw[j], s = sw[j];
+        if constexpr (!COL) {
+            o[2 * j] = mx_pair<false>(c, (s & 0xFFu) << 23);
+            o[2 * j + 1] = mx_pair<true>(c, (s & 0xFFu) << 23);
+        } else {
+            // Each conversion applies one scale to both codes of a pair:
+            // convert under each element's scale and keep its half.
+            const uint32_t lo_a = mx_pair<false>(c, (s & 0xFFu) << 23);
+            const uint32_t lo_b = mx_pair<false>(c, ((s >> 8) & 0xFFu) << 23);
+            const uint32_t hi_a = mx_pair<true>(c, ((s >> 16) & 0xFFu) << 23);
+            const uint32_t hi_b = mx_pair<true>(c, (s >> 24) << 23);
+            o[2 * j] = __builtin_amdgcn_perm(lo_b, lo_a, 0x07060100u);
+            o[2 * j + 1] = __builtin_amdgcn_perm(hi_b, hi_a, 0x07060100u);
+        }
+    }
+    if (any_byte_ge247(sw[0]) | any_byte_ge247(sw[1])) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const uint32_t c = cw[j], s = sw[j];
+            o[2 * j] = pack2(mx_deq1_exact(c & 0xFF, s & 0xFF),
+                             mx_deq1_exact((c >> 8) & 0xFF, (s >> 8) & 0xFF));
+            o[2 * j + 1] = pack2(mx_deq1_exact((c >> 16) & 0xFF, (s >> 16) & 0xFF),
+                                 mx_deq1_exact(c >> 24, s >> 24));
+        }
+    }
+    return o;
 }
 
+// COL == false: scales[row][cols/32]; COL == true: scales[row/32][cols].
+// n = rows * cols elements; per_row16 divides by cols / 16.
 template <bool COL>
 __global__ void __launch_bounds__(256) dequant_mxfp8_kernel(const uint8_t *__restrict__ codes,
                                                             const uint8_t *__restrict__ scales,
-                                                            int64_t units, int64_t cols,
-                                                            Div per_row, uint16_t *__restrict__ out)
+                                                            int64_t n, int64_t cols,
+                                                            Div per_row16, uint32_t nwg,
+                                                            uint16_t *__restrict__ out)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-        const int64_t f = u * 16;
-        const uint4 cq = ld_nt16(codes + f);
-        const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
-        uint32_t o[8];
-        if constexpr (!COL) {
-            const uint32_t b = scales[f >> 5];
-            const uint32_t sbits = b << 23;
+    const int64_t lane8 = (tid() & 63) * 8;
+    const int64_t waves = (int64_t)nwg * WAVES_PER_WG;
+    for (int64_t w = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group(); w * WAVE_SPAN < n;
+         w += waves) {
+        int64_t f[2];
+        uint2 cq[2], sq[2];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                o[2 * j] = mx_pair<false>(cw[j], sbits);
-                o[2 * j + 1] = mx_pair<true>(cw[j], sbits);
-            }
-            if (b >= 247u) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    o[2 * j] = pack2(mx_deq1_exact(cw[j] & 0xFF, b),
-                                     mx_deq1_exact((cw[j] >> 8) & 0xFF, b));
-                    o[2 * j + 1] = pack2(mx_deq1_exact((cw[j] >> 16) & 0xFF, b),
-                                         mx_deq1_exact(cw[j] >> 24, b));
-                }
-            }
-        } else {
-            const uint32_t row = udiv((uint32_t)u, per_row);
-            const int64_t k = f - (int64_t)row * cols;
-            const uint4 sq = ld16(scales + (int64_t)(row >> 5) * cols + k);
-            const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t s = sw[j];
-                const uint32_t lo_a = mx_pair<false>(cw[j], (s & 0xFFu) << 23);
-                const uint32_t lo_b = mx_pair<false>(cw[j], ((s >> 8) & 0xFFu) << 23);
-                const uint32_t hi_a = mx_pair<true>(cw[j], ((s >> 16) & 0xFFu) << 23);
-                const uint32_t hi_b = mx_pair<true>(cw[j], (s >> 24) << 23);
-                o[2 * j] = __builtin_amdgcn_perm(lo_b, lo_a, 0x07060100u);
-                o[2 * j + 1] = __builtin_amdgcn_perm(hi_b, hi_a, 0x07060100u);
-            }
-            if (any_byte_ge247(sw[0]) | any_byte_ge247(sw[1]) | any_byte_ge247(sw[2]) |
-                any_byte_ge247(sw[3])) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t c = cw[j], s = sw[j];
-                    o[2 * j] = pack2(mx_deq1_exact(c & 0xFF, s & 0xFF),
-                                     mx_deq1_exact((c >> 8) & 0xFF, (s >> 8) & 0xFF));
-                    o[2 * j + 1] = pack2(mx_deq1_exact((c >> 16) & 0xFF, (s >> 16) & 0xFF),
-                                         mx_deq1_exact(c >> 24, s >> 24));
+        for (int h = 0; h < 2; h++) {
+            f[h] = w * WAVE_SPAN + h * HALF_SPAN + lane8;
+            cq[h] = make_uint2(0, 0);
+            sq[h] = make_uint2(0, 0);
+            if (f[h] < n) {
+                cq[h] = ld_nt8(codes + f[h]);
+                if constexpr (COL) {
+                    const uint32_t row = udiv((uint32_t)(f[h] >> 4), per_row16);
+                    const int64_t k = f[h] - (int64_t)row * cols;
+                    sq[h] = ld8(scales + (int64_t)(row >> 5) * cols + k);
+                } else {
+                    const uint32_t b = scales[f[h] >> 5] * 0x01010101u;
+                    sq[h] = make_uint2(b, b);
                 }
             }
         }
-        st_nt16(out + f, o[0], o[1], o[2], o[3]);
-        st_nt16(out + f + 8, o[4], o[5], o[6], o[7]);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const u32x4_t o = mx_chunk<COL>(cq[h], sq[h]);
+            if (f[h] < n)
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + f[h]));
+        }
     }
 }
 
@@ -175,37 +194,62 @@ __device__ __attribute__((noinline)) uint32_t nv_pair_exact(uint32_t byte, float
                  bf16_from_f64((double)v[1] * (double)d * (double)s));
 }
 
+// Eight BF16 (16 bytes) of one NVFP4 chunk: 8 codes (4 bytes) of a block
+// with decoded block scale d under FP32 scale s.
+__device__ __forceinline__ u32x4_t nv_chunk(uint32_t cw, float d, float s)
+{
+    u32x4_t o;
+    const bool fast = s >= NV_FAST_MIN_S && fabsf((6.0f * d) * s) <= BF16_MAX &&
+                      !bf16_tie_hazard(d, s) && !bf16_tie_hazard(3.0f * d, s);
+    if (fast) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float2_t v = e2m1_values((cw >> (8 * j)) & 0xFFu);
+            const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
+            o[j] = __builtin_bit_cast(uint32_t, r);
+        }
+    } else {
+        for (int j = 0; j < 4; j++)
+            o[j] = nv_pair_exact((cw >> (8 * j)) & 0xFFu, d, s);
+    }
+    return o;
+}
+
+// n = rows * cols elements; per_scale divides a block index by the blocks
+// per FP32 scale.
 __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__restrict__ codes,
                                                             const uint8_t *__restrict__ bscales,
                                                             const float *__restrict__ fp32_scales,
-                                                            int64_t units, Div per_scale,
+                                                            int64_t n, Div per_scale,
+                                                            uint32_t nwg,
                                                             uint16_t *__restrict__ out)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-        const uint2 cq = *reinterpret_cast<const uint2 *>(codes + u * 8);
-        const float d = e4m3_value(bscales[u]);
-        const float s = fp32_scales[udiv((uint32_t)u, per_scale)];
-        uint32_t o[8];
-        const bool fast = s >= NV_FAST_MIN_S && fabsf((6.0f * d) * s) <= BF16_MAX &&
-                          !bf16_tie_hazard(d, s) && !bf16_tie_hazard(3.0f * d, s);
-        if (fast) {
-            const uint32_t cw[2] = {cq.x, cq.y};
+    const int64_t lane8 = (tid() & 63) * 8;
+    const int64_t waves = (int64_t)nwg * WAVES_PER_WG;
+    for (int64_t w = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group(); w * WAVE_SPAN < n;
+         w += waves) {
+        int64_t f[2];
+        uint32_t cw[2];
+        float d[2], s[2];
 #pragma unroll
-            for (int w = 0; w < 2; w++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float2_t v = e2m1_values((cw[w] >> (8 * j)) & 0xFFu);
-                    const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
-                    o[4 * w + j] = __builtin_bit_cast(uint32_t, r);
-                }
-        } else {
-            const uint32_t cw[2] = {cq.x, cq.y};
-            for (int i = 0; i < 8; i++)
-                o[i] = nv_pair_exact((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu, d, s);
+        for (int h = 0; h < 2; h++) {
+            f[h] = w * WAVE_SPAN + h * HALF_SPAN + lane8;
+            cw[h] = 0;
+            d[h] = 0.0f;
+            s[h] = 0.0f;
+            if (f[h] < n) {
+                const int64_t blk = f[h] >> 4;
+                cw[h] = ld_nt4(codes + (f[h] >> 1));
+                d[h] = e4m3_value(bscales[blk]);
+                s[h] = fp32_scales[udiv((uint32_t)blk, per_scale)];
+            }
         }
-        st_nt16(out + u * 16, o[0], o[1], o[2], o[3]);
-        st_nt16(out + u * 16 + 8, o[4], o[5], o[6], o[7]);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const u32x4_t o = nv_chunk(cw[h], d[h], s[h]);
+            if (f[h] < n)
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + f[h]));
+        }
     }
 }
 
@@ -213,36 +257,37 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__res
 // Launchers
 // ---------------------------------------------------------------------------
 
-static Div make_div(uint32_t d)
-{
-    uint32_t l = 0;
-    while (((uint64_t)1 << l) < d)
-        l++;
-    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
-    return Div{(uint32_t)m, l};
-}
-
 template <class K>
-static unsigned grid_for(K kernel, int64_t units)
+static unsigned grid_for(K kernel, int64_t n, int oversubscribe)
 {
-    int64_t wgs = resident_workgroups((const void *)kernel, 256) * OVERSUBSCRIBE;
-    const int64_t need = (units + 255) / 256;
-    if (wgs > need)
-        wgs = need;
+    const int64_t need = (n + WAVE_SPAN * WAVES_PER_WG - 1) / (WAVE_SPAN * WAVES_PER_WG);
+    int64_t wgs = need;
+    if (oversubscribe > 0) {
+        const int64_t cap = resident_workgroups((const void *)kernel, 64 * WAVES_PER_WG) *
+                            oversubscribe;
+        if (wgs > cap)
+            wgs = cap;
+    }
+    if (wgs > 0x7FFFFFFF)       // grid-stride covers the rest
+        wgs = 0x7FFFFFFF;
     return (unsigned)(wgs < 1 ? 1 : wgs);
 }
 
 hipError_t launch_dequant_mxfp8(bool col, const uint8_t *codes, const uint8_t *scales,
                                 int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream)
 {
-    const int64_t units = rows * cols / 16;     // < 2^32: checked by the caller
-    const Div per_row = make_div((uint32_t)(cols / 16));
-    if (col)
-        hipLaunchKernelGGL((dequant_mxfp8_kernel<true>), dim3(grid_for(dequant_mxfp8_kernel<true>, units)),
-                           dim3(256), 0, stream, codes, scales, units, cols, per_row, out);
-    else
-        hipLaunchKernelGGL((dequant_mxfp8_kernel<false>), dim3(grid_for(dequant_mxfp8_kernel<false>, units)),
-                           dim3(256), 0, stream, codes, scales, units, cols, per_row, out);
+    const int64_t n = rows * cols;              // n / 16 < 2^32: checked by the caller
+    const Div per_row16 = make_div((uint32_t)(cols / 16));
+    const dim3 block(64 * WAVES_PER_WG);
+    if (col) {
+        const unsigned g = grid_for(dequant_mxfp8_kernel<true>, n, MXFP8_OVERSUBSCRIBE);
+        hipLaunchKernelGGL((dequant_mxfp8_kernel<true>), dim3(g), block, 0, stream, codes, scales,
+                           n, cols, per_row16, g, out);
+    } else {
+        const unsigned g = grid_for(dequant_mxfp8_kernel<false>, n, MXFP8_OVERSUBSCRIBE);
+        hipLaunchKernelGGL((dequant_mxfp8_kernel<false>), dim3(g), block, 0, stream, codes,
+                           scales, n, cols, per_row16, g, out);
+    }
     return hipGetLastError();
 }
 
@@ -250,11 +295,13 @@ hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *bscales, co
                                 int64_t rows_per_scale, int64_t rows, int64_t cols, uint16_t *out,
                                 hipStream_t stream)
 {
-    const int64_t units = rows * cols / 16;     // < 2^32: checked by the caller
-    const int64_t per = (cols / 16) * rows_per_scale;   // units per FP32 scale
-    const Div per_scale = make_div((uint32_t)(per < units ? per : units));
-    hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3(grid_for(dequant_nvfp4_kernel, units)), dim3(256),
-                       0, stream, codes, bscales, fs, units, per_scale, out);
+    const int64_t n = rows * cols;              // n / 16 < 2^32: checked by the caller
+    const int64_t blocks = n / 16;
+    const int64_t per = (cols / 16) * rows_per_scale;   // blocks per FP32 scale
+    const Div per_scale = make_div((uint32_t)(per < blocks ? per : blocks));
+    const unsigned g = grid_for(dequant_nvfp4_kernel, n, NVFP4_OVERSUBSCRIBE);
+    hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3(g), dim3(64 * WAVES_PER_WG), 0, stream, codes,
+                       bscales, fs, n, per_scale, g, out);
     return hipGetLastError();
 }
 

@@ -52,11 +52,27 @@ __device__ __forceinline__ uint32_t hmax_u16(uint32_t a)
     return lo > hi ? lo : hi;
 }
 
+// Work-item, workgroup and lane indices straight from the hardware (the HIP
+// blockIdx / threadIdx / gridDim accessors and __umulhi are device-library
+// functions built with IEEE mode on, which the compiler will not inline into
+// this library's IEEE-off kernels: each use would be a call).  Grid-stride
+// kernels take their grid size as an argument.
+__device__ __forceinline__ uint32_t tid() { return __builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ uint32_t wg_id() { return __builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ uint32_t lane_id()
+{
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ __forceinline__ uint32_t mulhi(uint32_t a, uint32_t b)
+{
+    return (uint32_t)(((uint64_t)a * b) >> 32);
+}
+
 // Index of this wavefront within its workgroup, as a wave-uniform value (so
 // that everything derived from it lives in scalar registers).
 __device__ __forceinline__ int wave_in_group()
 {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    return __builtin_amdgcn_readfirstlane((int)(tid() >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -254,6 +270,39 @@ __device__ __forceinline__ uint4 ld16(const void *p)
 {
     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// Unsigned division of n < 2^32 by a fixed d via a multiply and a shift
+// (round-up method: m = floor(2^32 (2^l - d) / d) + 1, l = ceil(log2 d)),
+// exact for every n < 2^32 and 1 <= d < 2^32.
+struct Div {
+    uint32_t m, l;
+};
+__device__ __forceinline__ uint32_t udiv(uint32_t n, Div d)
+{
+    return (uint32_t)(((uint64_t)mulhi(n, d.m) + n) >> d.l);
+}
+static inline Div make_div(uint32_t d)
+{
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d)
+        l++;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return Div{(uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint2 ld_nt8(const void *p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint2 ld8(const void *p)
+{
+    const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
+    return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
 __device__ __forceinline__ void st_nt16(void *p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {

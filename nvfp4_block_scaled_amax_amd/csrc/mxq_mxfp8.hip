@@ -181,6 +181,7 @@ struct Geometry {
     const int64_t *off;    // grouped: segment offsets
     const int64_t *P;      // grouped: prefix of ceil(n_e / 32)
     int64_t n_groups;
+    int64_t nwaves;        // wavefronts in the grid
 };
 
 // Segment e's rows clamped into [0, total_rows): offsets are device data the
@@ -236,10 +237,10 @@ __global__ void __launch_bounds__(256) mxfp8_kernel(Geometry G, uint8_t *__restr
                                                     uint8_t *__restrict__ cc,
                                                     uint8_t *__restrict__ cs)
 {
-    const int lane = __lane_id();
+    const int lane = (int)lane_id();
     const int g = lane & 15, rg = lane >> 4;
-    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + wave_in_group();
-    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t wave = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group();
+    const int64_t nwaves = G.nwaves;
     // Strip and tile range of this wavefront.
     const int64_t strip = wave % G.nct;
     const int64_t slot = wave / G.nct, nslots = nwaves / G.nct;
@@ -311,28 +312,28 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
     __shared__ int64_t part[256];
     int64_t carry = 0;
     for (int64_t base = 0; base < n_groups; base += 256) {
-        const int64_t e = base + threadIdx.x;
+        const int64_t e = base + tid();
         int64_t n = 0;
         if (e < n_groups) {
             int64_t lo, hi;
             segment_rows(off, e, total_rows, &lo, &hi);
             n = (hi - lo + 31) >> 5;
         }
-        part[threadIdx.x] = n;
+        part[tid()] = n;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {
-            const int64_t add = threadIdx.x >= (unsigned)d ? part[threadIdx.x - d] : 0;
+            const int64_t add = tid() >= (unsigned)d ? part[tid() - d] : 0;
             __syncthreads();
-            part[threadIdx.x] += add;
+            part[tid()] += add;
             __syncthreads();
         }
         if (e < n_groups)
-            P[e] = carry + part[threadIdx.x] - n;   // exclusive
+            P[e] = carry + part[tid()] - n;   // exclusive
         const int64_t total = part[255];
         __syncthreads();
         carry += total;
     }
-    if (threadIdx.x == 0)
+    if (tid() == 0)
         P[n_groups] = carry;
 }
 
@@ -344,7 +345,7 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // once (measured: more wavefronts in flight keep more loads and stores
 // outstanding than the in-wave prefetch alone), but not more than one per
 // tile, as a whole number of strips.
-constexpr int OVERSUBSCRIBE = 4;
+constexpr int OVERSUBSCRIBE = 16;
 
 template <bool ROW, bool COL, bool GROUPED>
 static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
@@ -366,8 +367,10 @@ static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t
 {
     const int64_t waves = wave_count<ROW, COL, GROUPED>(G.nct, tiles_per_strip);
     const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    Geometry g = G;
+    g.nwaves = wgs * WAVES_PER_WG;
     hipLaunchKernelGGL((mxfp8_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
-                       dim3(64 * WAVES_PER_WG), 0, stream, G, rc, rs, cc, cs);
+                       dim3(64 * WAVES_PER_WG), 0, stream, g, rc, rs, cc, cs);
     return hipGetLastError();
 }
 
@@ -385,7 +388,7 @@ static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
                               uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
-    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0};
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0, 0};
     return launch<false>(G, (rows + TILE_ROWS - 1) / TILE_ROWS, rc, rs, cc, cs, stream);
 }
 
@@ -400,7 +403,7 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
         return err;
     const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
-               n_groups};
+               n_groups, 0};
     return launch<true>(G, max_tiles, rc, rs, cc, cs, stream);
 }
 
