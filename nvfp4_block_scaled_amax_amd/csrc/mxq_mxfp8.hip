@@ -303,6 +303,67 @@ __global__ void __launch_bounds__(256) mxfp8_kernel(Geometry G, uint8_t *__restr
     }
 }
 
+// Segment of tile T (grouped): the e with P[e] <= T < P[e + 1], by binary
+// search (T is wave-uniform, so the loads are scalar).
+__device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, int64_t n_groups,
+                                                int64_t T)
+{
+    int64_t lo = 0, hi = n_groups - 1;          // P[lo] <= T always (P[0] = 0)
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (P[mid] <= T)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
+// the four wavefronts of a workgroup cover 512 consecutive columns of one
+// 32-row band.  Launched over all tiles at once.
+template <bool ROW, bool COL, bool GROUPED>
+__global__ void __launch_bounds__(256) mxfp8_tile_kernel(Geometry G, uint8_t *__restrict__ rc,
+                                                         uint8_t *__restrict__ rs,
+                                                         uint8_t *__restrict__ cc,
+                                                         uint8_t *__restrict__ cs)
+{
+    const int lane = (int)lane_id();
+    const int g = lane & 15, rg = lane >> 4;
+    const int64_t wave = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group();
+    const int64_t strip = wave % G.nct, T = wave / G.nct;
+    Tile t;
+    t.srow = T;
+    if constexpr (!GROUPED) {
+        if (T * TILE_ROWS >= G.rows)
+            return;
+        t.row0 = T * TILE_ROWS;
+        const int64_t left = G.rows - t.row0;
+        t.nrows = left < TILE_ROWS ? (int)left : TILE_ROWS;
+    } else {
+        int64_t ntiles = G.P[G.n_groups];
+        if (ntiles > G.max_tiles)
+            ntiles = G.max_tiles;
+        if (T >= ntiles)
+            return;
+        const int64_t e = tile_segment(G.P, G.n_groups, T);
+        int64_t lo, hi;
+        segment_rows(G.off, e, G.rows, &lo, &hi);
+        t.row0 = lo + (T - G.P[e]) * TILE_ROWS;
+        const int64_t left = hi - t.row0;
+        t.nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+    }
+    const int64_t col0 = strip * TILE_COLS + 8 * g;
+    const bool col_ok = col0 < G.cols;
+    const bool full = strip * TILE_COLS + TILE_COLS <= G.cols && t.nrows == TILE_ROWS;
+    uint32_t v[8][4];
+    if (full)
+        load_tile<true>(v, G.x, G.cols, col0, t, rg, col_ok);
+    else
+        load_tile<false>(v, G.x, G.cols, col0, t, rg, col_ok);
+    do_tile<ROW, COL>(v, G, col0, t, full, g, rg, col_ok, rc, rs, cc, cs);
+}
+
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
 // sequential over chunks of 256 segments with a block scan.
 __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__restrict__ off,
@@ -361,10 +422,19 @@ static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
     return slots * nct;
 }
 
+constexpr bool ONE_TILE_PER_WAVE = true;
+
 template <bool ROW, bool COL, bool GROUPED>
 static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc,
                              uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
+    const int64_t all_waves = tiles_per_strip * G.nct;
+    if (ONE_TILE_PER_WAVE && all_waves <= (int64_t)0x7FFFFFFF * WAVES_PER_WG) {
+        const int64_t wgs = (all_waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
+        hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
+                           dim3(64 * WAVES_PER_WG), 0, stream, G, rc, rs, cc, cs);
+        return hipGetLastError();
+    }
     const int64_t waves = wave_count<ROW, COL, GROUPED>(G.nct, tiles_per_strip);
     const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
     Geometry g = G;
