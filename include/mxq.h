@@ -109,6 +109,7 @@ typedef enum {
  *   NULL to skip the columnwise copy (not both copies); one NULL of a pair is
  *   MXQ_ERR_OFFSETS.  Requires cols % 32 == 0, and rows % 32 == 0 when the
  *   columnwise copy is requested.  Code arrays must be 16-byte aligned.
+ *   cols must not exceed 2^26 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *row_codes, uint8_t *row_scales,
@@ -218,7 +219,8 @@ typedef struct {
  *   seg_offsets   device int64 [n_groups + 1], 0 = o_0 <= ... <= o_G =
  *                 total_rows (read on the device; not validated on the host).
  *   out           host pointer to the output struct (device arrays inside).
- *   For NVFP4, total_rows must be below 2^31 (MXQ_ERR_SIZE otherwise).
+ *   For NVFP4, total_rows must be below 2^31; for MXFP8, cols must not exceed
+ *   2^26 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
                          int64_t cols, const int64_t *seg_offsets,

@@ -23,6 +23,7 @@ struct Buf {
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 62;
 constexpr int64_t MAX_GRID_ROWS = 0x7FFFFFFF;     // per-token NVFP4: one workgroup per row
 constexpr int64_t MAX_BLOCKS = 0xFFFFFFFF;        // 16-element blocks indexed in 32 bits
+constexpr int64_t MAX_MXFP8_COLS = (int64_t)1 << 26;  // 32-row tile offsets fit 32 bits
 
 bool size_ok(int64_t a, int64_t b)
 {
@@ -123,7 +124,7 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols, uin
     if ((row_codes == nullptr) != (row_scales == nullptr) ||
         (col_codes == nullptr) != (col_scales == nullptr) || (!row_codes && !col_codes))
         return MXQ_ERR_OFFSETS;
-    if (!size_ok(rows, cols))
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS)
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0 || (col_codes && rows % 32 != 0))
         return MXQ_ERR_SHAPE;
@@ -281,6 +282,8 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t
         return MXQ_ERR_OFFSETS;
     if (cols % 32 != 0)
         return MXQ_ERR_SHAPE;
+    if (cols > MAX_MXFP8_COLS)
+        return MXQ_ERR_SIZE;
     const int64_t scale_rows = total_rows / 32 + n_groups;
     if (scale_rows > MAX_ELEMS / cols)
         return MXQ_ERR_SIZE;

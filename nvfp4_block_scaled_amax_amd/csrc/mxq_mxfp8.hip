@@ -24,12 +24,12 @@
 // Columnwise: rows 2p and 2p+1 of one column share a scale, so they are
 // paired with a byte permute, converted, and regrouped into row order.
 //
-// Schedule.  A persistent grid: each wavefront owns one 128-column strip and
-// a contiguous range of 32-row tiles down it, and loads the next tile while
-// it converts the current one.  For ragged segments (grouped call) the tile
-// range is in "segment tile" space: tile T lies in the segment e with
-// P[e] <= T < P[e+1], found by a forward scan that advances about once per
-// segment.
+// Schedule.  One tile per wavefront, every tile in one launch: wavefront w
+// converts 128-column strip w % nct of tile w / nct, so the four wavefronts
+// of a workgroup cover 512 consecutive columns of one 32-row band.  Each
+// tile's base addresses are wave-uniform (scalar registers) and lanes add
+// 32-bit offsets (cols < 2^27).  For ragged segments (grouped call) tile T
+// lies in the segment e with P[e] <= T < P[e+1] (binary search).
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -73,38 +73,52 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t old, uint32_t bf16pair, uint32
 
 struct Tile {
     int64_t row0;      // first row
-    int nrows;         // rows present, 1..32
+    int nrows;         // rows present, 0..32
     int64_t srow;      // row of col_scales
 };
 
+// Partial tiles (rows past the segment end, columns past cols) load from a
+// clamped address and select zero: no divergent loads, which would make the
+// compiler shuffle the whole tile between registers.  xt: the tile's first
+// element (row0, strip column 0); lane offsets are 32-bit.
 template <bool FULL>
-__device__ __forceinline__ void load_tile(uint32_t (&v)[8][4], const uint16_t *__restrict__ x,
-                                          int64_t cols, int64_t col0, const Tile &t, int rg,
+__device__ __forceinline__ void load_tile(uint32_t (&v)[8][4], const uint16_t *__restrict__ xt,
+                                          uint32_t cols, uint32_t c8, int nrows, int rg,
                                           bool col_ok)
 {
-    const uint16_t *p = x + (t.row0 + 8 * rg) * cols + col0;
-    const int nr = t.nrows - 8 * rg;
+    if constexpr (FULL) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        if (FULL || (col_ok && i < nr)) {
-            const uint4 q = ld_nt16(p + i * cols);
+        for (int i = 0; i < 8; i++) {
+            const uint4 q = ld_nt16(xt + ((uint32_t)(8 * rg + i) * cols + c8));
             v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
-        } else {
-            v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0u;
+        }
+    } else {
+        // A tile with no rows (nrows 0) reads its first row, which lies in
+        // the tensor, and keeps nothing.
+        const uint32_t last = nrows > 0 ? (uint32_t)(nrows - 1) : 0u;
+        const uint32_t c = col_ok ? c8 : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = 8 * rg + i;
+            const bool keep = col_ok && r < nrows;
+            const uint4 q = ld_nt16(xt + ((keep ? (uint32_t)r : last) * cols + c));
+            v[i][0] = keep ? q.x : 0u; v[i][1] = keep ? q.y : 0u;
+            v[i][2] = keep ? q.z : 0u; v[i][3] = keep ? q.w : 0u;
         }
     }
 }
 
+// Tile outputs: wave-uniform bases at (row0, strip column 0).
+struct TileOut {
+    uint8_t *rc, *rs, *cc, *cs;     // row codes, row scales, col codes, col scales
+};
+
 template <bool ROW, bool COL, bool FULL>
-__device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], int64_t cols, int64_t col0,
-                                             const Tile &t, int g, int rg, bool col_ok,
-                                             uint8_t *__restrict__ row_codes,
-                                             uint8_t *__restrict__ row_scales,
-                                             uint8_t *__restrict__ col_codes,
-                                             uint8_t *__restrict__ col_scales)
+__device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
+                                             uint32_t c8, int nrows, int g, int rg, bool col_ok,
+                                             const TileOut &o)
 {
-    const int64_t base = (t.row0 + 8 * rg) * cols + col0;
-    const int nr = t.nrows - 8 * rg;
+    const int nr = nrows - 8 * rg;
     uint32_t a[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++)
@@ -113,7 +127,7 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], int64_t 
             a[i][j] = v[i][j] & 0x7FFF7FFFu;
 
     if constexpr (ROW) {
-        const int64_t nb = cols >> 5;
+        const uint32_t nb = cols >> 5;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const uint32_t m = pk_max_u16(pk_max_u16(a[i][0], a[i][1]), pk_max_u16(a[i][2], a[i][3]));
@@ -125,9 +139,10 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], int64_t 
             const uint32_t w0 = cvt2<true>(cvt2<false>(0u, v[i][0], scale), v[i][1], scale);
             const uint32_t w1 = cvt2<true>(cvt2<false>(0u, v[i][2], scale), v[i][3], scale);
             if (FULL || (col_ok && i < nr)) {
-                st_nt8(row_codes + base + i * cols, w0, w1);
+                const uint32_t r = (uint32_t)(8 * rg + i);
+                st_nt8(o.rc + (r * cols + c8), w0, w1);
                 if ((g & 3) == 0)
-                    row_scales[(base >> 5) + i * nb] = (uint8_t)(sc >> 7);
+                    o.rs[r * nb + (c8 >> 5)] = (uint8_t)(sc >> 7);
             }
         }
     }
@@ -162,12 +177,12 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], int64_t 
             const uint32_t w0 = perm(P[p][1], P[p][0], sel);
             const uint32_t w1 = perm(P[p][3], P[p][2], sel);
             if (FULL || (col_ok && i < nr))
-                st_nt8(col_codes + base + i * cols, w0, w1);
+                st_nt8(o.cc + ((uint32_t)(8 * rg + i) * cols + c8), w0, w1);
         }
         if ((FULL || col_ok) && rg == 0) {
             const uint32_t s0 = perm(sb[1], sb[0], 0x06040200u);     // columns 0..3
             const uint32_t s1 = perm(sb[3], sb[2], 0x06040200u);     // columns 4..7
-            st_nt8(col_scales + t.srow * cols + col0, s0, s1);
+            st_nt8(o.cs + c8, s0, s1);
         }
     }
 }
@@ -181,7 +196,6 @@ struct Geometry {
     const int64_t *off;    // grouped: segment offsets
     const int64_t *P;      // grouped: prefix of ceil(n_e / 32)
     int64_t n_groups;
-    int64_t nwaves;        // wavefronts in the grid
 };
 
 // Segment e's rows clamped into [0, total_rows): offsets are device data the
@@ -195,112 +209,6 @@ __device__ __forceinline__ void segment_rows(const int64_t *__restrict__ off, in
     b = b < a ? a : (b > total_rows ? total_rows : b);
     *lo = a;
     *hi = b;
-}
-
-// Tile T of the strip -> rows.  Dense: T * 32.  Grouped: advance *e until
-// P[*e] <= T < P[*e + 1].
-template <bool GROUPED>
-__device__ __forceinline__ Tile tile_rows(const Geometry &G, int64_t T, int64_t *e)
-{
-    Tile t;
-    t.srow = T;
-    if constexpr (!GROUPED) {
-        t.row0 = T * TILE_ROWS;
-        const int64_t left = G.rows - t.row0;
-        t.nrows = left < TILE_ROWS ? (int)left : TILE_ROWS;
-    } else {
-        while (*e + 1 < G.n_groups && G.P[*e + 1] <= T)
-            ++*e;
-        int64_t lo, hi;
-        segment_rows(G.off, *e, G.rows, &lo, &hi);
-        t.row0 = lo + (T - G.P[*e]) * TILE_ROWS;
-        const int64_t left = hi - t.row0;
-        t.nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
-    }
-    return t;
-}
-
-template <bool ROW, bool COL>
-__device__ __forceinline__ void do_tile(const uint32_t (&v)[8][4], const Geometry &G, int64_t col0,
-                                        const Tile &t, bool full, int g, int rg, bool col_ok,
-                                        uint8_t *rc, uint8_t *rs, uint8_t *cc, uint8_t *cs)
-{
-    if (full)
-        convert_tile<ROW, COL, true>(v, G.cols, col0, t, g, rg, col_ok, rc, rs, cc, cs);
-    else
-        convert_tile<ROW, COL, false>(v, G.cols, col0, t, g, rg, col_ok, rc, rs, cc, cs);
-}
-
-template <bool ROW, bool COL, bool GROUPED>
-__global__ void __launch_bounds__(256) mxfp8_kernel(Geometry G, uint8_t *__restrict__ rc,
-                                                    uint8_t *__restrict__ rs,
-                                                    uint8_t *__restrict__ cc,
-                                                    uint8_t *__restrict__ cs)
-{
-    const int lane = (int)lane_id();
-    const int g = lane & 15, rg = lane >> 4;
-    const int64_t wave = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group();
-    const int64_t nwaves = G.nwaves;
-    // Strip and tile range of this wavefront.
-    const int64_t strip = wave % G.nct;
-    const int64_t slot = wave / G.nct, nslots = nwaves / G.nct;
-    int64_t ntiles;
-    if constexpr (GROUPED) {
-        ntiles = G.P[G.n_groups];
-        if (ntiles > G.max_tiles)
-            ntiles = G.max_tiles;
-    } else {
-        ntiles = (G.rows + TILE_ROWS - 1) / TILE_ROWS;
-    }
-    if (slot >= nslots)
-        return;
-    const int64_t per = (ntiles + nslots - 1) / nslots;
-    int64_t T = slot * per;
-    const int64_t Tend = T + per < ntiles ? T + per : ntiles;
-    if (T >= Tend)
-        return;
-    const int64_t col0 = strip * TILE_COLS + 8 * g;
-    const bool col_ok = col0 < G.cols;                  // cols % 32 == 0: whole 32-column blocks
-    const bool strip_full = strip * TILE_COLS + TILE_COLS <= G.cols;
-    int64_t e = 0;
-
-    uint32_t va[8][4], vb[8][4];
-    Tile ta = tile_rows<GROUPED>(G, T, &e), tb;
-    bool fa = strip_full && ta.nrows == TILE_ROWS, fb = false;
-    if (fa)
-        load_tile<true>(va, G.x, G.cols, col0, ta, rg, col_ok);
-    else
-        load_tile<false>(va, G.x, G.cols, col0, ta, rg, col_ok);
-    for (;;) {
-        // Prefetch T + 1 into vb, convert T from va.
-        const bool more = T + 1 < Tend;
-        if (more) {
-            tb = tile_rows<GROUPED>(G, T + 1, &e);
-            fb = strip_full && tb.nrows == TILE_ROWS;
-            if (fb)
-                load_tile<true>(vb, G.x, G.cols, col0, tb, rg, col_ok);
-            else
-                load_tile<false>(vb, G.x, G.cols, col0, tb, rg, col_ok);
-        }
-        do_tile<ROW, COL>(va, G, col0, ta, fa, g, rg, col_ok, rc, rs, cc, cs);
-        if (!more)
-            break;
-        T += 1;
-        // Prefetch T + 1 into va, convert T from vb.
-        const bool more2 = T + 1 < Tend;
-        if (more2) {
-            ta = tile_rows<GROUPED>(G, T + 1, &e);
-            fa = strip_full && ta.nrows == TILE_ROWS;
-            if (fa)
-                load_tile<true>(va, G.x, G.cols, col0, ta, rg, col_ok);
-            else
-                load_tile<false>(va, G.x, G.cols, col0, ta, rg, col_ok);
-        }
-        do_tile<ROW, COL>(vb, G, col0, tb, fb, g, rg, col_ok, rc, rs, cc, cs);
-        if (!more2)
-            break;
-        T += 1;
-    }
 }
 
 // Segment of tile T (grouped): the e with P[e] <= T < P[e + 1], by binary
@@ -353,15 +261,21 @@ __global__ void __launch_bounds__(256) mxfp8_tile_kernel(Geometry G, uint8_t *__
         const int64_t left = hi - t.row0;
         t.nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
     }
-    const int64_t col0 = strip * TILE_COLS + 8 * g;
-    const bool col_ok = col0 < G.cols;
-    const bool full = strip * TILE_COLS + TILE_COLS <= G.cols && t.nrows == TILE_ROWS;
+    const int64_t tcol = strip * TILE_COLS;              // wave-uniform
+    const uint32_t cols = (uint32_t)G.cols, c8 = 8u * (uint32_t)g;
+    const bool col_ok = tcol + c8 < G.cols;             // cols % 32 == 0: whole 32-column blocks
+    const bool full = tcol + TILE_COLS <= G.cols && t.nrows == TILE_ROWS;
+    const int64_t base = t.row0 * G.cols + tcol;
+    const uint16_t *xt = G.x + base;
+    const TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol};
     uint32_t v[8][4];
-    if (full)
-        load_tile<true>(v, G.x, G.cols, col0, t, rg, col_ok);
-    else
-        load_tile<false>(v, G.x, G.cols, col0, t, rg, col_ok);
-    do_tile<ROW, COL>(v, G, col0, t, full, g, rg, col_ok, rc, rs, cc, cs);
+    if (full) {
+        load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
+        convert_tile<ROW, COL, true>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+    } else {
+        load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
+        convert_tile<ROW, COL, false>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+    }
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
@@ -402,45 +316,15 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Wavefronts to launch: OVERSUBSCRIBE times as many as the device holds at
-// once (measured: more wavefronts in flight keep more loads and stores
-// outstanding than the in-wave prefetch alone), but not more than one per
-// tile, as a whole number of strips.
-constexpr int OVERSUBSCRIBE = 16;
-
-template <bool ROW, bool COL, bool GROUPED>
-static int64_t wave_count(int64_t nct, int64_t tiles_per_strip)
-{
-    const int64_t resident =
-        resident_workgroups((const void *)mxfp8_kernel<ROW, COL, GROUPED>, 64 * WAVES_PER_WG) *
-        WAVES_PER_WG * OVERSUBSCRIBE;
-    int64_t slots = resident / nct;
-    if (slots < 1)
-        slots = 1;
-    if (slots > tiles_per_strip)
-        slots = tiles_per_strip;
-    return slots * nct;
-}
-
-constexpr bool ONE_TILE_PER_WAVE = true;
-
 template <bool ROW, bool COL, bool GROUPED>
 static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc,
                              uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
-    const int64_t all_waves = tiles_per_strip * G.nct;
-    if (ONE_TILE_PER_WAVE && all_waves <= (int64_t)0x7FFFFFFF * WAVES_PER_WG) {
-        const int64_t wgs = (all_waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
-        hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
-                           dim3(64 * WAVES_PER_WG), 0, stream, G, rc, rs, cc, cs);
-        return hipGetLastError();
-    }
-    const int64_t waves = wave_count<ROW, COL, GROUPED>(G.nct, tiles_per_strip);
-    const int64_t wgs = (waves + WAVES_PER_WG - 1) / WAVES_PER_WG;
-    Geometry g = G;
-    g.nwaves = wgs * WAVES_PER_WG;
-    hipLaunchKernelGGL((mxfp8_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
-                       dim3(64 * WAVES_PER_WG), 0, stream, g, rc, rs, cc, cs);
+    const int64_t wgs = (tiles_per_strip * G.nct + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    if (wgs > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED>), dim3((unsigned)wgs),
+                       dim3(64 * WAVES_PER_WG), 0, stream, G, rc, rs, cc, cs);
     return hipGetLastError();
 }
 
@@ -458,7 +342,7 @@ static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
                               uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
-    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0, 0};
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0};
     return launch<false>(G, (rows + TILE_ROWS - 1) / TILE_ROWS, rc, rs, cc, cs, stream);
 }
 
@@ -473,7 +357,7 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
         return err;
     const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
-               n_groups, 0};
+               n_groups};
     return launch<true>(G, max_tiles, rc, rs, cc, cs, stream);
 }
 
