@@ -225,6 +225,20 @@ def test_nvfp4_wide_range(orc):
     check_nvfp4(orc, _wide_range_rows(40, 2048, 6), "wide range 40x2048")
 
 
+def test_nvfp4_every_token_amax(orc):
+    """Every finite BF16 magnitude as a token amax (so every FP32 token scale
+    the format can produce, subnormal scales included), one row each, with
+    the other elements of the row spread below it."""
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)            # all finite nonzero magnitudes
+    rows, cols = mags.size, 32
+    rng = np.random.default_rng(41)
+    frac = rng.integers(0, 0x8000, (rows, cols)).astype(np.uint32)
+    x = (frac * mags[:, None]) // 0x8000                    # magnitudes <= the row amax
+    x[:, 0] = mags
+    x |= (rng.integers(0, 2, (rows, cols)).astype(np.uint32) << 15)
+    check_nvfp4(orc, x.astype(np.uint16), f"every token amax {rows}x{cols}")
+
+
 def test_nvfp4_batch_invariance():
     """Per-token outputs of a row do not depend on the other rows of the batch."""
     x = W.config3()[:512]
