@@ -147,12 +147,12 @@ def build_exp(torch, E, W, legs, dev, empty):
     legs.append(Leg("nvfp4_export_gateup",
                     lambda: E.mxq_nvfp4_quantize_gateup_pair(g, u, NE, I, H, gc, gb, uc, ub, sp),
                     2 * 2 * ng, pair_out, 2 * ng,
-                    ["zero_u32_kernel", "scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
+                    ["scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
                     "NVFP4 gate/up export 128x2x768x2048, shared scale per pair"))
     legs.append(Leg("nvfp4_export_down",
                     lambda: E.mxq_nvfp4_quantize_gateup_pair(dn, None, NE, H, I, dc, db, None, None, sd),
                     2 * ng, down_out, ng,
-                    ["zero_u32_kernel", "scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
+                    ["scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
                     "NVFP4 down export 128x2048x768"))
 
     def exp_dequant():

@@ -148,9 +148,9 @@ int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
  *                        cols % 16 == 0.
  *   gate_codes, up_codes [n_experts][rows][cols/2], 16-byte aligned.
  *   gate_block_scales, up_block_scales  [n_experts][rows][cols/16].
- *   scope_scales         [n_experts] FP32; used as the amax accumulator during
- *                        the call and holding s_e = fp32(amax_e / 2688) when
- *                        it completes.
+ *   scope_scales         [n_experts] FP32: s_e = fp32(amax_e / 2688).
+ *   gate_codes also serves the call as scratch for per-chunk partial maxima
+ *   (written before, and overwritten by, the codes).
  *   up, up_codes and up_block_scales must be all NULL or all non-NULL.
  *   n_experts * rows * cols must be below 2^36 (MXQ_ERR_SIZE otherwise).
  */

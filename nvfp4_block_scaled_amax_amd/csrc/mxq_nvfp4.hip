@@ -335,34 +335,32 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Export: scope amax, FP32 scales, then a flat pass over the blocks.
+// Export: scope amax (per-chunk partial maxima, then one wavefront per scope),
+// FP32 scales, then a flat pass over the blocks.  Atomics on one word per
+// scope serialize (hundreds of workgroups per scope), so the partials are
+// written to distinct words: the start of the gate code array, which the
+// code pass overwrites afterwards (stream order; the code array is always
+// large enough, see launch_nvfp4_scoped).
 // ---------------------------------------------------------------------------
-__global__ void zero_u32_kernel(uint32_t *p, int64_t n)
-{
-    const int64_t i = (int64_t)wg_id() * 256 + tid();
-    if (i < n)
-        p[i] = 0u;
-}
-
+constexpr int AMAX_THREADS = 64;                            // one wavefront per workgroup
 constexpr int AMAX_LOADS = 8;                               // 16-byte loads per thread
-constexpr int64_t AMAX_CHUNK = 256 * 8 * AMAX_LOADS;        // elements per workgroup
+constexpr int64_t AMAX_CHUNK = AMAX_THREADS * 8 * AMAX_LOADS;   // elements per workgroup
 
-// Workgroup w reduces chunk w % chunks of scope w / chunks.  A scope is
-// tensor a's slice [e * n_per, (e+1) * n_per) followed by tensor b's (if any).
-// The result is the amax's BF16 magnitude bits (as u32) in amax[e].
-__global__ void __launch_bounds__(256) scope_amax_kernel(const uint16_t *__restrict__ a,
-                                                         const uint16_t *__restrict__ b,
-                                                         int64_t n_per, int64_t chunks,
-                                                         uint32_t *__restrict__ amax)
+// Workgroup w reduces chunk w % chunks of scope w / chunks into partial[w]
+// (BF16 magnitude bits as u32).  A scope is tensor a's slice
+// [e * n_per, (e+1) * n_per) followed by tensor b's (if any).
+__global__ void __launch_bounds__(AMAX_THREADS) scope_amax_kernel(const uint16_t *__restrict__ a,
+                                                                  const uint16_t *__restrict__ b,
+                                                                  int64_t n_per, int64_t chunks,
+                                                                  uint32_t *__restrict__ partial)
 {
-    __shared__ uint32_t part[4];
     const int64_t e = (int64_t)wg_id() / chunks;
     const int64_t ch = (int64_t)wg_id() - e * chunks;
     const int64_t n_scope = b ? 2 * n_per : n_per;
     uint32_t m = 0;
 #pragma unroll
     for (int it = 0; it < AMAX_LOADS; it++) {
-        const int64_t i = ch * AMAX_CHUNK + (int64_t)it * 2048 + 8 * tid();
+        const int64_t i = ch * AMAX_CHUNK + (int64_t)it * (8 * AMAX_THREADS) + 8 * tid();
         if (i < n_scope) {
             const uint16_t *p = (i < n_per) ? a + e * n_per + i : b + e * n_per + (i - n_per);
             const uint4 q = ld_nt16(p);
@@ -370,24 +368,23 @@ __global__ void __launch_bounds__(256) scope_amax_kernel(const uint16_t *__restr
                                          pk_max_u16(q.z & 0x7FFF7FFFu, q.w & 0x7FFF7FFFu)));
         }
     }
-    uint32_t h = wave_max_u32(hmax_u16(m));
+    const uint32_t h = wave_max_u32(hmax_u16(m));
     if (lane_id() == 0)
-        part[tid() >> 6] = h;
-    __syncthreads();
-    if (tid() == 0) {
-        h = max(max(part[0], part[1]), max(part[2], part[3]));
-        atomicMax(amax + e, h);
-    }
+        partial[wg_id()] = h;
 }
 
-// amax bits -> s = fp32(amax / 2688), in place.
-__global__ void scope_finalize_kernel(uint32_t *p, int64_t n)
+// One wavefront per scope: the max of its partials -> s = fp32(amax / 2688).
+__global__ void __launch_bounds__(64) scope_finalize_kernel(const uint32_t *__restrict__ partial,
+                                                            int64_t chunks,
+                                                            float *__restrict__ scope_s)
 {
-    const int64_t i = (int64_t)wg_id() * 256 + tid();
-    if (i < n) {
-        const float s = div2688(u2f(p[i] << 16));
-        p[i] = f2u(s);
-    }
+    const int64_t e = wg_id();
+    uint32_t m = 0;
+    for (int64_t c = lane_id(); c < chunks; c += 64)
+        m = max(m, partial[e * chunks + c]);
+    m = wave_max_u32(m);
+    if (lane_id() == 0)
+        scope_s[e] = div2688(u2f(m << 16));
 }
 
 // Flat export pass over one tensor of nblk blocks; block j belongs to scope
@@ -478,16 +475,17 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
                                uint8_t *uc, uint8_t *ubs, float *scope_scales,
                                hipStream_t stream)
 {
-    uint32_t *amax = reinterpret_cast<uint32_t *>(scope_scales);
-    const unsigned small_grid = (unsigned)((n_experts + 255) / 256);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(small_grid), dim3(256), 0, stream, amax, n_experts);
+    // Partials: chunks * n_experts words at the start of gate_codes, whose
+    // n_experts * n_per / 2 bytes always suffice: chunks <= 2 n_per / 4096 + 1
+    // and n_per >= 16, so 4 * chunks <= n_per / 512 + 4 <= n_per / 2.
     const int64_t n_per = rows * cols;
     const int64_t n_scope = up ? 2 * n_per : n_per;
     const int64_t chunks = (n_scope + AMAX_CHUNK - 1) / AMAX_CHUNK;
-    hipLaunchKernelGGL(scope_amax_kernel, dim3((unsigned)(chunks * n_experts)), dim3(256), 0,
-                       stream, gate, up, n_per, chunks, amax);
-    hipLaunchKernelGGL(scope_finalize_kernel, dim3(small_grid), dim3(256), 0, stream, amax,
-                       n_experts);
+    uint32_t *partial = reinterpret_cast<uint32_t *>(gc);
+    hipLaunchKernelGGL(scope_amax_kernel, dim3((unsigned)(chunks * n_experts)), dim3(AMAX_THREADS),
+                       0, stream, gate, up, n_per, chunks, partial);
+    hipLaunchKernelGGL(scope_finalize_kernel, dim3((unsigned)n_experts), dim3(64), 0, stream,
+                       (const uint32_t *)partial, chunks, scope_scales);
     // Blocks in all below 2^32: checked by the caller.
     const int64_t nblk = n_experts * n_per / 16;
     const Div bps = make_div((uint32_t)(n_per / 16));
