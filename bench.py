@@ -97,7 +97,7 @@ def build_legs(torch, mxq, api, W, log, want=lambda group: True):
         legs.append(Leg(f"mxfp8_rowcol_{name}",
                         (lambda x=x, rows=rows, cols=cols, rc=rc, rs=rs, cc=cc, cs=cs:
                          E.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs)),
-                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_tile_kernel<true, true, false>"],
+                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_tile_kernel<true, true, false, 4>"],
                         f"MXFP8 row+col {rows}x{cols}"))
     log("act/wgt ready")
 
@@ -183,7 +183,7 @@ def build_grp(torch, E, W, legs, dev, empty):
     nv_out = n // 2 + n // 16 + 4 * R
     legs.append(Leg("grouped_mxfp8_rowcol",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_MXFP8_ROWCOL, xg, R, K, off, G, g8),
-                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true>"],
+                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8>"],
                     f"grouped MXFP8 row+col {R}x{K}, {G} segments"))
     legs.append(Leg("grouped_nvfp4",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_NVFP4, xg, R, K, off, G, g4),
