@@ -13,8 +13,11 @@ Algorithmic bytes count each input read once and each output written once.
 Each leg is bracketed by HIP events on the stream the library launches on.
 
 Prints one JSON line.  Extra fields: per-leg GB/s and % of the 8 TB/s HBM
-peak ("legs"), the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample of the same workload on the host cores.
+peak ("legs"); per-config timings ("configs": 50 back-to-back launches per
+sample over rotating buffer sets larger than the MALL, median and minimum per
+launch, for C2a/C2b in four data modes, C3 quantize and dequant, C4 and C5);
+the roofline of the dominant kernel; and the CPU oracle timed on the host
+cores (all cores over a whole step, one thread over 1/16 of it).
 """
 from __future__ import annotations
 
@@ -200,55 +203,193 @@ def build_grp(torch, E, W, legs, dev, empty):
                     nv_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16"))
 
 
-CPU_SAMPLE_DIV = 1
+CPU_SAMPLE_DIV = 1          # all host cores: one whole step
+CPU_SINGLE_DIV = 16         # one thread: 1/16 of every leg
 
 
-def cpu_baseline(W, log):
-    """The oracle (as it stands) on a bounded sample of the workload: 1/D of
-    every leg's rows (1/D of the experts for the export; D = CPU_SAMPLE_DIV,
-    1 = one whole step, about 15 s on 16 host cores), timed on the host cores.
-    Input generation is outside the timed region."""
+def oracle_step(W, D):
+    """Inputs for the oracle over 1/D of every leg (generated here, outside any
+    timed region) and a function that runs the oracle on them and returns the
+    algorithmic bytes it processed."""
     import oracle
     if not os.path.exists(oracle._LIB):
         oracle.build()
-    D = CPU_SAMPLE_DIV
     wgt = W.config2_weight("random")[:8192 // D]
     act = W.config2_activation("random")[:2048 // D]
     tok = W.config3()[:8192 // D]
-    gate, up, down = W.config4(128 // D)
+    gate, up, down = W.config4(max(1, 128 // D))
     xg = W.student_t_activations(262144 // D, 2048, 5)
-    total_bytes, t0 = 0, time.perf_counter()
-    for x in (wgt, act):
-        oracle.mxfp8_rowwise(x)
-        oracle.mxfp8_colwise(x)
-        total_bytes += x.size * 4 + x.size // 16
-    c, b, s = oracle.nvfp4_per_token(tok)
-    oracle.dequant_nvfp4(c, b, s, 1)
-    total_bytes += 2 * (2 * tok.size + tok.size // 2 + tok.size // 16 + 4 * tok.shape[0])
-    gc, gb, uc, ub, sp = oracle.nvfp4_gateup_pair(gate, up)
-    dc, db, _, _, sd = oracle.nvfp4_gateup_pair(down, None)
-    oracle.dequant_nvfp4(gc.reshape(-1, 1024), gb.reshape(-1, 128), sp, 768)
-    oracle.dequant_nvfp4(uc.reshape(-1, 1024), ub.reshape(-1, 128), sp, 768)
-    oracle.dequant_nvfp4(dc.reshape(-1, 384), db.reshape(-1, 48), sd, 2048)
-    ng = gate.size
-    total_bytes += 2 * (3 * 2 * ng + 3 * (ng // 2 + ng // 16))
-    rc, rs = oracle.mxfp8_rowwise(xg)
-    oracle.mxfp8_colwise(xg)
-    c, b, s = oracle.nvfp4_per_token(xg)
-    oracle.dequant_mxfp8_rowwise(rc, rs)
-    oracle.dequant_nvfp4(c, b, s, 1)
-    n = xg.size
-    total_bytes += (2 * n + 2 * n + n // 16) + (2 * n + n // 2 + n // 16) + \
-        (n + n // 32 + 2 * n) + (n // 2 + n // 16 + 2 * n)
+
+    def run():
+        total = 0
+        for x in (wgt, act):
+            oracle.mxfp8_rowwise(x)
+            oracle.mxfp8_colwise(x)
+            total += x.size * 4 + x.size // 16
+        c, b, s = oracle.nvfp4_per_token(tok)
+        oracle.dequant_nvfp4(c, b, s, 1)
+        total += 2 * (2 * tok.size + tok.size // 2 + tok.size // 16 + 4 * tok.shape[0])
+        gc, gb, uc, ub, sp = oracle.nvfp4_gateup_pair(gate, up)
+        dc, db, _, _, sd = oracle.nvfp4_gateup_pair(down, None)
+        oracle.dequant_nvfp4(gc.reshape(-1, 1024), gb.reshape(-1, 128), sp, 768)
+        oracle.dequant_nvfp4(uc.reshape(-1, 1024), ub.reshape(-1, 128), sp, 768)
+        oracle.dequant_nvfp4(dc.reshape(-1, 384), db.reshape(-1, 48), sd, 2048)
+        ng = gate.size
+        total += 2 * (3 * 2 * ng + 3 * (ng // 2 + ng // 16))
+        rc, rs = oracle.mxfp8_rowwise(xg)
+        oracle.mxfp8_colwise(xg)
+        c, b, s = oracle.nvfp4_per_token(xg)
+        oracle.dequant_mxfp8_rowwise(rc, rs)
+        oracle.dequant_nvfp4(c, b, s, 1)
+        n = xg.size
+        total += (2 * n + 2 * n + n // 16) + (2 * n + n // 2 + n // 16) + \
+            (n + n // 32 + 2 * n) + (n // 2 + n // 16 + 2 * n)
+        return total
+
+    return run
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, log):
+    """The oracle (as it stands) timed on the host cores: all cores over one
+    whole step of the workload, and one thread over 1/16 of every leg."""
+    import oracle
+    run = oracle_step(W, CPU_SAMPLE_DIV)
+    cores = oracle.max_threads()
+    t0 = time.perf_counter()
+    nbytes = run()
     dt = time.perf_counter() - t0
-    log(f"cpu baseline: {total_bytes / 1e9:.3f} GB in {dt:.1f} s")
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": (f"1/{D} of each leg (one pass of the oracle over every leg of the step "
-                       f"at 1/{D} of its rows): {8192 // D} weight rows, {2048 // D} activation "
-                       f"rows, {8192 // D} tokens, {128 // D} of 128 experts, {262144 // D} "
-                       "grouped rows (one expert segment); input generation excluded"),
-            "seconds": round(dt, 2), "bytes": total_bytes}
+    log(f"cpu baseline ({cores} threads): {nbytes / 1e9:.3f} GB in {dt:.1f} s")
+    del run
+    run1 = oracle_step(W, CPU_SINGLE_DIV)
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    nbytes1 = run1()
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(cores)
+    log(f"cpu baseline (1 thread): {nbytes1 / 1e9:.3f} GB in {dt1:.1f} s")
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"one whole step (every leg at full size: 8192x2048 weight, 2048x2048 "
+                       "activation, 8192 tokens, 128 experts, 262144 grouped rows as one "
+                       "segment); input generation excluded"),
+            "seconds": round(dt, 2), "bytes": nbytes,
+            "single_thread": {"value": round(nbytes1 / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"1/{CPU_SINGLE_DIV} of every leg's rows",
+                              "seconds": round(dt1, 2), "bytes": nbytes1},
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES = 50, 10, 5
+ROTATE_BYTES = 1 << 30      # buffer sets rotated per config: > the 256 MB MALL
+
+
+def time_launches(torch, launches, n_launch, warmup, samples):
+    """Mean time per launch (ms) of n_launch back-to-back launches cycling
+    through `launches`, for each of `samples` samples (after warmup launches)."""
+    stream = torch.cuda.current_stream()
+    for k in range(warmup):
+        launches[k % len(launches)]()
+    out = []
+    for _ in range(samples):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(n_launch):
+            launches[k % len(launches)]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / n_launch)
+    return out
+
+
+def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels):
+    med, mn = float(np.median(ms_list)), float(np.min(ms_list))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return name, {"desc": desc, "kernels": kernels, "ms_median": round(med, 5),
+                  "ms_min": round(mn, 5), "bytes": nbytes, "GB_s": round(gbs, 1),
+                  "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                  "elements_per_s": round(elems / (med * 1e-3), 1), "buffer_sets": sets}
+
+
+def config_timings(torch, E, W, legs, log):
+    """The per-config protocol: hipEvents around 50 back-to-back launches per
+    sample (5 samples after 10 warm-up launches), median and minimum per launch.
+    Configs under 256 MB rotate distinct buffer sets totalling over 1 GiB, so
+    every launch reads inputs that are not in the MALL; C5 is over 1 GiB
+    itself.  C2b and C3 (and C5) are the shapes the 70% bar applies to."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    empty = lambda shape, dt=torch.uint8: torch.empty(shape, dtype=dt, device="cuda")
+    res = {}
+
+    def mxfp8_cfg(name, rows, cols, x_np):
+        n = rows * cols
+        nbytes = 2 * n + 2 * n + 2 * (n // 32)
+        sets = -(-ROTATE_BYTES // nbytes)
+        x0 = dev(x_np)
+        bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols)), empty((rows, cols // 32)),
+                 empty((rows, cols)), empty((rows // 32, cols))) for k in range(sets)]
+        launches = [(lambda b=b: E.mxq_mxfp8_quantize_rowcol(b[0], rows, cols, b[1], b[2], b[3],
+                                                               b[4])) for b in bufs]
+        ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
+                          ["mxfp8_tile_kernel"])
+        res[k] = v
+        del bufs, launches, x0
+        torch.cuda.empty_cache()
+
+    for mode in W.MXFP8_MODES:
+        mxfp8_cfg(f"C2a_{mode}", 2048, 2048, W.config2_activation(mode))
+        mxfp8_cfg(f"C2b_{mode}", 8192, 2048, W.config2_weight(mode))
+    log("C2 timed")
+
+    rows, cols = 8192, 2048
+    n = rows * cols
+    q_bytes = 2 * n + n // 2 + n // 16 + 4 * rows
+    d_bytes = n // 2 + n // 16 + 4 * rows + 2 * n
+    sets = -(-ROTATE_BYTES // q_bytes)
+    x0 = dev(W.config3())
+    bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols // 2)), empty((rows, cols // 16)),
+             empty((rows,), torch.float32), empty((rows, cols), torch.bfloat16))
+            for k in range(sets)]
+    q = [(lambda b=b: E.mxq_nvfp4_quantize_per_token(b[0], rows, cols, b[1], b[2], b[3]))
+         for b in bufs]
+    ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+    k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
+                      ["nvfp4_token_kernel"])
+    res[k] = v
+    d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows, cols,
+                                             b[4])) for b in bufs]
+    ms = time_launches(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+    k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", ms, d_bytes, n, sets,
+                      ["dequant_nvfp4_kernel"])
+    res[k] = v
+    del bufs, q, d, x0
+    torch.cuda.empty_cache()
+    log("C3 timed")
+
+    by_name = {l.name: l for l in legs}
+    for leg, cfg in (("grouped_mxfp8_rowcol", "C5_mxfp8"), ("grouped_nvfp4", "C5_nvfp4"),
+                     ("grouped_dequant_mxfp8", "C5_dequant_mxfp8"),
+                     ("grouped_dequant_nvfp4", "C5_dequant_nvfp4"),
+                     ("nvfp4_export_gateup", "C4_gateup"), ("nvfp4_export_down", "C4_down")):
+        if leg in by_name:
+            l = by_name[leg]
+            ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
+            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+            res[k] = v
+    log("C4/C5 timed")
+    return res
 
 
 def main():
@@ -257,6 +398,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config timings (50 back-to-back launches over "
+                         "rotating buffer sets)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--groups", default="act,wgt,tok,exp,grp",
                     help="comma list of leg groups to run (for profiling single kernels)")
@@ -377,6 +521,10 @@ def main():
                 "kernel": dom.kernels[-1], "leg": dom.name, "leg_kernels": dom.kernels,
                 "algorithmic_bytes": dom.bytes, "ms_per_launch": dom_ms}
 
+    configs = None
+    if not args.no_configs and "grp" in groups:
+        configs = config_timings(torch, mxq, W, legs, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W, log)
@@ -397,6 +545,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": leg_info,
+        "configs": configs,
         "copy_calibration": info(calib) if calib is not None else None,
         "csrc_digest": csrc_digest(),
     }

@@ -72,6 +72,7 @@ def lib():
         "oracle_nvfp4_scale_many": (None, [P, I64, P]),
         "oracle_bf16_round_sat_many": (None, [P, I64, P]),
         "oracle_max_threads": (ctypes.c_int, []),
+        "oracle_set_threads": (None, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -94,6 +95,11 @@ def _u16(x) -> np.ndarray:
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for later calls (timing only: results never depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 # -- scalar helpers ---------------------------------------------------------
