@@ -6,7 +6,7 @@
 //
 // Hardware conversions relied upon, each verified bit-exactly by the GPU
 // tests against the CPU oracle on every input class the kernels feed them:
-//   v_cvt_scalef32_pk_fp8_bf16 / _fp8_f32: x / 2^E(scale) rounded to E4M3,
+//   v_cvt_scalef32_pk_fp8_bf16: x / 2^E(scale) rounded to E4M3,
 //       nearest-even, sign kept, exact for |x / 2^E| <= 448 (MXFP8 never
 //       exceeds that: the scale is chosen so the block maximum fits).
 //       Only the scale's exponent field E is used, so an E8M0 byte b placed
@@ -16,6 +16,8 @@
 //   v_cvt_scalef32_pk_fp4_f32 (scale 1.0): f32 -> E2M1 nearest-even on the
 //       full f32 value, saturating at +-6, sign kept.
 //   v_cvt_f32_fp8 / v_cvt_scalef32_pk_f32_fp4: exact decoders.
+//   v_cvt_scalef32_pk_bf16_fp8: E4M3 x 2^E(scale) to BF16, exact except that
+//       it overflows to Inf (instead of saturating) for scale bytes >= 247.
 //   v_rcp_f32: reciprocal within 1 ulp.
 #pragma once
 
@@ -88,7 +90,6 @@ constexpr int DPP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
-constexpr int DPP_ROR8 = 0x128;      // row_ror:8, i.e. lane ^ 8 within a row
 
 // Reductions across lane ^ 16 and lane ^ 32 with the gfx950 permlane swaps.
 // Called with both operands equal to v, a swap leaves one register holding
@@ -130,52 +131,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 scale: for a block amax A (BF16 magnitude bits), the smallest
-// e >= -127 with A <= 448 * 2^e, as the byte e + 127.  With A = 1.m * 2^(E-127)
-// and 448 = 1.75 * 2^8: e = E - 127 - 8 when m <= 96 (m / 128 <= .75), one
-// more otherwise; clamped at -127 (which also covers E == 0).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e8m0_byte(uint32_t a)
-{
-    int E = (int)(a >> 7);
-    int up = (int)(((a & 0x7Fu) + 31u) >> 7);   // 1 iff m > 96
-    int b = E - 8 + up;
-    return b < 0 ? 0u : (uint32_t)b;
-}
-
-// The same for two amaxes packed in the 16-bit halves of a dword; the bytes
-// come back in the low byte of each half.
-__device__ __forceinline__ uint32_t e8m0_byte2(uint32_t a)
-{
-    ushort2_t v = __builtin_bit_cast(ushort2_t, a);
-    ushort2_t E = v >> (unsigned short)7;
-    ushort2_t up = ((v & (unsigned short)0x7F) + (unsigned short)31) >> (unsigned short)7;
-    short2_t b = __builtin_bit_cast(short2_t, (ushort2_t)(E + up)) - (short)8;
-    b = __builtin_elementwise_max(b, (short2_t)0);
-    return __builtin_bit_cast(uint32_t, b);
-}
-
-// ---------------------------------------------------------------------------
 // Conversions
 // ---------------------------------------------------------------------------
-
-// Two BF16 (packed) divided by 2^(b - 127) -> two E4M3 codes in the low 16
-// bits.  Exact while |x| <= 448 * 2^(b-127).
-__device__ __forceinline__ uint32_t mx_e4m3_pair(uint32_t bf16pair, uint32_t scale_byte)
-{
-    short2_t old = {0, 0};
-    short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
-        old, __builtin_bit_cast(bf16x2_t, bf16pair), u2f(scale_byte << 23), false);
-    return __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
-}
-
-// Two f32 values divided by 2^(b - 127) -> two E4M3 codes in the low 16 bits.
-__device__ __forceinline__ uint32_t mx_e4m3_pair_f32(float a, float b, uint32_t scale_byte)
-{
-    short2_t old = {0, 0};
-    short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, u2f(scale_byte << 23), false);
-    return __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
-}
 
 // f32 -> E4M3 nearest-even for 0 <= a, b <= 448 (codes in bits 0-7, 8-15).
 __device__ __forceinline__ uint32_t e4m3_pair_rne(float a, float b)
@@ -266,11 +223,6 @@ __device__ __forceinline__ uint4 ld_nt16(const void *p)
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ uint4 ld16(const void *p)
-{
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
 // Unsigned division of n < 2^32 by a fixed d via a multiply and a shift
 // (round-up method: m = floor(2^32 (2^l - d) / d) + 1, l = ceil(log2 d)),
 // exact for every n < 2^32 and 1 <= d < 2^32.
@@ -304,19 +256,10 @@ __device__ __forceinline__ uint32_t ld_nt4(const void *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
-__device__ __forceinline__ void st_nt16(void *p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
-{
-    const u32x4_t v = {a, b, c, d};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
-}
 __device__ __forceinline__ void st_nt8(void *p, uint32_t a, uint32_t b)
 {
     const u32x2_t v = {a, b};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(p));
-}
-__device__ __forceinline__ void st_nt4(void *p, uint32_t a)
-{
-    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t *>(p));
 }
 
 }  // namespace mxq

@@ -11,7 +11,7 @@ namespace mxq {
 // Workgroups of `kernel` (launched with `block_threads` threads) that the
 // current device holds at once: compute units x the occupancy the runtime
 // reports for the kernel's register and LDS use.  Cached per kernel and
-// device; the persistent kernels launch exactly this many (or fewer).
+// device; grid-stride kernels size their grids from it.
 int64_t resident_workgroups(const void *kernel, int block_threads);
 
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,

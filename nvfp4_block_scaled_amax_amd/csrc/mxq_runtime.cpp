@@ -1,4 +1,4 @@
-// mxq_runtime.cpp -- launch geometry for the persistent kernels.
+// mxq_runtime.cpp -- launch geometry for the grid-stride kernels.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
