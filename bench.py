@@ -100,7 +100,7 @@ def build_legs(torch, mxq, api, W, log, want=lambda group: True):
         legs.append(Leg(f"mxfp8_rowcol_{name}",
                         (lambda x=x, rows=rows, cols=cols, rc=rc, rs=rs, cc=cc, cs=cs:
                          E.mxq_mxfp8_quantize_rowcol(x, rows, cols, rc, rs, cc, cs)),
-                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_tile_kernel<true, true, false, 4>"],
+                        2 * n, 2 * n + 2 * n // 32, n, ["mxfp8_tile_kernel<true, true, false, 4, false>"],
                         f"MXFP8 row+col {rows}x{cols}"))
     log("act/wgt ready")
 
@@ -113,6 +113,9 @@ def build_legs(torch, mxq, api, W, log, want=lambda group: True):
     if want("grp"):
         build_grp(torch, E, W, legs, dev, empty)
         log("grp ready")
+    if want("dsp"):
+        build_dsp(torch, E, W, legs, dev, empty)
+        log("dsp ready")
     return legs
 
 
@@ -126,7 +129,7 @@ def build_tok(torch, E, W, legs, dev, empty):
     y = empty((rows, cols), torch.bfloat16)
     q_out = n // 2 + n // 16 + 4 * rows
     legs.append(Leg("nvfp4_tok", lambda: E.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts),
-                    2 * n, q_out, n, ["nvfp4_token_kernel<2, true>"], "NVFP4 per-token 8192x2048"))
+                    2 * n, q_out, n, ["nvfp4_token_kernel<2, true, false>"], "NVFP4 per-token 8192x2048"))
     legs.append(Leg("nvfp4_tok_dequant",
                     lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, codes, bs, ts, 1, rows, cols, y),
                     q_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 8192x2048"))
@@ -186,11 +189,11 @@ def build_grp(torch, E, W, legs, dev, empty):
     nv_out = n // 2 + n // 16 + 4 * R
     legs.append(Leg("grouped_mxfp8_rowcol",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_MXFP8_ROWCOL, xg, R, K, off, G, g8),
-                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8>"],
+                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8, false>"],
                     f"grouped MXFP8 row+col {R}x{K}, {G} segments"))
     legs.append(Leg("grouped_nvfp4",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_NVFP4, xg, R, K, off, G, g4),
-                    2 * n + 8 * (G + 1), nv_out, n, ["nvfp4_token_kernel<2, true>"],
+                    2 * n + 8 * (G + 1), nv_out, n, ["nvfp4_token_kernel<2, true, false>"],
                     f"grouped per-token NVFP4 {R}x{K}"))
     y8, y4 = empty((R, K), torch.bfloat16), empty((R, K), torch.bfloat16)
     legs.append(Leg("grouped_dequant_mxfp8",
@@ -389,6 +392,60 @@ def config_timings(torch, E, W, legs, log):
             k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
             res[k] = v
     log("C4/C5 timed")
+
+    if "grouped_mxfp8_rowcol" in by_name:
+        res.update(dispatch_timings(torch, E, W, dev, empty))
+        log("C5 dispatch timed")
+    return res
+
+
+def build_dsp(torch, E, W, legs, dev, empty):
+    """The grouped workload quantized straight from its 32768 unpermuted tokens
+    (top-8 of 128 experts): MXFP8 row+col and per-token NVFP4, plus torch's own
+    row gather, the pass the fused call saves.  The algorithmic bytes read each
+    token once."""
+    tok_np, rt_np, tr_np, off_np = W.config5_dispatch()
+    T, K = tok_np.shape
+    R, G, top_k = rt_np.size, off_np.size - 1, tr_np.shape[1]
+    tok = dev(tok_np)
+    del tok_np
+    rt, tr, off = (torch.from_numpy(a).cuda() for a in (rt_np, tr_np, off_np))
+    n = R * K
+    col_scale_rows = int(sum((int(off_np[e + 1]) - int(off_np[e]) + 31) // 32 for e in range(G)))
+    g8 = {"row_codes": empty((R, K)), "row_scales": empty((R, K // 32)),
+          "col_codes": empty((R, K)), "col_scales": empty((R // 32 + G, K)),
+          "col_scale_offsets": empty((G + 1,), torch.int64)}
+    g4 = {"codes": empty((R, K // 2)), "block_scales": empty((R, K // 16)),
+          "token_scales": empty((R,), torch.float32)}
+    legs.append(Leg("dispatch_mxfp8_rowcol",
+                    lambda: E.mxq_grouped_quantize_dispatch(E.MXQ_FMT_MXFP8_ROWCOL, tok, T, K, 0,
+                                                            None, rt, R, off, G, g8),
+                    2 * T * K + 8 * R + 8 * (G + 1),
+                    2 * n + n // 32 + col_scale_rows * K + 8 * (G + 1), n,
+                    ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8, true>"],
+                    f"dispatch + grouped MXFP8 row+col, {T} tokens -> {R}x{K}, {G} segments"))
+    legs.append(Leg("dispatch_nvfp4",
+                    lambda: E.mxq_grouped_quantize_dispatch(E.MXQ_FMT_NVFP4, tok, T, K, top_k, tr,
+                                                            None, R, None, 0, g4),
+                    2 * T * K + 8 * T * top_k, n // 2 + n // 16 + 4 * R, n,
+                    ["nvfp4_token_kernel<2, true, true>"],
+                    f"dispatch + per-token NVFP4, {T} tokens -> {R}x{K} (top-{top_k})"))
+    xg = empty((R, K), torch.bfloat16)
+    tb = tok.view(torch.bfloat16)
+    legs.append(Leg("gather_torch", lambda: torch.index_select(tb, 0, rt, out=xg),
+                    2 * T * K + 8 * R, 2 * n, n, ["index_select"],
+                    f"torch.index_select of {R} rows of {T}x{K} BF16 (the copy a fused "
+                    "dispatch avoids)"))
+
+
+def dispatch_timings(torch, E, W, dev, empty):
+    legs = []
+    build_dsp(torch, E, W, legs, dev, empty)
+    res = {}
+    for l, cfg in zip(legs, ("C5_dispatch_mxfp8", "C5_dispatch_nvfp4", "C5_gather_torch")):
+        ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+        res[k] = v
     return res
 
 
@@ -403,7 +460,9 @@ def main():
                          "rotating buffer sets)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--groups", default="act,wgt,tok,exp,grp",
-                    help="comma list of leg groups to run (for profiling single kernels)")
+                    help="comma list of leg groups to run (for profiling single kernels); "
+                         "'dsp' adds the fused-dispatch legs, which replace the grouped legs' "
+                         "separate gather and are therefore not part of the default step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also time a plain elementwise copy of this many MiB (int32 bitwise "
                          "not, reads and writes each byte once), reported apart from the step, "
@@ -503,7 +562,7 @@ def main():
     # The export legs (four kernels, two reads of the weights) and the
     # three-launch export dequant are reported per leg but are not one launch.
     single = [l for l in legs if l.name not in ("nvfp4_export_gateup", "nvfp4_export_down",
-                                                "nvfp4_export_dequant")]
+                                                "nvfp4_export_dequant", "gather_torch")]
     dom = max(single or legs, key=lambda l: leg_info[l.name]["ms"])
     dom_ms = leg_info[dom.name]["ms"]
     achieved = dom.bytes / (dom_ms * 1e-3) / 1e9

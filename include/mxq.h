@@ -227,6 +227,40 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
                          int64_t n_groups, const mxq_grouped_out *out,
                          void *stream);
 
+/*
+ * Grouped quantize fused with MoE dispatch: reads the unpermuted tokens
+ * instead of a gathered copy.  Row r of the expert-sorted layout is token
+ * row_tokens[r] of x; copy c of token t is row token_rows[t * top_k + c].
+ * The outputs are byte-identical to mxq_grouped_quantize on the gathered
+ * tensor x[row_tokens[r]] (same segments, same fields).  NVFP4 quantizes
+ * each token once and writes it to its top_k rows: per-token outputs do not
+ * depend on the rest of the batch (the batch-invariance argument of the
+ * per-token activation paragraphs of the page "Miles: end-to-end MXFP8 and
+ * per-token NVFP4 RL on Blackwell"); MXFP8 columnwise blocks need the rows
+ * in segment order, so the tiles gather their rows through row_tokens.
+ *
+ *   fmt           MXQ_FMT_MXFP8_ROWCOL or MXQ_FMT_NVFP4.
+ *   x             [n_tokens][cols] BF16, 16-byte aligned.
+ *   token_rows    device int64 [n_tokens][top_k] (NVFP4; ignored for MXFP8).
+ *                 An entry outside [0, total_rows) is skipped (a dropped
+ *                 copy); a row that no entry names is left unwritten.
+ *   row_tokens    device int64 [total_rows] (MXFP8; ignored for NVFP4).
+ *                 Entries are clamped into [0, n_tokens).
+ *   seg_offsets   as mxq_grouped_quantize (MXFP8 columnwise only; may be
+ *                 NULL when only the rowwise copy is requested, and for
+ *                 NVFP4).
+ *   out           as mxq_grouped_quantize, over total_rows rows.
+ * The maps are device data, not validated on the host: when they are not
+ * inverse to each other the outputs are unspecified bytes, but no access
+ * leaves the arrays.  For NVFP4, n_tokens must be below 2^31.
+ */
+int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens,
+                                  int64_t cols, int64_t top_k,
+                                  const int64_t *token_rows,
+                                  const int64_t *row_tokens, int64_t total_rows,
+                                  const int64_t *seg_offsets, int64_t n_groups,
+                                  const mxq_grouped_out *out, void *stream);
+
 /* A static, human-readable message for a status code. */
 const char *mxq_status_string(int status);
 

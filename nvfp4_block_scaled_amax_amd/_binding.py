@@ -39,6 +39,7 @@ EXPORTS = (
     "mxq_nvfp4_quantize_gateup_pair",
     "mxq_dequantize_bf16",
     "mxq_grouped_quantize",
+    "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
     "mxq_version",
 )
@@ -76,6 +77,8 @@ def lib():
         "mxq_nvfp4_quantize_gateup_pair": [P, P, I64, I64, I64, P, P, P, P, P, P],
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
+        "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
+                                          ctypes.POINTER(mxq_grouped_out), P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -158,3 +161,15 @@ def mxq_grouped_quantize(fmt, x, total_rows, cols, seg_offsets, n_groups, out, s
     _check(lib().mxq_grouped_quantize(fmt, _ptr(x), total_rows, cols, _ptr(seg_offsets),
                                       n_groups, ctypes.byref(out), _stream(stream)),
            "mxq_grouped_quantize")
+
+
+def mxq_grouped_quantize_dispatch(fmt, x, n_tokens, cols, top_k, token_rows, row_tokens,
+                                  total_rows, seg_offsets, n_groups, out, stream=None):
+    """`out`: an mxq_grouped_out, or a dict with its field names."""
+    if not isinstance(out, mxq_grouped_out):
+        out = mxq_grouped_out(**{k: _ptr(v) for k, v in out.items()})
+    _check(lib().mxq_grouped_quantize_dispatch(fmt, _ptr(x), n_tokens, cols, top_k,
+                                               _ptr(token_rows), _ptr(row_tokens), total_rows,
+                                               _ptr(seg_offsets), n_groups, ctypes.byref(out),
+                                               _stream(stream)),
+           "mxq_grouped_quantize_dispatch")

@@ -126,3 +126,35 @@ def grouped_quantize_nvfp4(x, seg_offsets, stream=None) -> NVFP4:
                            {"codes": res.codes, "block_scales": res.block_scales,
                             "token_scales": res.fp32_scales}, stream)
     return res
+
+
+def dispatch_quantize_mxfp8(tokens, row_tokens, seg_offsets, stream=None) -> GroupedMXFP8:
+    """Grouped MXFP8 row+col of the expert-sorted rows tokens[row_tokens[r]],
+    read straight from the unpermuted tokens."""
+    tokens = _bf16_bits(tokens)
+    T, cols = tokens.shape
+    R = row_tokens.numel()
+    G = seg_offsets.numel() - 1
+    u8 = torch.uint8
+    out = GroupedMXFP8(_empty((R, cols), u8, tokens), _empty((R, cols // 32), u8, tokens),
+                       _empty((R, cols), u8, tokens), _empty((R // 32 + G, cols), u8, tokens),
+                       _empty((G + 1,), torch.int64, tokens))
+    B.mxq_grouped_quantize_dispatch(B.MXQ_FMT_MXFP8_ROWCOL, tokens, T, cols, 0, None,
+                                    row_tokens, R, seg_offsets, G, out._asdict(), stream)
+    return out
+
+
+def dispatch_quantize_nvfp4(tokens, token_rows, total_rows, stream=None) -> NVFP4:
+    """Per-token NVFP4 of every token, written to its rows token_rows[t][c]
+    of a [total_rows] expert-sorted layout."""
+    tokens = _bf16_bits(tokens)
+    T, cols = tokens.shape
+    top_k = token_rows.shape[1]
+    res = NVFP4(_empty((total_rows, cols // 2), torch.uint8, tokens),
+                _empty((total_rows, cols // 16), torch.uint8, tokens),
+                _empty((total_rows,), torch.float32, tokens))
+    B.mxq_grouped_quantize_dispatch(B.MXQ_FMT_NVFP4, tokens, T, cols, top_k, token_rows, None,
+                                    total_rows, None, 0,
+                                    {"codes": res.codes, "block_scales": res.block_scales,
+                                     "token_scales": res.fp32_scales}, stream)
+    return res

@@ -144,7 +144,7 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols, uin
     if (st != MXQ_OK)
         return st;
     return launched(mxq::launch_mxfp8_dense(x, rows, cols, row_codes, row_scales, col_codes,
-                                            col_scales, (hipStream_t)stream));
+                                            col_scales, nullptr, 0, (hipStream_t)stream));
 }
 
 int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
@@ -306,10 +306,86 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t
     if (!cc) {
         // Rowwise only: identical to the dense call over all rows.
         return launched(mxq::launch_mxfp8_dense(x, total_rows, cols, rc, rs, nullptr, nullptr,
-                                                (hipStream_t)stream));
+                                                nullptr, 0, (hipStream_t)stream));
     }
     return launched(mxq::launch_mxfp8_grouped(x, total_rows, cols, seg_offsets, n_groups, rc, rs,
-                                              cc, cs, P, (hipStream_t)stream));
+                                              cc, cs, P, nullptr, 0, (hipStream_t)stream));
+}
+
+int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens, int64_t cols,
+                                  int64_t top_k, const int64_t *token_rows,
+                                  const int64_t *row_tokens, int64_t total_rows,
+                                  const int64_t *seg_offsets, int64_t n_groups,
+                                  const mxq_grouped_out *out, void *stream)
+{
+    if (fmt != MXQ_FMT_MXFP8_ROWCOL && fmt != MXQ_FMT_NVFP4)
+        return MXQ_ERR_ARG;
+    if (!x || !out)
+        return MXQ_ERR_NULL;
+    if (!size_ok(n_tokens, cols) || !size_ok(total_rows, cols))
+        return MXQ_ERR_SIZE;
+    const int64_t nx = n_tokens * cols, n = total_rows * cols;
+    if (fmt == MXQ_FMT_NVFP4) {
+        if (!token_rows || !out->codes || !out->block_scales || !out->token_scales)
+            return MXQ_ERR_NULL;
+        if (top_k < 1 || !size_ok(n_tokens, top_k) || n_tokens > MAX_GRID_ROWS)
+            return MXQ_ERR_SIZE;
+        if (cols % 16 != 0)
+            return MXQ_ERR_SHAPE;
+        const Buf b[5] = {{x, 2 * nx, 16, false},
+                          {token_rows, 8 * n_tokens * top_k, 8, false},
+                          {out->codes, n / 2, 16, true},
+                          {out->block_scales, n / 16, 1, true},
+                          {out->token_scales, 4 * total_rows, 4, true}};
+        const int st = check_bufs(b, 5);
+        if (st != MXQ_OK)
+            return st;
+        return launched(mxq::launch_nvfp4_dispatch(x, n_tokens, cols, token_rows, top_k,
+                                                   total_rows, out->codes, out->block_scales,
+                                                   out->token_scales, (hipStream_t)stream));
+    }
+    if (!row_tokens)
+        return MXQ_ERR_NULL;
+    uint8_t *rc = out->row_codes, *rs = out->row_scales, *cc = out->col_codes,
+            *cs = out->col_scales;
+    int64_t *P = out->col_scale_offsets;
+    if ((rc == nullptr) != (rs == nullptr) || (cc == nullptr) != (cs == nullptr) ||
+        (cc != nullptr) != (P != nullptr) || (!rc && !cc))
+        return MXQ_ERR_OFFSETS;
+    if (cc && !seg_offsets)
+        return MXQ_ERR_NULL;
+    if (cc && (n_groups < 1 || n_groups > MAX_ELEMS / 8))
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0)
+        return MXQ_ERR_SHAPE;
+    if (cols > MAX_MXFP8_COLS)
+        return MXQ_ERR_SIZE;
+    const int64_t scale_rows = total_rows / 32 + (cc ? n_groups : 0);
+    if (scale_rows > MAX_ELEMS / cols)
+        return MXQ_ERR_SIZE;
+    Buf b[8];
+    int k = 0;
+    b[k++] = {x, 2 * nx, 16, false};
+    b[k++] = {row_tokens, 8 * total_rows, 8, false};
+    if (rc) {
+        b[k++] = {rc, n, 16, true};
+        b[k++] = {rs, n / 32, 1, true};
+    }
+    if (cc) {
+        b[k++] = {seg_offsets, 8 * (n_groups + 1), 8, false};
+        b[k++] = {cc, n, 16, true};
+        b[k++] = {cs, scale_rows * cols, 8, true};
+        b[k++] = {P, 8 * (n_groups + 1), 8, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    if (!cc)
+        return launched(mxq::launch_mxfp8_dense(x, total_rows, cols, rc, rs, nullptr, nullptr,
+                                                row_tokens, n_tokens, (hipStream_t)stream));
+    return launched(mxq::launch_mxfp8_grouped(x, total_rows, cols, seg_offsets, n_groups, rc, rs,
+                                              cc, cs, P, row_tokens, n_tokens,
+                                              (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -14,19 +14,30 @@ namespace mxq {
 // device; grid-stride kernels size their grids from it.
 int64_t resident_workgroups(const void *kernel, int block_threads);
 
+// row_tokens != nullptr (dispatch): row r is row row_tokens[r] of x.
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,
                               uint8_t *row_scales, uint8_t *col_codes, uint8_t *col_scales,
-                              hipStream_t stream);
+                              const int64_t *row_tokens, int64_t n_tokens, hipStream_t stream);
 
 // Writes P (col_scale_offsets) and quantizes; at most `max_tiles` column
 // blocks (the capacity of col_scales) are written whatever the offsets say.
+// row_tokens != nullptr (dispatch): row r of the grouped layout is row
+// row_tokens[r] of x (x has n_tokens rows; entries are clamped into range).
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,
                                 const int64_t *seg_offsets, int64_t n_groups, uint8_t *row_codes,
                                 uint8_t *row_scales, uint8_t *col_codes, uint8_t *col_scales,
-                                int64_t *col_scale_offsets, hipStream_t stream);
+                                int64_t *col_scale_offsets, const int64_t *row_tokens,
+                                int64_t n_tokens, hipStream_t stream);
 
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *block_scales, float *token_scales, hipStream_t stream);
+
+// Quantizes each token once and writes it to rows token_rows[t * top_k + c]
+// (c < top_k) of the outputs; rows outside [0, out_rows) are skipped.
+hipError_t launch_nvfp4_dispatch(const uint16_t *x, int64_t n_tokens, int64_t cols,
+                                 const int64_t *token_rows, int64_t top_k, int64_t out_rows,
+                                 uint8_t *codes, uint8_t *block_scales, float *token_scales,
+                                 hipStream_t stream);
 
 hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
                                int64_t rows, int64_t cols, uint8_t *gate_codes,

@@ -107,6 +107,37 @@ __device__ __forceinline__ void load_tile(uint32_t (&v)[8][4], const uint16_t *_
     }
 }
 
+// Dispatch: row r of the tile is token row_tokens[row0 + r] of x, clamped
+// into [0, n_tokens) (the map is device data the host cannot check: a bad
+// entry gives meaningless bytes, never an out-of-bounds read).  Rows past
+// nrows read the tile's last row and select zero, as in load_tile.
+template <bool FULL>
+__device__ __forceinline__ void load_tile_gather(uint32_t (&v)[8][4],
+                                                 const uint16_t *__restrict__ x,
+                                                 const int64_t *__restrict__ row_tokens,
+                                                 int64_t n_tokens, int64_t cols, int64_t row0,
+                                                 int64_t col, int nrows, int rg, bool col_ok)
+{
+    const int last = nrows > 0 ? nrows - 1 : 0;
+    const int64_t c = FULL || col_ok ? col : 0;
+    int64_t tok[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int r = 8 * rg + i;
+        const bool keep = FULL || (col_ok && r < nrows);
+        int64_t t = row_tokens[row0 + (keep ? r : last)];
+        tok[i] = t < 0 ? 0 : (t >= n_tokens ? n_tokens - 1 : t);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int r = 8 * rg + i;
+        const bool keep = FULL || (col_ok && r < nrows);
+        const uint4 q = ld_nt16(x + tok[i] * cols + c);
+        v[i][0] = keep ? q.x : 0u; v[i][1] = keep ? q.y : 0u;
+        v[i][2] = keep ? q.z : 0u; v[i][3] = keep ? q.w : 0u;
+    }
+}
+
 // Tile outputs: wave-uniform bases at (row0, strip column 0).
 struct TileOut {
     uint8_t *rc, *rs, *cc, *cs;     // row codes, row scales, col codes, col scales
@@ -195,6 +226,8 @@ struct Geometry {
     const int64_t *off;    // grouped: segment offsets
     const int64_t *P;      // grouped: prefix of ceil(n_e / 32)
     int64_t n_groups;
+    const int64_t *row_tokens;  // dispatch: token of each (expert-sorted) row, else nullptr
+    int64_t n_tokens;           // dispatch: rows of x
 };
 
 // Segment e's rows clamped into [0, total_rows): offsets are device data the
@@ -229,7 +262,7 @@ __device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, i
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
-template <bool ROW, bool COL, bool GROUPED, int WPW>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
 __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_t *__restrict__ rc,
                                                          uint8_t *__restrict__ rs,
                                                          uint8_t *__restrict__ cc,
@@ -269,10 +302,18 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_
     const TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol};
     uint32_t v[8][4];
     if (full) {
-        load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
+        if constexpr (GATHER)
+            load_tile_gather<true>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
+                                   t.nrows, rg, col_ok);
+        else
+            load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
         convert_tile<ROW, COL, true>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
-        load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
+        if constexpr (GATHER)
+            load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
+                                    t.nrows, rg, col_ok);
+        else
+            load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
         convert_tile<ROW, COL, false>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
 }
@@ -320,49 +361,55 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // workgroups leave CUs idle (8192 x 2048: 20.5 us with 8, 17.3 us with 4).
 constexpr int64_t LARGE_LAUNCH_WAVES = 32768;
 
-template <bool ROW, bool COL, bool GROUPED, int WPW>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
 static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
                              uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
     const int64_t wgs = (waves + WPW - 1) / WPW;
     if (wgs > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER>), dim3((unsigned)wgs),
                        dim3(64 * WPW), 0, stream, G, rc, rs, cc, cs);
     return hipGetLastError();
 }
 
-template <bool ROW, bool COL, bool GROUPED>
+template <bool ROW, bool COL, bool GROUPED, bool GATHER>
 static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc,
                              uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
     const int64_t waves = tiles_per_strip * G.nct;
     if (waves >= LARGE_LAUNCH_WAVES)
-        return launch_wpw<ROW, COL, GROUPED, 8>(G, waves, rc, rs, cc, cs, stream);
-    return launch_wpw<ROW, COL, GROUPED, 4>(G, waves, rc, rs, cc, cs, stream);
+        return launch_wpw<ROW, COL, GROUPED, 8, GATHER>(G, waves, rc, rs, cc, cs, stream);
+    return launch_wpw<ROW, COL, GROUPED, 4, GATHER>(G, waves, rc, rs, cc, cs, stream);
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool GATHER>
 static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc, uint8_t *rs,
                          uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
     if (rc && cc)
-        return launch_one<true, true, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+        return launch_one<true, true, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
     if (rc)
-        return launch_one<true, false, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
-    return launch_one<false, true, GROUPED>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+        return launch_one<true, false, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+    return launch_one<false, true, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
 }
 
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
-                              uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
+                              uint8_t *rs, uint8_t *cc, uint8_t *cs, const int64_t *row_tokens,
+                              int64_t n_tokens, hipStream_t stream)
 {
-    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0};
-    return launch<false>(G, (rows + TILE_ROWS - 1) / TILE_ROWS, rc, rs, cc, cs, stream);
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0,
+               row_tokens, n_tokens};
+    const int64_t tiles = (rows + TILE_ROWS - 1) / TILE_ROWS;
+    if (row_tokens)
+        return launch<false, true>(G, tiles, rc, rs, cc, cs, stream);
+    return launch<false, false>(G, tiles, rc, rs, cc, cs, stream);
 }
 
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,
                                 const int64_t *off, int64_t n_groups, uint8_t *rc, uint8_t *rs,
-                                uint8_t *cc, uint8_t *cs, int64_t *P, hipStream_t stream)
+                                uint8_t *cc, uint8_t *cs, int64_t *P,
+                                const int64_t *row_tokens, int64_t n_tokens, hipStream_t stream)
 {
     hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
                        total_rows, P);
@@ -371,8 +418,10 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
         return err;
     const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
-               n_groups};
-    return launch<true>(G, max_tiles, rc, rs, cc, cs, stream);
+               n_groups, row_tokens, n_tokens};
+    if (row_tokens)
+        return launch<true, true>(G, max_tiles, rc, rs, cc, cs, stream);
+    return launch<true, false>(G, max_tiles, rc, rs, cc, cs, stream);
 }
 
 }  // namespace mxq

@@ -249,25 +249,29 @@ __device__ __forceinline__ void emit_blk(const BlkOut &o, int64_t j, uint8_t *__
 constexpr int WG_THREADS = 64;
 constexpr int ROWS_PER_WG = WG_THREADS / 64;
 
-__device__ __forceinline__ ScaleK token_scale(uint32_t amax_bits, int64_t row,
-                                              float *__restrict__ ts)
-{
-    const float s = div2688(u2f(amax_bits));
-    if (lane_id() == 0)
-        ts[row] = s;
-    return scale_k(s);
-}
+// Where a row's outputs go.  Per-token call: row i of the input is row i of
+// the outputs.  Dispatch call: the input rows are tokens, and token t's
+// outputs are written to each valid row dest[t * copies + c] of the outputs
+// (the expert-sorted rows holding that token); a row index outside
+// [0, out_rows) is skipped, so a malformed map cannot move a write out of
+// bounds.
+struct Dest {
+    const int64_t *dest;    // nullptr: identity
+    int64_t copies;
+    int64_t out_rows;
+};
 
 // Rows of up to 64 NB blocks (1024 NB elements), held in registers.  FULL:
 // exactly 64 NB blocks (no lane idle); otherwise missing blocks load a valid
 // address and are zeroed (no divergent loads) and are not stored.
-template <int NB, bool FULL>
-__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
-nvfp4_token_kernel(const uint16_t *__restrict__ x,
-                                                                 int64_t rows, int64_t cols,
-                                                                 uint8_t *__restrict__ codes,
-                                                                 uint8_t *__restrict__ bs,
-                                                                 float *__restrict__ ts)
+// Rows of up to 2048 elements fit 64 VGPRs (8 wavefronts per SIMD) without
+// spilling; longer ones are left to the compiler's occupancy choice.
+template <int NB, bool FULL, bool SCATTER>
+__global__ void __launch_bounds__(WG_THREADS)
+__attribute__((amdgpu_waves_per_eu(NB <= 2 ? 8 : 1, 8)))
+nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                   uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
+                   float *__restrict__ ts, Dest dst)
 {
     const int64_t row = (int64_t)wg_id() * ROWS_PER_WG + wave_in_group();
     if (row >= rows)
@@ -296,21 +300,48 @@ nvfp4_token_kernel(const uint16_t *__restrict__ x,
         f[k] = unpack_blk(r[k]);
         A = max(A, f[k].amax);
     }
-    const ScaleK sk = token_scale(__builtin_amdgcn_readfirstlane(wave_max_u32(A)), row, ts);
-    uint8_t *crow = codes + row * (cols >> 1);
-    uint8_t *brow = bs + row * (cols >> 4);
+    const float s = div2688(u2f(__builtin_amdgcn_readfirstlane(wave_max_u32(A))));
+    const ScaleK sk = scale_k(s);
+    if constexpr (!SCATTER) {
+        if (lane == 0)
+            ts[row] = s;
+        uint8_t *crow = codes + row * (cols >> 1);
+        uint8_t *brow = bs + row * (cols >> 4);
 #pragma unroll
-    for (int k = 0; k < NB; k++) {
-        const int j = lane + 64 * k;
-        if (FULL || j < nblk)
-            emit_blk(quant_blk(r[k], f[k], sk), j, crow, brow);
+        for (int k = 0; k < NB; k++) {
+            const int j = lane + 64 * k;
+            if (FULL || j < nblk)
+                emit_blk(quant_blk(r[k], f[k], sk), j, crow, brow);
+        }
+    } else {
+        BlkOut o[NB];
+#pragma unroll
+        for (int k = 0; k < NB; k++)
+            o[k] = quant_blk(r[k], f[k], sk);
+        for (int64_t c = 0; c < dst.copies; c++) {
+            const int64_t orow = dst.dest[row * dst.copies + c];      // wave-uniform
+            if (orow < 0 || orow >= dst.out_rows)
+                continue;
+            if (lane == 0)
+                ts[orow] = s;
+            uint8_t *crow = codes + orow * (cols >> 1);
+            uint8_t *brow = bs + orow * (cols >> 4);
+#pragma unroll
+            for (int k = 0; k < NB; k++) {
+                const int j = lane + 64 * k;
+                if (FULL || j < nblk)
+                    emit_blk(o[k], j, crow, brow);
+            }
+        }
     }
 }
 
-// Longer rows: read twice (amax, then codes).
+// Longer rows: read twice (amax, then codes).  Dispatch: each block is
+// written to every destination row as it is produced.
+template <bool SCATTER>
 __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ bs, float *__restrict__ ts)
+    uint8_t *__restrict__ bs, float *__restrict__ ts, Dest dst)
 {
     const int64_t row = (int64_t)wg_id() * ROWS_PER_WG + wave_in_group();
     if (row >= rows)
@@ -324,13 +355,31 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
         load_blk(b, xr + 16 * j);
         A = max(A, unpack_blk(b).amax);
     }
-    const ScaleK sk = token_scale(__builtin_amdgcn_readfirstlane(wave_max_u32(A)), row, ts);
-    uint8_t *crow = codes + row * (cols >> 1);
-    uint8_t *brow = bs + row * (cols >> 4);
+    const float s = div2688(u2f(__builtin_amdgcn_readfirstlane(wave_max_u32(A))));
+    const ScaleK sk = scale_k(s);
+    if constexpr (!SCATTER) {
+        if (lane == 0)
+            ts[row] = s;
+    } else {
+        for (int64_t c = 0; c < dst.copies; c++) {
+            const int64_t orow = dst.dest[row * dst.copies + c];
+            if (lane == 0 && orow >= 0 && orow < dst.out_rows)
+                ts[orow] = s;
+        }
+    }
     for (int64_t j = lane; j < nblk; j += 64) {
         Blk b;
         load_blk(b, xr + 16 * j);
-        emit_blk(quant_blk(b, unpack_blk(b), sk), j, crow, brow);
+        const BlkOut o = quant_blk(b, unpack_blk(b), sk);
+        if constexpr (!SCATTER) {
+            emit_blk(o, j, codes + row * (cols >> 1), bs + row * (cols >> 4));
+        } else {
+            for (int64_t c = 0; c < dst.copies; c++) {
+                const int64_t orow = dst.dest[row * dst.copies + c];
+                if (orow >= 0 && orow < dst.out_rows)
+                    emit_blk(o, j, codes + orow * (cols >> 1), bs + orow * (cols >> 4));
+            }
+        }
     }
 }
 
@@ -436,38 +485,53 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_scoped_kernel(const uint16_t
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <int NB, bool FULL>
+template <int NB, bool FULL, bool SCATTER>
 static void launch_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
-                         uint8_t *bs, float *ts, hipStream_t stream)
+                         uint8_t *bs, float *ts, Dest dst, hipStream_t stream)
 {
     const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(WG_THREADS);
-    hipLaunchKernelGGL((nvfp4_token_kernel<NB, FULL>), grid, block, 0, stream, x, rows, cols,
-                       codes, bs, ts);
+    hipLaunchKernelGGL((nvfp4_token_kernel<NB, FULL, SCATTER>), grid, block, 0, stream, x, rows,
+                       cols, codes, bs, ts, dst);
 }
 
-hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
-                                  uint8_t *bs, float *ts, hipStream_t stream)
+template <bool SCATTER>
+static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                              uint8_t *bs, float *ts, Dest dst, hipStream_t stream)
 {
     // rows < 2^31: checked by the caller.
     const int64_t nblk = cols >> 4;
     const int64_t nb = (nblk + 63) / 64;
     const bool full = nblk == 64 * nb;
     switch (nb) {
-    case 1: full ? launch_token<1, true>(x, rows, cols, codes, bs, ts, stream)
-                 : launch_token<1, false>(x, rows, cols, codes, bs, ts, stream); break;
-    case 2: full ? launch_token<2, true>(x, rows, cols, codes, bs, ts, stream)
-                 : launch_token<2, false>(x, rows, cols, codes, bs, ts, stream); break;
-    case 3: full ? launch_token<3, true>(x, rows, cols, codes, bs, ts, stream)
-                 : launch_token<3, false>(x, rows, cols, codes, bs, ts, stream); break;
-    case 4: full ? launch_token<4, true>(x, rows, cols, codes, bs, ts, stream)
-                 : launch_token<4, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 1: full ? launch_token<1, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<1, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 2: full ? launch_token<2, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<2, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 3: full ? launch_token<3, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<3, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 4: full ? launch_token<4, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<4, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
     default: {
         const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(WG_THREADS);
-        hipLaunchKernelGGL(nvfp4_token_long_kernel, grid, block, 0, stream, x, rows, cols, codes,
-                           bs, ts);
+        hipLaunchKernelGGL((nvfp4_token_long_kernel<SCATTER>), grid, block, 0, stream, x, rows,
+                           cols, codes, bs, ts, dst);
     }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                                  uint8_t *bs, float *ts, hipStream_t stream)
+{
+    return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows}, stream);
+}
+
+hipError_t launch_nvfp4_dispatch(const uint16_t *x, int64_t n_tokens, int64_t cols,
+                                 const int64_t *token_rows, int64_t top_k, int64_t out_rows,
+                                 uint8_t *codes, uint8_t *bs, float *ts, hipStream_t stream)
+{
+    return launch_rows<true>(x, n_tokens, cols, codes, bs, ts,
+                             Dest{token_rows, top_k, out_rows}, stream);
 }
 
 hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,

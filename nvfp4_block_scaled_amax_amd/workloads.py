@@ -225,6 +225,38 @@ def routing(n_tokens: int = N_TOKENS, n_experts: int = N_EXPERTS, top_k: int = T
     return tok[order], offsets
 
 
+def dispatch_maps(n_tokens: int = N_TOKENS, n_experts: int = N_EXPERTS, top_k: int = TOP_K,
+                  seed: int = 6, drop: float = 0.0):
+    """Routing of `routing` (same draws for drop = 0) as the two index maps of
+    a fused dispatch: row_tokens[R] (token of each expert-sorted row),
+    token_rows[n_tokens][top_k] (row of each copy; -1 for a dropped copy) and
+    the segment offsets[E+1].  drop > 0 drops that fraction of the copies
+    (seed + 1000 picks them), as a capacity limit would."""
+    rng = np.random.default_rng(seed)
+    choice = rng.random((n_tokens, n_experts)).argsort(1)[:, :top_k]
+    tok = np.repeat(np.arange(n_tokens, dtype=np.int64), top_k)
+    exp = choice.reshape(-1).astype(np.int64)
+    keep = np.ones(tok.size, bool)
+    if drop > 0:
+        keep = np.random.default_rng(seed + 1000).random(tok.size) >= drop
+    flat = np.nonzero(keep)[0]
+    order = flat[np.lexsort((tok[flat], exp[flat]))]      # flat copy index of each row
+    counts = np.bincount(exp[flat], minlength=n_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    token_rows = np.full(tok.size, -1, np.int64)
+    token_rows[order] = np.arange(order.size, dtype=np.int64)
+    return tok[order], token_rows.reshape(n_tokens, top_k), offsets
+
+
+def config5_dispatch(n_tokens: int = N_TOKENS, hidden: int = HIDDEN):
+    """Config 5's tokens (unpermuted, [n_tokens][hidden]) and routing as
+    dispatch maps: (tokens, row_tokens, token_rows, offsets).  Gathering
+    tokens[row_tokens] gives exactly config5()'s X."""
+    tokens = student_t_activations(n_tokens, hidden, 5)
+    row_tokens, token_rows, offsets = dispatch_maps(n_tokens, N_EXPERTS, TOP_K, 6)
+    return tokens, row_tokens, token_rows, offsets
+
+
 def config5(n_tokens: int = N_TOKENS, hidden: int = HIDDEN):
     """Grouped MoE input: tokens Student-t(3)*0.5 (seed 5) routed top-8 of 128
     experts (seed 6), gathered expert-sorted.  Returns (X[R][hidden],

@@ -91,6 +91,25 @@ def test_validation_before_any_device_call():
     assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 64, 32, A, 2, bad, 0) == mxq.MXQ_ERR_OFFSETS
     assert status_of(g, mxq.MXQ_FMT_NVFP4, A, 64, 32, A, 2, {"codes": A}, 0) == mxq.MXQ_ERR_NULL
 
+    gd = mxq.mxq_grouped_quantize_dispatch
+    nv = {"codes": A, "block_scales": A, "token_scales": A}
+    F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL
+    assert status_of(gd, mxq.MXQ_FMT_MXFP8_ROW, A, 8, 32, 1, A, A, 8, A, 1, out8, 0) == \
+        mxq.MXQ_ERR_ARG
+    assert status_of(gd, F4, A, 8, 32, 2, None, None, 16, None, 0, nv, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gd, F4, A, 8, 32, 0, A, None, 16, None, 0, nv, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gd, F4, A, 8, 24, 2, A, None, 16, None, 0, nv, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(gd, F4, A, -1, 32, 2, A, None, 16, None, 0, nv, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gd, F4, A, 8, 32, 2, A + 4, None, 16, None, 0, nv, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gd, F8, A, 8, 32, 0, None, None, 16, A, 1, out8, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gd, F8, A, 8, 32, 0, None, A, 16, None, 1, out8, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gd, F8, A, 8, 32, 0, None, A, 16, A, 0, out8, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gd, F8, A, 8, 48, 0, None, A, 16, A, 1, out8, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(gd, F8, A, 8, 32, 0, None, A, 16, A, 1, bad, 0) == mxq.MXQ_ERR_OFFSETS
+    row_only = {"row_codes": A, "row_scales": A}
+    assert status_of(gd, F8, A, 8, 32, 0, None, A + 4, 16, None, 0, row_only, 0) == \
+        mxq.MXQ_ERR_ALIGN
+
 
 def test_fake_device_pointers_rejected_without_gpu():
     """Well-formed arguments that are not device memory fail host-side."""

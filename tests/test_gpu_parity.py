@@ -447,6 +447,78 @@ def test_grouped_config5_full(orc):
 
 
 # ---------------------------------------------------------------------------
+# Grouped quantize fused with dispatch (reads the unpermuted tokens)
+# ---------------------------------------------------------------------------
+
+def check_dispatch(orc, tokens, row_tokens, token_rows, off, name, seg_sample=None,
+                   row_sample=None):
+    """Both dispatch outputs against the oracle on the gathered rows
+    tokens[row_tokens] (the definition of the fused call)."""
+    R, K = row_tokens.size, tokens.shape[1]
+    announce(f"dispatch {name} T={tokens.shape[0]} R={R} K={K} G={off.size - 1}")
+    td = dev(tokens)
+    d8 = api.dispatch_quantize_mxfp8(td, torch.from_numpy(row_tokens).cuda(),
+                                     torch.from_numpy(off).cuda())
+    d4 = api.dispatch_quantize_nvfp4(td, torch.from_numpy(token_rows).cuda(), R)
+    torch.cuda.synchronize()
+    x = tokens[row_tokens]
+    G = off.size - 1
+    P = host(d8.col_scale_offsets)
+    counts = [(int(off[e + 1]) - int(off[e]) + 31) // 32 for e in range(G)]
+    assert list(P) == list(np.concatenate([[0], np.cumsum(counts)]))
+    rc, rs, cc, cs = host(d8.row_codes), host(d8.row_scales), host(d8.col_codes), \
+        host(d8.col_scales)
+    for e in (range(G) if seg_sample is None else seg_sample):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        seg = x[a:b]
+        oc, os_, _ = orc.mxfp8_colwise_grouped(seg, np.array([0, b - a], np.int64))
+        assert_same(cc[a:b], oc, f"{name} seg{e} col codes")
+        assert_same(cs[P[e]:P[e + 1]], os_, f"{name} seg{e} col scales")
+        orow, orows = orc.mxfp8_rowwise(seg)
+        assert_same(rc[a:b], orow, f"{name} seg{e} row codes")
+        assert_same(rs[a:b], orows, f"{name} seg{e} row scales")
+    rows = np.arange(R) if row_sample is None else np.asarray(row_sample)
+    nc, nb, ns = orc.nvfp4_per_token(np.ascontiguousarray(x[rows]))
+    assert_same(host(d4.codes)[rows], nc, f"{name} nvfp4 codes")
+    assert_same(host(d4.block_scales)[rows], nb, f"{name} nvfp4 bs")
+    assert_same(host(d4.fp32_scales)[rows].view(np.uint32), ns.view(np.uint32),
+                f"{name} nvfp4 s")
+    return d8, d4
+
+
+def test_dispatch_small_with_dropped_copies(orc):
+    """300 tokens, top-3 of 8 experts, 30% of the copies dropped (a capacity
+    limit): token_rows holds -1 for them and rows only for the kept copies."""
+    row_tokens, token_rows, off = W.dispatch_maps(300, 8, 3, seed=11, drop=0.3)
+    tokens = W.student_t_activations(300, 256, 12)
+    check_dispatch(orc, tokens, row_tokens, token_rows, off, "small dropped")
+
+
+def test_dispatch_shapes(orc):
+    """Short rows (K = 96: partial NVFP4 row, one partial MXFP8 strip), long
+    rows (K = 4160: the two-pass NVFP4 kernel) and empty experts."""
+    row_tokens, token_rows, off = W.dispatch_maps(200, 40, 2, seed=13)
+    check_dispatch(orc, W.student_t_activations(200, 96, 14), row_tokens, token_rows, off,
+                   "K96 40 experts")
+    row_tokens, token_rows, off = W.dispatch_maps(70, 6, 2, seed=15)
+    check_dispatch(orc, W.student_t_activations(70, 4160, 16), row_tokens, token_rows, off,
+                   "K4160")
+
+
+def test_dispatch_config5_full(orc):
+    """The grouped workload read from its 32,768 unpermuted tokens (top-8 of
+    128), sampled segments and rows."""
+    tokens, row_tokens, token_rows, off = W.config5_dispatch()
+    rng = np.random.default_rng(17)
+    sample = np.concatenate([np.arange(64), rng.integers(0, row_tokens.size, 2048),
+                             np.arange(row_tokens.size - 64, row_tokens.size)])
+    check_dispatch(orc, tokens, row_tokens, token_rows, off, "config5",
+                   seg_sample=[0, 1, 64, 127], row_sample=sample)
+
+
+# ---------------------------------------------------------------------------
 # Error paths: nothing launched, nothing written
 # ---------------------------------------------------------------------------
 
@@ -554,3 +626,74 @@ def test_grouped_malformed_offsets_stay_in_bounds():
     torch.cuda.synchronize()
     assert bool((big[:guard] == 0x5A).all()) and bool((big[-guard:] == 0x5A).all())
     assert bool((cs_big[:guard] == 0x5A).all()) and bool((cs_big[-guard:] == 0x5A).all())
+
+
+def test_dispatch_malformed_maps_stay_in_bounds():
+    """The index maps are device data: token_rows entries outside the output
+    rows are skipped and row_tokens entries outside the tokens are clamped,
+    so no access leaves the arrays (the bytes are meaningless).  Outputs are
+    bracketed by canaries."""
+    T, cols, R = 16, 64, 40
+    x = dev(W.mode_random(T, cols, 21))
+    guard = 4096
+    token_rows = torch.tensor([[-1, R, 10 ** 9, 3]] * T, dtype=torch.int64, device="cuda")
+    c_big = torch.full((R * cols // 2 + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    b_big = torch.full((R * cols // 16 + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    s_big = torch.full((R + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    announce("dispatch malformed token_rows")
+    mxq.mxq_grouped_quantize_dispatch(
+        mxq.MXQ_FMT_NVFP4, x, T, cols, 4, token_rows, None, R, None, 0,
+        {"codes": c_big[guard:guard + R * cols // 2],
+         "block_scales": b_big[guard:guard + R * cols // 16],
+         "token_scales": s_big[guard:guard + R]})
+    torch.cuda.synchronize()
+    for big, fill in ((c_big, 0x5A), (b_big, 0x5A), (s_big, 7.0)):
+        assert bool((big[:guard] == fill).all()) and bool((big[-guard:] == fill).all())
+    row_tokens = torch.tensor([-3, 10 ** 9] * (R // 2), dtype=torch.int64, device="cuda")
+    off = torch.tensor([0, 7, R], dtype=torch.int64, device="cuda")
+    G = 2
+    rc_big = torch.full((R * cols + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    cs_big = torch.full(((R // 32 + G) * cols + 2 * guard,), 0x5A, dtype=torch.uint8,
+                        device="cuda")
+    announce("dispatch malformed row_tokens")
+    mxq.mxq_grouped_quantize_dispatch(
+        mxq.MXQ_FMT_MXFP8_ROWCOL, x, T, cols, 0, None, row_tokens, R, off, G,
+        {"row_codes": rc_big[guard:guard + R * cols],
+         "row_scales": torch.empty(R * cols // 32, dtype=torch.uint8, device="cuda"),
+         "col_codes": torch.empty(R * cols, dtype=torch.uint8, device="cuda"),
+         "col_scales": cs_big[guard:guard + (R // 32 + G) * cols],
+         "col_scale_offsets": torch.empty(G + 1, dtype=torch.int64, device="cuda")})
+    torch.cuda.synchronize()
+    for big in (rc_big, cs_big):
+        assert bool((big[:guard] == 0x5A).all()) and bool((big[-guard:] == 0x5A).all())
+
+
+def test_dispatch_mxfp8_single_copy(orc):
+    """Rowwise-only (the dense kernel with a row gather) and columnwise-only
+    dispatch calls give the same bytes as the two-copy call."""
+    row_tokens, token_rows, off = W.dispatch_maps(500, 16, 4, seed=19)
+    tokens = W.student_t_activations(500, 512, 20)
+    d8, _ = check_dispatch(orc, tokens, row_tokens, token_rows, off, "single copy ref",
+                           row_sample=[0])
+    R, cols, G = row_tokens.size, 512, off.size - 1
+    td, rt, od = dev(tokens), torch.from_numpy(row_tokens).cuda(), torch.from_numpy(off).cuda()
+    rc = torch.empty(R * cols, dtype=torch.uint8, device="cuda")
+    rs = torch.empty(R * cols // 32, dtype=torch.uint8, device="cuda")
+    announce("dispatch rowwise only")
+    mxq.mxq_grouped_quantize_dispatch(mxq.MXQ_FMT_MXFP8_ROWCOL, td, 500, cols, 0, None, rt, R,
+                                      None, 0, {"row_codes": rc, "row_scales": rs})
+    cc = torch.empty(R * cols, dtype=torch.uint8, device="cuda")
+    cs = torch.empty((R // 32 + G) * cols, dtype=torch.uint8, device="cuda")
+    P = torch.empty(G + 1, dtype=torch.int64, device="cuda")
+    announce("dispatch columnwise only")
+    mxq.mxq_grouped_quantize_dispatch(mxq.MXQ_FMT_MXFP8_ROWCOL, td, 500, cols, 0, None, rt, R,
+                                      od, G, {"col_codes": cc, "col_scales": cs,
+                                              "col_scale_offsets": P})
+    torch.cuda.synchronize()
+    assert_same(host(rc).reshape(R, cols), host(d8.row_codes), "row-only codes")
+    assert_same(host(rs).reshape(R, cols // 32), host(d8.row_scales), "row-only scales")
+    assert_same(host(cc).reshape(R, cols), host(d8.col_codes), "col-only codes")
+    used = int(off.size and host(d8.col_scale_offsets)[-1])      # rows past P[G] are unused
+    assert_same(host(cs).reshape(-1, cols)[:used], host(d8.col_scales)[:used],
+                "col-only scales")
+    assert_same(host(P), host(d8.col_scale_offsets), "col-only offsets")
