@@ -242,6 +242,13 @@ static inline Div make_div(uint32_t d)
     return Div{(uint32_t)m, l};
 }
 
+// Gathered rows are re-read (a token by each expert it is routed to), so
+// they are loaded with the default cache policy.
+__device__ __forceinline__ uint4 ld16(const void *p)
+{
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ uint2 ld_nt8(const void *p)
 {
     const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
@@ -260,6 +267,11 @@ __device__ __forceinline__ void st_nt8(void *p, uint32_t a, uint32_t b)
 {
     const u32x2_t v = {a, b};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(p));
+}
+__device__ __forceinline__ void st8(void *p, uint32_t a, uint32_t b)
+{
+    const u32x2_t v = {a, b};
+    *reinterpret_cast<u32x2_t *>(p) = v;
 }
 
 }  // namespace mxq
