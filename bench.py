@@ -39,7 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 CSRC = os.path.join(ROOT, "nvfp4_block_scaled_amax_amd", "csrc")
-COMMON_SOURCES = ["mxq_device.h", "mxq_launch.h", "mxq_runtime.cpp", "../build.py"]
+COMMON_SOURCES = ["mxq_device.h", "mxq_dequant.h", "mxq_launch.h", "mxq_runtime.cpp", "../build.py"]
 KERNEL_SOURCES = {
     "mxfp8_tile_kernel": ["mxq_mxfp8.hip"],
     "grouped_prefix_kernel": ["mxq_mxfp8.hip"],
@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     "nvfp4_scoped_kernel": ["mxq_nvfp4.hip"],
     "dequant_mxfp8_kernel": ["mxq_dequant.hip"],
     "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
+    "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
+    "nvfp4_token_qdq_kernel": ["mxq_nvfp4.hip"],
 }
 
 
@@ -116,6 +118,9 @@ def build_legs(torch, mxq, api, W, log, want=lambda group: True):
     if want("dsp"):
         build_dsp(torch, E, W, legs, dev, empty)
         log("dsp ready")
+    if want("qdq"):
+        build_qdq(torch, E, W, legs, dev, empty)
+        log("qdq ready")
     return legs
 
 
@@ -169,6 +174,9 @@ def build_exp(torch, E, W, legs, dev, empty):
                     ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 of gate, up, down"))
 
 
+_SHARED = {}     # inputs one leg group lends another (generated once)
+
+
 def build_grp(torch, E, W, legs, dev, empty):
     """Grouped MXFP8 row+col and NVFP4 over 262144 expert-sorted rows, + dequant."""
     u8 = torch.uint8
@@ -177,6 +185,7 @@ def build_grp(torch, E, W, legs, dev, empty):
     G = off_np.size - 1
     xg = dev(xg_np)
     del xg_np
+    _SHARED["grouped_x"] = xg
     off = torch.from_numpy(off_np).cuda()
     n = R * K
     g8 = {"row_codes": empty((R, K)), "row_scales": empty((R, K // 32)),
@@ -396,6 +405,79 @@ def config_timings(torch, E, W, legs, log):
     if "grouped_mxfp8_rowcol" in by_name:
         res.update(dispatch_timings(torch, E, W, dev, empty))
         log("C5 dispatch timed")
+        res.update(qdq_timings(torch, E, W, dev, empty))
+        log("quantize + dequant timed")
+    return res
+
+
+def build_qdq(torch, E, W, legs, dev, empty):
+    """Quantize + BF16 dequant in one pass over the grouped rows (262144 x
+    2048, Student-t): rowwise MXFP8 and per-token NVFP4.  Each is the
+    alternative to a quantize leg followed by its dequant leg."""
+    xg = _SHARED.get("grouped_x")
+    if xg is None:
+        xg = dev(W.student_t_activations(262144, 2048, 5))
+    R, K = xg.shape
+    n = R * K
+    y = empty((R, K), torch.bfloat16)
+    rc, rs = empty((R, K)), empty((R, K // 32))
+    c4, b4, t4 = empty((R, K // 2)), empty((R, K // 16)), empty((R,), torch.float32)
+    legs.append(Leg("qdq_mxfp8_rowwise",
+                    lambda: E.mxq_quantize_dequant_bf16(E.MXQ_FMT_MXFP8_ROW, xg, R, K, rc, rs, None,
+                                                        y),
+                    2 * n, n + n // 32 + 2 * n, n, ["mxfp8_row_qdq_kernel<true, 8>"],
+                    f"MXFP8 rowwise quantize + BF16 dequant, one pass, {R}x{K}"))
+    legs.append(Leg("qdq_nvfp4",
+                    lambda: E.mxq_quantize_dequant_bf16(E.MXQ_FMT_NVFP4, xg, R, K, c4, b4, t4, y),
+                    2 * n, n // 2 + n // 16 + 4 * R + 2 * n, n,
+                    ["nvfp4_token_qdq_kernel<2, true>"],
+                    f"per-token NVFP4 quantize + BF16 dequant, one pass, {R}x{K}"))
+
+
+def qdq_small_timings(torch, E, W, dev, empty):
+    """One-pass quantize + dequant on the 8192 x 2048 shapes (weight, random
+    mode; Student-t activations), rotating buffer sets over 1 GiB."""
+    res = {}
+    rows, cols = 8192, 2048
+    n = rows * cols
+    for name, fmt, x_np, out_b in (
+            ("C2b_qdq_mxfp8", E.MXQ_FMT_MXFP8_ROW, W.config2_weight("random"),
+             n + n // 32 + 2 * n),
+            ("C3_qdq_nvfp4", E.MXQ_FMT_NVFP4, W.config3(), n // 2 + n // 16 + 4 * rows + 2 * n)):
+        nbytes = 2 * n + out_b
+        sets = -(-ROTATE_BYTES // nbytes)
+        x0 = dev(x_np)
+        if fmt == E.MXQ_FMT_NVFP4:
+            bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols // 2)),
+                     empty((rows, cols // 16)), empty((rows,), torch.float32),
+                     empty((rows, cols), torch.bfloat16)) for k in range(sets)]
+        else:
+            bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols)), empty((rows, cols // 32)),
+                     None, empty((rows, cols), torch.bfloat16)) for k in range(sets)]
+        launches = [(lambda b=b, fmt=fmt: E.mxq_quantize_dequant_bf16(fmt, b[0], rows, cols, b[1],
+                                                                      b[2], b[3], b[4]))
+                    for b in bufs]
+        ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_qdq_kernel"
+        k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
+                          n, sets, [kern])
+        res[k] = v
+        del bufs, launches, x0
+        torch.cuda.empty_cache()
+    return res
+
+
+def qdq_timings(torch, E, W, dev, empty):
+    legs = []
+    build_qdq(torch, E, W, legs, dev, empty)
+    res = {}
+    for l, cfg in zip(legs, ("C5_qdq_mxfp8", "C5_qdq_nvfp4")):
+        ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+        res[k] = v
+    del legs
+    torch.cuda.empty_cache()
+    res.update(qdq_small_timings(torch, E, W, dev, empty))
     return res
 
 
@@ -461,8 +543,9 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--groups", default="act,wgt,tok,exp,grp",
                     help="comma list of leg groups to run (for profiling single kernels); "
-                         "'dsp' adds the fused-dispatch legs, which replace the grouped legs' "
-                         "separate gather and are therefore not part of the default step")
+                         "'dsp' adds the fused-dispatch legs and 'qdq' the one-pass quantize + "
+                         "dequant legs; each replaces legs of the default step (the separate "
+                         "gather; quantize followed by dequant), so neither is part of it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also time a plain elementwise copy of this many MiB (int32 bitwise "
                          "not, reads and writes each byte once), reported apart from the step, "

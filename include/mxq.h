@@ -183,6 +183,30 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
                         int64_t rows, int64_t cols, uint16_t *out, void *stream);
 
 /*
+ * Quantize and dequantize in one pass: the rowwise MXFP8 or per-token NVFP4
+ * quantization of x together with its BF16 dequantization, written from
+ * registers, so the dequantized-backward mode (backward GEMMs consume BF16
+ * dequantizations of the exact forward operands: the dequantized-backward
+ * paragraph) needs no second pass over the codes.  Byte-identical to the
+ * quantize call followed by mxq_dequantize_bf16 on its outputs.
+ *
+ *   fmt == MXQ_FMT_MXFP8_ROW: codes [rows][cols] (16-byte aligned), scales
+ *          [rows][cols/32] as mxq_mxfp8_quantize_rowcol's rowwise copy;
+ *          token_scales must be NULL; cols % 32 == 0, cols <= 2^26.
+ *   fmt == MXQ_FMT_NVFP4: codes [rows][cols/2] (16-byte aligned), scales
+ *          [rows][cols/16], token_scales [rows] as
+ *          mxq_nvfp4_quantize_per_token; cols % 16 == 0, rows < 2^31.
+ *   out  [rows][cols] BF16, 16-byte aligned, required.
+ *   codes and scales must be both NULL or both non-NULL (NULL: not stored,
+ *   only the dequantized copy is written); NVFP4 token_scales may be NULL
+ *   (not stored).  A mismatched pair, or token_scales with MXFP8, gives
+ *   MXQ_ERR_OFFSETS.
+ */
+int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t cols,
+                              uint8_t *codes, uint8_t *scales, float *token_scales,
+                              uint16_t *out, void *stream);
+
+/*
  * Outputs of the grouped call.  MXFP8 uses the first five fields, NVFP4 the
  * last three; the others are ignored.
  *   row_codes, row_scales  as mxq_mxfp8_quantize_rowcol over all total_rows.

@@ -12,4 +12,4 @@ from ._binding import (  # noqa: F401
     MXQError, lib, mxq_dequantize_bf16, mxq_grouped_out, mxq_grouped_quantize,
     mxq_grouped_quantize_dispatch,
     mxq_mxfp8_quantize_rowcol, mxq_nvfp4_quantize_gateup_pair, mxq_nvfp4_quantize_per_token,
-    mxq_status_string, mxq_version)
+    mxq_quantize_dequant_bf16, mxq_status_string, mxq_version)

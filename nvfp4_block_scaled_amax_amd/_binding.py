@@ -38,6 +38,7 @@ EXPORTS = (
     "mxq_nvfp4_quantize_per_token",
     "mxq_nvfp4_quantize_gateup_pair",
     "mxq_dequantize_bf16",
+    "mxq_quantize_dequant_bf16",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
@@ -76,6 +77,7 @@ def lib():
         "mxq_nvfp4_quantize_per_token": [P, I64, I64, P, P, P, P],
         "mxq_nvfp4_quantize_gateup_pair": [P, P, I64, I64, I64, P, P, P, P, P, P],
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
+        "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
@@ -152,6 +154,12 @@ def mxq_dequantize_bf16(fmt, codes, scales, fp32_scales, rows_per_fp32_scale, ro
     _check(lib().mxq_dequantize_bf16(fmt, _ptr(codes), _ptr(scales), _ptr(fp32_scales),
                                      rows_per_fp32_scale, rows, cols, _ptr(out), _stream(stream)),
            "mxq_dequantize_bf16")
+
+
+def mxq_quantize_dequant_bf16(fmt, x, rows, cols, codes, scales, token_scales, out, stream=None):
+    _check(lib().mxq_quantize_dequant_bf16(fmt, _ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                           _ptr(token_scales), _ptr(out), _stream(stream)),
+           "mxq_quantize_dequant_bf16")
 
 
 def mxq_grouped_quantize(fmt, x, total_rows, cols, seg_offsets, n_groups, out, stream=None):

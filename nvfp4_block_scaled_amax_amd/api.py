@@ -95,6 +95,32 @@ def dequantize_bf16(fmt: int, codes, scales, fp32_scales=None, rows_per_fp32_sca
     return out
 
 
+class QuantDequant(NamedTuple):
+    codes: Optional[torch.Tensor]
+    scales: Optional[torch.Tensor]
+    fp32_scales: Optional[torch.Tensor]     # NVFP4 only
+    dequant: torch.Tensor                    # torch.bfloat16 [rows][cols]
+
+
+def quantize_dequant_bf16(fmt: int, x, keep_codes: bool = True, stream=None) -> QuantDequant:
+    """Rowwise MXFP8 (fmt MXQ_FMT_MXFP8_ROW) or per-token NVFP4 and the BF16
+    dequantization of the result, in one pass; keep_codes=False stores only
+    the dequantized copy."""
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    u8 = torch.uint8
+    codes = scales = ts = None
+    if fmt == B.MXQ_FMT_NVFP4:
+        if keep_codes:
+            codes, scales = _empty((rows, cols // 2), u8, x), _empty((rows, cols // 16), u8, x)
+            ts = _empty((rows,), torch.float32, x)
+    elif keep_codes:
+        codes, scales = _empty((rows, cols), u8, x), _empty((rows, cols // 32), u8, x)
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+    B.mxq_quantize_dequant_bf16(fmt, x, rows, cols, codes, scales, ts, out, stream)
+    return QuantDequant(codes, scales, ts, out)
+
+
 class GroupedMXFP8(NamedTuple):
     row_codes: torch.Tensor
     row_scales: torch.Tensor

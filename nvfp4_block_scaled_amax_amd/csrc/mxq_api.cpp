@@ -243,6 +243,56 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
                                               (hipStream_t)stream));
 }
 
+int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t cols,
+                              uint8_t *codes, uint8_t *scales, float *token_scales,
+                              uint16_t *out, void *stream)
+{
+    if (fmt != MXQ_FMT_MXFP8_ROW && fmt != MXQ_FMT_NVFP4)
+        return MXQ_ERR_ARG;
+    if (!x || !out)
+        return MXQ_ERR_NULL;
+    if ((codes == nullptr) != (scales == nullptr) ||
+        (fmt == MXQ_FMT_MXFP8_ROW && token_scales != nullptr))
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols))
+        return MXQ_ERR_SIZE;
+    const int64_t n = rows * cols;
+    Buf b[5];
+    int k = 0;
+    b[k++] = {x, 2 * n, 16, false};
+    b[k++] = {out, 2 * n, 16, true};
+    if (fmt == MXQ_FMT_NVFP4) {
+        if (rows > MAX_GRID_ROWS)
+            return MXQ_ERR_SIZE;
+        if (cols % 16 != 0)
+            return MXQ_ERR_SHAPE;
+        if (codes) {
+            b[k++] = {codes, n / 2, 16, true};
+            b[k++] = {scales, n / 16, 1, true};
+        }
+        if (token_scales)
+            b[k++] = {token_scales, 4 * rows, 4, true};
+        const int st = check_bufs(b, k);
+        if (st != MXQ_OK)
+            return st;
+        return launched(mxq::launch_nvfp4_qdq(x, rows, cols, codes, scales, token_scales, out,
+                                              (hipStream_t)stream));
+    }
+    if (cols > MAX_MXFP8_COLS)
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0)
+        return MXQ_ERR_SHAPE;
+    if (codes) {
+        b[k++] = {codes, n, 16, true};
+        b[k++] = {scales, n / 32, 1, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_row_qdq(x, rows, cols, codes, scales, out,
+                                              (hipStream_t)stream));
+}
+
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t cols,
                          const int64_t *seg_offsets, int64_t n_groups, const mxq_grouped_out *out,
                          void *stream)

@@ -12,25 +12,11 @@
 // streaming stores turn into extra HBM write traffic.  Grid-stride over
 // wave steps.
 //
-// MXFP8.  dec(c) 2^e has at most 4 significant bits, so it is a BF16 value
-// unless it lies below the BF16 normal range or overflows.  One
-// v_cvt_scalef32_pk_bf16_fp8 per element pair computes it (the E8M0 byte sits
-// in the exponent field of the scale operand); measured exact for every code
-// and every scale byte, BF16 subnormals included, except that it returns Inf
-// instead of saturating, which only happens for scale bytes >= 247 -- those
-// units take an exact path.  Rowwise: one scale per unit (index f / 32).
-// Columnwise: one scale per element, so each pair is converted twice and the
+// The arithmetic (exact conversion instructions, and the exact fallbacks)
+// is in mxq_dequant.h.  MXFP8 rowwise: one scale per unit (index f / 32);
+// columnwise: one scale per element, so each pair is converted twice and the
 // halves merged.
-//
-// NVFP4.  dec(c) dec(b) is exact (at most 6 bits) and p = fp32(dec(c) dec(b) s)
-// is its one f32 rounding.  The f32 -> BF16 conversion (nearest-even) is the
-// second; the two can differ from one rounding of the exact product only when
-// p lands exactly on a BF16 midpoint without being exact.  Within a block,
-// dec(c) dec(b) s = 2^j d s or 2^j 3 d s, so p is 2^j fp32(d s) or
-// 2^j fp32(3 d s): checking those two products once per block settles every
-// element.  Blocks where that check fires, whose values could overflow BF16,
-// or whose FP32 scale is below 2^-100 take an exact binary64 path.
-#include "mxq_device.h"
+#include "mxq_dequant.h"
 #include "mxq_launch.h"
 
 namespace mxq {
@@ -41,83 +27,8 @@ constexpr int WAVES_PER_WG = 4;
 // 2048 grouped shape.
 constexpr int MXFP8_OVERSUBSCRIBE = 0;
 constexpr int NVFP4_OVERSUBSCRIBE = 16;
-constexpr float NV_FAST_MIN_S = 0x1p-100f;
-constexpr float BF16_MAX = 0x1.FEp127f;
-
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-
-// f32 -> BF16 bits, nearest-even, saturating (for finite inputs, or Inf from
-// an f32 overflow).
-__device__ __forceinline__ uint32_t bf16_rne_sat(uint32_t u)
-{
-    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return ((r & 0x7F80u) == 0x7F80u) ? ((r & 0x8000u) | 0x7F7Fu) : r;
-}
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
-
-// Exact BF16 of dec(c) * 2^(b - 127): the product is exact in f32 (possibly
-// subnormal, at least 2^-136) or overflows to Inf, which saturates.
-__device__ __forceinline__ uint32_t mx_deq1_exact(uint32_t c, uint32_t b)
-{
-    const float y = ldexpf(e4m3_value(c), (int)b - 127);
-    return bf16_rne_sat(f2u(y));
-}
-
-// Two codes (bytes of the low or high half of `w`) under one scale byte.
-template <bool HI>
-__device__ __forceinline__ uint32_t mx_pair(uint32_t w, uint32_t scale_bits)
-{
-    const bf16x2v_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, u2f(scale_bits), HI);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// 1 iff some byte of w is >= 247.
-__device__ __forceinline__ uint32_t any_byte_ge247(uint32_t w)
-{
-    return (((w & 0x7F7F7F7Fu) + 0x09090909u) & w & 0x80808080u) != 0u;
-}
-
 constexpr int64_t WAVE_SPAN = 1024;     // elements per wavefront step
 constexpr int64_t HALF_SPAN = 512;
-
-// Eight BF16 (16 bytes) of one MXFP8 chunk: codes cw (8 bytes), scales sw
-// (one byte per element for the columnwise layout, else the chunk's one
-// scale byte in every byte).
-template <bool COL>
-__device__ __forceinline__ u32x4_t mx_chunk(uint2 cq, uint2 sq)
-{
-    const uint32_t cw[2] = {cq.x, cq.y}, sw[2] = {sq.x, sq.y};
-    u32x4_t o;
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const uint32_t c = cw[j], s = sw[j];
-        if constexpr (!COL) {
-            o[2 * j] = mx_pair<false>(c, (s & 0xFFu) << 23);
-            o[2 * j + 1] = mx_pair<true>(c, (s & 0xFFu) << 23);
-        } else {
-            // Each conversion applies one scale to both codes of a pair:
-            // convert under each element's scale and keep its half.
-            const uint32_t lo_a = mx_pair<false>(c, (s & 0xFFu) << 23);
-            const uint32_t lo_b = mx_pair<false>(c, ((s >> 8) & 0xFFu) << 23);
-            const uint32_t hi_a = mx_pair<true>(c, ((s >> 16) & 0xFFu) << 23);
-            const uint32_t hi_b = mx_pair<true>(c, (s >> 24) << 23);
-            o[2 * j] = __builtin_amdgcn_perm(lo_b, lo_a, 0x07060100u);
-            o[2 * j + 1] = __builtin_amdgcn_perm(hi_b, hi_a, 0x07060100u);
-        }
-    }
-    if (any_byte_ge247(sw[0]) | any_byte_ge247(sw[1])) {
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const uint32_t c = cw[j], s = sw[j];
-            o[2 * j] = pack2(mx_deq1_exact(c & 0xFF, s & 0xFF),
-                             mx_deq1_exact((c >> 8) & 0xFF, (s >> 8) & 0xFF));
-            o[2 * j + 1] = pack2(mx_deq1_exact((c >> 16) & 0xFF, (s >> 16) & 0xFF),
-                                 mx_deq1_exact(c >> 24, s >> 24));
-        }
-    }
-    return o;
-}
 
 // COL == false: scales[row][cols/32]; COL == true: scales[row/32][cols].
 // n = rows * cols elements; per_row16 divides by cols / 16.
@@ -158,61 +69,6 @@ __global__ void __launch_bounds__(256) dequant_mxfp8_kernel(const uint8_t *__res
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + f[h]));
         }
     }
-}
-
-// BF16 of the exact product y (binary64, exact), nearest-even, saturating.
-__device__ __forceinline__ uint32_t bf16_from_f64(double y)
-{
-    const uint32_t sign = signbit(y) ? 0x8000u : 0u;
-    const double a = fabs(y);
-    if (a >= (double)BF16_MAX)
-        return sign | 0x7F7Fu;
-    if (a == 0.0)
-        return sign;
-    int e = 0;
-    (void)frexp(a, &e);
-    int E = e - 1;
-    if (E < -126)
-        E = -126;
-    const double n = rint(ldexp(a, 7 - E));        // exact scaling, nearest-even
-    const float r = (float)ldexp(n, E - 7);         // a BF16 value: exact in f32
-    return sign | (f2u(r) >> 16);
-}
-
-// 1 iff fp32(a * s) is a BF16 midpoint that is not the exact product.
-__device__ __forceinline__ bool bf16_tie_hazard(float a, float s)
-{
-    const float p = a * s;
-    return (f2u(p) & 0xFFFFu) == 0x8000u && __builtin_fmaf(a, s, -p) != 0.0f;
-}
-
-// Exact BF16 pair for one code byte (two E2M1 codes) under (d, s).
-__device__ __attribute__((noinline)) uint32_t nv_pair_exact(uint32_t byte, float d, float s)
-{
-    const float2_t v = e2m1_values(byte);
-    return pack2(bf16_from_f64((double)v[0] * (double)d * (double)s),
-                 bf16_from_f64((double)v[1] * (double)d * (double)s));
-}
-
-// Eight BF16 (16 bytes) of one NVFP4 chunk: 8 codes (4 bytes) of a block
-// with decoded block scale d under FP32 scale s.
-__device__ __forceinline__ u32x4_t nv_chunk(uint32_t cw, float d, float s)
-{
-    u32x4_t o;
-    const bool fast = s >= NV_FAST_MIN_S && fabsf((6.0f * d) * s) <= BF16_MAX &&
-                      !bf16_tie_hazard(d, s) && !bf16_tie_hazard(3.0f * d, s);
-    if (fast) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float2_t v = e2m1_values((cw >> (8 * j)) & 0xFFu);
-            const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
-            o[j] = __builtin_bit_cast(uint32_t, r);
-        }
-    } else {
-        for (int j = 0; j < 4; j++)
-            o[j] = nv_pair_exact((cw >> (8 * j)) & 0xFFu, d, s);
-    }
-    return o;
 }
 
 // n = rows * cols elements; per_scale divides a block index by the blocks

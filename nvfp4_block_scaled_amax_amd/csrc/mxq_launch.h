@@ -29,6 +29,17 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
                                 int64_t *col_scale_offsets, const int64_t *row_tokens,
                                 int64_t n_tokens, hipStream_t stream);
 
+// Rowwise MXFP8 and its BF16 dequantization in one pass; rc/rs may be null
+// (only the dequantized copy is stored).
+hipError_t launch_mxfp8_row_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,
+                                uint8_t *row_scales, uint16_t *dq, hipStream_t stream);
+
+// Per-token NVFP4 and its BF16 dequantization in one pass; codes/block_scales
+// and token_scales may be null (not stored).
+hipError_t launch_nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                            uint8_t *block_scales, float *token_scales, uint16_t *dq,
+                            hipStream_t stream);
+
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *block_scales, float *token_scales, hipStream_t stream);
 

@@ -30,7 +30,7 @@
 // tile's base addresses are wave-uniform (scalar registers) and lanes add
 // 32-bit offsets (cols < 2^27).  For ragged segments (grouped call) tile T
 // lies in the segment e with P[e] <= T < P[e+1] (binary search).
-#include "mxq_device.h"
+#include "mxq_dequant.h"
 #include "mxq_launch.h"
 
 namespace mxq {
@@ -144,9 +144,32 @@ __device__ __forceinline__ void load_tile_gather(uint32_t (&v)[8][4],
 // Tile outputs: wave-uniform bases at (row0, strip column 0).
 struct TileOut {
     uint8_t *rc, *rs, *cc, *cs;     // row codes, row scales, col codes, col scales
+    uint16_t *dq;                   // dequantized rowwise copy (BF16), DQ kernels
 };
 
-template <bool ROW, bool COL, bool FULL>
+// Eight BF16 of one row's 8 rowwise codes (w0: columns 0..3, w1: 4..7) under
+// the block's scale (byte << 23), exact (mxq_dequant.h).
+__device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t scale)
+{
+    u32x4_t o;
+    const uint32_t byte = scale >> 23;
+    if (byte < 247) {
+        o[0] = mx_pair<false>(w0, scale);
+        o[1] = mx_pair<true>(w0, scale);
+        o[2] = mx_pair<false>(w1, scale);
+        o[3] = mx_pair<true>(w1, scale);
+    } else {
+        o[0] = pack2(mx_deq1_exact(w0 & 0xFF, byte), mx_deq1_exact((w0 >> 8) & 0xFF, byte));
+        o[1] = pack2(mx_deq1_exact((w0 >> 16) & 0xFF, byte), mx_deq1_exact(w0 >> 24, byte));
+        o[2] = pack2(mx_deq1_exact(w1 & 0xFF, byte), mx_deq1_exact((w1 >> 8) & 0xFF, byte));
+        o[3] = pack2(mx_deq1_exact((w1 >> 16) & 0xFF, byte), mx_deq1_exact(w1 >> 24, byte));
+    }
+    return o;
+}
+
+// DQ: also write the BF16 dequantization of the rowwise codes (o.dq); ROW
+// may then be false (codes and scales computed but not stored).
+template <bool ROW, bool COL, bool FULL, bool DQ = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -159,7 +182,7 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
         for (int j = 0; j < 4; j++)
             a[i][j] = v[i][j] & 0x7FFF7FFFu;
 
-    if constexpr (ROW) {
+    if constexpr (ROW || DQ) {
         const uint32_t nb = cols >> 5;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -173,9 +196,14 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
             const uint32_t w1 = cvt2<true>(cvt2<false>(0u, v[i][2], scale), v[i][3], scale);
             if (FULL || (col_ok && i < nr)) {
                 const uint32_t r = (uint32_t)(8 * rg + i);
-                st_nt8(o.rc + (r * cols + c8), w0, w1);
-                if ((g & 3) == 0)
-                    o.rs[r * nb + (c8 >> 5)] = (uint8_t)(sc >> 7);
+                if constexpr (ROW) {
+                    st_nt8(o.rc + (r * cols + c8), w0, w1);
+                    if ((g & 3) == 0)
+                        o.rs[r * nb + (c8 >> 5)] = (uint8_t)(sc >> 7);
+                }
+                if constexpr (DQ)
+                    __builtin_nontemporal_store(row_dq(w0, w1, scale),
+                                                reinterpret_cast<u32x4_t *>(o.dq + (r * cols + c8)));
             }
         }
     }
@@ -265,11 +293,10 @@ __device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, i
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
-__global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_t *__restrict__ rc,
-                                                         uint8_t *__restrict__ rs,
-                                                         uint8_t *__restrict__ cc,
-                                                         uint8_t *__restrict__ cs)
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ>
+__device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict__ rc,
+                                          uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
+                                          uint8_t *__restrict__ cs, uint16_t *__restrict__ dq)
 {
     const int lane = (int)lane_id();
     const int g = lane & 15, rg = lane >> 4;
@@ -302,7 +329,8 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_
     const bool full = tcol + TILE_COLS <= G.cols && t.nrows == TILE_ROWS;
     const int64_t base = t.row0 * G.cols + tcol;
     const uint16_t *xt = G.x + base;
-    const TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol};
+    const TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol,
+                    DQ ? dq + base : nullptr};
     uint32_t v[8][4];
     if (full) {
         if constexpr (GATHER)
@@ -310,15 +338,35 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_
                                    t.nrows, rg, col_ok);
         else
             load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, true>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, true, DQ>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
         if constexpr (GATHER)
             load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
                                     t.nrows, rg, col_ok);
         else
             load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, false>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, false, DQ>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
+}
+
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_t *__restrict__ rc,
+                                                         uint8_t *__restrict__ rs,
+                                                         uint8_t *__restrict__ cc,
+                                                         uint8_t *__restrict__ cs)
+{
+    tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr);
+}
+
+// Rowwise quantize + BF16 dequant of the rowwise copy in one pass; ROW =
+// false stores only the dequantized copy.
+template <bool ROW, int WPW>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_row_qdq_kernel(Geometry G,
+                                                            uint8_t *__restrict__ rc,
+                                                            uint8_t *__restrict__ rs,
+                                                            uint16_t *__restrict__ dq)
+{
+    tile_body<ROW, false, false, WPW, false, true>(G, rc, rs, nullptr, nullptr, dq);
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
@@ -407,6 +455,34 @@ hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uin
     if (row_tokens)
         return launch<false, true>(G, tiles, rc, rs, cc, cs, stream);
     return launch<false, false>(G, tiles, rc, rs, cc, cs, stream);
+}
+
+template <bool ROW, int WPW>
+static hipError_t launch_qdq_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
+                                 uint16_t *dq, hipStream_t stream)
+{
+    const int64_t wgs = (waves + WPW - 1) / WPW;
+    if (wgs > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mxfp8_row_qdq_kernel<ROW, WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
+                       stream, G, rc, rs, dq);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_row_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
+                                uint8_t *rs, uint16_t *dq, hipStream_t stream)
+{
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0,
+               nullptr, 0};
+    const int64_t waves = (rows + TILE_ROWS - 1) / TILE_ROWS * G.nct;
+    if (rc) {
+        if (waves >= LARGE_LAUNCH_WAVES)
+            return launch_qdq_wpw<true, 8>(G, waves, rc, rs, dq, stream);
+        return launch_qdq_wpw<true, 4>(G, waves, rc, rs, dq, stream);
+    }
+    if (waves >= LARGE_LAUNCH_WAVES)
+        return launch_qdq_wpw<false, 8>(G, waves, rc, rs, dq, stream);
+    return launch_qdq_wpw<false, 4>(G, waves, rc, rs, dq, stream);
 }
 
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,

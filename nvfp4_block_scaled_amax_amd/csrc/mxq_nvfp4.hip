@@ -34,7 +34,7 @@
 // against midpoint * D, a product of at most 31 significant bits, hence exact.
 // Scales below 2^-101 would take the reciprocals out of the normal range; such
 // scopes use a binary64 path that divides once per element.
-#include "mxq_device.h"
+#include "mxq_dequant.h"
 #include "mxq_launch.h"
 
 namespace mxq {
@@ -266,7 +266,22 @@ struct Dest {
     const int64_t *dest;    // nullptr: identity
     int64_t copies;
     int64_t out_rows;
+    uint16_t *dq;           // quantize-dequant kernels: BF16 [rows][cols]
 };
+
+// Block j's 16 dequantized BF16 values (32 bytes at out + 16 j): the exact
+// product of the codes, the block scale and s, rounded once (mxq_dequant.h).
+// Default-policy stores: each store instruction covers half of the lines it
+// touches, and the other half follows at once from the same wavefront.
+__device__ __forceinline__ void emit_dq(const BlkOut &o, int64_t j, float s,
+                                        uint16_t *__restrict__ out)
+{
+    const float d = e4m3_value(o.b);
+    u32x4_t lo, hi;
+    nv_block16(o.c0, o.c1, d, s, lo, hi);
+    *reinterpret_cast<u32x4_t *>(out + 16 * j) = lo;
+    *reinterpret_cast<u32x4_t *>(out + 16 * j + 8) = hi;
+}
 
 // Destination rows c0 .. c0+63 of dispatched row `row`, one per lane (-1 past
 // the last copy): one vector load, issued before the quantize so that its
@@ -291,14 +306,16 @@ __device__ __forceinline__ int64_t lane_i64(int64_t v, int c)
 // Rows of up to 64 NB blocks (1024 NB elements), held in registers.  FULL:
 // exactly 64 NB blocks (no lane idle); otherwise missing blocks load a valid
 // address and are zeroed (no divergent loads) and are not stored.
-// Rows of up to 2048 elements fit 64 VGPRs (8 wavefronts per SIMD) without
-// spilling; longer ones are left to the compiler's occupancy choice.
-template <int NB, bool FULL, bool SCATTER>
-__global__ void __launch_bounds__(WG_THREADS)
-__attribute__((amdgpu_waves_per_eu(NB <= 2 ? 8 : 1, 8)))
-nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
-                   uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
-                   float *__restrict__ ts, Dest dst)
+// Full rows of up to 2048 elements fit 64 VGPRs (8 wavefronts per SIMD)
+// without spilling; partial or longer rows are left to the compiler's
+// occupancy choice (a partial row of 65..127 blocks spilled at 64).
+// DQ: also the dequantized row (dst.dq); codes/bs and ts may then be null
+// (not stored).
+template <int NB, bool FULL, bool SCATTER, bool DQ>
+__device__ __forceinline__ void token_body(const uint16_t *__restrict__ x, int64_t rows,
+                                           int64_t cols, uint8_t *__restrict__ codes,
+                                           uint8_t *__restrict__ bs, float *__restrict__ ts,
+                                           const Dest &dst)
 {
     const int64_t row = (int64_t)wg_id() * ROWS_PER_WG + wave_in_group();
     if (row >= rows)
@@ -331,15 +348,37 @@ nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
     const float s = div2688(u2f(__builtin_amdgcn_readfirstlane(wave_max_u32(A))));
     const ScaleK sk = scale_k(s);
     if constexpr (!SCATTER) {
-        if (lane == 0)
+        if (lane == 0 && (!DQ || ts))
             ts[row] = s;
         uint8_t *crow = codes + row * (cols >> 1);
         uint8_t *brow = bs + row * (cols >> 4);
+        // DQ: the row's BF16 goes through LDS (32 bytes per block at block
+        // j), so that every global store instruction writes 1 KiB of whole
+        // lines; lane-owned 32-byte pieces would leave each instruction
+        // writing half lines.  One wavefront per workgroup, so the buffer is
+        // the wavefront's own.
+        static_assert(ROWS_PER_WG == 1, "LDS staging assumes one row per workgroup");
+        __shared__ u32x4_t stage[DQ ? 128 * NB : 1];
 #pragma unroll
         for (int k = 0; k < NB; k++) {
             const int j = lane + 64 * k;
-            if (FULL || j < nblk)
-                emit_blk(quant_blk(r[k], f[k], sk), j, crow, brow);
+            if (FULL || j < nblk) {
+                const BlkOut o = quant_blk(r[k], f[k], sk);
+                if (!DQ || codes)
+                    emit_blk(o, j, crow, brow);
+                if constexpr (DQ)
+                    nv_block16(o.c0, o.c1, e4m3_value(o.b), s, stage[2 * j], stage[2 * j + 1]);
+            }
+        }
+        if constexpr (DQ) {
+            __syncthreads();
+            uint16_t *out = dst.dq + row * cols;
+#pragma unroll
+            for (int q = 0; q < 2 * NB; q++) {
+                const int u = 64 * q + lane;            // 16-byte unit of the row
+                if (FULL || u < 2 * nblk)
+                    __builtin_nontemporal_store(stage[u], reinterpret_cast<u32x4_t *>(out + 8 * u));
+            }
         }
     } else {
         BlkOut o[NB];
@@ -368,9 +407,29 @@ nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
     }
 }
 
+template <int NB, bool FULL, bool SCATTER>
+__global__ void __launch_bounds__(WG_THREADS)
+__attribute__((amdgpu_waves_per_eu(NB == 1 || (NB == 2 && FULL) ? 8 : 1, 8)))
+nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                   uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
+                   float *__restrict__ ts, Dest dst)
+{
+    token_body<NB, FULL, SCATTER, false>(x, rows, cols, codes, bs, ts, dst);
+}
+
+template <int NB, bool FULL>
+__global__ void __launch_bounds__(WG_THREADS)
+__attribute__((amdgpu_waves_per_eu(NB == 1 || (NB == 2 && FULL) ? 8 : 1, 8)))
+nvfp4_token_qdq_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                       uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
+                       float *__restrict__ ts, Dest dst)
+{
+    token_body<NB, FULL, false, true>(x, rows, cols, codes, bs, ts, dst);
+}
+
 // Longer rows: read twice (amax, then codes).  Dispatch: each block is
 // written to every destination row as it is produced.
-template <bool SCATTER>
+template <bool SCATTER, bool DQ>
 __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ bs, float *__restrict__ ts, Dest dst)
@@ -390,13 +449,16 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
     const float s = div2688(u2f(__builtin_amdgcn_readfirstlane(wave_max_u32(A))));
     const ScaleK sk = scale_k(s);
     if constexpr (!SCATTER) {
-        if (lane == 0)
+        if (lane == 0 && (!DQ || ts))
             ts[row] = s;
         for (int64_t j = lane; j < nblk; j += 64) {
             Blk b;
             load_blk(b, xr + 16 * j);
-            emit_blk(quant_blk(b, unpack_blk(b), sk), j, codes + row * (cols >> 1),
-                     bs + row * (cols >> 4));
+            const BlkOut o = quant_blk(b, unpack_blk(b), sk);
+            if (!DQ || codes)
+                emit_blk(o, j, codes + row * (cols >> 1), bs + row * (cols >> 4));
+            if constexpr (DQ)
+                emit_dq(o, j, s, dst.dq + row * cols);
         }
     } else {
         // Copies in chunks of 64 (the row is re-read per chunk; top-k is
@@ -523,16 +585,20 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_scoped_kernel(const uint16_t
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <int NB, bool FULL, bool SCATTER>
+template <int NB, bool FULL, bool SCATTER, bool DQ>
 static void launch_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                          uint8_t *bs, float *ts, Dest dst, hipStream_t stream)
 {
     const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(WG_THREADS);
-    hipLaunchKernelGGL((nvfp4_token_kernel<NB, FULL, SCATTER>), grid, block, 0, stream, x, rows,
-                       cols, codes, bs, ts, dst);
+    if constexpr (DQ)
+        hipLaunchKernelGGL((nvfp4_token_qdq_kernel<NB, FULL>), grid, block, 0, stream, x, rows,
+                           cols, codes, bs, ts, dst);
+    else
+        hipLaunchKernelGGL((nvfp4_token_kernel<NB, FULL, SCATTER>), grid, block, 0, stream, x,
+                           rows, cols, codes, bs, ts, dst);
 }
 
-template <bool SCATTER>
+template <bool SCATTER, bool DQ = false>
 static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                               uint8_t *bs, float *ts, Dest dst, hipStream_t stream)
 {
@@ -541,18 +607,18 @@ static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uin
     const int64_t nb = (nblk + 63) / 64;
     const bool full = nblk == 64 * nb;
     switch (nb) {
-    case 1: full ? launch_token<1, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
-                 : launch_token<1, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
-    case 2: full ? launch_token<2, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
-                 : launch_token<2, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
-    case 3: full ? launch_token<3, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
-                 : launch_token<3, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
-    case 4: full ? launch_token<4, true, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream)
-                 : launch_token<4, false, SCATTER>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 1: full ? launch_token<1, true, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<1, false, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 2: full ? launch_token<2, true, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<2, false, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 3: full ? launch_token<3, true, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<3, false, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream); break;
+    case 4: full ? launch_token<4, true, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream)
+                 : launch_token<4, false, SCATTER, DQ>(x, rows, cols, codes, bs, ts, dst, stream); break;
     default: {
         const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(WG_THREADS);
-        hipLaunchKernelGGL((nvfp4_token_long_kernel<SCATTER>), grid, block, 0, stream, x, rows,
-                           cols, codes, bs, ts, dst);
+        hipLaunchKernelGGL((nvfp4_token_long_kernel<SCATTER, DQ>), grid, block, 0, stream, x,
+                           rows, cols, codes, bs, ts, dst);
     }
     }
     return hipGetLastError();
@@ -561,7 +627,15 @@ static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uin
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *bs, float *ts, hipStream_t stream)
 {
-    return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows}, stream);
+    return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, nullptr},
+                              stream);
+}
+
+hipError_t launch_nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                            uint8_t *bs, float *ts, uint16_t *dq, hipStream_t stream)
+{
+    return launch_rows<false, true>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, dq},
+                                    stream);
 }
 
 hipError_t launch_nvfp4_dispatch(const uint16_t *x, int64_t n_tokens, int64_t cols,
@@ -569,7 +643,7 @@ hipError_t launch_nvfp4_dispatch(const uint16_t *x, int64_t n_tokens, int64_t co
                                  uint8_t *codes, uint8_t *bs, float *ts, hipStream_t stream)
 {
     return launch_rows<true>(x, n_tokens, cols, codes, bs, ts,
-                             Dest{token_rows, top_k, out_rows}, stream);
+                             Dest{token_rows, top_k, out_rows, nullptr}, stream);
 }
 
 hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,

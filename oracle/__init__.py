@@ -295,3 +295,20 @@ def dequant_nvfp4(codes, block_scales, fp32_scales, rows_per_scale: int) -> np.n
     lib().oracle_dequant_nvfp4(_p(codes), _p(bs), _p(fs), int(rows_per_scale), rows,
                                cols, _p(out))
     return out
+
+
+def quantize_dequant_mxfp8_rowwise(x):
+    """Rowwise MXFP8 of x and the BF16 dequantization of those codes: the
+    forward operand and the BF16 copy that a dequantized backward consumes
+    (page "Miles: end-to-end MXFP8 and per-token NVFP4 RL on Blackwell",
+    dequantized-backward paragraph).  By definition the composition of the
+    two steps; returns (codes, scales, bf16 bits)."""
+    codes, scales = mxfp8_rowwise(x)
+    return codes, scales, dequant_mxfp8_rowwise(codes, scales)
+
+
+def quantize_dequant_nvfp4(x):
+    """Per-token NVFP4 of x and its BF16 dequantization (same paragraph);
+    returns (codes, block_scales, token_scales, bf16 bits)."""
+    codes, bs, ts = nvfp4_per_token(x)
+    return codes, bs, ts, dequant_nvfp4(codes, bs, ts, 1)

@@ -91,6 +91,19 @@ def test_validation_before_any_device_call():
     assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 64, 32, A, 2, bad, 0) == mxq.MXQ_ERR_OFFSETS
     assert status_of(g, mxq.MXQ_FMT_NVFP4, A, 64, 32, A, 2, {"codes": A}, 0) == mxq.MXQ_ERR_NULL
 
+    qd = mxq.mxq_quantize_dequant_bf16
+    R = mxq.MXQ_FMT_MXFP8_ROW
+    assert status_of(qd, mxq.MXQ_FMT_MXFP8_COL, A, 32, 32, A, A, None, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(qd, R, A, 32, 32, A, A, None, None, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(qd, R, A, 32, 32, A, None, None, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(qd, R, A, 32, 32, A, A, A, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(qd, R, A, 32, 48, A, A, None, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(qd, R, A, 0, 32, A, A, None, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(qd, R, A, 32, 32, A, A, None, A + 8, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(qd, F4 := mxq.MXQ_FMT_NVFP4, A, 4, 24, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(qd, F4, A, 1 << 31, 16, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(qd, F4, A, 4, 16, A + 4, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+
     gd = mxq.mxq_grouped_quantize_dispatch
     nv = {"codes": A, "block_scales": A, "token_scales": A}
     F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL

@@ -447,6 +447,85 @@ def test_grouped_config5_full(orc):
 
 
 # ---------------------------------------------------------------------------
+# Quantize + dequant in one pass
+# ---------------------------------------------------------------------------
+
+def check_qdq(orc, x: np.ndarray, fmt: int, name: str, codes_only_check=True):
+    """Codes, scales and the BF16 dequant of the one-pass call against the
+    oracle's quantize followed by its dequant; then the dequant-only call
+    (no codes stored) must give the same BF16."""
+    tag = "mxfp8" if fmt == mxq.MXQ_FMT_MXFP8_ROW else "nvfp4"
+    announce(f"quantize-dequant {tag} {name} shape={x.shape}")
+    xd = dev(x)
+    r = api.quantize_dequant_bf16(fmt, xd)
+    torch.cuda.synchronize()
+    if fmt == mxq.MXQ_FMT_MXFP8_ROW:
+        c, s_, y = orc.quantize_dequant_mxfp8_rowwise(x)
+    else:
+        c, s_, t, y = orc.quantize_dequant_nvfp4(x)
+        assert_same(host(r.fp32_scales).view(np.uint32), t.view(np.uint32), f"{name} ts")
+    assert_same(host(r.codes), c, f"{name} codes")
+    assert_same(host(r.scales), s_, f"{name} scales")
+    assert_same(host(r.dequant), y, f"{name} dequant")
+    if codes_only_check:
+        announce(f"quantize-dequant {tag} {name} dequant only")
+        r2 = api.quantize_dequant_bf16(fmt, xd, keep_codes=False)
+        torch.cuda.synchronize()
+        assert r2.codes is None
+        assert_same(host(r2.dequant), y, f"{name} dequant only")
+
+
+@pytest.mark.parametrize("mode", W.MXFP8_MODES)
+def test_qdq_mxfp8_config2_weight(orc, mode):
+    """8192 x 2048 in every data mode (maxes: scale byte 247, the exact
+    saturating path)."""
+    check_qdq(orc, W.config2_weight(mode), mxq.MXQ_FMT_MXFP8_ROW, f"C2b {mode}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (77, 96), (33, 2080), (160, 544), (5, 4128)])
+def test_qdq_mxfp8_shapes(orc, rows, cols):
+    """Ragged row counts and partial column strips."""
+    check_qdq(orc, W.mode_boundary(-(-rows // 32) * 32, cols, rows)[:rows], mxq.MXQ_FMT_MXFP8_ROW,
+              f"boundary {rows}x{cols}")
+
+
+def test_qdq_mxfp8_exhaustive(orc):
+    """Every finite BF16 value under every scale its block can have: every
+    (code, scale) pair the dequant can meet in a rowwise copy."""
+    check_qdq(orc, _mxfp8_exhaustive_input(), mxq.MXQ_FMT_MXFP8_ROW, "exhaustive rows")
+
+
+def test_qdq_nvfp4_config3(orc):
+    check_qdq(orc, W.config3(), mxq.MXQ_FMT_NVFP4, "C3 8192x2048")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (5, 48), (7, 768), (9, 1040), (6, 2048),
+                                       (3, 2064), (4, 4096), (2, 4112)])
+def test_qdq_nvfp4_shapes(orc, rows, cols):
+    """Every register-resident chunk count, partial chunks and the re-reading
+    path above 4096, on heavy-tailed and boundary rows."""
+    check_qdq(orc, W.student_t_activations(rows, cols, rows * cols), mxq.MXQ_FMT_NVFP4,
+              f"t3 {rows}x{cols}")
+    check_qdq(orc, W.nvfp4_boundary(rows, cols, cols + 1), mxq.MXQ_FMT_NVFP4,
+              f"boundary {rows}x{cols}", codes_only_check=False)
+
+
+def test_qdq_nvfp4_ties_and_range(orc):
+    """Exact ties of both rounding steps, scales across the whole range (the
+    binary64 paths of quantize and dequant) and every token amax."""
+    check_qdq(orc, _tie_sweep(), mxq.MXQ_FMT_NVFP4, "tie sweep")
+    check_qdq(orc, _wide_range_rows(300, 256, 7), mxq.MXQ_FMT_NVFP4, "wide range")
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)
+    rng = np.random.default_rng(45)
+    frac = rng.integers(0, 0x8000, (mags.size, 32)).astype(np.uint32)
+    x = (frac * mags[:, None]) // 0x8000
+    x[:, 0] = mags
+    x |= (rng.integers(0, 2, x.shape).astype(np.uint32) << 15)
+    check_qdq(orc, x.astype(np.uint16), mxq.MXQ_FMT_NVFP4, "every token amax",
+              codes_only_check=False)
+
+
+# ---------------------------------------------------------------------------
 # Grouped quantize fused with dispatch (reads the unpermuted tokens)
 # ---------------------------------------------------------------------------
 

@@ -407,6 +407,53 @@ def test_dequant_matches_exact_spec(orc):
                 assert out[i, k] == want
 
 
+def test_quantize_dequant_matches_exact_spec(orc):
+    """The one-pass quantize + dequant composition, whole tensors, against the
+    Fraction spec: codes and scales from its quantizers, BF16 from the exact
+    product rounded once."""
+    xm = W.mode_boundary(32, 64, 9)
+    c8, s8, y8 = orc.quantize_dequant_mxfp8_rowwise(xm)
+    rc, rs = X.mxfp8_rowwise(xm.tolist())
+    assert c8.tolist() == rc and s8.tolist() == rs
+    for i in range(32):
+        for k in range(64):
+            y = X.E4M3_POS[rc[i][k] & 0x7F] * F(2) ** (rs[i][k // 32] - 127)
+            want = X.bf16_nearest_sat(-y if rc[i][k] & 0x80 else y)
+            if y == 0:
+                want = 0x8000 if rc[i][k] & 0x80 else 0
+            assert y8[i, k] == want, (i, k)
+    xn = W.nvfp4_boundary(8, 64, 5)
+    c4, b4, t4, y4 = orc.quantize_dequant_nvfp4(xn)
+    C, Bs, S = X.nvfp4_per_token(xn.tolist())
+    assert c4.tolist() == C and b4.tolist() == Bs
+    assert [F(float(v)) for v in t4] == S
+    for i in range(8):
+        for k in range(64):
+            c = (C[i][k // 2] >> (4 * (k % 2))) & 0xF
+            y = X.E2M1_POS[c & 7] * X.E4M3_POS[Bs[i][k // 16]] * S[i]
+            want = X.bf16_nearest_sat(-y if c & 8 else y)
+            if y == 0:
+                want = 0x8000 if c & 8 else 0
+            assert y4[i, k] == want, (i, k)
+
+
+def test_mxfp8_quantize_dequant_is_a_projection(orc):
+    """For values in range, dequant(quant(x)) lies on the grid it was rounded
+    to, so quantizing it again returns it unchanged (the block amax can only
+    lower the exponent, and an E4M3 value times a power of two up to 448 is
+    an E4M3 value); and it stays within half a step of x."""
+    for x in (W.config1(), W.student_t_activations(64, 256, 31)):
+        _, s, y = orc.quantize_dequant_mxfp8_rowwise(x)
+        _, s2, y2 = orc.quantize_dequant_mxfp8_rowwise(y)
+        assert np.array_equal(y2, y)
+        assert np.all(s2 <= s)
+        xv, yv = f64(x), f64(y)
+        scale = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=1)
+        # E4M3 spacing at |y| / 2^e: 2^(floor(log2) - 3), and 2^-9 below 2^-6
+        e = np.floor(np.log2(np.maximum(np.abs(yv) / scale, 2.0 ** -6))).astype(np.int64)
+        assert np.all(np.abs(xv - yv) <= np.ldexp(1.0, e - 3) * scale / 2)
+
+
 # ---------------------------------------------------------------------------
 # Invariants the contract implies
 # ---------------------------------------------------------------------------
