@@ -670,6 +670,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W, log)
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1)
+        cpu["gpu_over_cpu_single_thread"] = round(value / cpu["single_thread"]["value"], 1)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -91,6 +91,11 @@ typedef enum {
     MXQ_FMT_NVFP4 = 4          /* NVFP4 with a per-token FP32 scale          */
 } mxq_format;
 
+typedef enum {
+    MXQ_OUT_F32 = 0,           /* GEMM result as fp32                        */
+    MXQ_OUT_BF16 = 1           /* GEMM result rounded to BF16, nearest-even  */
+} mxq_out_dtype;
+
 /*
  * MXFP8 quantize, rowwise and columnwise copies from one read of X.
  * Implements the MXFP8 format paragraph (32 E4M3 values per E8M0 scale, scale
@@ -205,6 +210,25 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
 int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *codes, uint8_t *scales, float *token_scales,
                               uint16_t *out, void *stream);
+
+/*
+ * Block-scaled GEMM on MXFP8 operands: C = A x B^T with
+ *   C[m][n] = sum_k dec(a[m][k]) 2^(sa[m][k/32] - 127) dec(b[n][k]) 2^(sb[n][k/32] - 127),
+ * the forward GEMM that consumes the rowwise copies made by
+ * mxq_mxfp8_quantize_rowcol (activations [M][K], weights [N][K], both
+ * K-contiguous; the MXFP8 format and recipe paragraphs).  Products are
+ * exact; the sum is accumulated in fp32 by the matrix instructions, so C
+ * differs from the exact sum by at most K 2^-24 sum_k |a b| (plus one BF16
+ * rounding, nearest-even, for MXQ_OUT_BF16).
+ *
+ *   a  [M][K] E4M3 codes, 16-byte aligned;  a_scales [M][K/32] E8M0, 4-byte aligned.
+ *   b  [N][K] E4M3 codes, 16-byte aligned;  b_scales [N][K/32] E8M0, 4-byte aligned.
+ *   c  [M][N] fp32 or BF16 (out_dtype), row-major.
+ *   K % 128 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1.
+ */
+int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                   const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                   void *c, void *stream);
 
 /*
  * Outputs of the grouped call.  MXFP8 uses the first five fields, NVFP4 the

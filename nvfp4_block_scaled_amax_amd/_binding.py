@@ -31,6 +31,8 @@ MXQ_FMT_MXFP8_ROW = 1
 MXQ_FMT_MXFP8_COL = 2
 MXQ_FMT_MXFP8_ROWCOL = 3
 MXQ_FMT_NVFP4 = 4
+MXQ_OUT_F32 = 0
+MXQ_OUT_BF16 = 1
 
 # Every symbol include/mxq.h declares.
 EXPORTS = (
@@ -39,6 +41,7 @@ EXPORTS = (
     "mxq_nvfp4_quantize_gateup_pair",
     "mxq_dequantize_bf16",
     "mxq_quantize_dequant_bf16",
+    "mxq_mxfp8_gemm",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
@@ -78,6 +81,7 @@ def lib():
         "mxq_nvfp4_quantize_gateup_pair": [P, P, I64, I64, I64, P, P, P, P, P, P],
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
+        "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
@@ -160,6 +164,12 @@ def mxq_quantize_dequant_bf16(fmt, x, rows, cols, codes, scales, token_scales, o
     _check(lib().mxq_quantize_dequant_bf16(fmt, _ptr(x), rows, cols, _ptr(codes), _ptr(scales),
                                            _ptr(token_scales), _ptr(out), _stream(stream)),
            "mxq_quantize_dequant_bf16")
+
+
+def mxq_mxfp8_gemm(a, a_scales, b, b_scales, M, N, K, out_dtype, c, stream=None):
+    _check(lib().mxq_mxfp8_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), M, N, K,
+                                out_dtype, _ptr(c), _stream(stream)),
+           "mxq_mxfp8_gemm")
 
 
 def mxq_grouped_quantize(fmt, x, total_rows, cols, seg_offsets, n_groups, out, stream=None):

@@ -121,6 +121,18 @@ def quantize_dequant_bf16(fmt: int, x, keep_codes: bool = True, stream=None) -> 
     return QuantDequant(codes, scales, ts, out)
 
 
+def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16,
+               stream=None) -> torch.Tensor:
+    """C = A x B^T on MXFP8 operands (rowwise copies: a [M][K], b [N][K] with
+    [.][K/32] E8M0 scales); returns C [M][N] as fp32 or BF16."""
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    code = B.MXQ_OUT_BF16 if out_dtype == torch.bfloat16 else B.MXQ_OUT_F32
+    B.mxq_mxfp8_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, code, c, stream)
+    return c
+
+
 class GroupedMXFP8(NamedTuple):
     row_codes: torch.Tensor
     row_scales: torch.Tensor

@@ -21,6 +21,8 @@ struct Buf {
 };
 
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 62;
+// GEMM tiles address their 256 rows with 32-bit offsets.
+constexpr int64_t MAX_GEMM_K = (int64_t)1 << 23;
 constexpr int64_t MAX_GRID_ROWS = 0x7FFFFFFF;     // per-token NVFP4: one workgroup per row
 constexpr int64_t MAX_BLOCKS = 0xFFFFFFFF;        // 16-element blocks indexed in 32 bits
 constexpr int64_t MAX_MXFP8_COLS = (int64_t)1 << 26;  // 32-row tile offsets fit 32 bits
@@ -291,6 +293,33 @@ int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t 
         return st;
     return launched(mxq::launch_mxfp8_row_qdq(x, rows, cols, codes, scales, out,
                                               (hipStream_t)stream));
+}
+
+int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                   const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                   void *c, void *stream)
+{
+    if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
+        return MXQ_ERR_ARG;
+    if (!a || !a_scales || !b || !b_scales || !c)
+        return MXQ_ERR_NULL;
+    if (!size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N))
+        return MXQ_ERR_SIZE;
+    if (K % 128 != 0)
+        return MXQ_ERR_SHAPE;
+    if (K > MAX_GEMM_K)
+        return MXQ_ERR_SIZE;
+    const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
+    const Buf bb[5] = {{a, M * K, 16, false},
+                       {a_scales, M * (K / 32), 4, false},
+                       {b, N * K, 16, false},
+                       {b_scales, N * (K / 32), 4, false},
+                       {c, esz * M * N, esz, true}};
+    const int st = check_bufs(bb, 5);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_gemm(a, a_scales, b, b_scales, M, N, K,
+                                           out_dtype == MXQ_OUT_BF16, c, (hipStream_t)stream));
 }
 
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t cols,

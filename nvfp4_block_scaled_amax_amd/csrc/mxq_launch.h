@@ -62,4 +62,10 @@ hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *block_scale
                                 const float *fp32_scales, int64_t rows_per_scale, int64_t rows,
                                 int64_t cols, uint16_t *out, hipStream_t stream);
 
+// C[M][N] = A (MXFP8 [M][K], scales [M][K/32]) x B (MXFP8 [N][K], scales
+// [N][K/32])^T, fp32 accumulation, fp32 or BF16 result; K % 128 == 0.
+hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                             const uint8_t *b_scales, int64_t M, int64_t N, int64_t K,
+                             bool bf16_out, void *c, hipStream_t stream);
+
 }  // namespace mxq

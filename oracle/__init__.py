@@ -312,3 +312,27 @@ def quantize_dequant_nvfp4(x):
     returns (codes, block_scales, token_scales, bf16 bits)."""
     codes, bs, ts = nvfp4_per_token(x)
     return codes, bs, ts, dequant_nvfp4(codes, bs, ts, 1)
+
+
+def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
+    """The exact block-scaled product C = A B^T of two MXFP8 operands stored
+    K-contiguous (rowwise copies: a [M][K], b [N][K], E8M0 scales per 32
+    along K): C[m][n] = sum_k dec(a[m][k]) 2^(sa - 127) dec(b[n][k]) 2^(sb - 127)
+    (page "Miles: end-to-end MXFP8 and per-token NVFP4 RL on Blackwell",
+    MXFP8 format and recipe paragraphs: the forward GEMM consumes the rowwise
+    copies).  Every decoded value and product is exact in binary64; the sum
+    is a binary64 matrix product, whose rounding (at most K 2^-53 sum |a b|)
+    is far below the fp32 accumulation being checked.  Returns float64 [M][N]
+    and the magnitude sum S[m][n] = sum_k |a b| that error bounds scale with."""
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    table[[0x7F, 0xFF]] = np.nan                        # never produced by the quantizer
+
+    def decode(codes, scales):
+        codes = np.ascontiguousarray(codes, np.uint8)
+        scales = np.ascontiguousarray(scales, np.uint8)
+        s = np.ldexp(1.0, scales.astype(np.int64) - 127)
+        return table[codes] * np.repeat(s, 32, axis=1)
+
+    A = decode(a_codes, a_scales)
+    B = decode(b_codes, b_scales)
+    return A @ B.T, np.abs(A) @ np.abs(B).T

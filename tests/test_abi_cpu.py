@@ -104,6 +104,16 @@ def test_validation_before_any_device_call():
     assert status_of(qd, F4, A, 1 << 31, 16, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
     assert status_of(qd, F4, A, 4, 16, A + 4, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
 
+    gm = mxq.mxq_mxfp8_gemm
+    assert status_of(gm, A, A, A, A, 64, 64, 128, 7, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(gm, A, None, A, A, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gm, A, A, A, A, 64, 64, 96, 0, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(gm, A, A, A, A, 0, 64, 128, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gm, A, A, A, A, 64, 64, 1 << 24, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gm, A + 8, A, A, A, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gm, A, A + 2, A, A, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gm, A, A, A, A, 64, 64, 128, 0, A + 2, 0) == mxq.MXQ_ERR_ALIGN
+
     gd = mxq.mxq_grouped_quantize_dispatch
     nv = {"codes": A, "block_scales": A, "token_scales": A}
     F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL

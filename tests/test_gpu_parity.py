@@ -447,6 +447,95 @@ def test_grouped_config5_full(orc):
 
 
 # ---------------------------------------------------------------------------
+# Block-scaled GEMM on MXFP8 operands
+# ---------------------------------------------------------------------------
+
+# The fp8 matrix instruction sums the 64 products of one K slice to about
+# 12 bits relative to their magnitude sum (measured on MI355X: at most
+# 2^-11.6 sum|a b| on all-positive operands, independent of K; the fp32
+# accumulator itself adds at full precision).  Realistic operands are held
+# to 2^-10 sum|a b| plus the fp32 accumulation term; operands whose products
+# fit a narrow window, where the instruction's sum is exact, to bit equality.
+GEMM_REL = 2.0 ** -10
+
+
+def check_gemm(orc, x: np.ndarray, w: np.ndarray, name: str, row_sample=None):
+    """A = rowwise MXFP8 of x [M][K], B = rowwise MXFP8 of w [N][K] (both made
+    by the oracle), C = A B^T on the GPU in fp32 and BF16, against the
+    oracle's exact product: |C - exact| <= (2^-10 + K 2^-24) sum|a b|, plus
+    half a BF16 step of |exact| (at most 2^-8 |exact|) for the BF16 result."""
+    M, K = x.shape
+    N = w.shape[0]
+    ac, as_ = orc.mxfp8_rowwise(x)
+    bc, bs_ = orc.mxfp8_rowwise(w)
+    rows = np.arange(M) if row_sample is None else np.asarray(row_sample)
+    C, S = orc.mxfp8_gemm(ac[rows], as_[rows], bc, bs_)
+    bound = (GEMM_REL + K * 2.0 ** -24) * S
+    for dt in (torch.float32, torch.bfloat16):
+        announce(f"mxfp8 gemm {name} M={M} N={N} K={K} {dt}")
+        c = api.mxfp8_gemm(dev(ac), dev(as_), dev(bc), dev(bs_), out_dtype=dt)
+        torch.cuda.synchronize()
+        got = c.float().cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(got - C)
+        lim = bound if dt == torch.float32 else bound + 2.0 ** -8 * np.abs(C)
+        bad = np.argwhere(err > lim)
+        assert bad.size == 0, (f"{name} {dt}: {len(bad)} outside the bound, first {tuple(bad[0])}: "
+                               f"got {got[tuple(bad[0])]!r} want {C[tuple(bad[0])]!r}")
+
+
+def test_gemm_exact_when_products_fit(orc):
+    """Codes 1 .. 3.75 and block scales 2^-1 .. 2^1: every slice's sum of
+    products is exact inside the instruction and every partial sum is exact
+    in fp32, so C must equal the oracle bit for bit (fp32), and the BF16
+    result must be the nearest-even rounding of it.  Ragged M and N."""
+    rng = np.random.default_rng(73)
+    M, N, K = 300, 200, 256
+    codes = np.array([c for c in range(256) if ((c >> 3) & 15) in (7, 8)], np.uint8)
+    a = rng.choice(codes, (M, K)).astype(np.uint8)
+    b = rng.choice(codes, (N, K)).astype(np.uint8)
+    sa = rng.integers(126, 129, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(126, 129, (N, K // 32)).astype(np.uint8)
+    C, _ = orc.mxfp8_gemm(a, sa, b, sb)
+    announce(f"mxfp8 gemm exact {M}x{N}x{K}")
+    c32 = api.mxfp8_gemm(dev(a), dev(sa), dev(b), dev(sb), out_dtype=torch.float32)
+    c16 = api.mxfp8_gemm(dev(a), dev(sa), dev(b), dev(sb), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.astype(np.float32), C)          # exact in fp32 by construction
+    assert_same(host(c32).view(np.uint32), C.astype(np.float32).view(np.uint32), "fp32 C")
+    assert_same(host(c16), orc.bf16_round_sat_many(C).reshape(M, N), "bf16 C")
+
+
+def test_gemm_small_shapes(orc):
+    """One tile, ragged M and N (partial tiles), several K steps."""
+    for (M, N, K, seed) in ((256, 256, 128, 1), (300, 200, 256, 2), (1, 1, 128, 3),
+                            (64, 520, 384, 4), (513, 33, 640, 5)):
+        x = W.student_t_activations(M, K, seed)
+        w = W.mode_random(N, K, seed + 100)
+        check_gemm(orc, x, w, f"t3 x random {M}x{N}x{K}")
+
+
+def test_gemm_scale_range(orc):
+    """Operands whose 32-blocks span many binades (every block scale differs),
+    with products kept inside the fp32 range."""
+    rng = np.random.default_rng(71)
+    M, N, K = 96, 160, 512
+    x = rng.standard_normal((M, K)) * np.ldexp(1.0, rng.integers(-30, 30, (M, K // 32))).repeat(32, 1)
+    w = rng.standard_normal((N, K)) * np.ldexp(1.0, rng.integers(-30, 30, (N, K // 32))).repeat(32, 1)
+    check_gemm(orc, W.bf16_bits(x), W.bf16_bits(w), "wide scales")
+
+
+def test_gemm_dense_forward_full(orc):
+    """The dense forward of the pages' layer: activation 2048 x 2048 times a
+    weight with out_features 8192 (both random mode), every column of 384
+    sampled rows."""
+    x = W.config2_activation("random")
+    w = W.config2_weight("random")
+    rng = np.random.default_rng(72)
+    rows = np.concatenate([np.arange(64), rng.integers(0, 2048, 256), np.arange(1984, 2048)])
+    check_gemm(orc, x, w, "2048x8192x2048", row_sample=rows)
+
+
+# ---------------------------------------------------------------------------
 # Quantize + dequant in one pass
 # ---------------------------------------------------------------------------
 

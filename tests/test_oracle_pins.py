@@ -613,3 +613,69 @@ def test_grouped_colwise_equals_standalone_and_zero_pad(orc):
         sc, ss = orc.mxfp8_colwise(pad)
         assert np.array_equal(codes[a:b], sc[:n])
         assert np.array_equal(scales[P[e]:P[e + 1]], ss)
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled GEMM (the consumer of the rowwise MXFP8 copies)
+# ---------------------------------------------------------------------------
+
+def _e4m3_frac(c: int) -> F:
+    v = X.E4M3_POS[c & 0x7F]
+    return -v if c & 0x80 else v
+
+
+def test_mxfp8_gemm_bruteforce(orc):
+    """Tiny GEMMs against sums of Fractions over every k (M != N, so a
+    transposed operand or a scale taken from the wrong block or row fails).
+    Over the whole code range the binary64 sum may round (within K 2^-53 of
+    the magnitude sum); with codes and scales in a few binades it is exact."""
+    rng = np.random.default_rng(61)
+    M, N, K = 3, 5, 96
+    every = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    narrow = np.array([c for c in every if 5 <= ((c >> 3) & 15) <= 10], np.uint8)
+    for codes, lo, hi, exact_sum in ((every, 118, 137, False), (narrow, 125, 130, True)):
+        a = rng.choice(codes, (M, K)).astype(np.uint8)
+        b = rng.choice(codes, (N, K)).astype(np.uint8)
+        sa = rng.integers(lo, hi, (M, K // 32)).astype(np.uint8)
+        sb = rng.integers(lo, hi, (N, K // 32)).astype(np.uint8)
+        C, S = orc.mxfp8_gemm(a, sa, b, sb)
+        for m in range(M):
+            for n in range(N):
+                terms = [_e4m3_frac(int(a[m, k])) * _e4m3_frac(int(b[n, k])) *
+                         F(2) ** (int(sa[m, k // 32]) + int(sb[n, k // 32]) - 254)
+                         for k in range(K)]
+                exact, mag = sum(terms), sum(abs(v) for v in terms)
+                if exact_sum:
+                    assert F(C[m, n]) == exact and F(S[m, n]) == mag
+                else:
+                    assert abs(F(C[m, n]) - exact) <= K * mag / 2 ** 53
+                    assert abs(F(S[m, n]) - mag) <= K * mag / 2 ** 53
+
+
+def test_mxfp8_gemm_special_cases(orc):
+    """B = identity-like codes (1.0 at k = n, unit scales) returns A's decoded
+    values; raising one scale byte of A doubles exactly that block's share."""
+    rng = np.random.default_rng(62)
+    M, K = 4, 128
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    a = rng.choice(codes, (M, K)).astype(np.uint8)
+    sa = rng.integers(120, 134, (M, K // 32)).astype(np.uint8)
+    b = np.zeros((K, K), np.uint8)
+    b[np.arange(K), np.arange(K)] = 0x38                    # E4M3 1.0
+    sb = np.full((K, K // 32), 127, np.uint8)
+    C, _ = orc.mxfp8_gemm(a, sa, b, sb)
+    want = np.array([[float(_e4m3_frac(int(a[m, k]))) * 2.0 ** (int(sa[m, k // 32]) - 127)
+                      for k in range(K)] for m in range(M)])
+    assert np.array_equal(C, want)
+    bn = rng.choice(codes, (6, K)).astype(np.uint8)
+    sbn = rng.integers(124, 130, (6, K // 32)).astype(np.uint8)
+    C0, _ = orc.mxfp8_gemm(a, sa, bn, sbn)
+    sa2 = sa.copy()
+    sa2[1, 2] += 1
+    C1, _ = orc.mxfp8_gemm(a, sa2, bn, sbn)
+    blk = a.copy()
+    blk[:, :64] = 0
+    blk[:, 96:] = 0                                          # only block 2 (k 64..95)
+    Cb, _ = orc.mxfp8_gemm(blk, sa, bn, sbn)
+    assert np.array_equal(C1[1], C0[1] + Cb[1])
+    assert np.array_equal(np.delete(C1, 1, 0), np.delete(C0, 1, 0))
