@@ -18,13 +18,20 @@
 //
 // Tiling.  A workgroup of four wavefronts computes a 256x256 tile of C in K
 // steps of 128; wavefront (wm, wn) owns a 128x128 quarter: 4x4 instruction
-// tiles, 256 fp32 accumulators per lane.  Each K step, the workgroup copies
-// the 256x128-byte A and B slices (and their 4 scale bytes per row) from
-// global memory to LDS; 16-byte chunks of each 128-byte LDS row are XOR-
-// swizzled by the row index, so the 32 rows one fragment read touches fall
-// in distinct banks.  Two LDS buffers: the next step's global loads are in
-// flight while the current step computes, then land in the other buffer.
-// Rows past M or N read the last valid row and are not stored.
+// tiles, 256 fp32 accumulators per lane.  Each K step's 256x128-byte A and B
+// slices and their scale bytes go from global memory straight into LDS
+// (global_load_lds: lane l of a wavefront writes the 16 bytes at LDS base +
+// 16 l), into the buffer the step after next computes from, so the loads
+// run under the current step's matrix instructions.  16-byte chunks of each
+// 128-byte LDS row are XOR-swizzled by the row index (each lane fetches the
+// global chunk that belongs in its slot), so the 32 rows one fragment read
+// touches fall in distinct banks.  Fragments of the step's second 64-wide
+// sub-step are read while the first sub-step's instructions run.  Rows past
+// M or N read the last valid row and are not stored.
+//
+// BF16 result: the accumulators go through LDS (rows padded to 272 bytes, so
+// the two row groups a store instruction writes miss each other's banks) and
+// leave as 16-byte stores that cover 256 contiguous bytes of a row.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -32,108 +39,167 @@ namespace mxq {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
 constexpr int GEMM_BM = 256, GEMM_BN = 256, GEMM_BK = 128;
 constexpr int GEMM_THREADS = 256;
-constexpr int GEMM_TILE_BYTES = GEMM_BM * GEMM_BK;              // 32 KiB per operand
+constexpr int GEMM_CHUNKS = GEMM_BM * GEMM_BK / 16;             // 16-byte chunks per operand slice
+constexpr int GEMM_STAGE_BYTES = 2 * GEMM_CHUNKS * 16 + 2 * GEMM_BM * 4;
+constexpr int GEMM_EPI_ROW = 128 * 2 + 16;                      // padded BF16 row of a quarter
+constexpr int GEMM_EPI_BYTES = 4 * 128 * GEMM_EPI_ROW;
+constexpr int GEMM_LDS_BYTES =
+    2 * GEMM_STAGE_BYTES > GEMM_EPI_BYTES ? 2 * GEMM_STAGE_BYTES : GEMM_EPI_BYTES;
 
-struct GemmSmem {
-    u32x4_t a[2][GEMM_BM * GEMM_BK / 16];
-    u32x4_t b[2][GEMM_BN * GEMM_BK / 16];
-    uint32_t as[2][GEMM_BM];          // 4 scale bytes (the K step's 4 blocks) per row
-    uint32_t bs[2][GEMM_BN];
+// One stage in LDS: A chunks, B chunks, A scale words, B scale words.
+struct GemmStageLds {
+    u32x4_t *a, *b;
+    uint32_t *as, *bs;
 };
+__device__ __forceinline__ GemmStageLds gemm_stage(uint8_t *lds, int buf)
+{
+    uint8_t *p = lds + buf * GEMM_STAGE_BYTES;
+    return GemmStageLds{reinterpret_cast<u32x4_t *>(p),
+                        reinterpret_cast<u32x4_t *>(p + GEMM_CHUNKS * 16),
+                        reinterpret_cast<uint32_t *>(p + 2 * GEMM_CHUNKS * 16),
+                        reinterpret_cast<uint32_t *>(p + 2 * GEMM_CHUNKS * 16 + GEMM_BM * 4)};
+}
 
-// 16-byte chunk c of LDS row r (8 chunks per 128-byte row), swizzled.
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// 16-byte chunk c of LDS row r (8 chunks per 128-byte row), swizzled by
+// (r / 2) % 8.  A 16-byte read serves 16 lanes per cycle (64 banks: 16
+// slots of 16 bytes); a fragment read's 16 lanes are 16 consecutive rows at
+// one logical chunk, and 8 (r % 2) + (c ^ (r / 2) % 8) is distinct over any
+// 16 consecutive rows.  (Swizzling by r % 8 left rows r and r + 8 in one
+// slot: half of all LDS cycles were bank conflicts.)
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// Thread t's share of one K step: rows t/8 + 32 i (i < 8) at chunk t % 8 of
-// each operand, and one scale word per operand (row t).  The row offsets are
-// 32-bit and fixed for the whole K loop (rows past M or N clamped to the
-// last row); the K step only moves the wave-uniform base pointers.
-struct GemmStage {
-    u32x4_t a[8], b[8];
-    uint32_t as, bs;
-};
+// Per-lane global offsets of one stage, fixed over the K loop (the K step
+// only moves the wave-uniform base pointers).  Copy i of wavefront w fills
+// LDS rows 8q .. 8q+7, q = 4i + w: lane l lands in row r = 8q + l/8,
+// physical chunk l%8, which holds logical chunk (l%8) ^ ((r/2) % 8) =
+// (l%8) ^ ((4w + l/16) % 8) (the same for every i).  Scale words: row
+// 64w + l.  Rows past M or N are clamped to the last row.  Only the first
+// row and the clamp are kept; the offsets are recomputed per stage (a min
+// and a multiply-add each), which keeps registers for fragments.
 struct GemmOffsets {
-    uint32_t a[8], b[8];    // (row - tile row 0) * K + 16 (t % 8)
-    uint32_t as, bs;        // (row - tile row 0) * K / 32
+    uint32_t r0, c16;           // first row of copy 0 (8w + l/8), 16 * logical chunk
+    uint32_t ra_max, rb_max;    // last valid row of the A and B tiles
+    uint32_t K;
+    uint32_t as, bs;            // scale-row offsets (clamped row * K / 32)
+    __device__ __forceinline__ uint32_t a(int i) const
+    {
+        const uint32_t r = r0 + 32 * i;
+        return (r < ra_max ? r : ra_max) * K + c16;
+    }
+    __device__ __forceinline__ uint32_t b(int i) const
+    {
+        const uint32_t r = r0 + 32 * i;
+        return (r < rb_max ? r : rb_max) * K + c16;
+    }
 };
-
 __device__ __forceinline__ GemmOffsets gemm_offsets(int64_t m0, int64_t n0, int64_t M, int64_t N,
-                                                    int64_t K, int t)
+                                                    int64_t K, int w, int lane)
 {
     GemmOffsets o;
-    const int c = t & 7;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int r = (t >> 3) + 32 * i;
-        const int64_t ra = m0 + r < M ? r : M - 1 - m0;
-        const int64_t rb = n0 + r < N ? r : N - 1 - n0;
-        o.a[i] = (uint32_t)(ra * K + 16 * c);
-        o.b[i] = (uint32_t)(rb * K + 16 * c);
-    }
-    const int64_t ra = m0 + t < M ? t : M - 1 - m0;
-    const int64_t rb = n0 + t < N ? t : N - 1 - n0;
-    o.as = (uint32_t)(ra * (K >> 5));
-    o.bs = (uint32_t)(rb * (K >> 5));
+    o.r0 = (uint32_t)(8 * w + (lane >> 3));
+    o.c16 = 16u * (uint32_t)((lane & 7) ^ ((4 * w + (lane >> 4)) & 7));
+    o.ra_max = (uint32_t)(M - 1 - m0 < GEMM_BM ? M - 1 - m0 : GEMM_BM - 1);
+    o.rb_max = (uint32_t)(N - 1 - n0 < GEMM_BN ? N - 1 - n0 : GEMM_BN - 1);
+    o.K = (uint32_t)K;
+    const uint32_t r = (uint32_t)(64 * w + lane);
+    o.as = (r < o.ra_max ? r : o.ra_max) * (uint32_t)(K >> 5);
+    o.bs = (r < o.rb_max ? r : o.rb_max) * (uint32_t)(K >> 5);
     return o;
 }
 
-// a, b: the tile's first row at column k0; as_, bs_: its scale row at block k0/32.
-__device__ __forceinline__ void gemm_load(GemmStage &st, const GemmOffsets &o,
-                                          const uint8_t *__restrict__ a,
-                                          const uint8_t *__restrict__ as_,
-                                          const uint8_t *__restrict__ b,
-                                          const uint8_t *__restrict__ bs_)
+// Global -> LDS copies of one wavefront: lane l's bytes land at LDS byte
+// address lds + size * l.  Issued as instructions the compiler does not
+// track, so that it does not make the current step's LDS reads wait for the
+// next step's copies (it cannot tell the two buffers apart and would wait
+// for all of them); the kernel orders them itself: every wavefront waits
+// for its own copies (vmcnt 0) before the barrier that publishes a stage.
+__device__ __forceinline__ void lds_copy16(const uint8_t *base, uint32_t off, uint32_t lds)
 {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        st.a[i] = *reinterpret_cast<const u32x4_t *>(a + o.a[i]);
-        st.b[i] = *reinterpret_cast<const u32x4_t *>(b + o.b[i]);
-    }
-    st.as = *reinterpret_cast<const uint32_t *>(as_ + o.as);
-    st.bs = *reinterpret_cast<const uint32_t *>(bs_ + o.bs);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const uint8_t *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
 }
 
-__device__ __forceinline__ void gemm_store_lds(GemmSmem &sm, int buf, const GemmStage &st, int t)
+// Issue one stage's copies (a, b: the tile's first row at column k0; as_,
+// bs_: its scale row at block k0/32; all wave-uniform, so they sit in scalar
+// registers and each lane adds a 32-bit offset) into the LDS stage at byte
+// address st.
+__device__ __forceinline__ void gemm_issue(uint32_t st, const GemmOffsets &o, const uint8_t *a,
+                                           const uint8_t *as_, const uint8_t *b,
+                                           const uint8_t *bs_, int w)
 {
-    const int c = t & 7;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int r = (t >> 3) + 32 * i;
-        sm.a[buf][swz(r, c)] = st.a[i];
-        sm.b[buf][swz(r, c)] = st.b[i];
+    for (int i = 0; i < GEMM_CHUNKS / (4 * 64); i++) {
+        const uint32_t q = (uint32_t)(4 * i + w) * 1024;
+        lds_copy16(a, o.a(i), st + q);
+        lds_copy16(b, o.b(i), st + GEMM_CHUNKS * 16 + q);
     }
-    sm.as[buf][t] = st.as;
-    sm.bs[buf][t] = st.bs;
+    lds_copy4(as_, o.as, st + 2 * GEMM_CHUNKS * 16 + 256 * w);
+    lds_copy4(bs_, o.bs, st + 2 * GEMM_CHUNKS * 16 + GEMM_BM * 4 + 256 * w);
 }
 
-// One 32x64 fragment (A rows or B columns r0 .. r0+31) of K sub-step s for
-// this lane, and its scale word shifted so that byte 2s holds the lane's
-// block scale.
-__device__ __forceinline__ i32x8_t gemm_frag(const u32x4_t *__restrict__ tile, int r, int h, int s)
+// One 32x64 fragment (A rows or B columns) of K sub-step s for this lane:
+// bytes 0..15 from logical chunk 4s + h (k = 64s + 16h, block 2s), bytes
+// 16..31 from chunk 4s + 2 + h (k = 64s + 32 + 16h, block 2s + 1).
+__device__ __forceinline__ i32x8_t gemm_frag(const u32x4_t *tile, int r, int h, int s)
 {
     const u32x4_t lo = tile[swz(r, 4 * s + h)];
     const u32x4_t hi = tile[swz(r, 4 * s + 2 + h)];
-    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2, so workgroup w runs on XCD w % 8.  Workgroup w takes position
+// L = (w % 8) * per_xcd + w / 8 of a grouped order (GM tile rows at a time,
+// column-major inside a group), so each XCD's L2 serves one compact block
+// of the tile grid and fetches only that block's A rows and B columns
+// (2048 x 8192 x 2048: 48 MiB from memory instead of 160 MiB).
+struct GemmGrid {
+    uint32_t tiles_m, tiles_n, per_xcd, group_m;
+};
+__device__ __forceinline__ bool gemm_tile(const GemmGrid &g, uint32_t w, uint32_t *mt,
+                                          uint32_t *nt)
+{
+    const uint32_t L = (w & 7) * g.per_xcd + (w >> 3);
+    if (L >= g.tiles_m * g.tiles_n)
+        return false;
+    const uint32_t span = g.group_m * g.tiles_n;
+    const uint32_t grp = L / span, r = L % span;
+    const uint32_t rows = g.tiles_m - grp * g.group_m < g.group_m ? g.tiles_m - grp * g.group_m
+                                                                  : g.group_m;
+    *mt = grp * g.group_m + r % rows;
+    *nt = r / rows;
+    return true;
 }
 
 template <bool BF16_OUT>
 __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
-    const uint8_t *__restrict__ Bs, int64_t M, int64_t N, int64_t K, uint32_t tiles_n,
+    const uint8_t *__restrict__ Bs, int64_t M, int64_t N, int64_t K, GemmGrid grid,
     void *__restrict__ C)
 {
-    __shared__ GemmSmem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
     const int t = (int)tid();
-    const int lane = t & 63, wave = t >> 6;
+    const int lane = t & 63, wave = (int)wave_in_group();    // wave index: uniform
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
-    const uint32_t tile = wg_id();
-    const int64_t m0 = (int64_t)(tile / tiles_n) * GEMM_BM;
-    const int64_t n0 = (int64_t)(tile % tiles_n) * GEMM_BN;
+    uint32_t mt, nt;
+    if (!gemm_tile(grid, wg_id(), &mt, &nt))
+        return;
+    const int64_t m0 = (int64_t)mt * GEMM_BM;
+    const int64_t n0 = (int64_t)nt * GEMM_BN;
     const int64_t ksteps = K / GEMM_BK;
 
     f32x16_t acc[4][4];
@@ -143,74 +209,108 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
         for (int j = 0; j < 4; j++)
             acc[i][j] = f32x16_t{};
 
-    const GemmOffsets off = gemm_offsets(m0, n0, M, N, K, t);
+    const GemmOffsets off = gemm_offsets(m0, n0, M, N, K, wave, lane);
     const uint8_t *a = A + m0 * K, *b = B + n0 * K;
     const uint8_t *as_ = As + m0 * (K >> 5), *bs_ = Bs + n0 * (K >> 5);
-    GemmStage st;
-    gemm_load(st, off, a, as_, b, bs_);
-    gemm_store_lds(sm, 0, st, t);
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+    gemm_issue(lds_addr, off, a, as_, b, bs_, wave);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int64_t ks = 0; ks < ksteps; ks++) {
-        const int buf = (int)(ks & 1);
-        const bool more = ks + 1 < ksteps;
-        if (more) {
+        const GemmStageLds cur = gemm_stage(lds, (int)(ks & 1));
+        if (ks + 1 < ksteps) {
             const int64_t k1 = (ks + 1) * GEMM_BK;
-            gemm_load(st, off, a + k1, as_ + (k1 >> 5), b + k1, bs_ + (k1 >> 5));
+            gemm_issue(lds_addr + (uint32_t)((ks + 1) & 1) * GEMM_STAGE_BYTES, off, a + k1,
+                       as_ + (k1 >> 5), b + k1, bs_ + (k1 >> 5), wave);
         }
         uint32_t sa[4], sb[4];
+        i32x8_t fa[2][4], fb[2][4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            sa[i] = sm.as[buf][128 * wm + 32 * i + r32] >> (8 * h);
-            sb[i] = sm.bs[buf][128 * wn + 32 * i + r32] >> (8 * h);
+            sa[i] = cur.as[128 * wm + 32 * i + r32] >> (8 * h);
+            sb[i] = cur.bs[128 * wn + 32 * i + r32] >> (8 * h);
+            fa[0][i] = gemm_frag(cur.a, 128 * wm + 32 * i + r32, h, 0);
+            fb[0][i] = gemm_frag(cur.b, 128 * wn + 32 * i + r32, h, 0);
         }
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            i32x8_t fb[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                fb[j] = gemm_frag(sm.b[buf], 128 * wn + 32 * j + r32, h, s);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const i32x8_t fa = gemm_frag(sm.a[buf], 128 * wm + 32 * i + r32, h, s);
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    if (s == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa, fb[j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa, fb[j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
-                }
-            }
+        for (int i = 0; i < 4; i++) {
+            fa[1][i] = gemm_frag(cur.a, 128 * wm + 32 * i + r32, h, 1);
+            fb[1][i] = gemm_frag(cur.b, 128 * wn + 32 * i + r32, h, 1);
         }
-        if (more)
-            gemm_store_lds(sm, buf ^ 1, st, t);
-        __syncthreads();
-    }
-
-    // Epilogue: lane holds column n of each instruction tile, rows 8(e/4) +
-    // 4h + e%4.
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t n = n0 + 128 * wn + 32 * j + r32;
-        if (n >= N)
-            continue;
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < M) {
-                    if constexpr (BF16_OUT) {
-                        const uint32_t u = f2u(acc[i][j][e]);
-                        reinterpret_cast<uint16_t *>(C)[m * N + n] =
-                            (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-                    } else {
-                        reinterpret_cast<float *>(C)[m * N + n] = acc[i][j][e];
-                    }
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa[0][i], fb[0][j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa[1][i], fb[1][j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
+        // This wavefront's copies of the next stage have landed (and its
+        // reads of this one returned); after the barrier, everyone's have.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // The epilogue reuses the stage buffers: no wavefront may still be
+    // reading them.
+    __syncthreads();
+
+    // Epilogue: lane holds column r32 of each instruction tile, rows 8(e/4) +
+    // 4h + e%4.
+    if constexpr (BF16_OUT) {
+        uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int r = 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                    const uint32_t u = f2u(acc[i][j][e]);
+                    *reinterpret_cast<uint16_t *>(q + r * GEMM_EPI_ROW + 2 * (32 * j + r32)) =
+                        (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                }
+        __syncthreads();
+        // 16 lanes per 256-byte row, 4 rows per instruction.
+        const int64_t col = n0 + 128 * wn + 8 * (lane & 15);
+        uint16_t *c = reinterpret_cast<uint16_t *>(C);
+        // 16-byte stores need every row start 16-byte aligned.
+        const bool vec = (N & 7) == 0 && ((uintptr_t)C & 15) == 0;
+        for (int rr = 0; rr < 128; rr += 4) {
+            const int r = rr + (lane >> 4);
+            const int64_t m = m0 + 128 * wm + r;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(q + r * GEMM_EPI_ROW +
+                                                                  16 * (lane & 15));
+            if (m < M) {
+                if (vec && col + 8 <= N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + col));
+                } else {
+                    const uint16_t *p = reinterpret_cast<const uint16_t *>(&v);
+                    for (int e = 0; e < 8 && col + e < N; e++)
+                        c[m * N + col + e] = p[e];
                 }
             }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t n = n0 + 128 * wn + 32 * j + r32;
+            if (n >= N)
+                continue;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                    if (m < M)
+                        reinterpret_cast<float *>(C)[m * N + n] = acc[i][j][e];
+                }
+        }
     }
 }
 
@@ -219,15 +319,20 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const ui
                              bool bf16_out, void *c, hipStream_t stream)
 {
     const int64_t tm = (M + GEMM_BM - 1) / GEMM_BM, tn = (N + GEMM_BN - 1) / GEMM_BN;
-    if (tm * tn > 0x7FFFFFFF)
+    if (tm * tn > 0x7FFFFFF)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(tm * tn)), block(GEMM_THREADS);
+    GemmGrid g;
+    g.tiles_m = (uint32_t)tm;
+    g.tiles_n = (uint32_t)tn;
+    g.per_xcd = (uint32_t)((tm * tn + 7) / 8);
+    g.group_m = (uint32_t)(tm < 8 ? tm : 8);
+    const dim3 grid(8 * g.per_xcd), block(GEMM_THREADS);
     if (bf16_out)
         hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, grid, block, 0, stream, a, a_scales, b,
-                           b_scales, M, N, K, (uint32_t)tn, c);
+                           b_scales, M, N, K, g, c);
     else
         hipLaunchKernelGGL(mxfp8_gemm_kernel<false>, grid, block, 0, stream, a, a_scales, b,
-                           b_scales, M, N, K, (uint32_t)tn, c);
+                           b_scales, M, N, K, g, c);
     return hipGetLastError();
 }
 

@@ -508,7 +508,7 @@ def test_gemm_exact_when_products_fit(orc):
 def test_gemm_small_shapes(orc):
     """One tile, ragged M and N (partial tiles), several K steps."""
     for (M, N, K, seed) in ((256, 256, 128, 1), (300, 200, 256, 2), (1, 1, 128, 3),
-                            (64, 520, 384, 4), (513, 33, 640, 5)):
+                            (64, 520, 384, 4), (513, 33, 640, 5), (40, 300, 128, 6)):
         x = W.student_t_activations(M, K, seed)
         w = W.mode_random(N, K, seed + 100)
         check_gemm(orc, x, w, f"t3 x random {M}x{N}x{K}")
