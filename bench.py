@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     "nvfp4_scoped_kernel": ["mxq_nvfp4.hip"],
     "dequant_mxfp8_kernel": ["mxq_dequant.hip"],
     "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
+    "mxfp8_gemm_kernel": ["mxq_gemm.hip"],
+    "nvfp4_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_token_qdq_kernel": ["mxq_nvfp4.hip"],
 }
@@ -407,6 +409,8 @@ def config_timings(torch, E, W, legs, log):
         log("C5 dispatch timed")
         res.update(qdq_timings(torch, E, W, dev, empty))
         log("quantize + dequant timed")
+        res.update(gemm_timings(torch, E, W, dev, empty))
+        log("GEMM timed")
     return res
 
 
@@ -463,6 +467,67 @@ def qdq_small_timings(torch, E, W, dev, empty):
                           n, sets, [kern])
         res[k] = v
         del bufs, launches, x0
+        torch.cuda.empty_cache()
+    return res
+
+
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+
+
+def gemm_timings(torch, E, W, dev, empty):
+    """Block-scaled MXFP8 GEMM of the dense layer: the 2048 x 2048 activation
+    times the 8192 x 2048 weight (rowwise MXFP8 copies made by the library's
+    quantizer), BF16 result; timed like the other configs and priced against
+    the fp8 matrix-instruction peak."""
+    res = {}
+    for name, (M, N, K) in (("G_mxfp8_gemm_2048x8192x2048", (2048, 8192, 2048)),
+                            ("G_mxfp8_gemm_8192x8192x2048", (8192, 8192, 2048))):
+        x = dev(W.student_t_activations(M, K, 81) if M != 2048 else W.config2_activation("random"))
+        w = dev(W.config2_weight("random") if N == 8192 and K == 2048 else
+                W.mode_random(N, K, 82))
+        ac, as_ = empty((M, K)), empty((M, K // 32))
+        bc, bs_ = empty((N, K)), empty((N, K // 32))
+        E.mxq_mxfp8_quantize_rowcol(x, M, K, ac, as_, None, None)
+        E.mxq_mxfp8_quantize_rowcol(w, N, K, bc, bs_, None, None)
+        c = empty((M, N), torch.bfloat16)
+        fn = lambda: E.mxq_mxfp8_gemm(ac, as_, bc, bs_, M, N, K, E.MXQ_OUT_BF16, c)
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        med = float(np.median(ms))
+        flops = 2.0 * M * N * K
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"desc": f"MXFP8 GEMM C[{M}][{N}] = A[{M}][{K}] B[{N}][{K}]^T, BF16 out",
+                     "kernels": ["mxfp8_gemm_kernel<true>"], "ms_median": round(med, 5),
+                     "ms_min": round(float(np.min(ms)), 5), "flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                  "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}}
+        del x, w, ac, as_, bc, bs_, c
+        torch.cuda.empty_cache()
+    # NVFP4: per-token activations times a weight with one scope scale; the
+    # matrix instructions are BF16 (the per-16 E4M3 block scales rule out the
+    # fp4 ones), so the peak is the BF16 one.
+    for name, (M, N, K) in (("G_nvfp4_gemm_2048x8192x2048", (2048, 8192, 2048)),):
+        x = dev(W.student_t_activations(M, K, 83))
+        w = dev(W.bf16_bits(np.random.default_rng(84).normal(0, 0.02, (N, K))))
+        ac, ab, as_ = empty((M, K // 2)), empty((M, K // 16)), empty((M,), torch.float32)
+        bc, bb, bs_ = empty((N, K // 2)), empty((N, K // 16)), empty((1,), torch.float32)
+        E.mxq_nvfp4_quantize_per_token(x, M, K, ac, ab, as_)
+        E.mxq_nvfp4_quantize_gateup_pair(w, None, 1, N, K, bc, bb, None, None, bs_)
+        c = empty((M, N), torch.bfloat16)
+        fn = lambda: E.mxq_nvfp4_gemm(ac, ab, as_, 1, bc, bb, bs_, N, M, N, K, E.MXQ_OUT_BF16, c)
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        med = float(np.median(ms))
+        flops = 2.0 * M * N * K
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"desc": f"NVFP4 GEMM C[{M}][{N}] = A[{M}][{K}] B[{N}][{K}]^T, per-token and "
+                             "per-tensor FP32 scales, BF16 out",
+                     "kernels": ["nvfp4_gemm_kernel<true>"], "ms_median": round(med, 5),
+                     "ms_min": round(float(np.min(ms)), 5), "flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}}
+        del x, w, ac, ab, as_, bc, bb, bs_, c
         torch.cuda.empty_cache()
     return res
 

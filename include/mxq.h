@@ -231,6 +231,31 @@ int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    void *c, void *stream);
 
 /*
+ * Block-scaled GEMM on NVFP4 operands: C = A x B^T with
+ *   C[m][n] = sa[m / rows_per_a_scale] sb[n / rows_per_b_scale]
+ *             sum_k dec(a[m][k]) dec(ba[m][k/16]) dec(b[n][k]) dec(bb[n][k/16]),
+ * the forward GEMM of the per-token NVFP4 recipe (activations with one FP32
+ * scale per token, rows_per_a_scale = 1; weights with one FP32 scale per
+ * tensor or expert, rows_per_b_scale = its rows): the NVFP4 format and
+ * per-token activation scale paragraphs.  Each dec(code) dec(block scale) is
+ * exactly a BF16 value; the sum is accumulated in fp32 by the BF16 matrix
+ * instructions and the FP32 scales are applied to it as
+ * fp32(fp32(sum * sa) * sb), then rounded to BF16 (nearest-even) for
+ * MXQ_OUT_BF16.
+ *
+ *   a  [M][K/2] packed E2M1 (even element in the low nibble), 16-byte aligned;
+ *   a_block_scales [M][K/16] E4M3, 4-byte aligned;  a_scales FP32, one per
+ *   rows_per_a_scale rows.  b, b_block_scales, b_scales likewise for [N][K].
+ *   c  [M][N] fp32 or BF16 (out_dtype).
+ *   K % 64 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1;
+ *   rows_per_a_scale, rows_per_b_scale >= 1.
+ */
+int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
+                   int64_t rows_per_a_scale, const uint8_t *b, const uint8_t *b_block_scales,
+                   const float *b_scales, int64_t rows_per_b_scale, int64_t M, int64_t N,
+                   int64_t K, int out_dtype, void *c, void *stream);
+
+/*
  * Outputs of the grouped call.  MXFP8 uses the first five fields, NVFP4 the
  * last three; the others are ignored.
  *   row_codes, row_scales  as mxq_mxfp8_quantize_rowcol over all total_rows.

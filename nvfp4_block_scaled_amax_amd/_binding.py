@@ -42,6 +42,7 @@ EXPORTS = (
     "mxq_dequantize_bf16",
     "mxq_quantize_dequant_bf16",
     "mxq_mxfp8_gemm",
+    "mxq_nvfp4_gemm",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
@@ -82,6 +83,7 @@ def lib():
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
+        "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
@@ -170,6 +172,14 @@ def mxq_mxfp8_gemm(a, a_scales, b, b_scales, M, N, K, out_dtype, c, stream=None)
     _check(lib().mxq_mxfp8_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), M, N, K,
                                 out_dtype, _ptr(c), _stream(stream)),
            "mxq_mxfp8_gemm")
+
+
+def mxq_nvfp4_gemm(a, a_block_scales, a_scales, rows_per_a_scale, b, b_block_scales, b_scales,
+                   rows_per_b_scale, M, N, K, out_dtype, c, stream=None):
+    _check(lib().mxq_nvfp4_gemm(_ptr(a), _ptr(a_block_scales), _ptr(a_scales), rows_per_a_scale,
+                                _ptr(b), _ptr(b_block_scales), _ptr(b_scales), rows_per_b_scale,
+                                M, N, K, out_dtype, _ptr(c), _stream(stream)),
+           "mxq_nvfp4_gemm")
 
 
 def mxq_grouped_quantize(fmt, x, total_rows, cols, seg_offsets, n_groups, out, stream=None):

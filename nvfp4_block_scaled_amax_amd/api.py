@@ -133,6 +133,22 @@ def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16,
     return c
 
 
+def nvfp4_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
+               rows_per_a_scale: int = 1, rows_per_b_scale: Optional[int] = None,
+               out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """C = A x B^T on NVFP4 operands (a [M][K/2], b [N][K/2], E4M3 block
+    scales per 16, FP32 scales per rows_per_*_scale rows; by default one per
+    token of A and one for all of B)."""
+    M, half = a_codes.shape
+    N, K = b_codes.shape[0], 2 * half
+    rpb = N if rows_per_b_scale is None else rows_per_b_scale
+    c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    code = B.MXQ_OUT_BF16 if out_dtype == torch.bfloat16 else B.MXQ_OUT_F32
+    B.mxq_nvfp4_gemm(a_codes, a_block_scales, a_scales, rows_per_a_scale, b_codes,
+                     b_block_scales, b_scales, rpb, M, N, K, code, c, stream)
+    return c
+
+
 class GroupedMXFP8(NamedTuple):
     row_codes: torch.Tensor
     row_scales: torch.Tensor

@@ -322,6 +322,38 @@ int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                                            out_dtype == MXQ_OUT_BF16, c, (hipStream_t)stream));
 }
 
+int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
+                   int64_t rows_per_a_scale, const uint8_t *b, const uint8_t *b_block_scales,
+                   const float *b_scales, int64_t rows_per_b_scale, int64_t M, int64_t N,
+                   int64_t K, int out_dtype, void *c, void *stream)
+{
+    if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
+        return MXQ_ERR_ARG;
+    if (!a || !a_block_scales || !a_scales || !b || !b_block_scales || !b_scales || !c)
+        return MXQ_ERR_NULL;
+    if (!size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N) || rows_per_a_scale < 1 ||
+        rows_per_b_scale < 1)
+        return MXQ_ERR_SIZE;
+    if (K % 64 != 0)
+        return MXQ_ERR_SHAPE;
+    if (K > MAX_GEMM_K)
+        return MXQ_ERR_SIZE;
+    const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
+    const Buf bb[7] = {{a, M * K / 2, 16, false},
+                       {a_block_scales, M * (K / 16), 4, false},
+                       {a_scales, 4 * ((M + rows_per_a_scale - 1) / rows_per_a_scale), 4, false},
+                       {b, N * K / 2, 16, false},
+                       {b_block_scales, N * (K / 16), 4, false},
+                       {b_scales, 4 * ((N + rows_per_b_scale - 1) / rows_per_b_scale), 4, false},
+                       {c, esz * M * N, esz, true}};
+    const int st = check_bufs(bb, 7);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_gemm(a, a_block_scales, a_scales, rows_per_a_scale, b,
+                                           b_block_scales, b_scales, rows_per_b_scale, M, N, K,
+                                           out_dtype == MXQ_OUT_BF16, c, (hipStream_t)stream));
+}
+
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t cols,
                          const int64_t *seg_offsets, int64_t n_groups, const mxq_grouped_out *out,
                          void *stream)

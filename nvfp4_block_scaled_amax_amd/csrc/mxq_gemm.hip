@@ -184,6 +184,90 @@ __device__ __forceinline__ bool gemm_tile(const GemmGrid &g, uint32_t w, uint32_
     return true;
 }
 
+// Write the wavefront's 128x128 quarter of the C tile.  Lane holds column
+// r32 of each instruction tile, rows 8(e/4) + 4h + e%4.  SCALED: multiply by
+// the FP32 scales of the row (sa[m / rows_per_a]) and of the column
+// (sb[n / rows_per_b]), as fp32(fp32(acc * sa) * sb).  BF16: through LDS
+// (rows padded to 272 bytes), 16 lanes per 256-byte row, 4 rows per store
+// instruction; the caller has synchronised the workgroup, so LDS is free.
+template <bool BF16_OUT, bool SCALED>
+__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8_t *lds, int wave,
+                                              int lane, int64_t m0, int64_t n0, int64_t M,
+                                              int64_t N, void *__restrict__ C,
+                                              const float *__restrict__ sa, int64_t rows_per_a,
+                                              const float *__restrict__ sb, int64_t rows_per_b)
+{
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, h = lane >> 5;
+    float cs[4] = {1.0f, 1.0f, 1.0f, 1.0f};     // column scales of the lane's 4 columns
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int64_t n = n0 + 128 * wn + 32 * j + r32;
+            n = n < N ? n : N - 1;
+            cs[j] = sb[n / rows_per_b];
+        }
+    }
+    auto value = [&](int i, int j, int e) {
+        float v = acc[i][j][e];
+        if constexpr (SCALED) {
+            int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+            m = m < M ? m : M - 1;
+            v = (v * sa[m / rows_per_a]) * cs[j];
+        }
+        return v;
+    };
+    if constexpr (BF16_OUT) {
+        uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int r = 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                    const uint32_t u = f2u(value(i, j, e));
+                    *reinterpret_cast<uint16_t *>(q + r * GEMM_EPI_ROW + 2 * (32 * j + r32)) =
+                        (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                }
+        __syncthreads();
+        const int64_t col = n0 + 128 * wn + 8 * (lane & 15);
+        uint16_t *c = reinterpret_cast<uint16_t *>(C);
+        // 16-byte stores need every row start 16-byte aligned.
+        const bool vec = (N & 7) == 0 && ((uintptr_t)C & 15) == 0;
+        for (int rr = 0; rr < 128; rr += 4) {
+            const int r = rr + (lane >> 4);
+            const int64_t m = m0 + 128 * wm + r;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(q + r * GEMM_EPI_ROW +
+                                                                  16 * (lane & 15));
+            if (m < M) {
+                if (vec && col + 8 <= N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + col));
+                } else {
+                    const uint16_t *p = reinterpret_cast<const uint16_t *>(&v);
+                    for (int e = 0; e < 8 && col + e < N; e++)
+                        c[m * N + col + e] = p[e];
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t n = n0 + 128 * wn + 32 * j + r32;
+            if (n >= N)
+                continue;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                    if (m < M)
+                        reinterpret_cast<float *>(C)[m * N + n] = value(i, j, e);
+                }
+        }
+    }
+}
+
 template <bool BF16_OUT>
 __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
@@ -259,59 +343,171 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     // The epilogue reuses the stage buffers: no wavefront may still be
     // reading them.
     __syncthreads();
+    gemm_epilogue<BF16_OUT, false>(acc, lds, wave, lane, m0, n0, M, N, C, nullptr, 1, nullptr, 1);
+}
 
-    // Epilogue: lane holds column r32 of each instruction tile, rows 8(e/4) +
-    // 4h + e%4.
-    if constexpr (BF16_OUT) {
-        uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
+// ---------------------------------------------------------------------------
+// NVFP4 GEMM: C[m][n] = sa[m / rows_per_a] sb[n / rows_per_b] sum_k
+// dec(ca[m][k]) dec(ba[m][k/16]) dec(cb[n][k]) dec(bb[n][k/16]).  The
+// per-16 E4M3 block scales are not an E8M0 power of two, so the fp4 matrix
+// instructions cannot apply them; but dec(code) dec(block scale) has at most
+// 6 significant bits and lies in [2^-10, 2688], so it is exactly a BF16
+// value.  The kernel dequantizes each K step to BF16 on its way into LDS
+// (register-staged: the next step's codes and scales are loaded while the
+// current step's BF16 matrix instructions run) and applies the FP32 scales
+// in the epilogue.
+//
+// BF16 instruction: v_mfma_f32_32x32x16_bf16, lane (r, h) holds 8
+// consecutive K values: chunk 2s + h (16 bytes) of the 64-element step for
+// slice s.  LDS rows are 64 BF16 = 128 bytes, swizzled as above.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int NVG_BK = 64;                                       // K elements per step
+constexpr int NVG_STAGE_BYTES = 2 * GEMM_BM * NVG_BK * 2;       // A and B BF16 slices
+
+// Thread t's share of one step: row t of A and of B (clamped), 64 codes
+// (32 bytes) and 4 block-scale bytes each.
+struct NvStage {
+    u32x4_t ca[2], cb[2];
+    uint32_t sa, sb;
+};
+
+__device__ __forceinline__ void nv_load(NvStage &st, const uint8_t *a, const uint8_t *ab,
+                                        const uint8_t *b, const uint8_t *bb, uint32_t ra,
+                                        uint32_t rb, uint32_t half_k, uint32_t blk_k)
+{
+    st.ca[0] = *reinterpret_cast<const u32x4_t *>(a + ra * half_k);
+    st.ca[1] = *reinterpret_cast<const u32x4_t *>(a + ra * half_k + 16);
+    st.cb[0] = *reinterpret_cast<const u32x4_t *>(b + rb * half_k);
+    st.cb[1] = *reinterpret_cast<const u32x4_t *>(b + rb * half_k + 16);
+    st.sa = *reinterpret_cast<const uint32_t *>(ab + ra * blk_k);
+    st.sb = *reinterpret_cast<const uint32_t *>(bb + rb * blk_k);
+}
+
+// 8 BF16 (one 16-byte chunk) from 4 code bytes under block scale value d:
+// dec(c) d is exact in f32 and has at most 8 significant bits, so its BF16
+// is the upper half of its f32 bits.
+__device__ __forceinline__ u32x4_t nv_chunk_bf16(uint32_t codes, float d)
+{
+    u32x4_t o;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+    for (int j = 0; j < 4; j++) {
+        const float2_t v = e2m1_values((codes >> (8 * j)) & 0xFFu);
+        o[j] = __builtin_amdgcn_perm(f2u(v[1] * d), f2u(v[0] * d), 0x07060302u);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void nv_store_row(u32x4_t *tile, int r, const u32x4_t (&c)[2],
+                                             uint32_t scales)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float d = e4m3_value((scales >> (8 * (j >> 1))) & 0xFFu);
+        tile[swz(r, j)] = nv_chunk_bf16(c[j >> 2][j & 3], d);
+    }
+}
+
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ Ab, const float *__restrict__ As,
+    int64_t rows_per_a, const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bb,
+    const float *__restrict__ Bs, int64_t rows_per_b, int64_t M, int64_t N, int64_t K,
+    GemmGrid grid, void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    const int t = (int)tid();
+    const int lane = t & 63, wave = (int)wave_in_group();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, h = lane >> 5;
+    uint32_t mt, nt;
+    if (!gemm_tile(grid, wg_id(), &mt, &nt))
+        return;
+    const int64_t m0 = (int64_t)mt * GEMM_BM;
+    const int64_t n0 = (int64_t)nt * GEMM_BN;
+    const int64_t ksteps = K / NVG_BK;
+    const uint32_t half_k = (uint32_t)(K >> 1), blk_k = (uint32_t)(K >> 4);
+    const uint32_t ra = (uint32_t)(m0 + t < M ? t : M - 1 - m0);
+    const uint32_t rb = (uint32_t)(n0 + t < N ? t : N - 1 - n0);
+    const uint8_t *a = A + m0 * (K >> 1), *b = B + n0 * (K >> 1);
+    const uint8_t *ab = Ab + m0 * (K >> 4), *bb = Bb + n0 * (K >> 4);
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = f32x16_t{};
+
+    auto tile_a = [&](int buf) { return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES); };
+    auto tile_b = [&](int buf) {
+        return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES + GEMM_BM * NVG_BK * 2);
+    };
+    NvStage st;
+    nv_load(st, a, ab, b, bb, ra, rb, half_k, blk_k);
+    nv_store_row(tile_a(0), t, st.ca, st.sa);
+    nv_store_row(tile_b(0), t, st.cb, st.sb);
+    __syncthreads();
+
+    for (int64_t ks = 0; ks < ksteps; ks++) {
+        const int buf = (int)(ks & 1);
+        const bool more = ks + 1 < ksteps;
+        if (more) {
+            const int64_t k1 = (ks + 1) * NVG_BK;
+            nv_load(st, a + (k1 >> 1), ab + (k1 >> 4), b + (k1 >> 1), bb + (k1 >> 4), ra, rb,
+                    half_k, blk_k);
+        }
+        const u32x4_t *ta = tile_a(buf), *tb = tile_b(buf);
+#pragma unroll
+        for (int sl = 0; sl < NVG_BK / 16; sl++) {
+            bf16x8_t fb[4];
 #pragma unroll
             for (int j = 0; j < 4; j++)
+                fb[j] = __builtin_bit_cast(bf16x8_t, tb[swz(128 * wn + 32 * j + r32, 2 * sl + h)]);
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int r = 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-                    const uint32_t u = f2u(acc[i][j][e]);
-                    *reinterpret_cast<uint16_t *>(q + r * GEMM_EPI_ROW + 2 * (32 * j + r32)) =
-                        (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-                }
-        __syncthreads();
-        // 16 lanes per 256-byte row, 4 rows per instruction.
-        const int64_t col = n0 + 128 * wn + 8 * (lane & 15);
-        uint16_t *c = reinterpret_cast<uint16_t *>(C);
-        // 16-byte stores need every row start 16-byte aligned.
-        const bool vec = (N & 7) == 0 && ((uintptr_t)C & 15) == 0;
-        for (int rr = 0; rr < 128; rr += 4) {
-            const int r = rr + (lane >> 4);
-            const int64_t m = m0 + 128 * wm + r;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(q + r * GEMM_EPI_ROW +
-                                                                  16 * (lane & 15));
-            if (m < M) {
-                if (vec && col + 8 <= N) {
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + col));
-                } else {
-                    const uint16_t *p = reinterpret_cast<const uint16_t *>(&v);
-                    for (int e = 0; e < 8 && col + e < N; e++)
-                        c[m * N + col + e] = p[e];
-                }
+            for (int i = 0; i < 4; i++) {
+                const bf16x8_t fa =
+                    __builtin_bit_cast(bf16x8_t, ta[swz(128 * wm + 32 * i + r32, 2 * sl + h)]);
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0,
+                                                                        0);
             }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t n = n0 + 128 * wn + 32 * j + r32;
-            if (n >= N)
-                continue;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-                    if (m < M)
-                        reinterpret_cast<float *>(C)[m * N + n] = acc[i][j][e];
-                }
+        if (more) {
+            nv_store_row(tile_a(buf ^ 1), t, st.ca, st.sa);
+            nv_store_row(tile_b(buf ^ 1), t, st.cb, st.sb);
         }
+        __syncthreads();
     }
+    gemm_epilogue<BF16_OUT, true>(acc, lds, wave, lane, m0, n0, M, N, C, As, rows_per_a, Bs,
+                                  rows_per_b);
+}
+
+hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
+                             const float *a_scales, int64_t rows_per_a, const uint8_t *b,
+                             const uint8_t *b_block_scales, const float *b_scales,
+                             int64_t rows_per_b, int64_t M, int64_t N, int64_t K, bool bf16_out,
+                             void *c, hipStream_t stream)
+{
+    const int64_t tm = (M + GEMM_BM - 1) / GEMM_BM, tn = (N + GEMM_BN - 1) / GEMM_BN;
+    if (tm * tn > 0x7FFFFFF)
+        return hipErrorInvalidValue;
+    GemmGrid g;
+    g.tiles_m = (uint32_t)tm;
+    g.tiles_n = (uint32_t)tn;
+    g.per_xcd = (uint32_t)((tm * tn + 7) / 8);
+    g.group_m = (uint32_t)(tm < 8 ? tm : 8);
+    const dim3 grid(8 * g.per_xcd), block(GEMM_THREADS);
+    if (bf16_out)
+        hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, grid, block, 0, stream, a, a_block_scales,
+                           a_scales, rows_per_a, b, b_block_scales, b_scales, rows_per_b, M, N, K,
+                           g, c);
+    else
+        hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, block, 0, stream, a, a_block_scales,
+                           a_scales, rows_per_a, b, b_block_scales, b_scales, rows_per_b, M, N, K,
+                           g, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,

@@ -68,4 +68,12 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const ui
                              const uint8_t *b_scales, int64_t M, int64_t N, int64_t K,
                              bool bf16_out, void *c, hipStream_t stream);
 
+// C[M][N] = sa[m / rows_per_a] sb[n / rows_per_b] x A (NVFP4 [M][K/2], E4M3
+// block scales [M][K/16]) x B (NVFP4 [N][K/2], [N][K/16])^T; K % 64 == 0.
+hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
+                             const float *a_scales, int64_t rows_per_a, const uint8_t *b,
+                             const uint8_t *b_block_scales, const float *b_scales,
+                             int64_t rows_per_b, int64_t M, int64_t N, int64_t K, bool bf16_out,
+                             void *c, hipStream_t stream);
+
 }  // namespace mxq

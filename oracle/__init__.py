@@ -336,3 +336,32 @@ def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
     A = decode(a_codes, a_scales)
     B = decode(b_codes, b_scales)
     return A @ B.T, np.abs(A) @ np.abs(B).T
+
+
+def nvfp4_gemm(a_codes, a_block_scales, a_scales, rows_per_a, b_codes, b_block_scales,
+               b_scales, rows_per_b) -> np.ndarray:
+    """The exact block-scaled product of two NVFP4 operands stored
+    K-contiguous: C[m][n] = sa[m // rows_per_a] sb[n // rows_per_b]
+    sum_k dec(a) dec(ba) dec(b) dec(bb) (page "Miles: end-to-end MXFP8 and
+    per-token NVFP4 RL on Blackwell", NVFP4 format and per-token activation
+    scale paragraphs: an element's value is its E2M1 code times its 16-block's
+    E4M3 scale times the FP32 scale of its scope).  Every decoded value and
+    product is exact in binary64, the sum a binary64 matrix product.  Returns
+    float64 [M][N] and the magnitude sum S = sum_k |a b| times |sa sb|."""
+    e2 = np.array([e2m1_value(c) for c in range(16)], np.float64)
+    e4 = np.array([e4m3_value(c) for c in range(256)], np.float64)
+
+    def decode(codes, bs, fs, per):
+        codes = np.ascontiguousarray(codes, np.uint8)
+        rows, half = codes.shape
+        vals = np.empty((rows, 2 * half), np.float64)
+        vals[:, 0::2] = e2[codes & 15]
+        vals[:, 1::2] = e2[codes >> 4]
+        vals *= np.repeat(e4[np.ascontiguousarray(bs, np.uint8)], 16, axis=1)
+        s = np.asarray(fs, np.float32).astype(np.float64)[np.arange(rows) // per]
+        return vals, s
+
+    A, sa = decode(a_codes, a_block_scales, a_scales, rows_per_a)
+    B, sb = decode(b_codes, b_block_scales, b_scales, rows_per_b)
+    scale = sa[:, None] * sb[None, :]
+    return (A @ B.T) * scale, (np.abs(A) @ np.abs(B).T) * np.abs(scale)

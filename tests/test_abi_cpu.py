@@ -114,6 +114,14 @@ def test_validation_before_any_device_call():
     assert status_of(gm, A, A + 2, A, A, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
     assert status_of(gm, A, A, A, A, 64, 64, 128, 0, A + 2, 0) == mxq.MXQ_ERR_ALIGN
 
+    ng = mxq.mxq_nvfp4_gemm
+    assert status_of(ng, A, A, A, 1, A, A, A, 64, 64, 64, 64, 5, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(ng, A, A, None, 1, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(ng, A, A, A, 0, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(ng, A, A, A, 1, A, A, A, 64, 64, 64, 96, 0, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(ng, A + 4, A, A, 1, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(ng, A, A + 2, A, 1, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+
     gd = mxq.mxq_grouped_quantize_dispatch
     nv = {"codes": A, "block_scales": A, "token_scales": A}
     F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL

@@ -535,6 +535,83 @@ def test_gemm_dense_forward_full(orc):
     check_gemm(orc, x, w, "2048x8192x2048", row_sample=rows)
 
 
+def check_nvfp4_gemm(orc, qa, qb, rows_per_b, name, row_sample=None, rel=0.0):
+    """qa = (codes, block scales, fp32 scales per row), qb = (codes, block
+    scales, fp32 scales per rows_per_b rows), both made by the oracle; C on
+    the GPU in fp32 and BF16 against the oracle's exact product, to
+    (rel + K 2^-24 + 2^-23) sum|a b| |sa sb| (fp32 accumulation -- the BF16
+    matrix instructions accumulate at full fp32 precision, measured at most
+    2^-23.8 sum|a b| -- and the two FP32 scale multiplications), plus half a
+    BF16 step for the BF16 result."""
+    ac, ab, as_ = qa
+    bc, bb, bs_ = qb
+    M, K = ac.shape[0], 2 * ac.shape[1]
+    N = bc.shape[0]
+    rows = np.arange(M) if row_sample is None else np.asarray(row_sample)
+    C, S = orc.nvfp4_gemm(ac[rows], ab[rows], as_[rows], 1, bc, bb, bs_, rows_per_b)
+    bound = (rel + K * 2.0 ** -24 + 2.0 ** -23) * S
+    for dt in (torch.float32, torch.bfloat16):
+        announce(f"nvfp4 gemm {name} M={M} N={N} K={K} {dt}")
+        c = api.nvfp4_gemm(dev(ac), dev(ab), dev(as_), dev(bc), dev(bb), dev(bs_),
+                           rows_per_b_scale=rows_per_b, out_dtype=dt)
+        torch.cuda.synchronize()
+        got = c.float().cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(got - C)
+        lim = bound if dt == torch.float32 else bound + 2.0 ** -8 * np.abs(C)
+        bad = np.argwhere(err > lim)
+        worst = float(np.max(err / np.maximum(S, 1e-300)))
+        announce(f"  max err / sum|ab| = 2^{np.log2(max(worst, 1e-300)):.1f}")
+        assert bad.size == 0, (f"{name} {dt}: {len(bad)} outside the bound, first {tuple(bad[0])}: "
+                               f"got {got[tuple(bad[0])]!r} want {C[tuple(bad[0])]!r}")
+
+
+def test_nvfp4_gemm_exact_when_products_fit(orc):
+    """E2M1 magnitudes up to 3, block scales 1 .. 1.875, power-of-two FP32
+    scales: every partial sum is exact in fp32, so the fp32 result must equal
+    the oracle bit for bit.  Ragged M and N, several FP32 scales in B."""
+    rng = np.random.default_rng(74)
+    M, N, K = 300, 200, 128
+    nib = np.array([0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13], np.uint8)   # |value| <= 3
+    a = (rng.choice(nib, (M, K // 2)) | (rng.choice(nib, (M, K // 2)) << 4)).astype(np.uint8)
+    b = (rng.choice(nib, (N, K // 2)) | (rng.choice(nib, (N, K // 2)) << 4)).astype(np.uint8)
+    ba = rng.integers(0x38, 0x40, (M, K // 16)).astype(np.uint8)           # 1 .. 1.875
+    bb = rng.integers(0x38, 0x40, (N, K // 16)).astype(np.uint8)
+    sa = np.ldexp(1.0, rng.integers(-3, 4, M)).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-3, 4, (N + 49) // 50)).astype(np.float32)
+    C, _ = orc.nvfp4_gemm(a, ba, sa, 1, b, bb, sb, 50)
+    announce(f"nvfp4 gemm exact {M}x{N}x{K}")
+    c32 = api.nvfp4_gemm(dev(a), dev(ba), dev(sa), dev(b), dev(bb), dev(sb), rows_per_b_scale=50,
+                         out_dtype=torch.float32)
+    c16 = api.nvfp4_gemm(dev(a), dev(ba), dev(sa), dev(b), dev(bb), dev(sb), rows_per_b_scale=50,
+                         out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.astype(np.float32), C)
+    assert_same(host(c32).view(np.uint32), C.astype(np.float32).view(np.uint32), "fp32 C")
+    assert_same(host(c16), orc.bf16_round_sat_many(C).reshape(M, N), "bf16 C")
+
+
+def test_nvfp4_gemm_shapes(orc):
+    """Per-token NVFP4 activations (Student-t) times a weight quantized with
+    one FP32 scale for the tensor (the down-projection scope), ragged shapes."""
+    for (M, N, K, seed) in ((256, 256, 64, 1), (300, 200, 192, 2), (1, 1, 64, 3),
+                            (513, 40, 640, 4)):
+        qa = orc.nvfp4_per_token(W.student_t_activations(M, K, seed))
+        w = W.bf16_bits(np.random.default_rng(seed + 50).normal(0, 0.02, (1, N, K)))
+        wc, wb, _, _, ws = orc.nvfp4_gateup_pair(w, None)
+        check_nvfp4_gemm(orc, qa, (wc[0], wb[0], ws), N, f"t3 x N(0,0.02) {M}x{N}x{K}")
+
+
+def test_nvfp4_gemm_dense_forward_full(orc):
+    """The dense forward at the pages' shape: 2048 tokens x 2048 (per-token
+    NVFP4) times an 8192 x 2048 weight with one scope scale; 384 sampled rows."""
+    qa = orc.nvfp4_per_token(W.student_t_activations(2048, 2048, 83))
+    w = W.bf16_bits(np.random.default_rng(84).normal(0, 0.02, (1, 8192, 2048)))
+    wc, wb, _, _, ws = orc.nvfp4_gateup_pair(w, None)
+    rng = np.random.default_rng(85)
+    rows = np.concatenate([np.arange(64), rng.integers(0, 2048, 256), np.arange(1984, 2048)])
+    check_nvfp4_gemm(orc, qa, (wc[0], wb[0], ws), 8192, "2048x8192x2048", row_sample=rows)
+
+
 # ---------------------------------------------------------------------------
 # Quantize + dequant in one pass
 # ---------------------------------------------------------------------------

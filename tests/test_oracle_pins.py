@@ -679,3 +679,35 @@ def test_mxfp8_gemm_special_cases(orc):
     Cb, _ = orc.mxfp8_gemm(blk, sa, bn, sbn)
     assert np.array_equal(C1[1], C0[1] + Cb[1])
     assert np.array_equal(np.delete(C1, 1, 0), np.delete(C0, 1, 0))
+
+
+def test_nvfp4_gemm_bruteforce_and_dequant_route(orc):
+    """Tiny NVFP4 GEMMs against sums of Fractions (codes, 16-block scales and
+    FP32 scales decoded by the Fraction spec's tables); and, with unit FP32
+    scales, the same product through the oracle's own (pinned) BF16 dequant,
+    which is exact here because dec(code) dec(block scale) is a BF16 value."""
+    rng = np.random.default_rng(63)
+    M, N, K = 3, 4, 64
+    a = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
+    b = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    ba = rng.integers(0, 0x7F, (M, K // 16)).astype(np.uint8)
+    bb = rng.integers(0, 0x7F, (N, K // 16)).astype(np.uint8)
+    sa = np.ldexp(1.0, rng.integers(-4, 5, M)).astype(np.float32) * np.float32(1.25)
+    sb = np.array([0.375, 3.0], np.float32)                 # one scale per 2 rows of B
+    C, S = orc.nvfp4_gemm(a, ba, sa, 1, b, bb, sb, 2)
+
+    def val(codes, bs, m, k):
+        c = (int(codes[m, k // 2]) >> (4 * (k % 2))) & 15
+        v = X.E2M1_POS[c & 7] * X.E4M3_POS[int(bs[m, k // 16])]
+        return -v if c & 8 else v
+    for m in range(M):
+        for n in range(N):
+            s = F(float(sa[m])) * F(float(sb[n // 2]))
+            terms = [val(a, ba, m, k) * val(b, bb, n, k) for k in range(K)]
+            exact, mag = s * sum(terms), abs(s) * sum(abs(t) for t in terms)
+            assert abs(F(C[m, n]) - exact) <= K * mag / 2 ** 52
+    one_a, one_b = np.ones(M, np.float32), np.ones(N, np.float32)
+    C1, _ = orc.nvfp4_gemm(a, ba, one_a, 1, b, bb, one_b, N)
+    ya = W.bf16_to_f64(orc.dequant_nvfp4(a, ba, one_a, 1))
+    yb = W.bf16_to_f64(orc.dequant_nvfp4(b, bb, one_b, 1))
+    assert np.array_equal(C1, ya @ yb.T)
