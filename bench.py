@@ -123,6 +123,9 @@ def build_legs(torch, mxq, api, W, log, want=lambda group: True):
     if want("qdq"):
         build_qdq(torch, E, W, legs, dev, empty)
         log("qdq ready")
+    if want("gemm"):
+        build_gemm(torch, E, W, legs, dev, empty)
+        log("gemm ready")
     return legs
 
 
@@ -471,6 +474,31 @@ def qdq_small_timings(torch, E, W, dev, empty):
     return res
 
 
+def build_gemm(torch, E, W, legs, dev, empty):
+    """The dense-layer GEMMs (2048 x 8192 x 2048, BF16 result) as legs, for
+    kernel statistics; bytes are the operands read and the result written,
+    elems the multiply-adds.  Timed with their matrix roofline in the configs."""
+    M, N, K = 2048, 8192, 2048
+    x, w = dev(W.config2_activation("random")), dev(W.config2_weight("random"))
+    ac, as_, bc, bs_ = empty((M, K)), empty((M, K // 32)), empty((N, K)), empty((N, K // 32))
+    E.mxq_mxfp8_quantize_rowcol(x, M, K, ac, as_, None, None)
+    E.mxq_mxfp8_quantize_rowcol(w, N, K, bc, bs_, None, None)
+    c = empty((M, N), torch.bfloat16)
+    legs.append(Leg("gemm_mxfp8", lambda: E.mxq_mxfp8_gemm(ac, as_, bc, bs_, M, N, K,
+                                                           E.MXQ_OUT_BF16, c),
+                    (M + N) * K * (1 + 1 / 32), 2 * M * N, M * N * K, ["mxfp8_gemm_kernel<true>"],
+                    f"MXFP8 GEMM {M}x{N}x{K}, BF16 out"))
+    na, nb, ns = empty((M, K // 2)), empty((M, K // 16)), empty((M,), torch.float32)
+    wa, wb, ws = empty((N, K // 2)), empty((N, K // 16)), empty((1,), torch.float32)
+    E.mxq_nvfp4_quantize_per_token(x, M, K, na, nb, ns)
+    E.mxq_nvfp4_quantize_gateup_pair(w, None, 1, N, K, wa, wb, None, None, ws)
+    c4 = empty((M, N), torch.bfloat16)
+    legs.append(Leg("gemm_nvfp4", lambda: E.mxq_nvfp4_gemm(na, nb, ns, 1, wa, wb, ws, N, M, N, K,
+                                                           E.MXQ_OUT_BF16, c4),
+                    (M + N) * K * (0.5 + 1 / 16) + 4 * M + 4, 2 * M * N, M * N * K,
+                    ["nvfp4_gemm_kernel<true>"], f"NVFP4 GEMM {M}x{N}x{K}, BF16 out"))
+
+
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 
@@ -608,9 +636,10 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--groups", default="act,wgt,tok,exp,grp",
                     help="comma list of leg groups to run (for profiling single kernels); "
-                         "'dsp' adds the fused-dispatch legs and 'qdq' the one-pass quantize + "
-                         "dequant legs; each replaces legs of the default step (the separate "
-                         "gather; quantize followed by dequant), so neither is part of it")
+                         "'dsp' adds the fused-dispatch legs, 'qdq' the one-pass quantize + "
+                         "dequant legs, 'gemm' the dense-layer GEMMs; the first two replace legs "
+                         "of the default step (the separate gather; quantize followed by "
+                         "dequant) and the GEMMs consume its outputs, so none is part of it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also time a plain elementwise copy of this many MiB (int32 bitwise "
                          "not, reads and writes each byte once), reported apart from the step, "
@@ -710,7 +739,8 @@ def main():
     # The export legs (four kernels, two reads of the weights) and the
     # three-launch export dequant are reported per leg but are not one launch.
     single = [l for l in legs if l.name not in ("nvfp4_export_gateup", "nvfp4_export_down",
-                                                "nvfp4_export_dequant", "gather_torch")]
+                                                "nvfp4_export_dequant", "gather_torch",
+                                                "gemm_mxfp8", "gemm_nvfp4")]
     dom = max(single or legs, key=lambda l: leg_info[l.name]["ms"])
     dom_ms = leg_info[dom.name]["ms"]
     achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
