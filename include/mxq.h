@@ -122,6 +122,19 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols,
                               void *stream);
 
 /*
+ * Comparison variant, not the contract: both MXFP8 copies under the OCP MX
+ * scale rule, shared exponent floor(log2 amax) - 8 (E4M3's largest
+ * exponent), elements the nearest E4M3 of x / 2^e saturated at 448.  Unlike
+ * the contract's rounded-up scale (the MXFP8 format paragraph: the block
+ * maximum is not clipped) this clips every block whose amax mantissa exceeds
+ * 1.75; the call exists to measure that.  Arguments, layouts and errors as
+ * mxq_mxfp8_quantize_rowcol.
+ */
+int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes,
+                                 uint8_t *col_scales, void *stream);
+
+/*
  * NVFP4 quantize with one online FP32 scale per token (row), in one call that
  * returns the packed codes, the E4M3 block scales and the per-token scales.
  * Implements the NVFP4 format paragraph (E2M1 codes, one E4M3 scale per 16

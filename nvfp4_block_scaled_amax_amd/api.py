@@ -42,6 +42,21 @@ def mxfp8_quantize_rowcol(x, rowwise: bool = True, colwise: bool = True,
     return MXFP8RowCol(rc, rs, cc, cs)
 
 
+def mxfp8_quantize_ocp_floor(x, rowwise: bool = True, colwise: bool = True,
+                             stream=None) -> MXFP8RowCol:
+    """Comparison variant: both MXFP8 copies under the OCP MX scale rule
+    (floor(log2 amax) - 8, saturating at 448), which clips."""
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    u8 = torch.uint8
+    rc = _empty((rows, cols), u8, x) if rowwise else None
+    rs = _empty((rows, cols // 32), u8, x) if rowwise else None
+    cc = _empty((rows, cols), u8, x) if colwise else None
+    cs = _empty((rows // 32, cols), u8, x) if colwise else None
+    B.mxq_mxfp8_quantize_ocp_floor(x, rows, cols, rc, rs, cc, cs, stream)
+    return MXFP8RowCol(rc, rs, cc, cs)
+
+
 class NVFP4(NamedTuple):
     codes: torch.Tensor
     block_scales: torch.Tensor
@@ -56,6 +71,19 @@ def nvfp4_quantize_per_token(x, stream=None) -> NVFP4:
     ts = _empty((rows,), torch.float32, x)
     B.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts, stream)
     return NVFP4(codes, bs, ts)
+
+
+def nvfp4_quantize_per_tensor(x, stream=None) -> NVFP4:
+    """Comparison variant: NVFP4 of an activation tensor with ONE FP32 scale
+    for the whole tensor (the batch-dependent scope the per-token recipe
+    replaces); the weight-export call with a single one-tensor scope."""
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    codes = _empty((1, rows, cols // 2), torch.uint8, x)
+    bs = _empty((1, rows, cols // 16), torch.uint8, x)
+    s = _empty((1,), torch.float32, x)
+    B.mxq_nvfp4_quantize_gateup_pair(x, None, 1, rows, cols, codes, bs, None, None, s, stream)
+    return NVFP4(codes[0], bs[0], s)
 
 
 class GateUpNVFP4(NamedTuple):

@@ -149,6 +149,38 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols, uin
                                             col_scales, nullptr, 0, (hipStream_t)stream));
 }
 
+int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes,
+                                 uint8_t *col_scales, void *stream)
+{
+    if (!x)
+        return MXQ_ERR_NULL;
+    if ((row_codes == nullptr) != (row_scales == nullptr) ||
+        (col_codes == nullptr) != (col_scales == nullptr) || (!row_codes && !col_codes))
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS)
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0 || (col_codes && rows % 32 != 0))
+        return MXQ_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    Buf b[5];
+    int k = 0;
+    b[k++] = {x, 2 * n, 16, false};
+    if (row_codes) {
+        b[k++] = {row_codes, n, 16, true};
+        b[k++] = {row_scales, n / 32, 1, true};
+    }
+    if (col_codes) {
+        b[k++] = {col_codes, n, 16, true};
+        b[k++] = {col_scales, n / 32, 8, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_ocp_floor(x, rows, cols, row_codes, row_scales, col_codes,
+                                                col_scales, (hipStream_t)stream));
+}
+
 int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                  uint8_t *block_scales, float *token_scales, void *stream)
 {

@@ -47,6 +47,14 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Element-wise min of the two unsigned 16-bit halves (v_pk_min_u16).
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    ushort2_t r = __builtin_elementwise_min(__builtin_bit_cast(ushort2_t, a),
+                                            __builtin_bit_cast(ushort2_t, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Max of the two halves of a dword, as a u32 in [0, 0xFFFF].
 __device__ __forceinline__ uint32_t hmax_u16(uint32_t a)
 {

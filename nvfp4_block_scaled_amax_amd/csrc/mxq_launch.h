@@ -29,6 +29,12 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
                                 int64_t *col_scale_offsets, const int64_t *row_tokens,
                                 int64_t n_tokens, hipStream_t stream);
 
+// Both MXFP8 copies under the OCP MX scale rule (floor(log2 amax) - 8,
+// saturating), a comparison variant; arguments as launch_mxfp8_dense.
+hipError_t launch_mxfp8_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
+                                  uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes,
+                                  uint8_t *col_scales, hipStream_t stream);
+
 // Rowwise MXFP8 and its BF16 dequantization in one pass; rc/rs may be null
 // (only the dequantized copy is stored).
 hipError_t launch_mxfp8_row_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,

@@ -169,7 +169,13 @@ __device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t sca
 
 // DQ: also write the BF16 dequantization of the rowwise codes (o.dq); ROW
 // may then be false (codes and scales computed but not stored).
-template <bool ROW, bool COL, bool FULL, bool DQ = false>
+// OCP: the OCP MX scale rule instead (a comparison variant): byte =
+// max(0, E - 8) = max(0, a - 1024) >> 7, i.e. floor(log2 amax) - 8, under
+// which x / 2^e can exceed 448.  The conversion instruction does not
+// saturate (it gives NaN from 464 up), so magnitudes are first clamped to
+// 448 * 2^e, whose BF16 bits are ((byte + 8) << 7) | 0x60; the nearest E4M3
+// of anything at or above that is 448.
+template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -190,10 +196,18 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
             uint32_t am = hmax_u16(m);
             am = max(am, dpp<DPP_XOR1>(am));
             am = max(am, dpp<DPP_XOR2>(am));
-            const uint32_t sc = subsat(am, 993u) & 0xFF80u;      // byte << 7
+            const uint32_t sc = subsat(am, OCP ? 1024u : 993u) & 0xFF80u;   // byte << 7
             const uint32_t scale = sc << 16;                     // byte << 23
-            const uint32_t w0 = cvt2<true>(cvt2<false>(0u, v[i][0], scale), v[i][1], scale);
-            const uint32_t w1 = cvt2<true>(cvt2<false>(0u, v[i][2], scale), v[i][3], scale);
+            uint32_t x0 = v[i][0], x1 = v[i][1], x2 = v[i][2], x3 = v[i][3];
+            if constexpr (OCP) {
+                const uint32_t lim = ((sc + 0x400u) | 0x60u) * 0x10001u;
+                x0 = (x0 & 0x80008000u) | pk_min_u16(a[i][0], lim);
+                x1 = (x1 & 0x80008000u) | pk_min_u16(a[i][1], lim);
+                x2 = (x2 & 0x80008000u) | pk_min_u16(a[i][2], lim);
+                x3 = (x3 & 0x80008000u) | pk_min_u16(a[i][3], lim);
+            }
+            const uint32_t w0 = cvt2<true>(cvt2<false>(0u, x0, scale), x1, scale);
+            const uint32_t w1 = cvt2<true>(cvt2<false>(0u, x2, scale), x3, scale);
             if (FULL || (col_ok && i < nr)) {
                 const uint32_t r = (uint32_t)(8 * rg + i);
                 if constexpr (ROW) {
@@ -209,25 +223,33 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
     }
 
     if constexpr (COL) {
-        uint32_t slo[4], shi[4], sb[4];
+        uint32_t slo[4], shi[4], sb[4], lim[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a[0][j], a[1][j]), pk_max_u16(a[2][j], a[3][j])),
                                     pk_max_u16(pk_max_u16(a[4][j], a[5][j]), pk_max_u16(a[6][j], a[7][j])));
             m = max16_pk_u16(m);
             m = max32_pk_u16(m);
-            const uint32_t sc = pk_subsat(m, 0x03E103E1u) & 0xFF80FF80u;   // bytes << 7, per half
+            const uint32_t sc = pk_subsat(m, OCP ? 0x04000400u : 0x03E103E1u) & 0xFF80FF80u;
             slo[j] = sc << 16;                                          // column 2j
             shi[j] = sc & 0xFFFF0000u;                                  // column 2j+1
             sb[j] = pk_shr7(sc);                                        // the two bytes
+            if constexpr (OCP)
+                lim[j] = (sc + 0x04000400u) | 0x00600060u;              // 448 * 2^e per column
         }
+        uint32_t vc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                vc[i][j] = OCP ? (v[i][j] & 0x80008000u) | pk_min_u16(a[i][j], lim[j]) : v[i][j];
         // P[p][j] bytes: {col 2j: row 2p, 2p+1 | col 2j+1: row 2p, 2p+1}.
         uint32_t P[4][4];
 #pragma unroll
         for (int p = 0; p < 4; p++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const uint32_t ra = v[2 * p][j], rb = v[2 * p + 1][j];
+                const uint32_t ra = vc[2 * p][j], rb = vc[2 * p + 1][j];
                 P[p][j] = cvt2<true>(cvt2<false>(0u, perm(rb, ra, 0x05040100u), slo[j]),
                                      perm(rb, ra, 0x07060302u), shi[j]);
             }
@@ -293,7 +315,7 @@ __device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, i
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool OCP = false>
 __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict__ rc,
                                           uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
                                           uint8_t *__restrict__ cs, uint16_t *__restrict__ dq)
@@ -338,14 +360,14 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
                                    t.nrows, rg, col_ok);
         else
             load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, true, DQ>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, true, DQ, OCP>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
         if constexpr (GATHER)
             load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
                                     t.nrows, rg, col_ok);
         else
             load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, false, DQ>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, false, DQ, OCP>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
 }
 
@@ -367,6 +389,16 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_row_qdq_kernel(Geometry G,
                                                             uint16_t *__restrict__ dq)
 {
     tile_body<ROW, false, false, WPW, false, true>(G, rc, rs, nullptr, nullptr, dq);
+}
+
+// Both copies under the OCP MX scale rule (comparison variant).
+template <bool ROW, bool COL, int WPW>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_ocp_kernel(Geometry G, uint8_t *__restrict__ rc,
+                                                        uint8_t *__restrict__ rs,
+                                                        uint8_t *__restrict__ cc,
+                                                        uint8_t *__restrict__ cs)
+{
+    tile_body<ROW, COL, false, WPW, false, false, true>(G, rc, rs, cc, cs, nullptr);
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
@@ -483,6 +515,31 @@ hipError_t launch_mxfp8_row_qdq(const uint16_t *x, int64_t rows, int64_t cols, u
     if (waves >= LARGE_LAUNCH_WAVES)
         return launch_qdq_wpw<false, 8>(G, waves, rc, rs, dq, stream);
     return launch_qdq_wpw<false, 4>(G, waves, rc, rs, dq, stream);
+}
+
+template <bool ROW, bool COL>
+static hipError_t launch_ocp(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
+                             uint8_t *cc, uint8_t *cs, hipStream_t stream)
+{
+    const int64_t wgs = (waves + 3) / 4;
+    if (wgs > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mxfp8_ocp_kernel<ROW, COL, 4>), dim3((unsigned)wgs), dim3(256), 0, stream,
+                       G, rc, rs, cc, cs);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
+                                  uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
+{
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0,
+               nullptr, 0};
+    const int64_t waves = (rows + TILE_ROWS - 1) / TILE_ROWS * G.nct;
+    if (rc && cc)
+        return launch_ocp<true, true>(G, waves, rc, rs, cc, cs, stream);
+    if (rc)
+        return launch_ocp<true, false>(G, waves, rc, rs, cc, cs, stream);
+    return launch_ocp<false, true>(G, waves, rc, rs, cc, cs, stream);
 }
 
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,

@@ -55,6 +55,9 @@ def lib():
         "oracle_e4m3_nearest": (ctypes.c_uint8, [ctypes.c_double, ctypes.c_double]),
         "oracle_e2m1_nearest": (ctypes.c_uint8, [ctypes.c_double, ctypes.c_double]),
         "oracle_e8m0_byte": (ctypes.c_int, [ctypes.c_double]),
+        "oracle_e8m0_byte_ocp": (ctypes.c_int, [ctypes.c_double]),
+        "oracle_mxfp8_rowwise_rule": (None, [P, I64, I64, P, P, ctypes.c_int]),
+        "oracle_mxfp8_colwise_rule": (None, [P, I64, I64, P, P, ctypes.c_int]),
         "oracle_nvfp4_scale": (ctypes.c_float, [ctypes.c_double]),
         "oracle_bf16_round_sat": (ctypes.c_uint16, [ctypes.c_double]),
         "oracle_mxfp8_rowwise": (None, [P, I64, I64, P, P]),
@@ -202,6 +205,30 @@ def mxfp8_colwise(x):
     scales = np.empty((rows // 32, cols), np.uint8)
     lib().oracle_mxfp8_colwise(_p(x), rows, cols, _p(codes), _p(scales))
     return codes, scales
+
+
+def e8m0_byte_ocp(amax: float) -> int:
+    return lib().oracle_e8m0_byte_ocp(amax)
+
+
+def mxfp8_ocp_floor(x):
+    """Both MXFP8 copies under the OCP MX scale rule instead of the contract's
+    (a comparison variant; it clips): the shared exponent is floor(log2 amax)
+    - 8, E4M3's largest exponent, and each element is the nearest E4M3 of
+    x / 2^e, saturating at 448 (OCP Microscaling Formats v1.0, the
+    conversion of a block to MX; named as the alternative to P2's rounded-up
+    scale on the page "Miles: end-to-end MXFP8 and per-token NVFP4 RL on
+    Blackwell").  Returns (row codes, row scales, col codes, col scales)."""
+    x = _u16(x)
+    rows, cols = x.shape
+    assert cols % 32 == 0 and rows % 32 == 0
+    rc = np.empty((rows, cols), np.uint8)
+    rs = np.empty((rows, cols // 32), np.uint8)
+    cc = np.empty((rows, cols), np.uint8)
+    cs = np.empty((rows // 32, cols), np.uint8)
+    lib().oracle_mxfp8_rowwise_rule(_p(x), rows, cols, _p(rc), _p(rs), 1)
+    lib().oracle_mxfp8_colwise_rule(_p(x), rows, cols, _p(cc), _p(cs), 1)
+    return rc, rs, cc, cs
 
 
 def mxfp8_colwise_grouped(x, offsets):

@@ -178,6 +178,29 @@ int oracle_e8m0_byte(double A)
     return 254;
 }
 
+/* The OCP MX rule, a variant the library offers for comparison (it can
+ * clip): the shared exponent is floor(log2 A) minus the largest exponent of
+ * the element format (8 for E4M3, whose largest value is 1.75 * 2^8),
+ * clamped to [-127, 127]; A = 0 gives -127.  Stored as e + 127. */
+int oracle_e8m0_byte_ocp(double A)
+{
+    if (A == 0.0)
+        return 0;
+    int ex;
+    frexp(A, &ex);                          /* A = f * 2^ex, f in [.5, 1) */
+    int e = (ex - 1) - 8;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e + 127;
+}
+
+static int scale_byte(double A, int ocp)
+{
+    return ocp ? oracle_e8m0_byte_ocp(A) : oracle_e8m0_byte(A);
+}
+
 /* NVFP4 FP32 scale of a scope whose largest magnitude is A (A is a BF16 value,
  * hence exact in binary32): one IEEE binary32 division. */
 float oracle_nvfp4_scale(double A)
@@ -224,8 +247,8 @@ uint16_t oracle_bf16_round_sat(double y)
 
 /* Rowwise copy: X[rows][cols], cols % 32 == 0.  codes[rows][cols],
  * scales[rows][cols/32]. */
-void oracle_mxfp8_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
-                          uint8_t *codes, uint8_t *scales)
+void oracle_mxfp8_rowwise_rule(const uint16_t *x, int64_t rows, int64_t cols,
+                               uint8_t *codes, uint8_t *scales, int ocp)
 {
     int64_t nb = cols / 32;
 #pragma omp parallel for schedule(static)
@@ -237,7 +260,7 @@ void oracle_mxfp8_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
                 if (a > A)
                     A = a;
             }
-            int byte = oracle_e8m0_byte(A);
+            int byte = scale_byte(A, ocp);
             double D = ldexp(1.0, byte - 127);
             scales[i * nb + j] = (uint8_t)byte;
             for (int64_t k = 0; k < 32; k++) {
@@ -248,11 +271,17 @@ void oracle_mxfp8_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
     }
 }
 
+void oracle_mxfp8_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
+                          uint8_t *codes, uint8_t *scales)
+{
+    oracle_mxfp8_rowwise_rule(x, rows, cols, codes, scales, 0);
+}
+
 /* Columnwise blocks over the rows [r0, r1) of X (r1 - r0 <= 32; a short block
  * takes its largest magnitude over the rows that exist).  Writes codes at the
  * same [row][col] index as X and one scale row scales_row[cols]. */
 static void colwise_block_rows(const uint16_t *x, int64_t cols, int64_t r0,
-                               int64_t r1, uint8_t *codes, uint8_t *scales_row)
+                               int64_t r1, uint8_t *codes, uint8_t *scales_row, int ocp)
 {
     for (int64_t j = 0; j < cols; j++) {
         double A = 0.0;
@@ -261,7 +290,7 @@ static void colwise_block_rows(const uint16_t *x, int64_t cols, int64_t r0,
             if (a > A)
                 A = a;
         }
-        int byte = oracle_e8m0_byte(A);
+        int byte = scale_byte(A, ocp);
         double D = ldexp(1.0, byte - 127);
         scales_row[j] = (uint8_t)byte;
         for (int64_t r = r0; r < r1; r++)
@@ -271,13 +300,19 @@ static void colwise_block_rows(const uint16_t *x, int64_t cols, int64_t r0,
 }
 
 /* Columnwise copy: rows % 32 == 0.  codes[rows][cols], scales[rows/32][cols]. */
-void oracle_mxfp8_colwise(const uint16_t *x, int64_t rows, int64_t cols,
-                          uint8_t *codes, uint8_t *scales)
+void oracle_mxfp8_colwise_rule(const uint16_t *x, int64_t rows, int64_t cols,
+                               uint8_t *codes, uint8_t *scales, int ocp)
 {
     int64_t nt = rows / 32;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < nt; t++)
-        colwise_block_rows(x, cols, 32 * t, 32 * t + 32, codes, scales + t * cols);
+        colwise_block_rows(x, cols, 32 * t, 32 * t + 32, codes, scales + t * cols, ocp);
+}
+
+void oracle_mxfp8_colwise(const uint16_t *x, int64_t rows, int64_t cols,
+                          uint8_t *codes, uint8_t *scales)
+{
+    oracle_mxfp8_colwise_rule(x, rows, cols, codes, scales, 0);
 }
 
 /* Columnwise copy over ragged segments: segment e is rows [off[e], off[e+1]).
@@ -303,7 +338,7 @@ void oracle_mxfp8_colwise_grouped(const uint16_t *x, int64_t cols,
             int64_t r0 = off[e] + 32 * t;
             int64_t r1 = r0 + 32 < off[e + 1] ? r0 + 32 : off[e + 1];
             colwise_block_rows(x, cols, r0, r1, codes,
-                               scales + (scale_offsets[e] + t) * cols);
+                               scales + (scale_offsets[e] + t) * cols, 0);
         }
     }
 }

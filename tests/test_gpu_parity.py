@@ -447,6 +447,51 @@ def test_grouped_config5_full(orc):
 
 
 # ---------------------------------------------------------------------------
+# Comparison variants (not the contract): OCP MX scale rule, per-tensor scope
+# ---------------------------------------------------------------------------
+
+def check_ocp(orc, x: np.ndarray, name: str):
+    announce(f"mxfp8 ocp floor {name} shape={x.shape}")
+    r = api.mxfp8_quantize_ocp_floor(dev(x))
+    torch.cuda.synchronize()
+    rc, rs, cc, cs = orc.mxfp8_ocp_floor(x)
+    assert_same(host(r.row_scales), rs, f"{name} row scales")
+    assert_same(host(r.row_codes), rc, f"{name} row codes")
+    assert_same(host(r.col_scales), cs, f"{name} col scales")
+    assert_same(host(r.col_codes), cc, f"{name} col codes")
+    return rc
+
+
+@pytest.mark.parametrize("mode", W.MXFP8_MODES)
+def test_ocp_floor_config2(orc, mode):
+    """The OCP-rule variant on the 8192 x 2048 weight in every data mode
+    (boundary: the 448 / 450 / power-of-two amaxes where the two rules part;
+    maxes: saturation at the top scale)."""
+    rc = check_ocp(orc, W.config2_weight(mode), f"C2b {mode}")
+    if mode == "random":
+        assert int(((rc & 0x7F) == 0x7E).sum()) > 0      # it clips
+
+
+def test_ocp_floor_shapes_and_exhaustive(orc):
+    for rows, cols in ((32, 32), (64, 96), (96, 288), (32, 4128)):
+        check_ocp(orc, W.mode_boundary(rows, cols, rows + cols), f"boundary {rows}x{cols}")
+    check_ocp(orc, _mxfp8_exhaustive_input(), "exhaustive rows")
+
+
+def test_per_tensor_nvfp4(orc):
+    """Per-tensor activation NVFP4 (one FP32 scale for the tensor) equals the
+    oracle's one-tensor scope."""
+    x = W.config3()[:1024]
+    announce("nvfp4 per-tensor 1024x2048")
+    r = api.nvfp4_quantize_per_tensor(dev(x))
+    torch.cuda.synchronize()
+    c, b, _, _, s = orc.nvfp4_gateup_pair(x[None], None)
+    assert_same(host(r.fp32_scales).view(np.uint32), s.view(np.uint32), "per-tensor scale")
+    assert_same(host(r.codes), c[0], "per-tensor codes")
+    assert_same(host(r.block_scales), b[0], "per-tensor block scales")
+
+
+# ---------------------------------------------------------------------------
 # Block-scaled GEMM on MXFP8 operands
 # ---------------------------------------------------------------------------
 

@@ -711,3 +711,57 @@ def test_nvfp4_gemm_bruteforce_and_dequant_route(orc):
     ya = W.bf16_to_f64(orc.dequant_nvfp4(a, ba, one_a, 1))
     yb = W.bf16_to_f64(orc.dequant_nvfp4(b, bb, one_b, 1))
     assert np.array_equal(C1, ya @ yb.T)
+
+
+# ---------------------------------------------------------------------------
+# Comparison variants: OCP MX scale rule, per-tensor activation scope
+# ---------------------------------------------------------------------------
+
+def test_ocp_rule_closed_form_and_relation(orc):
+    """Every non-negative finite BF16 amax: the OCP byte is max(0, E - 8) on
+    the BF16 exponent field E (0 for zero and subnormals), computed here from
+    the bit fields; the contract's byte exceeds it by exactly 1 when the
+    mantissa is above 1.75 (and E >= 8), else equals it."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    A = W.bf16_to_f64(bits.astype(np.uint16))
+    E, m = bits >> 7, bits & 0x7F
+    want = np.where(E == 0, 0, np.maximum(0, E.astype(np.int64) - 8))
+    got = np.array([orc.e8m0_byte_ocp(float(a)) for a in A])
+    assert np.array_equal(got, want)
+    contract = orc.e8m0_byte_many(A).astype(np.int64)
+    assert np.array_equal(contract - got, ((m > 96) & (E >= 8)).astype(np.int64))
+
+
+def test_ocp_variant_codes_and_clipping(orc):
+    """OCP-rule codes equal torch's E4M3 conversion of x / 2^e clamped to
+    +-448 (exact scaling, nearest-even in range); clipping happens exactly
+    where |x| / 2^e > 448, which the contract's rule never allows."""
+    x = W.config2_activation("random")[:256]
+    rc, rs, cc, cs = orc.mxfp8_ocp_floor(x)
+    xv = W.bf16_to_f64(x)
+    for codes, scales, axis in ((rc, rs, 1), (cc, cs, 0)):
+        e = np.repeat(scales.astype(np.int64) - 127, 32, axis=axis)
+        q = xv / np.ldexp(1.0, e)
+        want = torch.from_numpy(np.clip(q, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(codes, want.numpy())
+        clipped = np.abs(q) > 448
+        assert clipped.sum() > 0 and np.all((codes[clipped] & 0x7F) == 0x7E)
+    c2, s2 = orc.mxfp8_rowwise(x)
+    e2 = np.repeat(s2.astype(np.int64) - 127, 32, axis=1)
+    assert not np.any(np.abs(xv / np.ldexp(1.0, e2)) > 448)
+
+
+def test_per_tensor_scope_is_batch_dependent(orc):
+    """The per-tensor activation scope (one FP32 scale for the whole tensor,
+    here the one-tensor weight scope) changes a row's bytes when other rows
+    of the batch change; the per-token scope does not (the batch-invariance
+    paragraph's reason for per-token scales)."""
+    x = W.config3()[:64]
+    y = x.copy()
+    y[5] = W.bf16_bits(W.bf16_to_f64(y[5]) * 8.0)       # a louder token elsewhere in the batch
+    px = orc.nvfp4_gateup_pair(x[None], None)
+    py = orc.nvfp4_gateup_pair(y[None], None)
+    assert px[4][0] != py[4][0]
+    assert not np.array_equal(px[0][0][0], py[0][0][0])  # row 0 quantized differently
+    tx, ty = orc.nvfp4_per_token(x), orc.nvfp4_per_token(y)
+    assert np.array_equal(tx[0][0], ty[0][0]) and tx[2][0] == ty[2][0]
