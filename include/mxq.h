@@ -135,6 +135,20 @@ int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *col_scales, void *stream);
 
 /*
+ * Layout variant: both MXFP8 copies from one read, the columnwise one stored
+ * transposed, codes [cols][rows] and scales [cols][rows/32] (the same bytes as
+ * mxq_mxfp8_quantize_rowcol's columnwise copy, permuted).  Each 32x1 block
+ * then lies along a row, so a GEMM contracting over the rows (the weight
+ * gradient of the MXFP8 recipe's backward) reads it K-contiguous, as
+ * mxq_mxfp8_gemm requires.
+ *   col_codes_t, col_scales_t required (16-byte aligned codes); row_codes and
+ *   row_scales both or neither; rows % 32 == 0, cols % 32 == 0, rows < 2^31.
+ */
+int mxq_mxfp8_quantize_rowcol_t(const uint16_t *x, int64_t rows, int64_t cols,
+                                uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes_t,
+                                uint8_t *col_scales_t, void *stream);
+
+/*
  * NVFP4 quantize with one online FP32 scale per token (row), in one call that
  * returns the packed codes, the E4M3 block scales and the per-token scales.
  * Implements the NVFP4 format paragraph (E2M1 codes, one E4M3 scale per 16

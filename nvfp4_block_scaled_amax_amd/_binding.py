@@ -44,6 +44,7 @@ EXPORTS = (
     "mxq_mxfp8_gemm",
     "mxq_nvfp4_gemm",
     "mxq_mxfp8_quantize_ocp_floor",
+    "mxq_mxfp8_quantize_rowcol_t",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
@@ -86,6 +87,7 @@ def lib():
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_quantize_ocp_floor": [P, I64, I64, P, P, P, P, P],
+        "mxq_mxfp8_quantize_rowcol_t": [P, I64, I64, P, P, P, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
@@ -146,6 +148,14 @@ def mxq_mxfp8_quantize_ocp_floor(x, rows, cols, row_codes, row_scales, col_codes
                                               _ptr(row_scales), _ptr(col_codes),
                                               _ptr(col_scales), _stream(stream)),
            "mxq_mxfp8_quantize_ocp_floor")
+
+
+def mxq_mxfp8_quantize_rowcol_t(x, rows, cols, row_codes, row_scales, col_codes_t, col_scales_t,
+                                stream=None):
+    _check(lib().mxq_mxfp8_quantize_rowcol_t(_ptr(x), rows, cols, _ptr(row_codes),
+                                             _ptr(row_scales), _ptr(col_codes_t),
+                                             _ptr(col_scales_t), _stream(stream)),
+           "mxq_mxfp8_quantize_rowcol_t")
 
 
 def mxq_nvfp4_quantize_per_token(x, rows, cols, codes, block_scales, token_scales, stream=None):

@@ -42,6 +42,20 @@ def mxfp8_quantize_rowcol(x, rowwise: bool = True, colwise: bool = True,
     return MXFP8RowCol(rc, rs, cc, cs)
 
 
+def mxfp8_quantize_rowcol_t(x, rowwise: bool = True, stream=None) -> MXFP8RowCol:
+    """Both MXFP8 copies, the columnwise one transposed: col_codes [cols][rows],
+    col_scales [cols][rows/32] (K-contiguous for a GEMM contracting over rows)."""
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    u8 = torch.uint8
+    rc = _empty((rows, cols), u8, x) if rowwise else None
+    rs = _empty((rows, cols // 32), u8, x) if rowwise else None
+    cc = _empty((cols, rows), u8, x)
+    cs = _empty((cols, rows // 32), u8, x)
+    B.mxq_mxfp8_quantize_rowcol_t(x, rows, cols, rc, rs, cc, cs, stream)
+    return MXFP8RowCol(rc, rs, cc, cs)
+
+
 def mxfp8_quantize_ocp_floor(x, rowwise: bool = True, colwise: bool = True,
                              stream=None) -> MXFP8RowCol:
     """Comparison variant: both MXFP8 copies under the OCP MX scale rule

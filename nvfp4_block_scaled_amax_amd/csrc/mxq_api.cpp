@@ -181,6 +181,35 @@ int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
                                                 col_scales, (hipStream_t)stream));
 }
 
+int mxq_mxfp8_quantize_rowcol_t(const uint16_t *x, int64_t rows, int64_t cols,
+                                uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes_t,
+                                uint8_t *col_scales_t, void *stream)
+{
+    if (!x || !col_codes_t || !col_scales_t)
+        return MXQ_ERR_NULL;
+    if ((row_codes == nullptr) != (row_scales == nullptr))
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS || rows > MAX_GRID_ROWS)
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0 || rows % 32 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    Buf b[5];
+    int k = 0;
+    b[k++] = {x, 2 * n, 16, false};
+    b[k++] = {col_codes_t, n, 16, true};
+    b[k++] = {col_scales_t, n / 32, 1, true};
+    if (row_codes) {
+        b[k++] = {row_codes, n, 16, true};
+        b[k++] = {row_scales, n / 32, 1, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_colt(x, rows, cols, row_codes, row_scales, col_codes_t,
+                                           col_scales_t, (hipStream_t)stream));
+}
+
 int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                  uint8_t *block_scales, float *token_scales, void *stream)
 {

@@ -35,6 +35,12 @@ hipError_t launch_mxfp8_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
                                   uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes,
                                   uint8_t *col_scales, hipStream_t stream);
 
+// Both MXFP8 copies with the columnwise one transposed: codes [cols][rows],
+// scales [cols][rows/32] (rows % 32 == 0); row_codes/row_scales may be null.
+hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,
+                             uint8_t *row_scales, uint8_t *col_codes_t, uint8_t *col_scales_t,
+                             hipStream_t stream);
+
 // Rowwise MXFP8 and its BF16 dequantization in one pass; rc/rs may be null
 // (only the dequantized copy is stored).
 hipError_t launch_mxfp8_row_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *row_codes,

@@ -145,6 +145,7 @@ __device__ __forceinline__ void load_tile_gather(uint32_t (&v)[8][4],
 struct TileOut {
     uint8_t *rc, *rs, *cc, *cs;     // row codes, row scales, col codes, col scales
     uint16_t *dq;                   // dequantized rowwise copy (BF16), DQ kernels
+    uint32_t ld_t, lds_t;           // transposed columnwise copy: row pitch of codes, scales
 };
 
 // Eight BF16 of one row's 8 rowwise codes (w0: columns 0..3, w1: 4..7) under
@@ -175,7 +176,12 @@ __device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t sca
 // saturate (it gives NaN from 464 up), so magnitudes are first clamped to
 // 448 * 2^e, whose BF16 bits are ((byte + 8) << 7) | 0x60; the nearest E4M3
 // of anything at or above that is 448.
-template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false>
+// COLT: the columnwise copy transposed (a layout variant): codes [cols][rows]
+// and scales [cols][rows/32]; o.cc / o.cs then point at column tcol's row
+// row0 (codes) and its scale for this 32-row block, with row pitches ld_t
+// (= rows) and lds_t (= rows / 32).  Each lane writes, per column, its 8 rows
+// as 8 contiguous bytes.
+template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false, bool COLT = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -253,19 +259,37 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
                 P[p][j] = cvt2<true>(cvt2<false>(0u, perm(rb, ra, 0x05040100u), slo[j]),
                                      perm(rb, ra, 0x07060302u), shi[j]);
             }
+        if constexpr (!COLT) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int p = i >> 1;
-            const uint32_t sel = (i & 1) ? 0x07050301u : 0x06040200u;
-            const uint32_t w0 = perm(P[p][1], P[p][0], sel);
-            const uint32_t w1 = perm(P[p][3], P[p][2], sel);
-            if (FULL || (col_ok && i < nr))
-                st_nt8(o.cc + ((uint32_t)(8 * rg + i) * cols + c8), w0, w1);
-        }
-        if ((FULL || col_ok) && rg == 0) {
-            const uint32_t s0 = perm(sb[1], sb[0], 0x06040200u);     // columns 0..3
-            const uint32_t s1 = perm(sb[3], sb[2], 0x06040200u);     // columns 4..7
-            st_nt8(o.cs + c8, s0, s1);
+            for (int i = 0; i < 8; i++) {
+                const int p = i >> 1;
+                const uint32_t sel = (i & 1) ? 0x07050301u : 0x06040200u;
+                const uint32_t w0 = perm(P[p][1], P[p][0], sel);
+                const uint32_t w1 = perm(P[p][3], P[p][2], sel);
+                if (FULL || (col_ok && i < nr))
+                    st_nt8(o.cc + ((uint32_t)(8 * rg + i) * cols + c8), w0, w1);
+            }
+            if ((FULL || col_ok) && rg == 0) {
+                const uint32_t s0 = perm(sb[1], sb[0], 0x06040200u);     // columns 0..3
+                const uint32_t s1 = perm(sb[3], sb[2], 0x06040200u);     // columns 4..7
+                st_nt8(o.cs + c8, s0, s1);
+            }
+        } else if (FULL || col_ok) {
+            // Column 2j: rows 0..3 are bytes 0, 1 of P[0][j], P[1][j]; rows
+            // 4..7 those of P[2][j], P[3][j].  Column 2j+1: bytes 2, 3.
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+#pragma unroll
+                for (int e = 0; e < 2; e++) {
+                    const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = perm(P[1][j], P[0][j], sel);
+                    const uint32_t hi = perm(P[3][j], P[2][j], sel);
+                    const uint32_t c = c8 + 2 * j + e;
+                    st_nt8(o.cc + (c * o.ld_t + 8 * rg), lo, hi);
+                    if (rg == 0)
+                        o.cs[c * o.lds_t] = (uint8_t)(sb[j] >> (16 * e));
+                }
+            }
         }
     }
 }
@@ -315,7 +339,8 @@ __device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, i
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool OCP = false>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool OCP = false,
+          bool COLT = false>
 __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict__ rc,
                                           uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
                                           uint8_t *__restrict__ cs, uint16_t *__restrict__ dq)
@@ -351,8 +376,14 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
     const bool full = tcol + TILE_COLS <= G.cols && t.nrows == TILE_ROWS;
     const int64_t base = t.row0 * G.cols + tcol;
     const uint16_t *xt = G.x + base;
-    const TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol,
-                    DQ ? dq + base : nullptr};
+    TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol,
+              DQ ? dq + base : nullptr, 0, 0};
+    if constexpr (COLT) {
+        o.ld_t = (uint32_t)G.rows;
+        o.lds_t = (uint32_t)(G.rows >> 5);
+        o.cc = cc + tcol * G.rows + t.row0;
+        o.cs = cs + tcol * (G.rows >> 5) + t.srow;
+    }
     uint32_t v[8][4];
     if (full) {
         if constexpr (GATHER)
@@ -360,14 +391,14 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
                                    t.nrows, rg, col_ok);
         else
             load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, true, DQ, OCP>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, true, DQ, OCP, COLT>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
         if constexpr (GATHER)
             load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
                                     t.nrows, rg, col_ok);
         else
             load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, false, DQ, OCP>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, false, DQ, OCP, COLT>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
 }
 
@@ -399,6 +430,16 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_ocp_kernel(Geometry G, uint8_t
                                                         uint8_t *__restrict__ cs)
 {
     tile_body<ROW, COL, false, WPW, false, false, true>(G, rc, rs, cc, cs, nullptr);
+}
+
+// Both copies, the columnwise one transposed (layout variant).
+template <bool ROW, int WPW>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_t *__restrict__ rc,
+                                                         uint8_t *__restrict__ rs,
+                                                         uint8_t *__restrict__ cct,
+                                                         uint8_t *__restrict__ cst)
+{
+    tile_body<ROW, true, false, WPW, false, false, false, true>(G, rc, rs, cct, cst, nullptr);
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
@@ -540,6 +581,24 @@ hipError_t launch_mxfp8_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
     if (rc)
         return launch_ocp<true, false>(G, waves, rc, rs, cc, cs, stream);
     return launch_ocp<false, true>(G, waves, rc, rs, cc, cs, stream);
+}
+
+hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
+                             uint8_t *rs, uint8_t *cct, uint8_t *cst, hipStream_t stream)
+{
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0,
+               nullptr, 0};
+    const int64_t waves = rows / TILE_ROWS * G.nct;         // rows % 32 == 0: checked by the caller
+    const int64_t wgs = (waves + 3) / 4;
+    if (wgs > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    if (rc)
+        hipLaunchKernelGGL((mxfp8_colt_kernel<true, 4>), dim3((unsigned)wgs), dim3(256), 0,
+                           stream, G, rc, rs, cct, cst);
+    else
+        hipLaunchKernelGGL((mxfp8_colt_kernel<false, 4>), dim3((unsigned)wgs), dim3(256), 0,
+                           stream, G, rc, rs, cct, cst);
+    return hipGetLastError();
 }
 
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,

@@ -128,6 +128,12 @@ def test_validation_before_any_device_call():
     assert status_of(oq, A, 48, 32, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
     assert status_of(oq, A + 2, 32, 32, A, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
 
+    ct = mxq.mxq_mxfp8_quantize_rowcol_t
+    assert status_of(ct, A, 32, 32, A, A, None, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(ct, A, 32, 32, A, None, A, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(ct, A, 48, 32, None, None, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(ct, A, 32, 32, None, None, A + 8, A, 0) == mxq.MXQ_ERR_ALIGN
+
     gd = mxq.mxq_grouped_quantize_dispatch
     nv = {"codes": A, "block_scales": A, "token_scales": A}
     F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL

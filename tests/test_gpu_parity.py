@@ -478,6 +478,47 @@ def test_ocp_floor_shapes_and_exhaustive(orc):
     check_ocp(orc, _mxfp8_exhaustive_input(), "exhaustive rows")
 
 
+def check_colt(orc, x: np.ndarray, name: str):
+    announce(f"mxfp8 transposed columnwise {name} shape={x.shape}")
+    r = api.mxfp8_quantize_rowcol_t(dev(x))
+    torch.cuda.synchronize()
+    cc, cs = orc.mxfp8_colwise(x)
+    rc, rs = orc.mxfp8_rowwise(x)
+    assert_same(host(r.col_codes), np.ascontiguousarray(cc.T), f"{name} col codes (transposed)")
+    assert_same(host(r.col_scales), np.ascontiguousarray(cs.T), f"{name} col scales (transposed)")
+    assert_same(host(r.row_codes), rc, f"{name} row codes")
+    assert_same(host(r.row_scales), rs, f"{name} row scales")
+
+
+def test_colwise_transposed_layout(orc):
+    """The transposed columnwise layout holds exactly the columnwise bytes,
+    permuted; partial column strips included."""
+    for mode in ("random", "boundary"):
+        check_colt(orc, W.config2_weight(mode), f"C2b {mode}")
+    for rows, cols in ((32, 32), (64, 96), (96, 288), (32, 4128)):
+        check_colt(orc, W.mode_boundary(rows, cols, rows + 3 * cols), f"boundary {rows}x{cols}")
+
+
+def test_gemm_weight_gradient_from_transposed_copies(orc):
+    """dW[N][K] = dY^T X over the M rows: both operands' columnwise copies,
+    transposed, are K-contiguous operands of the same GEMM kernel."""
+    M, N, K = 512, 256, 384
+    dy = W.student_t_activations(M, N, 91)
+    x = W.mode_random(M, K, 92)
+    announce(f"mxfp8 wgrad {N}x{K} over M={M}")
+    qd = api.mxfp8_quantize_rowcol_t(dev(dy), rowwise=False)
+    qx = api.mxfp8_quantize_rowcol_t(dev(x), rowwise=False)
+    c = api.mxfp8_gemm(qd.col_codes, qd.col_scales, qx.col_codes, qx.col_scales,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    dc, ds = orc.mxfp8_colwise(dy)
+    xc, xs = orc.mxfp8_colwise(x)
+    C, S = orc.mxfp8_gemm(np.ascontiguousarray(dc.T), np.ascontiguousarray(ds.T),
+                          np.ascontiguousarray(xc.T), np.ascontiguousarray(xs.T))
+    err = np.abs(host(c).astype(np.float64) - C)
+    assert np.all(err <= (GEMM_REL + M * 2.0 ** -24) * S)
+
+
 def test_per_tensor_nvfp4(orc):
     """Per-tensor activation NVFP4 (one FP32 scale for the tensor) equals the
     oracle's one-tensor scope."""
