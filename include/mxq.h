@@ -167,6 +167,20 @@ int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
                                  float *token_scales, void *stream);
 
 /*
+ * Opt-in approximate variant, not the contract (the exactness paragraph makes
+ * approximation opt-in): per-token NVFP4 as mxq_nvfp4_quantize_per_token, but
+ * the block scale and each code come from one conversion of a
+ * reciprocal-multiply, with no exactness fix-up.  The FP32 token scale is
+ * exact.  A block scale or code can differ from the exact one only where the
+ * exact quotient lies within about 2^-21 (relative) of a rounding midpoint,
+ * and then it is the other neighbour.  cols <= 4096 (MXQ_ERR_SIZE); other
+ * arguments and errors as mxq_nvfp4_quantize_per_token.
+ */
+int mxq_nvfp4_quantize_per_token_approx(const uint16_t *x, int64_t rows, int64_t cols,
+                                        uint8_t *codes, uint8_t *block_scales,
+                                        float *token_scales, void *stream);
+
+/*
  * NVFP4 weight export with one FP32 scale per scope.  Implements the gate/up
  * pairing paragraph: a SwiGLU expert's gate and up projections are quantized
  * together under one shared FP32 scale (the scope is gate[e] together with

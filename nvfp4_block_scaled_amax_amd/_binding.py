@@ -45,6 +45,7 @@ EXPORTS = (
     "mxq_nvfp4_gemm",
     "mxq_mxfp8_quantize_ocp_floor",
     "mxq_mxfp8_quantize_rowcol_t",
+    "mxq_nvfp4_quantize_per_token_approx",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
     "mxq_status_string",
@@ -88,6 +89,7 @@ def lib():
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_quantize_ocp_floor": [P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_quantize_rowcol_t": [P, I64, I64, P, P, P, P, P],
+        "mxq_nvfp4_quantize_per_token_approx": [P, I64, I64, P, P, P, P],
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
@@ -163,6 +165,14 @@ def mxq_nvfp4_quantize_per_token(x, rows, cols, codes, block_scales, token_scale
                                               _ptr(block_scales), _ptr(token_scales),
                                               _stream(stream)),
            "mxq_nvfp4_quantize_per_token")
+
+
+def mxq_nvfp4_quantize_per_token_approx(x, rows, cols, codes, block_scales, token_scales,
+                                        stream=None):
+    _check(lib().mxq_nvfp4_quantize_per_token_approx(_ptr(x), rows, cols, _ptr(codes),
+                                                     _ptr(block_scales), _ptr(token_scales),
+                                                     _stream(stream)),
+           "mxq_nvfp4_quantize_per_token_approx")
 
 
 def mxq_nvfp4_quantize_gateup_pair(gate, up, n_experts, rows, cols, gate_codes,

@@ -87,6 +87,18 @@ def nvfp4_quantize_per_token(x, stream=None) -> NVFP4:
     return NVFP4(codes, bs, ts)
 
 
+def nvfp4_quantize_per_token_approx(x, stream=None) -> NVFP4:
+    """Opt-in approximate per-token NVFP4 (not the contract): one
+    reciprocal-multiply and one conversion per block scale and per code."""
+    x = _bf16_bits(x)
+    rows, cols = x.shape
+    codes = _empty((rows, cols // 2), torch.uint8, x)
+    bs = _empty((rows, cols // 16), torch.uint8, x)
+    ts = _empty((rows,), torch.float32, x)
+    B.mxq_nvfp4_quantize_per_token_approx(x, rows, cols, codes, bs, ts, stream)
+    return NVFP4(codes, bs, ts)
+
+
 def nvfp4_quantize_per_tensor(x, stream=None) -> NVFP4:
     """Comparison variant: NVFP4 of an activation tensor with ONE FP32 scale
     for the whole tensor (the batch-dependent scope the per-token recipe

@@ -231,6 +231,28 @@ int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols, 
                                                 (hipStream_t)stream));
 }
 
+int mxq_nvfp4_quantize_per_token_approx(const uint16_t *x, int64_t rows, int64_t cols,
+                                        uint8_t *codes, uint8_t *block_scales,
+                                        float *token_scales, void *stream)
+{
+    if (!x || !codes || !block_scales || !token_scales)
+        return MXQ_ERR_NULL;
+    if (!size_ok(rows, cols) || rows > MAX_GRID_ROWS || cols > 4096)
+        return MXQ_ERR_SIZE;
+    if (cols % 16 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    const Buf b[4] = {{x, 2 * n, 16, false},
+                      {codes, n / 2, 16, true},
+                      {block_scales, n / 16, 1, true},
+                      {token_scales, 4 * rows, 4, true}};
+    const int st = check_bufs(b, 4);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_approx(x, rows, cols, codes, block_scales, token_scales,
+                                             (hipStream_t)stream));
+}
+
 int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
                                    int64_t rows, int64_t cols, uint8_t *gate_codes,
                                    uint8_t *gate_block_scales, uint8_t *up_codes,

@@ -52,6 +52,11 @@ hipError_t launch_nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8
                             uint8_t *block_scales, float *token_scales, uint16_t *dq,
                             hipStream_t stream);
 
+// Approximate per-token NVFP4 (opt-in variant, cols <= 4096): one
+// reciprocal-multiply and one conversion per block scale and per code.
+hipError_t launch_nvfp4_approx(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                               uint8_t *block_scales, float *token_scales, hipStream_t stream);
+
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *block_scales, float *token_scales, hipStream_t stream);
 

@@ -201,11 +201,27 @@ __device__ __attribute__((noinline)) BlkOut quant_blk_f64(uint32_t w0, uint32_t 
     return o;
 }
 
-// Quantize one block under scale k (any path).
+// Quantize one block under scale k (any path).  APPROX (an opt-in variant,
+// not the contract): the block scale and the codes each from one conversion
+// of a reciprocal-multiply (v_rcp_f32, about 1 ulp) with no exactness
+// fix-up, so a quotient within about 2^-21 of a rounding midpoint may take
+// the other neighbour; the FP32 scale and the tiny-scale binary64 path are
+// unchanged.
+template <bool APPROX = false>
 __device__ __forceinline__ BlkOut quant_blk(const Blk &blk, const BlkF &f, const ScaleK &k)
 {
     BlkOut o;
-    if (k.s >= S_FAST_MIN) {
+    if (APPROX && k.s >= S_FAST_MIN) {
+        const float A = u2f(f.amax);
+        const float r6 = k.inv_s * ONE_SIXTH;
+        o.b = e4m3_pair_rne(fminf(A * r6, 448.0f), 0.0f) & 0xFFu;
+        o.c0 = o.c1 = 0u;
+        if (o.b != 0) {
+            const float r = __builtin_amdgcn_rcpf(e4m3_value(o.b)) * k.inv_s;
+            o.c0 = codes8(f.x, r);
+            o.c1 = codes8(f.x + 8, r);
+        }
+    } else if (k.s >= S_FAST_MIN) {
         const float A = u2f(f.amax);
         const uint32_t bb = e4m3_pair_rne(fminf(A * k.r6_lo, 448.0f), fminf(A * k.r6_hi, 448.0f));
         o.b = bb & 0xFFu;
@@ -311,7 +327,7 @@ __device__ __forceinline__ int64_t lane_i64(int64_t v, int c)
 // occupancy choice (a partial row of 65..127 blocks spilled at 64).
 // DQ: also the dequantized row (dst.dq); codes/bs and ts may then be null
 // (not stored).
-template <int NB, bool FULL, bool SCATTER, bool DQ>
+template <int NB, bool FULL, bool SCATTER, bool DQ, bool APPROX = false>
 __device__ __forceinline__ void token_body(const uint16_t *__restrict__ x, int64_t rows,
                                            int64_t cols, uint8_t *__restrict__ codes,
                                            uint8_t *__restrict__ bs, float *__restrict__ ts,
@@ -363,7 +379,7 @@ __device__ __forceinline__ void token_body(const uint16_t *__restrict__ x, int64
         for (int k = 0; k < NB; k++) {
             const int j = lane + 64 * k;
             if (FULL || j < nblk) {
-                const BlkOut o = quant_blk(r[k], f[k], sk);
+                const BlkOut o = quant_blk<APPROX>(r[k], f[k], sk);
                 if (!DQ || codes)
                     emit_blk(o, j, crow, brow);
                 if constexpr (DQ)
@@ -415,6 +431,16 @@ nvfp4_token_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
                    float *__restrict__ ts, Dest dst)
 {
     token_body<NB, FULL, SCATTER, false>(x, rows, cols, codes, bs, ts, dst);
+}
+
+template <int NB, bool FULL>
+__global__ void __launch_bounds__(WG_THREADS)
+__attribute__((amdgpu_waves_per_eu(NB == 1 || (NB == 2 && FULL) ? 8 : 1, 8)))
+nvfp4_token_approx_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                          uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
+                          float *__restrict__ ts, Dest dst)
+{
+    token_body<NB, FULL, false, false, true>(x, rows, cols, codes, bs, ts, dst);
 }
 
 template <int NB, bool FULL>
@@ -629,6 +655,35 @@ hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols,
 {
     return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, nullptr},
                               stream);
+}
+
+template <int NB, bool FULL>
+static void launch_approx(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                          uint8_t *bs, float *ts, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)), block(WG_THREADS);
+    hipLaunchKernelGGL((nvfp4_token_approx_kernel<NB, FULL>), grid, block, 0, stream, x, rows,
+                       cols, codes, bs, ts, Dest{nullptr, 1, rows, nullptr});
+}
+
+hipError_t launch_nvfp4_approx(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                               uint8_t *bs, float *ts, hipStream_t stream)
+{
+    // cols <= 4096 (checked by the caller): rows held in registers.
+    const int64_t nblk = cols >> 4;
+    const int64_t nb = (nblk + 63) / 64;
+    const bool full = nblk == 64 * nb;
+    switch (nb) {
+    case 1: full ? launch_approx<1, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_approx<1, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 2: full ? launch_approx<2, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_approx<2, false>(x, rows, cols, codes, bs, ts, stream); break;
+    case 3: full ? launch_approx<3, true>(x, rows, cols, codes, bs, ts, stream)
+                 : launch_approx<3, false>(x, rows, cols, codes, bs, ts, stream); break;
+    default: full ? launch_approx<4, true>(x, rows, cols, codes, bs, ts, stream)
+                  : launch_approx<4, false>(x, rows, cols, codes, bs, ts, stream);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,

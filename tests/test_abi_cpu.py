@@ -134,6 +134,11 @@ def test_validation_before_any_device_call():
     assert status_of(ct, A, 48, 32, None, None, A, A, 0) == mxq.MXQ_ERR_SHAPE
     assert status_of(ct, A, 32, 32, None, None, A + 8, A, 0) == mxq.MXQ_ERR_ALIGN
 
+    ap = mxq.mxq_nvfp4_quantize_per_token_approx
+    assert status_of(ap, A, 4, 16, A, A, None, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(ap, A, 4, 8192, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(ap, A, 4, 24, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+
     gd = mxq.mxq_grouped_quantize_dispatch
     nv = {"codes": A, "block_scales": A, "token_scales": A}
     F4, F8 = mxq.MXQ_FMT_NVFP4, mxq.MXQ_FMT_MXFP8_ROWCOL

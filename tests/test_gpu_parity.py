@@ -519,6 +519,43 @@ def test_gemm_weight_gradient_from_transposed_copies(orc):
     assert np.all(err <= (GEMM_REL + M * 2.0 ** -24) * S)
 
 
+def test_nvfp4_approx_differs_only_at_midpoints(orc):
+    """The opt-in approximate variant: the FP32 token scales are exact; a block
+    scale differs from the exact one only where amax / (6 s) lies within
+    2^-19 (relative) of the E4M3 midpoint between the two; inside blocks with
+    the exact scale, a code differs only where |x| / (dec(b) s) lies within
+    2^-19 of the E2M1 midpoint between it and the exact code.  Student-t
+    tokens plus rows whose scales span the range."""
+    x = np.concatenate([W.config3()[:4096], _wide_range_rows(256, 2048, 9)])
+    announce(f"nvfp4 approx {x.shape}")
+    r = api.nvfp4_quantize_per_token_approx(dev(x))
+    torch.cuda.synchronize()
+    c, b, s = orc.nvfp4_per_token(x)
+    ac, ab, as_ = host(r.codes), host(r.block_scales), host(r.fp32_scales)
+    assert_same(as_.view(np.uint32), s.view(np.uint32), "token scales")
+    e4 = np.array([orc.e4m3_value(i) for i in range(256)])
+    e2 = np.array([orc.e2m1_value(i) for i in range(16)])
+    xv = np.abs(W.bf16_to_f64(x))
+    S = s.astype(np.float64)[:, None]
+    amax = xv.reshape(x.shape[0], -1, 16).max(axis=2)
+    bad_b = np.argwhere(ab != b)
+    for i, j in bad_b:
+        mid = (e4[b[i, j]] + e4[ab[i, j]]) / 2
+        assert abs(amax[i, j] / (6 * S[i, 0]) - mid) <= 2.0 ** -19 * mid, (i, j)
+    nib = lambda q: np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], -1)
+    ce, ca = nib(c), nib(ac)
+    same_b = np.repeat(ab == b, 16, axis=1)
+    diff = np.argwhere((ce != ca) & same_b)
+    q = xv / (np.repeat(e4[b], 16, axis=1) * S)
+    for i, k in diff:
+        ke, ka = int(ce[i, k]), int(ca[i, k])
+        assert (ke & 8) == (ka & 8) and abs((ke & 7) - (ka & 7)) == 1, (i, k)
+        mid = (e2[ke & 7] + e2[ka & 7]) / 2
+        assert abs(q[i, k] - mid) <= 2.0 ** -19 * mid, (i, k)
+    announce(f"  approx: {len(bad_b)} block scales and {len(diff)} codes differ "
+             f"of {b.size} and {ce.size}")
+
+
 def test_per_tensor_nvfp4(orc):
     """Per-tensor activation NVFP4 (one FP32 scale for the tensor) equals the
     oracle's one-tensor scope."""
