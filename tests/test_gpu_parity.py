@@ -971,6 +971,52 @@ def test_errors_other_entry_points():
     assert ei.value.status == mxq.MXQ_ERR_ALIAS
 
 
+def test_errors_newer_entry_points_write_nothing():
+    """The fused, one-pass, variant and GEMM entry points reject aliasing,
+    host memory and bad enums before any launch: their canary-filled outputs
+    stay untouched."""
+    x = dev(W.config1())                                    # 256 x 512 BF16
+    rows, cols = 256, 512
+    host_buf = np.zeros(rows * cols * 2, np.uint8)
+    canary = lambda *shape, dt=torch.uint8: torch.full(shape, 0x5A if dt == torch.uint8 else 7,
+                                                       dtype=dt, device="cuda")
+    c8, s8 = canary(rows, cols), canary(rows, cols // 32)
+    c4, b4, t4 = canary(rows, cols // 2), canary(rows, cols // 16), canary(rows, dt=torch.float32)
+    y = canary(rows, cols, dt=torch.int16)
+    g = canary(rows, rows, dt=torch.float32)
+    announce("error paths: newer entry points")
+    cases = [
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_quantize_dequant_bf16(
+            mxq.MXQ_FMT_NVFP4, x, rows, cols, c4, b4, t4, x)),
+        (mxq.MXQ_ERR_DEVICE, lambda: mxq.mxq_quantize_dequant_bf16(
+            mxq.MXQ_FMT_MXFP8_ROW, x, rows, cols, c8, s8, None, host_buf.ctypes.data)),
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_mxfp8_quantize_ocp_floor(
+            x, rows, cols, c8, s8, c8, s8)),
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_mxfp8_quantize_rowcol_t(
+            x, rows, cols, c8, s8, c8, s8)),
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_nvfp4_quantize_per_token_approx(
+            x, rows, cols, c4, c4, t4)),
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_mxfp8_gemm(
+            c8, s8, c8, s8, rows, rows, cols, mxq.MXQ_OUT_BF16, c8)),
+        (mxq.MXQ_ERR_ARG, lambda: mxq.mxq_nvfp4_gemm(
+            c4, b4, t4, 1, c4, b4, t4, rows, rows, rows, cols, 9, g)),
+        (mxq.MXQ_ERR_DEVICE, lambda: mxq.mxq_nvfp4_gemm(
+            c4, b4, t4, 1, host_buf.ctypes.data, b4, t4, rows, rows, rows, cols,
+            mxq.MXQ_OUT_F32, g)),
+        (mxq.MXQ_ERR_ALIAS, lambda: mxq.mxq_grouped_quantize_dispatch(
+            mxq.MXQ_FMT_NVFP4, x, rows, cols, 1, c4, None, rows, None, 0,
+            {"codes": c4, "block_scales": b4, "token_scales": t4})),
+    ]
+    for status, call in cases:
+        with pytest.raises(mxq.MXQError) as ei:
+            call()
+        assert ei.value.status == status, (status, ei.value)
+    torch.cuda.synchronize()
+    for t, fill in ((c8, 0x5A), (s8, 0x5A), (c4, 0x5A), (b4, 0x5A), (y, 7)):
+        assert bool((t == fill).all())
+    assert bool((t4 == 7).all()) and bool((g == 7).all())
+
+
 def test_grouped_malformed_offsets_stay_in_bounds():
     """Offsets are device data the host cannot validate: non-monotone or
     out-of-range offsets must not move any access out of bounds (the call
