@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "mxfp8_tile_kernel": ["mxq_mxfp8.hip"],
     "grouped_prefix_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_token_kernel": ["mxq_nvfp4.hip"],
+    "nvfp4_token_split_kernel": ["mxq_nvfp4.hip"],
     "nvfp4_scoped_kernel": ["mxq_nvfp4.hip"],
     "dequant_mxfp8_kernel": ["mxq_dequant.hip"],
     "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
@@ -139,7 +140,7 @@ def build_tok(torch, E, W, legs, dev, empty):
     y = empty((rows, cols), torch.bfloat16)
     q_out = n // 2 + n // 16 + 4 * rows
     legs.append(Leg("nvfp4_tok", lambda: E.mxq_nvfp4_quantize_per_token(x, rows, cols, codes, bs, ts),
-                    2 * n, q_out, n, ["nvfp4_token_kernel<2, true, false>"], "NVFP4 per-token 8192x2048"))
+                    2 * n, q_out, n, ["nvfp4_token_split_kernel<1, true>"], "NVFP4 per-token 8192x2048"))
     legs.append(Leg("nvfp4_tok_dequant",
                     lambda: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, codes, bs, ts, 1, rows, cols, y),
                     q_out, 2 * n, n, ["dequant_nvfp4_kernel"], "NVFP4 -> BF16 8192x2048"))
@@ -383,7 +384,7 @@ def config_timings(torch, E, W, legs, log):
          for b in bufs]
     ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
     k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
-                      ["nvfp4_token_kernel"])
+                      ["nvfp4_token_split_kernel"])
     res[k] = v
     d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows, cols,
                                              b[4])) for b in bufs]

@@ -453,6 +453,66 @@ nvfp4_token_qdq_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t col
     token_body<NB, FULL, false, true>(x, rows, cols, codes, bs, ts, dst);
 }
 
+// Small launches: each row split over the two wavefronts of a workgroup,
+// wavefront w taking blocks [64 NB w, 64 NB (w + 1)) (lane l the blocks
+// 64 NB w + l + 64 k); the token amax is combined through LDS.  Twice the
+// wavefronts, each with half the arithmetic: when the grid is about one
+// round of resident wavefronts, the arithmetic that follows the last loads
+// is halved (8192 x 2048: 13.5 -> 12.2 us); on large grids the one-wavefront
+// rows are faster (262144 x 2048: 248 against 274 us).
+template <int NB, bool FULL>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(8, 8)))
+nvfp4_token_split_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                         uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
+                         float *__restrict__ ts)
+{
+    const int64_t row = (int64_t)wg_id();
+    if (row >= rows)                    // uniform over the workgroup
+        return;
+    const int w = wave_in_group();
+    const int lane = lane_id();
+    const int nblk = (int)(cols >> 4);
+    const uint16_t *xr = x + row * cols;
+    Blk r[NB];
+    BlkF f[NB];
+    uint32_t A = 0;
+#pragma unroll
+    for (int k = 0; k < NB; k++) {
+        const int j = 64 * NB * w + lane + 64 * k;
+        if (FULL) {
+            load_blk(r[k], xr + 16 * j);
+        } else {
+            const bool ok = j < nblk;
+            load_blk(r[k], xr + 16 * (ok ? j : 0));
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                r[k].w[i] = ok ? r[k].w[i] : 0u;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NB; k++) {
+        f[k] = unpack_blk(r[k]);
+        A = max(A, f[k].amax);
+    }
+    __shared__ uint32_t part[2];
+    const uint32_t Aw = __builtin_amdgcn_readfirstlane(wave_max_u32(A));
+    if (lane == 0)
+        part[w] = Aw;
+    __syncthreads();
+    const float s = div2688(u2f(max(part[0], part[1])));
+    const ScaleK sk = scale_k(s);
+    if (w == 0 && lane == 0)
+        ts[row] = s;
+    uint8_t *crow = codes + row * (cols >> 1);
+    uint8_t *brow = bs + row * (cols >> 4);
+#pragma unroll
+    for (int k = 0; k < NB; k++) {
+        const int j = 64 * NB * w + lane + 64 * k;
+        if (FULL || j < nblk)
+            emit_blk(quant_blk(r[k], f[k], sk), j, crow, brow);
+    }
+}
+
 // Longer rows: read twice (amax, then codes).  Dispatch: each block is
 // written to every destination row as it is produced.
 template <bool SCATTER, bool DQ>
@@ -650,9 +710,37 @@ static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uin
     return hipGetLastError();
 }
 
+// Rows of 65..256 blocks use the split kernel on grids of up to 8192 rows
+// (up to 128 blocks) or 16384 rows (129..256 blocks): measured crossovers,
+// e.g. 2048 x 2048: 8.0 -> 6.4 us, 8192 x 4096: 26.8 -> 21.5 us, and
+// 16384 x 2048: 20.8 against 21.6 us split.
+__host__ static bool use_split(int64_t rows, int64_t nblk)
+{
+    return nblk > 64 && nblk <= 256 && rows <= (nblk <= 128 ? 8192 : 16384);
+}
+
+template <int NB, bool FULL>
+static void launch_split(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                         uint8_t *bs, float *ts, hipStream_t stream)
+{
+    hipLaunchKernelGGL((nvfp4_token_split_kernel<NB, FULL>), dim3((unsigned)rows), dim3(128), 0,
+                       stream, x, rows, cols, codes, bs, ts);
+}
+
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *bs, float *ts, hipStream_t stream)
 {
+    const int64_t nblk = cols >> 4;
+    if (use_split(rows, nblk)) {
+        // Two wavefronts of NB blocks per lane: 64 NB < nblk <= 128 NB.
+        if (nblk <= 128)
+            nblk == 128 ? launch_split<1, true>(x, rows, cols, codes, bs, ts, stream)
+                        : launch_split<1, false>(x, rows, cols, codes, bs, ts, stream);
+        else
+            nblk == 256 ? launch_split<2, true>(x, rows, cols, codes, bs, ts, stream)
+                        : launch_split<2, false>(x, rows, cols, codes, bs, ts, stream);
+        return hipGetLastError();
+    }
     return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, nullptr},
                               stream);
 }

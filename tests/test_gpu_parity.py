@@ -145,6 +145,14 @@ def test_nvfp4_shapes(orc, rows, cols):
     check_nvfp4(orc, W.nvfp4_boundary(rows, cols, cols), f"boundary {rows}x{cols}")
 
 
+@pytest.mark.parametrize("rows,cols", [(8193, 1040), (8200, 2048), (16385, 2064), (16400, 4096)])
+def test_nvfp4_shapes_one_wave_rows(orc, rows, cols):
+    """Grids above the row counts that split each row over two wavefronts
+    (8192 rows up to 2048 columns, 16384 up to 4096): one wavefront per row,
+    full and partial rows."""
+    check_nvfp4(orc, W.student_t_activations(rows, cols, rows + cols), f"t3 {rows}x{cols}")
+
+
 def test_nvfp4_boundary_rows(orc):
     check_nvfp4(orc, W.nvfp4_boundary(64, 2048, 17), "boundary 64x2048")
     check_nvfp4(orc, W.nvfp4_boundary(64, 64, 18), "boundary 64x64")
