@@ -116,8 +116,12 @@ def _ptr(a):
 
 def _stream(stream):
     if stream is None:
+        # The raw handle of torch's current stream on the current device:
+        # the same value as torch.cuda.current_stream().cuda_stream without
+        # building a Stream object (0.1 against 2.8 us per call, which
+        # matters for back-to-back launches of kernels of a few us).
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
