@@ -466,7 +466,7 @@ def qdq_small_timings(torch, E, W, dev, empty):
                                                                       b[2], b[3], b[4]))
                     for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
-        kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_qdq_kernel"
+        kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_split_kernel"
         k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
                           n, sets, [kern])
         res[k] = v

@@ -460,11 +460,11 @@ nvfp4_token_qdq_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t col
 // round of resident wavefronts, the arithmetic that follows the last loads
 // is halved (8192 x 2048: 13.5 -> 12.2 us); on large grids the one-wavefront
 // rows are faster (262144 x 2048: 248 against 274 us).
-template <int NB, bool FULL>
+template <int NB, bool FULL, bool DQ>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(8, 8)))
 nvfp4_token_split_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
                          uint8_t *__restrict__ codes, uint8_t *__restrict__ bs,
-                         float *__restrict__ ts)
+                         float *__restrict__ ts, uint16_t *__restrict__ dq)
 {
     const int64_t row = (int64_t)wg_id();
     if (row >= rows)                    // uniform over the workgroup
@@ -501,15 +501,39 @@ nvfp4_token_split_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t c
     __syncthreads();
     const float s = div2688(u2f(max(part[0], part[1])));
     const ScaleK sk = scale_k(s);
-    if (w == 0 && lane == 0)
+    if (w == 0 && lane == 0 && (!DQ || ts))
         ts[row] = s;
     uint8_t *crow = codes + row * (cols >> 1);
     uint8_t *brow = bs + row * (cols >> 4);
+    // DQ: each wavefront stages its half of the BF16 row in LDS (32 bytes
+    // per block), so that every global store instruction writes 1 KiB of
+    // whole lines.
+    __shared__ u32x4_t stage[DQ ? 2 * 128 * NB : 1];
 #pragma unroll
     for (int k = 0; k < NB; k++) {
         const int j = 64 * NB * w + lane + 64 * k;
-        if (FULL || j < nblk)
-            emit_blk(quant_blk(r[k], f[k], sk), j, crow, brow);
+        if (FULL || j < nblk) {
+            const BlkOut o = quant_blk(r[k], f[k], sk);
+            if (!DQ || codes)
+                emit_blk(o, j, crow, brow);
+            if constexpr (DQ) {
+                const int jl = lane + 64 * k;           // block within the wavefront's half
+                nv_block16(o.c0, o.c1, e4m3_value(o.b), s, stage[128 * NB * w + 2 * jl],
+                           stage[128 * NB * w + 2 * jl + 1]);
+            }
+        }
+    }
+    if constexpr (DQ) {
+        __syncthreads();
+        uint16_t *out = dq + row * cols + 16 * (64 * NB * w);
+        const int units = 2 * (nblk - 64 * NB * w);     // 16-byte units in this half
+#pragma unroll
+        for (int q = 0; q < 2 * NB; q++) {
+            const int u = 64 * q + lane;
+            if (FULL || u < units)
+                __builtin_nontemporal_store(stage[128 * NB * w + u],
+                                            reinterpret_cast<u32x4_t *>(out + 8 * u));
+        }
     }
 }
 
@@ -719,28 +743,35 @@ __host__ static bool use_split(int64_t rows, int64_t nblk)
     return nblk > 64 && nblk <= 256 && rows <= (nblk <= 128 ? 8192 : 16384);
 }
 
-template <int NB, bool FULL>
+template <int NB, bool FULL, bool DQ>
 static void launch_split(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
-                         uint8_t *bs, float *ts, hipStream_t stream)
+                         uint8_t *bs, float *ts, uint16_t *dq, hipStream_t stream)
 {
-    hipLaunchKernelGGL((nvfp4_token_split_kernel<NB, FULL>), dim3((unsigned)rows), dim3(128), 0,
-                       stream, x, rows, cols, codes, bs, ts);
+    hipLaunchKernelGGL((nvfp4_token_split_kernel<NB, FULL, DQ>), dim3((unsigned)rows), dim3(128),
+                       0, stream, x, rows, cols, codes, bs, ts, dq);
+}
+
+// Two wavefronts of NB blocks per lane: 64 NB < nblk <= 128 NB.
+template <bool DQ>
+static hipError_t launch_split_rows(const uint16_t *x, int64_t rows, int64_t cols,
+                                    uint8_t *codes, uint8_t *bs, float *ts, uint16_t *dq,
+                                    hipStream_t stream)
+{
+    const int64_t nblk = cols >> 4;
+    if (nblk <= 128)
+        nblk == 128 ? launch_split<1, true, DQ>(x, rows, cols, codes, bs, ts, dq, stream)
+                    : launch_split<1, false, DQ>(x, rows, cols, codes, bs, ts, dq, stream);
+    else
+        nblk == 256 ? launch_split<2, true, DQ>(x, rows, cols, codes, bs, ts, dq, stream)
+                    : launch_split<2, false, DQ>(x, rows, cols, codes, bs, ts, dq, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                                   uint8_t *bs, float *ts, hipStream_t stream)
 {
-    const int64_t nblk = cols >> 4;
-    if (use_split(rows, nblk)) {
-        // Two wavefronts of NB blocks per lane: 64 NB < nblk <= 128 NB.
-        if (nblk <= 128)
-            nblk == 128 ? launch_split<1, true>(x, rows, cols, codes, bs, ts, stream)
-                        : launch_split<1, false>(x, rows, cols, codes, bs, ts, stream);
-        else
-            nblk == 256 ? launch_split<2, true>(x, rows, cols, codes, bs, ts, stream)
-                        : launch_split<2, false>(x, rows, cols, codes, bs, ts, stream);
-        return hipGetLastError();
-    }
+    if (use_split(rows, cols >> 4))
+        return launch_split_rows<false>(x, rows, cols, codes, bs, ts, nullptr, stream);
     return launch_rows<false>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, nullptr},
                               stream);
 }
@@ -777,6 +808,8 @@ hipError_t launch_nvfp4_approx(const uint16_t *x, int64_t rows, int64_t cols, ui
 hipError_t launch_nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                             uint8_t *bs, float *ts, uint16_t *dq, hipStream_t stream)
 {
+    if (use_split(rows, cols >> 4))
+        return launch_split_rows<true>(x, rows, cols, codes, bs, ts, dq, stream);
     return launch_rows<false, true>(x, rows, cols, codes, bs, ts, Dest{nullptr, 1, rows, dq},
                                     stream);
 }

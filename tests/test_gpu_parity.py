@@ -808,6 +808,14 @@ def test_qdq_nvfp4_shapes(orc, rows, cols):
               f"boundary {rows}x{cols}", codes_only_check=False)
 
 
+@pytest.mark.parametrize("rows,cols", [(8193, 1040), (8200, 2048), (16385, 2064)])
+def test_qdq_nvfp4_shapes_one_wave_rows(orc, rows, cols):
+    """Grids above the row counts that split each row over two wavefronts:
+    one wavefront per row, full and partial rows."""
+    check_qdq(orc, W.student_t_activations(rows, cols, rows * cols), mxq.MXQ_FMT_NVFP4,
+              f"t3 {rows}x{cols}")
+
+
 def test_qdq_nvfp4_ties_and_range(orc):
     """Exact ties of both rounding steps, scales across the whole range (the
     binary64 paths of quantize and dequant) and every token amax."""
