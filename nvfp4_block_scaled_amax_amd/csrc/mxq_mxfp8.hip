@@ -181,7 +181,8 @@ __device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t sca
 // row0 (codes) and its scale for this 32-row block, with row pitches ld_t
 // (= rows) and lds_t (= rows / 32).  Each lane writes, per column, its 8 rows
 // as 8 contiguous bytes.
-template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false, bool COLT = false>
+template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false, bool COLT = false,
+          bool LATE = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -194,6 +195,7 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
         for (int j = 0; j < 4; j++)
             a[i][j] = v[i][j] & 0x7FFF7FFFu;
 
+    uint32_t rw0[8], rw1[8], rsb[8];        // LATE: rowwise codes and scale bytes, stored last
     if constexpr (ROW || DQ) {
         const uint32_t nb = cols >> 5;
 #pragma unroll
@@ -214,9 +216,12 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
             }
             const uint32_t w0 = cvt2<true>(cvt2<false>(0u, x0, scale), x1, scale);
             const uint32_t w1 = cvt2<true>(cvt2<false>(0u, x2, scale), x3, scale);
+            rw0[i] = w0;
+            rw1[i] = w1;
+            rsb[i] = sc >> 7;
             if (FULL || (col_ok && i < nr)) {
                 const uint32_t r = (uint32_t)(8 * rg + i);
-                if constexpr (ROW) {
+                if constexpr (ROW && !LATE) {
                     st_nt8(o.rc + (r * cols + c8), w0, w1);
                     if ((g & 3) == 0)
                         o.rs[r * nb + (c8 >> 5)] = (uint8_t)(sc >> 7);
@@ -292,6 +297,25 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
             }
         }
     }
+    // LATE: stores count in the same counter as loads on this architecture,
+    // so rowwise stores issued between the per-row waits make each later
+    // wait cover more loads than the row needs; storing the rowwise copy
+    // after the last load is consumed lets row i's arithmetic start as soon
+    // as load i lands.  Pays where a SIMD holds few wavefronts (small grids:
+    // 8192 x 2048 15.0 -> 14.5 us), not on large grids (262144 x 2048
+    // grouped: 370 -> 375 us).
+    if constexpr (ROW && LATE) {
+        const uint32_t nb = cols >> 5;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (FULL || (col_ok && i < nr)) {
+                const uint32_t r = (uint32_t)(8 * rg + i);
+                st_nt8(o.rc + (r * cols + c8), rw0[i], rw1[i]);
+                if ((g & 3) == 0)
+                    o.rs[r * nb + (c8 >> 5)] = (uint8_t)rsb[i];
+            }
+        }
+    }
 }
 
 struct Geometry {
@@ -345,6 +369,7 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
                                           uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
                                           uint8_t *__restrict__ cs, uint16_t *__restrict__ dq)
 {
+    constexpr bool LATE = ROW && COL && !DQ && !OCP && !COLT && WPW == 4;
     const int lane = (int)lane_id();
     const int g = lane & 15, rg = lane >> 4;
     const int64_t wave = (int64_t)wg_id() * WPW + wave_in_group();
@@ -391,14 +416,14 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
                                    t.nrows, rg, col_ok);
         else
             load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, true, DQ, OCP, COLT>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, true, DQ, OCP, COLT, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
         if constexpr (GATHER)
             load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
                                     t.nrows, rg, col_ok);
         else
             load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, false, DQ, OCP, COLT>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, false, DQ, OCP, COLT, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
 }
 
