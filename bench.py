@@ -625,6 +625,128 @@ def dispatch_timings(torch, E, W, dev, empty):
     return res
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (CPU only): the HBM traffic of each kernel from two
+# counter runs, and the kernel statistics of a kernel-trace run.
+# ---------------------------------------------------------------------------
+
+PMC_CMD = ("rocprofv3 --pmc {counter} -d gpurun_out/pmc_{tag} -o {tag} --output-format csv -- "
+           "python3 bench.py --groups grp,dsp,qdq --steps 2 --warmup 1 --no-cpu-baseline "
+           "--no-configs --copy-calibration-mib 1024")
+STATS_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_bench -o bench --output-format "
+             "csv -- python3 bench.py --groups act,wgt,tok,exp,grp,dsp,qdq,gemm --steps 5 "
+             "--warmup 2 --no-cpu-baseline --no-configs")
+
+
+def kernel_short_name(name: str) -> str:
+    """'void mxq::k<a, b>(args)' -> 'k<a, b>' (the names the legs use)."""
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            name = name[:i]
+            break
+    return name[5:] if name.startswith("mxq::") else name
+
+
+def pmc_per_dispatch(path: str):
+    """{raw kernel name: [counter value summed per dispatch, ...]} of a
+    rocprofv3 counter-collection CSV holding one counter."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            k = per.setdefault(r["Kernel_Name"], {})
+            k[d] = k.get(d, 0.0) + float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, bench_log: str, out_json: str, out_txt: str):
+    """HBM bytes per launch of every single-kernel leg of one bench run under
+    the two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
+    counter scaled by what it reads for the plain copy of the same run."""
+    line = [ln for ln in open(bench_log) if ln.startswith("{")][-1]
+    run = json.loads(line)
+    fetch, write = pmc_per_dispatch(fetch_csv), pmc_per_dispatch(write_csv)
+    mean = lambda v: sum(v) / len(v)
+    copy_bytes = run["copy_calibration"]["bytes"] // 2          # read once, written once
+    copy_f = [mean(v) for k, v in fetch.items() if "bitwise_not" in k]
+    copy_w = [mean(v) for k, v in write.items() if "bitwise_not" in k]
+    f_scale = copy_bytes / (copy_f[0] * 1024)
+    w_scale = copy_bytes / (copy_w[0] * 1024)
+    short_f = {kernel_short_name(k): v for k, v in fetch.items()}
+    short_w = {kernel_short_name(k): v for k, v in write.items()}
+    kernels = {}
+    rows = []
+    for leg, info in run["legs"].items():
+        kern = info["kernels"][-1]
+        if kern not in short_f or kern not in short_w:
+            continue
+        users = [l for l, i in run["legs"].items() if i["kernels"][-1] == kern]
+        if len(users) != 1:
+            continue                    # one kernel for several legs: sizes differ
+        fk, wk = mean(short_f[kern]), mean(short_w[kern])
+        hbm = int(round(fk * 1024 * f_scale + wk * 1024 * w_scale))
+        kernels[kern] = {"leg": leg, "source_digest": kernel_digest(kern), "fetch_kib": fk,
+                         "write_kib": wk, "hbm_bytes_per_launch": hbm,
+                         "algorithmic_bytes": info["bytes"], "launches": len(short_f[kern])}
+        rows.append((kern, leg, fk, wk, hbm, info["bytes"]))
+    doc = {"calibration": {"copy_bytes": copy_bytes, "fetch_kib": copy_f[0],
+                           "write_kib": copy_w[0], "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(doc, f, indent=1)
+    out = ["HBM traffic per launch from rocprofv3 TCC counters (FETCH_SIZE and WRITE_SIZE, KiB per",
+           "dispatch, averaged over the launches of each kernel), each scaled by what the same counter",
+           f"reads for a plain copy kernel (int32 bitwise not of {copy_bytes} bytes: reads and writes",
+           "each byte once).", "",
+           "Commands (run from the repository root on one MI355X, ROCm 7.2, TMPDIR=/tmp):",
+           "  " + PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
+           "  " + PMC_CMD.format(counter="WRITE_SIZE", tag="write"),
+           "Summary: python3 bench.py --summarize-pmc <fetch csv> <write csv> <log of the fetch run>",
+           "",
+           f"copy calibration: FETCH_SIZE {copy_f[0]:.0f} KiB for {copy_bytes} bytes read -> "
+           f"scale {f_scale:.4f};",
+           f"                  WRITE_SIZE {copy_w[0]:.0f} KiB for {copy_bytes} bytes written -> "
+           f"scale {w_scale:.4f}", "",
+           f"{'kernel':<46} {'leg':<26} {'FETCH KiB':>10} {'WRITE KiB':>10} {'HBM bytes':>14} "
+           f"{'algorithmic':>14} {'ratio':>6}"]
+    for kern, leg, fk, wk, hbm, alg in rows:
+        out.append(f"{kern:<46} {leg:<26} {fk:>10.0f} {wk:>10.0f} {hbm:>14} {alg:>14} "
+                   f"{hbm / alg:>6.3f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def summarize_stats(stats_csv: str, out_txt: str, title: str):
+    """Kernel statistics of a rocprofv3 --stats run as a text table."""
+    import csv
+    rows = []
+    with open(stats_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((kernel_short_name(r["Name"]) if "mxq::" in r["Name"] else
+                         r["Name"].split("(")[0].replace("void ", ""), int(r["Calls"]),
+                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda t: -t[5])
+    out = [title, "", "Command (run from the repository root on one MI355X, ROCm 7.2):",
+           "  " + STATS_CMD, "Summary: python3 bench.py --summarize-stats <kernel_stats.csv>", "",
+           f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share':>6}"]
+    for name, calls, avg, mn, mx, pct in rows:
+        out.append(f"{name[:72]:<72} {calls:>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
+                   f"{pct:>5.1f}%")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -645,7 +767,29 @@ def main():
                     help="also time a plain elementwise copy of this many MiB (int32 bitwise "
                          "not, reads and writes each byte once), reported apart from the step, "
                          "to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LOG"),
+                    help="(no GPU) write profiles/traffic.json and its text table from the "
+                         "counter CSVs of the FETCH_SIZE and WRITE_SIZE runs and the bench output "
+                         "of the first")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="(no GPU) write profiles/step_all_kernels_stats.txt from rocprofv3's "
+                         "kernel statistics")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, TRAFFIC_FILE,
+                      os.path.join(ROOT, "profiles", "grouped_262144x2048_hbm_traffic.txt"))
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats,
+                        os.path.join(ROOT, "profiles", "step_all_kernels_stats.txt"),
+                        "rocprofv3 kernel statistics of bench.py: every leg of the step (MXFP8 "
+                        "row+col 2048x2048 and 8192x2048, per-token NVFP4 8192x2048, NVFP4 export "
+                        "of 128 experts, grouped MXFP8/NVFP4 262144x2048 and their dequant) plus "
+                        "the fused-dispatch legs (32768 tokens top-8 of 128), the one-pass "
+                        "quantize + dequant legs (262144x2048) and the dense-layer GEMMs "
+                        "(2048x8192x2048).")
+        return
 
     def log(msg):
         if not args.quiet:
@@ -653,7 +797,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the quantizers shard by rows with no exchange, "
-              "and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "and runs on several GPUs are not supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
