@@ -630,10 +630,10 @@ def dispatch_timings(torch, E, W, dev, empty):
 # counter runs, and the kernel statistics of a kernel-trace run.
 # ---------------------------------------------------------------------------
 
-PMC_CMD = ("rocprofv3 --pmc {counter} -d gpurun_out/pmc_{tag} -o {tag} --output-format csv -- "
+PMC_CMD = ("rocprofv3 --pmc {counter} -d OUT/pmc_{tag} -o {tag} --output-format csv -- "
            "python3 bench.py --groups grp,dsp,qdq --steps 2 --warmup 1 --no-cpu-baseline "
            "--no-configs --copy-calibration-mib 1024")
-STATS_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_bench -o bench --output-format "
+STATS_CMD = ("rocprofv3 --kernel-trace --stats -d OUT/prof_bench -o bench --output-format "
              "csv -- python3 bench.py --groups act,wgt,tok,exp,grp,dsp,qdq,gemm --steps 5 "
              "--warmup 2 --no-cpu-baseline --no-configs")
 
@@ -706,7 +706,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_log: str, out_json: str,
            "dispatch, averaged over the launches of each kernel), each scaled by what the same counter",
            f"reads for a plain copy kernel (int32 bitwise not of {copy_bytes} bytes: reads and writes",
            "each byte once).", "",
-           "Commands (run from the repository root on one MI355X, ROCm 7.2, TMPDIR=/tmp):",
+           "Commands (run from the repository root on one MI355X, ROCm 7.2, TMPDIR=/tmp; OUT is the",
+           "directory the CSVs go to):",
            "  " + PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
            "  " + PMC_CMD.format(counter="WRITE_SIZE", tag="write"),
            "Summary: python3 bench.py --summarize-pmc <fetch csv> <write csv> <log of the fetch run>",
@@ -736,7 +737,8 @@ def summarize_stats(stats_csv: str, out_txt: str, title: str):
                          float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                          float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     rows.sort(key=lambda t: -t[5])
-    out = [title, "", "Command (run from the repository root on one MI355X, ROCm 7.2):",
+    out = [title, "", "Command (run from the repository root on one MI355X, ROCm 7.2; OUT is the "
+           "directory the CSVs go to):",
            "  " + STATS_CMD, "Summary: python3 bench.py --summarize-stats <kernel_stats.csv>", "",
            f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share':>6}"]
     for name, calls, avg, mn, mx, pct in rows:
