@@ -66,6 +66,13 @@ def test_mxfp8_shapes(orc, rows, cols):
     check_mxfp8(orc, xb, f"boundary {rows}x{cols}")
 
 
+def test_mxfp8_large_grid(orc):
+    """A dense grid above the large-launch threshold (32768 tiles: eight
+    wavefronts per workgroup, rowwise codes stored as each row is converted),
+    with a partial last column strip."""
+    check_mxfp8(orc, W.mode_random(8192, 16416, 12), "random 8192x16416")
+
+
 def test_mxfp8_rowwise_only_and_ragged_rows(orc):
     x = W.mode_boundary(96, 256, 3)[:77]
     check_mxfp8(orc, x, "rowwise 77x256", rowwise=True, colwise=False)
