@@ -114,6 +114,23 @@ def test_mxfp8_exhaustive_code_map(orc):
     check_mxfp8(orc, XT, "exhaustive transposed", rowwise=True, colwise=True)
 
 
+def test_binding_stream_is_torch_current_stream():
+    """The binding's default stream is torch's current stream, also inside a
+    stream context, and a call there is ordered on that stream."""
+    from nvfp4_block_scaled_amax_amd import _binding as B
+    assert B._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    x = dev(W.config1())
+    with torch.cuda.stream(s):
+        assert B._stream(None) == s.cuda_stream
+        r = api.mxfp8_quantize_rowcol(x)
+    s.synchronize()
+    ref = api.mxfp8_quantize_rowcol(x)
+    torch.cuda.synchronize()
+    for u, v in zip(r, ref):
+        assert torch.equal(u, v)
+
+
 def test_mxfp8_deterministic():
     x = dev(W.config2_weight("random"))
     announce("mxfp8 determinism 8192x2048")
