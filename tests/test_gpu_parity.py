@@ -131,6 +131,50 @@ def test_binding_stream_is_torch_current_stream():
         assert torch.equal(u, v)
 
 
+def test_graph_capture_replays_match_eager():
+    """MXFP8 row+col, per-token NVFP4 and the NVFP4 dequant captured in one
+    HIP graph: every replay (with eager work and synchronisations between
+    replays, and new inputs copied in) gives the eager bytes.  The calls
+    launch kernels only (no memset nodes)."""
+    x1 = dev(W.config2_weight("random"))
+    x2 = dev(W.config3())
+    a1 = torch.empty_like(x1)
+    a2 = torch.empty_like(x2)
+    a1.copy_(x1)
+    a2.copy_(x2)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm-up outside the capture
+        api.mxfp8_quantize_rowcol(a1)
+        nv = api.nvfp4_quantize_per_token(a2)
+        api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, nv.codes, nv.block_scales, nv.fp32_scales)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        r1 = api.mxfp8_quantize_rowcol(a1)
+        r2 = api.nvfp4_quantize_per_token(a2)
+        y2 = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, r2.codes, r2.block_scales, r2.fp32_scales)
+    inputs = [(x1, x2), (dev(W.config2_weight("boundary")), dev(W.config3()[::-1].copy()))]
+    for rep in range(4):
+        announce(f"graph replay {rep}")
+        src1, src2 = inputs[rep % 2]
+        a1.copy_(src1)
+        a2.copy_(src2)
+        g.replay()
+        torch.cuda.synchronize()
+        e1 = api.mxfp8_quantize_rowcol(src1)
+        e2 = api.nvfp4_quantize_per_token(src2)
+        ey = api.dequantize_bf16(mxq.MXQ_FMT_NVFP4, e2.codes, e2.block_scales, e2.fp32_scales)
+        torch.cuda.synchronize()
+        for u, v in zip(r1, e1):
+            assert torch.equal(u, v), f"replay {rep}: MXFP8"
+        for u, v in zip(r2, e2):
+            assert torch.equal(u, v), f"replay {rep}: NVFP4"
+        assert torch.equal(y2, ey), f"replay {rep}: dequant"
+
+
 def test_mxfp8_deterministic():
     x = dev(W.config2_weight("random"))
     announce("mxfp8 determinism 8192x2048")
