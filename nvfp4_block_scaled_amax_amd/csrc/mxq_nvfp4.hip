@@ -458,8 +458,9 @@ nvfp4_token_qdq_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t col
 // 64 NB w + l + 64 k); the token amax is combined through LDS.  Twice the
 // wavefronts, each with half the arithmetic: when the grid is about one
 // round of resident wavefronts, the arithmetic that follows the last loads
-// is halved (8192 x 2048: 13.5 -> 12.2 us); on large grids the one-wavefront
-// rows are faster (262144 x 2048: 248 against 274 us).
+// is halved (2048 x 2048: 8.1 -> 6.4 us, 8192 x 2048: 13.6 -> 13.2 us); on
+// large grids the one-wavefront rows are faster (262144 x 2048: 248 against
+// 274 us).
 template <int NB, bool FULL, bool DQ>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(8, 8)))
 nvfp4_token_split_kernel(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
