@@ -331,13 +331,43 @@ def time_launches(torch, launches, n_launch, warmup, samples):
     return out
 
 
-def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels):
+def time_graph(torch, launches, n_launch, samples):
+    """Per-launch time (ms) of n_launch launches cycling through `launches`,
+    captured once in a HIP graph and replayed `samples` times: the device's
+    rate without the host's per-call cost (argument checks, Python), which
+    bounds back-to-back eager launches of kernels of a few us."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for k in range(n_launch):
+            launches[k % len(launches)]()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / n_launch)
+    del g
+    return out
+
+
+def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None):
     med, mn = float(np.median(ms_list)), float(np.min(ms_list))
     gbs = nbytes / (med * 1e-3) / 1e9
-    return name, {"desc": desc, "kernels": kernels, "ms_median": round(med, 5),
-                  "ms_min": round(mn, 5), "bytes": nbytes, "GB_s": round(gbs, 1),
-                  "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                  "elements_per_s": round(elems / (med * 1e-3), 1), "buffer_sets": sets}
+    rec = {"desc": desc, "kernels": kernels, "ms_median": round(med, 5),
+           "ms_min": round(mn, 5), "bytes": nbytes, "GB_s": round(gbs, 1),
+           "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "elements_per_s": round(elems / (med * 1e-3), 1), "buffer_sets": sets}
+    if graph_ms is not None:
+        gmed = float(np.median(graph_ms))
+        ggbs = nbytes / (gmed * 1e-3) / 1e9
+        rec.update({"graph_ms_median": round(gmed, 5), "graph_GB_s": round(ggbs, 1),
+                    "graph_pct_hbm_peak": round(100 * ggbs / HBM_PEAK_GBS, 2)})
+    return name, rec
 
 
 def config_timings(torch, E, W, legs, log):
@@ -360,8 +390,9 @@ def config_timings(torch, E, W, legs, log):
         launches = [(lambda b=b: E.mxq_mxfp8_quantize_rowcol(b[0], rows, cols, b[1], b[2], b[3],
                                                                b[4])) for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
         k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
-                          ["mxfp8_tile_kernel"])
+                          ["mxfp8_tile_kernel"], gms)
         res[k] = v
         del bufs, launches, x0
         torch.cuda.empty_cache()
@@ -383,14 +414,16 @@ def config_timings(torch, E, W, legs, log):
     q = [(lambda b=b: E.mxq_nvfp4_quantize_per_token(b[0], rows, cols, b[1], b[2], b[3]))
          for b in bufs]
     ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+    gms = time_graph(torch, q, CFG_LAUNCHES, CFG_SAMPLES)
     k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
-                      ["nvfp4_token_split_kernel"])
+                      ["nvfp4_token_split_kernel"], gms)
     res[k] = v
     d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows, cols,
                                              b[4])) for b in bufs]
     ms = time_launches(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+    gms = time_graph(torch, d, CFG_LAUNCHES, CFG_SAMPLES)
     k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", ms, d_bytes, n, sets,
-                      ["dequant_nvfp4_kernel"])
+                      ["dequant_nvfp4_kernel"], gms)
     res[k] = v
     del bufs, q, d, x0
     torch.cuda.empty_cache()
@@ -466,9 +499,10 @@ def qdq_small_timings(torch, E, W, dev, empty):
                                                                       b[2], b[3], b[4]))
                     for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
         kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_split_kernel"
         k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
-                          n, sets, [kern])
+                          n, sets, [kern], gms)
         res[k] = v
         del bufs, launches, x0
         torch.cuda.empty_cache()
