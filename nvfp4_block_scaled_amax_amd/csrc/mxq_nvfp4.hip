@@ -255,9 +255,13 @@ template <bool NT = true>
 __device__ __forceinline__ void emit_blk(const BlkOut &o, int64_t j, uint8_t *__restrict__ codes,
                                          uint8_t *__restrict__ bs)
 {
-    if constexpr (NT)
+    if constexpr (NT) {
+        // Keeps the store where it is: with one block per lane, the
+        // optimizer otherwise merges the stores that follow the arithmetic
+        // paths of quant_blk and drops their non-temporal mark.
+        asm volatile("" ::: "memory");
         st_nt8(codes + 8 * j, o.c0, o.c1);
-    else
+    } else
         st8(codes + 8 * j, o.c0, o.c1);
     bs[j] = (uint8_t)o.b;
 }
