@@ -739,13 +739,18 @@ static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uin
     return hipGetLastError();
 }
 
-// Rows of 65..256 blocks use the split kernel on grids of up to 8192 rows
-// (up to 128 blocks) or 16384 rows (129..256 blocks): measured crossovers,
-// e.g. 2048 x 2048: 8.0 -> 6.4 us, 8192 x 4096: 26.8 -> 21.5 us, and
-// 16384 x 2048: 20.8 against 21.6 us split.
-__host__ static bool use_split(int64_t rows, int64_t nblk)
+// Rows of 65..256 blocks use the split kernel on grids of up to one round of
+// resident one-wavefront rows (up to 128 blocks) or two (129..256 blocks):
+// 8192 and 16384 rows on 256 CUs, the measured crossovers (2048 x 2048:
+// 8.0 -> 6.4 us, 8192 x 4096: 26.8 -> 21.5 us; 16384 x 2048: 20.8 against
+// 21.6 us split).  The round scales with the device's CU count.
+static bool use_split(int64_t rows, int64_t nblk)
 {
-    return nblk > 64 && nblk <= 256 && rows <= (nblk <= 128 ? 8192 : 16384);
+    if (nblk <= 64 || nblk > 256)
+        return false;
+    const int64_t round =
+        resident_workgroups((const void *)nvfp4_token_kernel<2, true, false>, WG_THREADS);
+    return rows <= (nblk <= 128 ? round : 2 * round);
 }
 
 template <int NB, bool FULL, bool DQ>
