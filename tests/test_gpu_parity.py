@@ -1196,3 +1196,46 @@ def test_dispatch_mxfp8_single_copy(orc):
     assert_same(host(cs).reshape(-1, cols)[:used], host(d8.col_scales)[:used],
                 "col-only scales")
     assert_same(host(P), host(d8.col_scale_offsets), "col-only offsets")
+
+
+# ---------------------------------------------------------------------------
+# Seeded random shapes and value laws across every kernel path
+# ---------------------------------------------------------------------------
+
+def _random_values(rng, rows, cols):
+    """One of several value laws: normal at a random scale, heavy tails,
+    log-uniform magnitudes over many binades, sparse (zeros), or constant
+    rows; BF16 bits."""
+    kind = int(rng.integers(0, 5))
+    if kind == 0:
+        v = rng.standard_normal((rows, cols)) * 2.0 ** float(rng.integers(-40, 40))
+    elif kind == 1:
+        v = rng.standard_t(2, (rows, cols)) * 0.5
+    elif kind == 2:
+        v = np.exp2(rng.uniform(-60, 60, (rows, cols))) * rng.choice([-1.0, 1.0], (rows, cols))
+    elif kind == 3:
+        v = rng.standard_normal((rows, cols))
+        v[rng.random((rows, cols)) < 0.7] = 0.0
+    else:
+        v = np.repeat(rng.standard_normal((rows, 1)), cols, axis=1)
+    return W.bf16_bits(np.clip(v, -3.38e38, 3.38e38))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_all_paths(orc, seed):
+    """MXFP8 row+col, per-token NVFP4 and both one-pass quantize + dequant
+    calls on seeded random shapes: row counts on both sides of the grid-size
+    switches, column counts that leave partial tiles, strips and blocks."""
+    rng = np.random.default_rng(1000 + seed)
+    for _ in range(3):
+        rows = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(7000, 9500))]))
+        cols16 = int(rng.integers(1, 260)) * 16
+        x = _random_values(rng, rows, cols16)
+        check_nvfp4(orc, x, f"random {rows}x{cols16}")
+        check_qdq(orc, x, mxq.MXQ_FMT_NVFP4, f"random {rows}x{cols16}", codes_only_check=False)
+        rows32 = max(32, rows - rows % 32)
+        cols32 = int(rng.integers(1, 130)) * 32
+        y = _random_values(rng, rows32, cols32)
+        check_mxfp8(orc, y, f"random {rows32}x{cols32}")
+        check_qdq(orc, y, mxq.MXQ_FMT_MXFP8_ROW, f"random {rows32}x{cols32}",
+                  codes_only_check=False)
