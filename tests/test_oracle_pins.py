@@ -765,3 +765,41 @@ def test_per_tensor_scope_is_batch_dependent(orc):
     assert not np.array_equal(px[0][0][0], py[0][0][0])  # row 0 quantized differently
     tx, ty = orc.nvfp4_per_token(x), orc.nvfp4_per_token(y)
     assert np.array_equal(tx[0][0], ty[0][0]) and tx[2][0] == ty[2][0]
+
+
+# ---------------------------------------------------------------------------
+# Property sweep: the oracle against the exact spec on arbitrary finite BF16
+# bit patterns (hypothesis draws the bits, so scales range over the whole
+# exponent range, subnormals, ties and saturation included).
+# ---------------------------------------------------------------------------
+
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+_finite_bf16 = st.integers(0, 0xFFFF).filter(lambda b: (b & 0x7F80) != 0x7F80)
+
+
+def _narrowed(bits, shift):
+    """Bit patterns pulled toward one magnitude band (2^-shift of the range),
+    so that blocks hold values of comparable size and codes are not all 0."""
+    return [(b & 0x8000) | (0x3F80 + ((b & 0x7FFF) >> shift)) if shift else b for b in bits]
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(_finite_bf16, min_size=64, max_size=64), st.integers(0, 8))
+def test_property_mxfp8_rowwise_vs_exact_spec(orc, bits, shift):
+    x = np.array(_narrowed(bits, shift), np.uint16).reshape(2, 32)
+    codes, scales = orc.mxfp8_rowwise(x)
+    ec, es = X.mxfp8_rowwise([[int(v) for v in row] for row in x])
+    assert np.array_equal(scales, np.array(es, np.uint8))
+    assert np.array_equal(codes, np.array(ec, np.uint8))
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(_finite_bf16, min_size=64, max_size=64), st.integers(0, 8))
+def test_property_nvfp4_per_token_vs_exact_spec(orc, bits, shift):
+    x = np.array(_narrowed(bits, shift), np.uint16).reshape(2, 32)
+    codes, bs, ts = orc.nvfp4_per_token(x)
+    ec, eb, es = X.nvfp4_per_token([[int(v) for v in row] for row in x])
+    assert [F(float(t)) for t in ts] == es
+    assert np.array_equal(bs, np.array(eb, np.uint8))
+    assert np.array_equal(codes, np.array(ec, np.uint8))
