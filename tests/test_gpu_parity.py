@@ -1239,3 +1239,23 @@ def test_random_shapes_all_paths(orc, seed):
         check_mxfp8(orc, y, f"random {rows32}x{cols32}")
         check_qdq(orc, y, mxq.MXQ_FMT_MXFP8_ROW, f"random {rows32}x{cols32}",
                   codes_only_check=False)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_grouped_segments(orc, seed):
+    """Grouped MXFP8 row+col and NVFP4 on seeded random segmentations: empty
+    segments, segments of 1..31 rows, exact multiples of 32 and long ones,
+    random column counts (partial strips), every segment checked."""
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.integers(1, 40))
+    kinds = rng.integers(0, 4, G)
+    sizes = np.where(kinds == 0, 0,
+                     np.where(kinds == 1, rng.integers(1, 32, G),
+                              np.where(kinds == 2, 32 * rng.integers(1, 5, G),
+                                       rng.integers(33, 700, G))))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    if off[-1] == 0:
+        off[-1] = 1
+    cols = int(rng.integers(1, 80)) * 32
+    x = _random_values(rng, int(off[-1]), cols)
+    check_grouped(orc, x, off, f"random G={G} cols={cols}")
