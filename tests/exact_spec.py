@@ -11,10 +11,12 @@ shares none of its code or arithmetic route.  Slow: tiny tensors only.
 from __future__ import annotations
 
 from fractions import Fraction as F
+from functools import lru_cache
 
 TWO = F(2)
 
 
+@lru_cache(maxsize=None)
 def bf16_frac(bits: int) -> F:
     sign = -1 if bits & 0x8000 else 1
     E = (bits >> 7) & 0xFF

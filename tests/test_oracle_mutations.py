@@ -35,6 +35,18 @@ MUTATIONS = {
     "zero_block_not_zero": ("(d > 0.0) ? oracle_e2m1_nearest(v, d * sd) : 0",
                             "oracle_e2m1_nearest(v, d * sd)"),
     "row_block_offset": ("x[i * cols + j * 32 + k]", "x[i * cols + j * 16 + k]"),
+    "colwise_dequant_neighbour_scale": ("oracle_e8m0_value(scales[(i / 32) * cols + k])",
+                                        "oracle_e8m0_value(scales[(i / 32) * cols + (k ^ 1)])"),
+    "dequant_nvfp4_first_fp32_scale": ("(double)fp32_scales[i / rows_per_scale]",
+                                       "(double)fp32_scales[0]"),
+    "scoped_row_swap": ("float s, uint8_t *codes, uint8_t *block_scales)\n{\n"
+                        "#pragma omp parallel for schedule(static)\n"
+                        "    for (int64_t t = 0; t < rows; t++)\n"
+                        "        nvfp4_row(x + t * cols,",
+                        "float s, uint8_t *codes, uint8_t *block_scales)\n{\n"
+                        "#pragma omp parallel for schedule(static)\n"
+                        "    for (int64_t t = 0; t < rows; t++)\n"
+                        "        nvfp4_row(x + (t ^ 1) * cols,"),
 }
 
 

@@ -598,6 +598,94 @@ def test_pair_equals_concatenated_scope(orc):
     assert np.array_equal(gc1, gc2) and np.array_equal(gb1, gb2) and np.array_equal(sc1, sc2)
 
 
+def _bf16_of_exact(y: F, negative: bool) -> int:
+    """BF16 bits of the exact product y rounded once (nearest-even, saturating);
+    a product that is zero keeps the sign of the code that made it."""
+    if y == 0:
+        return 0x8000 if negative else 0
+    return X.bf16_nearest_sat(-y if negative else y)
+
+
+@pytest.mark.parametrize("mode", ["boundary", "maxes", "codes"])
+def test_dequant_mxfp8_colwise_vs_exact_spec(orc, mode):
+    """Columnwise MXFP8 -> BF16, every element: the E4M3 value times the scale of
+    the element's own 32-row block of its own column, rounded once.  The 'codes'
+    case feeds every non-NaN code byte under random scale bytes that differ from
+    column to column (the whole E8M0 range, so BF16 saturation and underflow to
+    signed zero both occur)."""
+    if mode == "codes":
+        rng = np.random.default_rng(21)
+        rows, cols = 64, 24
+        codes = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] ^= 1                 # NaN codes -> +-448
+        scales = rng.integers(0, 255, (rows // 32, cols), dtype=np.uint8)
+    else:
+        rows, cols = 64, 32
+        x = W.mxfp8_mode(mode, rows, cols, 11)
+        codes, scales = orc.mxfp8_colwise(x)
+    out = orc.dequant_mxfp8_colwise(codes, scales)
+    for i in range(rows):
+        for k in range(cols):
+            c = int(codes[i, k])
+            y = X.E4M3_POS[c & 0x7F] * F(2) ** (int(scales[i // 32, k]) - 127)
+            assert out[i, k] == _bf16_of_exact(y, bool(c & 0x80)), (mode, i, k)
+
+
+@pytest.mark.parametrize("per", [2, 3, 12])
+def test_dequant_nvfp4_shared_fp32_scales_vs_exact_spec(orc, per):
+    """NVFP4 -> BF16 where consecutive rows share one FP32 scale (one scale per
+    expert or per tensor, as in the weight export round trip): row i uses
+    fp32_scales[i // per].  Every group's scale differs from the others'."""
+    rng = np.random.default_rng(30 + per)
+    rows, cols = 12, 32
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    bs = rng.integers(0, 127, (rows, cols // 16), dtype=np.uint8)
+    n_sc = -(-rows // per)
+    fs = (rng.uniform(1.0, 2.0, n_sc) * 2.0 ** rng.integers(-30, 30, n_sc)).astype(np.float32)
+    assert len(set(fs.tolist())) == n_sc
+    out = orc.dequant_nvfp4(codes, bs, fs, per)
+    for i in range(rows):
+        s = F(float(fs[i // per]))
+        for k in range(cols):
+            c = (int(codes[i, k // 2]) >> (4 * (k % 2))) & 0xF
+            y = X.E2M1_POS[c & 7] * X.E4M3_POS[int(bs[i, k // 16])] * s
+            assert out[i, k] == _bf16_of_exact(y, bool(c & 8)), (per, i, k)
+
+
+def test_scoped_quantize_vs_exact_spec(orc):
+    """The weight-export scopes row by row against the Fraction spec: the scope's
+    FP32 scale is the binary32 rounding of (amax over every element of the
+    scope) / 2688, and each row of each tensor is quantized under it (gate and
+    up of one expert share one scope; down is its own).  Also the bare
+    'quantize under a given scale' call, under a scale no row picks itself."""
+    rng = np.random.default_rng(40)
+    E, rows, cols = 2, 6, 32
+    g = W.bf16_bits(rng.normal(0, 0.02, (E, rows, cols)))
+    u = W.bf16_bits(rng.standard_t(3, (E, rows, cols)) * 0.01)
+    gc, gb, uc, ub, sc = orc.nvfp4_gateup_pair(g, u)
+    dc, db, _, _, dsc = orc.nvfp4_gateup_pair(u, None)
+    for e in range(E):
+        A = max(abs(X.bf16_frac(int(b))) for b in np.concatenate([g[e].ravel(), u[e].ravel()]))
+        s = X.nvfp4_scale(A)
+        assert F(float(sc[e])) == s
+        Ad = max(abs(X.bf16_frac(int(b))) for b in u[e].ravel())
+        sd = X.nvfp4_scale(Ad)
+        assert F(float(dsc[e])) == sd
+        for t in range(rows):
+            for (src, codes, bsc, ss) in ((g, gc, gb, s), (u, uc, ub, s), (u, dc, db, sd)):
+                ec, eb = X.nvfp4_row([int(v) for v in src[e, t]], ss)
+                assert codes[e, t].tolist() == ec, (e, t)
+                assert bsc[e, t].tolist() == eb, (e, t)
+    x = W.student_t_activations(8, 48, 41)
+    A = max(abs(X.bf16_frac(int(b))) for b in x.ravel())
+    s = X.nvfp4_scale(A) * 3      # not the RN32 of any amax / 2688 of this tensor
+    s = X.rn_binary32(s)
+    c, b = orc.nvfp4_with_scale(x, float(s))
+    for t in range(8):
+        ec, eb = X.nvfp4_row([int(v) for v in x[t]], s)
+        assert c[t].tolist() == ec and b[t].tolist() == eb, t
+
+
 def test_grouped_colwise_equals_standalone_and_zero_pad(orc):
     off = np.array([0, 0, 1, 32, 63, 96, 96, 160, 193], np.int64)
     x = W.mode_random(int(off[-1]), 64, 9)
