@@ -74,7 +74,8 @@ extern "C" {
 typedef enum {
     MXQ_OK = 0,
     MXQ_ERR_NULL = 1,      /* a required pointer is NULL                      */
-    MXQ_ERR_SIZE = 2,      /* a size is <= 0 (or n_groups < 1)                */
+    MXQ_ERR_SIZE = 2,      /* a size is <= 0 (or n_groups < 1), or beyond a   */
+                           /* limit stated below                              */
     MXQ_ERR_SHAPE = 3,     /* cols (or rows) not divisible as required        */
     MXQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                */
     MXQ_ERR_ALIAS = 5,     /* an output overlaps an input or another output   */
@@ -83,6 +84,21 @@ typedef enum {
     MXQ_ERR_LAUNCH = 8,    /* the kernel launch failed                        */
     MXQ_ERR_ARG = 9        /* an enum argument has an unknown value           */
 } mxq_status;
+
+/*
+ * Size limits common to the entry points (MXQ_ERR_SIZE beyond them).  Each
+ * launch is one grid of at most 2^32 - 1 work-items, so:
+ *   - per-token NVFP4 calls take rows (tokens) below 2^26 (one 64-lane
+ *     workgroup per row);
+ *   - MXFP8 quantize calls take at most 2^26 - 9 tiles of 32 rows x 128
+ *     columns: ceil(rows / 32) * ceil(cols / 128), where grouped and
+ *     dispatch calls with a columnwise copy count total_rows / 32 + n_groups
+ *     row tiles;
+ *   - GEMMs take at most 2^24 - 9 output tiles: ceil(M/256) * ceil(N/256);
+ *   - the weight export takes n_experts below 2^26 and at most 2^26 - 1
+ *     amax chunks: ceil(elements per scope / 4096) * n_experts.
+ * Dequant walks its grid in strides and has no grid limit of its own.
+ */
 
 typedef enum {
     MXQ_FMT_MXFP8_ROW = 1,     /* MXFP8 rowwise 1x32 copy                    */
@@ -114,7 +130,8 @@ typedef enum {
  *   NULL to skip the columnwise copy (not both copies); one NULL of a pair is
  *   MXQ_ERR_OFFSETS.  Requires cols % 32 == 0, and rows % 32 == 0 when the
  *   columnwise copy is requested.  Code arrays must be 16-byte aligned.
- *   cols must not exceed 2^26 (MXQ_ERR_SIZE otherwise).
+ *   cols must not exceed 2^26, and the tile count is limited as stated above
+ *   (MXQ_ERR_SIZE otherwise).
  */
 int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *row_codes, uint8_t *row_scales,
@@ -142,7 +159,8 @@ int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
  * gradient of the MXFP8 recipe's backward) reads it K-contiguous, as
  * mxq_mxfp8_gemm requires.
  *   col_codes_t, col_scales_t required (16-byte aligned codes); row_codes and
- *   row_scales both or neither; rows % 32 == 0, cols % 32 == 0, rows < 2^31.
+ *   row_scales both or neither; rows % 32 == 0, cols % 32 == 0; MXFP8 tile
+ *   limit as above.
  */
 int mxq_mxfp8_quantize_rowcol_t(const uint16_t *x, int64_t rows, int64_t cols,
                                 uint8_t *row_codes, uint8_t *row_scales, uint8_t *col_codes_t,
@@ -160,7 +178,7 @@ int mxq_mxfp8_quantize_rowcol_t(const uint16_t *x, int64_t rows, int64_t cols,
  *   codes        [rows][cols/2] packed E2M1, 16-byte aligned.
  *   block_scales [rows][cols/16] E4M3.
  *   token_scales [rows] FP32: s_t = fp32(amax_t / 2688), the decode multiplier.
- *   rows must be below 2^31 (MXQ_ERR_SIZE otherwise).
+ *   rows must be below 2^26 (MXQ_ERR_SIZE otherwise).
  */
 int mxq_nvfp4_quantize_per_token(const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *codes, uint8_t *block_scales,
@@ -198,7 +216,8 @@ int mxq_nvfp4_quantize_per_token_approx(const uint16_t *x, int64_t rows, int64_t
  *   gate_codes also serves the call as scratch for per-chunk partial maxima
  *   (written before, and overwritten by, the codes).
  *   up, up_codes and up_block_scales must be all NULL or all non-NULL.
- *   n_experts * rows * cols must be below 2^36 (MXQ_ERR_SIZE otherwise).
+ *   n_experts * rows * cols must be below 2^36, and the export limits above
+ *   hold (MXQ_ERR_SIZE otherwise).
  */
 int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up,
                                    int64_t n_experts, int64_t rows, int64_t cols,
@@ -238,10 +257,11 @@ int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
  *
  *   fmt == MXQ_FMT_MXFP8_ROW: codes [rows][cols] (16-byte aligned), scales
  *          [rows][cols/32] as mxq_mxfp8_quantize_rowcol's rowwise copy;
- *          token_scales must be NULL; cols % 32 == 0, cols <= 2^26.
+ *          token_scales must be NULL; cols % 32 == 0, cols <= 2^26, MXFP8
+ *          tile limit as above.
  *   fmt == MXQ_FMT_NVFP4: codes [rows][cols/2] (16-byte aligned), scales
  *          [rows][cols/16], token_scales [rows] as
- *          mxq_nvfp4_quantize_per_token; cols % 16 == 0, rows < 2^31.
+ *          mxq_nvfp4_quantize_per_token; cols % 16 == 0, rows < 2^26.
  *   out  [rows][cols] BF16, 16-byte aligned, required.
  *   codes and scales must be both NULL or both non-NULL (NULL: not stored,
  *   only the dequantized copy is written); NVFP4 token_scales may be NULL
@@ -265,7 +285,8 @@ int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t 
  *   a  [M][K] E4M3 codes, 16-byte aligned;  a_scales [M][K/32] E8M0, 4-byte aligned.
  *   b  [N][K] E4M3 codes, 16-byte aligned;  b_scales [N][K/32] E8M0, 4-byte aligned.
  *   c  [M][N] fp32 or BF16 (out_dtype), row-major.
- *   K % 128 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1.
+ *   K % 128 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1
+ *   within the GEMM tile limit above.
  */
 int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
@@ -288,7 +309,8 @@ int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
  *   a_block_scales [M][K/16] E4M3, 4-byte aligned;  a_scales FP32, one per
  *   rows_per_a_scale rows.  b, b_block_scales, b_scales likewise for [N][K].
  *   c  [M][N] fp32 or BF16 (out_dtype).
- *   K % 64 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1;
+ *   K % 64 == 0 (MXQ_ERR_SHAPE) and K <= 2^23 (MXQ_ERR_SIZE); any M, N >= 1
+ *   within the GEMM tile limit above;
  *   rows_per_a_scale, rows_per_b_scale >= 1.
  */
 int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
@@ -333,8 +355,8 @@ typedef struct {
  *   seg_offsets   device int64 [n_groups + 1], 0 = o_0 <= ... <= o_G =
  *                 total_rows (read on the device; not validated on the host).
  *   out           host pointer to the output struct (device arrays inside).
- *   For NVFP4, total_rows must be below 2^31; for MXFP8, cols must not exceed
- *   2^26 (MXQ_ERR_SIZE otherwise).
+ *   For NVFP4, total_rows must be below 2^26; for MXFP8, cols must not exceed
+ *   2^26 and the tile limit above holds (MXQ_ERR_SIZE otherwise).
  */
 int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
                          int64_t cols, const int64_t *seg_offsets,
@@ -366,7 +388,8 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows,
  *   out           as mxq_grouped_quantize, over total_rows rows.
  * The maps are device data, not validated on the host: when they are not
  * inverse to each other the outputs are unspecified bytes, but no access
- * leaves the arrays.  For NVFP4, n_tokens must be below 2^31.
+ * leaves the arrays.  For NVFP4, n_tokens must be below 2^26; for MXFP8 the
+ * tile limit above holds.
  */
 int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens,
                                   int64_t cols, int64_t top_k,

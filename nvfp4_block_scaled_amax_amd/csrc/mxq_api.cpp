@@ -23,13 +23,20 @@ struct Buf {
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 62;
 // GEMM tiles address their 256 rows with 32-bit offsets.
 constexpr int64_t MAX_GEMM_K = (int64_t)1 << 23;
-constexpr int64_t MAX_GRID_ROWS = 0x7FFFFFFF;     // per-token NVFP4: one workgroup per row
+constexpr int64_t MAX_GRID_ROWS = mxq::MAX_TOKEN_ROWS;   // per-token NVFP4: one workgroup per row
 constexpr int64_t MAX_BLOCKS = 0xFFFFFFFF;        // 16-element blocks indexed in 32 bits
 constexpr int64_t MAX_MXFP8_COLS = (int64_t)1 << 26;  // 32-row tile offsets fit 32 bits
 
 bool size_ok(int64_t a, int64_t b)
 {
     return a > 0 && b > 0 && a <= MAX_ELEMS / b;
+}
+
+// The MXFP8 tile launches over `row_tiles` 32-row tiles of `cols` columns
+// fit one grid.
+bool mxfp8_grid_ok(int64_t row_tiles, int64_t cols)
+{
+    return row_tiles <= MAX_ELEMS / cols && mxq::mxfp8_tiles(row_tiles, cols) <= mxq::MAX_MXFP8_TILES;
 }
 
 // One allocation of the current device: [base, base + size).
@@ -152,7 +159,7 @@ int mxq_mxfp8_quantize_rowcol(const uint16_t *x, int64_t rows, int64_t cols, uin
     if ((row_codes == nullptr) != (row_scales == nullptr) ||
         (col_codes == nullptr) != (col_scales == nullptr) || (!row_codes && !col_codes))
         return MXQ_ERR_OFFSETS;
-    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS)
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS || !mxfp8_grid_ok((rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0 || (col_codes && rows % 32 != 0))
         return MXQ_ERR_SHAPE;
@@ -184,7 +191,7 @@ int mxq_mxfp8_quantize_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
     if ((row_codes == nullptr) != (row_scales == nullptr) ||
         (col_codes == nullptr) != (col_scales == nullptr) || (!row_codes && !col_codes))
         return MXQ_ERR_OFFSETS;
-    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS)
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS || !mxfp8_grid_ok((rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0 || (col_codes && rows % 32 != 0))
         return MXQ_ERR_SHAPE;
@@ -215,7 +222,7 @@ int mxq_mxfp8_quantize_rowcol_t(const uint16_t *x, int64_t rows, int64_t cols,
         return MXQ_ERR_NULL;
     if ((row_codes == nullptr) != (row_scales == nullptr))
         return MXQ_ERR_OFFSETS;
-    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS || rows > MAX_GRID_ROWS)
+    if (!size_ok(rows, cols) || cols > MAX_MXFP8_COLS || !mxfp8_grid_ok((rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0 || rows % 32 != 0)
         return MXQ_ERR_SHAPE;
@@ -294,7 +301,9 @@ int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up, int
     if (cols % 16 != 0)
         return MXQ_ERR_SHAPE;
     const int64_t n = n_experts * rows * cols;
-    if (n / 16 > MAX_BLOCKS)
+    if (n / 16 > MAX_BLOCKS || n_experts > mxq::MAX_GRID_ITEMS / 64 ||
+        mxq::scoped_amax_workgroups(n_experts, rows * cols, has_up) >
+            mxq::MAX_SCOPED_AMAX_WORKGROUPS)
         return MXQ_ERR_SIZE;
     Buf b[7];
     int k = 0;
@@ -389,7 +398,7 @@ int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t 
         return launched(mxq::launch_nvfp4_qdq(x, rows, cols, codes, scales, token_scales, out,
                                               (hipStream_t)stream));
     }
-    if (cols > MAX_MXFP8_COLS)
+    if (cols > MAX_MXFP8_COLS || !mxfp8_grid_ok((rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0)
         return MXQ_ERR_SHAPE;
@@ -416,7 +425,7 @@ int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
         return MXQ_ERR_SIZE;
     if (K % 128 != 0)
         return MXQ_ERR_SHAPE;
-    if (K > MAX_GEMM_K)
+    if (K > MAX_GEMM_K || ((M + 255) / 256) * ((N + 255) / 256) > mxq::MAX_GEMM_TILES)
         return MXQ_ERR_SIZE;
     const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
     const Buf bb[5] = {{a, M * K, 16, false},
@@ -445,7 +454,7 @@ int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float 
         return MXQ_ERR_SIZE;
     if (K % 64 != 0)
         return MXQ_ERR_SHAPE;
-    if (K > MAX_GEMM_K)
+    if (K > MAX_GEMM_K || ((M + 255) / 256) * ((N + 255) / 256) > mxq::MAX_GEMM_TILES)
         return MXQ_ERR_SIZE;
     const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
     const Buf bb[7] = {{a, M * K / 2, 16, false},
@@ -505,7 +514,8 @@ int mxq_grouped_quantize(int fmt, const uint16_t *x, int64_t total_rows, int64_t
     if (cols > MAX_MXFP8_COLS)
         return MXQ_ERR_SIZE;
     const int64_t scale_rows = total_rows / 32 + n_groups;
-    if (scale_rows > MAX_ELEMS / cols)
+    if (scale_rows > MAX_ELEMS / cols ||
+        !mxfp8_grid_ok(cc ? scale_rows : (total_rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     Buf b[7];
     int k = 0;
@@ -581,7 +591,8 @@ int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens, 
     if (cols > MAX_MXFP8_COLS)
         return MXQ_ERR_SIZE;
     const int64_t scale_rows = total_rows / 32 + (cc ? n_groups : 0);
-    if (scale_rows > MAX_ELEMS / cols)
+    if (scale_rows > MAX_ELEMS / cols ||
+        !mxfp8_grid_ok(cc ? scale_rows : (total_rows + 31) / 32, cols))
         return MXQ_ERR_SIZE;
     Buf b[8];
     int k = 0;

@@ -124,8 +124,8 @@ static unsigned grid_for(K kernel, int64_t n, int oversubscribe)
         if (wgs > cap)
             wgs = cap;
     }
-    if (wgs > 0x7FFFFFFF)       // grid-stride covers the rest
-        wgs = 0x7FFFFFFF;
+    if (wgs > MAX_GRID_ITEMS / (64 * WAVES_PER_WG))     // grid-stride covers the rest
+        wgs = MAX_GRID_ITEMS / (64 * WAVES_PER_WG);
     return (unsigned)(wgs < 1 ? 1 : wgs);
 }
 

@@ -43,6 +43,8 @@ typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
 constexpr int GEMM_BM = 256, GEMM_BN = 256, GEMM_BK = 128;
 constexpr int GEMM_THREADS = 256;
+static_assert(GEMM_BM == 256 && GEMM_BN == 256 && GEMM_THREADS == 256,
+              "MAX_GEMM_TILES counts 256 x 256 tiles of 256 threads");
 constexpr int GEMM_CHUNKS = GEMM_BM * GEMM_BK / 16;             // 16-byte chunks per operand slice
 constexpr int GEMM_STAGE_BYTES = 2 * GEMM_CHUNKS * 16 + 2 * GEMM_BM * 4;
 constexpr int GEMM_EPI_ROW = 128 * 2 + 16;                      // padded BF16 row of a quarter
@@ -491,7 +493,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
                              void *c, hipStream_t stream)
 {
     const int64_t tm = (M + GEMM_BM - 1) / GEMM_BM, tn = (N + GEMM_BN - 1) / GEMM_BN;
-    if (tm * tn > 0x7FFFFFF)
+    if (tm * tn > MAX_GEMM_TILES)            // checked by the caller
         return hipErrorInvalidValue;
     GemmGrid g;
     g.tiles_m = (uint32_t)tm;
@@ -515,7 +517,7 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const ui
                              bool bf16_out, void *c, hipStream_t stream)
 {
     const int64_t tm = (M + GEMM_BM - 1) / GEMM_BM, tn = (N + GEMM_BN - 1) / GEMM_BN;
-    if (tm * tn > 0x7FFFFFF)
+    if (tm * tn > MAX_GEMM_TILES)            // checked by the caller
         return hipErrorInvalidValue;
     GemmGrid g;
     g.tiles_m = (uint32_t)tm;

@@ -8,6 +8,34 @@
 
 namespace mxq {
 
+// Grid limits.  A dispatch packet holds the grid size in work-items as a
+// 32-bit field per dimension, and every launcher here uses a one-dimensional
+// grid, so a launch has at most 2^32 - 1 work-items.  The C entry points
+// check the limits below before anything is launched.
+constexpr int64_t MAX_GRID_ITEMS = 0xFFFFFFFF;
+
+// Rows (tokens) of the per-token NVFP4 launches: one 64-lane workgroup per
+// row.  (The split path uses two wavefronts per row, on grids of at most a
+// few tens of thousands of rows.)
+constexpr int64_t MAX_TOKEN_ROWS = MAX_GRID_ITEMS / 64;
+
+// 32 x 128 tiles of the MXFP8 tile launches: one wavefront per tile, in
+// workgroups of up to 8 wavefronts (the last workgroup rounded up).
+constexpr int64_t MAX_MXFP8_TILES = MAX_GRID_ITEMS / 64 - 8;
+inline int64_t mxfp8_tiles(int64_t row_tiles, int64_t cols)
+{
+    return row_tiles * ((cols + 127) / 128);
+}
+
+// 256 x 256 output tiles of the GEMM launches: one 256-thread workgroup per
+// tile, the count rounded up to a multiple of 8 (one share per XCD).
+constexpr int64_t MAX_GEMM_TILES = MAX_GRID_ITEMS / 256 - 8;
+
+// Workgroups (64 lanes each) of the export's amax pass over n_experts scopes
+// of n_per elements per tensor (two tensors when `pair`).
+int64_t scoped_amax_workgroups(int64_t n_experts, int64_t n_per, bool pair);
+constexpr int64_t MAX_SCOPED_AMAX_WORKGROUPS = MAX_GRID_ITEMS / 64;
+
 // Workgroups of `kernel` (launched with `block_threads` threads) that the
 // current device holds at once: compute units x the occupancy the runtime
 // reports for the kernel's register and LDS use.  Cached per kernel and

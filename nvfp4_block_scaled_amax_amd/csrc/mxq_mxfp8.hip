@@ -37,6 +37,7 @@ namespace mxq {
 
 constexpr int TILE_ROWS = 32;
 constexpr int TILE_COLS = 128;                  // per wavefront
+static_assert(TILE_ROWS == 32 && TILE_COLS == 128, "mxfp8_tiles counts 32 x 128 tiles");
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
@@ -515,7 +516,7 @@ static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint
                              uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
     const int64_t wgs = (waves + WPW - 1) / WPW;
-    if (wgs > 0x7FFFFFFF)
+    if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER>), dim3((unsigned)wgs),
                        dim3(64 * WPW), 0, stream, G, rc, rs, cc, cs);
@@ -560,7 +561,7 @@ static hipError_t launch_qdq_wpw(const Geometry &G, int64_t waves, uint8_t *rc, 
                                  uint16_t *dq, hipStream_t stream)
 {
     const int64_t wgs = (waves + WPW - 1) / WPW;
-    if (wgs > 0x7FFFFFFF)
+    if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((mxfp8_row_qdq_kernel<ROW, WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
                        stream, G, rc, rs, dq);
@@ -588,7 +589,7 @@ static hipError_t launch_ocp(const Geometry &G, int64_t waves, uint8_t *rc, uint
                              uint8_t *cc, uint8_t *cs, hipStream_t stream)
 {
     const int64_t wgs = (waves + 3) / 4;
-    if (wgs > 0x7FFFFFFF)
+    if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((mxfp8_ocp_kernel<ROW, COL, 4>), dim3((unsigned)wgs), dim3(256), 0, stream,
                        G, rc, rs, cc, cs);
@@ -615,7 +616,7 @@ hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint
                nullptr, 0};
     const int64_t waves = rows / TILE_ROWS * G.nct;         // rows % 32 == 0: checked by the caller
     const int64_t wgs = (waves + 3) / 4;
-    if (wgs > 0x7FFFFFFF)
+    if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
         return hipErrorInvalidValue;
     if (rc)
         hipLaunchKernelGGL((mxfp8_colt_kernel<true, 4>), dim3((unsigned)wgs), dim3(256), 0,
@@ -631,12 +632,14 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
                                 uint8_t *cc, uint8_t *cs, int64_t *P,
                                 const int64_t *row_tokens, int64_t n_tokens, hipStream_t stream)
 {
+    const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
+    if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
                        total_rows, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
                n_groups, row_tokens, n_tokens};
     if (row_tokens)

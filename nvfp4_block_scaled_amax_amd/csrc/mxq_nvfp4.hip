@@ -617,6 +617,13 @@ __global__ void __launch_bounds__(WG_THREADS) nvfp4_token_long_kernel(
 constexpr int AMAX_THREADS = 64;                            // one wavefront per workgroup
 constexpr int AMAX_LOADS = 8;                               // 16-byte loads per thread
 constexpr int64_t AMAX_CHUNK = AMAX_THREADS * 8 * AMAX_LOADS;   // elements per workgroup
+static_assert(AMAX_THREADS == 64, "scoped_amax_workgroups counts 64-lane workgroups");
+
+int64_t scoped_amax_workgroups(int64_t n_experts, int64_t n_per, bool pair)
+{
+    const int64_t n_scope = pair ? 2 * n_per : n_per;
+    return (n_scope + AMAX_CHUNK - 1) / AMAX_CHUNK * n_experts;
+}
 
 // Workgroup w reduces chunk w % chunks of scope w / chunks into partial[w]
 // (BF16 magnitude bits as u32).  A scope is tensor a's slice
@@ -725,7 +732,8 @@ template <bool SCATTER, bool DQ = false>
 static hipError_t launch_rows(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                               uint8_t *bs, float *ts, Dest dst, hipStream_t stream)
 {
-    // rows < 2^31: checked by the caller.
+    if (rows > MAX_TOKEN_ROWS)          // checked by the caller
+        return hipErrorInvalidValue;
     const int64_t nblk = cols >> 4;
     const int64_t nb = (nblk + 63) / 64;
     const bool full = nblk == 64 * nb;
@@ -851,6 +859,10 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
     const int64_t n_per = rows * cols;
     const int64_t n_scope = up ? 2 * n_per : n_per;
     const int64_t chunks = (n_scope + AMAX_CHUNK - 1) / AMAX_CHUNK;
+    // Grid limits (checked by the caller): chunks * n_experts and n_experts
+    // workgroups of 64 lanes.
+    if (chunks * n_experts > MAX_SCOPED_AMAX_WORKGROUPS || n_experts > MAX_GRID_ITEMS / 64)
+        return hipErrorInvalidValue;
     uint32_t *partial = reinterpret_cast<uint32_t *>(gc);
     hipLaunchKernelGGL(scope_amax_kernel, dim3((unsigned)(chunks * n_experts)), dim3(AMAX_THREADS),
                        0, stream, gate, up, n_per, chunks, partial);

@@ -159,6 +159,61 @@ def test_validation_before_any_device_call():
         mxq.MXQ_ERR_ALIGN
 
 
+def test_grid_limits_are_size_errors():
+    """Sizes whose launch would exceed one grid's 2^32 - 1 work-items are
+    MXQ_ERR_SIZE before any device call; one below each limit passes the size
+    checks and fails only at the device-memory check (the pointers are fake)."""
+    B1, B2, B3, B4, B5 = (A * k for k in (2, 3, 4, 5, 6))
+    n = mxq.mxq_nvfp4_quantize_per_token
+    assert status_of(n, A, 1 << 26, 16, B1, B2, B3, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(n, A, (1 << 26) - 1, 16, B1, B2, B3, 0) == mxq.MXQ_ERR_DEVICE
+    qd = mxq.mxq_quantize_dequant_bf16
+    assert status_of(qd, mxq.MXQ_FMT_NVFP4, A, 1 << 26, 16, B1, B2, B3, B4, 0) == \
+        mxq.MXQ_ERR_SIZE
+    # MXFP8 tiles: ceil(rows/32) * ceil(cols/128) <= 2^26 - 9.
+    q = mxq.mxq_mxfp8_quantize_rowcol
+    top = (1 << 26) - 9
+    assert status_of(q, A, 32 * (top + 1), 128, B1, B2, B3, B4, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(q, A, 32 * top, 128, B1, B2, B3, B4, 0) == mxq.MXQ_ERR_DEVICE
+    assert status_of(q, A, 32 * ((top + 1) // 2 + 1), 256, B1, B2, None, None, 0) == \
+        mxq.MXQ_ERR_SIZE
+    ct = mxq.mxq_mxfp8_quantize_rowcol_t
+    assert status_of(ct, A, 32 * (top + 1), 128, None, None, B3, B4, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(qd, mxq.MXQ_FMT_MXFP8_ROW, A, 32 * (top + 1), 128, B1, B2, None, B3, 0) \
+        == mxq.MXQ_ERR_SIZE
+    g = mxq.mxq_grouped_quantize
+    out8 = {"row_codes": B1, "row_scales": B2, "col_codes": B3, "col_scales": B4,
+            "col_scale_offsets": B5}
+    # row tiles with a columnwise copy: total_rows / 32 + n_groups
+    assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 32 * (top - 9), 128, A * 7, 10, out8, 0) \
+        == mxq.MXQ_ERR_SIZE
+    assert status_of(g, mxq.MXQ_FMT_MXFP8_ROWCOL, A, 32 * (top - 9), 128, A * 7, 9, out8, 0) \
+        == mxq.MXQ_ERR_DEVICE
+    assert status_of(g, mxq.MXQ_FMT_NVFP4, A, 1 << 26, 16, A * 7, 2,
+                     {"codes": B1, "block_scales": B2, "token_scales": B3}, 0) == \
+        mxq.MXQ_ERR_SIZE
+    gd = mxq.mxq_grouped_quantize_dispatch
+    assert status_of(gd, mxq.MXQ_FMT_NVFP4, A, 1 << 26, 16, 1, A * 7, None, 1 << 26, None, 0,
+                     {"codes": B1, "block_scales": B2, "token_scales": B3}, 0) == \
+        mxq.MXQ_ERR_SIZE
+    # GEMM tiles: ceil(M/256) * ceil(N/256) <= 2^24 - 9.
+    gm = mxq.mxq_mxfp8_gemm
+    assert status_of(gm, A, B1, B2, B3, 256 * ((1 << 24) - 8), 256, 128, 0, B4, 0) == \
+        mxq.MXQ_ERR_SIZE
+    assert status_of(gm, A, B1, B2, B3, 256 * ((1 << 24) - 9), 256, 128, 0, B4, 0) == \
+        mxq.MXQ_ERR_DEVICE
+    ng = mxq.mxq_nvfp4_gemm
+    assert status_of(ng, A, B1, B2, 1, B3, B4, B5, 1, 256 * ((1 << 24) - 8), 256, 64, 0,
+                     A * 7, 0) == mxq.MXQ_ERR_SIZE
+    # Export: n_experts < 2^26 (with fewer than 2^36 elements this also keeps
+    # the amax pass's ceil(scope / 4096) * n_experts chunks below 2^26).
+    p = mxq.mxq_nvfp4_quantize_gateup_pair
+    assert status_of(p, A, None, 1 << 26, 1, 16, B1, B2, None, None, B3, 0) == \
+        mxq.MXQ_ERR_SIZE
+    assert status_of(p, A, None, (1 << 26) - 1, 1, 16, B1, B2, None, None, B3, 0) == \
+        mxq.MXQ_ERR_DEVICE
+
+
 def test_fake_device_pointers_rejected_without_gpu():
     """Well-formed arguments that are not device memory fail host-side."""
     import torch
