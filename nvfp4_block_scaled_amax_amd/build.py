@@ -29,17 +29,19 @@ def sources():
         sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def command(out: str = LIB):
-    return ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def command(out: str = LIB, extra_flags=(), opt: str = "-O3"):
+    """The hipcc command.  extra_flags: more flags (the host-sanitizer test
+    passes host-only sanitizer flags, each behind -Xarch_host)."""
+    return ["hipcc", f"--offload-arch={ARCH}", opt, "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-fno-honor-nans", "-mno-amdgpu-ieee",
+            "-fno-honor-nans", "-mno-amdgpu-ieee", *extra_flags,
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *sources(), "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = command(LIB + ".tmp")
+def build(verbose: bool = False, out: str = LIB, extra_flags=(), opt: str = "-O3") -> str:
+    cmd = command(out + ".tmp", extra_flags, opt)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +53,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -24,11 +24,12 @@ _LIB = os.path.join(_HERE, "libmxq_oracle.so")
 _lib = None
 
 
-def build(verbose: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
     """Compile mxq_oracle.c with gcc into libmxq_oracle.so (no fast-math, no
-    FMA contraction, OpenMP over rows)."""
+    FMA contraction, OpenMP over rows).  extra_flags: more gcc flags (the
+    sanitizer test builds an instrumented copy)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra", *extra_flags,
            src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
