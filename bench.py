@@ -150,8 +150,14 @@ def build_exp(torch, E, W, legs, dev, empty):
     """NVFP4 export of 128 experts (gate/up pairs + down), + dequant."""
     gate, up, down = W.config4()
     g, u, dn = dev(gate), dev(up), dev(down)
-    del gate, up, down
     NE, I, H = 128, 768, 2048
+    # Each scope's largest magnitude as BF16 bits (an integer max), for the
+    # export variant that takes the scope amax from the caller.
+    amax_pair = np.maximum((gate.reshape(NE, -1) & 0x7FFF).max(1),
+                           (up.reshape(NE, -1) & 0x7FFF).max(1)).astype(np.uint16)
+    amax_down = (down.reshape(NE, -1) & 0x7FFF).max(1).astype(np.uint16)
+    ap, ad = dev(amax_pair), dev(amax_down)
+    del gate, up, down
     ng = NE * I * H
     gc, gb, uc, ub = empty((NE, I, H // 2)), empty((NE, I, H // 16)), empty((NE, I, H // 2)), \
         empty((NE, I, H // 16))
@@ -171,6 +177,18 @@ def build_exp(torch, E, W, legs, dev, empty):
                     2 * ng, down_out, ng,
                     ["scope_amax_kernel", "scope_finalize_kernel", "nvfp4_scoped_kernel"],
                     "NVFP4 down export 128x2048x768"))
+
+    _SHARED["exp_amax_legs"] = [
+        Leg("nvfp4_export_gateup_amax",
+            lambda: E.mxq_nvfp4_quantize_gateup_pair_amax(g, u, ap, NE, I, H, gc, gb, uc, ub, sp),
+            2 * 2 * ng + 2 * NE, pair_out, 2 * ng, ["scope_scale_from_amax_kernel",
+                                                    "nvfp4_scoped_kernel"],
+            "NVFP4 gate/up export 128x2x768x2048, scope amax supplied (one read)"),
+        Leg("nvfp4_export_down_amax",
+            lambda: E.mxq_nvfp4_quantize_gateup_pair_amax(dn, None, ad, NE, H, I, dc, db, None,
+                                                          None, sd),
+            2 * ng + 2 * NE, down_out, ng, ["scope_scale_from_amax_kernel", "nvfp4_scoped_kernel"],
+            "NVFP4 down export 128x2048x768, scope amax supplied (one read)")]
 
     def exp_dequant():
         E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, gc, gb, sp, I, NE * I, H, yg)
@@ -355,32 +373,73 @@ def time_graph(torch, launches, n_launch, samples):
     return out
 
 
-def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None):
+_FLOORS = {}
+
+
+def copy_floor(torch, E, rbytes, wbytes, sets, graph, n_launch=CFG_LAUNCHES, warmup=CFG_WARMUP):
+    """The copy floor of a workload: mxq_copy_floor (a kernel that only reads
+    rbytes and writes wbytes, no arithmetic) timed with the workload's own
+    protocol and buffer rotation.  Returns (eager ms list, graph ms list or
+    None); cached per byte counts."""
+    key = (rbytes, wbytes, sets, graph, n_launch)
+    if key in _FLOORS:
+        return _FLOORS[key]
+    r16, w16 = -(-rbytes // 16) * 16, -(-wbytes // 16) * 16
+    bufs = [(torch.empty(r16, dtype=torch.uint8, device="cuda"),
+             torch.empty(w16, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+    launches = [(lambda b=b: E.mxq_copy_floor(b[0], r16, b[1], w16)) for b in bufs]
+    ms = time_launches(torch, launches, n_launch, warmup, CFG_SAMPLES)
+    gms = time_graph(torch, launches, n_launch, CFG_SAMPLES) if graph else None
+    del bufs, launches
+    torch.cuda.empty_cache()
+    _FLOORS[key] = (ms, gms)
+    return _FLOORS[key]
+
+
+def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None, floor=None):
+    """One config's record.  floor: (eager, graph) ms lists of the copy floor of
+    the same read and write bytes: "vs_copy_floor" is the floor's time over the
+    kernel's (1.0 = as fast as a plain copy of those bytes)."""
     med, mn = float(np.median(ms_list)), float(np.min(ms_list))
     gbs = nbytes / (med * 1e-3) / 1e9
     rec = {"desc": desc, "kernels": kernels, "ms_median": round(med, 5),
            "ms_min": round(mn, 5), "bytes": nbytes, "GB_s": round(gbs, 1),
            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
            "elements_per_s": round(elems / (med * 1e-3), 1), "buffer_sets": sets}
+    if floor is not None:
+        fmed = float(np.median(floor[0]))
+        fgbs = nbytes / (fmed * 1e-3) / 1e9
+        rec.update({"copy_floor_ms": round(fmed, 5), "copy_floor_GB_s": round(fgbs, 1),
+                    "copy_floor_pct_hbm_peak": round(100 * fgbs / HBM_PEAK_GBS, 2),
+                    "vs_copy_floor": round(fmed / med, 4)})
     if graph_ms is not None:
         gmed = float(np.median(graph_ms))
         ggbs = nbytes / (gmed * 1e-3) / 1e9
         rec.update({"graph_ms_median": round(gmed, 5), "graph_GB_s": round(ggbs, 1),
                     "graph_pct_hbm_peak": round(100 * ggbs / HBM_PEAK_GBS, 2)})
+        if floor is not None and floor[1] is not None:
+            fg = float(np.median(floor[1]))
+            rec.update({"graph_copy_floor_ms": round(fg, 5),
+                        "graph_vs_copy_floor": round(fg / gmed, 4)})
     return name, rec
 
 
-def config_timings(torch, E, W, legs, log):
+def config_timings(torch, E, W, legs, log, only=None):
     """The per-config protocol: hipEvents around 50 back-to-back launches per
     sample (5 samples after 10 warm-up launches), median and minimum per launch.
     Configs under 256 MB rotate distinct buffer sets totalling over 1 GiB, so
     every launch reads inputs that are not in the MALL; C5 is over 1 GiB
-    itself.  C2b and C3 (and C5) are the shapes the 70% bar applies to."""
+    itself.  C2b and C3 (and C5) are the shapes the 70% bar applies to.  Each
+    config is timed beside the copy floor of its read and write bytes.
+    only: a set of config names to time (all when None)."""
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     empty = lambda shape, dt=torch.uint8: torch.empty(shape, dtype=dt, device="cuda")
     res = {}
+    sel = (lambda name: True) if only is None else (lambda name: name in only)
 
     def mxfp8_cfg(name, rows, cols, x_np):
+        if not sel(name):
+            return
         n = rows * cols
         nbytes = 2 * n + 2 * n + 2 * (n // 32)
         sets = -(-ROTATE_BYTES // nbytes)
@@ -391,11 +450,12 @@ def config_timings(torch, E, W, legs, log):
                                                                b[4])) for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
-        k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
-                          ["mxfp8_tile_kernel"], gms)
-        res[k] = v
         del bufs, launches, x0
         torch.cuda.empty_cache()
+        fl = copy_floor(torch, E, 2 * n, 2 * n + 2 * (n // 32), sets, True)
+        k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
+                          ["mxfp8_tile_kernel"], gms, fl)
+        res[k] = v
 
     for mode in W.MXFP8_MODES:
         mxfp8_cfg(f"C2a_{mode}", 2048, 2048, W.config2_activation(mode))
@@ -404,44 +464,57 @@ def config_timings(torch, E, W, legs, log):
 
     rows, cols = 8192, 2048
     n = rows * cols
-    q_bytes = 2 * n + n // 2 + n // 16 + 4 * rows
-    d_bytes = n // 2 + n // 16 + 4 * rows + 2 * n
-    sets = -(-ROTATE_BYTES // q_bytes)
-    x0 = dev(W.config3())
-    bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols // 2)), empty((rows, cols // 16)),
-             empty((rows,), torch.float32), empty((rows, cols), torch.bfloat16))
-            for k in range(sets)]
-    q = [(lambda b=b: E.mxq_nvfp4_quantize_per_token(b[0], rows, cols, b[1], b[2], b[3]))
-         for b in bufs]
-    ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
-    gms = time_graph(torch, q, CFG_LAUNCHES, CFG_SAMPLES)
-    k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
-                      ["nvfp4_token_split_kernel"], gms)
-    res[k] = v
-    d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows, cols,
-                                             b[4])) for b in bufs]
-    ms = time_launches(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
-    gms = time_graph(torch, d, CFG_LAUNCHES, CFG_SAMPLES)
-    k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", ms, d_bytes, n, sets,
-                      ["dequant_nvfp4_kernel"], gms)
-    res[k] = v
-    del bufs, q, d, x0
-    torch.cuda.empty_cache()
-    log("C3 timed")
+    q_out = n // 2 + n // 16 + 4 * rows
+    q_bytes = 2 * n + q_out
+    d_bytes = q_out + 2 * n
+    if sel("C3_nvfp4") or sel("C3_dequant"):
+        sets = -(-ROTATE_BYTES // q_bytes)
+        x0 = dev(W.config3())
+        bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols // 2)),
+                 empty((rows, cols // 16)), empty((rows,), torch.float32),
+                 empty((rows, cols), torch.bfloat16)) for k in range(sets)]
+        q = [(lambda b=b: E.mxq_nvfp4_quantize_per_token(b[0], rows, cols, b[1], b[2], b[3]))
+             for b in bufs]
+        ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        gms = time_graph(torch, q, CFG_LAUNCHES, CFG_SAMPLES)
+        d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows,
+                                                 cols, b[4])) for b in bufs]
+        dms = time_launches(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
+        dgms = time_graph(torch, d, CFG_LAUNCHES, CFG_SAMPLES)
+        del bufs, q, d, x0
+        torch.cuda.empty_cache()
+        if sel("C3_nvfp4"):
+            fl = copy_floor(torch, E, 2 * n, q_out, sets, True)
+            k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
+                              ["nvfp4_token_split_kernel"], gms, fl)
+            res[k] = v
+        if sel("C3_dequant"):
+            fl = copy_floor(torch, E, q_out, 2 * n, sets, True)
+            k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", dms, d_bytes, n,
+                              sets, ["dequant_nvfp4_kernel"], dgms, fl)
+            res[k] = v
+        log("C3 timed")
 
     by_name = {l.name: l for l in legs}
     for leg, cfg in (("grouped_mxfp8_rowcol", "C5_mxfp8"), ("grouped_nvfp4", "C5_nvfp4"),
                      ("grouped_dequant_mxfp8", "C5_dequant_mxfp8"),
                      ("grouped_dequant_nvfp4", "C5_dequant_nvfp4"),
                      ("nvfp4_export_gateup", "C4_gateup"), ("nvfp4_export_down", "C4_down")):
-        if leg in by_name:
+        if leg in by_name and sel(cfg):
             l = by_name[leg]
             ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
-            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+            fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
+            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
+            res[k] = v
+    for l, cfg in zip(_SHARED.get("exp_amax_legs", []), ("C4_gateup_amax", "C4_down_amax")):
+        if sel(cfg):
+            ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
+            fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
+            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
             res[k] = v
     log("C4/C5 timed")
 
-    if "grouped_mxfp8_rowcol" in by_name:
+    if "grouped_mxfp8_rowcol" in by_name and only is None:
         res.update(dispatch_timings(torch, E, W, dev, empty))
         log("C5 dispatch timed")
         res.update(qdq_timings(torch, E, W, dev, empty))
@@ -500,12 +573,13 @@ def qdq_small_timings(torch, E, W, dev, empty):
                     for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
-        kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_split_kernel"
-        k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
-                          n, sets, [kern], gms)
-        res[k] = v
         del bufs, launches, x0
         torch.cuda.empty_cache()
+        fl = copy_floor(torch, E, 2 * n, out_b, sets, True)
+        kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_split_kernel"
+        k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
+                          n, sets, [kern], gms, fl)
+        res[k] = v
     return res
 
 
@@ -601,7 +675,8 @@ def qdq_timings(torch, E, W, dev, empty):
     res = {}
     for l, cfg in zip(legs, ("C5_qdq_mxfp8", "C5_qdq_nvfp4")):
         ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
-        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+        fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
         res[k] = v
     del legs
     torch.cuda.empty_cache()
@@ -654,7 +729,8 @@ def dispatch_timings(torch, E, W, dev, empty):
     res = {}
     for l, cfg in zip(legs, ("C5_dispatch_mxfp8", "C5_dispatch_nvfp4", "C5_gather_torch")):
         ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
-        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels)
+        fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
         res[k] = v
     return res
 
@@ -799,6 +875,12 @@ def main():
                          "dequant legs, 'gemm' the dense-layer GEMMs; the first two replace legs "
                          "of the default step (the separate gather; quantize followed by "
                          "dequant) and the GEMMs consume its outputs, so none is part of it")
+    ap.add_argument("--config-only", default=None,
+                    help="comma list of config names (C2a_<mode>, C2b_<mode>, C3_nvfp4, "
+                         "C3_dequant, C4_gateup, C4_down, C4_gateup_amax, C4_down_amax, C5_mxfp8, C5_nvfp4, C5_dequant_mxfp8, "
+                         "C5_dequant_nvfp4): time only these, each beside its copy floor, and "
+                         "print them as one JSON line (no step, no CPU baseline); for "
+                         "profiling one shape per run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also time a plain elementwise copy of this many MiB (int32 bitwise "
                          "not, reads and writes each byte once), reported apart from the step, "
@@ -843,6 +925,18 @@ def main():
 
     mxq.lib()
     torch.cuda.set_device(0)
+    if args.config_only:
+        only = set(args.config_only.split(","))
+        need = set()
+        if only & {"C4_gateup", "C4_down", "C4_gateup_amax", "C4_down_amax"}:
+            need.add("exp")
+        if any(c.startswith("C5_") for c in only):
+            need.add("grp")
+        legs = build_legs(torch, mxq, api, W, log,
+                          want=lambda g: g in need and g not in ("act", "wgt"))
+        res = config_timings(torch, mxq, W, legs, log, only=only)
+        print(json.dumps({"configs": res, "csrc_digest": csrc_digest()}), flush=True)
+        return
     t_gen = time.perf_counter()
     groups = set(args.groups.split(","))
     legs = build_legs(torch, mxq, api, W, log, want=lambda g: g in groups)
@@ -952,7 +1046,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->mxfp8|nvfp4",
         "data": "synthetic",
         "config": {"workload": "moe-layer quantize step: MXFP8 row+col 2048x2048 + 8192x2048, "
                                "per-token NVFP4 8192x2048 + dequant, NVFP4 export of 128 "

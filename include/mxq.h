@@ -226,6 +226,30 @@ int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up,
                                    float *scope_scales, void *stream);
 
 /*
+ * The weight export of mxq_nvfp4_quantize_gateup_pair with each scope's amax
+ * supplied by the caller, which skips the export's first read of the weights
+ * (the amax pass).  The gate/up pairing paragraph fixes the scope and its one
+ * FP32 scale; whoever last wrote the weights (for instance the optimizer step)
+ * can reduce the scope amax on the way and hand it over here.
+ *
+ *   scope_amax  [n_experts] BF16 bit patterns (device memory, 2-byte
+ *               aligned): A_e, the largest magnitude in scope e (the sign bit
+ *               is ignored).  s_e = fp32(A_e / 2688) is written to
+ *               scope_scales and every tensor of the scope is quantized
+ *               under it.
+ *   Every other argument, layout, alignment and limit as
+ *   mxq_nvfp4_quantize_gateup_pair.  With A_e the true amax of scope e the
+ *   bytes equal that call's; with any other A_e they are the scope quantized
+ *   under s_e (codes saturate where A_e is too small).
+ */
+int mxq_nvfp4_quantize_gateup_pair_amax(const uint16_t *gate, const uint16_t *up,
+                                        const uint16_t *scope_amax, int64_t n_experts,
+                                        int64_t rows, int64_t cols, uint8_t *gate_codes,
+                                        uint8_t *gate_block_scales, uint8_t *up_codes,
+                                        uint8_t *up_block_scales, float *scope_scales,
+                                        void *stream);
+
+/*
  * Dequantize to BF16: the exact low-precision operands made by the calls
  * above, decoded and rounded once to BF16.  Implements the dequantized-
  * backward paragraph (backward GEMMs consume BF16 dequantizations of the exact
@@ -397,6 +421,25 @@ int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens,
                                   const int64_t *row_tokens, int64_t total_rows,
                                   const int64_t *seg_offsets, int64_t n_groups,
                                   const mxq_grouped_out *out, void *stream);
+
+/*
+ * Measurement reference, not an operation of the pages: reads src_bytes of
+ * src and writes dst_bytes of dst with no arithmetic beyond an XOR fold, in
+ * the quantizers' launch style (one-shot grid, 16-byte coalesced accesses).
+ * Timed on a workload's read and write byte counts it gives the floor that
+ * any kernel moving exactly those bytes meets on the device, against which
+ * the quantizers' times are reported beside the HBM peak.
+ *   With n_r = src_bytes / 16 and n_w = dst_bytes / 16 chunks of 16 bytes:
+ *   n_r >= n_w: dst chunk j = XOR of src chunks j + i n_w (every i with
+ *               j + i n_w < n_r);
+ *   n_r <  n_w: dst chunk j = src chunk floor(j m / 2^32), where
+ *               m = floor(n_r 2^32 / n_w).
+ *   src, dst device memory of the current device, 16-byte aligned, not
+ *   overlapping; src_bytes and dst_bytes positive multiples of 16
+ *   (MXQ_ERR_SHAPE) of at most 2^35 (MXQ_ERR_SIZE).
+ */
+int mxq_copy_floor(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes,
+                   void *stream);
 
 /* A static, human-readable message for a status code. */
 const char *mxq_status_string(int status);

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     MXQ_OUT_BF16, MXQ_OUT_F32, mxq_mxfp8_gemm, mxq_nvfp4_gemm, mxq_mxfp8_quantize_ocp_floor,
     mxq_mxfp8_quantize_rowcol_t, mxq_nvfp4_quantize_per_token_approx,
     MXQError, lib, mxq_dequantize_bf16, mxq_grouped_out, mxq_grouped_quantize,
-    mxq_grouped_quantize_dispatch,
+    mxq_grouped_quantize_dispatch, mxq_copy_floor,
     mxq_mxfp8_quantize_rowcol, mxq_nvfp4_quantize_gateup_pair, mxq_nvfp4_quantize_per_token,
+    mxq_nvfp4_quantize_gateup_pair_amax,
     mxq_quantize_dequant_bf16, mxq_status_string, mxq_version)

@@ -14,7 +14,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmxq.so")
+# MXQ_LIB_PATH selects another build of the same library (the host-sanitizer
+# test loads a build instrumented with AddressSanitizer and UBSan).
+LIB_PATH = os.environ.get("MXQ_LIB_PATH") or os.path.join(HERE, "libmxq.so")
 
 MXQ_OK = 0
 MXQ_ERR_NULL = 1
@@ -39,6 +41,7 @@ EXPORTS = (
     "mxq_mxfp8_quantize_rowcol",
     "mxq_nvfp4_quantize_per_token",
     "mxq_nvfp4_quantize_gateup_pair",
+    "mxq_nvfp4_quantize_gateup_pair_amax",
     "mxq_dequantize_bf16",
     "mxq_quantize_dequant_bf16",
     "mxq_mxfp8_gemm",
@@ -48,6 +51,7 @@ EXPORTS = (
     "mxq_nvfp4_quantize_per_token_approx",
     "mxq_grouped_quantize",
     "mxq_grouped_quantize_dispatch",
+    "mxq_copy_floor",
     "mxq_status_string",
     "mxq_version",
 )
@@ -83,6 +87,7 @@ def lib():
         "mxq_mxfp8_quantize_rowcol": [P, I64, I64, P, P, P, P, P],
         "mxq_nvfp4_quantize_per_token": [P, I64, I64, P, P, P, P],
         "mxq_nvfp4_quantize_gateup_pair": [P, P, I64, I64, I64, P, P, P, P, P, P],
+        "mxq_nvfp4_quantize_gateup_pair_amax": [P, P, P, I64, I64, I64, P, P, P, P, P, P],
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
@@ -93,6 +98,7 @@ def lib():
         "mxq_grouped_quantize": [I, P, I64, I64, P, I64, ctypes.POINTER(mxq_grouped_out), P],
         "mxq_grouped_quantize_dispatch": [I, P, I64, I64, I64, P, P, I64, P, I64,
                                           ctypes.POINTER(mxq_grouped_out), P],
+        "mxq_copy_floor": [P, I64, P, I64, P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -197,6 +203,17 @@ def mxq_nvfp4_quantize_gateup_pair(gate, up, n_experts, rows, cols, gate_codes,
            "mxq_nvfp4_quantize_gateup_pair")
 
 
+def mxq_nvfp4_quantize_gateup_pair_amax(gate, up, scope_amax, n_experts, rows, cols, gate_codes,
+                                        gate_block_scales, up_codes, up_block_scales,
+                                        scope_scales, stream=None):
+    _check(lib().mxq_nvfp4_quantize_gateup_pair_amax(_ptr(gate), _ptr(up), _ptr(scope_amax),
+                                                     n_experts, rows, cols, _ptr(gate_codes),
+                                                     _ptr(gate_block_scales), _ptr(up_codes),
+                                                     _ptr(up_block_scales), _ptr(scope_scales),
+                                                     _stream(stream)),
+           "mxq_nvfp4_quantize_gateup_pair_amax")
+
+
 def mxq_dequantize_bf16(fmt, codes, scales, fp32_scales, rows_per_fp32_scale, rows, cols, out,
                         stream=None):
     _check(lib().mxq_dequantize_bf16(fmt, _ptr(codes), _ptr(scales), _ptr(fp32_scales),
@@ -243,3 +260,8 @@ def mxq_grouped_quantize_dispatch(fmt, x, n_tokens, cols, top_k, token_rows, row
                                                _ptr(seg_offsets), n_groups, ctypes.byref(out),
                                                _stream(stream)),
            "mxq_grouped_quantize_dispatch")
+
+
+def mxq_copy_floor(src, src_bytes, dst, dst_bytes, stream=None):
+    _check(lib().mxq_copy_floor(_ptr(src), src_bytes, _ptr(dst), dst_bytes, _stream(stream)),
+           "mxq_copy_floor")

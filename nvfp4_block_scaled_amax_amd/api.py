@@ -137,6 +137,29 @@ def nvfp4_quantize_gateup_pair(gate, up=None, stream=None) -> GateUpNVFP4:
     return GateUpNVFP4(gc, gb, uc, ub, sc)
 
 
+def nvfp4_quantize_gateup_pair_amax(gate, up, scope_amax, stream=None) -> GateUpNVFP4:
+    """The export with each scope's amax supplied: scope_amax is a device
+    tensor of n_experts BF16 values (torch.bfloat16 or int16 bits)."""
+    gate = _bf16_bits(gate)
+    E, rows, cols = gate.shape
+    amax = _bf16_bits(scope_amax)
+    if amax.numel() != E:
+        raise ValueError("scope_amax must hold one value per expert")
+    gc = _empty((E, rows, cols // 2), torch.uint8, gate)
+    gb = _empty((E, rows, cols // 16), torch.uint8, gate)
+    uc = ub = None
+    if up is not None:
+        up = _bf16_bits(up)
+        if up.shape != gate.shape:
+            raise ValueError("gate and up must have the same shape")
+        uc = torch.empty_like(gc)
+        ub = torch.empty_like(gb)
+    sc = _empty((E,), torch.float32, gate)
+    B.mxq_nvfp4_quantize_gateup_pair_amax(gate, up, amax, E, rows, cols, gc, gb, uc, ub, sc,
+                                          stream)
+    return GateUpNVFP4(gc, gb, uc, ub, sc)
+
+
 def dequantize_bf16(fmt: int, codes, scales, fp32_scales=None, rows_per_fp32_scale: int = 1,
                     stream=None) -> torch.Tensor:
     """Returns a torch.bfloat16 tensor [rows][cols]."""

@@ -26,6 +26,7 @@ constexpr int64_t MAX_GEMM_K = (int64_t)1 << 23;
 constexpr int64_t MAX_GRID_ROWS = mxq::MAX_TOKEN_ROWS;   // per-token NVFP4: one workgroup per row
 constexpr int64_t MAX_BLOCKS = 0xFFFFFFFF;        // 16-element blocks indexed in 32 bits
 constexpr int64_t MAX_MXFP8_COLS = (int64_t)1 << 26;  // 32-row tile offsets fit 32 bits
+constexpr int64_t MAX_COPY_FLOOR_BYTES = (int64_t)1 << 35;
 
 bool size_ok(int64_t a, int64_t b)
 {
@@ -324,6 +325,46 @@ int mxq_nvfp4_quantize_gateup_pair(const uint16_t *gate, const uint16_t *up, int
                                              scope_scales, (hipStream_t)stream));
 }
 
+int mxq_nvfp4_quantize_gateup_pair_amax(const uint16_t *gate, const uint16_t *up,
+                                        const uint16_t *scope_amax, int64_t n_experts,
+                                        int64_t rows, int64_t cols, uint8_t *gate_codes,
+                                        uint8_t *gate_block_scales, uint8_t *up_codes,
+                                        uint8_t *up_block_scales, float *scope_scales,
+                                        void *stream)
+{
+    if (!gate || !scope_amax || !gate_codes || !gate_block_scales || !scope_scales)
+        return MXQ_ERR_NULL;
+    const bool has_up = up != nullptr;
+    if ((up_codes != nullptr) != has_up || (up_block_scales != nullptr) != has_up)
+        return MXQ_ERR_OFFSETS;
+    if (!size_ok(rows, cols) || n_experts <= 0 || !size_ok(n_experts, rows * cols))
+        return MXQ_ERR_SIZE;
+    if (cols % 16 != 0)
+        return MXQ_ERR_SHAPE;
+    const int64_t n = n_experts * rows * cols;
+    if (n / 16 > MAX_BLOCKS || n_experts > mxq::MAX_GRID_ITEMS / 64)
+        return MXQ_ERR_SIZE;
+    Buf b[8];
+    int k = 0;
+    b[k++] = {gate, 2 * n, 16, false};
+    b[k++] = {scope_amax, 2 * n_experts, 2, false};
+    b[k++] = {gate_codes, n / 2, 16, true};
+    b[k++] = {gate_block_scales, n / 16, 1, true};
+    b[k++] = {scope_scales, 4 * n_experts, 4, true};
+    if (has_up) {
+        b[k++] = {up, 2 * n, 16, false};
+        b[k++] = {up_codes, n / 2, 16, true};
+        b[k++] = {up_block_scales, n / 16, 1, true};
+    }
+    const int st = check_bufs(b, k);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_scoped_amax(gate, up, scope_amax, n_experts, rows, cols,
+                                                  gate_codes, gate_block_scales, up_codes,
+                                                  up_block_scales, scope_scales,
+                                                  (hipStream_t)stream));
+}
+
 int mxq_dequantize_bf16(int fmt, const uint8_t *codes, const uint8_t *scales,
                         const float *fp32_scales, int64_t rows_per_fp32_scale, int64_t rows,
                         int64_t cols, uint16_t *out, void *stream)
@@ -617,6 +658,23 @@ int mxq_grouped_quantize_dispatch(int fmt, const uint16_t *x, int64_t n_tokens, 
     return launched(mxq::launch_mxfp8_grouped(x, total_rows, cols, seg_offsets, n_groups, rc, rs,
                                               cc, cs, P, row_tokens, n_tokens,
                                               (hipStream_t)stream));
+}
+
+int mxq_copy_floor(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes,
+                   void *stream)
+{
+    if (!src || !dst)
+        return MXQ_ERR_NULL;
+    if (src_bytes <= 0 || dst_bytes <= 0 || src_bytes > MAX_COPY_FLOOR_BYTES ||
+        dst_bytes > MAX_COPY_FLOOR_BYTES)
+        return MXQ_ERR_SIZE;
+    if (src_bytes % 16 != 0 || dst_bytes % 16 != 0)
+        return MXQ_ERR_SHAPE;
+    const Buf b[2] = {{src, src_bytes, 16, false}, {dst, dst_bytes, 16, true}};
+    const int st = check_bufs(b, 2);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_copy_floor(src, src_bytes, dst, dst_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

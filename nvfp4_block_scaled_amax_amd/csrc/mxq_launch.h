@@ -100,6 +100,14 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
                                uint8_t *gate_block_scales, uint8_t *up_codes,
                                uint8_t *up_block_scales, float *scope_scales, hipStream_t stream);
 
+// The export's code pass alone, under s_e = fp32(A_e / 2688) from scope
+// amaxes the caller supplies (BF16 bits, [n_experts]).
+hipError_t launch_nvfp4_scoped_amax(const uint16_t *gate, const uint16_t *up,
+                                    const uint16_t *scope_amax, int64_t n_experts, int64_t rows,
+                                    int64_t cols, uint8_t *gate_codes, uint8_t *gate_block_scales,
+                                    uint8_t *up_codes, uint8_t *up_block_scales,
+                                    float *scope_scales, hipStream_t stream);
+
 hipError_t launch_dequant_mxfp8(bool col, const uint8_t *codes, const uint8_t *scales,
                                 int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream);
 
@@ -120,5 +128,11 @@ hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
                              const uint8_t *b_block_scales, const float *b_scales,
                              int64_t rows_per_b, int64_t M, int64_t N, int64_t K, bool bf16_out,
                              void *c, hipStream_t stream);
+
+// Reads src_bytes and writes dst_bytes (both multiples of 16, at most 2^35)
+// with an XOR fold or spread and no other arithmetic: the measurement
+// reference of mxq_copy_floor.
+hipError_t launch_copy_floor(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes,
+                             hipStream_t stream);
 
 }  // namespace mxq

@@ -666,6 +666,16 @@ __global__ void __launch_bounds__(64) scope_finalize_kernel(const uint32_t *__re
         scope_s[e] = div2688(u2f(m << 16));
 }
 
+// Scope scales from amaxes the caller supplies (BF16 magnitudes, the sign bit
+// ignored): one lane per scope.
+__global__ void __launch_bounds__(64) scope_scale_from_amax_kernel(
+    const uint16_t *__restrict__ amax, int64_t n_experts, float *__restrict__ scope_s)
+{
+    const int64_t e = (int64_t)wg_id() * 64 + lane_id();
+    if (e < n_experts)
+        scope_s[e] = div2688(u2f((uint32_t)(amax[e] & 0x7FFFu) << 16));
+}
+
 // Flat export pass over one tensor of nblk blocks; block j belongs to scope
 // j / bps.  Each wavefront takes 64 SCOPED_NB consecutive blocks, lane l the
 // blocks base + l + 64 k.  When the wavefront's span lies in one scope (the
@@ -848,6 +858,36 @@ hipError_t launch_nvfp4_dispatch(const uint16_t *x, int64_t n_tokens, int64_t co
                              Dest{token_rows, top_k, out_rows, nullptr}, stream);
 }
 
+// The code pass of the export over both tensors under scope_scales.
+static void launch_scoped_codes(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
+                                int64_t n_per, uint8_t *gc, uint8_t *gbs, uint8_t *uc,
+                                uint8_t *ubs, const float *scope_scales, hipStream_t stream)
+{
+    // Blocks in all below 2^32: checked by the caller.
+    const int64_t nblk = n_experts * n_per / 16;
+    const Div bps = make_div((uint32_t)(n_per / 16));
+    const int64_t per_wg = 64 * SCOPED_NB * ROWS_PER_WG;
+    const dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg)), block(WG_THREADS);
+    hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, gate, nblk, bps,
+                       scope_scales, gc, gbs);
+    if (up)
+        hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, up, nblk, bps,
+                           scope_scales, uc, ubs);
+}
+
+hipError_t launch_nvfp4_scoped_amax(const uint16_t *gate, const uint16_t *up,
+                                    const uint16_t *scope_amax, int64_t n_experts, int64_t rows,
+                                    int64_t cols, uint8_t *gc, uint8_t *gbs, uint8_t *uc,
+                                    uint8_t *ubs, float *scope_scales, hipStream_t stream)
+{
+    if (n_experts > MAX_GRID_ITEMS / 64)    // checked by the caller
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scope_scale_from_amax_kernel, dim3((unsigned)((n_experts + 63) / 64)),
+                       dim3(64), 0, stream, scope_amax, n_experts, scope_scales);
+    launch_scoped_codes(gate, up, n_experts, rows * cols, gc, gbs, uc, ubs, scope_scales, stream);
+    return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t n_experts,
                                int64_t rows, int64_t cols, uint8_t *gc, uint8_t *gbs,
                                uint8_t *uc, uint8_t *ubs, float *scope_scales,
@@ -868,16 +908,7 @@ hipError_t launch_nvfp4_scoped(const uint16_t *gate, const uint16_t *up, int64_t
                        0, stream, gate, up, n_per, chunks, partial);
     hipLaunchKernelGGL(scope_finalize_kernel, dim3((unsigned)n_experts), dim3(64), 0, stream,
                        (const uint32_t *)partial, chunks, scope_scales);
-    // Blocks in all below 2^32: checked by the caller.
-    const int64_t nblk = n_experts * n_per / 16;
-    const Div bps = make_div((uint32_t)(n_per / 16));
-    const int64_t per_wg = 64 * SCOPED_NB * ROWS_PER_WG;
-    const dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg)), block(WG_THREADS);
-    hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, gate, nblk, bps,
-                       (const float *)scope_scales, gc, gbs);
-    if (up)
-        hipLaunchKernelGGL(nvfp4_scoped_kernel, grid, block, 0, stream, up, nblk, bps,
-                           (const float *)scope_scales, uc, ubs);
+    launch_scoped_codes(gate, up, n_experts, n_per, gc, gbs, uc, ubs, scope_scales, stream);
     return hipGetLastError();
 }
 

@@ -75,6 +75,16 @@ def test_validation_before_any_device_call():
     assert status_of(p, A, A, 0, 4, 16, A, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
     assert status_of(p, A, A, 2, 4, 8, A, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
 
+    pa = mxq.mxq_nvfp4_quantize_gateup_pair_amax
+    assert status_of(pa, A, A, None, 2, 4, 16, A, A, A, A, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(pa, A, A, A, 2, 4, 16, A, A, None, A, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(pa, A, None, A, 2, 4, 16, A, A, A, None, A, 0) == mxq.MXQ_ERR_OFFSETS
+    assert status_of(pa, A, A, A, 0, 4, 16, A, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(pa, A, None, A, 1 << 26, 1, 16, A, A, None, None, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(pa, A, A, A, 2, 4, 8, A, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(pa, A, A, A + 1, 2, 4, 16, A, A, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(pa, A, A, A, 2, 4, 16, A + 8, A, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+
     d = mxq.mxq_dequantize_bf16
     assert status_of(d, 0, A, A, None, 0, 32, 32, A, 0) == mxq.MXQ_ERR_ARG
     assert status_of(d, mxq.MXQ_FMT_NVFP4, A, A, None, 1, 32, 32, A, 0) == mxq.MXQ_ERR_NULL
@@ -212,6 +222,15 @@ def test_grid_limits_are_size_errors():
         mxq.MXQ_ERR_SIZE
     assert status_of(p, A, None, (1 << 26) - 1, 1, 16, B1, B2, None, None, B3, 0) == \
         mxq.MXQ_ERR_DEVICE
+
+
+def test_copy_floor_validation():
+    cf = mxq.mxq_copy_floor
+    assert status_of(cf, None, 16, A, 16, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(cf, A, 0, A * 2, 16, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(cf, A, 16, A * 2, (1 << 35) + 16, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(cf, A, 24, A * 2, 16, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(cf, A + 8, 16, A * 2, 16, 0) == mxq.MXQ_ERR_ALIGN
 
 
 def test_fake_device_pointers_rejected_without_gpu():

@@ -348,6 +348,50 @@ def check_pair(orc, gate, up, name):
     return r, (gc, gb, uc, ub, s)
 
 
+def scope_amax_bits(gate, up=None):
+    """Each scope's largest magnitude as BF16 bits (positive BF16 values order
+    like their bit patterns, so this is an integer max)."""
+    E = gate.shape[0]
+    m = (gate.reshape(E, -1) & 0x7FFF).max(axis=1)
+    if up is not None:
+        m = np.maximum(m, (up.reshape(E, -1) & 0x7FFF).max(axis=1))
+    return m.astype(np.uint16)
+
+
+def check_pair_amax(orc, gate, up, amax, name):
+    """The export with caller-supplied scope amaxes: every scope quantized under
+    s_e = fp32(amax_e / 2688) (the oracle's quantize under a given scale)."""
+    announce(f"nvfp4 gateup amax {name} gate={gate.shape}")
+    r = api.nvfp4_quantize_gateup_pair_amax(dev(gate), None if up is None else dev(up), dev(amax))
+    torch.cuda.synchronize()
+    sc = host(r.scope_scales)
+    for e in range(gate.shape[0]):
+        s = orc.nvfp4_scale(float(orc.bf16_value(int(amax[e]) & 0x7FFF)))
+        assert sc[e].view(np.uint32) == np.float32(s).view(np.uint32), (name, e)
+        for src, codes, bs in ((gate, r.gate_codes, r.gate_block_scales),
+                               (up, r.up_codes, r.up_block_scales)):
+            if src is None:
+                continue
+            c, b = orc.nvfp4_with_scale(src[e], s)
+            assert_same(host(codes[e]), c, f"{name} e{e} codes")
+            assert_same(host(bs[e]), b, f"{name} e{e} block scales")
+
+
+def test_gateup_amax_variant_small(orc):
+    rng = np.random.default_rng(19)
+    g = W.bf16_bits(rng.normal(0, 0.02, (4, 48, 64)))
+    u = W.bf16_bits(rng.normal(0, 0.05, (4, 48, 64)))
+    true = scope_amax_bits(g, u)
+    check_pair_amax(orc, g, u, true, "true amax pair")
+    check_pair_amax(orc, g, None, scope_amax_bits(g), "true amax single")
+    # Not the scopes' own amax: a quarter (codes and block scales saturate),
+    # four times, a negative sign bit, zero, and a BF16 subnormal.
+    other = W.bf16_bits(W.bf16_to_f64(true) * np.array([0.25, 4.0, 1.0, 1.0]))
+    other[2] |= 0x8000
+    check_pair_amax(orc, g, u, other, "other amax")
+    check_pair_amax(orc, g, u, np.array([0, 1, 0x0080, 0x7F7F], np.uint16), "edge amax")
+
+
 def test_gateup_small(orc):
     rng = np.random.default_rng(9)
     g = W.bf16_bits(rng.normal(0, 0.02, (3, 48, 64)))
@@ -369,6 +413,21 @@ def test_gateup_config4_full(orc):
     E = gate.shape[0]
     rp, (gc, gb, uc, ub, sp) = check_pair(orc, gate, up, "config4 gate/up")
     rd, (dc, db, _, _, sd) = check_pair(orc, down, None, "config4 down")
+    # The same export with each scope's amax supplied by the caller.
+    for g_, u_, want, label in ((gate, up, (gc, gb, uc, ub, sp), "gate/up"),
+                                (down, None, (dc, db, None, None, sd), "down")):
+        announce(f"nvfp4 gateup amax config4 {label}")
+        ra = api.nvfp4_quantize_gateup_pair_amax(dev(g_), None if u_ is None else dev(u_),
+                                                 dev(scope_amax_bits(g_, u_)))
+        torch.cuda.synchronize()
+        assert_same(host(ra.scope_scales).view(np.uint32), want[4].view(np.uint32),
+                    f"config4 amax {label} scales")
+        assert_same(host(ra.gate_codes), want[0], f"config4 amax {label} codes")
+        assert_same(host(ra.gate_block_scales), want[1], f"config4 amax {label} bs")
+        if u_ is not None:
+            assert_same(host(ra.up_codes), want[2], f"config4 amax {label} up codes")
+            assert_same(host(ra.up_block_scales), want[3], f"config4 amax {label} up bs")
+        del ra
     del gate, up, down
     for label, codes, bs, sc, wc, wb, ws, rows in (
             ("gate", rp.gate_codes, rp.gate_block_scales, rp.scope_scales, gc, gb, sp, 768),
@@ -990,6 +1049,31 @@ def test_dispatch_config5_full(orc):
     128): every segment and every row of both outputs."""
     tokens, row_tokens, token_rows, off = W.config5_dispatch()
     check_dispatch(orc, tokens, row_tokens, token_rows, off, "config5")
+
+
+# ---------------------------------------------------------------------------
+# Measurement reference (the copy floor the benchmark times beside each
+# workload): its output is its stated definition, so no load is optimized away
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_r,n_w", [(1, 1), (300, 300), (1000, 257), (4096, 1024),
+                                     (37, 1000), (5, 4096), (70000, 20000)])
+def test_copy_floor_definition(n_r, n_w):
+    rng = np.random.default_rng(n_r * 7 + n_w)
+    src = rng.integers(0, 256, (n_r, 16), dtype=np.uint8)
+    announce(f"copy floor n_r={n_r} n_w={n_w}")
+    dst = torch.empty((n_w, 16), dtype=torch.uint8, device="cuda")
+    mxq.mxq_copy_floor(dev(src), 16 * n_r, dst, 16 * n_w)
+    torch.cuda.synchronize()
+    if n_r >= n_w:
+        want = src[:n_w].copy()
+        for i in range(1, -(-n_r // n_w)):
+            part = src[i * n_w:(i + 1) * n_w]
+            want[:part.shape[0]] ^= part
+    else:
+        m = (n_r << 32) // n_w
+        want = src[[(j * m) >> 32 for j in range(n_w)]]
+    assert_same(host(dst), want, "copy floor")
 
 
 # ---------------------------------------------------------------------------
