@@ -3,14 +3,25 @@
 // per-token NVFP4 RL on Blackwell").  y = BF16(dec(code) * dec(scale) [* s]),
 // rounded once from the exact product, ties to even, saturating at 0x7F7F.
 //
-// Work layout: each wavefront takes 1024 consecutive elements of the flattened
-// [rows][cols] array per step; lane l converts the 8-element chunks starting
-// at 8l and 512 + 8l (cols is a multiple of 16, so a chunk never straddles a
-// row or an NVFP4 block).  Every 16-byte store instruction of the wave then
-// covers 1 KiB of contiguous output, whole cache lines: 32 contiguous bytes
-// per lane would leave each store instruction writing half lines, which the
-// streaming stores turn into extra HBM write traffic.  Grid-stride over
-// wave steps.
+// Work layout: each wavefront takes 1024 (MXFP8) or 2048 (NVFP4) consecutive
+// elements of the flattened [rows][cols] array per step; lane l converts the
+// 8-element chunks starting at 8l + 512h (h = 0, 1, or 0..3; cols is a
+// multiple of 16, so a chunk never straddles a row or an NVFP4 block).  Every
+// 16-byte store instruction of the wave then covers 1 KiB of contiguous
+// output, whole cache lines: 32 contiguous bytes per lane would leave each
+// store instruction writing half lines, which the streaming stores turn into
+// extra HBM write traffic.  Grid-stride over wave steps.
+//
+// NVFP4 issues every load of a step before using any of them (chunks past
+// the end load from element 0 and are not stored), and reads the FP32 scale
+// with one scalar load when the step lies within one scale's rows.  Measured
+// against two chunks per lane with the loads in bounds branches (which made
+// the first chunk's loads land before the second's were issued): 8192 x 2048
+// 11.9 -> 10.7 us, 262144 x 2048 254 -> 232 us; eight chunks per lane were
+// slower (12.3 and 236 us), and so was decoding the codes through a byte-
+// permute table of the block's eight BF16 products instead of converting
+// them (11.2 and 242 us).  The MXFP8 kernels keep two chunks per lane: four
+// were no faster at 8192 x 2048 and slower at 262144 x 2048 (254 -> 264 us).
 //
 // The arithmetic (exact conversion instructions, and the exact fallbacks)
 // is in mxq_dequant.h.  MXFP8 rowwise: one scale per unit (index f / 32);
@@ -27,8 +38,10 @@ constexpr int WAVES_PER_WG = 4;
 // 2048 grouped shape.
 constexpr int MXFP8_OVERSUBSCRIBE = 0;
 constexpr int NVFP4_OVERSUBSCRIBE = 16;
-constexpr int64_t WAVE_SPAN = 1024;     // elements per wavefront step
+constexpr int64_t WAVE_SPAN = 1024;     // MXFP8: elements per wavefront step
 constexpr int64_t HALF_SPAN = 512;
+constexpr int NV_CHUNKS = 4;            // NVFP4: chunks per lane per step
+constexpr int64_t NV_SPAN = HALF_SPAN * NV_CHUNKS;
 
 // COL == false: scales[row][cols/32]; COL == true: scales[row/32][cols].
 // n = rows * cols elements; per_row16 divides by cols / 16.
@@ -82,28 +95,42 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__res
 {
     const int64_t lane8 = (tid() & 63) * 8;
     const int64_t waves = (int64_t)nwg * WAVES_PER_WG;
-    for (int64_t w = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group(); w * WAVE_SPAN < n;
+    for (int64_t w = (int64_t)wg_id() * WAVES_PER_WG + wave_in_group(); w * NV_SPAN < n;
          w += waves) {
-        int64_t f[2];
-        uint32_t cw[2];
-        float d[2], s[2];
+        int64_t f[NV_CHUNKS];
+        bool ok[NV_CHUNKS];
+        uint32_t cw[NV_CHUNKS], bb[NV_CHUNKS];
+        float d[NV_CHUNKS], s[NV_CHUNKS];
+        // One FP32 scale for the whole step?  (Wave-uniform.)
+        const int64_t f0 = w * NV_SPAN;
+        const int64_t f1 = (f0 + NV_SPAN <= n ? f0 + NV_SPAN : n) - 1;
+        const uint32_t s0 = udiv((uint32_t)(f0 >> 4), per_scale);
+        const bool one = s0 == udiv((uint32_t)(f1 >> 4), per_scale);
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            f[h] = w * WAVE_SPAN + h * HALF_SPAN + lane8;
-            cw[h] = 0;
-            d[h] = 0.0f;
-            s[h] = 0.0f;
-            if (f[h] < n) {
-                const int64_t blk = f[h] >> 4;
-                cw[h] = ld_nt4(codes + (f[h] >> 1));
-                d[h] = e4m3_value(bscales[blk]);
-                s[h] = fp32_scales[udiv((uint32_t)blk, per_scale)];
-            }
+        for (int h = 0; h < NV_CHUNKS; h++) {
+            f[h] = f0 + h * HALF_SPAN + lane8;
+            ok[h] = f[h] < n;
+            const int64_t blk = ok[h] ? f[h] >> 4 : 0;
+            cw[h] = ld_nt4(codes + 8 * blk + ((f[h] >> 1) & 4));
+            bb[h] = bscales[blk];
+            s[h] = one ? 0.0f : fp32_scales[udiv((uint32_t)blk, per_scale)];
+        }
+        __builtin_amdgcn_sched_barrier(0);      // keep the vector loads ahead of their uses
+        if (one) {
+            const float su = fp32_scales[s0];
+#pragma unroll
+            for (int h = 0; h < NV_CHUNKS; h++)
+                s[h] = su;
         }
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+        for (int h = 0; h < NV_CHUNKS; h++) {
+            d[h] = ok[h] ? e4m3_value(bb[h]) : 0.0f;
+            cw[h] = ok[h] ? cw[h] : 0u;
+        }
+#pragma unroll
+        for (int h = 0; h < NV_CHUNKS; h++) {
             const u32x4_t o = nv_chunk(cw[h], d[h], s[h]);
-            if (f[h] < n)
+            if (ok[h])
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + f[h]));
         }
     }
@@ -114,9 +141,9 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__res
 // ---------------------------------------------------------------------------
 
 template <class K>
-static unsigned grid_for(K kernel, int64_t n, int oversubscribe)
+static unsigned grid_for(K kernel, int64_t n, int64_t span, int oversubscribe)
 {
-    const int64_t need = (n + WAVE_SPAN * WAVES_PER_WG - 1) / (WAVE_SPAN * WAVES_PER_WG);
+    const int64_t need = (n + span * WAVES_PER_WG - 1) / (span * WAVES_PER_WG);
     int64_t wgs = need;
     if (oversubscribe > 0) {
         const int64_t cap = resident_workgroups((const void *)kernel, 64 * WAVES_PER_WG) *
@@ -136,11 +163,13 @@ hipError_t launch_dequant_mxfp8(bool col, const uint8_t *codes, const uint8_t *s
     const Div per_row16 = make_div((uint32_t)(cols / 16));
     const dim3 block(64 * WAVES_PER_WG);
     if (col) {
-        const unsigned g = grid_for(dequant_mxfp8_kernel<true>, n, MXFP8_OVERSUBSCRIBE);
+        const unsigned g =
+            grid_for(dequant_mxfp8_kernel<true>, n, WAVE_SPAN, MXFP8_OVERSUBSCRIBE);
         hipLaunchKernelGGL((dequant_mxfp8_kernel<true>), dim3(g), block, 0, stream, codes, scales,
                            n, cols, per_row16, g, out);
     } else {
-        const unsigned g = grid_for(dequant_mxfp8_kernel<false>, n, MXFP8_OVERSUBSCRIBE);
+        const unsigned g =
+            grid_for(dequant_mxfp8_kernel<false>, n, WAVE_SPAN, MXFP8_OVERSUBSCRIBE);
         hipLaunchKernelGGL((dequant_mxfp8_kernel<false>), dim3(g), block, 0, stream, codes,
                            scales, n, cols, per_row16, g, out);
     }
@@ -155,7 +184,7 @@ hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *bscales, co
     const int64_t blocks = n / 16;
     const int64_t per = (cols / 16) * rows_per_scale;   // blocks per FP32 scale
     const Div per_scale = make_div((uint32_t)(per < blocks ? per : blocks));
-    const unsigned g = grid_for(dequant_nvfp4_kernel, n, NVFP4_OVERSUBSCRIBE);
+    const unsigned g = grid_for(dequant_nvfp4_kernel, n, NV_SPAN, NVFP4_OVERSUBSCRIBE);
     hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3(g), dim3(64 * WAVES_PER_WG), 0, stream, codes,
                        bscales, fs, n, per_scale, g, out);
     return hipGetLastError();
