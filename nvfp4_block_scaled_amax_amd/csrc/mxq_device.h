@@ -213,12 +213,6 @@ __device__ __forceinline__ uint32_t e2m1_code_f64(double q)
     return k;
 }
 
-__device__ __forceinline__ double e2m1_value_f64(uint32_t k)
-{
-    const double v[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-    return v[k & 7];
-}
-
 // ---------------------------------------------------------------------------
 // Global memory access (native vector types, so the nontemporal builtins
 // apply: streaming data is touched once).

@@ -29,11 +29,11 @@
 // q_hi = x * r (1 + 2^-19), so |q_lo| < |x / D| < |q_hi| with all operands
 // normal.  Conversion is monotone, so when the hardware's exact nearest-even
 // conversions of q_lo and q_hi agree, that code is the exactly rounded code of
-// x / D.  When they differ (x / D within ~2^-18 of a rounding midpoint, a few
-// per million random elements), the lane decides exactly in binary64: |x|
-// against midpoint * D, a product of at most 31 significant bits, hence exact.
-// Scales below 2^-101 would take the reciprocals out of the normal range; such
-// scopes use a binary64 path that divides once per element.
+// x / D.  When they differ (x / D within ~2^-18 of a rounding midpoint), the
+// lane decides exactly with one FMA: the sign of midpoint * c * s - |x|, which
+// FP32 gets right (see block_scale_fix).  Scales below 2^-101 would take the
+// reciprocals out of the normal range; such scopes use a binary64 path that
+// divides once per element.
 #include "mxq_dequant.h"
 #include "mxq_launch.h"
 
@@ -98,54 +98,49 @@ __device__ __forceinline__ BlkF unpack_blk(const Blk &b)
     return f;
 }
 
-// Exact block scale when the bracket straddles a midpoint: blo and blo + 1 are
-// the candidates; compare A with their midpoint times 6 s exactly.
-__device__ __attribute__((noinline)) uint32_t block_scale_exact(float A, float s, uint32_t blo)
+// Exact decisions where the bracket straddles a midpoint (fast path only,
+// s >= 2^-101).  For a midpoint m of the target format and a divisor
+// D = c s (c = 6 for block scales, c = dec(b) for codes), m c has at most 7
+// significant bits, so it is exact in FP32, and fma(m c, s, -a) rounds the
+// exact m c s - a once.  Rounding keeps the sign, and the exact difference is
+// 0 or a nonzero multiple of 2^-135 (m c is a multiple of 2^-11, s one of
+// 2^-124, a BF16 value one of 2^-133), which FP32 (denormals kept) represents,
+// so the FMA's sign is the sign of m c s - a and a tie is exactly t == 0.
+// These cases are far more common than random quotients would suggest: with
+// BF16 inputs of 8 significant bits and 2688 = 2^7 * 21, quotients such as
+// x 2688 / (dec(b) A) often equal a midpoint before the inexact s moves them
+// by a relative 2^-24, so the decision stays inline (an out-of-line binary64
+// fix-up measured 12.7 us against 10.0 us without it on 8192 x 2048).
+
+// Block scale: the candidates are blo and blo + 1; 6 * midpoint =
+// 3 (dec(blo) + dec(blo + 1)).
+__device__ __forceinline__ uint32_t block_scale_fix(float A, float s, uint32_t blo)
 {
-    const double mid2 = (double)e4m3_value(blo) + (double)e4m3_value(blo + 1);  // 2 * midpoint
-    const double t = mid2 * 3.0 * (double)s;                                    // midpoint * 6 s
-    const double a = (double)A;
-    if (a > t)
-        return blo + 1;
-    if (a < t)
-        return blo;
-    return (blo & 1u) ? blo + 1 : blo;
+    const float m6 = 3.0f * (e4m3_value(blo) + e4m3_value(blo + 1u));
+    const float t = __builtin_fmaf(m6, s, -A);
+    return t < 0.0f ? blo + 1u : (t > 0.0f ? blo : ((blo & 1u) ? blo + 1u : blo));
 }
 
-// Nibble i of the bracket results lo/hi differ: decide it exactly.  x: the
-// element (BF16 bits), Dd = dec(b) s in binary64 (exact).
-__device__ __forceinline__ uint32_t fix_nibble(uint32_t lo, uint32_t hi, int i, uint32_t xbits,
-                                               double Dd)
+// The nibbles of one 8-code word where the bracket words lo and hi differ
+// (there the magnitudes are klo and klo + 1): decided against the midpoint.
+// x: the word's 8 elements as f32.
+__device__ __forceinline__ uint32_t codes_fix(uint32_t lo, uint32_t hi, const float *x, float d,
+                                              float s)
 {
-    const uint32_t a = (lo >> (4 * i)) & 0xFu, b = (hi >> (4 * i)) & 0xFu;
-    if (a == b)
-        return lo;
-    const uint32_t klo = a & 7u, khi = b & 7u;     // khi == klo + 1
-    const double t = (e2m1_value_f64(klo) + e2m1_value_f64(khi)) * Dd;   // 2 * mid * D
-    const double ax = 2.0 * fabs((double)u2f(xbits << 16));
-    uint32_t k;
-    if (ax > t)
-        k = khi;
-    else if (ax < t)
-        k = klo;
-    else
-        k = (klo & 1u) ? khi : klo;
-    return (lo & ~(0xFu << (4 * i))) | ((k | (a & 8u)) << (4 * i));
-}
-
-// Fix the nibbles of one 8-code word.  w0..w3: the 8 inputs (BF16 pairs).
-__device__ __attribute__((noinline)) uint32_t codes_exact(uint32_t lo, uint32_t hi, uint32_t w0,
-                                                          uint32_t w1, uint32_t w2, uint32_t w3,
-                                                          float d, float s)
-{
-    const double D = (double)d * (double)s;
-    const uint32_t w[4] = {w0, w1, w2, w3};
+    const uint32_t diff = lo ^ hi;
+    uint32_t out = lo;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-        lo = fix_nibble(lo, hi, i, bits, D);
+        if ((diff >> (4 * i)) & 0xFu) {
+            const uint32_t a = (lo >> (4 * i)) & 0xFu, klo = a & 7u;
+            const float2_t v = e2m1_values(klo | ((klo + 1u) << 4));
+            const float md = (0.5f * (v[0] + v[1])) * d;
+            const float t = __builtin_fmaf(md, s, -fabsf(x[i]));
+            const uint32_t k = t < 0.0f ? klo + 1u : (t > 0.0f ? klo : ((klo & 1u) ? klo + 1u : klo));
+            out = (out & ~(0xFu << (4 * i))) | ((k | (a & 8u)) << (4 * i));
+        }
     }
-    return lo;
+    return out;
 }
 
 // The 8 codes of 8 values times r, written with the hardware conversion.  The
@@ -234,7 +229,7 @@ __device__ __forceinline__ BlkOut quant_blk(const Blk &blk, const BlkF &f, const
         const uint32_t bb = e4m3_pair_rne(fminf(A * k.r6_lo, 448.0f), fminf(A * k.r6_hi, 448.0f));
         o.b = bb & 0xFFu;
         if (o.b != (bb >> 8))
-            o.b = block_scale_exact(A, k.s, o.b);
+            o.b = block_scale_fix(A, k.s, o.b);
         o.c0 = o.c1 = 0u;
         if (o.b != 0) {
             const float d = e4m3_value(o.b);
@@ -242,8 +237,8 @@ __device__ __forceinline__ BlkOut quant_blk(const Blk &blk, const BlkF &f, const
             const float rlo = r * BRACKET_LO, rhi = r * BRACKET_HI;
             const uint32_t lo0 = codes8(f.x, rlo), hi0 = codes8(f.x, rhi);
             const uint32_t lo1 = codes8(f.x + 8, rlo), hi1 = codes8(f.x + 8, rhi);
-            o.c0 = lo0 == hi0 ? lo0 : codes_exact(lo0, hi0, blk.w[0], blk.w[1], blk.w[2], blk.w[3], d, k.s);
-            o.c1 = lo1 == hi1 ? lo1 : codes_exact(lo1, hi1, blk.w[4], blk.w[5], blk.w[6], blk.w[7], d, k.s);
+            o.c0 = lo0 == hi0 ? lo0 : codes_fix(lo0, hi0, f.x, d, k.s);
+            o.c1 = lo1 == hi1 ? lo1 : codes_fix(lo1, hi1, f.x + 8, d, k.s);
         }
     } else if (k.s == 0.0f) {
         o.b = 0u;
