@@ -127,12 +127,20 @@ __device__ __forceinline__ bool bf16_tie_hazard(float a, float s)
     return (f2u(p) & 0xFFFFu) == 0x8000u && __builtin_fmaf(a, s, -p) != 0.0f;
 }
 
-// Exact BF16 pair for one code byte (two E2M1 codes) under (d, s).
-static __device__ __attribute__((noinline)) uint32_t nv_pair_exact(uint32_t byte, float d, float s)
+// Exact BF16 pair for one code byte (two E2M1 codes) under (d, s).  Inlined
+// into the dequant kernel (an out-of-line call there cost 8192 x 2048
+// 9.8 -> 10.8 us); the one-pass quantize + dequant kernels call it out of
+// line, since inlined it would add to their register pressure (the
+// quantizers spilled when their own binary64 path was inlined).
+__device__ __forceinline__ uint32_t nv_pair_exact_inl(uint32_t byte, float d, float s)
 {
     const float2_t v = e2m1_values(byte);
     return pack2(bf16_from_f64((double)v[0] * (double)d * (double)s),
                  bf16_from_f64((double)v[1] * (double)d * (double)s));
+}
+static __device__ __attribute__((noinline)) uint32_t nv_pair_exact(uint32_t byte, float d, float s)
+{
+    return nv_pair_exact_inl(byte, d, s);
 }
 
 // Eight BF16 (16 bytes) of one NVFP4 chunk: 8 codes (4 bytes) of a block
@@ -151,7 +159,7 @@ __device__ __forceinline__ u32x4_t nv_chunk(uint32_t cw, float d, float s)
         }
     } else {
         for (int j = 0; j < 4; j++)
-            o[j] = nv_pair_exact((cw >> (8 * j)) & 0xFFu, d, s);
+            o[j] = nv_pair_exact_inl((cw >> (8 * j)) & 0xFFu, d, s);
     }
     return o;
 }
