@@ -396,7 +396,8 @@ def copy_floor(torch, E, rbytes, wbytes, sets, graph, n_launch=CFG_LAUNCHES, war
     return _FLOORS[key]
 
 
-def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None, floor=None):
+def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None, floor=None,
+               rw=None):
     """One config's record.  floor: (eager, graph) ms lists of the copy floor of
     the same read and write bytes: "vs_copy_floor" is the floor's time over the
     kernel's (1.0 = as fast as a plain copy of those bytes)."""
@@ -406,6 +407,8 @@ def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None,
            "ms_min": round(mn, 5), "bytes": nbytes, "GB_s": round(gbs, 1),
            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
            "elements_per_s": round(elems / (med * 1e-3), 1), "buffer_sets": sets}
+    if rw is not None:
+        rec.update({"bytes_in": rw[0], "bytes_out": rw[1]})
     if floor is not None:
         fmed = float(np.median(floor[0]))
         fgbs = nbytes / (fmed * 1e-3) / 1e9
@@ -452,9 +455,10 @@ def config_timings(torch, E, W, legs, log, only=None):
         gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
         del bufs, launches, x0
         torch.cuda.empty_cache()
-        fl = copy_floor(torch, E, 2 * n, 2 * n + 2 * (n // 32), sets, True)
+        rw = (2 * n, 2 * n + 2 * (n // 32))
+        fl = copy_floor(torch, E, *rw, sets, True)
         k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
-                          ["mxfp8_tile_kernel"], gms, fl)
+                          ["mxfp8_tile_kernel"], gms, fl, rw)
         res[k] = v
 
     for mode in W.MXFP8_MODES:
@@ -486,12 +490,12 @@ def config_timings(torch, E, W, legs, log, only=None):
         if sel("C3_nvfp4"):
             fl = copy_floor(torch, E, 2 * n, q_out, sets, True)
             k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
-                              ["nvfp4_token_split_kernel"], gms, fl)
+                              ["nvfp4_token_split_kernel"], gms, fl, (2 * n, q_out))
             res[k] = v
         if sel("C3_dequant"):
             fl = copy_floor(torch, E, q_out, 2 * n, sets, True)
             k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", dms, d_bytes, n,
-                              sets, ["dequant_nvfp4_kernel"], dgms, fl)
+                              sets, ["dequant_nvfp4_kernel"], dgms, fl, (q_out, 2 * n))
             res[k] = v
         log("C3 timed")
 
@@ -504,13 +508,15 @@ def config_timings(torch, E, W, legs, log, only=None):
             l = by_name[leg]
             ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
             fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
-            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
+            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl,
+                              (l.bytes_in, l.bytes_out))
             res[k] = v
     for l, cfg in zip(_SHARED.get("exp_amax_legs", []), ("C4_gateup_amax", "C4_down_amax")):
         if sel(cfg):
             ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
             fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
-            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
+            k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl,
+                              (l.bytes_in, l.bytes_out))
             res[k] = v
     log("C4/C5 timed")
 
@@ -578,7 +584,7 @@ def qdq_small_timings(torch, E, W, dev, empty):
         fl = copy_floor(torch, E, 2 * n, out_b, sets, True)
         kern = "mxfp8_row_qdq_kernel" if fmt == E.MXQ_FMT_MXFP8_ROW else "nvfp4_token_split_kernel"
         k, v = cfg_record(name, f"quantize + BF16 dequant, one pass, {rows}x{cols}", ms, nbytes,
-                          n, sets, [kern], gms, fl)
+                          n, sets, [kern], gms, fl, (2 * n, out_b))
         res[k] = v
     return res
 
@@ -676,7 +682,8 @@ def qdq_timings(torch, E, W, dev, empty):
     for l, cfg in zip(legs, ("C5_qdq_mxfp8", "C5_qdq_nvfp4")):
         ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
         fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
-        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl,
+                          (l.bytes_in, l.bytes_out))
         res[k] = v
     del legs
     torch.cuda.empty_cache()
@@ -730,7 +737,8 @@ def dispatch_timings(torch, E, W, dev, empty):
     for l, cfg in zip(legs, ("C5_dispatch_mxfp8", "C5_dispatch_nvfp4", "C5_gather_torch")):
         ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
         fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
-        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl)
+        k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl,
+                          (l.bytes_in, l.bytes_out))
         res[k] = v
     return res
 
@@ -836,6 +844,140 @@ def summarize_pmc(fetch_csv: str, write_csv: str, bench_log: str, out_json: str,
     print("\n".join(out))
 
 
+SHAPE_VALU = ("SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+              "SQ_INSTS_VALU_CVT SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE")
+SHAPE_BENCH = "python3 bench.py --config-only {configs} --copy-calibration-mib 1024"
+SHAPE_CMDS = (
+    ("stats", "rocprofv3 --kernel-trace --stats -d OUT/{tag}_stats -o s --output-format csv -- "),
+    ("fetch", "rocprofv3 --pmc FETCH_SIZE -d OUT/{tag}_fetch -o f --output-format csv -- "),
+    ("write", "rocprofv3 --pmc WRITE_SIZE -d OUT/{tag}_write -o w --output-format csv -- "),
+    ("valu", "rocprofv3 --pmc " + SHAPE_VALU + " -d OUT/{tag}_valu -o v --output-format csv -- "))
+
+
+def pmc_counters(path: str):
+    """{(raw kernel name, grid size): {counter: [value summed per dispatch, ...]}}."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            c = per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+            c[d] = c.get(d, 0.0) + float(r["Counter_Value"])
+    return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+
+
+def trace_durations(path: str):
+    """{(raw kernel name, grid size): [duration in us, ...]} of a kernel trace."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) *
+                   int(r["Grid_Size_Z"]))
+            per.setdefault(key, []).append((int(r["End_Timestamp"]) -
+                                            int(r["Start_Timestamp"])) / 1e3)
+    return per
+
+
+def floor_grid(rbytes: int, wbytes: int):
+    """(variant, grid size in work-items) of mxq_copy_floor over those bytes."""
+    r16, w16 = -(-rbytes // 16), -(-wbytes // 16)
+    return ("true" if r16 >= w16 else "false"), -(-w16 // 256) * 256
+
+
+def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, write_csv: str,
+                    valu_csv: str, bench_json: str, out_txt: str):
+    """One shape's profile from four rocprofv3 runs of bench.py --config-only:
+    device durations from the kernel trace, HBM bytes per launch (FETCH_SIZE
+    and WRITE_SIZE, KiB per dispatch, scaled by what each counter reads for
+    the 1 GiB calibration copy of the same run) against algorithmic bytes, the
+    copy floor of each config's bytes, and VALU counters per wavefront.
+    Dispatches are grouped by kernel and grid size."""
+    run = json.loads([ln for ln in open(bench_json) if ln.startswith("{")][-1])
+    cfgs = run["configs"]
+    copy_bytes = run["copy_calibration"]["bytes"] // 2
+    mean = lambda v: sum(v) / len(v)
+    med = lambda v: sorted(v)[len(v) // 2]
+    fetch, write, valu = pmc_counters(fetch_csv), pmc_counters(write_csv), pmc_counters(valu_csv)
+    dur = trace_durations(trace_csv)
+    cal = lambda d, c: [mean(v[c]) for k, v in d.items() if "bitwise_not" in k[0]][0]
+    f_scale = copy_bytes / (cal(fetch, "FETCH_SIZE") * 1024)
+    w_scale = copy_bytes / (cal(write, "WRITE_SIZE") * 1024)
+    # Which config each (kernel, grid) group belongs to.
+    owner = {}
+    for key in dur:
+        short = kernel_short_name(key[0])
+        base = short.split("<")[0]
+        if base == "copy_floor_kernel":
+            var = "true" if "<true>" in short else "false"
+            names = [n for n, c in cfgs.items() if "copy_floor_ms" in c and
+                     floor_grid(c["bytes_in"], c["bytes_out"]) == (var, key[1])]
+            owner[key] = ("floor", names)
+        elif "mxq::" in key[0]:
+            names = [n for n, c in cfgs.items() if any(k.split("<")[0] == base
+                                                       for k in c["kernels"])]
+            owner[key] = ("kernel", names)
+    cmds = ["  " + pre.format(tag=tag) + SHAPE_BENCH.format(configs=configs)
+            for _, pre in SHAPE_CMDS]
+    what = ", ".join(f"{n} ({c['desc']})" for n, c in cfgs.items())
+    out = [f"{tag}: rocprofv3 profile of {what}.",
+           "", "Commands (repository root, one MI355X, ROCm 7.2, TMPDIR=/tmp; OUT is where the "
+           "CSVs go):", *cmds,
+           f"Summary: python3 bench.py --summarize-shape {tag} {configs} <stats "
+           "kernel_trace.csv> <fetch counter_collection.csv> <write ...> <valu ...> "
+           "<stdout of the stats run>", "",
+           f"Calibration (int32 bitwise not of {copy_bytes} bytes, read once and written once): "
+           f"FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f} -> bytes.",
+           "Durations are device times from the kernel trace (the bench's own event timings in",
+           "the traced run include the tracer's per-dispatch overhead and are not used).", "",
+           f"{'kernel':<50} {'grid':>9} {'calls':>5} {'avg us':>8} {'HBM read':>12} "
+           f"{'HBM write':>12}  config"]
+    rows = []
+    for key, ts in sorted(dur.items(), key=lambda t: -sum(t[1])):
+        if key not in owner:
+            continue
+        short = kernel_short_name(key[0])
+        fk = mean(fetch[key]["FETCH_SIZE"]) * 1024 * f_scale if key in fetch else float("nan")
+        wk = mean(write[key]["WRITE_SIZE"]) * 1024 * w_scale if key in write else float("nan")
+        kind, names = owner[key]
+        label = ("copy floor of " if kind == "floor" else "") + ", ".join(names)
+        out.append(f"{short[:50]:<50} {key[1]:>9} {len(ts):>5} {mean(ts):>8.2f} {fk:>12.0f} "
+                   f"{wk:>12.0f}  {label}")
+        rows.append((key, short, kind, names, mean(ts), fk, wk))
+    out += ["", "Per config (kernels owned by that config alone; algorithmic bytes count each "
+            "input read once and each output written once):", "",
+            f"{'config':<18} {'kernel us':>9} {'% of 8TB/s':>10} {'HBM bytes':>12} "
+            f"{'algorithmic':>12} {'ratio':>6} {'floor us':>9} {'floor/kernel':>12}"]
+    for n, c in cfgs.items():
+        mine = [r for r in rows if r[2] == "kernel" and r[3] == [n]]
+        fl = [r for r in rows if r[2] == "floor" and n in r[3]]
+        if not mine:
+            continue
+        t = sum(r[4] for r in mine)
+        hbm = sum(r[5] + r[6] for r in mine)
+        ft = fl[0][4] if fl else float("nan")
+        out.append(f"{n:<18} {t:>9.2f} {100 * c['bytes'] / (t * 1e-6) / 8e12:>10.2f} "
+                   f"{hbm:>12.0f} {c['bytes']:>12} {hbm / c['bytes']:>6.3f} {ft:>9.2f} "
+                   f"{ft / t:>12.3f}")
+    out += ["", "VALU counters (medians over dispatches); per wave: instructions, conversion",
+            "instructions, VALU issue quad-cycles; 'VALU share' = SQ_ACTIVE_INST_VALU /",
+            "SQ_WAVE_CYCLES, the fraction of the waves' resident time spent issuing VALU:", "",
+            f"{'kernel':<50} {'grid':>9} {'waves':>7} {'VALU/w':>7} {'cvt/w':>6} {'qcyc/w':>7} "
+            f"{'VALU share':>10}"]
+    for key, short, *_ in rows:
+        if key not in valu:
+            continue
+        c = {k: med(v) for k, v in valu[key].items()}
+        w = c["SQ_WAVES"]
+        out.append(f"{short[:50]:<50} {key[1]:>9} {w:>7.0f} {c['SQ_INSTS_VALU'] / w:>7.1f} "
+                   f"{c['SQ_INSTS_VALU_CVT'] / w:>6.1f} {c['SQ_ACTIVE_INST_VALU'] / w:>7.1f} "
+                   f"{c['SQ_ACTIVE_INST_VALU'] / c['SQ_WAVE_CYCLES']:>10.3f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def summarize_stats(stats_csv: str, out_txt: str, title: str):
     """Kernel statistics of a rocprofv3 --stats run as a text table."""
     import csv
@@ -889,6 +1031,11 @@ def main():
                     help="(no GPU) write profiles/traffic.json and its text table from the "
                          "counter CSVs of the FETCH_SIZE and WRITE_SIZE runs and the bench output "
                          "of the first")
+    ap.add_argument("--summarize-shape", nargs=7,
+                    metavar=("TAG", "CONFIGS", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
+                             "BENCH_JSON"),
+                    help="(no GPU) write profiles/TAG_profile.txt from the four rocprofv3 runs of "
+                         "bench.py --config-only CONFIGS --copy-calibration-mib 1024")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="(no GPU) write profiles/step_all_kernels_stats.txt from rocprofv3's "
                          "kernel statistics")
@@ -897,6 +1044,11 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, TRAFFIC_FILE,
                       os.path.join(ROOT, "profiles", "grouped_262144x2048_hbm_traffic.txt"))
+        return
+    if args.summarize_shape:
+        tag = args.summarize_shape[0]
+        summarize_shape(*args.summarize_shape,
+                        os.path.join(ROOT, "profiles", f"{tag}_profile.txt"))
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats,
@@ -935,7 +1087,17 @@ def main():
         legs = build_legs(torch, mxq, api, W, log,
                           want=lambda g: g in need and g not in ("act", "wgt"))
         res = config_timings(torch, mxq, W, legs, log, only=only)
-        print(json.dumps({"configs": res, "csrc_digest": csrc_digest()}), flush=True)
+        calib = None
+        if args.copy_calibration_mib > 0:
+            nbytes = args.copy_calibration_mib << 20
+            src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32,
+                                device="cuda")
+            dst = torch.empty_like(src)
+            ms = time_launches(torch, [lambda: torch.bitwise_not(src, out=dst)], 5, 2, 1)
+            calib = {"bytes": 2 * nbytes, "ms": round(float(np.median(ms)), 5)}  # in + out
+            del src, dst
+        print(json.dumps({"configs": res, "copy_calibration": calib,
+                          "csrc_digest": csrc_digest()}), flush=True)
         return
     t_gen = time.perf_counter()
     groups = set(args.groups.split(","))
