@@ -949,17 +949,32 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
             "input read once and each output written once):", "",
             f"{'config':<18} {'kernel us':>9} {'% of 8TB/s':>10} {'HBM bytes':>12} "
             f"{'algorithmic':>12} {'ratio':>6} {'floor us':>9} {'floor/kernel':>12}"]
+    notes = set()
     for n, c in cfgs.items():
         mine = [r for r in rows if r[2] == "kernel" and r[3] == [n]]
         fl = [r for r in rows if r[2] == "floor" and n in r[3]]
-        if not mine:
-            continue
-        t = sum(r[4] for r in mine)
-        hbm = sum(r[5] + r[6] for r in mine)
-        ft = fl[0][4] if fl else float("nan")
-        out.append(f"{n:<18} {t:>9.2f} {100 * c['bytes'] / (t * 1e-6) / 8e12:>10.2f} "
-                   f"{hbm:>12.0f} {c['bytes']:>12} {hbm / c['bytes']:>6.3f} {ft:>9.2f} "
-                   f"{ft / t:>12.3f}")
+        if mine:
+            t = sum(r[4] for r in mine)
+            hbm = sum(r[5] + r[6] for r in mine)
+            hbm_s, ratio_s = f"{hbm:>12.0f}", f"{hbm / c['bytes']:>6.3f}"
+        else:       # kernels shared with other configs of the run: the bench's timing
+            t = 1e3 * c["ms_median"]
+            hbm_s, ratio_s = f"{'-':>12}", f"{'-':>6}"
+            notes.add("b")
+        if len(fl) == 1 and len(fl[0][3]) == 1:
+            ft, mark = fl[0][4], " "
+        else:       # a floor grid shared by configs of equal write bytes
+            ft, mark = 1e3 * c.get("copy_floor_ms", float("nan")), "*"
+            notes.add("f")
+        out.append(f"{n:<18} {t:>9.2f}{'b' if not mine else ' '} "
+                   f"{100 * c['bytes'] / (t * 1e-6) / 8e12:>9.2f} {hbm_s} {c['bytes']:>12} "
+                   f"{ratio_s} {ft:>8.2f}{mark} {ft / t:>12.3f}")
+    if "b" in notes:
+        out.append("b: the config's kernels also run for other configs of this run; its time is "
+                   "the bench's median per call (tracer overhead included).")
+    if "f" in notes:
+        out.append("*: the copy floor's grid is shared with another config; the floor time is the "
+                   "bench's median for this config's bytes (tracer overhead included).")
     out += ["", "VALU counters (medians over dispatches); per wave: instructions, conversion",
             "instructions, VALU issue quad-cycles; 'VALU share' = SQ_ACTIVE_INST_VALU /",
             "SQ_WAVE_CYCLES, the fraction of the waves' resident time spent issuing VALU:", "",
