@@ -16,22 +16,29 @@
 // The accumulator (16 floats per lane) holds column l % 32, rows 8(i/4) +
 // 4h + i%4.
 //
-// Tiling.  A workgroup of four wavefronts computes a 256x256 tile of C in K
-// steps of 128; wavefront (wm, wn) owns a 128x128 quarter: 4x4 instruction
-// tiles, 256 fp32 accumulators per lane.  Each K step's 256x128-byte A and B
-// slices and their scale bytes go from global memory straight into LDS
-// (global_load_lds: lane l of a wavefront writes the 16 bytes at LDS base +
-// 16 l), into the buffer the step after next computes from, so the loads
-// run under the current step's matrix instructions.  16-byte chunks of each
-// 128-byte LDS row are XOR-swizzled by the row index (each lane fetches the
-// global chunk that belongs in its slot), so the 32 rows one fragment read
-// touches fall in distinct banks.  Fragments of the step's second 64-wide
-// sub-step are read while the first sub-step's instructions run.  Rows past
-// M or N read the last valid row and are not stored.
+// Tiling.  A workgroup of four wavefronts computes a 256x256 tile of C;
+// wavefront (wm, wn) owns a 128x128 quarter: 4x4 instruction tiles, 256
+// fp32 accumulators per lane.  A and B go from global memory straight into
+// LDS (global_load_lds: lane l of a wavefront writes the 16 bytes at LDS
+// base + 16 l) through a ring of K steps, and 16-byte chunks of each LDS
+// row are XOR-swizzled by the row index (each lane fetches the global chunk
+// that belongs in its slot), so the rows one fragment read touches fall in
+// distinct banks.  Rows past M or N read the last valid row and are not
+// stored.  The MXFP8 kernel's pipeline is described at the kernel.
 //
 // BF16 result: the accumulators go through LDS (rows padded to 272 bytes, so
-// the two row groups a store instruction writes miss each other's banks) and
+// the row groups a store instruction writes miss each other's banks) and
 // leave as 16-byte stores that cover 256 contiguous bytes of a row.
+//
+// Measured (2048x8192x2048, BF16 result, one workgroup's clock counters):
+// the earlier form of the MXFP8 kernel (K steps of 128, two LDS stages, the
+// next step's copies waited for at the end of the current one, BF16 values
+// written to LDS one at a time) spent 65k cycles in its K loop, 48k of them
+// with its global copies switched off, and 14.5k in the epilogue; the
+// pipelined form spends 58k (49k without copies) and 10.4k, and takes
+// 43.9 us against 46.5 us per call (8192x8192x2048: 163 us against 170 us).
+// Without copies the loop issues a matrix instruction every ~95 cycles
+// against its 64-cycle occupancy; the clock under this load is 1.6-2.0 GHz.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -41,30 +48,27 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
-constexpr int GEMM_BM = 256, GEMM_BN = 256, GEMM_BK = 128;
+constexpr int GEMM_BM = 256, GEMM_BN = 256;
 constexpr int GEMM_THREADS = 256;
 static_assert(GEMM_BM == 256 && GEMM_BN == 256 && GEMM_THREADS == 256,
               "MAX_GEMM_TILES counts 256 x 256 tiles of 256 threads");
-constexpr int GEMM_CHUNKS = GEMM_BM * GEMM_BK / 16;             // 16-byte chunks per operand slice
-constexpr int GEMM_STAGE_BYTES = 2 * GEMM_CHUNKS * 16 + 2 * GEMM_BM * 4;
 constexpr int GEMM_EPI_ROW = 128 * 2 + 16;                      // padded BF16 row of a quarter
 constexpr int GEMM_EPI_BYTES = 4 * 128 * GEMM_EPI_ROW;
-constexpr int GEMM_LDS_BYTES =
-    2 * GEMM_STAGE_BYTES > GEMM_EPI_BYTES ? 2 * GEMM_STAGE_BYTES : GEMM_EPI_BYTES;
+constexpr int GEMM_LDS_BYTES = GEMM_EPI_BYTES;                  // 136 KiB, the largest LDS use
 
-// One stage in LDS: A chunks, B chunks, A scale words, B scale words.
-struct GemmStageLds {
-    u32x4_t *a, *b;
-    uint32_t *as, *bs;
-};
-__device__ __forceinline__ GemmStageLds gemm_stage(uint8_t *lds, int buf)
-{
-    uint8_t *p = lds + buf * GEMM_STAGE_BYTES;
-    return GemmStageLds{reinterpret_cast<u32x4_t *>(p),
-                        reinterpret_cast<u32x4_t *>(p + GEMM_CHUNKS * 16),
-                        reinterpret_cast<uint32_t *>(p + 2 * GEMM_CHUNKS * 16),
-                        reinterpret_cast<uint32_t *>(p + 2 * GEMM_CHUNKS * 16 + GEMM_BM * 4)};
-}
+// MXFP8 ring: four 64-deep K steps of A and B codes (16 KiB each) and three
+// buffers of scale words (one 4-block word per row of A and of B).
+constexpr int MXG_BK = 64;
+constexpr int MXG_STAGES = 4, MXG_SCALE_BUFS = 3;
+constexpr int MXG_OP_BYTES = GEMM_BM * MXG_BK;
+constexpr int MXG_STAGE_BYTES = 2 * MXG_OP_BYTES;
+constexpr int MXG_SCALE_BYTES = 2 * GEMM_BM * 4;
+constexpr int MXG_SCALE_BASE = MXG_STAGES * MXG_STAGE_BYTES;
+static_assert(MXG_SCALE_BASE + MXG_SCALE_BUFS * MXG_SCALE_BYTES <= GEMM_LDS_BYTES,
+              "the ring fits in the epilogue's LDS");
+// Loads one wavefront issues per step: four 16-byte copies each of A and B,
+// and on even steps one scale word each of A and B.
+constexpr int MXG_LOADS_ODD = 8, MXG_LOADS_EVEN = 10;
 
 // 16-byte chunk c of LDS row r (8 chunks per 128-byte row), swizzled by
 // (r / 2) % 8.  A 16-byte read serves 16 lanes per cycle (64 banks: 16
@@ -74,36 +78,38 @@ __device__ __forceinline__ GemmStageLds gemm_stage(uint8_t *lds, int buf)
 // slot: half of all LDS cycles were bank conflicts.)
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// Per-lane global offsets of one stage, fixed over the K loop (the K step
-// only moves the wave-uniform base pointers).  Copy i of wavefront w fills
-// LDS rows 8q .. 8q+7, q = 4i + w: lane l lands in row r = 8q + l/8,
-// physical chunk l%8, which holds logical chunk (l%8) ^ ((r/2) % 8) =
-// (l%8) ^ ((4w + l/16) % 8) (the same for every i).  Scale words: row
-// 64w + l.  Rows past M or N are clamped to the last row.  Only the first
-// row and the clamp are kept; the offsets are recomputed per stage (a min
-// and a multiply-add each), which keeps registers for fragments.
-struct GemmOffsets {
-    uint32_t r0, c16;           // first row of copy 0 (8w + l/8), 16 * logical chunk
+// The same for 64-byte rows (4 chunks): slot 4 (r % 4) + (c ^ (r / 4) % 4)
+// is distinct over any 16 consecutive rows.
+__device__ __forceinline__ int swz64(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// Per-lane global offsets of one MXFP8 step, fixed over the K loop (the
+// step only moves the wave-uniform base pointers).  Copy i of wavefront w
+// fills LDS chunks 64 (4i + w) .. +63: lane l lands in row r = 64i + 16w +
+// l/4, physical chunk l%4, which holds logical chunk (l%4) ^ ((r/4) % 4) =
+// (l%4) ^ ((l/16) % 4) (the same for every i).  Scale words: row 64w + l.
+// Rows past M or N are clamped to the last row.
+struct MxgOffsets {
+    uint32_t r0, c16;           // first row of copy 0 (16w + l/4), 16 * logical chunk
     uint32_t ra_max, rb_max;    // last valid row of the A and B tiles
     uint32_t K;
     uint32_t as, bs;            // scale-row offsets (clamped row * K / 32)
     __device__ __forceinline__ uint32_t a(int i) const
     {
-        const uint32_t r = r0 + 32 * i;
+        const uint32_t r = r0 + 64 * i;
         return (r < ra_max ? r : ra_max) * K + c16;
     }
     __device__ __forceinline__ uint32_t b(int i) const
     {
-        const uint32_t r = r0 + 32 * i;
+        const uint32_t r = r0 + 64 * i;
         return (r < rb_max ? r : rb_max) * K + c16;
     }
 };
-__device__ __forceinline__ GemmOffsets gemm_offsets(int64_t m0, int64_t n0, int64_t M, int64_t N,
-                                                    int64_t K, int w, int lane)
+__device__ __forceinline__ MxgOffsets mxg_offsets(int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                                  int64_t K, int w, int lane)
 {
-    GemmOffsets o;
-    o.r0 = (uint32_t)(8 * w + (lane >> 3));
-    o.c16 = 16u * (uint32_t)((lane & 7) ^ ((4 * w + (lane >> 4)) & 7));
+    MxgOffsets o;
+    o.r0 = (uint32_t)(16 * w + (lane >> 2));
+    o.c16 = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     o.ra_max = (uint32_t)(M - 1 - m0 < GEMM_BM ? M - 1 - m0 : GEMM_BM - 1);
     o.rb_max = (uint32_t)(N - 1 - n0 < GEMM_BN ? N - 1 - n0 : GEMM_BN - 1);
     o.K = (uint32_t)K;
@@ -115,10 +121,11 @@ __device__ __forceinline__ GemmOffsets gemm_offsets(int64_t m0, int64_t n0, int6
 
 // Global -> LDS copies of one wavefront: lane l's bytes land at LDS byte
 // address lds + size * l.  Issued as instructions the compiler does not
-// track, so that it does not make the current step's LDS reads wait for the
-// next step's copies (it cannot tell the two buffers apart and would wait
-// for all of them); the kernel orders them itself: every wavefront waits
-// for its own copies (vmcnt 0) before the barrier that publishes a stage.
+// track, so that it does not make the current step's LDS reads wait for
+// later steps' copies (it cannot tell the buffers apart and would wait for
+// all of them); the kernel orders them itself: every wavefront waits for
+// its own copies of a step (a vmcnt that leaves only the later steps'
+// copies outstanding) before the barrier that publishes it.
 __device__ __forceinline__ void lds_copy16(const uint8_t *base, uint32_t off, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -134,32 +141,96 @@ __device__ __forceinline__ void lds_copy4(const uint8_t *base, uint32_t off, uin
                  : "memory", "m0");
 }
 
-// Issue one stage's copies (a, b: the tile's first row at column k0; as_,
-// bs_: its scale row at block k0/32; all wave-uniform, so they sit in scalar
-// registers and each lane adds a 32-bit offset) into the LDS stage at byte
-// address st.
-__device__ __forceinline__ void gemm_issue(uint32_t st, const GemmOffsets &o, const uint8_t *a,
-                                           const uint8_t *as_, const uint8_t *b,
-                                           const uint8_t *bs_, int w)
+// Codes of step s (K columns 64s .. 64s+63 of the tile's A and B rows) into
+// ring stage s % 4 at LDS byte address ring.
+__device__ __forceinline__ void mxg_issue_codes(uint32_t ring, uint32_t s, const MxgOffsets &o,
+                                                const uint8_t *a, const uint8_t *b, int w)
 {
+    const uint32_t st = ring + (s & 3u) * MXG_STAGE_BYTES;
+    const uint8_t *ak = a + (size_t)s * MXG_BK, *bk = b + (size_t)s * MXG_BK;
 #pragma unroll
-    for (int i = 0; i < GEMM_CHUNKS / (4 * 64); i++) {
-        const uint32_t q = (uint32_t)(4 * i + w) * 1024;
-        lds_copy16(a, o.a(i), st + q);
-        lds_copy16(b, o.b(i), st + GEMM_CHUNKS * 16 + q);
+    for (int i = 0; i < 4; i++) {
+        const uint32_t q = (uint32_t)(4 * i + w) * 1024u;
+        lds_copy16(ak, o.a(i), st + q);
+        lds_copy16(bk, o.b(i), st + MXG_OP_BYTES + q);
     }
-    lds_copy4(as_, o.as, st + 2 * GEMM_CHUNKS * 16 + 256 * w);
-    lds_copy4(bs_, o.bs, st + 2 * GEMM_CHUNKS * 16 + GEMM_BM * 4 + 256 * w);
+}
+// Scale group g (blocks 4g .. 4g+3 of every row: steps 2g and 2g + 1) into
+// scale buffer g % 3.
+__device__ __forceinline__ void mxg_issue_scales(uint32_t ring, uint32_t g, const MxgOffsets &o,
+                                                 const uint8_t *as_, const uint8_t *bs_, int w)
+{
+    const uint32_t sb = ring + MXG_SCALE_BASE + (g % 3u) * MXG_SCALE_BYTES;
+    lds_copy4(as_ + 4 * (size_t)g, o.as, sb + 256 * w);
+    lds_copy4(bs_ + 4 * (size_t)g, o.bs, sb + GEMM_BM * 4 + 256 * w);
 }
 
-// One 32x64 fragment (A rows or B columns) of K sub-step s for this lane:
-// bytes 0..15 from logical chunk 4s + h (k = 64s + 16h, block 2s), bytes
-// 16..31 from chunk 4s + 2 + h (k = 64s + 32 + 16h, block 2s + 1).
-__device__ __forceinline__ i32x8_t gemm_frag(const u32x4_t *tile, int r, int h, int s)
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited), then a workgroup
+// barrier.  The empty asm statements keep the compiler from moving LDS
+// accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void mxg_sync()
 {
-    const u32x4_t lo = tile[swz(r, 4 * s + h)];
-    const u32x4_t hi = tile[swz(r, 4 * s + 2 + h)];
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One lane's operands of a step: for each of its 4 row blocks of A and of
+// B, 32 bytes of codes (bytes 0..15: k = 16h .. 16h+15, chunk h; bytes
+// 16..31: k = 32 + 16h .., chunk 2 + h) and the row's scale word (blocks
+// 4g .. 4g+3 of the step's group g).
+struct MxgFrags {
+    i32x8_t a[4], b[4];
+    uint32_t sa[4], sb[4];
+};
+__device__ __forceinline__ i32x8_t mxg_frag(const u32x4_t *tile, int r, int h)
+{
+    const u32x4_t lo = tile[swz64(r, h)];
+    const u32x4_t hi = tile[swz64(r, 2 + h)];
     return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ void mxg_read(MxgFrags &f, const uint8_t *lds, uint32_t t, int wm,
+                                         int wn, int r32, int h)
+{
+    const uint8_t *st = lds + (t & 3u) * MXG_STAGE_BYTES;
+    const u32x4_t *ta = reinterpret_cast<const u32x4_t *>(st);
+    const u32x4_t *tb = reinterpret_cast<const u32x4_t *>(st + MXG_OP_BYTES);
+    const uint32_t *sw = reinterpret_cast<const uint32_t *>(lds + MXG_SCALE_BASE +
+                                                             ((t >> 1) % 3u) * MXG_SCALE_BYTES);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int ra = 128 * wm + 32 * i + r32, rb = 128 * wn + 32 * i + r32;
+        f.a[i] = mxg_frag(ta, ra, h);
+        f.b[i] = mxg_frag(tb, rb, h);
+        f.sa[i] = sw[ra];
+        f.sb[i] = sw[GEMM_BM + rb];
+    }
+}
+// The step's 16 matrix instructions.  B is the instruction's first operand,
+// so the accumulator of block (i, j) holds C transposed: lane (r, h) holds
+// C[32i + r][32j + 8g + 4h + e] in element 4g + e, four consecutive columns.
+// Scales: the instruction takes byte OPSEL of each lane's scale register,
+// block 0 of the step from lanes h = 0 and block 1 from lanes h = 1, so lane
+// h's word is shifted right by 8h (here, after the step's barrier, so that
+// the shift does not make the previous step wait for its reads).
+template <int OPSEL>
+__device__ __forceinline__ void mxg_mfma(f32x16_t (&acc)[4][4], const MxgFrags &f, int h)
+{
+    int sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        sa[i] = (int)(f.sa[i] >> (8 * h));
+        sb[i] = (int)(f.sb[i] >> (8 * h));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f.b[j], f.a[i], acc[i][j], 0, 0, OPSEL, sb[j], OPSEL, sa[i]);
 }
 
 // Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
@@ -270,6 +341,108 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8
     }
 }
 
+// Write the wavefront's 128x128 quarter of the C tile from the transposed
+// accumulators of mxg_mfma: lane (r, h) holds, for each block (i, j) and
+// g = 0..3, C[32i + r][32j + 8g + 4h .. +3].  BF16: through LDS (rows
+// padded to 272 bytes; one 8-byte write per four values) and out as 16-byte
+// stores covering 256 contiguous bytes of a row; the caller has synchronised
+// the workgroup, so LDS is free.  FP32: one 16-byte store per four values.
+// Order of a step's instructions for the scheduler: the next step's 20 LDS
+// reads (16 fragment halves, 4 scale-word pairs) go out among the first
+// matrix instructions, four after each of the first five, so that they
+// return under the step's matrix work instead of delaying its final wait.
+__device__ __forceinline__ void mxg_interleave()
+{
+#pragma unroll
+    for (int k = 0; k < 5; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // matrix
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 11, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool BF16_OUT>
+__device__ __forceinline__ void mxg_epilogue(const f32x16_t (&acc)[4][4], uint8_t *lds, int wave,
+                                             int lane, int64_t m0, int64_t n0, int64_t M,
+                                             int64_t N, void *__restrict__ C)
+{
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, h = lane >> 5;
+    if constexpr (BF16_OUT) {
+        uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const bf16x2_t lo = {(__bf16)acc[i][j][4 * g], (__bf16)acc[i][j][4 * g + 1]};
+                    const bf16x2_t hi = {(__bf16)acc[i][j][4 * g + 2],
+                                         (__bf16)acc[i][j][4 * g + 3]};
+                    const int r = 32 * i + r32, c = 32 * j + 8 * g + 4 * h;
+                    *reinterpret_cast<uint2_t *>(q + r * GEMM_EPI_ROW + 2 * c) =
+                        uint2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                }
+        __syncthreads();
+        const int64_t col = n0 + 128 * wn + 8 * (lane & 15);
+        uint16_t *c = reinterpret_cast<uint16_t *>(C);
+        // 16-byte stores need every row start 16-byte aligned.
+        const bool vec = (N & 7) == 0 && ((uintptr_t)C & 15) == 0;
+        for (int rr = 0; rr < 128; rr += 4) {
+            const int r = rr + (lane >> 4);
+            const int64_t m = m0 + 128 * wm + r;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(q + r * GEMM_EPI_ROW +
+                                                                  16 * (lane & 15));
+            if (m < M) {
+                if (vec && col + 8 <= N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + col));
+                } else {
+                    const uint16_t *p = reinterpret_cast<const uint16_t *>(&v);
+                    for (int e = 0; e < 8 && col + e < N; e++)
+                        c[m * N + col + e] = p[e];
+                }
+            }
+        }
+    } else {
+        float *c = reinterpret_cast<float *>(C);
+        const bool vec = (N & 3) == 0 && ((uintptr_t)C & 15) == 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t m = m0 + 128 * wm + 32 * i + r32;
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int64_t n = n0 + 128 * wn + 32 * j + 8 * g + 4 * h;
+                    if (vec && n + 4 <= N) {
+                        const u32x4_t v = {f2u(acc[i][j][4 * g]), f2u(acc[i][j][4 * g + 1]),
+                                           f2u(acc[i][j][4 * g + 2]), f2u(acc[i][j][4 * g + 3])};
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + n));
+                    } else {
+                        for (int e = 0; e < 4 && n + e < N; e++)
+                            c[m * N + n + e] = acc[i][j][4 * g + e];
+                    }
+                }
+        }
+    }
+}
+
+// MXFP8 GEMM.  A workgroup of four wavefronts computes a 256x256 tile of C
+// in K steps of 64 (one matrix instruction deep); wavefront (wm, wn) owns a
+// 128x128 quarter: 4x4 instruction tiles, 256 fp32 accumulators per lane.
+// Pipeline, per step s: issue the global -> LDS copies of step s + 3 into
+// ring stage (s + 3) % 4 (the stage step s - 1 used, read by everyone
+// before the previous barrier); read step s + 1's fragments and scale words
+// into registers; run step s's 16 matrix instructions on the registers read
+// during step s - 1; wait for this wavefront's copies of step s + 2 and for
+// its LDS reads; barrier.  So a copy has three steps to land, and LDS reads
+// run under the matrix instructions.  Scale groups (4 blocks, two steps)
+// travel with the even steps into a ring of three buffers.  The loop is
+// unrolled by two so that the registers of alternate steps and the scale
+// byte selectors are static.
 template <bool BF16_OUT>
 __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
@@ -286,7 +459,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
         return;
     const int64_t m0 = (int64_t)mt * GEMM_BM;
     const int64_t n0 = (int64_t)nt * GEMM_BN;
-    const int64_t ksteps = K / GEMM_BK;
+    const uint32_t nsteps = (uint32_t)(K / MXG_BK);          // even: K % 128 == 0
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -295,57 +468,64 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
         for (int j = 0; j < 4; j++)
             acc[i][j] = f32x16_t{};
 
-    const GemmOffsets off = gemm_offsets(m0, n0, M, N, K, wave, lane);
+    const MxgOffsets off = mxg_offsets(m0, n0, M, N, K, wave, lane);
     const uint8_t *a = A + m0 * K, *b = B + n0 * K;
     const uint8_t *as_ = As + m0 * (K >> 5), *bs_ = Bs + n0 * (K >> 5);
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-    gemm_issue(lds_addr, off, a, as_, b, bs_, wave);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    const uint32_t ring = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
 
-    for (int64_t ks = 0; ks < ksteps; ks++) {
-        const GemmStageLds cur = gemm_stage(lds, (int)(ks & 1));
-        if (ks + 1 < ksteps) {
-            const int64_t k1 = (ks + 1) * GEMM_BK;
-            gemm_issue(lds_addr + (uint32_t)((ks + 1) & 1) * GEMM_STAGE_BYTES, off, a + k1,
-                       as_ + (k1 >> 5), b + k1, bs_ + (k1 >> 5), wave);
-        }
-        uint32_t sa[4], sb[4];
-        i32x8_t fa[2][4], fb[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            sa[i] = cur.as[128 * wm + 32 * i + r32] >> (8 * h);
-            sb[i] = cur.bs[128 * wn + 32 * i + r32] >> (8 * h);
-            fa[0][i] = gemm_frag(cur.a, 128 * wm + 32 * i + r32, h, 0);
-            fb[0][i] = gemm_frag(cur.b, 128 * wn + 32 * i + r32, h, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            fa[1][i] = gemm_frag(cur.a, 128 * wm + 32 * i + r32, h, 1);
-            fb[1][i] = gemm_frag(cur.b, 128 * wn + 32 * i + r32, h, 1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[0][i], fb[0][j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[1][i], fb[1][j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
-        // This wavefront's copies of the next stage have landed (and its
-        // reads of this one returned); after the barrier, everyone's have.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    // Prologue: steps 0, 1 and 2 in flight; wait for steps 0 and 1.
+    mxg_issue_codes(ring, 0, off, a, b, wave);
+    mxg_issue_scales(ring, 0, off, as_, bs_, wave);
+    mxg_issue_codes(ring, 1, off, a, b, wave);
+    if (nsteps > 2) {
+        mxg_issue_codes(ring, 2, off, a, b, wave);
+        mxg_issue_scales(ring, 1, off, as_, bs_, wave);
+        mxg_sync<MXG_LOADS_EVEN>();
+    } else {
+        mxg_sync<0>();
     }
+    MxgFrags f0, f1;
+    mxg_read(f0, lds, 0, wm, wn, r32, h);
 
-    // The epilogue reuses the stage buffers: no wavefront may still be
-    // reading them.
+    // Steady state: both steps issue copies.
+    uint32_t s = 0;
+    for (; s + 4 < nsteps; s += 2) {
+        // Step s (even): matrix work on f0; read step s + 1 into f1.
+        mxg_issue_codes(ring, s + 3, off, a, b, wave);
+        mxg_read(f1, lds, s + 1, wm, wn, r32, h);
+        mxg_mfma<0>(acc, f0, h);
+        mxg_interleave();
+        mxg_sync<MXG_LOADS_ODD>();
+        // Step s + 1 (odd): matrix work on f1; read step s + 2 into f0.
+        mxg_issue_codes(ring, s + 4, off, a, b, wave);
+        mxg_issue_scales(ring, (s + 4) >> 1, off, as_, bs_, wave);
+        mxg_read(f0, lds, s + 2, wm, wn, r32, h);
+        mxg_mfma<2>(acc, f1, h);
+        mxg_interleave();
+        mxg_sync<MXG_LOADS_EVEN>();
+    }
+    // The last two or four steps (s = nsteps - 4 or nsteps - 2).
+    if (s + 4 == nsteps) {
+        mxg_issue_codes(ring, s + 3, off, a, b, wave);
+        mxg_read(f1, lds, s + 1, wm, wn, r32, h);
+        mxg_mfma<0>(acc, f0, h);
+        mxg_interleave();
+        mxg_sync<MXG_LOADS_ODD>();
+        mxg_read(f0, lds, s + 2, wm, wn, r32, h);
+        mxg_mfma<2>(acc, f1, h);
+        mxg_interleave();
+        mxg_sync<0>();
+    }
+    mxg_read(f1, lds, nsteps - 1, wm, wn, r32, h);
+    mxg_mfma<0>(acc, f0, h);
+    mxg_interleave();
+    mxg_sync<0>();
+    mxg_mfma<2>(acc, f1, h);
+
+    // Every copy has landed and every LDS read returned (the last syncs wait
+    // for all); after this barrier no wavefront reads the ring.
     __syncthreads();
-    gemm_epilogue<BF16_OUT, false>(acc, lds, wave, lane, m0, n0, M, N, C, nullptr, 1, nullptr, 1);
+    mxg_epilogue<BF16_OUT>(acc, lds, wave, lane, m0, n0, M, N, C);
 }
 
 // ---------------------------------------------------------------------------
