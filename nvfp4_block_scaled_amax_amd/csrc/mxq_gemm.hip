@@ -46,6 +46,7 @@ namespace mxq {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
 constexpr int GEMM_BM = 256, GEMM_BN = 256;
@@ -54,7 +55,8 @@ static_assert(GEMM_BM == 256 && GEMM_BN == 256 && GEMM_THREADS == 256,
               "MAX_GEMM_TILES counts 256 x 256 tiles of 256 threads");
 constexpr int GEMM_EPI_ROW = 128 * 2 + 16;                      // padded BF16 row of a quarter
 constexpr int GEMM_EPI_BYTES = 4 * 128 * GEMM_EPI_ROW;
-constexpr int GEMM_LDS_BYTES = GEMM_EPI_BYTES;                  // 136 KiB, the largest LDS use
+constexpr int GEMM_SCALE_BYTES = 2 * GEMM_BM * 4;                // epilogue row and column scales
+constexpr int GEMM_LDS_BYTES = GEMM_EPI_BYTES + GEMM_SCALE_BYTES;  // 138 KiB
 
 // MXFP8 ring: four 64-deep K steps of A and B codes (16 KiB each) and three
 // buffers of scale words (one 4-block word per row of A and of B).
@@ -257,96 +259,6 @@ __device__ __forceinline__ bool gemm_tile(const GemmGrid &g, uint32_t w, uint32_
     return true;
 }
 
-// Write the wavefront's 128x128 quarter of the C tile.  Lane holds column
-// r32 of each instruction tile, rows 8(e/4) + 4h + e%4.  SCALED: multiply by
-// the FP32 scales of the row (sa[m / rows_per_a]) and of the column
-// (sb[n / rows_per_b]), as fp32(fp32(acc * sa) * sb).  BF16: through LDS
-// (rows padded to 272 bytes), 16 lanes per 256-byte row, 4 rows per store
-// instruction; the caller has synchronised the workgroup, so LDS is free.
-template <bool BF16_OUT, bool SCALED>
-__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8_t *lds, int wave,
-                                              int lane, int64_t m0, int64_t n0, int64_t M,
-                                              int64_t N, void *__restrict__ C,
-                                              const float *__restrict__ sa, int64_t rows_per_a,
-                                              const float *__restrict__ sb, int64_t rows_per_b)
-{
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r32 = lane & 31, h = lane >> 5;
-    float cs[4] = {1.0f, 1.0f, 1.0f, 1.0f};     // column scales of the lane's 4 columns
-    if constexpr (SCALED) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            int64_t n = n0 + 128 * wn + 32 * j + r32;
-            n = n < N ? n : N - 1;
-            cs[j] = sb[n / rows_per_b];
-        }
-    }
-    auto value = [&](int i, int j, int e) {
-        float v = acc[i][j][e];
-        if constexpr (SCALED) {
-            int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-            m = m < M ? m : M - 1;
-            v = (v * sa[m / rows_per_a]) * cs[j];
-        }
-        return v;
-    };
-    if constexpr (BF16_OUT) {
-        uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-#pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int r = 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-                    const uint32_t u = f2u(value(i, j, e));
-                    *reinterpret_cast<uint16_t *>(q + r * GEMM_EPI_ROW + 2 * (32 * j + r32)) =
-                        (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-                }
-        __syncthreads();
-        const int64_t col = n0 + 128 * wn + 8 * (lane & 15);
-        uint16_t *c = reinterpret_cast<uint16_t *>(C);
-        // 16-byte stores need every row start 16-byte aligned.
-        const bool vec = (N & 7) == 0 && ((uintptr_t)C & 15) == 0;
-        for (int rr = 0; rr < 128; rr += 4) {
-            const int r = rr + (lane >> 4);
-            const int64_t m = m0 + 128 * wm + r;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(q + r * GEMM_EPI_ROW +
-                                                                  16 * (lane & 15));
-            if (m < M) {
-                if (vec && col + 8 <= N) {
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + col));
-                } else {
-                    const uint16_t *p = reinterpret_cast<const uint16_t *>(&v);
-                    for (int e = 0; e < 8 && col + e < N; e++)
-                        c[m * N + col + e] = p[e];
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t n = n0 + 128 * wn + 32 * j + r32;
-            if (n >= N)
-                continue;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-                    if (m < M)
-                        reinterpret_cast<float *>(C)[m * N + n] = value(i, j, e);
-                }
-        }
-    }
-}
-
-// Write the wavefront's 128x128 quarter of the C tile from the transposed
-// accumulators of mxg_mfma: lane (r, h) holds, for each block (i, j) and
-// g = 0..3, C[32i + r][32j + 8g + 4h .. +3].  BF16: through LDS (rows
-// padded to 272 bytes; one 8-byte write per four values) and out as 16-byte
-// stores covering 256 contiguous bytes of a row; the caller has synchronised
-// the workgroup, so LDS is free.  FP32: one 16-byte store per four values.
 // Order of a step's instructions for the scheduler: the next step's 20 LDS
 // reads (16 fragment halves, 4 scale-word pairs) go out among the first
 // matrix instructions, four after each of the first five, so that they
@@ -362,13 +274,52 @@ __device__ __forceinline__ void mxg_interleave()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool BF16_OUT>
-__device__ __forceinline__ void mxg_epilogue(const f32x16_t (&acc)[4][4], uint8_t *lds, int wave,
-                                             int lane, int64_t m0, int64_t n0, int64_t M,
-                                             int64_t N, void *__restrict__ C)
+// Write the wavefront's 128x128 quarter of the C tile from transposed
+// accumulators (B was the matrix instructions' first operand): lane (r, h)
+// holds, for each block (i, j) and g = 0..3, C[32i + r][32j + 8g + 4h .. +3]
+// in elements 4g .. 4g+3.  SCALED: multiply by the FP32 scales of the row
+// (sa[m / rows_per_a]) and of the column (sb[n / rows_per_b]), as
+// fp32(fp32(acc * sa) * sb).  BF16: through LDS (rows padded to 272 bytes;
+// one 8-byte write per four values) and out as 16-byte stores covering 256
+// contiguous bytes of a row; the caller has synchronised the workgroup, so
+// LDS is free.  FP32: one 16-byte store per four values.
+template <bool BF16_OUT, bool SCALED>
+__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8_t *lds, int wave,
+                                              int lane, int64_t m0, int64_t n0, int64_t M,
+                                              int64_t N, void *__restrict__ C,
+                                              const float *__restrict__ sa, int64_t rows_per_a,
+                                              const float *__restrict__ sb, int64_t rows_per_b)
 {
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
+    // SCALED: the tile's 256 row and 256 column scales go to LDS past the
+    // staging area (one of each per thread), so that a lane's 64 columns
+    // take 16 reads of four consecutive scales and no division each.
+    float rs[4] = {1.0f, 1.0f, 1.0f, 1.0f};     // row scales of the lane's 4 rows
+    const float *csc = nullptr;                 // the tile's column scales in LDS
+    if constexpr (SCALED) {
+        float *sc = reinterpret_cast<float *>(lds + GEMM_EPI_BYTES);
+        const int t = 64 * wave + lane;
+        const int64_t m = m0 + t < M ? m0 + t : M - 1;
+        const int64_t n = n0 + t < N ? n0 + t : N - 1;
+        sc[t] = sa[m / rows_per_a];
+        sc[GEMM_BM + t] = sb[n / rows_per_b];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            rs[i] = sc[128 * wm + 32 * i + r32];
+        csc = sc + GEMM_BM + 128 * wn;
+    }
+    // The four values of block (i, j), group g, scaled.
+    auto quad = [&](int i, int j, int g) {
+        f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                     acc[i][j][4 * g + 3]};
+        if constexpr (SCALED) {
+            const f32x4_t cs = *reinterpret_cast<const f32x4_t *>(csc + 32 * j + 8 * g + 4 * h);
+            v = (v * rs[i]) * cs;
+        }
+        return v;
+    };
     if constexpr (BF16_OUT) {
         uint8_t *q = lds + wave * (128 * GEMM_EPI_ROW);
 #pragma unroll
@@ -377,9 +328,9 @@ __device__ __forceinline__ void mxg_epilogue(const f32x16_t (&acc)[4][4], uint8_
             for (int j = 0; j < 4; j++)
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    const bf16x2_t lo = {(__bf16)acc[i][j][4 * g], (__bf16)acc[i][j][4 * g + 1]};
-                    const bf16x2_t hi = {(__bf16)acc[i][j][4 * g + 2],
-                                         (__bf16)acc[i][j][4 * g + 3]};
+                    const f32x4_t v = quad(i, j, g);
+                    const bf16x2_t lo = {(__bf16)v[0], (__bf16)v[1]};
+                    const bf16x2_t hi = {(__bf16)v[2], (__bf16)v[3]};
                     const int r = 32 * i + r32, c = 32 * j + 8 * g + 4 * h;
                     *reinterpret_cast<uint2_t *>(q + r * GEMM_EPI_ROW + 2 * c) =
                         uint2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
@@ -417,13 +368,13 @@ __device__ __forceinline__ void mxg_epilogue(const f32x16_t (&acc)[4][4], uint8_
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
                     const int64_t n = n0 + 128 * wn + 32 * j + 8 * g + 4 * h;
+                    const f32x4_t v = quad(i, j, g);
                     if (vec && n + 4 <= N) {
-                        const u32x4_t v = {f2u(acc[i][j][4 * g]), f2u(acc[i][j][4 * g + 1]),
-                                           f2u(acc[i][j][4 * g + 2]), f2u(acc[i][j][4 * g + 3])};
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(c + m * N + n));
+                        const u32x4_t u = {f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
+                        __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t *>(c + m * N + n));
                     } else {
                         for (int e = 0; e < 4 && n + e < N; e++)
-                            c[m * N + n + e] = acc[i][j][4 * g + e];
+                            c[m * N + n + e] = v[e];
                     }
                 }
         }
@@ -525,7 +476,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     // Every copy has landed and every LDS read returned (the last syncs wait
     // for all); after this barrier no wavefront reads the ring.
     __syncthreads();
-    mxg_epilogue<BF16_OUT>(acc, lds, wave, lane, m0, n0, M, N, C);
+    gemm_epilogue<BF16_OUT, false>(acc, lds, wave, lane, m0, n0, M, N, C, nullptr, 1, nullptr, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -542,6 +493,12 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
 // BF16 instruction: v_mfma_f32_32x32x16_bf16, lane (r, h) holds 8
 // consecutive K values: chunk 2s + h (16 bytes) of the 64-element step for
 // slice s.  LDS rows are 64 BF16 = 128 bytes, swizzled as above.
+//
+// Measured (2048x8192x2048, BF16 result): the earlier form, which ran the
+// step's 64 matrix instructions and then the next step's dequantization,
+// took 104 us; interleaving the dequantization with the matrix instructions
+// (and the transposed epilogue) 80 us (8192x8192x2048: 372 -> 287 us),
+// byte-identical.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int NVG_BK = 64;                                       // K elements per step
@@ -590,6 +547,93 @@ __device__ __forceinline__ void nv_store_row(u32x4_t *tile, int r, const u32x4_t
     }
 }
 
+__device__ __forceinline__ u32x4_t *nvg_tile_a(uint8_t *lds, int buf)
+{
+    return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES);
+}
+__device__ __forceinline__ u32x4_t *nvg_tile_b(uint8_t *lds, int buf)
+{
+    return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES + GEMM_BM * NVG_BK * 2);
+}
+
+// Fragments of slice sl (16 K values) for the wavefront's 4 row blocks of A
+// and of B.
+__device__ __forceinline__ void nvg_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4],
+                                          const u32x4_t *ta, const u32x4_t *tb, int sl, int wm,
+                                          int wn, int r32, int h)
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        fa[i] = __builtin_bit_cast(bf16x8_t, ta[swz(128 * wm + 32 * i + r32, 2 * sl + h)]);
+        fb[i] = __builtin_bit_cast(bf16x8_t, tb[swz(128 * wn + 32 * i + r32, 2 * sl + h)]);
+    }
+}
+// Row i's 4 instructions of a slice; B is the first operand, so the
+// accumulators hold C transposed (the layout gemm_epilogue takes).
+__device__ __forceinline__ void nvg_mfma_row(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                             const bf16x8_t (&fb)[4], int i)
+{
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// Chunk u (0..15: A's 8 chunks, then B's) of row t of the next step,
+// dequantized into stage buf.
+__device__ __forceinline__ void nvg_convert(uint8_t *lds, int buf, const NvStage &nx, int t, int u)
+{
+    const bool isb = u >= 8;
+    const int j = u & 7;
+    const u32x4_t *c = isb ? nx.cb : nx.ca;
+    const uint32_t sc = isb ? nx.sb : nx.sa;
+    const float d = e4m3_value((sc >> (8 * (j >> 1))) & 0xFFu);
+    u32x4_t *tile = isb ? nvg_tile_b(lds, buf) : nvg_tile_a(lds, buf);
+    tile[swz(t, j)] = nv_chunk_bf16(c[j >> 2][j & 3], d);
+}
+
+// One K step: the 64 matrix instructions on LDS stage buf and, if CONVERT,
+// the dequantization of the next step (registers nx) into the other stage,
+// in a fixed order: per slice, the next slice's fragments are read first;
+// then per row block i, its 4 (independent) instructions and one chunk of
+// the conversion, fenced from the next group so that the compiler neither
+// chains dependent instructions nor moves the VALU work after the matrix
+// work.  The VALU work then runs while the matrix unit is busy.
+template <bool CONVERT>
+__device__ __forceinline__ void nvg_step(f32x16_t (&acc)[4][4], uint8_t *lds, int buf,
+                                         const NvStage &nx, int t, int wm, int wn, int r32, int h)
+{
+    const u32x4_t *ta = nvg_tile_a(lds, buf), *tb = nvg_tile_b(lds, buf);
+    bf16x8_t fa[2][4], fb[2][4];
+    nvg_frags(fa[0], fb[0], ta, tb, 0, wm, wn, r32, h);
+#pragma unroll
+    for (int sl = 0; sl < 4; sl++) {
+        if (sl < 3)
+            nvg_frags(fa[(sl + 1) & 1], fb[(sl + 1) & 1], ta, tb, sl + 1, wm, wn, r32, h);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            nvg_mfma_row(acc, fa[sl & 1], fb[sl & 1], i);
+            if constexpr (CONVERT)
+                nvg_convert(lds, buf ^ 1, nx, t, 4 * sl + i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// lgkmcnt(0) (this wavefront's LDS writes and reads done) and a workgroup
+// barrier, leaving global loads in flight (the compiler waits for those
+// where their registers are used).
+__device__ __forceinline__ void nvg_sync()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Pipeline: step ks computes from LDS stage ks % 2 while the registers of
+// step ks + 1 (loaded one step earlier) are dequantized into the other
+// stage and step ks + 2 is loaded into the registers step ks used.  The
+// loop is unrolled by two so that the two register sets keep their roles.
 template <bool BF16_OUT>
 __global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ Ab, const float *__restrict__ As,
@@ -613,6 +657,11 @@ __global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
     const uint32_t rb = (uint32_t)(n0 + t < N ? t : N - 1 - n0);
     const uint8_t *a = A + m0 * (K >> 1), *b = B + n0 * (K >> 1);
     const uint8_t *ab = Ab + m0 * (K >> 4), *bb = Bb + n0 * (K >> 4);
+    auto load = [&](NvStage &st, int64_t step) {
+        const int64_t k = step * NVG_BK;
+        nv_load(st, a + (k >> 1), ab + (k >> 4), b + (k >> 1), bb + (k >> 4), ra, rb, half_k,
+                blk_k);
+    };
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -621,47 +670,30 @@ __global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
         for (int j = 0; j < 4; j++)
             acc[i][j] = f32x16_t{};
 
-    auto tile_a = [&](int buf) { return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES); };
-    auto tile_b = [&](int buf) {
-        return reinterpret_cast<u32x4_t *>(lds + buf * NVG_STAGE_BYTES + GEMM_BM * NVG_BK * 2);
-    };
-    NvStage st;
-    nv_load(st, a, ab, b, bb, ra, rb, half_k, blk_k);
-    nv_store_row(tile_a(0), t, st.ca, st.sa);
-    nv_store_row(tile_b(0), t, st.cb, st.sb);
-    __syncthreads();
+    // Loads past the last step re-read the last step (valid memory); their
+    // conversions land in a stage no later step reads.  So the loop body has
+    // no branch and the register sets of alternate steps stay static.
+    const int64_t last = ksteps - 1;
+    NvStage s0, s1;
+    load(s0, 0);
+    load(s1, last < 1 ? last : 1);
+    nv_store_row(nvg_tile_a(lds, 0), t, s0.ca, s0.sa);
+    nv_store_row(nvg_tile_b(lds, 0), t, s0.cb, s0.sb);
+    nvg_sync();
 
-    for (int64_t ks = 0; ks < ksteps; ks++) {
-        const int buf = (int)(ks & 1);
-        const bool more = ks + 1 < ksteps;
-        if (more) {
-            const int64_t k1 = (ks + 1) * NVG_BK;
-            nv_load(st, a + (k1 >> 1), ab + (k1 >> 4), b + (k1 >> 1), bb + (k1 >> 4), ra, rb,
-                    half_k, blk_k);
-        }
-        const u32x4_t *ta = tile_a(buf), *tb = tile_b(buf);
-#pragma unroll
-        for (int sl = 0; sl < NVG_BK / 16; sl++) {
-            bf16x8_t fb[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                fb[j] = __builtin_bit_cast(bf16x8_t, tb[swz(128 * wn + 32 * j + r32, 2 * sl + h)]);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const bf16x8_t fa =
-                    __builtin_bit_cast(bf16x8_t, ta[swz(128 * wm + 32 * i + r32, 2 * sl + h)]);
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0,
-                                                                        0);
-            }
-        }
-        if (more) {
-            nv_store_row(tile_a(buf ^ 1), t, st.ca, st.sa);
-            nv_store_row(tile_b(buf ^ 1), t, st.cb, st.sb);
-        }
-        __syncthreads();
+    int64_t ks = 0;
+    for (; ks + 1 < ksteps; ks += 2) {
+        load(s0, ks + 2 < last ? ks + 2 : last);
+        nvg_step<true>(acc, lds, 0, s1, t, wm, wn, r32, h);
+        nvg_sync();
+        load(s1, ks + 3 < last ? ks + 3 : last);
+        nvg_step<true>(acc, lds, 1, s0, t, wm, wn, r32, h);
+        nvg_sync();
     }
+    if (ks < ksteps)                        // odd step count: the last step
+        nvg_step<false>(acc, lds, 0, s0, t, wm, wn, r32, h);
+    // No wavefront reads the stages after this barrier.
+    __syncthreads();
     gemm_epilogue<BF16_OUT, true>(acc, lds, wave, lane, m0, n0, M, N, C, As, rows_per_a, Bs,
                                   rows_per_b);
 }
