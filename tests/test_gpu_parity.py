@@ -886,6 +886,16 @@ def test_nvfp4_gemm_shapes(orc):
         check_nvfp4_gemm(orc, qa, (wc[0], wb[0], ws), N, f"t3 x N(0,0.02) {M}x{N}x{K}")
 
 
+def test_nvfp4_gemm_per_row_b_scales(orc):
+    """Both operands per-token NVFP4 (one FP32 scale per row of A and of B:
+    rows_per_b_scale 1), five K steps (the pipeline's odd tail after a full
+    unrolled pair), ragged M and N."""
+    M, N, K = 300, 200, 320
+    qa = orc.nvfp4_per_token(W.student_t_activations(M, K, 11))
+    qb = orc.nvfp4_per_token(W.student_t_activations(N, K, 12))
+    check_nvfp4_gemm(orc, qa, qb, 1, f"per-token x per-token {M}x{N}x{K}")
+
+
 def test_nvfp4_gemm_dense_forward_full(orc):
     """The dense forward at the pages' shape: 2048 tokens x 2048 (per-token
     NVFP4) times an 8192 x 2048 weight with one scope scale; 384 sampled rows."""
