@@ -180,10 +180,14 @@ __device__ __forceinline__ void mxg_sync()
     asm volatile("" ::: "memory");
 }
 
-// One lane's operands of a step: for each of its 4 row blocks of A and of
+// One lane's operands of step t: for each of its 4 row blocks of A and of
 // B, 32 bytes of codes (bytes 0..15: k = 16h .. 16h+15, chunk h; bytes
-// 16..31: k = 32 + 16h .., chunk 2 + h) and the row's scale word (blocks
-// 4g .. 4g+3 of the step's group g).
+// 16..31: k = 32 + 16h .., chunk 2 + h) and the row's scale byte for the
+// lane's block of the step (block 2 (t % 2) + h of the scale word), read
+// alone so that it arrives in byte 0 of the register: the matrix
+// instruction takes block 0's scale from lanes h = 0 and block 1's from
+// lanes h = 1, both at byte 0 (no VALU shift before the instructions; with
+// shifts, the instructions ran ~13 cycles apart more).
 struct MxgFrags {
     i32x8_t a[4], b[4];
     uint32_t sa[4], sb[4];
@@ -194,45 +198,34 @@ __device__ __forceinline__ i32x8_t mxg_frag(const u32x4_t *tile, int r, int h)
     const u32x4_t hi = tile[swz64(r, 2 + h)];
     return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+template <int PAR>       // t % 2
 __device__ __forceinline__ void mxg_read(MxgFrags &f, const uint8_t *lds, uint32_t t, int wm,
                                          int wn, int r32, int h)
 {
     const uint8_t *st = lds + (t & 3u) * MXG_STAGE_BYTES;
     const u32x4_t *ta = reinterpret_cast<const u32x4_t *>(st);
     const u32x4_t *tb = reinterpret_cast<const u32x4_t *>(st + MXG_OP_BYTES);
-    const uint32_t *sw = reinterpret_cast<const uint32_t *>(lds + MXG_SCALE_BASE +
-                                                             ((t >> 1) % 3u) * MXG_SCALE_BYTES);
+    const uint8_t *sb = lds + MXG_SCALE_BASE + ((t >> 1) % 3u) * MXG_SCALE_BYTES + 2 * PAR + h;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int ra = 128 * wm + 32 * i + r32, rb = 128 * wn + 32 * i + r32;
         f.a[i] = mxg_frag(ta, ra, h);
         f.b[i] = mxg_frag(tb, rb, h);
-        f.sa[i] = sw[ra];
-        f.sb[i] = sw[GEMM_BM + rb];
+        f.sa[i] = sb[4 * ra];
+        f.sb[i] = sb[4 * (GEMM_BM + rb)];
     }
 }
 // The step's 16 matrix instructions.  B is the instruction's first operand,
 // so the accumulator of block (i, j) holds C transposed: lane (r, h) holds
 // C[32i + r][32j + 8g + 4h + e] in element 4g + e, four consecutive columns.
-// Scales: the instruction takes byte OPSEL of each lane's scale register,
-// block 0 of the step from lanes h = 0 and block 1 from lanes h = 1, so lane
-// h's word is shifted right by 8h (here, after the step's barrier, so that
-// the shift does not make the previous step wait for its reads).
-template <int OPSEL>
-__device__ __forceinline__ void mxg_mfma(f32x16_t (&acc)[4][4], const MxgFrags &f, int h)
+__device__ __forceinline__ void mxg_mfma(f32x16_t (&acc)[4][4], const MxgFrags &f)
 {
-    int sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        sa[i] = (int)(f.sa[i] >> (8 * h));
-        sb[i] = (int)(f.sb[i] >> (8 * h));
-    }
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                f.b[j], f.a[i], acc[i][j], 0, 0, OPSEL, sb[j], OPSEL, sa[i]);
+                f.b[j], f.a[i], acc[i][j], 0, 0, 0, (int)f.sb[j], 0, (int)f.sa[i]);
 }
 
 // Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
@@ -259,18 +252,18 @@ __device__ __forceinline__ bool gemm_tile(const GemmGrid &g, uint32_t w, uint32_
     return true;
 }
 
-// Order of a step's instructions for the scheduler: the next step's 20 LDS
-// reads (16 fragment halves, 4 scale-word pairs) go out among the first
-// matrix instructions, four after each of the first five, so that they
-// return under the step's matrix work instead of delaying its final wait.
+// Order of a step's instructions for the scheduler: the next step's 24 LDS
+// reads (16 fragment halves, 8 scale bytes) go out among the first matrix
+// instructions, four after each of the first six, so that they return under
+// the step's matrix work instead of delaying its final wait.
 __device__ __forceinline__ void mxg_interleave()
 {
 #pragma unroll
-    for (int k = 0; k < 5; k++) {
+    for (int k = 0; k < 6; k++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // matrix
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // LDS reads
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -436,42 +429,42 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
         mxg_sync<0>();
     }
     MxgFrags f0, f1;
-    mxg_read(f0, lds, 0, wm, wn, r32, h);
+    mxg_read<0>(f0, lds, 0, wm, wn, r32, h);
 
     // Steady state: both steps issue copies.
     uint32_t s = 0;
     for (; s + 4 < nsteps; s += 2) {
         // Step s (even): matrix work on f0; read step s + 1 into f1.
         mxg_issue_codes(ring, s + 3, off, a, b, wave);
-        mxg_read(f1, lds, s + 1, wm, wn, r32, h);
-        mxg_mfma<0>(acc, f0, h);
+        mxg_read<1>(f1, lds, s + 1, wm, wn, r32, h);
+        mxg_mfma(acc, f0);
         mxg_interleave();
         mxg_sync<MXG_LOADS_ODD>();
         // Step s + 1 (odd): matrix work on f1; read step s + 2 into f0.
         mxg_issue_codes(ring, s + 4, off, a, b, wave);
         mxg_issue_scales(ring, (s + 4) >> 1, off, as_, bs_, wave);
-        mxg_read(f0, lds, s + 2, wm, wn, r32, h);
-        mxg_mfma<2>(acc, f1, h);
+        mxg_read<0>(f0, lds, s + 2, wm, wn, r32, h);
+        mxg_mfma(acc, f1);
         mxg_interleave();
         mxg_sync<MXG_LOADS_EVEN>();
     }
     // The last two or four steps (s = nsteps - 4 or nsteps - 2).
     if (s + 4 == nsteps) {
         mxg_issue_codes(ring, s + 3, off, a, b, wave);
-        mxg_read(f1, lds, s + 1, wm, wn, r32, h);
-        mxg_mfma<0>(acc, f0, h);
+        mxg_read<1>(f1, lds, s + 1, wm, wn, r32, h);
+        mxg_mfma(acc, f0);
         mxg_interleave();
         mxg_sync<MXG_LOADS_ODD>();
-        mxg_read(f0, lds, s + 2, wm, wn, r32, h);
-        mxg_mfma<2>(acc, f1, h);
+        mxg_read<0>(f0, lds, s + 2, wm, wn, r32, h);
+        mxg_mfma(acc, f1);
         mxg_interleave();
         mxg_sync<0>();
     }
-    mxg_read(f1, lds, nsteps - 1, wm, wn, r32, h);
-    mxg_mfma<0>(acc, f0, h);
+    mxg_read<1>(f1, lds, nsteps - 1, wm, wn, r32, h);
+    mxg_mfma(acc, f0);
     mxg_interleave();
     mxg_sync<0>();
-    mxg_mfma<2>(acc, f1, h);
+    mxg_mfma(acc, f1);
 
     // Every copy has landed and every LDS read returned (the last syncs wait
     // for all); after this barrier no wavefront reads the ring.
@@ -568,36 +561,16 @@ __device__ __forceinline__ void nvg_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4],
         fb[i] = __builtin_bit_cast(bf16x8_t, tb[swz(128 * wn + 32 * i + r32, 2 * sl + h)]);
     }
 }
-// Row i's 4 instructions of a slice; B is the first operand, so the
-// accumulators hold C transposed (the layout gemm_epilogue takes).
-__device__ __forceinline__ void nvg_mfma_row(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
-                                             const bf16x8_t (&fb)[4], int i)
-{
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-
-// Chunk u (0..15: A's 8 chunks, then B's) of row t of the next step,
-// dequantized into stage buf.
-__device__ __forceinline__ void nvg_convert(uint8_t *lds, int buf, const NvStage &nx, int t, int u)
-{
-    const bool isb = u >= 8;
-    const int j = u & 7;
-    const u32x4_t *c = isb ? nx.cb : nx.ca;
-    const uint32_t sc = isb ? nx.sb : nx.sa;
-    const float d = e4m3_value((sc >> (8 * (j >> 1))) & 0xFFu);
-    u32x4_t *tile = isb ? nvg_tile_b(lds, buf) : nvg_tile_a(lds, buf);
-    tile[swz(t, j)] = nv_chunk_bf16(c[j >> 2][j & 3], d);
-}
-
-// One K step: the 64 matrix instructions on LDS stage buf and, if CONVERT,
-// the dequantization of the next step (registers nx) into the other stage,
-// in a fixed order: per slice, the next slice's fragments are read first;
-// then per row block i, its 4 (independent) instructions and one chunk of
-// the conversion, fenced from the next group so that the compiler neither
-// chains dependent instructions nor moves the VALU work after the matrix
-// work.  The VALU work then runs while the matrix unit is busy.
+// One K step: the 64 matrix instructions on LDS stage buf (B is their
+// first operand, so the accumulators hold C transposed, the layout
+// gemm_epilogue takes) and, if CONVERT, the dequantization of the next step
+// (registers nx: row t of A and of B) into the other stage.  The order is
+// fixed by scheduling fences: per slice, the next slice's fragments are read
+// first; then per row block i, each of its 4 independent instructions is
+// followed by one code pair of conversion chunk 4 sl + i (A's 8 chunks, then
+// B's), and the chunk's LDS write ends the group.  So the VALU work issues
+// while the matrix unit is busy, and no two instructions on one accumulator
+// are adjacent.
 template <bool CONVERT>
 __device__ __forceinline__ void nvg_step(f32x16_t (&acc)[4][4], uint8_t *lds, int buf,
                                          const NvStage &nx, int t, int wm, int wn, int r32, int h)
@@ -611,10 +584,23 @@ __device__ __forceinline__ void nvg_step(f32x16_t (&acc)[4][4], uint8_t *lds, in
             nvg_frags(fa[(sl + 1) & 1], fb[(sl + 1) & 1], ta, tb, sl + 1, wm, wn, r32, h);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            nvg_mfma_row(acc, fa[sl & 1], fb[sl & 1], i);
+            const int u = 4 * sl + i, j8 = u & 7;
+            const bool isb = u >= 8;
+            const uint32_t codes = (isb ? nx.cb : nx.ca)[j8 >> 2][j8 & 3];
+            const float d = e4m3_value(((isb ? nx.sb : nx.sa) >> (8 * (j8 >> 1))) & 0xFFu);
+            u32x4_t o;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[sl & 1][j], fa[sl & 1][i],
+                                                                    acc[i][j], 0, 0, 0);
+                if constexpr (CONVERT) {
+                    const float2_t v = e2m1_values((codes >> (8 * j)) & 0xFFu);
+                    o[j] = __builtin_amdgcn_perm(f2u(v[1] * d), f2u(v[0] * d), 0x07060302u);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (CONVERT)
-                nvg_convert(lds, buf ^ 1, nx, t, 4 * sl + i);
-            __builtin_amdgcn_sched_barrier(0);
+                (isb ? nvg_tile_b(lds, buf ^ 1) : nvg_tile_a(lds, buf ^ 1))[swz(t, j8)] = o;
         }
     }
 }
