@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "dequant_mxfp8_kernel": ["mxq_dequant.hip"],
     "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
     "mxfp8_gemm_kernel": ["mxq_gemm.hip"],
+    "mxfp8_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "nvfp4_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_token_qdq_kernel": ["mxq_nvfp4.hip"],
@@ -527,6 +528,9 @@ def config_timings(torch, E, W, legs, log, only=None):
         log("quantize + dequant timed")
         res.update(gemm_timings(torch, E, W, dev, empty))
         log("GEMM timed")
+    elif only is not None and any(c.startswith("G_") for c in only):
+        res.update({k: v for k, v in gemm_timings(torch, E, W, dev, empty).items() if k in only})
+        log("GEMM timed")
     return res
 
 
@@ -646,6 +650,36 @@ def gemm_timings(torch, E, W, dev, empty):
                                   "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}}
         del x, w, ac, as_, bc, bs_, c
+        torch.cuda.empty_cache()
+    # Grouped (MoE expert layer): config 5's expert-sorted rows (262144 x 2048,
+    # 128 segments of the top-8 routing of 32768 tokens) times each expert's
+    # 768 x 2048 weight.  Inputs are seeded torch normals generated on the
+    # device (generating 2^29 Student-t values on the host would take longer
+    # than the timing), quantized by the library.
+    for name, (R, N, K, G) in (("G_mxfp8_grouped_gemm_262144x768x2048", (262144, 768, 2048, 128)),):
+        _, offsets = W.routing(W.N_TOKENS, G, W.TOP_K, 6)
+        gen = torch.Generator(device="cuda").manual_seed(93)
+        x = (torch.randn((R, K), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+        w = (torch.randn((G * N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+        ac, as_ = empty((R, K)), empty((R, K // 32))
+        bc, bs_ = empty((G * N, K)), empty((G * N, K // 32))
+        E.mxq_mxfp8_quantize_rowcol(x, R, K, ac, as_, None, None)
+        E.mxq_mxfp8_quantize_rowcol(w, G * N, K, bc, bs_, None, None)
+        off = torch.from_numpy(offsets).cuda()
+        c = empty((R, N), torch.bfloat16)
+        fn = lambda: E.mxq_mxfp8_grouped_gemm(ac, as_, bc, bs_, off, G, R, N, K, E.MXQ_OUT_BF16, c)
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        med = float(np.median(ms))
+        flops = 2.0 * R * N * K
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"desc": f"grouped MXFP8 GEMM: {R} expert-sorted rows x {G} experts' "
+                             f"[{N}][{K}] weights (config 5 routing), BF16 out",
+                     "kernels": ["mxfp8_grouped_gemm_kernel<true>"], "ms_median": round(med, 5),
+                     "ms_min": round(float(np.min(ms)), 5), "flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                  "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}}
+        del x, w, ac, as_, bc, bs_, off, c
         torch.cuda.empty_cache()
     # NVFP4: per-token activations times a weight with one scope scale; the
     # matrix instructions are BF16 (the per-16 E4M3 block scales rule out the

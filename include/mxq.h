@@ -302,9 +302,10 @@ int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t 
  * the forward GEMM that consumes the rowwise copies made by
  * mxq_mxfp8_quantize_rowcol (activations [M][K], weights [N][K], both
  * K-contiguous; the MXFP8 format and recipe paragraphs).  Products are
- * exact; the sum is accumulated in fp32 by the matrix instructions, so C
- * differs from the exact sum by at most K 2^-24 sum_k |a b| (plus one BF16
- * rounding, nearest-even, for MXQ_OUT_BF16).
+ * exact; each matrix instruction sums its 64 products to about 12 bits of
+ * their magnitude sum and the instructions' results are accumulated in
+ * fp32, so C differs from the exact sum by at most (2^-10 + K 2^-24)
+ * sum_k |a b| (plus one BF16 rounding, nearest-even, for MXQ_OUT_BF16).
  *
  *   a  [M][K] E4M3 codes, 16-byte aligned;  a_scales [M][K/32] E8M0, 4-byte aligned.
  *   b  [N][K] E4M3 codes, 16-byte aligned;  b_scales [N][K/32] E8M0, 4-byte aligned.
@@ -315,6 +316,33 @@ int mxq_quantize_dequant_bf16(int fmt, const uint16_t *x, int64_t rows, int64_t 
 int mxq_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                    void *c, void *stream);
+
+/*
+ * Grouped (per-expert) MXFP8 GEMM, the MoE expert layer fed by the grouped
+ * quantizer: for every expert e and every row r of its segment
+ * seg_offsets[e] <= r < seg_offsets[e+1],
+ *   C[r][n] = sum_k dec(a[r][k]) 2^(sa[r][k/32] - 127) dec(b_e[n][k]) 2^(sb_e[n][k/32] - 127),
+ * the product of the expert-sorted rowwise copy (the grouped MXFP8
+ * quantize's row_codes / row_scales; the expert layers that the MXFP8
+ * recipe paragraph of "Miles: end-to-end MXFP8 and per-token NVFP4 RL on
+ * Blackwell" runs) with expert e's weight.  Same accumulation and bound as
+ * mxq_mxfp8_gemm.
+ *
+ *   a  [total_rows][K] E4M3 codes, 16-byte aligned; a_scales [total_rows][K/32] E8M0.
+ *   b  [n_groups][N][K] E4M3 codes, 16-byte aligned; b_scales [n_groups][N][K/32] E8M0.
+ *   seg_offsets  [n_groups + 1] int64, device memory, 0 = o_0 <= ... <= o_G = total_rows.
+ *   c  [total_rows][N] fp32 or BF16 (out_dtype), row-major; rows outside every
+ *      segment are not written.
+ *   K % 128 == 0 (MXQ_ERR_SHAPE); K <= 2^23, n_groups >= 1 and
+ *   (ceil(total_rows / 256) + n_groups) * ceil(N / 256) within the GEMM tile
+ *   limit above (MXQ_ERR_SIZE).  The offsets are device data the host cannot
+ *   check: each segment is clamped into [0, total_rows), so malformed
+ *   offsets give meaningless rows, never an access out of bounds.
+ */
+int mxq_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                           const uint8_t *b_scales, const int64_t *seg_offsets, int64_t n_groups,
+                           int64_t total_rows, int64_t N, int64_t K, int out_dtype, void *c,
+                           void *stream);
 
 /*
  * Block-scaled GEMM on NVFP4 operands: C = A x B^T with

@@ -45,6 +45,7 @@ EXPORTS = (
     "mxq_dequantize_bf16",
     "mxq_quantize_dequant_bf16",
     "mxq_mxfp8_gemm",
+    "mxq_mxfp8_grouped_gemm",
     "mxq_nvfp4_gemm",
     "mxq_mxfp8_quantize_ocp_floor",
     "mxq_mxfp8_quantize_rowcol_t",
@@ -91,6 +92,7 @@ def lib():
         "mxq_dequantize_bf16": [I, P, P, P, I64, I64, I64, P, P],
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
+        "mxq_mxfp8_grouped_gemm": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_quantize_ocp_floor": [P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_quantize_rowcol_t": [P, I64, I64, P, P, P, P, P],
@@ -231,6 +233,14 @@ def mxq_mxfp8_gemm(a, a_scales, b, b_scales, M, N, K, out_dtype, c, stream=None)
     _check(lib().mxq_mxfp8_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), M, N, K,
                                 out_dtype, _ptr(c), _stream(stream)),
            "mxq_mxfp8_gemm")
+
+
+def mxq_mxfp8_grouped_gemm(a, a_scales, b, b_scales, seg_offsets, n_groups, total_rows, N, K,
+                           out_dtype, c, stream=None):
+    _check(lib().mxq_mxfp8_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                        _ptr(seg_offsets), n_groups, total_rows, N, K, out_dtype,
+                                        _ptr(c), _stream(stream)),
+           "mxq_mxfp8_grouped_gemm")
 
 
 def mxq_nvfp4_gemm(a, a_block_scales, a_scales, rows_per_a_scale, b, b_block_scales, b_scales,

@@ -210,6 +210,22 @@ def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16,
     return c
 
 
+def mxfp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, seg_offsets,
+                       out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """Per-expert C[r] = A[r] x B_e^T for the rows r of each segment e of
+    seg_offsets (device int64 [G+1]): a [R][K] and a_scales [R][K/32] are the
+    expert-sorted rowwise MXFP8 copy, b [G][N][K] and b_scales [G][N][K/32]
+    the experts' weights; returns C [R][N] as fp32 or BF16 (rows outside
+    every segment left unwritten)."""
+    R, K = a_codes.shape
+    G, N = b_codes.shape[0], b_codes.shape[1]
+    c = torch.empty((R, N), dtype=out_dtype, device=a_codes.device)
+    code = B.MXQ_OUT_BF16 if out_dtype == torch.bfloat16 else B.MXQ_OUT_F32
+    B.mxq_mxfp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, seg_offsets, G, R, N, K, code,
+                             c, stream)
+    return c
+
+
 def nvfp4_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
                rows_per_a_scale: int = 1, rows_per_b_scale: Optional[int] = None,
                out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:

@@ -387,22 +387,18 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8
 // travel with the even steps into a ring of three buffers.  The loop is
 // unrolled by two so that the registers of alternate steps and the scale
 // byte selectors are static.
+// One 256x256 tile of C = A B^T at (m0, n0), C row-major [M][N].
 template <bool BF16_OUT>
-__global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
-    const uint8_t *__restrict__ Bs, int64_t M, int64_t N, int64_t K, GemmGrid grid,
-    void *__restrict__ C)
+__device__ __forceinline__ void mxg_tile(uint8_t *lds, const uint8_t *__restrict__ A,
+                                         const uint8_t *__restrict__ As,
+                                         const uint8_t *__restrict__ B,
+                                         const uint8_t *__restrict__ Bs, int64_t M, int64_t N,
+                                         int64_t K, int64_t m0, int64_t n0, void *__restrict__ C)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
     const int t = (int)tid();
     const int lane = t & 63, wave = (int)wave_in_group();    // wave index: uniform
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
-    uint32_t mt, nt;
-    if (!gemm_tile(grid, wg_id(), &mt, &nt))
-        return;
-    const int64_t m0 = (int64_t)mt * GEMM_BM;
-    const int64_t n0 = (int64_t)nt * GEMM_BN;
     const uint32_t nsteps = (uint32_t)(K / MXG_BK);          // even: K % 128 == 0
 
     f32x16_t acc[4][4];
@@ -470,6 +466,108 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     // for all); after this barrier no wavefront reads the ring.
     __syncthreads();
     gemm_epilogue<BF16_OUT, false>(acc, lds, wave, lane, m0, n0, M, N, C, nullptr, 1, nullptr, 1);
+}
+
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, int64_t M, int64_t N, int64_t K, GemmGrid grid,
+    void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    uint32_t mt, nt;
+    if (!gemm_tile(grid, wg_id(), &mt, &nt))
+        return;
+    mxg_tile<BF16_OUT>(lds, A, As, B, Bs, M, N, K, (int64_t)mt * GEMM_BM, (int64_t)nt * GEMM_BN,
+                       C);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped MXFP8 GEMM (the MoE expert layer): rows seg_offsets[e] ..
+// seg_offsets[e+1] of A (the expert-sorted rowwise copy that the grouped
+// quantizer writes) times expert e's weight B_e [N][K]:
+// C[r][n] = sum_k dec(a[r][k]) 2^(sa[r][k/32]) dec(b_e[n][k]) 2^(sb_e[n][k/32]).
+// Each segment is cut into 256-row tiles; global m-tile mg (the segments'
+// tiles concatenated) and n-tile nt come from the workgroup index, dealt to
+// the XCDs in contiguous runs so each XCD works on few experts.
+// ---------------------------------------------------------------------------
+struct GroupedGemmGrid {
+    uint32_t tiles_n, per_xcd, max_mtiles;
+};
+
+// The segment that global m-tile mg falls in, by a wavefront prefix sum of
+// the segments' tile counts, 64 segments at a time (offsets are device data
+// the host cannot check: each segment is clamped into [0, rows), so
+// malformed offsets give meaningless rows, never an access out of bounds).
+// Every output is wave-uniform.  False if mg lies past the last tile.
+__device__ __forceinline__ bool grouped_mtile(const int64_t *__restrict__ off, int64_t G,
+                                              int64_t rows, int64_t mg, int64_t *e_out,
+                                              int64_t *lo_out, int64_t *n_out, int64_t *mt_out)
+{
+    const int lane = (int)lane_id();
+    int64_t before = 0;
+    for (int64_t base = 0; base < G; base += 64) {
+        const int64_t e = base + lane;
+        int64_t lo = 0, hi = 0;
+        if (e < G) {
+            lo = off[e];
+            hi = off[e + 1];
+            lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+            hi = hi < lo ? lo : (hi > rows ? rows : hi);
+        }
+        const int64_t n = (hi - lo + GEMM_BM - 1) / GEMM_BM;
+        int64_t inc = n;                                      // inclusive prefix over lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t v = __shfl_up(inc, d);
+            if (lane >= d)
+                inc += v;
+        }
+        const int64_t total = __shfl(inc, 63);
+        if (mg < before + total) {
+            const unsigned long long hit = __ballot(before + inc > mg);
+            const int l = (int)__builtin_amdgcn_readfirstlane((uint32_t)(__ffsll((long long)hit) - 1));
+            *e_out = base + l;
+            *lo_out = __shfl(lo, l);
+            *n_out = __shfl(hi - lo, l);
+            *mt_out = mg - before - (__shfl(inc, l) - __shfl(n, l));
+            return true;
+        }
+        before += total;
+    }
+    return false;
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) mxfp8_grouped_gemm_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const int64_t *__restrict__ off, int64_t G, int64_t rows,
+    int64_t N, int64_t K, GroupedGemmGrid grid, void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    const uint32_t w = wg_id();
+    const uint32_t L = (w & 7) * grid.per_xcd + (w >> 3);
+    const uint32_t mg = L / grid.tiles_n, nt = L % grid.tiles_n;
+    if (mg >= grid.max_mtiles)
+        return;
+    int64_t e, lo, n, mt;
+    if (!grouped_mtile(off, G, rows, mg, &e, &lo, &n, &mt))
+        return;
+    e = uniform_i64(e);
+    lo = uniform_i64(lo);
+    n = uniform_i64(n);
+    mt = uniform_i64(mt);
+    const int64_t esz = BF16_OUT ? 2 : 4;
+    mxg_tile<BF16_OUT>(lds, A + lo * K, As + lo * (K >> 5), B + e * N * K, Bs + e * N * (K >> 5),
+                       n, N, K, mt * GEMM_BM, (int64_t)nt * GEMM_BN,
+                       reinterpret_cast<uint8_t *>(C) + lo * N * esz);
 }
 
 // ---------------------------------------------------------------------------
@@ -707,6 +805,29 @@ hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
         hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, block, 0, stream, a, a_block_scales,
                            a_scales, rows_per_a, b, b_block_scales, b_scales, rows_per_b, M, N, K,
                            g, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales,
+                                     const uint8_t *b, const uint8_t *b_scales,
+                                     const int64_t *seg_offsets, int64_t n_groups, int64_t rows,
+                                     int64_t N, int64_t K, bool bf16_out, void *c,
+                                     hipStream_t stream)
+{
+    const int64_t tm = grouped_gemm_mtiles(rows, n_groups), tn = (N + GEMM_BN - 1) / GEMM_BN;
+    if (tm * tn > MAX_GEMM_TILES)            // checked by the caller
+        return hipErrorInvalidValue;
+    GroupedGemmGrid g;
+    g.tiles_n = (uint32_t)tn;
+    g.max_mtiles = (uint32_t)tm;
+    g.per_xcd = (uint32_t)((tm * tn + 7) / 8);
+    const dim3 grid(8 * g.per_xcd), block(GEMM_THREADS);
+    if (bf16_out)
+        hipLaunchKernelGGL(mxfp8_grouped_gemm_kernel<true>, grid, block, 0, stream, a, a_scales,
+                           b, b_scales, seg_offsets, n_groups, rows, N, K, g, c);
+    else
+        hipLaunchKernelGGL(mxfp8_grouped_gemm_kernel<false>, grid, block, 0, stream, a, a_scales,
+                           b, b_scales, seg_offsets, n_groups, rows, N, K, g, c);
     return hipGetLastError();
 }
 

@@ -31,6 +31,13 @@ inline int64_t mxfp8_tiles(int64_t row_tiles, int64_t cols)
 // tile, the count rounded up to a multiple of 8 (one share per XCD).
 constexpr int64_t MAX_GEMM_TILES = MAX_GRID_ITEMS / 256 - 8;
 
+// 256-row tiles the grouped GEMM launches for: every segment's rows in
+// 256-row tiles, at most one partial tile per segment.
+inline int64_t grouped_gemm_mtiles(int64_t rows, int64_t n_groups)
+{
+    return (rows + 255) / 256 + n_groups;
+}
+
 // Workgroups (64 lanes each) of the export's amax pass over n_experts scopes
 // of n_per elements per tensor (two tensors when `pair`).
 int64_t scoped_amax_workgroups(int64_t n_experts, int64_t n_per, bool pair);
@@ -120,6 +127,15 @@ hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *block_scale
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                              const uint8_t *b_scales, int64_t M, int64_t N, int64_t K,
                              bool bf16_out, void *c, hipStream_t stream);
+
+// Grouped: C[r][N] = A[r] (MXFP8 rows of segment e) x B_e^T for every r in
+// segment e = seg_offsets[e] .. seg_offsets[e+1] (device data); B [G][N][K],
+// scales [G][N][K/32]; K % 128 == 0.
+hipError_t launch_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales,
+                                     const uint8_t *b, const uint8_t *b_scales,
+                                     const int64_t *seg_offsets, int64_t n_groups, int64_t rows,
+                                     int64_t N, int64_t K, bool bf16_out, void *c,
+                                     hipStream_t stream);
 
 // C[M][N] = sa[m / rows_per_a] sb[n / rows_per_b] x A (NVFP4 [M][K/2], E4M3
 // block scales [M][K/16]) x B (NVFP4 [N][K/2], [N][K/16])^T; K % 64 == 0.

@@ -124,6 +124,17 @@ def test_validation_before_any_device_call():
     assert status_of(gm, A, A + 2, A, A, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
     assert status_of(gm, A, A, A, A, 64, 64, 128, 0, A + 2, 0) == mxq.MXQ_ERR_ALIGN
 
+    gg = mxq.mxq_mxfp8_grouped_gemm
+    assert status_of(gg, A, A, A, A, A, 2, 64, 64, 128, 7, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(gg, A, A, A, A, None, 2, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gg, A, A, A, A, A, 0, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gg, A, A, A, A, A, 2, 0, 64, 128, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gg, A, A, A, A, A, 2, 64, 64, 96, 0, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(gg, A, A, A, A, A, 2, 64, 64, 1 << 24, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gg, A + 8, A, A, A, A, 2, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gg, A, A, A, A, A + 4, 2, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gg, A, A, A, A, A, 2, 64, 64, 128, 1, A + 1, 0) == mxq.MXQ_ERR_ALIGN
+
     ng = mxq.mxq_nvfp4_gemm
     assert status_of(ng, A, A, A, 1, A, A, A, 64, 64, 64, 64, 5, A, 0) == mxq.MXQ_ERR_ARG
     assert status_of(ng, A, A, None, 1, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_NULL
@@ -215,6 +226,12 @@ def test_grid_limits_are_size_errors():
     ng = mxq.mxq_nvfp4_gemm
     assert status_of(ng, A, B1, B2, 1, B3, B4, B5, 1, 256 * ((1 << 24) - 8), 256, 64, 0,
                      A * 7, 0) == mxq.MXQ_ERR_SIZE
+    # Grouped GEMM: (ceil(R/256) + n_groups) * ceil(N/256) <= 2^24 - 9.
+    gg = mxq.mxq_mxfp8_grouped_gemm
+    assert status_of(gg, A, B1, B2, B3, B4, 1, 256 * ((1 << 24) - 9), 256, 128, 0, B5, 0) == \
+        mxq.MXQ_ERR_SIZE
+    assert status_of(gg, A, B1, B2, B3, B4, 1, 256 * ((1 << 24) - 10), 256, 128, 0, B5, 0) == \
+        mxq.MXQ_ERR_DEVICE
     # Export: n_experts < 2^26 (with fewer than 2^36 elements this also keeps
     # the amax pass's ceil(scope / 4096) * n_experts chunks below 2^26).
     p = mxq.mxq_nvfp4_quantize_gateup_pair

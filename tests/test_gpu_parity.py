@@ -820,6 +820,74 @@ def test_gemm_dense_forward_full(orc):
     check_gemm(orc, x, w, "2048x8192x2048", row_sample=rows)
 
 
+def check_grouped_gemm(orc, x: np.ndarray, offsets: np.ndarray, w: np.ndarray, name: str,
+                       per_segment=None):
+    """A = rowwise MXFP8 of the expert-sorted rows x [R][K], B_e = rowwise
+    MXFP8 of w[e] [N][K] (both made by the oracle); C [R][N] on the GPU in
+    fp32 and BF16 through the grouped entry point, each segment's rows (all,
+    or per_segment sampled ones) against the oracle's exact product with
+    that segment's expert, to check_gemm's bound.  Rows in no segment must
+    keep the bytes the output held before the call."""
+    R, K = x.shape
+    G, N = w.shape[0], w.shape[1]
+    ac, as_ = orc.mxfp8_rowwise(x)
+    q = [orc.mxfp8_rowwise(w[e]) for e in range(G)]
+    bc = np.stack([p[0] for p in q])
+    bs_ = np.stack([p[1] for p in q])
+    rng = np.random.default_rng(91)
+    covered = np.zeros(R, bool)
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        covered[a:b] = True
+    for dt, code in ((torch.float32, mxq.MXQ_OUT_F32), (torch.bfloat16, mxq.MXQ_OUT_BF16)):
+        announce(f"mxfp8 grouped gemm {name} R={R} G={G} N={N} K={K} {dt}")
+        c = torch.full((R, N), -7.0, dtype=dt, device="cuda")
+        before = host(c).copy()
+        mxq.mxq_mxfp8_grouped_gemm(dev(ac), dev(as_), dev(bc), dev(bs_), dev(offsets), G, R, N,
+                                   K, code, c)
+        torch.cuda.synchronize()
+        got_all = host(c)
+        assert_same(got_all[~covered], before[~covered], "rows in no segment")
+        gotf = c.float().cpu().numpy().astype(np.float64)
+        for e in range(G):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            if hi <= lo:
+                continue
+            rows = np.arange(lo, hi)
+            if per_segment is not None and rows.size > per_segment:
+                rows = np.unique(np.concatenate([rows[:2], rows[-2:],
+                                                 rng.choice(rows, per_segment - 4, replace=False)]))
+            C, S = orc.mxfp8_gemm(ac[rows], as_[rows], bc[e], bs_[e])
+            bound = (GEMM_REL + K * 2.0 ** -24) * S
+            lim = bound if dt == torch.float32 else bound + 2.0 ** -8 * np.abs(C)
+            err = np.abs(gotf[rows] - C)
+            bad = np.argwhere(err > lim)
+            assert bad.size == 0, (f"{name} {dt} expert {e}: {len(bad)} outside the bound, first "
+                                   f"row {rows[bad[0][0]]} col {bad[0][1]}: "
+                                   f"got {gotf[rows][tuple(bad[0])]!r} want {C[tuple(bad[0])]!r}")
+
+
+def test_grouped_gemm_ragged_segments(orc):
+    """Segments of 0, 1, 33, 256, 257 and 300 rows (empty, single-row, partial
+    and exact 256-row tiles), rows before the first and after the last
+    segment left alone, ragged N, several K steps."""
+    sizes = [0, 1, 300, 0, 257, 33, 256]
+    offsets = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)
+    R, N, K = int(offsets[-1]) + 5, 200, 384
+    x = W.student_t_activations(R, K, 21)
+    w = np.stack([W.mode_random(N, K, 30 + e) for e in range(len(sizes))])
+    check_grouped_gemm(orc, x, offsets, w, "ragged")
+
+
+def test_grouped_gemm_moe_layer_sampled(orc):
+    """The MoE expert layer at the pages' shape: config 5's 262144 expert-sorted
+    rows (32768 tokens, top-8 of 128 experts) times 128 experts' gate
+    weights 768 x 2048 (N(0, 0.02)), 12 sampled rows of every segment."""
+    x, offsets = W.config5()
+    rng = np.random.default_rng(92)
+    w = W.bf16_bits(rng.normal(0, 0.02, (128, 768, 2048)))
+    check_grouped_gemm(orc, x, offsets, w, "config 5 x 768", per_segment=12)
+
+
 def check_nvfp4_gemm(orc, qa, qb, rows_per_b, name, row_sample=None, rel=0.0):
     """qa = (codes, block scales, fp32 scales per row), qb = (codes, block
     scales, fp32 scales per rows_per_b rows), both made by the oracle; C on
