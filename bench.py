@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "mxfp8_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "nvfp4_gemm_kernel": ["mxq_gemm.hip"],
+    "nvfp4_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_token_qdq_kernel": ["mxq_nvfp4.hip"],
 }
@@ -680,6 +681,35 @@ def gemm_timings(torch, E, W, dev, empty):
                                   "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}}
         del x, w, ac, as_, bc, bs_, off, c
+        torch.cuda.empty_cache()
+    # The same expert layer on per-token NVFP4 rows and NVFP4 expert weights
+    # (one scope scale each, as the export writes them); BF16 matrix
+    # instructions, so priced against the BF16 peak.
+    for name, (R, N, K, G) in (("G_nvfp4_grouped_gemm_262144x768x2048", (262144, 768, 2048, 128)),):
+        _, offsets = W.routing(W.N_TOKENS, G, W.TOP_K, 6)
+        gen = torch.Generator(device="cuda").manual_seed(97)
+        x = (torch.randn((R, K), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+        w = (torch.randn((G, N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+        ac, ab, as_ = empty((R, K // 2)), empty((R, K // 16)), empty((R,), torch.float32)
+        bc, bb, bs_ = empty((G, N, K // 2)), empty((G, N, K // 16)), empty((G,), torch.float32)
+        E.mxq_nvfp4_quantize_per_token(x, R, K, ac, ab, as_)
+        E.mxq_nvfp4_quantize_gateup_pair(w, None, G, N, K, bc, bb, None, None, bs_)
+        off = torch.from_numpy(offsets).cuda()
+        c = empty((R, N), torch.bfloat16)
+        fn = lambda: E.mxq_nvfp4_grouped_gemm(ac, ab, as_, bc, bb, bs_, off, G, R, N, K,
+                                              E.MXQ_OUT_BF16, c)
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        med = float(np.median(ms))
+        flops = 2.0 * R * N * K
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"desc": f"grouped NVFP4 GEMM: {R} per-token NVFP4 rows x {G} experts' "
+                             f"[{N}][{K}] NVFP4 weights (config 5 routing), BF16 out",
+                     "kernels": ["nvfp4_grouped_gemm_kernel<true>"], "ms_median": round(med, 5),
+                     "ms_min": round(float(np.min(ms)), 5), "flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}}
+        del x, w, ac, ab, as_, bc, bb, bs_, off, c
         torch.cuda.empty_cache()
     # NVFP4: per-token activations times a weight with one scope scale; the
     # matrix instructions are BF16 (the per-16 E4M3 block scales rule out the

@@ -371,6 +371,33 @@ int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float 
                    int64_t K, int out_dtype, void *c, void *stream);
 
 /*
+ * Grouped (per-expert) NVFP4 GEMM, the MoE expert layer on per-token NVFP4
+ * rows (the rollout forward of the NVFP4 format and per-token
+ * activation-scale paragraphs of "Miles: end-to-end MXFP8 and per-token
+ * NVFP4 RL on Blackwell"): for every expert e and every row r of its
+ * segment seg_offsets[e] <= r < seg_offsets[e+1],
+ *   C[r][n] = fp32(fp32(S * a_scales[r]) * b_scales[e]),
+ *   S = sum_k dec(a[r][k]) dec(ab[r][k/16]) dec(b_e[n][k]) dec(bb_e[n][k/16]),
+ * the expert-sorted rows as the grouped NVFP4 quantize writes them (codes,
+ * E4M3 block scales, one FP32 scale per row) times expert e's weight as the
+ * export writes it (one FP32 scope scale per expert).  Same accumulation and
+ * bound as mxq_nvfp4_gemm.
+ *
+ *   a  [total_rows][K/2] E2M1 codes, 16-byte aligned; a_block_scales [total_rows][K/16]
+ *      E4M3, 4-byte aligned; a_scales [total_rows] fp32.
+ *   b  [n_groups][N][K/2], 16-byte aligned; b_block_scales [n_groups][N][K/16], 4-byte
+ *      aligned; b_scales [n_groups] fp32.
+ *   seg_offsets  [n_groups + 1] int64, device memory, as for mxq_mxfp8_grouped_gemm.
+ *   c  [total_rows][N] fp32 or BF16 (out_dtype); rows outside every segment are not written.
+ *   K % 64 == 0 (MXQ_ERR_SHAPE); the size limits and the treatment of malformed offsets
+ *   are those of mxq_mxfp8_grouped_gemm.
+ */
+int mxq_nvfp4_grouped_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
+                           const uint8_t *b, const uint8_t *b_block_scales, const float *b_scales,
+                           const int64_t *seg_offsets, int64_t n_groups, int64_t total_rows,
+                           int64_t N, int64_t K, int out_dtype, void *c, void *stream);
+
+/*
  * Outputs of the grouped call.  MXFP8 uses the first five fields, NVFP4 the
  * last three; the others are ignored.
  *   row_codes, row_scales  as mxq_mxfp8_quantize_rowcol over all total_rows.

@@ -47,6 +47,7 @@ EXPORTS = (
     "mxq_mxfp8_gemm",
     "mxq_mxfp8_grouped_gemm",
     "mxq_nvfp4_gemm",
+    "mxq_nvfp4_grouped_gemm",
     "mxq_mxfp8_quantize_ocp_floor",
     "mxq_mxfp8_quantize_rowcol_t",
     "mxq_nvfp4_quantize_per_token_approx",
@@ -93,6 +94,7 @@ def lib():
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
         "mxq_mxfp8_grouped_gemm": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
+        "mxq_nvfp4_grouped_gemm": [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_quantize_ocp_floor": [P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_quantize_rowcol_t": [P, I64, I64, P, P, P, P, P],
@@ -241,6 +243,15 @@ def mxq_mxfp8_grouped_gemm(a, a_scales, b, b_scales, seg_offsets, n_groups, tota
                                         _ptr(seg_offsets), n_groups, total_rows, N, K, out_dtype,
                                         _ptr(c), _stream(stream)),
            "mxq_mxfp8_grouped_gemm")
+
+
+def mxq_nvfp4_grouped_gemm(a, a_block_scales, a_scales, b, b_block_scales, b_scales,
+                           seg_offsets, n_groups, total_rows, N, K, out_dtype, c, stream=None):
+    _check(lib().mxq_nvfp4_grouped_gemm(_ptr(a), _ptr(a_block_scales), _ptr(a_scales), _ptr(b),
+                                        _ptr(b_block_scales), _ptr(b_scales), _ptr(seg_offsets),
+                                        n_groups, total_rows, N, K, out_dtype, _ptr(c),
+                                        _stream(stream)),
+           "mxq_nvfp4_grouped_gemm")
 
 
 def mxq_nvfp4_gemm(a, a_block_scales, a_scales, rows_per_a_scale, b, b_block_scales, b_scales,

@@ -226,6 +226,22 @@ def mxfp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, seg_offsets,
     return c
 
 
+def nvfp4_grouped_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
+                       seg_offsets, out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """Per-expert C[r] = a_scales[r] b_scales[e] A[r] x B_e^T for the rows r of
+    each segment e of seg_offsets (device int64 [G+1]): a [R][K/2] codes,
+    [R][K/16] block scales and [R] FP32 scales (the grouped per-token NVFP4
+    copy); b [G][N][K/2], [G][N][K/16] and [G] FP32 scope scales (the
+    experts' exported weights); returns C [R][N] as fp32 or BF16."""
+    R, K = a_codes.shape[0], 2 * a_codes.shape[1]
+    G, N = b_codes.shape[0], b_codes.shape[1]
+    c = torch.empty((R, N), dtype=out_dtype, device=a_codes.device)
+    code = B.MXQ_OUT_BF16 if out_dtype == torch.bfloat16 else B.MXQ_OUT_F32
+    B.mxq_nvfp4_grouped_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
+                             seg_offsets, G, R, N, K, code, c, stream)
+    return c
+
+
 def nvfp4_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
                rows_per_a_scale: int = 1, rows_per_b_scale: Optional[int] = None,
                out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:

@@ -515,6 +515,44 @@ int mxq_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales, const uint
                                                    (hipStream_t)stream));
 }
 
+int mxq_nvfp4_grouped_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
+                           const uint8_t *b, const uint8_t *b_block_scales, const float *b_scales,
+                           const int64_t *seg_offsets, int64_t n_groups, int64_t total_rows,
+                           int64_t N, int64_t K, int out_dtype, void *c, void *stream)
+{
+    if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
+        return MXQ_ERR_ARG;
+    if (!a || !a_block_scales || !a_scales || !b || !b_block_scales || !b_scales ||
+        !seg_offsets || !c)
+        return MXQ_ERR_NULL;
+    if (!size_ok(total_rows, K) || !size_ok(N, K) || !size_ok(total_rows, 4 * N) ||
+        n_groups < 1 || !size_ok(n_groups, N * K) || n_groups > MAX_ELEMS / 8 - 1)
+        return MXQ_ERR_SIZE;
+    if (K % 64 != 0)
+        return MXQ_ERR_SHAPE;
+    if (K > MAX_GEMM_K || total_rows > MAX_ELEMS / 4 - 255 ||
+        mxq::grouped_gemm_mtiles(total_rows, n_groups) > mxq::MAX_GEMM_TILES ||
+        mxq::grouped_gemm_mtiles(total_rows, n_groups) * ((N + 255) / 256) > mxq::MAX_GEMM_TILES)
+        return MXQ_ERR_SIZE;
+    const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
+    const Buf bb[8] = {{a, total_rows * (K / 2), 16, false},
+                       {a_block_scales, total_rows * (K / 16), 4, false},
+                       {a_scales, 4 * total_rows, 4, false},
+                       {b, n_groups * N * (K / 2), 16, false},
+                       {b_block_scales, n_groups * N * (K / 16), 4, false},
+                       {b_scales, 4 * n_groups, 4, false},
+                       {seg_offsets, 8 * (n_groups + 1), 8, false},
+                       {c, esz * total_rows * N, esz, true}};
+    const int st = check_bufs(bb, 8);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_nvfp4_grouped_gemm(a, a_block_scales, a_scales, b,
+                                                   b_block_scales, b_scales, seg_offsets,
+                                                   n_groups, total_rows, N, K,
+                                                   out_dtype == MXQ_OUT_BF16, c,
+                                                   (hipStream_t)stream));
+}
+
 int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
                    int64_t rows_per_a_scale, const uint8_t *b, const uint8_t *b_block_scales,
                    const float *b_scales, int64_t rows_per_b_scale, int64_t M, int64_t N,

@@ -718,23 +718,21 @@ __device__ __forceinline__ void nvg_sync()
 // step ks + 1 (loaded one step earlier) are dequantized into the other
 // stage and step ks + 2 is loaded into the registers step ks used.  The
 // loop is unrolled by two so that the two register sets keep their roles.
+// One 256x256 tile of the NVFP4 GEMM at (m0, n0), C row-major [M][N].
 template <bool BF16_OUT>
-__global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ Ab, const float *__restrict__ As,
-    int64_t rows_per_a, const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bb,
-    const float *__restrict__ Bs, int64_t rows_per_b, int64_t M, int64_t N, int64_t K,
-    GemmGrid grid, void *__restrict__ C)
+__device__ __forceinline__ void nvg_tile(uint8_t *lds, const uint8_t *__restrict__ A,
+                                         const uint8_t *__restrict__ Ab,
+                                         const float *__restrict__ As, int64_t rows_per_a,
+                                         const uint8_t *__restrict__ B,
+                                         const uint8_t *__restrict__ Bb,
+                                         const float *__restrict__ Bs, int64_t rows_per_b,
+                                         int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                         void *__restrict__ C)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
     const int t = (int)tid();
     const int lane = t & 63, wave = (int)wave_in_group();
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
-    uint32_t mt, nt;
-    if (!gemm_tile(grid, wg_id(), &mt, &nt))
-        return;
-    const int64_t m0 = (int64_t)mt * GEMM_BM;
-    const int64_t n0 = (int64_t)nt * GEMM_BN;
     const int64_t ksteps = K / NVG_BK;
     const uint32_t half_k = (uint32_t)(K >> 1), blk_k = (uint32_t)(K >> 4);
     const uint32_t ra = (uint32_t)(m0 + t < M ? t : M - 1 - m0);
@@ -780,6 +778,78 @@ __global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
     __syncthreads();
     gemm_epilogue<BF16_OUT, true>(acc, lds, wave, lane, m0, n0, M, N, C, As, rows_per_a, Bs,
                                   rows_per_b);
+}
+
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) nvfp4_gemm_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ Ab, const float *__restrict__ As,
+    int64_t rows_per_a, const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bb,
+    const float *__restrict__ Bs, int64_t rows_per_b, int64_t M, int64_t N, int64_t K,
+    GemmGrid grid, void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    uint32_t mt, nt;
+    if (!gemm_tile(grid, wg_id(), &mt, &nt))
+        return;
+    nvg_tile<BF16_OUT>(lds, A, Ab, As, rows_per_a, B, Bb, Bs, rows_per_b, M, N, K,
+                       (int64_t)mt * GEMM_BM, (int64_t)nt * GEMM_BN, C);
+}
+
+// Grouped NVFP4 GEMM (the MoE expert layer on per-token NVFP4 rows): rows of
+// segment e (codes, block scales and one FP32 scale per row, as the grouped
+// quantizer writes them) times expert e's NVFP4 weight [N][K/2] with its one
+// FP32 scope scale Bs[e]; tiles found as in the grouped MXFP8 kernel.
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) nvfp4_grouped_gemm_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ Ab, const float *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bb, const float *__restrict__ Bs,
+    const int64_t *__restrict__ off, int64_t G, int64_t rows, int64_t N, int64_t K,
+    GroupedGemmGrid grid, void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    const uint32_t w = wg_id();
+    const uint32_t L = (w & 7) * grid.per_xcd + (w >> 3);
+    const uint32_t mg = L / grid.tiles_n, nt = L % grid.tiles_n;
+    if (mg >= grid.max_mtiles)
+        return;
+    int64_t e, lo, n, mt;
+    if (!grouped_mtile(off, G, rows, mg, &e, &lo, &n, &mt))
+        return;
+    e = uniform_i64(e);
+    lo = uniform_i64(lo);
+    n = uniform_i64(n);
+    mt = uniform_i64(mt);
+    const int64_t esz = BF16_OUT ? 2 : 4;
+    nvg_tile<BF16_OUT>(lds, A + lo * (K >> 1), Ab + lo * (K >> 4), As + lo, 1,
+                       B + e * N * (K >> 1), Bb + e * N * (K >> 4), Bs + e, N, n, N, K,
+                       mt * GEMM_BM, (int64_t)nt * GEMM_BN,
+                       reinterpret_cast<uint8_t *>(C) + lo * N * esz);
+}
+
+hipError_t launch_nvfp4_grouped_gemm(const uint8_t *a, const uint8_t *a_block_scales,
+                                     const float *a_scales, const uint8_t *b,
+                                     const uint8_t *b_block_scales, const float *b_scales,
+                                     const int64_t *seg_offsets, int64_t n_groups, int64_t rows,
+                                     int64_t N, int64_t K, bool bf16_out, void *c,
+                                     hipStream_t stream)
+{
+    const int64_t tm = grouped_gemm_mtiles(rows, n_groups), tn = (N + GEMM_BN - 1) / GEMM_BN;
+    if (tm * tn > MAX_GEMM_TILES)            // checked by the caller
+        return hipErrorInvalidValue;
+    GroupedGemmGrid g;
+    g.tiles_n = (uint32_t)tn;
+    g.max_mtiles = (uint32_t)tm;
+    g.per_xcd = (uint32_t)((tm * tn + 7) / 8);
+    const dim3 grid(8 * g.per_xcd), block(GEMM_THREADS);
+    if (bf16_out)
+        hipLaunchKernelGGL(nvfp4_grouped_gemm_kernel<true>, grid, block, 0, stream, a,
+                           a_block_scales, a_scales, b, b_block_scales, b_scales, seg_offsets,
+                           n_groups, rows, N, K, g, c);
+    else
+        hipLaunchKernelGGL(nvfp4_grouped_gemm_kernel<false>, grid, block, 0, stream, a,
+                           a_block_scales, a_scales, b, b_block_scales, b_scales, seg_offsets,
+                           n_groups, rows, N, K, g, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,

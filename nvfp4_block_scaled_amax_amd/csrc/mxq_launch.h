@@ -137,6 +137,17 @@ hipError_t launch_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales,
                                      int64_t N, int64_t K, bool bf16_out, void *c,
                                      hipStream_t stream);
 
+// Grouped: C[r][N] = sa[r] sb[e] x A[r] (NVFP4 rows of segment e: codes
+// [R][K/2], E4M3 block scales [R][K/16], FP32 sa [R]) x B_e^T (codes
+// [G][N][K/2], block scales [G][N][K/16], one FP32 sb[e] per expert);
+// K % 64 == 0.
+hipError_t launch_nvfp4_grouped_gemm(const uint8_t *a, const uint8_t *a_block_scales,
+                                     const float *a_scales, const uint8_t *b,
+                                     const uint8_t *b_block_scales, const float *b_scales,
+                                     const int64_t *seg_offsets, int64_t n_groups, int64_t rows,
+                                     int64_t N, int64_t K, bool bf16_out, void *c,
+                                     hipStream_t stream);
+
 // C[M][N] = sa[m / rows_per_a] sb[n / rows_per_b] x A (NVFP4 [M][K/2], E4M3
 // block scales [M][K/16]) x B (NVFP4 [N][K/2], [N][K/16])^T; K % 64 == 0.
 hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,

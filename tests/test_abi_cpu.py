@@ -135,6 +135,15 @@ def test_validation_before_any_device_call():
     assert status_of(gg, A, A, A, A, A + 4, 2, 64, 64, 128, 0, A, 0) == mxq.MXQ_ERR_ALIGN
     assert status_of(gg, A, A, A, A, A, 2, 64, 64, 128, 1, A + 1, 0) == mxq.MXQ_ERR_ALIGN
 
+    gn = mxq.mxq_nvfp4_grouped_gemm
+    assert status_of(gn, A, A, A, A, A, A, A, 2, 64, 64, 64, 7, A, 0) == mxq.MXQ_ERR_ARG
+    assert status_of(gn, A, A, None, A, A, A, A, 2, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(gn, A, A, A, A, A, A, A, 0, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(gn, A, A, A, A, A, A, A, 2, 64, 64, 96, 0, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(gn, A + 8, A, A, A, A, A, A, 2, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gn, A, A + 2, A, A, A, A, A, 2, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(gn, A, A, A, A, A, A, A + 4, 2, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_ALIGN
+
     ng = mxq.mxq_nvfp4_gemm
     assert status_of(ng, A, A, A, 1, A, A, A, 64, 64, 64, 64, 5, A, 0) == mxq.MXQ_ERR_ARG
     assert status_of(ng, A, A, None, 1, A, A, A, 64, 64, 64, 64, 0, A, 0) == mxq.MXQ_ERR_NULL
@@ -226,6 +235,9 @@ def test_grid_limits_are_size_errors():
     ng = mxq.mxq_nvfp4_gemm
     assert status_of(ng, A, B1, B2, 1, B3, B4, B5, 1, 256 * ((1 << 24) - 8), 256, 64, 0,
                      A * 7, 0) == mxq.MXQ_ERR_SIZE
+    gn = mxq.mxq_nvfp4_grouped_gemm
+    assert status_of(gn, A, B1, B2, B3, B4, B5, A * 7, 1, 256 * ((1 << 24) - 9), 256, 64, 0,
+                     A * 11, 0) == mxq.MXQ_ERR_SIZE
     # Grouped GEMM: (ceil(R/256) + n_groups) * ceil(N/256) <= 2^24 - 9.
     gg = mxq.mxq_mxfp8_grouped_gemm
     assert status_of(gg, A, B1, B2, B3, B4, 1, 256 * ((1 << 24) - 9), 256, 128, 0, B5, 0) == \

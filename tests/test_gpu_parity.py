@@ -888,6 +888,73 @@ def test_grouped_gemm_moe_layer_sampled(orc):
     check_grouped_gemm(orc, x, offsets, w, "config 5 x 768", per_segment=12)
 
 
+def check_nvfp4_grouped_gemm(orc, x: np.ndarray, offsets: np.ndarray, w: np.ndarray, name: str,
+                             per_segment=None):
+    """A = per-token NVFP4 of the expert-sorted rows x [R][K], B_e = the
+    export's NVFP4 of w[e] [N][K] with one scope scale per expert (both made
+    by the oracle); C [R][N] on the GPU in fp32 and BF16 through the grouped
+    entry point, each segment's rows (all, or per_segment sampled ones)
+    against the oracle's exact product to check_nvfp4_gemm's bound.  Rows in
+    no segment must keep their bytes."""
+    R, K = x.shape
+    G, N = w.shape[0], w.shape[1]
+    ac, ab, as_ = orc.nvfp4_per_token(x)
+    bc, bb, _, _, bs_ = orc.nvfp4_gateup_pair(w, None)
+    rng = np.random.default_rng(94)
+    covered = np.zeros(R, bool)
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        covered[a:b] = True
+    for dt, code in ((torch.float32, mxq.MXQ_OUT_F32), (torch.bfloat16, mxq.MXQ_OUT_BF16)):
+        announce(f"nvfp4 grouped gemm {name} R={R} G={G} N={N} K={K} {dt}")
+        c = torch.full((R, N), -7.0, dtype=dt, device="cuda")
+        before = host(c).copy()
+        mxq.mxq_nvfp4_grouped_gemm(dev(ac), dev(ab), dev(as_), dev(bc), dev(bb), dev(bs_),
+                                   dev(offsets), G, R, N, K, code, c)
+        torch.cuda.synchronize()
+        assert_same(host(c)[~covered], before[~covered], "rows in no segment")
+        gotf = c.float().cpu().numpy().astype(np.float64)
+        for e in range(G):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            if hi <= lo:
+                continue
+            rows = np.arange(lo, hi)
+            if per_segment is not None and rows.size > per_segment:
+                rows = np.unique(np.concatenate([rows[:2], rows[-2:],
+                                                 rng.choice(rows, per_segment - 4, replace=False)]))
+            C, S = orc.nvfp4_gemm(ac[rows], ab[rows], as_[rows], 1, bc[e], bb[e], bs_[e:e + 1], N)
+            bound = (K * 2.0 ** -24 + 2.0 ** -23) * S
+            lim = bound if dt == torch.float32 else bound + 2.0 ** -8 * np.abs(C)
+            err = np.abs(gotf[rows] - C)
+            bad = np.argwhere(err > lim)
+            assert bad.size == 0, (f"{name} {dt} expert {e}: {len(bad)} outside the bound, first "
+                                   f"row {rows[bad[0][0]]} col {bad[0][1]}: "
+                                   f"got {gotf[rows][tuple(bad[0])]!r} want {C[tuple(bad[0])]!r}")
+
+
+def test_nvfp4_grouped_gemm_ragged_segments(orc):
+    """Per-token NVFP4 rows in segments of 0, 1, 33, 256, 257 and 300 rows
+    (rows outside the segments left alone) times experts' weights with
+    their own scope scales (expert amplitudes spread over 2^-4 .. 2^4),
+    three K steps."""
+    sizes = [0, 1, 300, 0, 257, 33, 256]
+    offsets = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)
+    R, N, K = int(offsets[-1]) + 5, 200, 192
+    x = W.student_t_activations(R, K, 23)
+    rng = np.random.default_rng(95)
+    amp = np.ldexp(1.0, rng.integers(-4, 5, len(sizes)))[:, None, None]
+    w = W.bf16_bits(rng.normal(0, 0.02, (len(sizes), N, K)) * amp)
+    check_nvfp4_grouped_gemm(orc, x, offsets, w, "ragged")
+
+
+def test_nvfp4_grouped_gemm_moe_layer_sampled(orc):
+    """Config 5's 262144 expert-sorted rows as per-token NVFP4 times 128
+    experts' exported gate weights 768 x 2048 (N(0, 0.02)), 12 sampled rows
+    of every segment."""
+    x, offsets = W.config5()
+    w = W.bf16_bits(np.random.default_rng(96).normal(0, 0.02, (128, 768, 2048)))
+    check_nvfp4_grouped_gemm(orc, x, offsets, w, "config 5 x 768", per_segment=12)
+
+
 def check_nvfp4_gemm(orc, qa, qb, rows_per_b, name, row_sample=None, rel=0.0):
     """qa = (codes, block scales, fp32 scales per row), qb = (codes, block
     scales, fp32 scales per rows_per_b rows), both made by the oracle; C on
