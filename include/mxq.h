@@ -69,7 +69,9 @@
 extern "C" {
 #endif
 
-#define MXQ_VERSION 1
+/* Raised whenever an entry point is added or changes (2: the caller-amax
+ * export variant, the copy floor and the grouped GEMMs). */
+#define MXQ_VERSION 2
 
 typedef enum {
     MXQ_OK = 0,
