@@ -680,6 +680,37 @@ def test_gemm_weight_gradient_from_transposed_copies(orc):
     assert np.all(err <= (GEMM_REL + M * 2.0 ** -24) * S)
 
 
+def test_grouped_gemm_data_gradient_from_transposed_weights(orc):
+    """The expert layer's data gradient dX[r][k] = sum_n dY[r][n] W_e[n][k]
+    for the rows r of segment e: dY's rowwise copy times each expert's
+    columnwise copy transposed ([K][N], blocks along n), through the grouped
+    entry point, against the oracle per segment."""
+    sizes = [130, 0, 257, 40]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    R, N, K, G = int(offsets[-1]), 256, 192, len(sizes)
+    dy = W.student_t_activations(R, N, 93)
+    w = np.stack([W.mode_random(N, K, 94 + e) for e in range(G)])
+    announce(f"mxfp8 grouped dgrad R={R} G={G} N={N} K={K}")
+    qw = [api.mxfp8_quantize_rowcol_t(dev(w[e]), rowwise=False) for e in range(G)]
+    wt = torch.stack([q.col_codes for q in qw])            # [G][K][N]
+    wts = torch.stack([q.col_scales for q in qw])          # [G][K][N/32]
+    qd = api.mxfp8_quantize_rowcol(dev(dy), colwise=False)
+    c = api.mxfp8_grouped_gemm(qd.row_codes, qd.row_scales, wt, wts, dev(offsets),
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = host(c).astype(np.float64)
+    dc, ds = orc.mxfp8_rowwise(dy)
+    for e in range(G):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        wc, ws = orc.mxfp8_colwise(w[e])
+        C, S = orc.mxfp8_gemm(dc[lo:hi], ds[lo:hi], np.ascontiguousarray(wc.T),
+                              np.ascontiguousarray(ws.T))
+        err = np.abs(got[lo:hi] - C)
+        assert np.all(err <= (GEMM_REL + N * 2.0 ** -24) * S), f"expert {e}"
+
+
 def test_nvfp4_approx_differs_only_at_midpoints(orc):
     """The opt-in approximate variant: the FP32 token scales are exact; a block
     scale differs from the exact one only where amax / (6 s) lies within
