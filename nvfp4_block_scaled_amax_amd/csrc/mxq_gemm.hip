@@ -1,11 +1,14 @@
-// mxq_gemm.hip -- block-scaled GEMM consuming the MXFP8 operands the
-// quantizers produce: C[m][n] = sum_k dec(a[m][k]) 2^(ea[m][k/32]) *
+// mxq_gemm.hip -- block-scaled GEMMs consuming the operands the quantizers
+// produce.  MXFP8: C[m][n] = sum_k dec(a[m][k]) 2^(ea[m][k/32]) *
 // dec(b[n][k]) 2^(eb[n][k/32]), with both operands K-contiguous (the rowwise
 // 1x32 copies: activations [M][K] and weights [N][K]), fp32 accumulation and
 // an fp32 or BF16 (nearest-even) result.  This is the forward GEMM that the
 // MXFP8 recipe paragraph of the page "Miles: end-to-end MXFP8 and per-token
 // NVFP4 RL on Blackwell" feeds; the E8M0 scale per 32 elements along K is
-// the block format of gfx950's scaled matrix instructions.
+// the block format of gfx950's scaled matrix instructions.  NVFP4 (further
+// down): the same tile with the E4M3 block scales applied while
+// dequantizing to BF16.  Each has a dense kernel and a grouped one (the MoE
+// expert layer: expert-sorted rows times each expert's weight).
 //
 // Matrix instruction.  v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32x64
 // A block by a 64x32 B block.  Measured lane layout (a probe on MI355X):
