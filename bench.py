@@ -50,6 +50,8 @@ KERNEL_SOURCES = {
     "dequant_nvfp4_kernel": ["mxq_dequant.hip"],
     "mxfp8_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_grouped_gemm_kernel": ["mxq_gemm.hip"],
+    "mxfp8_grouped_wgrad_kernel": ["mxq_gemm.hip"],
+    "mxfp8_grouped_colt_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_gemm_kernel": ["mxq_gemm.hip"],
     "nvfp4_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
@@ -529,9 +531,16 @@ def config_timings(torch, E, W, legs, log, only=None):
         log("quantize + dequant timed")
         res.update(gemm_timings(torch, E, W, dev, empty))
         log("GEMM timed")
-    elif only is not None and any(c.startswith("G_") for c in only):
-        res.update({k: v for k, v in gemm_timings(torch, E, W, dev, empty).items() if k in only})
-        log("GEMM timed")
+        res.update(wgrad_timings(torch, E, W, dev, empty))
+        log("weight gradient timed")
+    elif only is not None:
+        if any(c.startswith("G_") and "wgrad" not in c for c in only):
+            res.update({k: v for k, v in gemm_timings(torch, E, W, dev, empty).items()
+                        if k in only})
+            log("GEMM timed")
+        if any("wgrad" in c or c == "C5_colt_mxfp8" for c in only):
+            res.update(wgrad_timings(torch, E, W, dev, empty, only))
+            log("weight gradient timed")
     return res
 
 
@@ -792,6 +801,62 @@ def build_dsp(torch, E, W, legs, dev, empty):
                     2 * T * K + 8 * R, 2 * n, n, ["index_select"],
                     f"torch.index_select of {R} rows of {T}x{K} BF16 (the copy a fused "
                     "dispatch avoids)"))
+
+
+def wgrad_timings(torch, E, W, dev, empty, only=None):
+    """The expert layer's weight-gradient pair at config 5's routing: the
+    grouped transposed columnwise copies of X [262144][2048] (timed, with its
+    copy floor: a quantize config) and of dY [262144][768], then
+    dW_e [768][2048] = dY_e^T X_e for all 128 experts (timed, priced against
+    the fp8 matrix peak).  Inputs are seeded torch normals on the device."""
+    sel = (lambda n: True) if only is None else (lambda n: n in only)
+    res = {}
+    R, K, M, G = 262144, 2048, 768, 128
+    _, offsets = W.routing(W.N_TOKENS, G, W.TOP_K, 6)
+    off = torch.from_numpy(offsets).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(98)
+    x = (torch.randn((R, K), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    dy = (torch.randn((R, M), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    pitch = -(-R // 128) * 128 + 128 * G                 # grouped_colt_pitch
+    gx = (empty((K, pitch)), empty((K, pitch // 32)), empty((G + 1,), torch.int64))
+    gd = (empty((M, pitch)), empty((M, pitch // 32)), empty((G + 1,), torch.int64))
+    if sel("C5_colt_mxfp8"):
+        fn = lambda: E.mxq_mxfp8_grouped_colwise_t(x, R, K, off, G, gx[0], gx[1], gx[2])
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        # Algorithmic bytes: X once, every padded code and scale column written.
+        rb, wb = 2 * R * K + 8 * (G + 1), 0
+        fn()
+        torch.cuda.synchronize()
+        blocks = int(gx[2][-1].item())
+        wb = K * 32 * blocks + K * blocks + 8 * (G + 1)
+        fl = copy_floor(torch, E, rb, wb, 1, False, 10, 2)
+        k, v = cfg_record("C5_colt_mxfp8", f"grouped MXFP8 columnwise, transposed and padded to "
+                          f"128 rows per segment, {R}x{K}, {G} segments", ms, rb + wb, R * K, 1,
+                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel"], None, fl,
+                          (rb, wb))
+        res[k] = v
+    name = f"G_mxfp8_grouped_wgrad_{M}x{K}_over_{R}"
+    if sel(name):
+        E.mxq_mxfp8_grouped_colwise_t(x, R, K, off, G, gx[0], gx[1], gx[2])
+        E.mxq_mxfp8_grouped_colwise_t(dy, R, M, off, G, gd[0], gd[1], gd[2])
+        c = empty((G, M, K), torch.bfloat16)
+        fn = lambda: E.mxq_mxfp8_grouped_wgrad(gd[0], gd[1], gx[0], gx[1], gd[2], G, M, K, pitch,
+                                               E.MXQ_OUT_BF16, c)
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        med = float(np.median(ms))
+        flops = 2.0 * R * M * K
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"desc": f"grouped MXFP8 weight gradient: dW_e[{M}][{K}] = dY_e^T X_e over "
+                             f"each of {G} segments of {R} rows (config 5 routing), BF16 out",
+                     "kernels": ["mxfp8_grouped_wgrad_kernel<true>"], "ms_median": round(med, 5),
+                     "ms_min": round(float(np.min(ms)), 5), "flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                  "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}}
+        del c
+    del x, dy, gx, gd, off
+    torch.cuda.empty_cache()
+    return res
 
 
 def dispatch_timings(torch, E, W, dev, empty):

@@ -70,7 +70,8 @@ extern "C" {
 #endif
 
 /* Raised whenever an entry point is added or changes (2: the caller-amax
- * export variant, the copy floor and the grouped GEMMs). */
+ * export variant, the copy floor, the grouped GEMMs and the grouped
+ * weight-gradient pair). */
 #define MXQ_VERSION 2
 
 typedef enum {
@@ -371,6 +372,53 @@ int mxq_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float 
                    int64_t rows_per_a_scale, const uint8_t *b, const uint8_t *b_block_scales,
                    const float *b_scales, int64_t rows_per_b_scale, int64_t M, int64_t N,
                    int64_t K, int out_dtype, void *c, void *stream);
+
+/*
+ * Grouped columnwise MXFP8 copy in the layout of the expert layer's weight
+ * gradient (the columnwise copy of the MXFP8 recipe paragraph of "Miles:
+ * end-to-end MXFP8 and per-token NVFP4 RL on Blackwell", which feeds the
+ * backward GEMMs): the same 32x1 blocks as mxq_grouped_quantize's
+ * columnwise copy (32-row blocks from each segment's first row, a partial
+ * tail block per segment), stored transposed so that each segment's rows
+ * are contiguous, with every segment padded to a multiple of 128 rows by
+ * zero blocks (code 0, scale byte 0):
+ *   codes_t[c][32 P[e] + i] = code of x[o_e + i][c] for i < n_e, 0 up to the padding;
+ *   scales_t[c][P[e] + j] = E8M0 byte of block j of segment e in column c.
+ *
+ *   x  [total_rows][cols] BF16 (expert-sorted), 16-byte aligned; cols % 32 == 0.
+ *   seg_offsets  [n_groups + 1] int64, device memory, as for mxq_grouped_quantize.
+ *   codes_t [cols][pitch], 16-byte aligned, and scales_t [cols][pitch / 32],
+ *      4-byte aligned, pitch = 128 * ceil(total_rows / 128) + 128 * n_groups;
+ *      columns past the last segment's padding are not written.
+ *   block_offsets [n_groups + 1] int64 (written): P[e], segment e's first
+ *      32-row block in the padded layout (P[0] = 0).
+ *   n_groups <= 2^40; malformed offsets are clamped as in mxq_grouped_quantize.
+ */
+int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                const int64_t *seg_offsets, int64_t n_groups, uint8_t *codes_t,
+                                uint8_t *scales_t, int64_t *block_offsets, void *stream);
+
+/*
+ * The expert layer's MXFP8 weight gradient: for every expert e,
+ *   C_e[m][n] = sum over k in [32 P[e], 32 P[e+1]) of dec(a[m][k]) 2^(sa[m][k/32] - 127)
+ *               dec(b[n][k]) 2^(sb[n][k/32] - 127),
+ * a contraction over the segment's rows, with a and b two copies made by
+ * mxq_mxfp8_grouped_colwise_t over the same segments (a from dY [rows][M],
+ * b from X [rows][N]: C_e = dW_e = dY_e^T X_e) and P their block_offsets.
+ * Padding blocks hold zeros and add nothing.  Same accumulation and bound
+ * as mxq_mxfp8_gemm, with K the segment's rows.
+ *
+ *   a [M][pitch], a_scales [M][pitch / 32]; b [N][pitch], b_scales [N][pitch / 32].
+ *   block_offsets [n_groups + 1] int64, device memory.
+ *   c [n_groups][M][N] fp32 or BF16 (out_dtype); an expert with no rows gets zeros.
+ *   pitch % 128 == 0 (MXQ_ERR_SHAPE), pitch <= 2^23 and n_groups * ceil(M / 256) *
+ *   ceil(N / 256) within the GEMM tile limit (MXQ_ERR_SIZE).  Malformed
+ *   offsets are clamped into [0, pitch) and cut to whole 128-column steps.
+ */
+int mxq_mxfp8_grouped_wgrad(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                            const uint8_t *b_scales, const int64_t *block_offsets,
+                            int64_t n_groups, int64_t M, int64_t N, int64_t pitch, int out_dtype,
+                            void *c, void *stream);
 
 /*
  * Grouped (per-expert) NVFP4 GEMM, the MoE expert layer on per-token NVFP4

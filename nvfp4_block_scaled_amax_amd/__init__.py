@@ -10,7 +10,8 @@ from ._binding import (  # noqa: F401
     MXQ_ERR_LAUNCH, MXQ_ERR_NULL, MXQ_ERR_OFFSETS, MXQ_ERR_SHAPE, MXQ_ERR_SIZE,
     MXQ_FMT_MXFP8_COL, MXQ_FMT_MXFP8_ROW, MXQ_FMT_MXFP8_ROWCOL, MXQ_FMT_NVFP4, MXQ_OK,
     MXQ_OUT_BF16, MXQ_OUT_F32, mxq_mxfp8_gemm, mxq_mxfp8_grouped_gemm, mxq_nvfp4_gemm,
-    mxq_nvfp4_grouped_gemm, mxq_mxfp8_quantize_ocp_floor,
+    mxq_nvfp4_grouped_gemm, mxq_mxfp8_grouped_colwise_t, mxq_mxfp8_grouped_wgrad,
+    mxq_mxfp8_quantize_ocp_floor,
     mxq_mxfp8_quantize_rowcol_t, mxq_nvfp4_quantize_per_token_approx,
     MXQError, lib, mxq_dequantize_bf16, mxq_grouped_out, mxq_grouped_quantize,
     mxq_grouped_quantize_dispatch, mxq_copy_floor,

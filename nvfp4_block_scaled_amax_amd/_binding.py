@@ -46,6 +46,8 @@ EXPORTS = (
     "mxq_quantize_dequant_bf16",
     "mxq_mxfp8_gemm",
     "mxq_mxfp8_grouped_gemm",
+    "mxq_mxfp8_grouped_colwise_t",
+    "mxq_mxfp8_grouped_wgrad",
     "mxq_nvfp4_gemm",
     "mxq_nvfp4_grouped_gemm",
     "mxq_mxfp8_quantize_ocp_floor",
@@ -94,6 +96,8 @@ def lib():
         "mxq_quantize_dequant_bf16": [I, P, I64, I64, P, P, P, P, P],
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
         "mxq_mxfp8_grouped_gemm": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
+        "mxq_mxfp8_grouped_colwise_t": [P, I64, I64, P, I64, P, P, P, P],
+        "mxq_mxfp8_grouped_wgrad": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_grouped_gemm": [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_quantize_ocp_floor": [P, I64, I64, P, P, P, P, P],
@@ -243,6 +247,22 @@ def mxq_mxfp8_grouped_gemm(a, a_scales, b, b_scales, seg_offsets, n_groups, tota
                                         _ptr(seg_offsets), n_groups, total_rows, N, K, out_dtype,
                                         _ptr(c), _stream(stream)),
            "mxq_mxfp8_grouped_gemm")
+
+
+def mxq_mxfp8_grouped_colwise_t(x, total_rows, cols, seg_offsets, n_groups, codes_t, scales_t,
+                                block_offsets, stream=None):
+    _check(lib().mxq_mxfp8_grouped_colwise_t(_ptr(x), total_rows, cols, _ptr(seg_offsets),
+                                             n_groups, _ptr(codes_t), _ptr(scales_t),
+                                             _ptr(block_offsets), _stream(stream)),
+           "mxq_mxfp8_grouped_colwise_t")
+
+
+def mxq_mxfp8_grouped_wgrad(a, a_scales, b, b_scales, block_offsets, n_groups, M, N, pitch,
+                            out_dtype, c, stream=None):
+    _check(lib().mxq_mxfp8_grouped_wgrad(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                         _ptr(block_offsets), n_groups, M, N, pitch, out_dtype,
+                                         _ptr(c), _stream(stream)),
+           "mxq_mxfp8_grouped_wgrad")
 
 
 def mxq_nvfp4_grouped_gemm(a, a_block_scales, a_scales, b, b_block_scales, b_scales,

@@ -226,6 +226,48 @@ def mxfp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, seg_offsets,
     return c
 
 
+class GroupedColT(NamedTuple):
+    codes_t: torch.Tensor         # [cols][pitch]
+    scales_t: torch.Tensor        # [cols][pitch / 32]
+    block_offsets: torch.Tensor   # [G + 1] int64: segment e's first 32-row block
+
+
+def grouped_colt_pitch(total_rows: int, n_groups: int) -> int:
+    """Row pitch of the grouped transposed columnwise copy."""
+    return -(-total_rows // 128) * 128 + 128 * n_groups
+
+
+def mxfp8_grouped_colwise_t(x, seg_offsets, stream=None) -> GroupedColT:
+    """The grouped columnwise MXFP8 copy of the expert-sorted rows x [R][cols],
+    transposed with every segment padded to 128 rows (the weight-gradient
+    operand layout)."""
+    x = _bf16_bits(x)
+    R, cols = x.shape
+    G = seg_offsets.numel() - 1
+    pitch = grouped_colt_pitch(R, G)
+    out = GroupedColT(_empty((cols, pitch), torch.uint8, x),
+                      _empty((cols, pitch // 32), torch.uint8, x),
+                      _empty((G + 1,), torch.int64, x))
+    B.mxq_mxfp8_grouped_colwise_t(x, R, cols, seg_offsets, G, out.codes_t, out.scales_t,
+                                  out.block_offsets, stream)
+    return out
+
+
+def mxfp8_grouped_wgrad(a: GroupedColT, b: GroupedColT, out_dtype=torch.float32,
+                        stream=None) -> torch.Tensor:
+    """Per-expert C_e = A_e x B_e^T contracting over each segment's rows, from
+    two grouped transposed copies over the same segments (a from dY, b from
+    X: C_e = dW_e); returns C [G][M][N]."""
+    M, pitch = a.codes_t.shape
+    N = b.codes_t.shape[0]
+    G = a.block_offsets.numel() - 1
+    c = torch.empty((G, M, N), dtype=out_dtype, device=a.codes_t.device)
+    code = B.MXQ_OUT_BF16 if out_dtype == torch.bfloat16 else B.MXQ_OUT_F32
+    B.mxq_mxfp8_grouped_wgrad(a.codes_t, a.scales_t, b.codes_t, b.scales_t, a.block_offsets, G,
+                              M, N, pitch, code, c, stream)
+    return c
+
+
 def nvfp4_grouped_gemm(a_codes, a_block_scales, a_scales, b_codes, b_block_scales, b_scales,
                        seg_offsets, out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
     """Per-expert C[r] = a_scales[r] b_scales[e] A[r] x B_e^T for the rows r of

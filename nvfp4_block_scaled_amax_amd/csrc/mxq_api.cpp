@@ -515,6 +515,66 @@ int mxq_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales, const uint
                                                    (hipStream_t)stream));
 }
 
+int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                const int64_t *seg_offsets, int64_t n_groups, uint8_t *codes_t,
+                                uint8_t *scales_t, int64_t *block_offsets, void *stream)
+{
+    if (!x || !seg_offsets || !codes_t || !scales_t || !block_offsets)
+        return MXQ_ERR_NULL;
+    if (!size_ok(total_rows, cols) || cols > MAX_MXFP8_COLS || n_groups < 1 ||
+        n_groups > ((int64_t)1 << 40) || total_rows > MAX_ELEMS / 4)
+        return MXQ_ERR_SIZE;
+    const int64_t pitch = mxq::grouped_colt_pitch(total_rows, n_groups);
+    if (!size_ok(pitch, cols) || !mxfp8_grid_ok(pitch / 32, cols))
+        return MXQ_ERR_SIZE;
+    if (cols % 32 != 0)
+        return MXQ_ERR_SHAPE;
+    const Buf b[5] = {{x, 2 * total_rows * cols, 16, false},
+                      {seg_offsets, 8 * (n_groups + 1), 8, false},
+                      {codes_t, pitch * cols, 16, true},
+                      {scales_t, pitch / 32 * cols, 4, true},
+                      {block_offsets, 8 * (n_groups + 1), 8, true}};
+    const int st = check_bufs(b, 5);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_grouped_colt(x, total_rows, cols, seg_offsets, n_groups,
+                                                   codes_t, scales_t, block_offsets,
+                                                   (hipStream_t)stream));
+}
+
+int mxq_mxfp8_grouped_wgrad(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                            const uint8_t *b_scales, const int64_t *block_offsets,
+                            int64_t n_groups, int64_t M, int64_t N, int64_t pitch, int out_dtype,
+                            void *c, void *stream)
+{
+    if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
+        return MXQ_ERR_ARG;
+    if (!a || !a_scales || !b || !b_scales || !block_offsets || !c)
+        return MXQ_ERR_NULL;
+    if (!size_ok(M, pitch) || !size_ok(N, pitch) || !size_ok(M, 4 * N) || n_groups < 1 ||
+        !size_ok(n_groups, 4 * M * N) || n_groups > MAX_ELEMS / 8 - 1)
+        return MXQ_ERR_SIZE;
+    if (pitch % 128 != 0)
+        return MXQ_ERR_SHAPE;
+    if (pitch > MAX_GEMM_K ||
+        n_groups * ((M + 255) / 256) * ((N + 255) / 256) > mxq::MAX_GEMM_TILES)
+        return MXQ_ERR_SIZE;
+    const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
+    const Buf bb[6] = {{a, M * pitch, 16, false},
+                       {a_scales, M * (pitch / 32), 4, false},
+                       {b, N * pitch, 16, false},
+                       {b_scales, N * (pitch / 32), 4, false},
+                       {block_offsets, 8 * (n_groups + 1), 8, false},
+                       {c, esz * n_groups * M * N, esz, true}};
+    const int st = check_bufs(bb, 6);
+    if (st != MXQ_OK)
+        return st;
+    return launched(mxq::launch_mxfp8_grouped_wgrad(a, a_scales, b, b_scales, block_offsets,
+                                                    n_groups, M, N, pitch,
+                                                    out_dtype == MXQ_OUT_BF16, c,
+                                                    (hipStream_t)stream));
+}
+
 int mxq_nvfp4_grouped_gemm(const uint8_t *a, const uint8_t *a_block_scales, const float *a_scales,
                            const uint8_t *b, const uint8_t *b_block_scales, const float *b_scales,
                            const int64_t *seg_offsets, int64_t n_groups, int64_t total_rows,

@@ -74,6 +74,9 @@ static_assert(MXG_SCALE_BASE + MXG_SCALE_BUFS * MXG_SCALE_BYTES <= GEMM_LDS_BYTE
 // Loads one wavefront issues per step: four 16-byte copies each of A and B,
 // and on even steps one scale word each of A and B.
 constexpr int MXG_LOADS_ODD = 8, MXG_LOADS_EVEN = 10;
+// Rows per block of the grouped transposed columnwise copy (its offsets
+// count 32-row blocks).
+constexpr int64_t TILE_K_BLOCK = 32;
 
 // 16-byte chunk c of LDS row r (8 chunks per 128-byte row), swizzled by
 // (r / 2) % 8.  A 16-byte read serves 16 lanes per cycle (64 banks: 16
@@ -96,8 +99,8 @@ __device__ __forceinline__ int swz64(int r, int c) { return r * 4 + (c ^ ((r >> 
 struct MxgOffsets {
     uint32_t r0, c16;           // first row of copy 0 (16w + l/4), 16 * logical chunk
     uint32_t ra_max, rb_max;    // last valid row of the A and B tiles
-    uint32_t K;
-    uint32_t as, bs;            // scale-row offsets (clamped row * K / 32)
+    uint32_t K;                 // row pitch of A and B (bytes)
+    uint32_t as, bs;            // scale-row offsets (clamped row * pitch / 32)
     __device__ __forceinline__ uint32_t a(int i) const
     {
         const uint32_t r = r0 + 64 * i;
@@ -110,17 +113,17 @@ struct MxgOffsets {
     }
 };
 __device__ __forceinline__ MxgOffsets mxg_offsets(int64_t m0, int64_t n0, int64_t M, int64_t N,
-                                                  int64_t K, int w, int lane)
+                                                  int64_t ld, int w, int lane)
 {
     MxgOffsets o;
     o.r0 = (uint32_t)(16 * w + (lane >> 2));
     o.c16 = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     o.ra_max = (uint32_t)(M - 1 - m0 < GEMM_BM ? M - 1 - m0 : GEMM_BM - 1);
     o.rb_max = (uint32_t)(N - 1 - n0 < GEMM_BN ? N - 1 - n0 : GEMM_BN - 1);
-    o.K = (uint32_t)K;
+    o.K = (uint32_t)ld;
     const uint32_t r = (uint32_t)(64 * w + lane);
-    o.as = (r < o.ra_max ? r : o.ra_max) * (uint32_t)(K >> 5);
-    o.bs = (r < o.rb_max ? r : o.rb_max) * (uint32_t)(K >> 5);
+    o.as = (r < o.ra_max ? r : o.ra_max) * (uint32_t)(ld >> 5);
+    o.bs = (r < o.rb_max ? r : o.rb_max) * (uint32_t)(ld >> 5);
     return o;
 }
 
@@ -392,11 +395,14 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], uint8
 // byte selectors are static.
 // One 256x256 tile of C = A B^T at (m0, n0), C row-major [M][N].
 template <bool BF16_OUT>
+// A and B rows have pitch ld bytes (scale rows ld / 32); the product runs
+// over K <= ld columns (K % 128 == 0; K == 0 gives a zero tile).
 __device__ __forceinline__ void mxg_tile(uint8_t *lds, const uint8_t *__restrict__ A,
                                          const uint8_t *__restrict__ As,
                                          const uint8_t *__restrict__ B,
                                          const uint8_t *__restrict__ Bs, int64_t M, int64_t N,
-                                         int64_t K, int64_t m0, int64_t n0, void *__restrict__ C)
+                                         int64_t K, int64_t ld, int64_t m0, int64_t n0,
+                                         void *__restrict__ C)
 {
     const int t = (int)tid();
     const int lane = t & 63, wave = (int)wave_in_group();    // wave index: uniform
@@ -410,10 +416,15 @@ __device__ __forceinline__ void mxg_tile(uint8_t *lds, const uint8_t *__restrict
 #pragma unroll
         for (int j = 0; j < 4; j++)
             acc[i][j] = f32x16_t{};
+    if (nsteps == 0) {
+        gemm_epilogue<BF16_OUT, false>(acc, lds, wave, lane, m0, n0, M, N, C, nullptr, 1,
+                                       nullptr, 1);
+        return;
+    }
 
-    const MxgOffsets off = mxg_offsets(m0, n0, M, N, K, wave, lane);
-    const uint8_t *a = A + m0 * K, *b = B + n0 * K;
-    const uint8_t *as_ = As + m0 * (K >> 5), *bs_ = Bs + n0 * (K >> 5);
+    const MxgOffsets off = mxg_offsets(m0, n0, M, N, ld, wave, lane);
+    const uint8_t *a = A + m0 * ld, *b = B + n0 * ld;
+    const uint8_t *as_ = As + m0 * (ld >> 5), *bs_ = Bs + n0 * (ld >> 5);
     const uint32_t ring = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
 
     // Prologue: steps 0, 1 and 2 in flight; wait for steps 0 and 1.
@@ -481,8 +492,8 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_gemm_kernel(
     uint32_t mt, nt;
     if (!gemm_tile(grid, wg_id(), &mt, &nt))
         return;
-    mxg_tile<BF16_OUT>(lds, A, As, B, Bs, M, N, K, (int64_t)mt * GEMM_BM, (int64_t)nt * GEMM_BN,
-                       C);
+    mxg_tile<BF16_OUT>(lds, A, As, B, Bs, M, N, K, K, (int64_t)mt * GEMM_BM,
+                       (int64_t)nt * GEMM_BN, C);
 }
 
 // ---------------------------------------------------------------------------
@@ -569,7 +580,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_grouped_gemm_kernel(
     mt = uniform_i64(mt);
     const int64_t esz = BF16_OUT ? 2 : 4;
     mxg_tile<BF16_OUT>(lds, A + lo * K, As + lo * (K >> 5), B + e * N * K, Bs + e * N * (K >> 5),
-                       n, N, K, mt * GEMM_BM, (int64_t)nt * GEMM_BN,
+                       n, N, K, K, mt * GEMM_BM, (int64_t)nt * GEMM_BN,
                        reinterpret_cast<uint8_t *>(C) + lo * N * esz);
 }
 
@@ -878,6 +889,61 @@ hipError_t launch_nvfp4_gemm(const uint8_t *a, const uint8_t *a_block_scales,
         hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, block, 0, stream, a, a_block_scales,
                            a_scales, rows_per_a, b, b_block_scales, b_scales, rows_per_b, M, N, K,
                            g, c);
+    return hipGetLastError();
+}
+
+// Grouped product over each segment's rows (the expert layer's weight
+// gradient): for expert e, C_e[m][n] = sum over k in [32 P[e], 32 P[e+1])
+// of A[m][k] B[n][k], where A [M][ld] and B [N][ld] are grouped transposed
+// padded columnwise copies (scales [.][ld / 32]) whose segment e occupies
+// columns 32 P[e] .. 32 P[e+1] (a multiple of 128 wide); C [G][M][N].
+// P is device data: each range is clamped into [0, ld) and cut to whole
+// 128-column steps, so malformed offsets give meaningless tiles, never an
+// access out of bounds.
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(GEMM_THREADS) mxfp8_grouped_wgrad_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const int64_t *__restrict__ P, int64_t G, int64_t M,
+    int64_t N, int64_t ld, GroupedGemmGrid grid, void *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GEMM_LDS_BYTES];
+    const uint32_t w = wg_id();
+    const uint32_t L = (w & 7) * grid.per_xcd + (w >> 3);
+    const uint32_t per_e = grid.max_mtiles * grid.tiles_n;
+    const int64_t e = L / per_e;
+    if (e >= G)
+        return;
+    const uint32_t r = L % per_e, mt = r / grid.tiles_n, nt = r % grid.tiles_n;
+    int64_t k0 = P[e] * TILE_K_BLOCK, k1 = P[e + 1] * TILE_K_BLOCK;
+    k0 = k0 < 0 ? 0 : (k0 > ld ? ld : k0) & ~(int64_t)127;
+    k1 = k1 < k0 ? k0 : (k1 > ld ? ld : k1);
+    const int64_t K = (k1 - k0) & ~(int64_t)127;
+    const int64_t esz = BF16_OUT ? 2 : 4;
+    mxg_tile<BF16_OUT>(lds, A + k0, As + (k0 >> 5), B + k0, Bs + (k0 >> 5), M, N, K, ld,
+                       (int64_t)mt * GEMM_BM, (int64_t)nt * GEMM_BN,
+                       reinterpret_cast<uint8_t *>(C) + e * M * N * esz);
+}
+
+hipError_t launch_mxfp8_grouped_wgrad(const uint8_t *a, const uint8_t *a_scales,
+                                      const uint8_t *b, const uint8_t *b_scales,
+                                      const int64_t *block_offsets, int64_t n_groups, int64_t M,
+                                      int64_t N, int64_t ld, bool bf16_out, void *c,
+                                      hipStream_t stream)
+{
+    const int64_t tm = (M + GEMM_BM - 1) / GEMM_BM, tn = (N + GEMM_BN - 1) / GEMM_BN;
+    if (n_groups * tm * tn > MAX_GEMM_TILES)  // checked by the caller
+        return hipErrorInvalidValue;
+    GroupedGemmGrid g;
+    g.tiles_n = (uint32_t)tn;
+    g.max_mtiles = (uint32_t)tm;
+    g.per_xcd = (uint32_t)((n_groups * tm * tn + 7) / 8);
+    const dim3 grid(8 * g.per_xcd), block(GEMM_THREADS);
+    if (bf16_out)
+        hipLaunchKernelGGL(mxfp8_grouped_wgrad_kernel<true>, grid, block, 0, stream, a, a_scales,
+                           b, b_scales, block_offsets, n_groups, M, N, ld, g, c);
+    else
+        hipLaunchKernelGGL(mxfp8_grouped_wgrad_kernel<false>, grid, block, 0, stream, a,
+                           a_scales, b, b_scales, block_offsets, n_groups, M, N, ld, g, c);
     return hipGetLastError();
 }
 

@@ -31,6 +31,13 @@ inline int64_t mxfp8_tiles(int64_t row_tiles, int64_t cols)
 // tile, the count rounded up to a multiple of 8 (one share per XCD).
 constexpr int64_t MAX_GEMM_TILES = MAX_GRID_ITEMS / 256 - 8;
 
+// Row pitch of the grouped transposed columnwise copy: every segment's
+// rows rounded up to a multiple of 128 fit in it.
+inline int64_t grouped_colt_pitch(int64_t rows, int64_t n_groups)
+{
+    return (rows + 127) / 128 * 128 + 128 * n_groups;
+}
+
 // 256-row tiles the grouped GEMM launches for: every segment's rows in
 // 256-row tiles, at most one partial tile per segment.
 inline int64_t grouped_gemm_mtiles(int64_t rows, int64_t n_groups)
@@ -127,6 +134,23 @@ hipError_t launch_dequant_nvfp4(const uint8_t *codes, const uint8_t *block_scale
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                              const uint8_t *b_scales, int64_t M, int64_t N, int64_t K,
                              bool bf16_out, void *c, hipStream_t stream);
+
+// Grouped columnwise copy, transposed and padded: codes [cols][pitch] and
+// scales [cols][pitch / 32] (pitch = grouped_colt_pitch), segment e's
+// blocks from block P[e] (P [G+1], written), each segment rounded up to 128
+// rows with zero blocks.
+hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                     const int64_t *off, int64_t n_groups, uint8_t *cct,
+                                     uint8_t *cst, int64_t *P, hipStream_t stream);
+
+// Grouped weight gradient: C_e[M][N] = A[:, 32 P[e] .. 32 P[e+1]) x
+// B[:, same]^T for every expert e, A [M][ld] and B [N][ld] in the grouped
+// transposed padded layout (ld % 128 == 0); C [G][M][N].
+hipError_t launch_mxfp8_grouped_wgrad(const uint8_t *a, const uint8_t *a_scales,
+                                      const uint8_t *b, const uint8_t *b_scales,
+                                      const int64_t *block_offsets, int64_t n_groups, int64_t M,
+                                      int64_t N, int64_t ld, bool bf16_out, void *c,
+                                      hipStream_t stream);
 
 // Grouped: C[r][N] = A[r] (MXFP8 rows of segment e) x B_e^T for every r in
 // segment e = seg_offsets[e] .. seg_offsets[e+1] (device data); B [G][N][K],

@@ -183,7 +183,7 @@ __device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t sca
 // (= rows) and lds_t (= rows / 32).  Each lane writes, per column, its 8 rows
 // as 8 contiguous bytes.
 template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false, bool COLT = false,
-          bool LATE = false>
+          bool LATE = false, bool TLDS = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -291,9 +291,17 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
                     const uint32_t lo = perm(P[1][j], P[0][j], sel);
                     const uint32_t hi = perm(P[3][j], P[2][j], sel);
                     const uint32_t c = c8 + 2 * j + e;
-                    st_nt8(o.cc + (c * o.ld_t + 8 * rg), lo, hi);
+                    if constexpr (TLDS) {
+                        // LDS staging (o.cc, o.cs point into LDS): two
+                        // 4-byte writes, the column pitch being 4-aligned.
+                        uint32_t *d = reinterpret_cast<uint32_t *>(o.cc + c * o.ld_t + 8 * rg);
+                        d[0] = lo;
+                        d[1] = hi;
+                    } else {
+                        st_nt8(o.cc + ((size_t)c * o.ld_t + 8 * rg), lo, hi);
+                    }
                     if (rg == 0)
-                        o.cs[c * o.lds_t] = (uint8_t)(sb[j] >> (16 * e));
+                        o.cs[(size_t)c * o.lds_t] = (uint8_t)(sb[j] >> (16 * e));
                 }
             }
         }
@@ -482,10 +490,75 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
     tile_body<ROW, true, false, WPW, false, false, false, true>(G, rc, rs, cct, cst, nullptr);
 }
 
-// P[e] = sum_{f<e} ceil(n_f / 32), written to P[0..G].  One workgroup;
-// sequential over chunks of 256 segments with a block scan.
+// Grouped columnwise copy, transposed and padded (the weight-gradient
+// operand layout): codes [cols][pitch], scales [cols][pitch / 32]; segment
+// e's 32-row blocks, rounded up to a multiple of 4 (128 rows) with zero
+// blocks, start at block P[e].  Workgroup (strip, q) converts blocks
+// 4q .. 4q+3 (one segment's, by the padding) of a 128-column strip, one per
+// wavefront, stages the codes in LDS as [column][128 rows] and writes each
+// column's 128 bytes as one whole line of codes_t (written straight from
+// the lanes, each column's bytes were 32-byte pieces of four lines: 1.52 ms
+// on 262144 x 2048, 17 % of the copy floor).  Padding blocks (no rows) load
+// from row 0, which lies in the tensor, and keep nothing: zero codes and
+// scale bytes.
+constexpr int COLT_LDS_PITCH = TILE_COLS + 4;    // bytes per staged column (bank spread)
+__global__ void __launch_bounds__(256) mxfp8_grouped_colt_kernel(Geometry G,
+                                                                 uint8_t *__restrict__ cct,
+                                                                 uint8_t *__restrict__ cst)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t sc[TILE_COLS * COLT_LDS_PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t ss[TILE_COLS * 4];
+    const int lane = (int)lane_id(), w = (int)wave_in_group();
+    const int g = lane & 15, rg = lane >> 4;
+    const int64_t wg = wg_id();
+    const int64_t strip = wg % G.nct, T0 = 4 * (wg / G.nct);
+    int64_t ntiles = G.P[G.n_groups];
+    if (ntiles > G.max_tiles)
+        ntiles = G.max_tiles;
+    if (T0 >= ntiles)                      // uniform: ntiles is a multiple of 4
+        return;
+    const int64_t T = T0 + w;
+    const int64_t e = tile_segment(G.P, G.n_groups, T);
+    int64_t lo, hi;
+    segment_rows(G.off, e, G.rows, &lo, &hi);
+    const int64_t row0 = lo + (T - G.P[e]) * TILE_ROWS;
+    const int64_t left = hi - row0;
+    const int nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+    const int64_t tcol = strip * TILE_COLS;
+    const uint32_t cols = (uint32_t)G.cols, c8 = 8u * (uint32_t)g;
+    const bool col_ok = tcol + c8 < G.cols;
+    const uint16_t *xt = G.x + (nrows > 0 ? row0 : 0) * G.cols + tcol;
+    uint32_t v[8][4];
+    load_tile<false>(v, xt, cols, c8, nrows, rg, col_ok);
+    const TileOut o{nullptr, nullptr, sc + TILE_ROWS * w, ss + w, nullptr, COLT_LDS_PITCH, 4};
+    convert_tile<false, true, false, false, false, true, false, true>(v, cols, c8, nrows, g, rg,
+                                                                      col_ok, o);
+    __syncthreads();
+    const int t = (int)tid();
+    const int64_t pitch = G.max_tiles * TILE_ROWS;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int q = t + 256 * i, c = q >> 3, piece = q & 7;   // 16-byte piece of column c
+        if (tcol + c < G.cols) {
+            const uint32_t *s4 = reinterpret_cast<const uint32_t *>(sc + c * COLT_LDS_PITCH +
+                                                                    16 * piece);
+            const u32x4_t val = {s4[0], s4[1], s4[2], s4[3]};
+            __builtin_nontemporal_store(
+                val, reinterpret_cast<u32x4_t *>(cct + (tcol + c) * pitch + TILE_ROWS * T0 +
+                                                 16 * piece));
+        }
+    }
+    if (t < TILE_COLS && tcol + t < G.cols)
+        *reinterpret_cast<uint32_t *>(cst + (tcol + t) * G.max_tiles + T0) =
+            *reinterpret_cast<const uint32_t *>(ss + 4 * t);
+}
+
+// P[e] = sum_{f<e} ceil(n_f / 32) (each rounded up to a multiple of
+// `pad` 32-row blocks), written to P[0..G].  One workgroup; sequential over
+// chunks of 256 segments with a block scan.
 __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__restrict__ off,
                                                               int64_t n_groups, int64_t total_rows,
+                                                              int64_t pad,
                                                               int64_t *__restrict__ P)
 {
     __shared__ int64_t part[256];
@@ -497,6 +570,7 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
             int64_t lo, hi;
             segment_rows(off, e, total_rows, &lo, &hi);
             n = (hi - lo + 31) >> 5;
+            n = (n + pad - 1) / pad * pad;
         }
         part[tid()] = n;
         __syncthreads();
@@ -641,6 +715,26 @@ hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint
     return hipGetLastError();
 }
 
+hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                     const int64_t *off, int64_t n_groups, uint8_t *cct,
+                                     uint8_t *cst, int64_t *P, hipStream_t stream)
+{
+    const int64_t max_tiles = grouped_colt_pitch(total_rows, n_groups) / TILE_ROWS;
+    if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
+                       total_rows, (int64_t)4, P);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
+               n_groups, nullptr, 0};
+    const int64_t wgs = max_tiles / 4 * G.nct;          // max_tiles % 4 == 0
+    hipLaunchKernelGGL(mxfp8_grouped_colt_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, G,
+                       cct, cst);
+    return hipGetLastError();
+}
+
 hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t cols,
                                 const int64_t *off, int64_t n_groups, uint8_t *rc, uint8_t *rs,
                                 uint8_t *cc, uint8_t *cs, int64_t *P,
@@ -650,7 +744,7 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
     if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
-                       total_rows, P);
+                       total_rows, (int64_t)1, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -104,6 +104,16 @@ def test_grouped_quantize(fmt, x, off, rows, cols, G, o):
 
 
 @SETTINGS
+@given(x=ptrs, off=ptrs, ct=ptrs, cs=ptrs, P=ptrs, rows=sizes, cols=sizes, G=sizes, M=sizes,
+       N=sizes, pitch=sizes, dt=st.integers(-1, 2))
+def test_grouped_weight_gradient_pair(x, off, ct, cs, P, rows, cols, G, M, N, pitch, dt):
+    s = status(mxq.mxq_mxfp8_grouped_colwise_t, x, rows, cols, off, G, ct, cs, P, 0)
+    assert s in ERRORS
+    s = status(mxq.mxq_mxfp8_grouped_wgrad, ct, cs, x, cs, P, G, M, N, pitch, dt, off, 0)
+    assert s in ERRORS
+
+
+@SETTINGS
 @given(src=ptrs, dst=ptrs, nr=sizes, nw=sizes)
 def test_copy_floor(src, dst, nr, nw):
     s = status(mxq.mxq_copy_floor, src, nr, dst, nw, 0)

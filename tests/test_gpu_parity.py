@@ -574,6 +574,107 @@ def check_grouped(orc, x, off, name):
     return g8, g4, (rc, rs, c4, b4, s4)
 
 
+def padded_colt(orc, x, off):
+    """The oracle's grouped columnwise copy laid out as mxq_mxfp8_grouped_colwise_t
+    stores it: transposed, each segment padded to 128 rows with zero codes
+    and zero scale bytes.  Returns (codes_t, scales_t, block offsets)."""
+    R, cols = x.shape
+    G = off.size - 1
+    blocks = []
+    for e in range(G):
+        c = -(-(int(off[e + 1]) - int(off[e])) // 32)          # ceil(rows / 32)
+        blocks.append(-(-c // 4) * 4)                           # up to a multiple of 4
+    P = np.concatenate([[0], np.cumsum(blocks)]).astype(np.int64)
+    ct = np.zeros((cols, 32 * int(P[-1])), np.uint8)
+    st = np.zeros((cols, int(P[-1])), np.uint8)
+    for e in range(G):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        oc, os_, _ = orc.mxfp8_colwise_grouped(x[a:b], np.array([0, b - a], np.int64))
+        ct[:, 32 * P[e]:32 * P[e] + (b - a)] = oc.T
+        st[:, P[e]:P[e] + os_.shape[0]] = os_.T
+    return ct, st, P
+
+
+def check_grouped_colt(orc, x, off, name):
+    """mxq_mxfp8_grouped_colwise_t against padded_colt, byte for byte, over
+    every segment's padded columns and the block offsets."""
+    announce(f"grouped colwise transposed {name} R={x.shape[0]} G={off.size - 1}")
+    g = api.mxfp8_grouped_colwise_t(dev(x), dev(off))
+    torch.cuda.synchronize()
+    ct, st, P = padded_colt(orc, x, off)
+    assert list(host(g.block_offsets)) == list(P)
+    n = 32 * int(P[-1])
+    assert_same(host(g.codes_t)[:, :n], ct, f"{name} codes_t")
+    assert_same(host(g.scales_t)[:, :int(P[-1])], st, f"{name} scales_t")
+    return g
+
+
+def test_grouped_colwise_transposed_padded(orc):
+    """Segments of 0, 1, 31, 33, 128 and 200 rows (partial tail blocks, exact
+    128-row segments, empty ones), boundary-mode values."""
+    sizes = [0, 1, 31, 33, 128, 200, 0, 64]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    x = W.mode_boundary(512, 96, 4)[:int(off[-1])]
+    check_grouped_colt(orc, x, off, "ragged")
+    check_grouped_colt(orc, W.mode_random(40, 64, 5), np.array([0, 40], np.int64), "one segment")
+
+
+def test_grouped_weight_gradient(orc):
+    """The expert layer's weight gradient dW_e = dY_e^T X_e over each segment's
+    rows from two grouped transposed copies (dY [R][256], X [R][192]), every
+    expert (an empty one must give zeros) against the oracle's product of the
+    same padded operands."""
+    sizes = [0, 1, 31, 33, 128, 200, 0, 64]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    R = int(off[-1])
+    dy = W.student_t_activations(R, 256, 41)
+    x = W.mode_random(R, 192, 42)
+    announce(f"mxfp8 grouped wgrad R={R} G={len(sizes)} 256x192")
+    gd = api.mxfp8_grouped_colwise_t(dev(dy), dev(off))
+    gx = api.mxfp8_grouped_colwise_t(dev(x), dev(off))
+    for dt in (torch.float32, torch.bfloat16):
+        c = api.mxfp8_grouped_wgrad(gd, gx, out_dtype=dt)
+        torch.cuda.synchronize()
+        got = c.float().cpu().numpy().astype(np.float64)
+        dct, dst, P = padded_colt(orc, dy, off)
+        xct, xst, _ = padded_colt(orc, x, off)
+        for e in range(len(sizes)):
+            k0, k1 = 32 * int(P[e]), 32 * int(P[e + 1])
+            if k0 == k1:
+                assert np.all(got[e] == 0), f"empty expert {e}"
+                continue
+            C, S = orc.mxfp8_gemm(dct[:, k0:k1], dst[:, k0 // 32:k1 // 32],
+                                  xct[:, k0:k1], xst[:, k0 // 32:k1 // 32])
+            bound = (GEMM_REL + (k1 - k0) * 2.0 ** -24) * S
+            lim = bound if dt == torch.float32 else bound + 2.0 ** -8 * np.abs(C)
+            assert np.all(np.abs(got[e] - C) <= lim), f"expert {e} {dt}"
+
+
+def test_grouped_weight_gradient_moe_layer_sampled(orc):
+    """Config 5's routing (262144 rows, 128 experts): dW_e [768][2048] =
+    dY_e^T X_e for experts 0, 63 and 127 in full, the rest computed too."""
+    x, off = W.config5()
+    dy = W.student_t_activations(x.shape[0], 768, 43)
+    announce("mxfp8 grouped wgrad config5 768x2048")
+    gd = api.mxfp8_grouped_colwise_t(dev(dy), dev(off))
+    gx = api.mxfp8_grouped_colwise_t(dev(x), dev(off))
+    c = api.mxfp8_grouped_wgrad(gd, gx, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    P = host(gd.block_offsets)
+    assert list(P) == list(host(gx.block_offsets))
+    for e in (0, 63, 127):
+        a, b = int(off[e]), int(off[e + 1])
+        sub = np.array([0, b - a], np.int64)
+        dct, dst, Pe = padded_colt(orc, dy[a:b], sub)
+        xct, xst, _ = padded_colt(orc, x[a:b], sub)
+        assert 32 * (int(P[e + 1]) - int(P[e])) == dct.shape[1]
+        C, S = orc.mxfp8_gemm(dct, dst, xct, xst)
+        got = host(c[e]).astype(np.float64)
+        assert np.all(np.abs(got - C) <= (GEMM_REL + dct.shape[1] * 2.0 ** -24) * S), f"expert {e}"
+
+
 def test_grouped_ragged_stress(orc):
     """Segments of 0, 1, 31, 32, 33 and 4096 rows among random ones."""
     off = W.ragged_offsets(16384, 24, seed=7)
