@@ -494,63 +494,77 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
 // operand layout): codes [cols][pitch], scales [cols][pitch / 32]; segment
 // e's 32-row blocks, rounded up to a multiple of 4 (128 rows) with zero
 // blocks, start at block P[e].  Workgroup (strip, q) converts blocks
-// 4q .. 4q+3 (one segment's, by the padding) of a 128-column strip, one per
-// wavefront, stages the codes in LDS as [column][128 rows] and writes each
-// column's 128 bytes as one whole line of codes_t (written straight from
-// the lanes, each column's bytes were 32-byte pieces of four lines: 1.52 ms
-// on 262144 x 2048, 17 % of the copy floor).  Padding blocks (no rows) load
-// from row 0, which lies in the tensor, and keep nothing: zero codes and
-// scale bytes.
-constexpr int COLT_LDS_PITCH = TILE_COLS + 4;    // bytes per staged column (bank spread)
-__global__ void __launch_bounds__(256) mxfp8_grouped_colt_kernel(Geometry G,
-                                                                 uint8_t *__restrict__ cct,
-                                                                 uint8_t *__restrict__ cst)
+// WPW q .. WPW q + WPW - 1 of a 128-column strip, one per wavefront (each
+// finds its own segment), stages the codes in LDS as [column][32 WPW rows]
+// and writes each column's 32 WPW bytes as whole lines of codes_t.  Written
+// straight from the lanes, each column's bytes were 32-byte pieces of four
+// lines (1.52 ms on 262144 x 2048, 17 % of the copy floor; staged, 4 waves:
+// 330 us, 8 waves: 324 us, 16 waves: 325 us).  Consecutive workgroups take
+// consecutive q of one strip, so a column's row fills in order (320 us;
+// strip-fast 324 us).  What remains over the copy floor (255 us) is the
+// scatter itself: the same kernel writing each workgroup's 16 KB to one
+// contiguous block took 288 us, while padding the pitch against channel
+// aliasing changed nothing.  Padding blocks (no rows) load from row 0, which
+// lies in the tensor, and keep nothing: zero codes and scale bytes.
+template <int WPW>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G,
+                                                                      uint8_t *__restrict__ cct,
+                                                                      uint8_t *__restrict__ cst)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sc[TILE_COLS * COLT_LDS_PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t ss[TILE_COLS * 4];
+    constexpr int LP = TILE_ROWS * WPW + 4;          // bytes per staged column (bank spread)
+    constexpr int PIECES = 2 * WPW;                   // 16-byte pieces per staged column
+    __shared__ __attribute__((aligned(16))) uint8_t sc[TILE_COLS * LP];
+    __shared__ __attribute__((aligned(16))) uint8_t ss[TILE_COLS * WPW];
     const int lane = (int)lane_id(), w = (int)wave_in_group();
     const int g = lane & 15, rg = lane >> 4;
     const int64_t wg = wg_id();
-    const int64_t strip = wg % G.nct, T0 = 4 * (wg / G.nct);
+    const int64_t ngroups = (G.max_tiles + WPW - 1) / WPW;
+    const int64_t strip = wg / ngroups, T0 = WPW * (wg % ngroups);
     int64_t ntiles = G.P[G.n_groups];
     if (ntiles > G.max_tiles)
         ntiles = G.max_tiles;
-    if (T0 >= ntiles)                      // uniform: ntiles is a multiple of 4
+    if (T0 >= ntiles)                      // uniform
         return;
-    const int64_t T = T0 + w;
-    const int64_t e = tile_segment(G.P, G.n_groups, T);
-    int64_t lo, hi;
-    segment_rows(G.off, e, G.rows, &lo, &hi);
-    const int64_t row0 = lo + (T - G.P[e]) * TILE_ROWS;
-    const int64_t left = hi - row0;
-    const int nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+    const int nv = (int)min((int64_t)WPW, ntiles - T0);   // blocks of this group to write
     const int64_t tcol = strip * TILE_COLS;
     const uint32_t cols = (uint32_t)G.cols, c8 = 8u * (uint32_t)g;
     const bool col_ok = tcol + c8 < G.cols;
-    const uint16_t *xt = G.x + (nrows > 0 ? row0 : 0) * G.cols + tcol;
-    uint32_t v[8][4];
-    load_tile<false>(v, xt, cols, c8, nrows, rg, col_ok);
-    const TileOut o{nullptr, nullptr, sc + TILE_ROWS * w, ss + w, nullptr, COLT_LDS_PITCH, 4};
-    convert_tile<false, true, false, false, false, true, false, true>(v, cols, c8, nrows, g, rg,
-                                                                      col_ok, o);
+    if (w < nv) {                          // wave-uniform
+        const int64_t T = T0 + w;
+        const int64_t e = tile_segment(G.P, G.n_groups, T);
+        int64_t lo, hi;
+        segment_rows(G.off, e, G.rows, &lo, &hi);
+        const int64_t row0 = lo + (T - G.P[e]) * TILE_ROWS;
+        const int64_t left = hi - row0;
+        const int nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+        uint32_t v[8][4];
+        load_tile<false>(v, G.x + (nrows > 0 ? row0 : 0) * G.cols + tcol, cols, c8, nrows, rg,
+                         col_ok);
+        const TileOut o{nullptr, nullptr, sc + TILE_ROWS * w, ss + w, nullptr, LP, WPW};
+        convert_tile<false, true, false, false, false, true, false, true>(v, cols, c8, nrows, g,
+                                                                          rg, col_ok, o);
+    }
     __syncthreads();
     const int t = (int)tid();
     const int64_t pitch = G.max_tiles * TILE_ROWS;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int q = t + 256 * i, c = q >> 3, piece = q & 7;   // 16-byte piece of column c
-        if (tcol + c < G.cols) {
-            const uint32_t *s4 = reinterpret_cast<const uint32_t *>(sc + c * COLT_LDS_PITCH +
-                                                                    16 * piece);
+        const int q = t + 64 * WPW * i, c = q / PIECES, piece = q % PIECES;
+        if (tcol + c < G.cols && piece < 2 * nv) {
+            const uint32_t *s4 = reinterpret_cast<const uint32_t *>(sc + c * LP + 16 * piece);
             const u32x4_t val = {s4[0], s4[1], s4[2], s4[3]};
             __builtin_nontemporal_store(
                 val, reinterpret_cast<u32x4_t *>(cct + (tcol + c) * pitch + TILE_ROWS * T0 +
                                                  16 * piece));
         }
     }
-    if (t < TILE_COLS && tcol + t < G.cols)
-        *reinterpret_cast<uint32_t *>(cst + (tcol + t) * G.max_tiles + T0) =
-            *reinterpret_cast<const uint32_t *>(ss + 4 * t);
+    // Scale bytes: WPW per column, one dword per thread.
+    for (int q = t; q < TILE_COLS * WPW / 4; q += 64 * WPW) {
+        const int c = q / (WPW / 4), k = q % (WPW / 4);
+        if (tcol + c < G.cols && 4 * k < nv)
+            *reinterpret_cast<uint32_t *>(cst + (tcol + c) * G.max_tiles + T0 + 4 * k) =
+                *reinterpret_cast<const uint32_t *>(ss + WPW * c + 4 * k);
+    }
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32) (each rounded up to a multiple of
@@ -729,9 +743,10 @@ hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int6
         return err;
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
                n_groups, nullptr, 0};
-    const int64_t wgs = max_tiles / 4 * G.nct;          // max_tiles % 4 == 0
-    hipLaunchKernelGGL(mxfp8_grouped_colt_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, G,
-                       cct, cst);
+    constexpr int WPW = 8;
+    const int64_t wgs = (max_tiles + WPW - 1) / WPW * G.nct;
+    hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
+                       stream, G, cct, cst);
     return hipGetLastError();
 }
 
