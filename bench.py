@@ -538,7 +538,7 @@ def config_timings(torch, E, W, legs, log, only=None):
             res.update({k: v for k, v in gemm_timings(torch, E, W, dev, empty).items()
                         if k in only})
             log("GEMM timed")
-        if any("wgrad" in c or c == "C5_colt_mxfp8" for c in only):
+        if any("wgrad" in c or c in ("C5_colt_mxfp8", "C5_rowcolt_mxfp8") for c in only):
             res.update(wgrad_timings(torch, E, W, dev, empty, only))
             log("weight gradient timed")
     return res
@@ -806,7 +806,8 @@ def build_dsp(torch, E, W, legs, dev, empty):
 def wgrad_timings(torch, E, W, dev, empty, only=None):
     """The expert layer's weight-gradient pair at config 5's routing: the
     grouped transposed columnwise copies of X [262144][2048] (timed, with its
-    copy floor: a quantize config) and of dY [262144][768], then
+    copy floor: a quantize config; also with the rowwise copy from the same
+    read, the two copies dY needs) and of dY [262144][768], then
     dW_e [768][2048] = dY_e^T X_e for all 128 experts (timed, priced against
     the fp8 matrix peak).  Inputs are seeded torch normals on the device."""
     sel = (lambda n: True) if only is None else (lambda n: n in only)
@@ -832,9 +833,27 @@ def wgrad_timings(torch, E, W, dev, empty, only=None):
         fl = copy_floor(torch, E, rb, wb, 1, False, 10, 2)
         k, v = cfg_record("C5_colt_mxfp8", f"grouped MXFP8 columnwise, transposed and padded to "
                           f"128 rows per segment, {R}x{K}, {G} segments", ms, rb + wb, R * K, 1,
-                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel"], None, fl,
-                          (rb, wb))
+                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel<8, false>"], None,
+                          fl, (rb, wb))
         res[k] = v
+    if sel("C5_rowcolt_mxfp8"):
+        rc, rs = empty((R, K)), empty((R, K // 32))
+        fn = lambda: E.mxq_mxfp8_grouped_quantize_rowcol_t(x, R, K, off, G, rc, rs, gx[0], gx[1],
+                                                           gx[2])
+        ms = time_launches(torch, [fn], 10, 2, CFG_SAMPLES)
+        fn()
+        torch.cuda.synchronize()
+        blocks = int(gx[2][-1].item())
+        rb = 2 * R * K + 8 * (G + 1)
+        wb = R * K + R * K // 32 + K * 32 * blocks + K * blocks + 8 * (G + 1)
+        fl = copy_floor(torch, E, rb, wb, 1, False, 10, 2)
+        k, v = cfg_record("C5_rowcolt_mxfp8", f"grouped MXFP8 rowwise copy plus the columnwise "
+                          f"copy transposed and padded, one read, {R}x{K}, {G} segments", ms,
+                          rb + wb, R * K, 1,
+                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel<8, true>"], None,
+                          fl, (rb, wb))
+        res[k] = v
+        del rc, rs
     name = f"G_mxfp8_grouped_wgrad_{M}x{K}_over_{R}"
     if sel(name):
         E.mxq_mxfp8_grouped_colwise_t(x, R, K, off, G, gx[0], gx[1], gx[2])
@@ -1164,7 +1183,8 @@ def main():
     ap.add_argument("--config-only", default=None,
                     help="comma list of config names (C2a_<mode>, C2b_<mode>, C3_nvfp4, "
                          "C3_dequant, C4_gateup, C4_down, C4_gateup_amax, C4_down_amax, C5_mxfp8, C5_nvfp4, C5_dequant_mxfp8, "
-                         "C5_dequant_nvfp4): time only these, each beside its copy floor, and "
+                         "C5_dequant_nvfp4, C5_colt_mxfp8, C5_rowcolt_mxfp8, G_<gemm>): time "
+                         "only these, each beside its copy floor, and "
                          "print them as one JSON line (no step, no CPU baseline); for "
                          "profiling one shape per run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

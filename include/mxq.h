@@ -399,6 +399,25 @@ int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t c
                                 uint8_t *scales_t, int64_t *block_offsets, void *stream);
 
 /*
+ * Both MXFP8 copies the expert layer's backward needs from one read of its
+ * input (dY): the rowwise 1x32 copy, as mxq_grouped_quantize writes it
+ * (feeding the data gradient through mxq_mxfp8_grouped_gemm), and the
+ * columnwise copy of mxq_mxfp8_grouped_colwise_t (feeding
+ * mxq_mxfp8_grouped_wgrad), each block quantized independently from x as
+ * the MXFP8 recipe paragraph of "Miles: end-to-end MXFP8 and per-token NVFP4
+ * RL on Blackwell" states.  The bytes equal those two calls'.
+ *
+ *   row_codes [total_rows][cols], 16-byte aligned; row_scales [total_rows][cols / 32].
+ *      Rows in no segment are not written.
+ *   The other arguments as for mxq_mxfp8_grouped_colwise_t.
+ */
+int mxq_mxfp8_grouped_quantize_rowcol_t(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                        const int64_t *seg_offsets, int64_t n_groups,
+                                        uint8_t *row_codes, uint8_t *row_scales,
+                                        uint8_t *codes_t, uint8_t *scales_t,
+                                        int64_t *block_offsets, void *stream);
+
+/*
  * The expert layer's MXFP8 weight gradient: for every expert e,
  *   C_e[m][n] = sum over k in [32 P[e], 32 P[e+1]) of dec(a[m][k]) 2^(sa[m][k/32] - 127)
  *               dec(b[n][k]) 2^(sb[n][k/32] - 127),

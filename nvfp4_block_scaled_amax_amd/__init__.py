@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     MXQ_FMT_MXFP8_COL, MXQ_FMT_MXFP8_ROW, MXQ_FMT_MXFP8_ROWCOL, MXQ_FMT_NVFP4, MXQ_OK,
     MXQ_OUT_BF16, MXQ_OUT_F32, mxq_mxfp8_gemm, mxq_mxfp8_grouped_gemm, mxq_nvfp4_gemm,
     mxq_nvfp4_grouped_gemm, mxq_mxfp8_grouped_colwise_t, mxq_mxfp8_grouped_wgrad,
+    mxq_mxfp8_grouped_quantize_rowcol_t,
     mxq_mxfp8_quantize_ocp_floor,
     mxq_mxfp8_quantize_rowcol_t, mxq_nvfp4_quantize_per_token_approx,
     MXQError, lib, mxq_dequantize_bf16, mxq_grouped_out, mxq_grouped_quantize,

@@ -47,6 +47,7 @@ EXPORTS = (
     "mxq_mxfp8_gemm",
     "mxq_mxfp8_grouped_gemm",
     "mxq_mxfp8_grouped_colwise_t",
+    "mxq_mxfp8_grouped_quantize_rowcol_t",
     "mxq_mxfp8_grouped_wgrad",
     "mxq_nvfp4_gemm",
     "mxq_nvfp4_grouped_gemm",
@@ -97,6 +98,7 @@ def lib():
         "mxq_mxfp8_gemm": [P, P, P, P, I64, I64, I64, I, P, P],
         "mxq_mxfp8_grouped_gemm": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_mxfp8_grouped_colwise_t": [P, I64, I64, P, I64, P, P, P, P],
+        "mxq_mxfp8_grouped_quantize_rowcol_t": [P, I64, I64, P, I64, P, P, P, P, P, P],
         "mxq_mxfp8_grouped_wgrad": [P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_grouped_gemm": [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, P],
         "mxq_nvfp4_gemm": [P, P, P, I64, P, P, P, I64, I64, I64, I64, I, P, P],
@@ -255,6 +257,17 @@ def mxq_mxfp8_grouped_colwise_t(x, total_rows, cols, seg_offsets, n_groups, code
                                              n_groups, _ptr(codes_t), _ptr(scales_t),
                                              _ptr(block_offsets), _stream(stream)),
            "mxq_mxfp8_grouped_colwise_t")
+
+
+def mxq_mxfp8_grouped_quantize_rowcol_t(x, total_rows, cols, seg_offsets, n_groups, row_codes,
+                                        row_scales, codes_t, scales_t, block_offsets,
+                                        stream=None):
+    _check(lib().mxq_mxfp8_grouped_quantize_rowcol_t(_ptr(x), total_rows, cols,
+                                                     _ptr(seg_offsets), n_groups,
+                                                     _ptr(row_codes), _ptr(row_scales),
+                                                     _ptr(codes_t), _ptr(scales_t),
+                                                     _ptr(block_offsets), _stream(stream)),
+           "mxq_mxfp8_grouped_quantize_rowcol_t")
 
 
 def mxq_mxfp8_grouped_wgrad(a, a_scales, b, b_scales, block_offsets, n_groups, M, N, pitch,

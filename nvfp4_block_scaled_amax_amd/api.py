@@ -253,6 +253,25 @@ def mxfp8_grouped_colwise_t(x, seg_offsets, stream=None) -> GroupedColT:
     return out
 
 
+def mxfp8_grouped_quantize_rowcol_t(x, seg_offsets, stream=None):
+    """From one read of the expert-sorted rows x [R][cols]: the rowwise MXFP8
+    copy (codes [R][cols], scales [R][cols/32], as the grouped quantize writes
+    it) and the grouped transposed padded columnwise copy.  Returns
+    (row_codes, row_scales, GroupedColT)."""
+    x = _bf16_bits(x)
+    R, cols = x.shape
+    G = seg_offsets.numel() - 1
+    pitch = grouped_colt_pitch(R, G)
+    rc = _empty((R, cols), torch.uint8, x)
+    rs = _empty((R, cols // 32), torch.uint8, x)
+    out = GroupedColT(_empty((cols, pitch), torch.uint8, x),
+                      _empty((cols, pitch // 32), torch.uint8, x),
+                      _empty((G + 1,), torch.int64, x))
+    B.mxq_mxfp8_grouped_quantize_rowcol_t(x, R, cols, seg_offsets, G, rc, rs, out.codes_t,
+                                          out.scales_t, out.block_offsets, stream)
+    return rc, rs, out
+
+
 def mxfp8_grouped_wgrad(a: GroupedColT, b: GroupedColT, out_dtype=torch.float32,
                         stream=None) -> torch.Tensor:
     """Per-expert C_e = A_e x B_e^T contracting over each segment's rows, from

@@ -515,12 +515,13 @@ int mxq_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales, const uint
                                                    (hipStream_t)stream));
 }
 
-int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t cols,
-                                const int64_t *seg_offsets, int64_t n_groups, uint8_t *codes_t,
-                                uint8_t *scales_t, int64_t *block_offsets, void *stream)
+// Shared by the two grouped transposed entry points; rc == nullptr: the
+// columnwise copy alone.
+static int grouped_colt(const uint16_t *x, int64_t total_rows, int64_t cols,
+                        const int64_t *seg_offsets, int64_t n_groups, uint8_t *rc, uint8_t *rs,
+                        uint8_t *codes_t, uint8_t *scales_t, int64_t *block_offsets,
+                        void *stream)
 {
-    if (!x || !seg_offsets || !codes_t || !scales_t || !block_offsets)
-        return MXQ_ERR_NULL;
     if (!size_ok(total_rows, cols) || cols > MAX_MXFP8_COLS || n_groups < 1 ||
         n_groups > ((int64_t)1 << 40) || total_rows > MAX_ELEMS / 4)
         return MXQ_ERR_SIZE;
@@ -529,17 +530,43 @@ int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t c
         return MXQ_ERR_SIZE;
     if (cols % 32 != 0)
         return MXQ_ERR_SHAPE;
-    const Buf b[5] = {{x, 2 * total_rows * cols, 16, false},
-                      {seg_offsets, 8 * (n_groups + 1), 8, false},
-                      {codes_t, pitch * cols, 16, true},
-                      {scales_t, pitch / 32 * cols, 4, true},
-                      {block_offsets, 8 * (n_groups + 1), 8, true}};
-    const int st = check_bufs(b, 5);
+    const int64_t n = total_rows * cols;
+    Buf b[7] = {{x, 2 * n, 16, false},
+                {seg_offsets, 8 * (n_groups + 1), 8, false},
+                {codes_t, pitch * cols, 16, true},
+                {scales_t, pitch / 32 * cols, 4, true},
+                {block_offsets, 8 * (n_groups + 1), 8, true},
+                {rc, n, 16, true},
+                {rs, n / 32, 1, true}};
+    const int st = check_bufs(b, rc ? 7 : 5);
     if (st != MXQ_OK)
         return st;
     return launched(mxq::launch_mxfp8_grouped_colt(x, total_rows, cols, seg_offsets, n_groups,
-                                                   codes_t, scales_t, block_offsets,
+                                                   rc, rs, codes_t, scales_t, block_offsets,
                                                    (hipStream_t)stream));
+}
+
+int mxq_mxfp8_grouped_colwise_t(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                const int64_t *seg_offsets, int64_t n_groups, uint8_t *codes_t,
+                                uint8_t *scales_t, int64_t *block_offsets, void *stream)
+{
+    if (!x || !seg_offsets || !codes_t || !scales_t || !block_offsets)
+        return MXQ_ERR_NULL;
+    return grouped_colt(x, total_rows, cols, seg_offsets, n_groups, nullptr, nullptr, codes_t,
+                        scales_t, block_offsets, stream);
+}
+
+int mxq_mxfp8_grouped_quantize_rowcol_t(const uint16_t *x, int64_t total_rows, int64_t cols,
+                                        const int64_t *seg_offsets, int64_t n_groups,
+                                        uint8_t *row_codes, uint8_t *row_scales,
+                                        uint8_t *codes_t, uint8_t *scales_t,
+                                        int64_t *block_offsets, void *stream)
+{
+    if (!x || !seg_offsets || !row_codes || !row_scales || !codes_t || !scales_t ||
+        !block_offsets)
+        return MXQ_ERR_NULL;
+    return grouped_colt(x, total_rows, cols, seg_offsets, n_groups, row_codes, row_scales,
+                        codes_t, scales_t, block_offsets, stream);
 }
 
 int mxq_mxfp8_grouped_wgrad(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,

@@ -138,10 +138,12 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const ui
 // Grouped columnwise copy, transposed and padded: codes [cols][pitch] and
 // scales [cols][pitch / 32] (pitch = grouped_colt_pitch), segment e's
 // blocks from block P[e] (P [G+1], written), each segment rounded up to 128
-// rows with zero blocks.
+// rows with zero blocks; with rc != nullptr also the rowwise copy (rc
+// [rows][cols], rs [rows][cols / 32]) from the same read.
 hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int64_t cols,
-                                     const int64_t *off, int64_t n_groups, uint8_t *cct,
-                                     uint8_t *cst, int64_t *P, hipStream_t stream);
+                                     const int64_t *off, int64_t n_groups, uint8_t *rc,
+                                     uint8_t *rs, uint8_t *cct, uint8_t *cst, int64_t *P,
+                                     hipStream_t stream);
 
 // Grouped weight gradient: C_e[M][N] = A[:, 32 P[e] .. 32 P[e+1]) x
 // B[:, same]^T for every expert e, A [M][ld] and B [N][ld] in the grouped

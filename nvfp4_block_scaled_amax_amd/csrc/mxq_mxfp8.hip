@@ -506,8 +506,12 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
 // contiguous block took 288 us, while padding the pitch against channel
 // aliasing changed nothing.  Padding blocks (no rows) load from row 0, which
 // lies in the tensor, and keep nothing: zero codes and scale bytes.
-template <int WPW>
+// ROW: the rowwise copy [rows][cols] from the same read (the grouped
+// rowwise layout, stored straight from the lanes as the tile kernel does).
+template <int WPW, bool ROW>
 __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G,
+                                                                      uint8_t *__restrict__ rc,
+                                                                      uint8_t *__restrict__ rs,
                                                                       uint8_t *__restrict__ cct,
                                                                       uint8_t *__restrict__ cst)
 {
@@ -540,9 +544,12 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
         uint32_t v[8][4];
         load_tile<false>(v, G.x + (nrows > 0 ? row0 : 0) * G.cols + tcol, cols, c8, nrows, rg,
                          col_ok);
-        const TileOut o{nullptr, nullptr, sc + TILE_ROWS * w, ss + w, nullptr, LP, WPW};
-        convert_tile<false, true, false, false, false, true, false, true>(v, cols, c8, nrows, g,
-                                                                          rg, col_ok, o);
+        const int64_t r0 = nrows > 0 ? row0 : 0;     // no rowwise store when nrows is 0
+        const TileOut o{ROW ? rc + r0 * G.cols + tcol : nullptr,
+                        ROW ? rs + r0 * (G.cols / 32) + tcol / 32 : nullptr,
+                        sc + TILE_ROWS * w, ss + w, nullptr, LP, WPW};
+        convert_tile<ROW, true, false, false, false, true, false, true>(v, cols, c8, nrows, g, rg,
+                                                                        col_ok, o);
     }
     __syncthreads();
     const int t = (int)tid();
@@ -730,8 +737,9 @@ hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint
 }
 
 hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int64_t cols,
-                                     const int64_t *off, int64_t n_groups, uint8_t *cct,
-                                     uint8_t *cst, int64_t *P, hipStream_t stream)
+                                     const int64_t *off, int64_t n_groups, uint8_t *rc,
+                                     uint8_t *rs, uint8_t *cct, uint8_t *cst, int64_t *P,
+                                     hipStream_t stream)
 {
     const int64_t max_tiles = grouped_colt_pitch(total_rows, n_groups) / TILE_ROWS;
     if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
@@ -745,8 +753,12 @@ hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int6
                n_groups, nullptr, 0};
     constexpr int WPW = 8;
     const int64_t wgs = (max_tiles + WPW - 1) / WPW * G.nct;
-    hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
-                       stream, G, cct, cst);
+    if (rc)
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, true>), dim3((unsigned)wgs),
+                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
+    else
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, false>), dim3((unsigned)wgs),
+                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
     return hipGetLastError();
 }
 

@@ -152,6 +152,13 @@ def test_validation_before_any_device_call():
     assert status_of(ct, A, 64, 64, A, (1 << 40) + 1, A, A, A, 0) == mxq.MXQ_ERR_SIZE
     assert status_of(ct, A + 8, 64, 64, A, 2, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
     assert status_of(ct, A, 64, 64, A, 2, A, A + 2, A, 0) == mxq.MXQ_ERR_ALIGN
+    rt = mxq.mxq_mxfp8_grouped_quantize_rowcol_t
+    assert status_of(rt, A, 64, 64, A, 2, None, A, A, A, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(rt, A, 64, 64, A, 2, A, None, A, A, A, 0) == mxq.MXQ_ERR_NULL
+    assert status_of(rt, A, 64, 64, A, 0, A, A, A, A, A, 0) == mxq.MXQ_ERR_SIZE
+    assert status_of(rt, A, 64, 48, A, 2, A, A, A, A, A, 0) == mxq.MXQ_ERR_SHAPE
+    assert status_of(rt, A, 64, 64, A, 2, A + 8, A, A, A, A, 0) == mxq.MXQ_ERR_ALIGN
+    assert status_of(rt, A, 64, 64, A, 2, A, A, A, A + 2, A, 0) == mxq.MXQ_ERR_ALIGN
     wg = mxq.mxq_mxfp8_grouped_wgrad
     assert status_of(wg, A, A, A, A, A, 2, 64, 64, 256, 9, A, 0) == mxq.MXQ_ERR_ARG
     assert status_of(wg, A, A, A, A, None, 2, 64, 64, 256, 0, A, 0) == mxq.MXQ_ERR_NULL

@@ -111,6 +111,9 @@ def test_grouped_weight_gradient_pair(x, off, ct, cs, P, rows, cols, G, M, N, pi
     assert s in ERRORS
     s = status(mxq.mxq_mxfp8_grouped_wgrad, ct, cs, x, cs, P, G, M, N, pitch, dt, off, 0)
     assert s in ERRORS
+    s = status(mxq.mxq_mxfp8_grouped_quantize_rowcol_t, x, rows, cols, off, G, ct, cs, ct, cs,
+               P, 0)
+    assert s in ERRORS
 
 
 @SETTINGS

@@ -621,6 +621,42 @@ def test_grouped_colwise_transposed_padded(orc):
     check_grouped_colt(orc, W.mode_random(40, 64, 5), np.array([0, 40], np.int64), "one segment")
 
 
+def check_grouped_rowcolt(orc, x, off, name):
+    """mxq_mxfp8_grouped_quantize_rowcol_t: the transposed copy against
+    padded_colt and the rowwise copy against the oracle's rowwise quantize of
+    every row, byte for byte."""
+    announce(f"grouped rowwise + colwise transposed {name} R={x.shape[0]} G={off.size - 1}")
+    rc, rs, g = api.mxfp8_grouped_quantize_rowcol_t(dev(x), dev(off))
+    torch.cuda.synchronize()
+    ct, st, P = padded_colt(orc, x, off)
+    assert list(host(g.block_offsets)) == list(P)
+    n = 32 * int(P[-1])
+    assert_same(host(g.codes_t)[:, :n], ct, f"{name} codes_t")
+    assert_same(host(g.scales_t)[:, :int(P[-1])], st, f"{name} scales_t")
+    del ct, st, g
+    orow, orows = orc.mxfp8_rowwise(x)
+    assert_same(host(rc), orow, f"{name} row codes")
+    assert_same(host(rs), orows, f"{name} row scales")
+
+
+def test_grouped_rowcol_transposed_ragged(orc):
+    """Both backward copies from one read: segments of 0, 1, 31, 33, 128 and
+    200 rows (96 columns: a partial strip), boundary-mode values."""
+    sizes = [0, 1, 31, 33, 128, 200, 0, 64]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    x = W.mode_boundary(512, 96, 4)[:int(off[-1])]
+    check_grouped_rowcolt(orc, x, off, "ragged")
+    check_grouped_rowcolt(orc, W.mode_random(40, 64, 5), np.array([0, 40], np.int64),
+                          "one segment")
+
+
+def test_grouped_rowcol_transposed_config5_full(orc):
+    """Config 5's 262144 x 2048 expert-sorted rows over 128 segments: every
+    byte of both copies."""
+    x, off = W.config5()
+    check_grouped_rowcolt(orc, x, off, "config5")
+
+
 def test_grouped_weight_gradient(orc):
     """The expert layer's weight gradient dW_e = dY_e^T X_e over each segment's
     rows from two grouped transposed copies (dY [R][256], X [R][192]), every
