@@ -70,8 +70,8 @@ extern "C" {
 #endif
 
 /* Raised whenever an entry point is added or changes (2: the caller-amax
- * export variant, the copy floor, the grouped GEMMs and the grouped
- * weight-gradient pair). */
+ * export variant, the copy floor, the grouped GEMMs, the grouped
+ * weight-gradient pair and the grouped rowwise + transposed quantize). */
 #define MXQ_VERSION 2
 
 typedef enum {
