@@ -20,6 +20,7 @@
 namespace mxq {
 
 constexpr int FLOOR_THREADS = 256;
+constexpr int FLOOR_BATCH = 8;
 
 template <bool FOLD>
 __global__ void __launch_bounds__(FLOOR_THREADS)
@@ -31,11 +32,23 @@ __global__ void __launch_bounds__(FLOOR_THREADS)
         return;
     u32x4_t v;
     if constexpr (FOLD) {
+        // Eight loads in flight per thread before any is consumed (a plain
+        // loop waits for each load before issuing the next, which makes a
+        // read-heavy floor latency-bound: 4 reads per write took 9.5 us on
+        // 33.5 MB in + 9.5 MB out).
         v = __builtin_nontemporal_load(src + j);
-        for (int64_t i = 1; i < (int64_t)k; i++) {
-            const int64_t c = j + i * n_w;
-            if (c < n_r)
-                v ^= __builtin_nontemporal_load(src + c);
+        for (int64_t i0 = 1; i0 < (int64_t)k; i0 += FLOOR_BATCH) {
+            u32x4_t t[FLOOR_BATCH];
+#pragma unroll
+            for (int u = 0; u < FLOOR_BATCH; u++) {
+                const int64_t c = j + (i0 + u) * n_w;
+                t[u] = u32x4_t{0u, 0u, 0u, 0u};
+                if (i0 + u < (int64_t)k && c < n_r)
+                    t[u] = __builtin_nontemporal_load(src + c);
+            }
+#pragma unroll
+            for (int u = 0; u < FLOOR_BATCH; u++)
+                v ^= t[u];
         }
     } else {
         v = src[((uint64_t)j * k) >> 32];      // k = m: n_w <= 2^31, so j m < 2^63

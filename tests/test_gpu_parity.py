@@ -1370,7 +1370,8 @@ def test_dispatch_config5_full(orc):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n_r,n_w", [(1, 1), (300, 300), (1000, 257), (4096, 1024),
-                                     (37, 1000), (5, 4096), (70000, 20000)])
+                                     (37, 1000), (5, 4096), (70000, 20000), (1000, 100),
+                                     (5000, 300), (9000, 1000)])
 def test_copy_floor_definition(n_r, n_w):
     rng = np.random.default_rng(n_r * 7 + n_w)
     src = rng.integers(0, 256, (n_r, 16), dtype=np.uint8)
