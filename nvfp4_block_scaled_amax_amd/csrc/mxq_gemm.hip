@@ -42,6 +42,12 @@
 // 43.9 us against 46.5 us per call (8192x8192x2048: 163 us against 170 us).
 // Without copies the loop issues a matrix instruction every ~95 cycles
 // against its 64-cycle occupancy; the clock under this load is 1.6-2.0 GHz.
+// Issuing a step's eight copies one after each of its later matrix
+// instructions (rather than all after the barrier, where the matrix unit
+// waited for them) took 2048x8192x2048 from 40.3 to 37.1 us (counters
+// before: LDS busy 14 % of the time, bank conflicts 13 % of that, so the
+// copies' issue, not LDS bandwidth, was the cost); issuing them a step
+// earlier as well (four steps ahead) measured the same.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -150,18 +156,24 @@ __device__ __forceinline__ void lds_copy4(const uint8_t *base, uint32_t off, uin
 }
 
 // Codes of step s (K columns 64s .. 64s+63 of the tile's A and B rows) into
-// ring stage s % 4 at LDS byte address ring.
+// ring stage s % 4 at LDS byte address ring: the wavefront's eight copies,
+// copy c moving 64 rows of A (c even) or B (c odd).
+__device__ __forceinline__ void mxg_copy(uint32_t ring, uint32_t s, int c, const MxgOffsets &o,
+                                         const uint8_t *a, const uint8_t *b, int w)
+{
+    const uint32_t st = ring + (s & 3u) * MXG_STAGE_BYTES;
+    const uint32_t q = (uint32_t)(4 * (c >> 1) + w) * 1024u;
+    if ((c & 1) == 0)
+        lds_copy16(a + (size_t)s * MXG_BK, o.a(c >> 1), st + q);
+    else
+        lds_copy16(b + (size_t)s * MXG_BK, o.b(c >> 1), st + MXG_OP_BYTES + q);
+}
 __device__ __forceinline__ void mxg_issue_codes(uint32_t ring, uint32_t s, const MxgOffsets &o,
                                                 const uint8_t *a, const uint8_t *b, int w)
 {
-    const uint32_t st = ring + (s & 3u) * MXG_STAGE_BYTES;
-    const uint8_t *ak = a + (size_t)s * MXG_BK, *bk = b + (size_t)s * MXG_BK;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t q = (uint32_t)(4 * i + w) * 1024u;
-        lds_copy16(ak, o.a(i), st + q);
-        lds_copy16(bk, o.b(i), st + MXG_OP_BYTES + q);
-    }
+    for (int c = 0; c < 8; c++)
+        mxg_copy(ring, s, c, o, a, b, w);
 }
 // Scale group g (blocks 4g .. 4g+3 of every row: steps 2g and 2g + 1) into
 // scale buffer g % 3.
@@ -271,6 +283,42 @@ __device__ __forceinline__ void mxg_interleave()
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// One step's 16 matrix instructions with the next step's LDS reads among
+// the first six (as mxg_interleave) and the copies of step sc (and scale
+// group g when SCALES) one after each of the later ones, so that their issue
+// overlaps the matrix unit's work instead of following the barrier.
+template <bool SCALES>
+__device__ __forceinline__ void mxg_step(f32x16_t (&acc)[4][4], const MxgFrags &f, uint32_t ring,
+                                         uint32_t sc, uint32_t g, const MxgOffsets &o,
+                                         const uint8_t *a, const uint8_t *b,
+                                         const uint8_t *as_, const uint8_t *bs_, int w)
+{
+#pragma unroll
+    for (int q = 0; q < 7; q++)
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[q & 3], f.a[q >> 2], acc[q >> 2][q & 3], 0, 0, 0, (int)f.sb[q & 3], 0,
+            (int)f.sa[q >> 2]);
+#pragma unroll
+    for (int k = 0; k < 6; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // matrix
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 7; q < 16; q++) {
+        if (q < 15)
+            mxg_copy(ring, sc, q - 7, o, a, b, w);
+        else if (SCALES)
+            mxg_issue_scales(ring, g, o, as_, bs_, w);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[q & 3], f.a[q >> 2], acc[q >> 2][q & 3], 0, 0, 0, (int)f.sb[q & 3], 0,
+            (int)f.sa[q >> 2]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Write the wavefront's 128x128 quarter of the C tile from transposed
@@ -445,25 +493,18 @@ __device__ __forceinline__ void mxg_tile(uint8_t *lds, const uint8_t *__restrict
     uint32_t s = 0;
     for (; s + 4 < nsteps; s += 2) {
         // Step s (even): matrix work on f0; read step s + 1 into f1.
-        mxg_issue_codes(ring, s + 3, off, a, b, wave);
         mxg_read<1>(f1, lds, s + 1, wm, wn, r32, h);
-        mxg_mfma(acc, f0);
-        mxg_interleave();
+        mxg_step<false>(acc, f0, ring, s + 3, 0, off, a, b, as_, bs_, wave);
         mxg_sync<MXG_LOADS_ODD>();
         // Step s + 1 (odd): matrix work on f1; read step s + 2 into f0.
-        mxg_issue_codes(ring, s + 4, off, a, b, wave);
-        mxg_issue_scales(ring, (s + 4) >> 1, off, as_, bs_, wave);
         mxg_read<0>(f0, lds, s + 2, wm, wn, r32, h);
-        mxg_mfma(acc, f1);
-        mxg_interleave();
+        mxg_step<true>(acc, f1, ring, s + 4, (s + 4) >> 1, off, a, b, as_, bs_, wave);
         mxg_sync<MXG_LOADS_EVEN>();
     }
     // The last two or four steps (s = nsteps - 4 or nsteps - 2).
     if (s + 4 == nsteps) {
-        mxg_issue_codes(ring, s + 3, off, a, b, wave);
         mxg_read<1>(f1, lds, s + 1, wm, wn, r32, h);
-        mxg_mfma(acc, f0);
-        mxg_interleave();
+        mxg_step<false>(acc, f0, ring, s + 3, 0, off, a, b, as_, bs_, wave);
         mxg_sync<MXG_LOADS_ODD>();
         mxg_read<0>(f0, lds, s + 2, wm, wn, r32, h);
         mxg_mfma(acc, f1);
