@@ -902,6 +902,11 @@ PMC_CMD = ("rocprofv3 --pmc {counter} -d OUT/pmc_{tag} -o {tag} --output-format 
 STATS_CMD = ("rocprofv3 --kernel-trace --stats -d OUT/prof_bench -o bench --output-format "
              "csv -- python3 bench.py --groups act,wgt,tok,exp,grp,dsp,qdq,gemm --steps 5 "
              "--warmup 2 --no-cpu-baseline --no-configs")
+GEMM_CONFIGS = ("G_mxfp8_gemm_2048x8192x2048,G_mxfp8_gemm_8192x8192x2048,"
+                "G_nvfp4_gemm_2048x8192x2048,G_mxfp8_grouped_gemm_262144x768x2048,"
+                "G_nvfp4_grouped_gemm_262144x768x2048,G_mxfp8_grouped_wgrad_768x2048_over_262144")
+GEMM_STATS_CMD = ("rocprofv3 --kernel-trace --stats -d OUT/gemm_stats -o gemm --output-format "
+                  "csv -- python3 bench.py --config-only " + GEMM_CONFIGS)
 
 
 def kernel_short_name(name: str) -> str:
@@ -1063,8 +1068,12 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
                      floor_grid(c["bytes_in"], c["bytes_out"]) == (var, key[1])]
             owner[key] = ("floor", names)
         elif "mxq::" in key[0]:
-            names = [n for n, c in cfgs.items() if any(k.split("<")[0] == base
-                                                       for k in c["kernels"])]
+            # A config naming the kernel with its template arguments owns that
+            # instance alone; otherwise any instance of the kernel.
+            names = [n for n, c in cfgs.items() if short in c["kernels"]]
+            if not names:
+                names = [n for n, c in cfgs.items() if any(k.split("<")[0] == base
+                                                           for k in c["kernels"])]
             owner[key] = ("kernel", names)
     cmds = ["  " + pre.format(tag=tag) + SHAPE_BENCH.format(configs=configs)
             for _, pre in SHAPE_CMDS]
@@ -1141,7 +1150,8 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
     print("\n".join(out))
 
 
-def summarize_stats(stats_csv: str, out_txt: str, title: str):
+def summarize_stats(stats_csv: str, out_txt: str, title: str, cmd: str = STATS_CMD,
+                    flag: str = "--summarize-stats"):
     """Kernel statistics of a rocprofv3 --stats run as a text table."""
     import csv
     rows = []
@@ -1154,7 +1164,7 @@ def summarize_stats(stats_csv: str, out_txt: str, title: str):
     rows.sort(key=lambda t: -t[5])
     out = [title, "", "Command (run from the repository root on one MI355X, ROCm 7.2; OUT is the "
            "directory the CSVs go to):",
-           "  " + STATS_CMD, "Summary: python3 bench.py --summarize-stats <kernel_stats.csv>", "",
+           "  " + cmd, f"Summary: python3 bench.py {flag} <kernel_stats.csv>", "",
            f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share':>6}"]
     for name, calls, avg, mn, mx, pct in rows:
         out.append(f"{name[:72]:<72} {calls:>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
@@ -1200,6 +1210,9 @@ def main():
                              "BENCH_JSON"),
                     help="(no GPU) write profiles/TAG_profile.txt from the four rocprofv3 runs of "
                          "bench.py --config-only CONFIGS --copy-calibration-mib 1024")
+    ap.add_argument("--summarize-gemm-stats", metavar="KERNEL_STATS_CSV",
+                    help="(no GPU) write profiles/gemm_kernels_stats.txt from rocprofv3's "
+                         "kernel statistics of the GEMM configs")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="(no GPU) write profiles/step_all_kernels_stats.txt from rocprofv3's "
                          "kernel statistics")
@@ -1213,6 +1226,16 @@ def main():
         tag = args.summarize_shape[0]
         summarize_shape(*args.summarize_shape,
                         os.path.join(ROOT, "profiles", f"{tag}_profile.txt"))
+        return
+    if args.summarize_gemm_stats:
+        summarize_stats(args.summarize_gemm_stats,
+                        os.path.join(ROOT, "profiles", "gemm_kernels_stats.txt"),
+                        "rocprofv3 kernel statistics of the GEMM configs (each: 2 warm-up "
+                        "launches, then 5 samples of 10 back-to-back launches): dense MXFP8 2048x8192x2048 "
+                        "and 8192x8192x2048, dense NVFP4 2048x8192x2048, the grouped MXFP8 and "
+                        "NVFP4 expert layers over config 5's 262144 rows (128 experts, 768x2048 "
+                        "weights) and the grouped MXFP8 weight gradient (dW_e 768x2048).",
+                        GEMM_STATS_CMD, "--summarize-gemm-stats")
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats,
