@@ -1150,25 +1150,29 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
     print("\n".join(out))
 
 
-def summarize_stats(stats_csv: str, out_txt: str, title: str, cmd: str = STATS_CMD,
+def summarize_stats(trace_csv: str, out_txt: str, title: str, cmd: str = STATS_CMD,
                     flag: str = "--summarize-stats"):
-    """Kernel statistics of a rocprofv3 --stats run as a text table."""
-    import csv
+    """Per (kernel, grid size) statistics of a rocprofv3 kernel trace as a text
+    table: launches of one kernel on different shapes stay apart."""
+    dur = trace_durations(trace_csv)
+    total = sum(sum(v) for v in dur.values())
     rows = []
-    with open(stats_csv, newline="") as f:
-        for r in csv.DictReader(f):
-            rows.append((kernel_short_name(r["Name"]) if "mxq::" in r["Name"] else
-                         r["Name"].split("(")[0].replace("void ", ""), int(r["Calls"]),
-                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    rows.sort(key=lambda t: -t[5])
+    for (name, grid), ts in dur.items():
+        short = (kernel_short_name(name) if "mxq::" in name else
+                 name.replace("(anonymous namespace)", "{anon}").split("(")[0]
+                 .replace("void ", ""))
+        rows.append((short, grid, len(ts), sum(ts) / len(ts), min(ts), max(ts),
+                     100.0 * sum(ts) / total))
+    rows.sort(key=lambda t: -t[6])
     out = [title, "", "Command (run from the repository root on one MI355X, ROCm 7.2; OUT is the "
            "directory the CSVs go to):",
-           "  " + cmd, f"Summary: python3 bench.py {flag} <kernel_stats.csv>", "",
-           f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share':>6}"]
-    for name, calls, avg, mn, mx, pct in rows:
-        out.append(f"{name[:72]:<72} {calls:>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
-                   f"{pct:>5.1f}%")
+           "  " + cmd, f"Summary: python3 bench.py {flag} <kernel_trace.csv>", "",
+           "Device durations from the kernel trace, per kernel and grid size (work-items).", "",
+           f"{'kernel':<60} {'grid':>10} {'calls':>6} {'avg us':>10} {'min us':>10} "
+           f"{'max us':>10} {'share':>6}"]
+    for name, grid, calls, avg, mn, mx, pct in rows:
+        out.append(f"{name[:60]:<60} {grid:>10} {calls:>6} {avg:>10.2f} {mn:>10.2f} "
+                   f"{mx:>10.2f} {pct:>5.1f}%")
     with open(out_txt, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -1210,12 +1214,12 @@ def main():
                              "BENCH_JSON"),
                     help="(no GPU) write profiles/TAG_profile.txt from the four rocprofv3 runs of "
                          "bench.py --config-only CONFIGS --copy-calibration-mib 1024")
-    ap.add_argument("--summarize-gemm-stats", metavar="KERNEL_STATS_CSV",
+    ap.add_argument("--summarize-gemm-stats", metavar="KERNEL_TRACE_CSV",
                     help="(no GPU) write profiles/gemm_kernels_stats.txt from rocprofv3's "
-                         "kernel statistics of the GEMM configs")
-    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                         "kernel trace of the GEMM configs")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_TRACE_CSV",
                     help="(no GPU) write profiles/step_all_kernels_stats.txt from rocprofv3's "
-                         "kernel statistics")
+                         "kernel trace")
     args = ap.parse_args()
 
     if args.summarize_pmc:

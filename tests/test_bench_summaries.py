@@ -63,14 +63,21 @@ def test_summarize_pmc(tmp_path):
 
 
 def test_summarize_stats(tmp_path):
-    p = tmp_path / "s.csv"
-    p.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs",'
-                 '"StdDev"\n'
-                 '"mxq::dequant_nvfp4_kernel(unsigned char const*)",4,4000,1000.0,20.0,900,1100,1\n'
-                 '"void mxq::k<1>(int)",2,16000,8000.0,80.0,7000,9000,1\n')
+    """Rows per (kernel, grid): one kernel launched on two shapes gives two
+    rows; durations come from the trace's timestamps."""
+    p = tmp_path / "t.csv"
+    head = '"Kernel_Name","Grid_Size_X","Grid_Size_Y","Grid_Size_Z","Start_Timestamp","End_Timestamp"\n'
+    rows = ['"void mxq::k<1>(int)",256,1,1,0,8000\n',
+            '"void mxq::k<1>(int)",256,1,1,10000,18000\n',
+            '"void mxq::k<1>(int)",1024,1,1,20000,22000\n',
+            '"mxq::dequant_nvfp4_kernel(unsigned char const*)",64,1,1,30000,31000\n']
+    p.write_text(head + "".join(rows))
     out = tmp_path / "s.txt"
     bench.summarize_stats(str(p), str(out), "title")
     lines = out.read_text().splitlines()
-    body = [ln for ln in lines if ln.startswith(("k<1>", "dequant_nvfp4_kernel"))]
-    assert body[0].startswith("k<1>") and "8.00" in body[0] and "80.0%" in body[0]
-    assert body[1].startswith("dequant_nvfp4_kernel") and "1.00" in body[1]
+    body = [ln.split() for ln in lines if ln.startswith(("k<1>", "dequant_nvfp4_kernel"))]
+    assert [b[0] for b in body] == ["k<1>", "k<1>", "dequant_nvfp4_kernel"]
+    assert body[0][1:5] == ["256", "2", "8.00", "8.00"] and body[0][-1] == "84.2%"
+    assert body[1][1:4] == ["1024", "1", "2.00"]
+    assert body[2][1:4] == ["64", "1", "1.00"]
+
