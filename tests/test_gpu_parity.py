@@ -1546,6 +1546,45 @@ def test_grouped_malformed_offsets_stay_in_bounds():
     assert bool((cs_big[:guard] == 0x5A).all()) and bool((cs_big[-guard:] == 0x5A).all())
 
 
+def test_weight_gradient_pair_malformed_offsets_stay_in_bounds():
+    """The weight-gradient pair under malformed device offsets: overlapping
+    segments whose blocks exceed the padded capacity (P[G] past pitch / 32),
+    out-of-range and decreasing offsets, then block offsets past the pitch or
+    negative for the GEMM.  Every output is bracketed by canaries; the calls
+    complete and nothing outside the outputs changes (the bytes inside are
+    meaningless)."""
+    R, cols, G, guard = 1024, 64, 4, 4096
+    x = dev(W.mode_random(R, cols, 31))
+    pitch = api.grouped_colt_pitch(R, G)
+    fill = 0x5A
+
+    def guarded(n, dt=torch.uint8, v=fill):
+        big = torch.full((n + 2 * guard,), v, dtype=dt, device="cuda")
+        return big, big[guard:guard + n]
+
+    for off_list in ([0, R, 0, R, 0], [0, 1000, -5, 64, 10 ** 12]):
+        off = torch.tensor(off_list, dtype=torch.int64, device="cuda")
+        bufs = [guarded(cols * pitch), guarded(cols * pitch // 32), guarded(R * cols),
+                guarded(R * cols // 32), guarded(G + 1, torch.int64, -1)]
+        ct, st, rc, rs, P = (b[1] for b in bufs)
+        announce(f"weight-gradient pair malformed offsets {off_list}")
+        mxq.mxq_mxfp8_grouped_quantize_rowcol_t(x, R, cols, off, G, rc, rs, ct, st, P)
+        torch.cuda.synchronize()
+        for big, _ in bufs:
+            v = -1 if big.dtype == torch.int64 else fill
+            assert bool((big[:guard] == v).all()) and bool((big[-guard:] == v).all())
+    a = ct.view(cols, pitch)
+    sa = st.view(cols, pitch // 32)
+    bad = torch.tensor([0, 10 ** 9, -7, 3, pitch // 32], dtype=torch.int64, device="cuda")
+    cbig, c = guarded(G * cols * cols * 4, torch.uint8)
+    announce("weight gradient malformed block offsets")
+    mxq.mxq_mxfp8_grouped_wgrad(a, sa, a, sa, bad, G, cols, cols, pitch, mxq.MXQ_OUT_F32, c)
+    torch.cuda.synchronize()
+    assert bool((cbig[:guard] == fill).all()) and bool((cbig[-guard:] == fill).all())
+    cf = c.view(torch.float32).view(G, cols, cols)
+    assert bool((cf[1] == 0).all()) and bool((cf[2] == 0).all())   # empty after clamping
+
+
 def test_dispatch_malformed_maps_stay_in_bounds():
     """The index maps are device data: token_rows entries outside the output
     rows are skipped and row_tokens entries outside the tokens are clamped,
