@@ -355,7 +355,7 @@ int mxq_mxfp8_grouped_gemm(const uint8_t *a, const uint8_t *a_scales, const uint
  * scale per token, rows_per_a_scale = 1; weights with one FP32 scale per
  * tensor or expert, rows_per_b_scale = its rows): the NVFP4 format and
  * per-token activation scale paragraphs.  Each dec(code) dec(block scale) is
- * exactly a BF16 value; the sum is accumulated in fp32 by the BF16 matrix
+ * exactly an FP16 value; the sum is accumulated in fp32 by the FP16 matrix
  * instructions and the FP32 scales are applied to it as
  * fp32(fp32(sum * sa) * sb), then rounded to BF16 (nearest-even) for
  * MXQ_OUT_BF16.

@@ -7,7 +7,7 @@
 // NVFP4 RL on Blackwell" feeds; the E8M0 scale per 32 elements along K is
 // the block format of gfx950's scaled matrix instructions.  NVFP4 (further
 // down): the same tile with the E4M3 block scales applied while
-// dequantizing to BF16.  Each has a dense kernel and a grouped one (the MoE
+// dequantizing to FP16.  Each has a dense kernel and a grouped one (the MoE
 // expert layer: expert-sorted rows times each expert's weight).
 //
 // Matrix instruction.  v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32x64
@@ -630,15 +630,20 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_grouped_gemm_kernel(
 // dec(ca[m][k]) dec(ba[m][k/16]) dec(cb[n][k]) dec(bb[n][k/16]).  The
 // per-16 E4M3 block scales are not an E8M0 power of two, so the fp4 matrix
 // instructions cannot apply them; but dec(code) dec(block scale) has at most
-// 6 significant bits and lies in [2^-10, 2688], so it is exactly a BF16
-// value.  The kernel dequantizes each K step to BF16 on its way into LDS
-// (register-staged: the next step's codes and scales are loaded while the
-// current step's BF16 matrix instructions run) and applies the FP32 scales
-// in the epilogue.
+// 6 significant bits and lies in [2^-10, 2688], so it is exactly an FP16
+// value (and a BF16 one).  The kernel dequantizes each K step to FP16 on its
+// way into LDS (register-staged: the next step's codes and scales are loaded
+// while the current step's FP16 matrix instructions run) and applies the
+// FP32 scales in the epilogue.  FP16 rather than BF16 because gfx950 has a
+// packed FP16 multiply and an fp4 -> FP16 pair conversion selecting its
+// code byte: one conversion and one packed multiply per code pair, against
+// an fp4 -> f32 conversion, two multiplies and a byte permute for BF16
+// (byte-identical results, 2048x8192x2048 80 -> 77 us, 8192x8192x2048
+// 276 -> 265 us).
 //
-// BF16 instruction: v_mfma_f32_32x32x16_bf16, lane (r, h) holds 8
+// FP16 instruction: v_mfma_f32_32x32x16_f16, lane (r, h) holds 8
 // consecutive K values: chunk 2s + h (16 bytes) of the 64-element step for
-// slice s.  LDS rows are 64 BF16 = 128 bytes, swizzled as above.
+// slice s.  LDS rows are 64 FP16 = 128 bytes, swizzled as above.
 //
 // Measured (2048x8192x2048, BF16 result): the earlier form, which ran the
 // step's 64 matrix instructions and then the next step's dequantization,
@@ -646,9 +651,10 @@ __global__ void __launch_bounds__(GEMM_THREADS) mxfp8_grouped_gemm_kernel(
 // (and the transposed epilogue) 80 us (8192x8192x2048: 372 -> 287 us),
 // byte-identical.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 constexpr int NVG_BK = 64;                                       // K elements per step
-constexpr int NVG_STAGE_BYTES = 2 * GEMM_BM * NVG_BK * 2;       // A and B BF16 slices
+constexpr int NVG_STAGE_BYTES = 2 * GEMM_BM * NVG_BK * 2;       // A and B FP16 slices
 
 // Thread t's share of one step: row t of A and of B (clamped), 64 codes
 // (32 bytes) and 4 block-scale bytes each.
@@ -669,18 +675,25 @@ __device__ __forceinline__ void nv_load(NvStage &st, const uint8_t *a, const uin
     st.sb = *reinterpret_cast<const uint32_t *>(bb + rb * blk_k);
 }
 
-// 8 BF16 (one 16-byte chunk) from 4 code bytes under block scale value d:
-// dec(c) d is exact in f32 and has at most 8 significant bits, so its BF16
-// is the upper half of its f32 bits.
-__device__ __forceinline__ u32x4_t nv_chunk_bf16(uint32_t codes, float d)
+// Code pair (byte J of codes) times d2 = {d, d}: the conversion is exact
+// (E2M1 values are FP16 values) and so is the product (at most 6
+// significant bits, within FP16's normal range).  Low half: the low nibble.
+template <int J>
+__device__ __forceinline__ uint32_t nv_pair_f16(uint32_t codes, half2_t d2)
 {
-    u32x4_t o;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const float2_t v = e2m1_values((codes >> (8 * j)) & 0xFFu);
-        o[j] = __builtin_amdgcn_perm(f2u(v[1] * d), f2u(v[0] * d), 0x07060302u);
-    }
-    return o;
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, J) * d2);
+}
+// 8 FP16 (one 16-byte chunk) from 4 code bytes under block scale d.
+__device__ __forceinline__ u32x4_t nv_chunk_f16(uint32_t codes, half2_t d2)
+{
+    return u32x4_t{nv_pair_f16<0>(codes, d2), nv_pair_f16<1>(codes, d2),
+                   nv_pair_f16<2>(codes, d2), nv_pair_f16<3>(codes, d2)};
+}
+__device__ __forceinline__ half2_t nv_scale_f16(uint32_t byte)
+{
+    const _Float16 d = (_Float16)e4m3_value(byte);      // exact: E4M3 values are FP16 values
+    return half2_t{d, d};
 }
 
 __device__ __forceinline__ void nv_store_row(u32x4_t *tile, int r, const u32x4_t (&c)[2],
@@ -688,8 +701,8 @@ __device__ __forceinline__ void nv_store_row(u32x4_t *tile, int r, const u32x4_t
 {
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const float d = e4m3_value((scales >> (8 * (j >> 1))) & 0xFFu);
-        tile[swz(r, j)] = nv_chunk_bf16(c[j >> 2][j & 3], d);
+        tile[swz(r, j)] = nv_chunk_f16(c[j >> 2][j & 3],
+                                       nv_scale_f16((scales >> (8 * (j >> 1))) & 0xFFu));
     }
 }
 
@@ -704,14 +717,14 @@ __device__ __forceinline__ u32x4_t *nvg_tile_b(uint8_t *lds, int buf)
 
 // Fragments of slice sl (16 K values) for the wavefront's 4 row blocks of A
 // and of B.
-__device__ __forceinline__ void nvg_frags(bf16x8_t (&fa)[4], bf16x8_t (&fb)[4],
+__device__ __forceinline__ void nvg_frags(f16x8_t (&fa)[4], f16x8_t (&fb)[4],
                                           const u32x4_t *ta, const u32x4_t *tb, int sl, int wm,
                                           int wn, int r32, int h)
 {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        fa[i] = __builtin_bit_cast(bf16x8_t, ta[swz(128 * wm + 32 * i + r32, 2 * sl + h)]);
-        fb[i] = __builtin_bit_cast(bf16x8_t, tb[swz(128 * wn + 32 * i + r32, 2 * sl + h)]);
+        fa[i] = __builtin_bit_cast(f16x8_t, ta[swz(128 * wm + 32 * i + r32, 2 * sl + h)]);
+        fb[i] = __builtin_bit_cast(f16x8_t, tb[swz(128 * wn + 32 * i + r32, 2 * sl + h)]);
     }
 }
 // One K step: the 64 matrix instructions on LDS stage buf (B is their
@@ -729,7 +742,7 @@ __device__ __forceinline__ void nvg_step(f32x16_t (&acc)[4][4], uint8_t *lds, in
                                          const NvStage &nx, int t, int wm, int wn, int r32, int h)
 {
     const u32x4_t *ta = nvg_tile_a(lds, buf), *tb = nvg_tile_b(lds, buf);
-    bf16x8_t fa[2][4], fb[2][4];
+    f16x8_t fa[2][4], fb[2][4];
     nvg_frags(fa[0], fb[0], ta, tb, 0, wm, wn, r32, h);
 #pragma unroll
     for (int sl = 0; sl < 4; sl++) {
@@ -740,15 +753,17 @@ __device__ __forceinline__ void nvg_step(f32x16_t (&acc)[4][4], uint8_t *lds, in
             const int u = 4 * sl + i, j8 = u & 7;
             const bool isb = u >= 8;
             const uint32_t codes = (isb ? nx.cb : nx.ca)[j8 >> 2][j8 & 3];
-            const float d = e4m3_value(((isb ? nx.sb : nx.sa) >> (8 * (j8 >> 1))) & 0xFFu);
+            const half2_t d2 = nv_scale_f16(((isb ? nx.sb : nx.sa) >> (8 * (j8 >> 1))) & 0xFFu);
             u32x4_t o;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[sl & 1][j], fa[sl & 1][i],
-                                                                    acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[sl & 1][j], fa[sl & 1][i],
+                                                                   acc[i][j], 0, 0, 0);
                 if constexpr (CONVERT) {
-                    const float2_t v = e2m1_values((codes >> (8 * j)) & 0xFFu);
-                    o[j] = __builtin_amdgcn_perm(f2u(v[1] * d), f2u(v[0] * d), 0x07060302u);
+                    o[j] = j == 0 ? nv_pair_f16<0>(codes, d2)
+                         : j == 1 ? nv_pair_f16<1>(codes, d2)
+                         : j == 2 ? nv_pair_f16<2>(codes, d2)
+                                  : nv_pair_f16<3>(codes, d2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
