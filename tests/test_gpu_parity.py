@@ -1127,7 +1127,7 @@ def check_nvfp4_gemm(orc, qa, qb, rows_per_b, name, row_sample=None, rel=0.0):
     """qa = (codes, block scales, fp32 scales per row), qb = (codes, block
     scales, fp32 scales per rows_per_b rows), both made by the oracle; C on
     the GPU in fp32 and BF16 against the oracle's exact product, to
-    (rel + K 2^-24 + 2^-23) sum|a b| |sa sb| (fp32 accumulation -- the BF16
+    (rel + K 2^-24 + 2^-23) sum|a b| |sa sb| (fp32 accumulation -- the FP16
     matrix instructions accumulate at full fp32 precision, measured at most
     2^-23.8 sum|a b| -- and the two FP32 scale multiplications), plus half a
     BF16 step for the BF16 result."""
