@@ -226,7 +226,7 @@ def build_grp(torch, E, W, legs, dev, empty):
     nv_out = n // 2 + n // 16 + 4 * R
     legs.append(Leg("grouped_mxfp8_rowcol",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_MXFP8_ROWCOL, xg, R, K, off, G, g8),
-                    2 * n + 8 * (G + 1), mx_out, n, ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8, false>"],
+                    2 * n + 8 * (G + 1), mx_out, n, ["mxfp8_tile_kernel<true, true, true, 8, false, true>"],
                     f"grouped MXFP8 row+col {R}x{K}, {G} segments"))
     legs.append(Leg("grouped_nvfp4",
                     lambda: E.mxq_grouped_quantize(E.MXQ_FMT_NVFP4, xg, R, K, off, G, g4),
@@ -787,7 +787,7 @@ def build_dsp(torch, E, W, legs, dev, empty):
                                                             None, rt, R, off, G, g8),
                     2 * T * K + 8 * R + 8 * (G + 1),
                     2 * n + n // 32 + col_scale_rows * K + 8 * (G + 1), n,
-                    ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8, true>"],
+                    ["mxfp8_tile_kernel<true, true, true, 8, true, true>"],
                     f"dispatch + grouped MXFP8 row+col, {T} tokens -> {R}x{K}, {G} segments"))
     legs.append(Leg("dispatch_nvfp4",
                     lambda: E.mxq_grouped_quantize_dispatch(E.MXQ_FMT_NVFP4, tok, T, K, top_k, tr,
@@ -833,7 +833,7 @@ def wgrad_timings(torch, E, W, dev, empty, only=None):
         fl = copy_floor(torch, E, rb, wb, 1, False, 10, 2)
         k, v = cfg_record("C5_colt_mxfp8", f"grouped MXFP8 columnwise, transposed and padded to "
                           f"128 rows per segment, {R}x{K}, {G} segments", ms, rb + wb, R * K, 1,
-                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel<8, false>"], None,
+                          ["mxfp8_grouped_colt_kernel<8, false, true>"], None,
                           fl, (rb, wb))
         res[k] = v
     if sel("C5_rowcolt_mxfp8"):
@@ -850,7 +850,7 @@ def wgrad_timings(torch, E, W, dev, empty, only=None):
         k, v = cfg_record("C5_rowcolt_mxfp8", f"grouped MXFP8 rowwise copy plus the columnwise "
                           f"copy transposed and padded, one read, {R}x{K}, {G} segments", ms,
                           rb + wb, R * K, 1,
-                          ["grouped_prefix_kernel", "mxfp8_grouped_colt_kernel<8, true>"], None,
+                          ["mxfp8_grouped_colt_kernel<8, true, true>"], None,
                           fl, (rb, wb))
         res[k] = v
         del rc, rs
@@ -1363,7 +1363,8 @@ def main():
 
     leg_info = {l.name: info(l) for l in legs}
     # The dominant kernel: the longest leg that is one launch of one kernel
-    # (the grouped MXFP8 leg also runs the ~4 us segment prefix kernel first).
+    # (with up to 256 segments the grouped kernels form their segment prefix
+    # themselves; above that a ~4 us prefix launch precedes them).
     # The export legs (four kernels, two reads of the weights) and the
     # three-launch export dequant are reported per leg but are not one launch.
     single = [l for l in legs if l.name not in ("nvfp4_export_gateup", "nvfp4_export_down",

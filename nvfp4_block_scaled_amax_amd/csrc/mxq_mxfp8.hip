@@ -369,6 +369,51 @@ __device__ __forceinline__ int64_t tile_segment(const int64_t *__restrict__ P, i
     return lo;
 }
 
+// Up to SCAN_MAX_GROUPS segments, a grouped kernel forms the block prefix
+// P[0..G] itself instead of a separate one-workgroup launch before it (4.4 us
+// plus the launch gap for 128 segments): wavefront 0 of every workgroup
+// scans the offsets, 64 segments at a time, into LDS, and workgroup 0 also
+// stores P for the caller.  P[e] = sum over f < e of ceil(n_f / 32) rounded
+// up to a multiple of pad, each segment clamped as in segment_rows: the same
+// values the prefix kernel writes.
+constexpr int64_t SCAN_MAX_GROUPS = 256;
+__device__ __forceinline__ void wave_block_prefix(const int64_t *__restrict__ off, int64_t G,
+                                                  int64_t total_rows, int64_t pad,
+                                                  int64_t *__restrict__ Ps,
+                                                  int64_t *__restrict__ P_out)
+{
+    const int lane = (int)lane_id();
+    int64_t before = 0;
+    for (int64_t base = 0; base < G; base += 64) {
+        const int64_t e = base + lane;
+        int64_t n = 0;
+        if (e < G) {
+            int64_t lo, hi;
+            segment_rows(off, e, total_rows, &lo, &hi);
+            n = (hi - lo + 31) >> 5;
+            n = (n + pad - 1) / pad * pad;
+        }
+        int64_t inc = n;                                // inclusive prefix over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t v = __shfl_up(inc, d);
+            if (lane >= d)
+                inc += v;
+        }
+        if (e < G) {
+            Ps[e] = before + inc - n;
+            if (P_out)
+                P_out[e] = before + inc - n;
+        }
+        before += __shfl(inc, 63);
+    }
+    if (lane == 0) {
+        Ps[G] = before;
+        if (P_out)
+            P_out[G] = before;
+    }
+}
+
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
@@ -450,12 +495,22 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
     }
 }
 
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
+// SCAN (grouped, G <= SCAN_MAX_GROUPS): the block prefix formed in LDS
+// (wave_block_prefix; workgroup 0 stores it to P_out).
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool SCAN = false>
 __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_t *__restrict__ rc,
                                                          uint8_t *__restrict__ rs,
                                                          uint8_t *__restrict__ cc,
-                                                         uint8_t *__restrict__ cs)
+                                                         uint8_t *__restrict__ cs,
+                                                         int64_t *__restrict__ P_out)
 {
+    if constexpr (SCAN) {
+        __shared__ int64_t Ps[SCAN_MAX_GROUPS + 1];
+        if (wave_in_group() == 0)
+            wave_block_prefix(G.off, G.n_groups, G.rows, 1, Ps, wg_id() == 0 ? P_out : nullptr);
+        __syncthreads();
+        G.P = Ps;
+    }
     tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr);
 }
 
@@ -508,13 +563,22 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
 // lies in the tensor, and keep nothing: zero codes and scale bytes.
 // ROW: the rowwise copy [rows][cols] from the same read (the grouped
 // rowwise layout, stored straight from the lanes as the tile kernel does).
-template <int WPW, bool ROW>
+// SCAN: the block prefix formed in LDS, as in mxfp8_tile_kernel.
+template <int WPW, bool ROW, bool SCAN>
 __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G,
                                                                       uint8_t *__restrict__ rc,
                                                                       uint8_t *__restrict__ rs,
                                                                       uint8_t *__restrict__ cct,
-                                                                      uint8_t *__restrict__ cst)
+                                                                      uint8_t *__restrict__ cst,
+                                                                      int64_t *__restrict__ P_out)
 {
+    if constexpr (SCAN) {
+        __shared__ int64_t Ps[SCAN_MAX_GROUPS + 1];
+        if (wave_in_group() == 0)
+            wave_block_prefix(G.off, G.n_groups, G.rows, 4, Ps, wg_id() == 0 ? P_out : nullptr);
+        __syncthreads();
+        G.P = Ps;
+    }
     constexpr int LP = TILE_ROWS * WPW + 4;          // bytes per staged column (bank spread)
     constexpr int PIECES = 2 * WPW;                   // 16-byte pieces per staged column
     __shared__ __attribute__((aligned(16))) uint8_t sc[TILE_COLS * LP];
@@ -620,37 +684,43 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // workgroups leave CUs idle (8192 x 2048: 20.5 us with 8, 17.3 us with 4).
 constexpr int64_t LARGE_LAUNCH_WAVES = 32768;
 
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool SCAN>
 static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
-                             uint8_t *cc, uint8_t *cs, hipStream_t stream)
+                             uint8_t *cc, uint8_t *cs, int64_t *P_out, hipStream_t stream)
 {
     const int64_t wgs = (waves + WPW - 1) / WPW;
     if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER>), dim3((unsigned)wgs),
-                       dim3(64 * WPW), 0, stream, G, rc, rs, cc, cs);
+    hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER, SCAN>),
+                       dim3((unsigned)wgs), dim3(64 * WPW), 0, stream, G, rc, rs, cc, cs, P_out);
     return hipGetLastError();
 }
 
-template <bool ROW, bool COL, bool GROUPED, bool GATHER>
+template <bool ROW, bool COL, bool GROUPED, bool GATHER, bool SCAN>
 static hipError_t launch_one(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc,
-                             uint8_t *rs, uint8_t *cc, uint8_t *cs, hipStream_t stream)
+                             uint8_t *rs, uint8_t *cc, uint8_t *cs, int64_t *P_out,
+                             hipStream_t stream)
 {
     const int64_t waves = tiles_per_strip * G.nct;
     if (waves >= LARGE_LAUNCH_WAVES)
-        return launch_wpw<ROW, COL, GROUPED, 8, GATHER>(G, waves, rc, rs, cc, cs, stream);
-    return launch_wpw<ROW, COL, GROUPED, 4, GATHER>(G, waves, rc, rs, cc, cs, stream);
+        return launch_wpw<ROW, COL, GROUPED, 8, GATHER, SCAN>(G, waves, rc, rs, cc, cs, P_out,
+                                                              stream);
+    return launch_wpw<ROW, COL, GROUPED, 4, GATHER, SCAN>(G, waves, rc, rs, cc, cs, P_out,
+                                                          stream);
 }
 
-template <bool GROUPED, bool GATHER>
+template <bool GROUPED, bool GATHER, bool SCAN = false>
 static hipError_t launch(const Geometry &G, int64_t tiles_per_strip, uint8_t *rc, uint8_t *rs,
-                         uint8_t *cc, uint8_t *cs, hipStream_t stream)
+                         uint8_t *cc, uint8_t *cs, int64_t *P_out, hipStream_t stream)
 {
     if (rc && cc)
-        return launch_one<true, true, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+        return launch_one<true, true, GROUPED, GATHER, SCAN>(G, tiles_per_strip, rc, rs, cc, cs,
+                                                             P_out, stream);
     if (rc)
-        return launch_one<true, false, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
-    return launch_one<false, true, GROUPED, GATHER>(G, tiles_per_strip, rc, rs, cc, cs, stream);
+        return launch_one<true, false, GROUPED, GATHER, SCAN>(G, tiles_per_strip, rc, rs, cc, cs,
+                                                              P_out, stream);
+    return launch_one<false, true, GROUPED, GATHER, SCAN>(G, tiles_per_strip, rc, rs, cc, cs,
+                                                          P_out, stream);
 }
 
 hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
@@ -661,8 +731,8 @@ hipError_t launch_mxfp8_dense(const uint16_t *x, int64_t rows, int64_t cols, uin
                row_tokens, n_tokens};
     const int64_t tiles = (rows + TILE_ROWS - 1) / TILE_ROWS;
     if (row_tokens)
-        return launch<false, true>(G, tiles, rc, rs, cc, cs, stream);
-    return launch<false, false>(G, tiles, rc, rs, cc, cs, stream);
+        return launch<false, true>(G, tiles, rc, rs, cc, cs, nullptr, stream);
+    return launch<false, false>(G, tiles, rc, rs, cc, cs, nullptr, stream);
 }
 
 template <bool ROW, int WPW>
@@ -744,21 +814,30 @@ hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int6
     const int64_t max_tiles = grouped_colt_pitch(total_rows, n_groups) / TILE_ROWS;
     if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
-                       total_rows, (int64_t)4, P);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
+    const bool scan = n_groups <= SCAN_MAX_GROUPS;
+    if (!scan) {
+        hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
+                           total_rows, (int64_t)4, P);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
                n_groups, nullptr, 0};
     constexpr int WPW = 8;
-    const int64_t wgs = (max_tiles + WPW - 1) / WPW * G.nct;
-    if (rc)
-        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, true>), dim3((unsigned)wgs),
-                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
+    const dim3 grid((unsigned)((max_tiles + WPW - 1) / WPW * G.nct)), block(64 * WPW);
+    if (scan && rc)
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, true, true>), grid, block, 0, stream,
+                           G, rc, rs, cct, cst, P);
+    else if (scan)
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, false, true>), grid, block, 0, stream,
+                           G, rc, rs, cct, cst, P);
+    else if (rc)
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, true, false>), grid, block, 0, stream,
+                           G, rc, rs, cct, cst, nullptr);
     else
-        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, false>), dim3((unsigned)wgs),
-                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
+        hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, false, false>), grid, block, 0,
+                           stream, G, rc, rs, cct, cst, nullptr);
     return hipGetLastError();
 }
 
@@ -770,16 +849,21 @@ hipError_t launch_mxfp8_grouped(const uint16_t *x, int64_t total_rows, int64_t c
     const int64_t max_tiles = total_rows / TILE_ROWS + n_groups;
     if (mxfp8_tiles(max_tiles, cols) > MAX_MXFP8_TILES)     // checked by the caller
         return hipErrorInvalidValue;
+    Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
+               n_groups, row_tokens, n_tokens};
+    if (n_groups <= SCAN_MAX_GROUPS) {
+        if (row_tokens)
+            return launch<true, true, true>(G, max_tiles, rc, rs, cc, cs, P, stream);
+        return launch<true, false, true>(G, max_tiles, rc, rs, cc, cs, P, stream);
+    }
     hipLaunchKernelGGL(grouped_prefix_kernel, dim3(1), dim3(256), 0, stream, off, n_groups,
                        total_rows, (int64_t)1, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
-               n_groups, row_tokens, n_tokens};
     if (row_tokens)
-        return launch<true, true>(G, max_tiles, rc, rs, cc, cs, stream);
-    return launch<true, false>(G, max_tiles, rc, rs, cc, cs, stream);
+        return launch<true, true>(G, max_tiles, rc, rs, cc, cs, nullptr, stream);
+    return launch<true, false>(G, max_tiles, rc, rs, cc, cs, nullptr, stream);
 }
 
 }  // namespace mxq

@@ -718,6 +718,18 @@ def test_grouped_ragged_stress(orc):
     check_grouped(orc, x, off, "ragged stress")
 
 
+@pytest.mark.parametrize("G", [65, 256, 257, 300])
+def test_grouped_many_segments(orc, G):
+    """Segment counts across the in-kernel prefix limit (256 segments; above
+    it a prefix launch precedes the kernels) and across the 64-segment scan
+    chunks: every segment of both grouped outputs, and both copies of the
+    grouped transposed call."""
+    off = W.ragged_offsets(8192, G, seed=G, forced=(0, 1, 31, 32, 33, 700))
+    x = W.student_t_activations(int(off[-1]), 128, G + 1)
+    check_grouped(orc, x, off, f"{G} segments")
+    check_grouped_rowcolt(orc, x, off, f"{G} segments")
+
+
 def test_grouped_small_edge(orc):
     off = np.array([0, 0, 1, 1, 33, 65, 65, 96, 97], np.int64)
     x = W.mode_boundary(128, 64, 3)[:97]
@@ -1623,6 +1635,14 @@ def test_dispatch_malformed_maps_stay_in_bounds():
     torch.cuda.synchronize()
     for big in (rc_big, cs_big):
         assert bool((big[:guard] == 0x5A).all()) and bool((big[-guard:] == 0x5A).all())
+
+
+def test_dispatch_many_experts(orc):
+    """300 experts (past the in-kernel prefix limit of 256 segments): every
+    segment and row of both dispatch outputs."""
+    row_tokens, token_rows, off = W.dispatch_maps(600, 300, 3, seed=23)
+    tokens = W.student_t_activations(600, 256, 24)
+    check_dispatch(orc, tokens, row_tokens, token_rows, off, "300 experts")
 
 
 def test_dispatch_mxfp8_single_copy(orc):
