@@ -787,7 +787,7 @@ def build_dsp(torch, E, W, legs, dev, empty):
                                                             None, rt, R, off, G, g8),
                     2 * T * K + 8 * R + 8 * (G + 1),
                     2 * n + n // 32 + col_scale_rows * K + 8 * (G + 1), n,
-                    ["mxfp8_tile_kernel<true, true, true, 8, true, true>"],
+                    ["grouped_prefix_kernel", "mxfp8_tile_kernel<true, true, true, 8, true, false>"],
                     f"dispatch + grouped MXFP8 row+col, {T} tokens -> {R}x{K}, {G} segments"))
     legs.append(Leg("dispatch_nvfp4",
                     lambda: E.mxq_grouped_quantize_dispatch(E.MXQ_FMT_NVFP4, tok, T, K, top_k, tr,
