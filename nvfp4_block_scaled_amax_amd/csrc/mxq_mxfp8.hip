@@ -554,12 +554,12 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
 // and writes each column's 32 WPW bytes as whole lines of codes_t.  Written
 // straight from the lanes, each column's bytes were 32-byte pieces of four
 // lines (1.52 ms on 262144 x 2048, 17 % of the copy floor; staged, 4 waves:
-// 330 us, 8 waves: 324 us, 16 waves: 325 us).  Consecutive workgroups take
-// consecutive q of one strip, so a column's row fills in order (320 us;
-// strip-fast 324 us).  What remains over the copy floor (255 us) is the
-// scatter itself: the same kernel writing each workgroup's 16 KB to one
-// contiguous block took 288 us, while padding the pitch against channel
-// aliasing changed nothing.  Padding blocks (no rows) load from row 0, which
+// 330 us, 8 waves: 324 us, 16 waves: 325 us).  The workgroup order (below)
+// keeps each XCD on a contiguous range of (q, strip), strips fastest: 302 us.
+// Most of what remains over the copy floor (255 us) is the scatter itself:
+// the same kernel writing each workgroup's 16 KB to one contiguous block
+// took 288 us, while padding the pitch against channel aliasing changed
+// nothing.  Padding blocks (no rows) load from row 0, which
 // lies in the tensor, and keep nothing: zero codes and scale bytes.
 // ROW: the rowwise copy [rows][cols] from the same read (the grouped
 // rowwise layout, stored straight from the lanes as the tile kernel does).
@@ -585,15 +585,21 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
     __shared__ __attribute__((aligned(16))) uint8_t ss[TILE_COLS * WPW];
     const int lane = (int)lane_id(), w = (int)wave_in_group();
     const int g = lane & 15, rg = lane >> 4;
-    const int64_t wg = wg_id();
     const int64_t ngroups = (G.max_tiles + WPW - 1) / WPW;
-    // ROW: strips fastest, so that a row's scale bytes (one 4-byte piece
-    // per strip, 16 strips to a 64-byte line at 2048 columns) are written
-    // close together in time; in column-run order those lines were
-    // assembled from workgroups far apart and cost about 4x their bytes in
-    // HBM writes (262144 x 2048: 465 -> 435 us).
-    const int64_t strip = ROW ? wg % G.nct : wg / ngroups;
-    const int64_t T0 = WPW * (ROW ? wg / G.nct : wg % ngroups);
+    const int64_t total = ngroups * G.nct, per_xcd = (total + 7) / 8;
+    // Workgroups are dealt round-robin to the 8 XCDs; position L runs on the
+    // XCD that owns the L-range it falls in, strips fastest inside it.  So
+    // the small pieces of one line -- a row's scale bytes (4 bytes per
+    // strip) and a column's transposed scale bytes (8 bytes per workgroup)
+    // -- come from neighbouring workgroups on one XCD and meet in its L2;
+    // spread over XCDs, each piece reached HBM as a separate 32-byte write.
+    // 262144 x 2048: 465 -> 415 us with the rowwise copy, 320 -> 302 us
+    // without, byte-identical.
+    const int64_t hw = wg_id();
+    const int64_t wg = (hw & 7) * per_xcd + (hw >> 3);
+    if (wg >= total)
+        return;
+    const int64_t strip = wg % G.nct, T0 = WPW * (wg / G.nct);
     int64_t ntiles = G.P[G.n_groups];
     if (ntiles > G.max_tiles)
         ntiles = G.max_tiles;
@@ -831,7 +837,7 @@ hipError_t launch_mxfp8_grouped_colt(const uint16_t *x, int64_t total_rows, int6
     Geometry G{x, total_rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, max_tiles, off, P,
                n_groups, nullptr, 0};
     constexpr int WPW = 8;
-    const dim3 grid((unsigned)((max_tiles + WPW - 1) / WPW * G.nct)), block(64 * WPW);
+    const dim3 grid((unsigned)(((max_tiles + WPW - 1) / WPW * G.nct + 7) / 8 * 8)), block(64 * WPW);
     if (scan && rc)
         hipLaunchKernelGGL((mxfp8_grouped_colt_kernel<WPW, true, true>), grid, block, 0, stream,
                            G, rc, rs, cct, cst, P);
