@@ -421,12 +421,13 @@ template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool 
           bool COLT = false>
 __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict__ rc,
                                           uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
-                                          uint8_t *__restrict__ cs, uint16_t *__restrict__ dq)
+                                          uint8_t *__restrict__ cs, uint16_t *__restrict__ dq,
+                                          int64_t wg = -1)
 {
     constexpr bool LATE = ROW && COL && !DQ && !OCP && !COLT && WPW == 4;
     const int lane = (int)lane_id();
     const int g = lane & 15, rg = lane >> 4;
-    const int64_t wave = (int64_t)wg_id() * WPW + wave_in_group();
+    const int64_t wave = (wg < 0 ? (int64_t)wg_id() : wg) * WPW + wave_in_group();
     const int64_t strip = wave % G.nct, T = wave / G.nct;
     Tile t;
     t.srow = T;
@@ -511,7 +512,21 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_
         __syncthreads();
         G.P = Ps;
     }
-    tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr);
+    if constexpr (GATHER) {
+        // Dispatch: workgroups are dealt round-robin to the 8 XCDs; position
+        // L runs on the XCD that owns the L-range it falls in, so one XCD
+        // visits a contiguous window of tile positions and a token's copies
+        // in several segments are read by one XCD (311 -> 306.5 us on 32768
+        // tokens routed top-8 into 262144 x 2048; the window is larger than
+        // one L2, so most repeats still come from the memory-side cache).
+        const int64_t total = (int64_t)__builtin_amdgcn_readfirstlane(
+            (int)(gridDim.x)), per_xcd = total / 8;           // grid is a multiple of 8
+        const int64_t hw = wg_id();
+        tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr,
+                                                         (hw & 7) * per_xcd + (hw >> 3));
+    } else {
+        tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr);
+    }
 }
 
 // Rowwise quantize + BF16 dequant of the rowwise copy in one pass; ROW =
@@ -700,7 +715,7 @@ template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool SCAN>
 static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
                              uint8_t *cc, uint8_t *cs, int64_t *P_out, hipStream_t stream)
 {
-    const int64_t wgs = (waves + WPW - 1) / WPW;
+    const int64_t wgs = GATHER ? ((waves + WPW - 1) / WPW + 7) / 8 * 8 : (waves + WPW - 1) / WPW;
     if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER, SCAN>),
