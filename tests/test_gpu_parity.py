@@ -1437,6 +1437,48 @@ def test_errors_leave_outputs_untouched():
     assert not bool((rs == 0xA5).all())
 
 
+def test_errors_weight_gradient_pair_leave_outputs_untouched():
+    """Rejected calls of the grouped transposed quantize and of the grouped
+    weight-gradient GEMM (aliased outputs, host memory, misalignment, bad
+    shape) launch nothing: canary-filled outputs keep every byte."""
+    R, cols, G = 96, 64, 2
+    x = dev(W.mode_random(R, cols, 33))
+    off = torch.tensor([0, 40, R], dtype=torch.int64, device="cuda")
+    pitch = api.grouped_colt_pitch(R, G)
+    fill = lambda n, dt=torch.uint8: torch.full((n,), 0xA5 if dt == torch.uint8 else -7,
+                                                dtype=dt, device="cuda")
+    rc, rs, ct, st, P = (fill(R * cols), fill(R * cols // 32), fill(cols * pitch),
+                         fill(cols * pitch // 32), fill(G + 1, torch.int64))
+    host_buf = np.zeros(cols * pitch // 32, np.uint8)
+    f = mxq.mxq_mxfp8_grouped_quantize_rowcol_t
+    announce("error paths: weight-gradient pair")
+    cases = [
+        (mxq.MXQ_ERR_ALIAS, (x, R, cols, off, G, ct, rs, ct, st, P)),
+        (mxq.MXQ_ERR_DEVICE, (x, R, cols, off, G, rc, rs, ct, host_buf.ctypes.data, P)),
+        (mxq.MXQ_ERR_ALIGN, (x, R, cols, off, G, rc, rs, ct, st.data_ptr() + 2, P)),
+        (mxq.MXQ_ERR_SHAPE, (x, R, cols - 16, off, G, rc, rs, ct, st, P)),
+    ]
+    for status, args in cases:
+        with pytest.raises(mxq.MXQError) as ei:
+            f(*args)
+        assert ei.value.status == status, (status, ei.value)
+    c = torch.full((G * cols * cols,), -7.0, dtype=torch.float32, device="cuda")
+    a, sa = ct.view(cols, pitch), st.view(cols, pitch // 32)
+    wcases = [
+        (mxq.MXQ_ERR_ALIAS, (a, sa, c, sa, P, G, cols, cols, pitch, mxq.MXQ_OUT_F32, c)),
+        (mxq.MXQ_ERR_SHAPE, (a, sa, a, sa, P, G, cols, cols, pitch - 64, mxq.MXQ_OUT_F32, c)),
+        (mxq.MXQ_ERR_ARG, (a, sa, a, sa, P, G, cols, cols, pitch, 7, c)),
+    ]
+    for status, args in wcases:
+        with pytest.raises(mxq.MXQError) as ei:
+            mxq.mxq_mxfp8_grouped_wgrad(*args)
+        assert ei.value.status == status, (status, ei.value)
+    torch.cuda.synchronize()
+    for t in (rc, rs, ct, st):
+        assert bool((t == 0xA5).all())
+    assert bool((P == -7).all()) and bool((c == -7.0).all())
+
+
 def test_errors_buffer_too_small():
     """An array that ends before the call's extent is rejected when the array is
     its own allocation (hipMalloc).  Inside a caching-allocator segment only the
