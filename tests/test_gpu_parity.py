@@ -175,6 +175,56 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(y2, ey), f"replay {rep}: dequant"
 
 
+
+def test_graph_capture_grouped_backward_pair():
+    """The expert layer's backward operands and weight gradient captured in one
+    HIP graph: the grouped rowwise + transposed quantize of dY and of X (the
+    segment prefix formed inside the kernels) and the grouped weight-gradient
+    GEMM.  Every replay, with new inputs copied in and eager calls between
+    replays, gives the eager bytes."""
+    sizes = [0, 1, 31, 33, 128, 200, 0, 64]
+    off = dev(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64))
+    R = int(sum(sizes))
+    srcs = [(dev(W.student_t_activations(R, 256, 51 + k)), dev(W.mode_random(R, 192, 61 + k)))
+            for k in range(2)]
+    dy, x = torch.empty_like(srcs[0][0]), torch.empty_like(srcs[0][1])
+    dy.copy_(srcs[0][0])
+    x.copy_(srcs[0][1])
+    torch.cuda.synchronize()
+
+    def run(a, b):
+        ra = api.mxfp8_grouped_quantize_rowcol_t(a, off)
+        rb = api.mxfp8_grouped_quantize_rowcol_t(b, off)
+        c = api.mxfp8_grouped_wgrad(ra[2], rb[2], out_dtype=torch.bfloat16)
+        return ra, rb, c
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm-up outside the capture
+        run(dy, x)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        got = run(dy, x)
+    for rep in range(4):
+        announce(f"graph replay (grouped backward pair) {rep}")
+        sa, sb = srcs[rep % 2]
+        dy.copy_(sa)
+        x.copy_(sb)
+        g.replay()
+        torch.cuda.synchronize()
+        want = run(sa, sb)
+        torch.cuda.synchronize()
+        for gr, wr in zip(got[:2], want[:2]):
+            nb = int(wr[2].block_offsets[-1])          # columns past the padding are not written
+            assert torch.equal(gr[2].block_offsets, wr[2].block_offsets), f"replay {rep}: P"
+            for u, v in ((gr[0], wr[0]), (gr[1], wr[1]),
+                         (gr[2].codes_t[:, :32 * nb], wr[2].codes_t[:, :32 * nb]),
+                         (gr[2].scales_t[:, :nb], wr[2].scales_t[:, :nb])):
+                assert torch.equal(u, v), f"replay {rep}: quantize"
+        assert torch.equal(got[2].view(torch.int16), want[2].view(torch.int16)), f"replay {rep}: wgrad"
+
 def test_mxfp8_deterministic():
     x = dev(W.config2_weight("random"))
     announce("mxfp8 determinism 8192x2048")
