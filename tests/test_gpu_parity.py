@@ -1828,3 +1828,48 @@ def test_random_grouped_segments(orc, seed):
     cols = int(rng.integers(1, 80)) * 32
     x = _random_values(rng, int(off[-1]), cols)
     check_grouped(orc, x, off, f"random G={G} cols={cols}")
+    check_grouped_rowcolt(orc, x, off, f"random G={G} cols={cols}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_weight_gradient(orc, seed):
+    """The grouped weight gradient on seeded random segmentations (empty,
+    short, exact and long segments) and random M, N (partial 256-tiles):
+    every expert against the oracle's product of the padded operands, to the
+    GEMM bound; empty experts give zeros."""
+    rng = np.random.default_rng(3000 + seed)
+    G = int(rng.integers(1, 24))
+    kinds = rng.integers(0, 4, G)
+    sizes = np.where(kinds == 0, 0,
+                     np.where(kinds == 1, rng.integers(1, 32, G),
+                              np.where(kinds == 2, 32 * rng.integers(1, 5, G),
+                                       rng.integers(33, 700, G))))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    if off[-1] == 0:
+        off[-1] = 1
+    R = int(off[-1])
+    M, N = int(rng.integers(1, 12)) * 32, int(rng.integers(1, 12)) * 32
+    # Products kept inside the fp32 range (as in the dense GEMM tests): normal
+    # and heavy-tailed values at a random scale of 2^-10 .. 2^10.
+    def values(rows, cols):
+        v = (rng.standard_normal((rows, cols)) if rng.integers(0, 2) else
+             rng.standard_t(3, (rows, cols))) * 2.0 ** float(rng.integers(-10, 11))
+        return W.bf16_bits(v)
+    dy, x = values(R, M), values(R, N)
+    announce(f"random wgrad G={G} R={R} M={M} N={N}")
+    gd = api.mxfp8_grouped_colwise_t(dev(dy), dev(off))
+    gx = api.mxfp8_grouped_colwise_t(dev(x), dev(off))
+    c = api.mxfp8_grouped_wgrad(gd, gx, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = c.cpu().numpy().astype(np.float64)
+    dct, dst, P = padded_colt(orc, dy, off)
+    xct, xst, _ = padded_colt(orc, x, off)
+    for e in range(G):
+        k0, k1 = 32 * int(P[e]), 32 * int(P[e + 1])
+        if k0 == k1:
+            assert np.all(got[e] == 0), f"empty expert {e}"
+            continue
+        C, S = orc.mxfp8_gemm(dct[:, k0:k1], dst[:, k0 // 32:k1 // 32],
+                              xct[:, k0:k1], xst[:, k0 // 32:k1 // 32])
+        assert np.all(np.abs(got[e] - C) <= (GEMM_REL + (k1 - k0) * 2.0 ** -24) * S), \
+            f"expert {e}"
