@@ -377,15 +377,54 @@ def time_graph(torch, launches, n_launch, samples):
     return out
 
 
+STREAMS = 4
+
+
+def time_streams(torch, launches, n_launch, warmup, samples, n_streams=STREAMS):
+    """Per-call time (ms) of n_launch calls cycling through `launches` (each a
+    distinct buffer set), issued round-robin on n_streams streams of default
+    priority and captured once in a HIP graph, so that one call's ramp and
+    drain can overlap another's: the sustained device rate of independent
+    calls, without the host's per-call cost.  (Issued eagerly, the stream
+    switch per call costs the host more than these kernels take.)  The side
+    streams fork from the capture stream and join it at the end."""
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        cap = torch.cuda.current_stream()
+        for st in streams:
+            st.wait_stream(cap)
+        for k in range(n_launch):
+            with torch.cuda.stream(streams[k % n_streams]):
+                launches[k % len(launches)]()
+        for st in streams:
+            cap.wait_stream(st)
+    for _ in range(max(1, warmup // n_launch)):
+        g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / n_launch)
+    del g
+    return out
+
+
 _FLOORS = {}
 
 
-def copy_floor(torch, E, rbytes, wbytes, sets, graph, n_launch=CFG_LAUNCHES, warmup=CFG_WARMUP):
+def copy_floor(torch, E, rbytes, wbytes, sets, graph, n_launch=CFG_LAUNCHES, warmup=CFG_WARMUP,
+               streams=False):
     """The copy floor of a workload: mxq_copy_floor (a kernel that only reads
     rbytes and writes wbytes, no arithmetic) timed with the workload's own
     protocol and buffer rotation.  Returns (eager ms list, graph ms list or
-    None); cached per byte counts."""
-    key = (rbytes, wbytes, sets, graph, n_launch)
+    None[, concurrent-streams ms list when streams]); cached per byte counts."""
+    key = (rbytes, wbytes, sets, graph, n_launch, streams)
     if key in _FLOORS:
         return _FLOORS[key]
     r16, w16 = -(-rbytes // 16) * 16, -(-wbytes // 16) * 16
@@ -394,14 +433,15 @@ def copy_floor(torch, E, rbytes, wbytes, sets, graph, n_launch=CFG_LAUNCHES, war
     launches = [(lambda b=b: E.mxq_copy_floor(b[0], r16, b[1], w16)) for b in bufs]
     ms = time_launches(torch, launches, n_launch, warmup, CFG_SAMPLES)
     gms = time_graph(torch, launches, n_launch, CFG_SAMPLES) if graph else None
+    sms = time_streams(torch, launches, n_launch, warmup, CFG_SAMPLES) if streams else None
     del bufs, launches
     torch.cuda.empty_cache()
-    _FLOORS[key] = (ms, gms)
+    _FLOORS[key] = (ms, gms, sms) if streams else (ms, gms)
     return _FLOORS[key]
 
 
 def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None, floor=None,
-               rw=None):
+               rw=None, streams_ms=None):
     """One config's record.  floor: (eager, graph) ms lists of the copy floor of
     the same read and write bytes: "vs_copy_floor" is the floor's time over the
     kernel's (1.0 = as fast as a plain copy of those bytes)."""
@@ -428,6 +468,16 @@ def cfg_record(name, desc, ms_list, nbytes, elems, sets, kernels, graph_ms=None,
             fg = float(np.median(floor[1]))
             rec.update({"graph_copy_floor_ms": round(fg, 5),
                         "graph_vs_copy_floor": round(fg / gmed, 4)})
+    if streams_ms is not None:
+        smed = float(np.median(streams_ms))
+        sgbs = nbytes / (smed * 1e-3) / 1e9
+        rec.update({f"graph_streams{STREAMS}_ms_median": round(smed, 5),
+                    f"graph_streams{STREAMS}_GB_s": round(sgbs, 1),
+                    f"graph_streams{STREAMS}_pct_hbm_peak": round(100 * sgbs / HBM_PEAK_GBS, 2)})
+        if floor is not None and len(floor) > 2 and floor[2] is not None:
+            fs = float(np.median(floor[2]))
+            rec.update({f"graph_streams{STREAMS}_copy_floor_ms": round(fs, 5),
+                        f"graph_streams{STREAMS}_vs_copy_floor": round(fs / smed, 4)})
     return name, rec
 
 
@@ -457,12 +507,13 @@ def config_timings(torch, E, W, legs, log, only=None):
                                                                b[4])) for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
+        sms = time_streams(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         del bufs, launches, x0
         torch.cuda.empty_cache()
         rw = (2 * n, 2 * n + 2 * (n // 32))
-        fl = copy_floor(torch, E, *rw, sets, True)
+        fl = copy_floor(torch, E, *rw, sets, True, streams=True)
         k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
-                          ["mxfp8_tile_kernel"], gms, fl, rw)
+                          ["mxfp8_tile_kernel"], gms, fl, rw, sms)
         res[k] = v
 
     for mode in W.MXFP8_MODES:
@@ -485,21 +536,23 @@ def config_timings(torch, E, W, legs, log, only=None):
              for b in bufs]
         ms = time_launches(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         gms = time_graph(torch, q, CFG_LAUNCHES, CFG_SAMPLES)
+        sms = time_streams(torch, q, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         d = [(lambda b=b: E.mxq_dequantize_bf16(E.MXQ_FMT_NVFP4, b[1], b[2], b[3], 1, rows,
                                                  cols, b[4])) for b in bufs]
         dms = time_launches(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         dgms = time_graph(torch, d, CFG_LAUNCHES, CFG_SAMPLES)
+        dsms = time_streams(torch, d, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         del bufs, q, d, x0
         torch.cuda.empty_cache()
         if sel("C3_nvfp4"):
-            fl = copy_floor(torch, E, 2 * n, q_out, sets, True)
+            fl = copy_floor(torch, E, 2 * n, q_out, sets, True, streams=True)
             k, v = cfg_record("C3_nvfp4", f"NVFP4 per-token {rows}x{cols}", ms, q_bytes, n, sets,
-                              ["nvfp4_token_split_kernel"], gms, fl, (2 * n, q_out))
+                              ["nvfp4_token_split_kernel"], gms, fl, (2 * n, q_out), sms)
             res[k] = v
         if sel("C3_dequant"):
-            fl = copy_floor(torch, E, q_out, 2 * n, sets, True)
+            fl = copy_floor(torch, E, q_out, 2 * n, sets, True, streams=True)
             k, v = cfg_record("C3_dequant", f"NVFP4 -> BF16 {rows}x{cols}", dms, d_bytes, n,
-                              sets, ["dequant_nvfp4_kernel"], dgms, fl, (q_out, 2 * n))
+                              sets, ["dequant_nvfp4_kernel"], dgms, fl, (q_out, 2 * n), dsms)
             res[k] = v
         log("C3 timed")
 
