@@ -124,7 +124,7 @@ __device__ __forceinline__ uint32_t bf16_from_f64(double y)
 __device__ __forceinline__ bool bf16_tie_hazard(float a, float s)
 {
     const float p = a * s;
-    return (f2u(p) & 0xFFFFu) == 0x8000u && __builtin_fmaf(a, s, -p) != 0.0f;
+    return ((f2u(p) & 0xFFFFu) == 0x8000u) & (__builtin_fmaf(a, s, -p) != 0.0f);
 }
 
 // Exact BF16 pair for one code byte (two E2M1 codes) under (d, s).  Inlined
@@ -143,24 +143,42 @@ static __device__ __attribute__((noinline)) uint32_t nv_pair_exact(uint32_t byte
     return nv_pair_exact_inl(byte, d, s);
 }
 
+// Whether a block with decoded block scale d under FP32 scale s takes the
+// fast path: every element's f32 product rounds to the same BF16 as the
+// exact product (no tie hazard, no overflow, s not tiny).
+__device__ __forceinline__ bool nv_fast(float d, float s)
+{
+    // Bitwise, not short-circuit: all four tests are cheap, and evaluating
+    // them all keeps the check free of branches.
+    return (s >= NV_FAST_MIN_S) & (fabsf((6.0f * d) * s) <= BF16_MAX) &
+           !bf16_tie_hazard(d, s) & !bf16_tie_hazard(3.0f * d, s);
+}
+
+// Fast-path BF16 pair of the two E2M1 codes in byte J of w (the conversion
+// reads the byte itself, so no shift is spent on it): dec(c) d is exact in
+// f32, and the product with s is rounded to f32 and then to BF16.
+template <int J>
+__device__ __forceinline__ uint32_t nv_pair_fast(uint32_t w, float d, float s)
+{
+    const float2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
+    const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Eight BF16 (16 bytes) of one NVFP4 chunk: 8 codes (4 bytes) of a block
-// with decoded block scale d under FP32 scale s.
-__device__ __forceinline__ u32x4_t nv_chunk(uint32_t cw, float d, float s)
+// with decoded block scale d under FP32 scale s, on the fast path.
+__device__ __forceinline__ u32x4_t nv_chunk_fast(uint32_t cw, float d, float s)
+{
+    return u32x4_t{nv_pair_fast<0>(cw, d, s), nv_pair_fast<1>(cw, d, s),
+                   nv_pair_fast<2>(cw, d, s), nv_pair_fast<3>(cw, d, s)};
+}
+
+// The same eight BF16 on the exact binary64 path.
+__device__ __forceinline__ u32x4_t nv_chunk_exact(uint32_t cw, float d, float s)
 {
     u32x4_t o;
-    const bool fast = s >= NV_FAST_MIN_S && fabsf((6.0f * d) * s) <= BF16_MAX &&
-                      !bf16_tie_hazard(d, s) && !bf16_tie_hazard(3.0f * d, s);
-    if (fast) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float2_t v = e2m1_values((cw >> (8 * j)) & 0xFFu);
-            const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
-            o[j] = __builtin_bit_cast(uint32_t, r);
-        }
-    } else {
-        for (int j = 0; j < 4; j++)
-            o[j] = nv_pair_exact_inl((cw >> (8 * j)) & 0xFFu, d, s);
-    }
+    for (int j = 0; j < 4; j++)
+        o[j] = nv_pair_exact_inl((cw >> (8 * j)) & 0xFFu, d, s);
     return o;
 }
 
@@ -169,18 +187,9 @@ __device__ __forceinline__ u32x4_t nv_chunk(uint32_t cw, float d, float s)
 __device__ __forceinline__ void nv_block16(uint32_t c0, uint32_t c1, float d, float s,
                                            u32x4_t &lo, u32x4_t &hi)
 {
-    const bool fast = s >= NV_FAST_MIN_S && fabsf((6.0f * d) * s) <= BF16_MAX &&
-                      !bf16_tie_hazard(d, s) && !bf16_tie_hazard(3.0f * d, s);
-    if (fast) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float2_t v = e2m1_values((c0 >> (8 * j)) & 0xFFu);
-            const float2_t u = e2m1_values((c1 >> (8 * j)) & 0xFFu);
-            const bf16x2v_t r = {(__bf16)((v[0] * d) * s), (__bf16)((v[1] * d) * s)};
-            const bf16x2v_t q = {(__bf16)((u[0] * d) * s), (__bf16)((u[1] * d) * s)};
-            lo[j] = __builtin_bit_cast(uint32_t, r);
-            hi[j] = __builtin_bit_cast(uint32_t, q);
-        }
+    if (nv_fast(d, s)) {
+        lo = nv_chunk_fast(c0, d, s);
+        hi = nv_chunk_fast(c1, d, s);
     } else {
         for (int j = 0; j < 4; j++) {
             lo[j] = nv_pair_exact((c0 >> (8 * j)) & 0xFFu, d, s);

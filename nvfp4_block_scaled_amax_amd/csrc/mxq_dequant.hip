@@ -23,6 +23,14 @@
 // them (11.2 and 242 us).  The MXFP8 kernels keep two chunks per lane: four
 // were no faster at 8192 x 2048 and slower at 262144 x 2048 (254 -> 264 us).
 //
+// NVFP4 takes the fast/exact choice once per chunk for the whole wave (one
+// uniform branch; the check itself is branch-free) and stores each chunk as
+// soon as it is converted.  Against a per-lane branch per chunk, which left
+// a wait for the previous store before each store: 262144 x 2048 234 -> 227
+// us, 8192 x 2048 unchanged (10.0-10.4 us).  Converting all four chunks
+// before the first store was slower at 8192 x 2048 (11.7 us): with one step
+// per wavefront the writes then start late.
+//
 // The arithmetic (exact conversion instructions, and the exact fallbacks)
 // is in mxq_dequant.h.  MXFP8 rowwise: one scale per unit (index f / 32);
 // columnwise: one scale per element, so each pair is converted twice and the
@@ -100,7 +108,7 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__res
         int64_t f[NV_CHUNKS];
         bool ok[NV_CHUNKS];
         uint32_t cw[NV_CHUNKS], bb[NV_CHUNKS];
-        float d[NV_CHUNKS], s[NV_CHUNKS];
+        float s[NV_CHUNKS];
         // One FP32 scale for the whole step?  (Wave-uniform.)
         const int64_t f0 = w * NV_SPAN;
         const int64_t f1 = (f0 + NV_SPAN <= n ? f0 + NV_SPAN : n) - 1;
@@ -122,14 +130,18 @@ __global__ void __launch_bounds__(256) dequant_nvfp4_kernel(const uint8_t *__res
             for (int h = 0; h < NV_CHUNKS; h++)
                 s[h] = su;
         }
+        // Chunk by chunk: the fast/exact choice is made for the whole wave
+        // (one branch, no divergence) and each chunk is stored as soon as it
+        // is converted, so the wave's first store leaves early.
 #pragma unroll
         for (int h = 0; h < NV_CHUNKS; h++) {
-            d[h] = ok[h] ? e4m3_value(bb[h]) : 0.0f;
-            cw[h] = ok[h] ? cw[h] : 0u;
-        }
-#pragma unroll
-        for (int h = 0; h < NV_CHUNKS; h++) {
-            const u32x4_t o = nv_chunk(cw[h], d[h], s[h]);
+            const float dh = e4m3_value(ok[h] ? bb[h] : 0u);     // code 0 decodes to 0
+            const uint32_t ch = ok[h] ? cw[h] : 0u;
+            const bool fast = nv_fast(dh, s[h]);
+            const u32x4_t o = __builtin_amdgcn_ballot_w64(!fast) == 0
+                                  ? nv_chunk_fast(ch, dh, s[h])
+                                  : (fast ? nv_chunk_fast(ch, dh, s[h])
+                                          : nv_chunk_exact(ch, dh, s[h]));
             if (ok[h])
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + f[h]));
         }
