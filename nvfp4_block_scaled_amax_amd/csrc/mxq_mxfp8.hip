@@ -338,6 +338,10 @@ struct Geometry {
     int64_t n_groups;
     const int64_t *row_tokens;  // dispatch: token of each (expert-sorted) row, else nullptr
     int64_t n_tokens;           // dispatch: rows of x
+    // Dense launches: band order (band_order), set by the launcher.
+    uint32_t bo_k;              // workgroups per 32-row band; 0: launch order
+    uint32_t bo_full;           // workgroups in whole groups of 8 bo_k
+    Div bo_grp;                 // division by 8 bo_k
 };
 
 // Segment e's rows clamped into [0, total_rows): offsets are device data the
@@ -496,6 +500,46 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
     }
 }
 
+// Band order of dense launches.  Workgroups are dealt round-robin to the 8
+// XCDs (workgroup h runs on XCD h % 8), and the k = nct / WPW workgroups of a
+// 32-row band, in launch order, would land on k different XCDs.  Workgroup
+// h instead takes position L (below), so that each band's k workgroups run on
+// one XCD and consecutive bands on consecutive XCDs.  The rowwise scale bytes
+// of a row (4 per 128-column strip) and its code segments then meet in one
+// L2 and leave it as whole lines, instead of as pieces that each cost HBM a
+// separate partial write.  Byte-identical; row+col 8192 x 2048 14.5 -> 14.0
+// us, 262144 x 2048 379 -> 356 us; the transposed layout at 8192 x 2048
+// 35.2 -> 29.9 us.  (Grouped
+// launches showed no change, 358-361 us either way, and keep launch order;
+// the dispatch gather keeps its own order.)  L permutes each group of 8 k
+// consecutive workgroups among themselves: position j of group q goes to
+// 8 k q + k (j % 8) + j / 8.  A last, partial group and bands that straddle
+// workgroups (nct % WPW != 0) keep launch order.  The group index is a
+// multiply-high by a constant formed on the host: a division per wavefront
+// delayed the loads of the small one-step launches.
+__device__ __forceinline__ int64_t band_order(int64_t hw, const Geometry &G)
+{
+    const uint32_t h = (uint32_t)hw, k = G.bo_k;
+    if (k == 0 || h >= G.bo_full)
+        return hw;
+    const uint32_t q0 = udiv(h, G.bo_grp) * 8 * k;   // first workgroup of h's group
+    const uint32_t j = h - q0;                       // 0 .. 8 k - 1
+    return (int64_t)(q0 + (j & 7) * k + (j >> 3));
+}
+
+static void set_band_order(Geometry &G, int64_t wgs, int wpw)
+{
+    G.bo_k = 0;
+    G.bo_full = 0;
+    G.bo_grp = Div{0, 0};
+    if (G.nct % wpw != 0 || G.nct / wpw < 2)
+        return;
+    const int64_t k = G.nct / wpw;          // cols <= 2^26: 8 k <= 2^20
+    G.bo_k = (uint32_t)k;
+    G.bo_full = (uint32_t)(wgs / (8 * k) * (8 * k));
+    G.bo_grp = make_div((uint32_t)(8 * k));
+}
+
 // SCAN (grouped, G <= SCAN_MAX_GROUPS): the block prefix formed in LDS
 // (wave_block_prefix; workgroup 0 stores it to P_out).
 template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool SCAN = false>
@@ -524,6 +568,9 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_tile_kernel(Geometry G, uint8_
         const int64_t hw = wg_id();
         tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr,
                                                          (hw & 7) * per_xcd + (hw >> 3));
+    } else if constexpr (!GROUPED) {
+        tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr,
+                                                         band_order(wg_id(), G));
     } else {
         tile_body<ROW, COL, GROUPED, WPW, GATHER, false>(G, rc, rs, cc, cs, nullptr);
     }
@@ -537,7 +584,8 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_row_qdq_kernel(Geometry G,
                                                             uint8_t *__restrict__ rs,
                                                             uint16_t *__restrict__ dq)
 {
-    tile_body<ROW, false, false, WPW, false, true>(G, rc, rs, nullptr, nullptr, dq);
+    tile_body<ROW, false, false, WPW, false, true>(G, rc, rs, nullptr, nullptr, dq,
+                                                   band_order(wg_id(), G));
 }
 
 // Both copies under the OCP MX scale rule (comparison variant).
@@ -547,7 +595,8 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_ocp_kernel(Geometry G, uint8_t
                                                         uint8_t *__restrict__ cc,
                                                         uint8_t *__restrict__ cs)
 {
-    tile_body<ROW, COL, false, WPW, false, false, true>(G, rc, rs, cc, cs, nullptr);
+    tile_body<ROW, COL, false, WPW, false, false, true>(G, rc, rs, cc, cs, nullptr,
+                                                        band_order(wg_id(), G));
 }
 
 // Both copies, the columnwise one transposed (layout variant).
@@ -557,7 +606,8 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
                                                          uint8_t *__restrict__ cct,
                                                          uint8_t *__restrict__ cst)
 {
-    tile_body<ROW, true, false, WPW, false, false, false, true>(G, rc, rs, cct, cst, nullptr);
+    tile_body<ROW, true, false, WPW, false, false, false, true>(G, rc, rs, cct, cst, nullptr,
+                                                                band_order(wg_id(), G));
 }
 
 // Grouped columnwise copy, transposed and padded (the weight-gradient
@@ -718,8 +768,11 @@ static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint
     const int64_t wgs = GATHER ? ((waves + WPW - 1) / WPW + 7) / 8 * 8 : (waves + WPW - 1) / WPW;
     if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
+    Geometry Gl = G;
+    if (!GROUPED && !GATHER)
+        set_band_order(Gl, wgs, WPW);
     hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER, SCAN>),
-                       dim3((unsigned)wgs), dim3(64 * WPW), 0, stream, G, rc, rs, cc, cs, P_out);
+                       dim3((unsigned)wgs), dim3(64 * WPW), 0, stream, Gl, rc, rs, cc, cs, P_out);
     return hipGetLastError();
 }
 
@@ -769,8 +822,10 @@ static hipError_t launch_qdq_wpw(const Geometry &G, int64_t waves, uint8_t *rc, 
     const int64_t wgs = (waves + WPW - 1) / WPW;
     if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
+    Geometry Gl = G;
+    set_band_order(Gl, wgs, WPW);
     hipLaunchKernelGGL((mxfp8_row_qdq_kernel<ROW, WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
-                       stream, G, rc, rs, dq);
+                       stream, Gl, rc, rs, dq);
     return hipGetLastError();
 }
 
@@ -797,8 +852,10 @@ static hipError_t launch_ocp(const Geometry &G, int64_t waves, uint8_t *rc, uint
     const int64_t wgs = (waves + 3) / 4;
     if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
         return hipErrorInvalidValue;
+    Geometry Gl = G;
+    set_band_order(Gl, wgs, 4);
     hipLaunchKernelGGL((mxfp8_ocp_kernel<ROW, COL, 4>), dim3((unsigned)wgs), dim3(256), 0, stream,
-                       G, rc, rs, cc, cs);
+                       Gl, rc, rs, cc, cs);
     return hipGetLastError();
 }
 
@@ -824,6 +881,7 @@ hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint
     const int64_t wgs = (waves + 3) / 4;
     if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
         return hipErrorInvalidValue;
+    set_band_order(G, wgs, 4);
     if (rc)
         hipLaunchKernelGGL((mxfp8_colt_kernel<true, 4>), dim3((unsigned)wgs), dim3(256), 0,
                            stream, G, rc, rs, cct, cst);
