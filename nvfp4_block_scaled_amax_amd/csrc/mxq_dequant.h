@@ -124,7 +124,7 @@ __device__ __forceinline__ uint32_t bf16_from_f64(double y)
 __device__ __forceinline__ bool bf16_tie_hazard(float a, float s)
 {
     const float p = a * s;
-    return ((f2u(p) & 0xFFFFu) == 0x8000u) & (__builtin_fmaf(a, s, -p) != 0.0f);
+    return ((int)((f2u(p) & 0xFFFFu) == 0x8000u) & (int)(__builtin_fmaf(a, s, -p) != 0.0f)) != 0;
 }
 
 // Exact BF16 pair for one code byte (two E2M1 codes) under (d, s).  Inlined
@@ -150,8 +150,8 @@ __device__ __forceinline__ bool nv_fast(float d, float s)
 {
     // Bitwise, not short-circuit: all four tests are cheap, and evaluating
     // them all keeps the check free of branches.
-    return (s >= NV_FAST_MIN_S) & (fabsf((6.0f * d) * s) <= BF16_MAX) &
-           !bf16_tie_hazard(d, s) & !bf16_tie_hazard(3.0f * d, s);
+    return ((int)(s >= NV_FAST_MIN_S) & (int)(fabsf((6.0f * d) * s) <= BF16_MAX) &
+            (int)!bf16_tie_hazard(d, s) & (int)!bf16_tie_hazard(3.0f * d, s)) != 0;
 }
 
 // Fast-path BF16 pair of the two E2M1 codes in byte J of w (the conversion

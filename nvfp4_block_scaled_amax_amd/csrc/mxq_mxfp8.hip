@@ -177,13 +177,13 @@ __device__ __forceinline__ u32x4_t row_dq(uint32_t w0, uint32_t w1, uint32_t sca
 // saturate (it gives NaN from 464 up), so magnitudes are first clamped to
 // 448 * 2^e, whose BF16 bits are ((byte + 8) << 7) | 0x60; the nearest E4M3
 // of anything at or above that is 448.
-// COLT: the columnwise copy transposed (a layout variant): codes [cols][rows]
-// and scales [cols][rows/32]; o.cc / o.cs then point at column tcol's row
-// row0 (codes) and its scale for this 32-row block, with row pitches ld_t
-// (= rows) and lds_t (= rows / 32).  Each lane writes, per column, its 8 rows
-// as 8 contiguous bytes.
+// COLT: the columnwise copy transposed, staged in LDS (the transposed
+// layouts): o.cc / o.cs point at the wavefront's first row in LDS arrays of
+// [column][rows] codes and [column][blocks] scale bytes with column pitches
+// ld_t and lds_t; each lane writes, per column, its 8 rows as two 4-byte
+// words (ld_t is a multiple of 4).
 template <bool ROW, bool COL, bool FULL, bool DQ = false, bool OCP = false, bool COLT = false,
-          bool LATE = false, bool TLDS = false>
+          bool LATE = false>
 __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t cols,
                                              uint32_t c8, int nrows, int g, int rg, bool col_ok,
                                              const TileOut &o)
@@ -291,15 +291,9 @@ __device__ __forceinline__ void convert_tile(const uint32_t (&v)[8][4], uint32_t
                     const uint32_t lo = perm(P[1][j], P[0][j], sel);
                     const uint32_t hi = perm(P[3][j], P[2][j], sel);
                     const uint32_t c = c8 + 2 * j + e;
-                    if constexpr (TLDS) {
-                        // LDS staging (o.cc, o.cs point into LDS): two
-                        // 4-byte writes, the column pitch being 4-aligned.
-                        uint32_t *d = reinterpret_cast<uint32_t *>(o.cc + c * o.ld_t + 8 * rg);
-                        d[0] = lo;
-                        d[1] = hi;
-                    } else {
-                        st_nt8(o.cc + ((size_t)c * o.ld_t + 8 * rg), lo, hi);
-                    }
+                    uint32_t *d = reinterpret_cast<uint32_t *>(o.cc + c * o.ld_t + 8 * rg);
+                    d[0] = lo;
+                    d[1] = hi;
                     if (rg == 0)
                         o.cs[(size_t)c * o.lds_t] = (uint8_t)(sb[j] >> (16 * e));
                 }
@@ -332,7 +326,7 @@ struct Geometry {
     int64_t rows;          // dense: rows; grouped: total rows
     int64_t cols;
     int64_t nct;           // 128-column strips
-    int64_t max_tiles;     // grouped: capacity of col_scales in rows
+    int64_t max_tiles;     // grouped: capacity of col_scales in rows; dense transposed: rows / 32
     const int64_t *off;    // grouped: segment offsets
     const int64_t *P;      // grouped: prefix of ceil(n_e / 32)
     int64_t n_groups;
@@ -421,14 +415,13 @@ __device__ __forceinline__ void wave_block_prefix(const int64_t *__restrict__ of
 // One tile per wavefront: wave w converts strip w % nct of tile w / nct, so
 // the four wavefronts of a workgroup cover 512 consecutive columns of one
 // 32-row band.  Launched over all tiles at once.
-template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool OCP = false,
-          bool COLT = false>
+template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool DQ, bool OCP = false>
 __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict__ rc,
                                           uint8_t *__restrict__ rs, uint8_t *__restrict__ cc,
                                           uint8_t *__restrict__ cs, uint16_t *__restrict__ dq,
                                           int64_t wg = -1)
 {
-    constexpr bool LATE = ROW && COL && !DQ && !OCP && !COLT && WPW == 4;
+    constexpr bool LATE = ROW && COL && !DQ && !OCP && WPW == 4;
     const int lane = (int)lane_id();
     const int g = lane & 15, rg = lane >> 4;
     const int64_t wave = (wg < 0 ? (int64_t)wg_id() : wg) * WPW + wave_in_group();
@@ -476,12 +469,6 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
     const uint16_t *xt = G.x + base;
     TileOut o{rc + base, rs + (base >> 5), cc + base, cs + t.srow * G.cols + tcol,
               DQ ? dq + base : nullptr, 0, 0};
-    if constexpr (COLT) {
-        o.ld_t = (uint32_t)G.rows;
-        o.lds_t = (uint32_t)(G.rows >> 5);
-        o.cc = cc + tcol * G.rows + t.row0;
-        o.cs = cs + tcol * (G.rows >> 5) + t.srow;
-    }
     uint32_t v[8][4];
     if (full) {
         if constexpr (GATHER)
@@ -489,14 +476,14 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
                                    t.nrows, rg, col_ok);
         else
             load_tile<true>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, true, DQ, OCP, COLT, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, true, DQ, OCP, false, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     } else {
         if constexpr (GATHER)
             load_tile_gather<false>(v, G.x, G.row_tokens, G.n_tokens, G.cols, t.row0, tcol + c8,
                                     t.nrows, rg, col_ok);
         else
             load_tile<false>(v, xt, cols, c8, t.nrows, rg, col_ok);
-        convert_tile<ROW, COL, false, DQ, OCP, COLT, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
+        convert_tile<ROW, COL, false, DQ, OCP, false, LATE>(v, cols, c8, t.nrows, g, rg, col_ok, o);
     }
 }
 
@@ -508,8 +495,7 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
 // of a row (4 per 128-column strip) and its code segments then meet in one
 // L2 and leave it as whole lines, instead of as pieces that each cost HBM a
 // separate partial write.  Byte-identical; row+col 8192 x 2048 14.5 -> 14.0
-// us, 262144 x 2048 379 -> 356 us; the transposed layout at 8192 x 2048
-// 35.2 -> 29.9 us.  (Grouped
+// us, 262144 x 2048 379 -> 356 us.  (Grouped
 // launches showed no change, 358-361 us either way, and keep launch order;
 // the dispatch gather keeps its own order.)  L permutes each group of 8 k
 // consecutive workgroups among themselves: position j of group q goes to
@@ -599,17 +585,6 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_ocp_kernel(Geometry G, uint8_t
                                                         band_order(wg_id(), G));
 }
 
-// Both copies, the columnwise one transposed (layout variant).
-template <bool ROW, int WPW>
-__global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_t *__restrict__ rc,
-                                                         uint8_t *__restrict__ rs,
-                                                         uint8_t *__restrict__ cct,
-                                                         uint8_t *__restrict__ cst)
-{
-    tile_body<ROW, true, false, WPW, false, false, false, true>(G, rc, rs, cct, cst, nullptr,
-                                                                band_order(wg_id(), G));
-}
-
 // Grouped columnwise copy, transposed and padded (the weight-gradient
 // operand layout): codes [cols][pitch], scales [cols][pitch / 32]; segment
 // e's 32-row blocks, rounded up to a multiple of 4 (128 rows) with zero
@@ -629,21 +604,19 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_colt_kernel(Geometry G, uint8_
 // ROW: the rowwise copy [rows][cols] from the same read (the grouped
 // rowwise layout, stored straight from the lanes as the tile kernel does).
 // SCAN: the block prefix formed in LDS, as in mxfp8_tile_kernel.
-template <int WPW, bool ROW, bool SCAN>
-__global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G,
-                                                                      uint8_t *__restrict__ rc,
-                                                                      uint8_t *__restrict__ rs,
-                                                                      uint8_t *__restrict__ cct,
-                                                                      uint8_t *__restrict__ cst,
-                                                                      int64_t *__restrict__ P_out)
+// DENSE: the same staging for one dense tensor (the transposed layout of
+// mxq_mxfp8_quantize_rowcol_t): block T is rows 32 T .. 32 T + 31, the codes'
+// row pitch is rows and the scales' rows / 32, which need not be a multiple
+// of 4, so scale bytes go out as dwords only where aligned and whole.
+// Against each lane writing its 8 rows of a column straight to HBM (8-byte
+// pieces of lines): 8192 x 2048 29.7 -> 18.0 us, 262144 x 2048 1670 -> 432
+// us, byte-identical.
+template <int WPW, bool ROW, bool DENSE>
+__device__ __forceinline__ void colt_staged_body(const Geometry &G, uint8_t *__restrict__ rc,
+                                                 uint8_t *__restrict__ rs,
+                                                 uint8_t *__restrict__ cct,
+                                                 uint8_t *__restrict__ cst)
 {
-    if constexpr (SCAN) {
-        __shared__ int64_t Ps[SCAN_MAX_GROUPS + 1];
-        if (wave_in_group() == 0)
-            wave_block_prefix(G.off, G.n_groups, G.rows, 4, Ps, wg_id() == 0 ? P_out : nullptr);
-        __syncthreads();
-        G.P = Ps;
-    }
     constexpr int LP = TILE_ROWS * WPW + 4;          // bytes per staged column (bank spread)
     constexpr int PIECES = 2 * WPW;                   // 16-byte pieces per staged column
     __shared__ __attribute__((aligned(16))) uint8_t sc[TILE_COLS * LP];
@@ -665,7 +638,7 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
     if (wg >= total)
         return;
     const int64_t strip = wg % G.nct, T0 = WPW * (wg / G.nct);
-    int64_t ntiles = G.P[G.n_groups];
+    int64_t ntiles = DENSE ? G.max_tiles : G.P[G.n_groups];
     if (ntiles > G.max_tiles)
         ntiles = G.max_tiles;
     if (T0 >= ntiles)                      // uniform
@@ -676,12 +649,19 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
     const bool col_ok = tcol + c8 < G.cols;
     if (w < nv) {                          // wave-uniform
         const int64_t T = T0 + w;
-        const int64_t e = tile_segment(G.P, G.n_groups, T);
-        int64_t lo, hi;
-        segment_rows(G.off, e, G.rows, &lo, &hi);
-        const int64_t row0 = lo + (T - G.P[e]) * TILE_ROWS;
-        const int64_t left = hi - row0;
-        const int nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+        int64_t row0;
+        int nrows;
+        if constexpr (DENSE) {
+            row0 = T * TILE_ROWS;          // rows % 32 == 0: every block is whole
+            nrows = TILE_ROWS;
+        } else {
+            const int64_t e = tile_segment(G.P, G.n_groups, T);
+            int64_t lo, hi;
+            segment_rows(G.off, e, G.rows, &lo, &hi);
+            row0 = lo + (T - G.P[e]) * TILE_ROWS;
+            const int64_t left = hi - row0;
+            nrows = left <= 0 ? 0 : (left < TILE_ROWS ? (int)left : TILE_ROWS);
+        }
         uint32_t v[8][4];
         load_tile<false>(v, G.x + (nrows > 0 ? row0 : 0) * G.cols + tcol, cols, c8, nrows, rg,
                          col_ok);
@@ -689,8 +669,8 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
         const TileOut o{ROW ? rc + r0 * G.cols + tcol : nullptr,
                         ROW ? rs + r0 * (G.cols / 32) + tcol / 32 : nullptr,
                         sc + TILE_ROWS * w, ss + w, nullptr, LP, WPW};
-        convert_tile<ROW, true, false, false, false, true, false, true>(v, cols, c8, nrows, g, rg,
-                                                                        col_ok, o);
+        convert_tile<ROW, true, false, false, false, true, false>(v, cols, c8, nrows, g, rg,
+                                                                  col_ok, o);
     }
     __syncthreads();
     const int t = (int)tid();
@@ -707,12 +687,49 @@ __global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G
         }
     }
     // Scale bytes: WPW per column, one dword per thread.
+    const bool dw = !DENSE || ((G.max_tiles & 3) == 0 && ((uintptr_t)cst & 3) == 0);
     for (int q = t; q < TILE_COLS * WPW / 4; q += 64 * WPW) {
         const int c = q / (WPW / 4), k = q % (WPW / 4);
-        if (tcol + c < G.cols && 4 * k < nv)
-            *reinterpret_cast<uint32_t *>(cst + (tcol + c) * G.max_tiles + T0 + 4 * k) =
-                *reinterpret_cast<const uint32_t *>(ss + WPW * c + 4 * k);
+        if (tcol + c >= G.cols || 4 * k >= nv)
+            continue;
+        uint8_t *d = cst + (tcol + c) * G.max_tiles + T0 + 4 * k;
+        const uint8_t *src = ss + WPW * c + 4 * k;
+        if (dw && 4 * k + 4 <= nv) {
+            *reinterpret_cast<uint32_t *>(d) = *reinterpret_cast<const uint32_t *>(src);
+        } else {
+            for (int b = 0; b < 4 && 4 * k + b < nv; b++)
+                d[b] = src[b];
+        }
     }
+}
+
+template <int WPW, bool ROW, bool SCAN>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_grouped_colt_kernel(Geometry G,
+                                                                      uint8_t *__restrict__ rc,
+                                                                      uint8_t *__restrict__ rs,
+                                                                      uint8_t *__restrict__ cct,
+                                                                      uint8_t *__restrict__ cst,
+                                                                      int64_t *__restrict__ P_out)
+{
+    if constexpr (SCAN) {
+        __shared__ int64_t Ps[SCAN_MAX_GROUPS + 1];
+        if (wave_in_group() == 0)
+            wave_block_prefix(G.off, G.n_groups, G.rows, 4, Ps, wg_id() == 0 ? P_out : nullptr);
+        __syncthreads();
+        G.P = Ps;
+    }
+    colt_staged_body<WPW, ROW, false>(G, rc, rs, cct, cst);
+}
+
+// The transposed layout of one dense tensor through the same staging.
+template <int WPW, bool ROW>
+__global__ void __launch_bounds__(64 * WPW) mxfp8_colt_staged_kernel(Geometry G,
+                                                                     uint8_t *__restrict__ rc,
+                                                                     uint8_t *__restrict__ rs,
+                                                                     uint8_t *__restrict__ cct,
+                                                                     uint8_t *__restrict__ cst)
+{
+    colt_staged_body<WPW, ROW, true>(G, rc, rs, cct, cst);
 }
 
 // P[e] = sum_{f<e} ceil(n_f / 32) (each rounded up to a multiple of
@@ -875,19 +892,19 @@ hipError_t launch_mxfp8_ocp_floor(const uint16_t *x, int64_t rows, int64_t cols,
 hipError_t launch_mxfp8_colt(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *rc,
                              uint8_t *rs, uint8_t *cct, uint8_t *cst, hipStream_t stream)
 {
-    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, 0, nullptr, nullptr, 0,
-               nullptr, 0};
-    const int64_t waves = rows / TILE_ROWS * G.nct;         // rows % 32 == 0: checked by the caller
-    const int64_t wgs = (waves + 3) / 4;
-    if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
+    // rows % 32 == 0: checked by the caller.
+    Geometry G{x, rows, cols, (cols + TILE_COLS - 1) / TILE_COLS, rows / TILE_ROWS, nullptr,
+               nullptr, 0, nullptr, 0};
+    constexpr int WPW = 8;
+    const int64_t wgs = ((G.max_tiles + WPW - 1) / WPW * G.nct + 7) / 8 * 8;
+    if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
-    set_band_order(G, wgs, 4);
     if (rc)
-        hipLaunchKernelGGL((mxfp8_colt_kernel<true, 4>), dim3((unsigned)wgs), dim3(256), 0,
-                           stream, G, rc, rs, cct, cst);
+        hipLaunchKernelGGL((mxfp8_colt_staged_kernel<WPW, true>), dim3((unsigned)wgs),
+                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
     else
-        hipLaunchKernelGGL((mxfp8_colt_kernel<false, 4>), dim3((unsigned)wgs), dim3(256), 0,
-                           stream, G, rc, rs, cct, cst);
+        hipLaunchKernelGGL((mxfp8_colt_staged_kernel<WPW, false>), dim3((unsigned)wgs),
+                           dim3(64 * WPW), 0, stream, G, rc, rs, cct, cst);
     return hipGetLastError();
 }
 
