@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "mxfp8_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_grouped_wgrad_kernel": ["mxq_gemm.hip"],
     "mxfp8_grouped_colt_kernel": ["mxq_mxfp8.hip"],
+    "mxfp8_colt_staged_kernel": ["mxq_mxfp8.hip"],
     "nvfp4_gemm_kernel": ["mxq_gemm.hip"],
     "nvfp4_grouped_gemm_kernel": ["mxq_gemm.hip"],
     "mxfp8_row_qdq_kernel": ["mxq_mxfp8.hip"],
@@ -494,17 +495,20 @@ def config_timings(torch, E, W, legs, log, only=None):
     res = {}
     sel = (lambda name: True) if only is None else (lambda name: name in only)
 
-    def mxfp8_cfg(name, rows, cols, x_np):
+    def mxfp8_cfg(name, rows, cols, x_np, transposed=False):
+        """transposed: the columnwise copy in the transposed layout
+        (mxq_mxfp8_quantize_rowcol_t), the same bytes permuted."""
         if not sel(name):
             return
         n = rows * cols
         nbytes = 2 * n + 2 * n + 2 * (n // 32)
         sets = -(-ROTATE_BYTES // nbytes)
         x0 = dev(x_np)
+        ccs = ((cols, rows), (cols, rows // 32)) if transposed else ((rows, cols), (rows // 32, cols))
         bufs = [(x0 if k == 0 else x0.clone(), empty((rows, cols)), empty((rows, cols // 32)),
-                 empty((rows, cols)), empty((rows // 32, cols))) for k in range(sets)]
-        launches = [(lambda b=b: E.mxq_mxfp8_quantize_rowcol(b[0], rows, cols, b[1], b[2], b[3],
-                                                               b[4])) for b in bufs]
+                 empty(ccs[0]), empty(ccs[1])) for k in range(sets)]
+        fn = E.mxq_mxfp8_quantize_rowcol_t if transposed else E.mxq_mxfp8_quantize_rowcol
+        launches = [(lambda b=b: fn(b[0], rows, cols, b[1], b[2], b[3], b[4])) for b in bufs]
         ms = time_launches(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
         gms = time_graph(torch, launches, CFG_LAUNCHES, CFG_SAMPLES)
         sms = time_streams(torch, launches, CFG_LAUNCHES, CFG_WARMUP, CFG_SAMPLES)
@@ -512,13 +516,17 @@ def config_timings(torch, E, W, legs, log, only=None):
         torch.cuda.empty_cache()
         rw = (2 * n, 2 * n + 2 * (n // 32))
         fl = copy_floor(torch, E, *rw, sets, True, streams=True)
-        k, v = cfg_record(name, f"MXFP8 row+col {rows}x{cols}", ms, nbytes, n, sets,
-                          ["mxfp8_tile_kernel"], gms, fl, rw, sms)
+        desc = f"MXFP8 row+col {rows}x{cols}" + (", columnwise copy transposed" if transposed
+                                                  else "")
+        k, v = cfg_record(name, desc, ms, nbytes, n, sets,
+                          ["mxfp8_colt_staged_kernel" if transposed else "mxfp8_tile_kernel"],
+                          gms, fl, rw, sms)
         res[k] = v
 
     for mode in W.MXFP8_MODES:
         mxfp8_cfg(f"C2a_{mode}", 2048, 2048, W.config2_activation(mode))
         mxfp8_cfg(f"C2b_{mode}", 8192, 2048, W.config2_weight(mode))
+    mxfp8_cfg("C2b_rowcol_t", 8192, 2048, W.config2_weight("random"), transposed=True)
     log("C2 timed")
 
     rows, cols = 8192, 2048
@@ -1171,9 +1179,13 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
             t = 1e3 * c["ms_median"]
             hbm_s, ratio_s = f"{'-':>12}", f"{'-':>6}"
             notes.add("b")
-        if len(fl) == 1 and len(fl[0][3]) == 1:
+        # A floor grid serves every config of the same read and write bytes;
+        # configs of equal write bytes but other read bytes share its grid
+        # without sharing its time.
+        if len(fl) == 1 and len({(cfgs[m]["bytes_in"], cfgs[m]["bytes_out"])
+                                 for m in fl[0][3]}) == 1:
             ft, mark = fl[0][4], " "
-        else:       # a floor grid shared by configs of equal write bytes
+        else:
             ft, mark = 1e3 * c.get("copy_floor_ms", float("nan")), "*"
             notes.add("f")
         out.append(f"{n:<18} {t:>9.2f}{'b' if not mine else ' '} "
@@ -1183,8 +1195,9 @@ def summarize_shape(tag: str, configs: str, trace_csv: str, fetch_csv: str, writ
         out.append("b: the config's kernels also run for other configs of this run; its time is "
                    "the bench's median per call (tracer overhead included).")
     if "f" in notes:
-        out.append("*: the copy floor's grid is shared with another config; the floor time is the "
-                   "bench's median for this config's bytes (tracer overhead included).")
+        out.append("*: the copy floor's grid is shared with a config of other read bytes; the "
+                   "floor time is the bench's median for this config's bytes (tracer overhead "
+                   "included).")
     out += ["", "VALU counters (medians over dispatches); per wave: instructions, conversion",
             "instructions, VALU issue quad-cycles; 'VALU share' = SQ_ACTIVE_INST_VALU /",
             "SQ_WAVE_CYCLES, the fraction of the waves' resident time spent issuing VALU:", "",
@@ -1248,7 +1261,7 @@ def main():
                          "of the default step (the separate gather; quantize followed by "
                          "dequant) and the GEMMs consume its outputs, so none is part of it")
     ap.add_argument("--config-only", default=None,
-                    help="comma list of config names (C2a_<mode>, C2b_<mode>, C3_nvfp4, "
+                    help="comma list of config names (C2a_<mode>, C2b_<mode>, C2b_rowcol_t, C3_nvfp4, "
                          "C3_dequant, C4_gateup, C4_down, C4_gateup_amax, C4_down_amax, C5_mxfp8, C5_nvfp4, C5_dequant_mxfp8, "
                          "C5_dequant_nvfp4, C5_colt_mxfp8, C5_rowcolt_mxfp8, G_<gemm>): time "
                          "only these, each beside its copy floor, and "
