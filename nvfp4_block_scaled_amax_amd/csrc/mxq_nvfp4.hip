@@ -279,14 +279,16 @@ __device__ __forceinline__ void emit_blk(const BlkOut &o, int64_t j, uint8_t *__
 constexpr int WG_THREADS = 64;
 constexpr int ROWS_PER_WG = WG_THREADS / 64;
 
-// Row order: workgroup h takes row L(h), so that 32 consecutive rows -- one
-// 128-byte line of FP32 token scales -- run on one XCD (workgroups are dealt
-// round-robin to the 8 XCDs) and consecutive 32-row runs on consecutive
-// XCDs; a last, partial group of 256 keeps launch order.  Each XCD's L2 then
-// holds whole lines of token scales instead of 4-byte pieces that each cost
-// HBM a partial write.  Byte-identical; 8192 x 2048 per token 10.9 -> 10.5
-// us, 2048 x 2048 5.5 -> 5.0 us, 262144 x 2048 unchanged.  The dispatch
-// kernel, whose rows go to scattered destinations, keeps launch order.
+// Row order of the split kernel: workgroup h takes row L(h), so that 32
+// consecutive rows -- one 128-byte line of FP32 token scales -- run on one
+// XCD (workgroups are dealt round-robin to the 8 XCDs) and consecutive 32-row
+// runs on consecutive XCDs; a last, partial group of 256 keeps launch order.
+// Each XCD's L2 then holds whole lines of token scales instead of 4-byte
+// pieces that each cost HBM a partial write.  Byte-identical; 8192 x 2048
+// per token 10.9 -> 10.5 us, 2048 x 2048 5.5 -> 5.0 us.  The one-wavefront
+// rows of large grids keep launch order: there it was no faster per token
+// (262144 x 2048, 233 us either way) and slower with the BF16 copy (one-pass
+// quantize + dequant 420 -> 435 us).
 __device__ __forceinline__ int64_t row_order(int64_t h, int64_t rows)
 {
     if (h >= (rows >> 8) << 8)
@@ -355,8 +357,7 @@ __device__ __forceinline__ void token_body(const uint16_t *__restrict__ x, int64
                                            uint8_t *__restrict__ bs, float *__restrict__ ts,
                                            const Dest &dst)
 {
-    static_assert(ROWS_PER_WG == 1, "row_order maps workgroups to rows");
-    const int64_t row = SCATTER ? (int64_t)wg_id() : row_order(wg_id(), rows);
+    const int64_t row = (int64_t)wg_id() * ROWS_PER_WG + wave_in_group();
     if (row >= rows)
         return;
     const int lane = lane_id();
