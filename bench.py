@@ -602,6 +602,10 @@ def config_timings(torch, E, W, legs, log, only=None):
         if any("wgrad" in c or c in ("C5_colt_mxfp8", "C5_rowcolt_mxfp8") for c in only):
             res.update(wgrad_timings(torch, E, W, dev, empty, only))
             log("weight gradient timed")
+        if any("_qdq_" in c for c in only):
+            res.update({k: v for k, v in qdq_timings(torch, E, W, dev, empty).items()
+                        if k in only})
+            log("quantize + dequant timed")
     return res
 
 
@@ -1263,7 +1267,8 @@ def main():
     ap.add_argument("--config-only", default=None,
                     help="comma list of config names (C2a_<mode>, C2b_<mode>, C2b_rowcol_t, C3_nvfp4, "
                          "C3_dequant, C4_gateup, C4_down, C4_gateup_amax, C4_down_amax, C5_mxfp8, C5_nvfp4, C5_dequant_mxfp8, "
-                         "C5_dequant_nvfp4, C5_colt_mxfp8, C5_rowcolt_mxfp8, G_<gemm>): time "
+                         "C5_dequant_nvfp4, C5_colt_mxfp8, C5_rowcolt_mxfp8, C5_qdq_<fmt>, C2b_qdq_mxfp8, "
+                         "C3_qdq_nvfp4, G_<gemm>): time "
                          "only these, each beside its copy floor, and "
                          "print them as one JSON line (no step, no CPU baseline); for "
                          "profiling one shape per run")

@@ -495,9 +495,12 @@ __device__ __forceinline__ void tile_body(const Geometry &G, uint8_t *__restrict
 // of a row (4 per 128-column strip) and its code segments then meet in one
 // L2 and leave it as whole lines, instead of as pieces that each cost HBM a
 // separate partial write.  Byte-identical; row+col 8192 x 2048 14.5 -> 14.0
-// us, 262144 x 2048 379 -> 356 us.  (Grouped
-// launches showed no change, 358-361 us either way, and keep launch order;
-// the dispatch gather keeps its own order.)  L permutes each group of 8 k
+// us, rowwise + BF16 copy 16.4 -> 15.9 us.  Small launches only (below
+// LARGE_LAUNCH_WAVES): on large ones the effect followed where the buffers
+// lay -- one-pass rowwise + dequant at 262144 x 2048 went 460 -> 440 us in
+// one process and 490 -> 510 us in another -- and grouped launches showed no
+// change (358-361 us either way).  The dispatch gather keeps its own order.
+// L permutes each group of 8 k
 // consecutive workgroups among themselves: position j of group q goes to
 // 8 k q + k (j % 8) + j / 8.  A last, partial group and bands that straddle
 // workgroups (nct % WPW != 0) keep launch order.  The group index is a
@@ -511,19 +514,6 @@ __device__ __forceinline__ int64_t band_order(int64_t hw, const Geometry &G)
     const uint32_t q0 = udiv(h, G.bo_grp) * 8 * k;   // first workgroup of h's group
     const uint32_t j = h - q0;                       // 0 .. 8 k - 1
     return (int64_t)(q0 + (j & 7) * k + (j >> 3));
-}
-
-static void set_band_order(Geometry &G, int64_t wgs, int wpw)
-{
-    G.bo_k = 0;
-    G.bo_full = 0;
-    G.bo_grp = Div{0, 0};
-    if (G.nct % wpw != 0 || G.nct / wpw < 2)
-        return;
-    const int64_t k = G.nct / wpw;          // cols <= 2^26: 8 k <= 2^20
-    G.bo_k = (uint32_t)k;
-    G.bo_full = (uint32_t)(wgs / (8 * k) * (8 * k));
-    G.bo_grp = make_div((uint32_t)(8 * k));
 }
 
 // SCAN (grouped, G <= SCAN_MAX_GROUPS): the block prefix formed in LDS
@@ -778,6 +768,21 @@ __global__ void __launch_bounds__(256) grouped_prefix_kernel(const int64_t *__re
 // workgroups leave CUs idle (8192 x 2048: 20.5 us with 8, 17.3 us with 4).
 constexpr int64_t LARGE_LAUNCH_WAVES = 32768;
 
+// Band order (band_order) for a dense launch of `wgs` workgroups of `wpw`
+// wavefronts covering `waves` tiles; launch order on large launches.
+static void set_band_order(Geometry &G, int64_t waves, int64_t wgs, int wpw)
+{
+    G.bo_k = 0;
+    G.bo_full = 0;
+    G.bo_grp = Div{0, 0};
+    if (waves >= LARGE_LAUNCH_WAVES || G.nct % wpw != 0 || G.nct / wpw < 2)
+        return;
+    const int64_t k = G.nct / wpw;          // cols <= 2^26: 8 k <= 2^20
+    G.bo_k = (uint32_t)k;
+    G.bo_full = (uint32_t)(wgs / (8 * k) * (8 * k));
+    G.bo_grp = make_div((uint32_t)(8 * k));
+}
+
 template <bool ROW, bool COL, bool GROUPED, int WPW, bool GATHER, bool SCAN>
 static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint8_t *rs,
                              uint8_t *cc, uint8_t *cs, int64_t *P_out, hipStream_t stream)
@@ -787,7 +792,7 @@ static hipError_t launch_wpw(const Geometry &G, int64_t waves, uint8_t *rc, uint
         return hipErrorInvalidValue;
     Geometry Gl = G;
     if (!GROUPED && !GATHER)
-        set_band_order(Gl, wgs, WPW);
+        set_band_order(Gl, waves, wgs, WPW);
     hipLaunchKernelGGL((mxfp8_tile_kernel<ROW, COL, GROUPED, WPW, GATHER, SCAN>),
                        dim3((unsigned)wgs), dim3(64 * WPW), 0, stream, Gl, rc, rs, cc, cs, P_out);
     return hipGetLastError();
@@ -840,7 +845,7 @@ static hipError_t launch_qdq_wpw(const Geometry &G, int64_t waves, uint8_t *rc, 
     if (wgs * 64 * WPW > MAX_GRID_ITEMS)     // checked by the caller
         return hipErrorInvalidValue;
     Geometry Gl = G;
-    set_band_order(Gl, wgs, WPW);
+    set_band_order(Gl, waves, wgs, WPW);
     hipLaunchKernelGGL((mxfp8_row_qdq_kernel<ROW, WPW>), dim3((unsigned)wgs), dim3(64 * WPW), 0,
                        stream, Gl, rc, rs, dq);
     return hipGetLastError();
@@ -870,7 +875,7 @@ static hipError_t launch_ocp(const Geometry &G, int64_t waves, uint8_t *rc, uint
     if (wgs * 256 > MAX_GRID_ITEMS)          // checked by the caller
         return hipErrorInvalidValue;
     Geometry Gl = G;
-    set_band_order(Gl, wgs, 4);
+    set_band_order(Gl, waves, wgs, 4);
     hipLaunchKernelGGL((mxfp8_ocp_kernel<ROW, COL, 4>), dim3((unsigned)wgs), dim3(256), 0, stream,
                        Gl, rc, rs, cc, cs);
     return hipGetLastError();
