@@ -571,6 +571,13 @@ def config_timings(torch, E, W, legs, log, only=None):
                      ("nvfp4_export_gateup", "C4_gateup"), ("nvfp4_export_down", "C4_down")):
         if leg in by_name and sel(cfg):
             l = by_name[leg]
+            # A dequant config decodes what its quantize leg wrote: run that
+            # leg once first (with --config-only it may not have run).
+            src = {"grouped_dequant_mxfp8": "grouped_mxfp8_rowcol",
+                   "grouped_dequant_nvfp4": "grouped_nvfp4"}.get(leg)
+            if src in by_name:
+                by_name[src].launch()
+                torch.cuda.synchronize()
             ms = time_launches(torch, [l.launch], 10, 2, CFG_SAMPLES)
             fl = copy_floor(torch, E, l.bytes_in, l.bytes_out, 1, False, 10, 2)
             k, v = cfg_record(cfg, l.desc, ms, l.bytes, l.elems, 1, l.kernels, None, fl,
