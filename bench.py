@@ -60,14 +60,44 @@ KERNEL_SOURCES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one
+    space: what the compiler sees, so that an edit of comments alone (which
+    leaves the code object unchanged) keeps a kernel's digest.  String and
+    character literals are kept whole."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def csrc_digest(files=None) -> str:
-    """Digest of the sources a kernel is built from (all of csrc/ by default)."""
+    """Digest of the sources a kernel is built from (all of csrc/ by default):
+    the code text of the C/C++ files (code_text) and build.py as it is."""
     if files is None:
         files = sorted(os.listdir(CSRC)) + ["../build.py"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+            raw = fh.read()
+        body = raw if f.endswith(".py") else code_text(raw.decode()).encode()
+        h.update(f.encode() + body)
     return h.hexdigest()[:16]
 
 

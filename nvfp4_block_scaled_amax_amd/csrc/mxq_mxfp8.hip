@@ -26,7 +26,9 @@
 //
 // Schedule.  One tile per wavefront, every tile in one launch: wavefront w
 // converts 128-column strip w % nct of tile w / nct, so the four wavefronts
-// of a workgroup cover 512 consecutive columns of one 32-row band.  Each
+// of a workgroup cover 512 consecutive columns of one 32-row band (small
+// dense launches first permute workgroups so that a band's workgroups share
+// an XCD: band_order).  Each
 // tile's base addresses are wave-uniform (scalar registers) and lanes add
 // 32-bit offsets (cols < 2^27).  For ragged segments (grouped call) tile T
 // lies in the segment e with P[e] <= T < P[e+1] (binary search).
