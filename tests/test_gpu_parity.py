@@ -859,6 +859,31 @@ def test_colwise_transposed_layout(orc):
         check_colt(orc, W.mode_boundary(rows, cols, rows + 3 * cols), f"boundary {rows}x{cols}")
 
 
+def test_colwise_transposed_scale_stores(orc):
+    """The transposed scales go out as dwords only where whole and 4-byte
+    aligned: scale pitches (rows / 32) of 13, 33 and 12 blocks, groups of
+    eight blocks that end mid-dword, and a scale pointer one byte past an
+    aligned address (every store then a byte store; the byte before it and
+    the codes stay as they are)."""
+    for rows, cols in ((416, 160), (1056, 64), (384, 128), (288, 4128)):
+        check_colt(orc, W.mode_boundary(rows, cols, rows + 5 * cols), f"pitch {rows // 32} "
+                   f"{rows}x{cols}")
+    rows, cols = 256, 256
+    x = W.mode_boundary(rows, cols, 77)
+    announce(f"mxfp8 transposed columnwise, scale pointer off alignment {rows}x{cols}")
+    ct = torch.zeros((cols, rows), dtype=torch.uint8, device="cuda")
+    st = torch.full((cols * (rows // 32) + 1,), 0xAB, dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    mxq.mxq_mxfp8_quantize_rowcol_t(xd, rows, cols, None, None, ct, st.data_ptr() + 1)
+    torch.cuda.synchronize()
+    cc, cs = orc.mxfp8_colwise(x)
+    got = host(st)
+    assert got[0] == 0xAB, "byte before the scales written"
+    assert_same(got[1:].reshape(cols, rows // 32), np.ascontiguousarray(cs.T),
+                "misaligned col scales (transposed)")
+    assert_same(host(ct), np.ascontiguousarray(cc.T), "col codes (transposed)")
+
+
 def test_gemm_weight_gradient_from_transposed_copies(orc):
     """dW[N][K] = dY^T X over the M rows: both operands' columnwise copies,
     transposed, are K-contiguous operands of the same GEMM kernel."""
