@@ -73,6 +73,21 @@ def test_mxfp8_large_grid(orc):
     check_mxfp8(orc, W.mode_random(8192, 16416, 12), "random 8192x16416")
 
 
+@pytest.mark.parametrize("rows,cols", [(288, 1024), (160, 1024), (1056, 2048), (544, 4096),
+                                       (800, 1536)])
+def test_mxfp8_band_order_shapes(orc, rows, cols):
+    """Small dense launches take their workgroups in band order: each group of
+    8 k consecutive workgroups (k per 32-row band) is permuted, a last partial
+    group keeps launch order.  Shapes with a partial last group (288x1024: 18
+    workgroups in groups of 16; 1056x2048: 132 in groups of 32), with no whole
+    group (160x1024), with k = 8 (544x4096) and with k = 3 (800x1536, 12
+    strips).  Row+col, rowwise + dequant and the OCP variant."""
+    x = W.mode_boundary(rows, cols, rows + 11 * cols)
+    check_mxfp8(orc, x, f"boundary {rows}x{cols}")
+    check_qdq(orc, x, mxq.MXQ_FMT_MXFP8_ROW, f"{rows}x{cols}", codes_only_check=False)
+    check_ocp(orc, x, f"{rows}x{cols}")
+
+
 def test_mxfp8_rowwise_only_and_ragged_rows(orc):
     x = W.mode_boundary(96, 256, 3)[:77]
     check_mxfp8(orc, x, "rowwise 77x256", rowwise=True, colwise=False)
@@ -269,6 +284,17 @@ def test_nvfp4_shapes_one_wave_rows(orc, rows, cols):
     (8192 rows up to 2048 columns, 16384 up to 4096): one wavefront per row,
     full and partial rows."""
     check_nvfp4(orc, W.student_t_activations(rows, cols, rows + cols), f"t3 {rows}x{cols}")
+
+
+@pytest.mark.parametrize("rows,cols", [(300, 2048), (255, 1040), (4097, 4096), (8191, 2064)])
+def test_nvfp4_split_row_order(orc, rows, cols):
+    """The split kernel takes rows in runs of 32 per XCD within groups of 256
+    workgroups, the last partial group in launch order: row counts with a
+    partial group (300, 4097, 8191) and with none whole (255), at one and two
+    blocks per lane."""
+    check_nvfp4(orc, W.student_t_activations(rows, cols, 5 * rows + cols), f"t3 {rows}x{cols}")
+    check_qdq(orc, W.nvfp4_boundary(rows, cols, cols + 1), mxq.MXQ_FMT_NVFP4,
+              f"boundary {rows}x{cols}", codes_only_check=False)
 
 
 def test_nvfp4_boundary_rows(orc):
