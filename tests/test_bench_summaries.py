@@ -81,3 +81,16 @@ def test_summarize_stats(tmp_path):
     assert body[1][1:4] == ["1024", "1", "2.00"]
     assert body[2][1:4] == ["64", "1", "1.00"]
 
+
+
+def test_code_text_drops_comments_only():
+    """The traffic digests hash code_text: comments and whitespace runs go,
+    string and character literals (which may hold comment markers) stay, and
+    any change to the code itself changes the text."""
+    src = ('int a = 1; // note\n/* block\n comment */ const char *s = "x//y /* z */";\n'
+           "char q = '\"'; const char *e = \"\\\"//\";\n")
+    assert bench.code_text(src) == ('int a = 1; const char *s = "x//y /* z */"; '
+                                    "char q = '\"'; const char *e = \"\\\"//\";")
+    assert bench.code_text(src) == bench.code_text(src.replace("note", "other words"))
+    assert bench.code_text(src) != bench.code_text(src.replace("a = 1", "a = 2"))
+    assert bench.code_text("x /* open") == "x"
